@@ -1,0 +1,403 @@
+"""Pin checks for the oracle: each returns (ok, detail) so that the mutation
+tests can show a planted mistake makes the corresponding pin fail.
+
+A pin ties an oracle function to something that is not the oracle: a value
+the pages print (tests/golden), a closed form, a library special case
+(PyTorch's casts), an invariant of the definition, or brute force.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_facts():
+    with open(os.path.join(GOLDEN, "pages_facts.json")) as f:
+        return json.load(f)
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            rows.append((parts[0], int(parts[1], 16)))
+    return rows
+
+
+def _parse_float(tok):
+    if tok.startswith(("0x", "-0x")):
+        return float.fromhex(tok)
+    return float(tok)
+
+
+def e4m3_worked_values():
+    return [(_parse_float(v), c) for v, c in _read_table("e4m3_worked_values.txt")]
+
+
+def bf16_worked_values():
+    return [(_parse_float(v), c) for v, c in _read_table("bf16_worked_values.txt")]
+
+
+# ------------------------------------------------------------------- P1 / P2
+
+def pin_lut_closed_form(O):
+    """P1: the table against the pages' facts and the bit-field definition."""
+    facts = golden_facts()["e4m3_range"]
+    t = O.e4m3_table()
+    nan_codes = sorted(int(c) for c in np.nonzero(np.isnan(t))[0])
+    if nan_codes != facts["nan_codes"]:
+        return False, f"NaN codes {nan_codes}"
+    fin = t[~np.isnan(t)]
+    if fin.size != 254:
+        return False, "finite count"
+    if fin.max() != facts["max_finite"] or fin.min() != facts["min_finite"]:
+        return False, "range"
+    if np.isinf(t).any():
+        return False, "inf present"
+    if not (t[0x7E] == 448.0 and t[0xFE] == -448.0):
+        return False, "448 codes"
+    if not (t[0x00] == 0 and not math.copysign(1, t[0x00]) < 0 and math.copysign(1, t[0x80]) < 0):
+        return False, "signed zeros"
+    if t[0x01] != 2.0 ** -9 or t[0x08] != 2.0 ** -6 or t[0x07] != 7 * 2.0 ** -9:
+        return False, "subnormal/normal boundary"
+    pos = t[0x00:0x7F]
+    if not np.all(np.diff(pos) > 0):
+        return False, "not increasing"
+    for c in range(0x80):
+        if not (np.isnan(t[c]) and np.isnan(t[c | 0x80])) and t[c | 0x80] != -t[c]:
+            return False, f"sign symmetry at {c:#x}"
+    # exponent/mantissa structure: within each binade 8 equally spaced values
+    for e in range(1, 16):
+        v = t[(e << 3):(e << 3) + (7 if e == 15 else 8)]
+        if not np.allclose(np.diff(v), 2.0 ** (e - 10)):
+            return False, f"binade {e}"
+    return True, ""
+
+
+def pin_lut_vs_torch(O):
+    """P1 (library special case): table equals PyTorch's float8_e4m3fn -> float32 decode."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    tv = codes.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    t = O.e4m3_table()
+    same = (np.isnan(tv) == np.isnan(t)) & ((tv == t) | np.isnan(t))
+    same &= (np.signbit(tv) == np.signbit(t)) | np.isnan(t)
+    return bool(same.all()), ""
+
+
+def pin_roundtrip(O):
+    """P2: ENC(dec(c)) == c for all 254 finite codes, -0.0 included."""
+    t = O.e4m3_table()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    back = O.e4m3_encode(t[codes].astype(np.float32))
+    bad = codes[back != codes]
+    scal = all(O.e4m3_encode_scalar(float(t[c])) == c for c in codes)
+    return (bad.size == 0 and scal), f"bad codes {bad[:8]}"
+
+
+# ------------------------------------------------------------------- P3 / P4
+
+def pin_worked_ties(O):
+    """P3: hand-derived encodings in tests/golden/e4m3_worked_values.txt."""
+    for v, c in e4m3_worked_values():
+        got = int(O.e4m3_encode(np.array([v], np.float32))[0])
+        got_s = O.e4m3_encode_scalar(float(np.float32(v)))
+        if got != c or got_s != c:
+            return False, f"{v!r}: {got:#x}/{got_s:#x} != {c:#x}"
+    return True, ""
+
+
+def _e4m3_boundary_inputs(O):
+    t = O.e4m3_table()
+    pos = np.sort(t[(~np.isnan(t)) & (t >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    base = np.concatenate([pos, mids]).astype(np.float32)
+    up = np.nextafter(base, np.float32(np.inf))
+    dn = np.nextafter(base, np.float32(-np.inf))
+    vals = np.concatenate([base, up, dn])
+    vals = vals[(vals >= 0) & (vals <= 448)]
+    return np.concatenate([vals, -vals]).astype(np.float32)
+
+
+def pin_encode_vs_torch(O, n_random=2_000_000, seed=7):
+    """P4: ENC equals PyTorch's float32 -> float8_e4m3fn cast on [-448, 448].
+
+    Every representable value, every midpoint and their float32 neighbours,
+    plus random values spread over all binades (log-uniform magnitudes).
+    """
+    import torch
+    g = np.random.default_rng(seed)
+    mag = np.exp2(g.uniform(-14.0, math.log2(448.0), n_random)).astype(np.float32)
+    rnd = np.where(g.random(n_random) < 0.5, -mag, mag).astype(np.float32)
+    rnd = np.clip(rnd, -448, 448).astype(np.float32)
+    vals = np.concatenate([_e4m3_boundary_inputs(O), rnd, np.array([0.0, -0.0], np.float32)])
+    ours = O.e4m3_encode(vals)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(ours != ref)[0]
+    return bad.size == 0, (f"{bad.size} mismatches, first {vals[bad[:4]]}" if bad.size else "")
+
+
+# ------------------------------------------------------------------------ P5
+
+def pin_bf16(O, n_random=1_000_000, seed=11):
+    """P5: BF16 RNE against hand-derived values and PyTorch's float32 -> bfloat16 cast."""
+    import torch
+    for v, c in bf16_worked_values():
+        got = int(O.f32_to_bf16_bits(np.array([v], np.float32))[0])
+        if got != c:
+            return False, f"{v!r}: {got:#x} != {c:#x}"
+    g = np.random.default_rng(seed)
+    bits = g.integers(0, 2 ** 32, n_random, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[~np.isnan(vals)]
+    ours = O.f32_to_bf16_bits(vals)
+    ref = torch.from_numpy(vals.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bad = np.nonzero(ours != ref)[0]
+    # widening is exact and inverts the narrowing on bf16-representable values
+    b = np.arange(0, 2 ** 16, dtype=np.uint32).astype(np.uint16)
+    f = O.bf16_bits_to_f32(b)
+    keep = ~np.isnan(f)
+    rt = O.f32_to_bf16_bits(f[keep]) == b[keep]
+    return bad.size == 0 and bool(rt.all()), f"{bad.size} mismatches"
+
+
+# ------------------------------------------------------------------------ P6
+
+def pin_grids(O):
+    """P6: the page's [128,256] -> [1,2], the workloads' grids, member-local origins."""
+    ex = golden_facts()["grid_example"]
+    if list(O.scale_grid_shape(*ex["weight_shape"])) != ex["scale_shape"]:
+        return False, "page example"
+    want = {(5120, 5120): (40, 40), (5000, 4000): (40, 32), (17408, 5120): (136, 40),
+            (5120, 17408): (40, 136), (6144, 5120): (48, 40), (1000, 5120): (8, 40),
+            (18432, 7168): (144, 56), (130, 300): (2, 3), (1, 1): (1, 1), (129, 128): (2, 1)}
+    for s, g in want.items():
+        if O.scale_grid_shape(*s) != g:
+            return False, f"{s}"
+    rows = [6144, 1000, 1000]
+    R, B = O.member_table(rows)
+    if R != [0, 6144, 7144] or B != [0, 48, 56]:
+        return False, f"member table {R} {B}"
+    checks = {0: 0, 6143: 47, 6144: 48, 7143: 55, 7144: 56, 7167: 56, 7271: 56, 7272: 57, 8143: 63}
+    for n, r in checks.items():
+        if O.stacked_scale_row(n, rows) != r:
+            return False, f"row {n}"
+    return True, ""
+
+
+# ------------------------------------------------------------------------ P7
+
+def pin_scale_direction(O, seed=3):
+    """P7: the multiply convention lands within FP8 error of the source weights; a divide is far off.
+
+    The source is BF16 N(0,0.02) [128,256], converted the way a checkpoint
+    converter does (PyTorch casts, ``synth.convert_checkpoint``).
+    """
+    import synth
+    facts = golden_facts()["scale_direction"]
+    g = np.random.default_rng(seed)
+    w = synth._bf16_round_torch(g.standard_normal((128, 256)).astype(np.float32) * np.float32(0.02))
+    mem = synth.convert_checkpoint(w)
+    s = mem.scale_f32()
+    wd = O.dequantize_block_scaled(mem.codes, s)
+    w64 = w.astype(np.float64)
+    normal = np.abs(O.e4m3_decode(mem.codes)) >= 2.0 ** -6
+    rel = np.abs(wd - w64)[normal] / np.abs(w64)[normal]
+    if not rel.max() <= facts["multiply_rel_error_upper"]:
+        return False, f"multiply rel err {rel.max()}"
+    frob_mul = np.linalg.norm(wd - w64) / np.linalg.norm(w64)
+    s_full = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)[:128, :256]
+    wdiv = O.e4m3_decode(mem.codes) / s_full
+    frob_div = np.linalg.norm(wdiv - w64) / np.linalg.norm(w64)
+    if not frob_div >= facts["divide_worse_by_at_least"] * frob_mul:
+        return False, f"divide not worse: {frob_div} vs {frob_mul}"
+    return True, f"mul {frob_mul:.3g} div {frob_div:.3g}"
+
+
+# ------------------------------------------------------------------------ P8
+
+def pin_quant_invariants(O, seed=5, M=257, K=1000):
+    """P8: per-group invariants of the activation quantizer."""
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((M, K)) * np.exp(g.uniform(-8, 8, (M, 1)))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, :130] = 1e-12
+    q, s = O.quant_act(x)
+    t = O.e4m3_table()
+    Kb = -(-K // 128)
+    if s.shape != (M, Kb) or q.shape != (M, K):
+        return False, "shapes"
+    for gi in range(Kb):
+        k0, k1 = gi * 128, min(K, gi * 128 + 128)
+        xg = x[:, k0:k1].astype(np.float64)
+        amax = np.abs(xg).max(axis=1).astype(np.float32)
+        want_s = (np.maximum(amax, np.float32(1e-10)) / np.float32(448)).astype(np.float32)
+        if not np.array_equal(s[:, gi], want_s):
+            return False, "scale formula"
+        dec = t[q[:, k0:k1]]
+        nz = amax > 1e-10
+        if not np.all(np.abs(dec[nz]).max(axis=1) == 448.0):
+            return False, "group max code"
+        err = np.abs(dec * s[:, gi:gi + 1].astype(np.float64) - xg)
+        if not np.all(err <= 2.0 ** -4 * np.abs(xg) + 2.0 ** -10 * s[:, gi:gi + 1]):
+            return False, "reconstruction error"
+    if not (np.all(q[0] == 0x00) and np.all(q[1] == 0x80)):
+        return False, "zero / negative-zero token"
+    return True, ""
+
+
+# ------------------------------------------------------------------- P9-P11
+
+def tiny_case(seed=1, M=5, K=300, rows=(130, 7)):
+    g = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    members = []
+    for r in rows:
+        codes = finite[g.integers(0, finite.size, (r, K))]
+        scale = np.exp2(g.uniform(-10, -2, (-(-r // 128), -(-K // 128)))).astype(np.float32)
+        members.append((codes, scale))
+    x = g.standard_normal((M, K)).astype(np.float32)
+    return x, members
+
+
+def pin_brute_force(O):
+    """P9: the NumPy paths equal pure-Python loops on a tiny grouped case with tails."""
+    x, members = tiny_case()
+    y = O.linear_w8a16(x, members)
+    yl = O.linear_w8a16_loops(x, members)
+    if not np.allclose(y, yl, rtol=1e-12, atol=1e-300):
+        return False, "w8a16"
+    xq, xs = O.quant_act(x)
+    y8 = O.linear_w8a8(xq, xs, members)
+    y8l = O.linear_w8a8_loops(xq, xs, members)
+    if not np.allclose(y8, y8l, rtol=1e-12, atol=1e-300):
+        return False, "w8a8"
+    return True, ""
+
+
+def pin_int_partials(O, seed=9):
+    """P10: float64 block sums of code products equal the exact integer sums."""
+    g = np.random.default_rng(seed)
+    t = O.e4m3_table()
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    for _ in range(200):
+        a = finite[g.integers(0, finite.size, 128)]
+        w = finite[g.integers(0, finite.size, 128)]
+        exact = O.w8a8_block_partial_int(a, w)
+        f = float(np.sum(t[a] * t[w]) * 2.0 ** 18)
+        if f != exact:
+            return False, f"{f} != {exact}"
+    return True, ""
+
+
+def pin_special_cases(O, seed=13):
+    """P11: reductions to plain integer matmul, per-tensor scaling and one-hot rows."""
+    g = np.random.default_rng(seed)
+    t = O.e4m3_table()
+    # (a) unit scales, integer-valued codes, integer X -> exact int64 matmul
+    int_codes = np.array([c for c in range(256) if not np.isnan(t[c]) and t[c] == np.round(t[c])
+                          and abs(t[c]) <= 16], np.uint8)
+    N, K, M = 20, 260, 3
+    codes = int_codes[g.integers(0, int_codes.size, (N, K))]
+    xi = g.integers(-5, 6, (M, K))
+    scale = np.ones(O.scale_grid_shape(N, K), np.float32)
+    y = O.linear_w8a16(xi.astype(np.float32), [(codes, scale)])
+    yi = xi.astype(np.int64) @ t[codes].astype(np.int64).T
+    if not np.array_equal(y, yi.astype(np.float64)):
+        return False, "integer matmul"
+    # (b) every scale equal to c -> c times the unscaled product (per-tensor degenerate case)
+    c = np.float32(0.0078125 * 3)
+    y1 = O.linear_w8a16(xi.astype(np.float32), [(codes, scale * c)])
+    if not np.array_equal(y1, yi.astype(np.float64) * float(c)):
+        return False, "uniform scale"
+    # (c) one-hot weight rows: y[m, n] = x[m, k_n] * dec(code) * s
+    K2 = 384
+    onehot = np.zeros((4, K2), np.uint8)
+    ks = [0, 127, 128, 383]
+    for n, k in enumerate(ks):
+        onehot[n, k] = 0x4B  # 1.375 * 2^2
+    sc = np.array([[0.5, 0.25, 2.0 ** -7]], np.float32)
+    x = g.standard_normal((2, K2)).astype(np.float32)
+    y = O.linear_w8a16(x, [(onehot, sc)])
+    for n, k in enumerate(ks):
+        want = x[:, k].astype(np.float64) * 5.5 * float(sc[0, k // 128])
+        if not np.array_equal(y[:, n], want):
+            return False, "one-hot"
+    return True, ""
+
+
+def pin_cross_arm(O):
+    """P12: the oracle's own W8A8-vs-W8A16 gate on a reduced decode-like case."""
+    import synth
+    w = synth.gaussian_weight(2, "pin_cross_arm_W", 512, 1024)
+    x = synth.gaussian_activations(2, "pin_cross_arm_X", 16, 1024)
+    members = [(w.codes, w.scale_f32())]
+    y16 = O.linear_w8a16(x, members)
+    xq, xs = O.quant_act(x)
+    y8 = O.linear_w8a8(xq, xs, members)
+    cos, rel = O.cross_arm_metrics(y8, y16)
+    gate = golden_facts()["cross_arm_gate"]
+    return (cos >= gate["cosine_min"] and rel <= gate["relative_rms_max"]), f"cos {cos} rel {rel}"
+
+
+# ------------------------------------------------------------ P8 brute force
+
+def _f32(v: float) -> float:
+    import struct
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def pin_quant_brute_force(O, seed=17, M=6, K=300):
+    """P8b: the vectorised quantizer equals a pure-Python float32 evaluation.
+
+    The pure-Python path divides in double precision and rounds once to
+    float32 (``struct``), which is the correctly rounded float32 quotient, so a
+    reciprocal-multiply or a missing clamp in the vectorised code shows up.
+    """
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((M, K)) * np.exp(g.uniform(-6, 6, (M, 1)))).astype(np.float32)
+    # Rows built to sit on E4M3 rounding midpoints after the division: each
+    # group holds its amax (so s is known) and values mid*s nudged by a few
+    # float32 ulps, where a reciprocal-multiply rounds differently.
+    t = O.e4m3_table()
+    pos = np.sort(t[(~np.isnan(t)) & (t > 0)])
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    adv = np.zeros((M, K), np.float32)
+    for m in range(M):
+        for gi in range(-(-K // 128)):
+            k0, k1 = gi * 128, min(K, gi * 128 + 128)
+            amax = np.float32(np.exp(g.uniform(-5, 5)))
+            sc = np.float32(amax / np.float32(448))
+            adv[m, k0] = amax
+            mu = g.choice(mids, k1 - k0 - 1)
+            base = (mu * np.float64(sc)).astype(np.float32)
+            nudge = g.integers(-3, 4, k1 - k0 - 1)
+            vals = base.view(np.int32) + nudge.astype(np.int32)
+            adv[m, k0 + 1:k1] = np.minimum(vals.view(np.float32), amax) * np.where(g.random(k1 - k0 - 1) < 0.5, -1, 1)
+    x = np.concatenate([x, adv]).astype(np.float32)
+    M = x.shape[0]
+    q, s = O.quant_act(x)
+    eps = _f32(1e-10)
+    for m in range(M):
+        for gi in range(-(-K // 128)):
+            k0, k1 = gi * 128, min(K, gi * 128 + 128)
+            amax = max(abs(float(v)) for v in x[m, k0:k1])
+            sc = _f32(max(amax, eps) / 448.0)
+            if float(s[m, gi]) != sc:
+                return False, f"scale {m},{gi}"
+            for k in range(k0, k1):
+                f = _f32(float(x[m, k]) / sc)
+                f = min(448.0, max(-448.0, f))
+                if int(q[m, k]) != O.e4m3_encode_scalar(f):
+                    return False, f"code {m},{k}"
+    return True, ""

@@ -1,0 +1,131 @@
+"""Planted mistakes in the oracle, on the CPU: each must make some pin fail.
+
+This shows the pins are strong enough to catch a dropped term, a wrong sign,
+a transposed grid or a wrong rounding rule anywhere in the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.bsf8_oracle as OM
+import oracle_pins as P
+
+
+def _fails(pin, O):
+    ok, _ = pin(O)
+    return not ok
+
+
+def test_pin_quant_brute_force_passes():
+    ok, detail = P.pin_quant_brute_force(OM)
+    assert ok, detail
+
+
+def test_mutation_divide_instead_of_multiply(monkeypatch):
+    orig = OM.dequantize_block_scaled
+
+    def divided(codes, scale):
+        N, K = codes.shape
+        s = np.repeat(np.repeat(np.asarray(scale, np.float64), 128, 0)[:N], 128, 1)[:, :K]
+        return OM.e4m3_decode(codes) / s
+    monkeypatch.setattr(OM, "dequantize_block_scaled", divided)
+    assert _fails(P.pin_scale_direction, OM)
+    monkeypatch.setattr(OM, "dequantize_block_scaled", orig)
+    assert not _fails(P.pin_scale_direction, OM)
+
+
+def test_mutation_wrong_bias(monkeypatch):
+    t = OM.e4m3_table() * 2.0
+    monkeypatch.setattr(OM, "e4m3_table", lambda: t.copy())
+    assert _fails(P.pin_lut_closed_form, OM)
+
+
+def test_mutation_ties_away_from_zero(monkeypatch):
+    def enc(f):
+        f = np.asarray(f, np.float32)
+        a = np.abs(f.astype(np.float64))
+        sign = np.where(np.signbit(f), 0x80, 0)
+        mant, exp = np.frexp(a)
+        t, e = mant * 2.0, exp - 1
+        mq = np.floor((t - 1.0) * 8.0 + 0.5).astype(np.int64)
+        e = np.where(mq == 8, e + 1, e)
+        mq = np.where(mq == 8, 0, mq)
+        sub = np.floor(a * 512 + 0.5).astype(np.int64)
+        return (np.where(a >= 2 ** -6, ((e + 7) << 3) | mq, sub) | sign).astype(np.uint8)
+    monkeypatch.setattr(OM, "e4m3_encode", enc)
+    assert _fails(P.pin_worked_ties, OM)
+    assert _fails(P.pin_encode_vs_torch, OM)
+
+
+def test_mutation_lost_negative_zero(monkeypatch):
+    orig = OM.e4m3_encode
+    monkeypatch.setattr(OM, "e4m3_encode", lambda f: np.where(np.asarray(f) == 0, 0, orig(f)).astype(np.uint8))
+    assert _fails(P.pin_roundtrip, OM)
+
+
+def test_mutation_reciprocal_multiply_in_quant(monkeypatch):
+    def quant(x, eps=OM.ACT_EPS):
+        x = np.asarray(x, np.float32)
+        M, K = x.shape
+        Kb = -(-K // 128)
+        q = np.empty((M, K), np.uint8)
+        s_all = np.empty((M, Kb), np.float32)
+        for g in range(Kb):
+            xg = x[:, g * 128:(g + 1) * 128]
+            s = (np.maximum(np.abs(xg).max(1), eps) / np.float32(448)).astype(np.float32)
+            inv = (np.float32(1) / s).astype(np.float32)
+            f = np.clip((xg * inv[:, None]).astype(np.float32), -448, 448)
+            q[:, g * 128:(g + 1) * 128] = OM.e4m3_encode(f)
+            s_all[:, g] = s
+        return q, s_all
+    monkeypatch.setattr(OM, "quant_act", quant)
+    assert _fails(P.pin_quant_brute_force, OM)
+
+
+def test_mutation_global_grid_for_grouped_members(monkeypatch):
+    def members_global(members):
+        codes = np.concatenate([c for c, _ in members])
+        scales = np.concatenate([s for _, s in members])
+        N, K = codes.shape
+        s = np.repeat(np.repeat(scales.astype(np.float64), 128, 0), 128, 1)
+        s = s[:N, :K] if s.shape[0] >= N else np.pad(s, ((0, N - s.shape[0]), (0, 0)), mode="edge")[:N, :K]
+        return OM.e4m3_decode(codes) * s
+    monkeypatch.setattr(OM, "dequantize_members", members_global)
+    assert _fails(P.pin_brute_force, OM)
+
+
+def test_mutation_dropped_tail_block(monkeypatch):
+    orig = OM.dequantize_act
+
+    def drop(codes, scales):
+        a = orig(codes, scales)
+        K = a.shape[1]
+        a[:, (K // 128) * 128:] = 0.0
+        return a
+    monkeypatch.setattr(OM, "dequantize_act", drop)
+    assert _fails(P.pin_brute_force, OM)
+
+
+def test_mutation_transposed_operand(monkeypatch):
+    orig = OM.dequantize_block_scaled
+
+    def transposed_scale(codes, scale):
+        N, K = codes.shape
+        s = np.asarray(scale, np.float64)
+        st = np.resize(s.T, s.shape)
+        sf = np.repeat(np.repeat(st, 128, 0)[:N], 128, 1)[:, :K]
+        return OM.e4m3_decode(codes) * sf
+    monkeypatch.setattr(OM, "dequantize_block_scaled", transposed_scale)
+    assert _fails(P.pin_brute_force, OM)
+
+
+def test_mutation_bf16_truncation(monkeypatch):
+    monkeypatch.setattr(OM, "f32_to_bf16_bits",
+                        lambda x: (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    assert _fails(P.pin_bf16, OM)
+
+
+def test_mutation_scale_grid_floor(monkeypatch):
+    monkeypatch.setattr(OM, "scale_grid_shape", lambda n, k, block=(128, 128): (n // 128, k // 128))
+    assert _fails(P.pin_grids, OM)
