@@ -1,0 +1,291 @@
+"""Python binding of libbsf8, the block-scaled FP8 linear projection for MI355X.
+
+Argument marshalling only: every step of the projection runs in the HIP
+library (``libbsf8.so``, built by ``python -m block_scaled_fp8_linear_amd.build``).
+PyTorch supplies device memory and the current stream.  There is no CPU path:
+if the library is missing, importing works but every call raises.
+
+Entry points mirror ``include/bsf8.h``:
+
+* ``validate(...)``                     header-only geometry check, returns a status name
+* ``BlockFP8Weight(members, ...)``      handle over borrowed device tensors
+* ``quant_act(x)``                      per-token 1x128 E4M3 quantization -> (xq, xs)
+* ``linear_w8a16(w, x)``                F32-activation arm
+* ``linear_w8a8(w, xq, xs)``            FP8 x FP8 arm with F32 epilogue
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsf8.so")
+
+DT_INVALID, DT_F8_E4M3, DT_F8_E5M2, DT_BF16, DT_F16, DT_F32, DT_U8, DT_OTHER = range(8)
+ARM_W8A16, ARM_W8A8 = 0, 1
+DTYPE_NAMES = {"F8_E4M3": DT_F8_E4M3, "F8_E5M2": DT_F8_E5M2, "BF16": DT_BF16, "F16": DT_F16,
+               "F32": DT_F32, "U8": DT_U8}
+MAX_MEMBERS = 8
+BLOCK = 128
+
+
+class BSF8Error(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status, self.name, self.detail = status, name, detail
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("rank", ctypes.c_int32), ("shape", ctypes.c_int64 * 4),
+                ("data", ctypes.c_void_p)]
+
+
+class MemberDesc(ctypes.Structure):
+    _fields_ = [("weight", TensorDesc), ("scale_inv", ctypes.POINTER(TensorDesc)),
+                ("scale", ctypes.POINTER(TensorDesc))]
+
+
+class Decl(ctypes.Structure):
+    _fields_ = [("quant_method_fp8", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32)]
+
+
+_lib = None
+
+# (name, restype, argtypes) of every entry point the header declares.
+EXPORTS = [
+    ("bsf8_abi_version", ctypes.c_int32, []),
+    ("bsf8_status_name", ctypes.c_char_p, [ctypes.c_int]),
+    ("bsf8_last_error", ctypes.c_char_p, []),
+    ("bsf8_validate", ctypes.c_int, [ctypes.POINTER(Decl), ctypes.POINTER(MemberDesc), ctypes.c_int32]),
+    ("bsf8_weight_create", ctypes.c_int, [ctypes.POINTER(Decl), ctypes.POINTER(MemberDesc), ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_void_p)]),
+    ("bsf8_weight_destroy", None, [ctypes.c_void_p]),
+    ("bsf8_weight_geometry", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                            ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
+    ("bsf8_weight_scale_row", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32),
+                                             ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
+    ("bsf8_quant_act", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_void_p]),
+    ("bsf8_workspace_size", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                           ctypes.POINTER(ctypes.c_size_t)]),
+    ("bsf8_linear_w8a16", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("bsf8_linear_w8a8", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("bsf8_describe", ctypes.c_char_p, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]),
+]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbsf8.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m block_scaled_fp8_linear_amd.build` "
+                              "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in EXPORTS:
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_name(st: int) -> str:
+    return lib().bsf8_status_name(st).decode()
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise BSF8Error(st, status_name(st), f"{what}: {lib().bsf8_last_error().decode()}")
+
+
+def _tdesc(dtype, shape, addr) -> TensorDesc:
+    d = TensorDesc()
+    d.dtype = DTYPE_NAMES[dtype] if isinstance(dtype, str) else int(dtype)
+    d.rank = len(shape)
+    for i, s in enumerate(shape):
+        d.shape[i] = int(s)
+    d.data = int(addr) if addr else None
+    return d
+
+
+def _members_array(members: Sequence[dict]):
+    """members: dicts with 'weight' (dtype, shape, addr) and optional 'scale_inv' / 'scale'."""
+    keep = []
+    arr = (MemberDesc * max(1, len(members)))()
+    for i, m in enumerate(members):
+        w = m["weight"]
+        arr[i].weight = _tdesc(w["dtype"], w["shape"], w.get("addr"))
+        for leaf in ("scale_inv", "scale"):
+            s = m.get(leaf)
+            if s is not None:
+                d = _tdesc(s["dtype"], s["shape"], s.get("addr"))
+                keep.append(d)
+                setattr(arr[i], leaf, ctypes.pointer(d))
+    return arr, keep
+
+
+def _decl(quant_method: str = "fp8", block=(BLOCK, BLOCK)) -> Decl:
+    d = Decl()
+    d.quant_method_fp8 = 1 if quant_method == "fp8" else 0
+    d.block_n, d.block_k = int(block[0]), int(block[1])
+    return d
+
+
+def validate(quant_method: str, block, members: Sequence[dict]) -> str:
+    """Header-only validation (no device access); returns the status name."""
+    decl = _decl(quant_method, block)
+    arr, _keep = _members_array(members)
+    return status_name(lib().bsf8_validate(ctypes.byref(decl), arr, len(members)))
+
+
+# ------------------------------------------------------------------ torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt_of(t) -> int:
+    torch = _torch()
+    return {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16, torch.uint8: DT_U8,
+            torch.float8_e4m3fn: DT_F8_E4M3, torch.float8_e5m2: DT_F8_E5M2}.get(t.dtype, DT_OTHER)
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class BlockFP8Weight:
+    """Immutable handle over a (possibly grouped) block-FP8 weight on the GPU.
+
+    ``members``: list of (weight, scale_inv) device tensors; weight is uint8 or
+    float8_e4m3fn [N_i, K] (contiguous), scale_inv is bfloat16 or float32
+    [ceil(N_i/128), ceil(K/128)] (contiguous).  The tensors are borrowed: this
+    object keeps references so they stay alive, and never modifies them.
+    """
+
+    def __init__(self, members: Sequence[Tuple[object, object]], quant_method: str = "fp8", block=(BLOCK, BLOCK)):
+        L = lib()
+        descs = []
+        self._tensors = []
+        for w, s in members:
+            if not (w.is_contiguous() and s.is_contiguous()):
+                raise ValueError("weights and scale grids must be contiguous")
+            wdt = DT_F8_E4M3 if _dt_of(w) in (DT_U8, DT_F8_E4M3) else _dt_of(w)
+            descs.append(dict(weight=dict(dtype=wdt, shape=tuple(w.shape), addr=w.data_ptr()),
+                              scale_inv=dict(dtype=_dt_of(s), shape=tuple(s.shape), addr=s.data_ptr())))
+            self._tensors += [w, s]
+        decl = _decl(quant_method, block)
+        arr, keep = _members_array(descs)
+        h = ctypes.c_void_p()
+        _check(L.bsf8_weight_create(ctypes.byref(decl), arr, len(descs), ctypes.byref(h)), "weight_create")
+        self._h = h
+        self.device = members[0][0].device
+        n, k, nm = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(L.bsf8_weight_geometry(h, ctypes.byref(n), ctypes.byref(k), ctypes.byref(nm)), "geometry")
+        self.n_total, self.K, self.n_members = n.value, k.value, nm.value
+        self._ws: Dict[tuple, object] = {}
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.bsf8_weight_destroy(h)
+            self._h = None
+
+    def describe(self, arm: int, M: int) -> str:
+        return lib().bsf8_describe(self._h, arm, M).decode()
+
+    def scale_row(self, n: int) -> Tuple[int, int, int]:
+        mi, lr, sr = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().bsf8_weight_scale_row(self._h, n, ctypes.byref(mi), ctypes.byref(lr), ctypes.byref(sr)),
+               "scale_row")
+        return mi.value, lr.value, sr.value
+
+    def workspace_size(self, arm: int, M: int) -> int:
+        b = ctypes.c_size_t()
+        _check(lib().bsf8_workspace_size(self._h, arm, M, ctypes.byref(b)), "workspace_size")
+        return b.value
+
+    def workspace(self, arm: int, M: int):
+        """A zero-filled device workspace, cached per stream and grown on demand."""
+        torch = _torch()
+        need = self.workspace_size(arm, M)
+        if need == 0:
+            return None, 0
+        key = _stream_ptr(self.device)
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws, ws.numel()
+
+
+def _out(out, M, N, dtype, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=dtype, device=device)
+    if out.dtype != dtype or out.dim() != 2 or out.shape[0] != M or out.shape[1] < N or out.stride(1) != 1:
+        raise ValueError("out must be [M, >=N] with unit column stride and the requested dtype")
+    return out
+
+
+def quant_act(x, xq=None, xs=None):
+    """Per-token 1x128 E4M3 quantization of x [M,K] (float32 or bfloat16) -> (xq uint8 [M,K], xs f32 [M,Kb])."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    Kb = -(-K // BLOCK)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M, Kb), dtype=torch.float32, device=x.device)
+    _check(lib().bsf8_quant_act(x.data_ptr(), _dt_of(x), M, K, x.stride(0), xq.data_ptr(), xq.stride(0),
+                                xs.data_ptr(), xs.stride(0), _stream_ptr(x.device)), "quant_act")
+    return xq, xs
+
+
+def linear_w8a16(w: BlockFP8Weight, x, out_dtype=None, out=None, workspace=None):
+    """F32-activation arm: y [M, N] = x . dequant(W)^T (float32 output unless out_dtype says bfloat16)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    if x.dim() != 2 or x.stride(1) != 1 or x.shape[1] != w.K:
+        raise ValueError("x must be [M, K] with unit column stride")
+    M = x.shape[0]
+    y = _out(out, M, w.n_total, out_dtype, x.device)
+    ws, wsb = workspace if workspace is not None else w.workspace(ARM_W8A16, M)
+    _check(lib().bsf8_linear_w8a16(w.handle, x.data_ptr(), _dt_of(x), M, x.stride(0), y.data_ptr(), _dt_of(y),
+                                   y.stride(0), ws.data_ptr() if ws is not None else None, wsb,
+                                   _stream_ptr(x.device)), "linear_w8a16")
+    return y
+
+
+def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=None):
+    """FP8 x FP8 arm with F32 epilogue: y [M, N] (bfloat16 output unless out_dtype says float32)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    if xq.dim() != 2 or xq.shape[1] != w.K or xq.stride(1) != 1 or xs.stride(1) != 1:
+        raise ValueError("xq must be [M, K] and xs [M, Kb], unit column stride")
+    M = xq.shape[0]
+    y = _out(out, M, w.n_total, out_dtype, xq.device)
+    ws, wsb = workspace if workspace is not None else w.workspace(ARM_W8A8, M)
+    _check(lib().bsf8_linear_w8a8(w.handle, xq.data_ptr(), xq.stride(0), xs.data_ptr(), xs.stride(0), M,
+                                  y.data_ptr(), _dt_of(y), y.stride(0),
+                                  ws.data_ptr() if ws is not None else None, wsb, _stream_ptr(xq.device)),
+           "linear_w8a8")
+    return y
+
+
+__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "linear_w8a16", "linear_w8a8", "lib",
+           "status_name", "ARM_W8A16", "ARM_W8A8", "EXPORTS", "LIB_PATH", "MAX_MEMBERS"]

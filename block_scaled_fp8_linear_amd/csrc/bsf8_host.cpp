@@ -1,0 +1,290 @@
+// Host side of libbsf8: status names, the header-only validator, weight handles,
+// argument checks and dispatch to the kernel launchers.  No device memory is
+// touched here except through the launchers.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "bsf8_internal.h"
+
+namespace bsf8 {
+
+static thread_local std::string g_last_error;
+static thread_local std::string g_describe;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+bsf8_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSF8_OK;
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return BSF8_E_DEVICE;
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static bsf8_status fail(bsf8_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(bsf8_status_name(s)) + ": " + buf;
+  return s;
+}
+
+static bool shape_is(const bsf8_tensor_desc* t, int64_t a, int64_t b) {
+  return t->rank == 2 && t->shape[0] == a && t->shape[1] == b;
+}
+
+// Header-only validation.  The order of the checks is the precedence the ABI
+// documents, so every bad input has exactly one status.
+static bsf8_status validate_impl(const bsf8_decl* decl, const bsf8_member_desc* members, int32_t n) {
+  if (decl == nullptr || (members == nullptr && n > 0)) return fail(BSF8_E_INVALID_ARG, "null descriptor");
+  if (n < 1 || n > kMaxMembers) return fail(BSF8_E_GROUP, "%d members (1..%d allowed)", n, kMaxMembers);
+  if (!decl->quant_method_fp8 || decl->block_n != kBlock || decl->block_k != kBlock)
+    return fail(BSF8_E_DECL, "declaration is not quant_method fp8 with weight_block_size [128,128] (got fp8=%d, [%d,%d])",
+                decl->quant_method_fp8, decl->block_n, decl->block_k);
+  for (int i = 0; i < n; ++i) {
+    const bsf8_member_desc& m = members[i];
+    const bsf8_tensor_desc& w = m.weight;
+    if (w.rank < 0 || w.rank > 4) return fail(BSF8_E_INVALID_ARG, "member %d: weight rank %d", i, w.rank);
+    if (w.dtype == BSF8_DT_F8_E5M2) return fail(BSF8_E_WEIGHT_E5M2, "member %d: E5M2 weight", i);
+    if (w.dtype != BSF8_DT_F8_E4M3) return fail(BSF8_E_WEIGHT_DTYPE, "member %d: weight dtype %d is not F8_E4M3", i, w.dtype);
+    if (w.rank != 2) return fail(BSF8_E_WEIGHT_RANK, "member %d: weight rank %d", i, w.rank);
+    if (w.shape[0] <= 0 || w.shape[1] <= 0)
+      return fail(BSF8_E_WEIGHT_EMPTY, "member %d: weight shape [%lld,%lld]", i, (long long)w.shape[0], (long long)w.shape[1]);
+    if (m.scale_inv == nullptr && m.scale == nullptr) return fail(BSF8_E_SCALE_MISSING, "member %d: FP8 weight without a scale", i);
+    if (m.scale_inv != nullptr && m.scale != nullptr)
+      return fail(BSF8_E_SCALE_AMBIGUOUS, "member %d: both a block grid and a row/tensor scale", i);
+    const bsf8_tensor_desc* leaf = m.scale_inv ? m.scale_inv : m.scale;
+    if (leaf->rank < 0 || leaf->rank > 4) return fail(BSF8_E_INVALID_ARG, "member %d: scale rank %d", i, leaf->rank);
+    if (leaf->rank == 1) return fail(BSF8_E_SCALE_ROWWISE, "member %d: rank-1 (row-wise) scale", i);
+    if (leaf->rank == 0 && m.scale != nullptr) return fail(BSF8_E_SCALE_PER_TENSOR, "member %d: per-tensor scale", i);
+    if (leaf->rank != 2) return fail(BSF8_E_SCALE_RANK, "member %d: scale rank %d", i, leaf->rank);
+    if (leaf->dtype != BSF8_DT_BF16 && leaf->dtype != BSF8_DT_F32)
+      return fail(BSF8_E_SCALE_DTYPE, "member %d: scale dtype %d is not BF16/F32", i, leaf->dtype);
+    const int64_t nb = ceil_div(w.shape[0], kBlock), kb = ceil_div(w.shape[1], kBlock);
+    if (!shape_is(leaf, nb, kb) && shape_is(leaf, kb, nb))
+      return fail(BSF8_E_SCALE_TRANSPOSED, "member %d: grid [%lld,%lld] is the transpose of [%lld,%lld]", i,
+                  (long long)leaf->shape[0], (long long)leaf->shape[1], (long long)nb, (long long)kb);
+    if (!shape_is(leaf, nb, kb))
+      return fail(BSF8_E_SCALE_GRID, "member %d: grid [%lld,%lld] != [%lld,%lld]", i, (long long)leaf->shape[0],
+                  (long long)leaf->shape[1], (long long)nb, (long long)kb);
+    if (m.scale != nullptr)
+      return fail(BSF8_E_SCALE_GRID, "member %d: a block-shaped weight_scale leaf is not a weight_scale_inv grid", i);
+  }
+  const int64_t k0 = members[0].weight.shape[1];
+  const int32_t dt0 = members[0].scale_inv->dtype;
+  for (int i = 1; i < n; ++i) {
+    if (members[i].weight.shape[1] != k0) return fail(BSF8_E_GROUP, "member %d: K differs from member 0", i);
+    if (members[i].scale_inv->dtype != dt0) return fail(BSF8_E_GROUP, "member %d: scale dtype differs from member 0", i);
+  }
+  for (int i = 0; i < n; ++i) {
+    const uintptr_t wa = reinterpret_cast<uintptr_t>(members[i].weight.data);
+    if (wa % 16 != 0) return fail(BSF8_E_ALIGNMENT, "member %d: weight address not 16-byte aligned", i);
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(members[i].scale_inv->data);
+    const uintptr_t esz = members[i].scale_inv->dtype == BSF8_DT_BF16 ? 2 : 4;
+    if (sa % esz != 0) return fail(BSF8_E_ALIGNMENT, "member %d: scale address not element aligned", i);
+  }
+  return BSF8_OK;
+}
+
+static bool dtype_ok(int32_t dt, bool f32, bool bf16) {
+  return (f32 && dt == BSF8_DT_F32) || (bf16 && dt == BSF8_DT_BF16);
+}
+
+}  // namespace bsf8
+
+using namespace bsf8;
+
+extern "C" {
+
+int32_t bsf8_abi_version(void) { return BSF8_ABI_VERSION; }
+
+const char* bsf8_status_name(bsf8_status s) {
+  switch (s) {
+    case BSF8_OK: return "OK";
+    case BSF8_E_INVALID_ARG: return "INVALID_ARG";
+    case BSF8_E_GROUP: return "GROUP";
+    case BSF8_E_DECL: return "DECL";
+    case BSF8_E_WEIGHT_E5M2: return "WEIGHT_E5M2";
+    case BSF8_E_WEIGHT_DTYPE: return "WEIGHT_DTYPE";
+    case BSF8_E_WEIGHT_RANK: return "WEIGHT_RANK";
+    case BSF8_E_WEIGHT_EMPTY: return "WEIGHT_EMPTY";
+    case BSF8_E_SCALE_MISSING: return "SCALE_MISSING";
+    case BSF8_E_SCALE_AMBIGUOUS: return "SCALE_AMBIGUOUS";
+    case BSF8_E_SCALE_ROWWISE: return "SCALE_ROWWISE";
+    case BSF8_E_SCALE_PER_TENSOR: return "SCALE_PER_TENSOR";
+    case BSF8_E_SCALE_RANK: return "SCALE_RANK";
+    case BSF8_E_SCALE_DTYPE: return "SCALE_DTYPE";
+    case BSF8_E_SCALE_TRANSPOSED: return "SCALE_TRANSPOSED";
+    case BSF8_E_SCALE_GRID: return "SCALE_GRID";
+    case BSF8_E_ALIGNMENT: return "ALIGNMENT";
+    case BSF8_E_UNSUPPORTED: return "UNSUPPORTED";
+    case BSF8_E_WORKSPACE: return "WORKSPACE";
+    case BSF8_E_DEVICE: return "DEVICE";
+  }
+  return "UNKNOWN";
+}
+
+const char* bsf8_last_error(void) { return g_last_error.c_str(); }
+
+bsf8_status bsf8_validate(const bsf8_decl* decl, const bsf8_member_desc* members, int32_t n_members) {
+  return validate_impl(decl, members, n_members);
+}
+
+bsf8_status bsf8_weight_create(const bsf8_decl* decl, const bsf8_member_desc* members, int32_t n_members,
+                               bsf8_weight** out) {
+  if (out == nullptr) return fail(BSF8_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  bsf8_status st = validate_impl(decl, members, n_members);
+  if (st != BSF8_OK) return st;
+  const int64_t K = members[0].weight.shape[1];
+  int64_t total = 0;
+  for (int i = 0; i < n_members; ++i) {
+    if (members[i].weight.data == nullptr || members[i].scale_inv->data == nullptr)
+      return fail(BSF8_E_INVALID_ARG, "member %d: a handle needs device addresses", i);
+    total += members[i].weight.shape[0];
+  }
+  if (K > INT32_MAX / 2 || total > INT32_MAX / 2)
+    return fail(BSF8_E_UNSUPPORTED, "N or K beyond 2^30");
+  bsf8_weight* h = new bsf8_weight();
+  std::memset(&h->dev, 0, sizeof(h->dev));
+  h->dev.n_members = n_members;
+  h->dev.K = static_cast<int32_t>(K);
+  h->dev.Kb = static_cast<int32_t>(ceil_div(K, kBlock));
+  h->dev.scale_bf16 = members[0].scale_inv->dtype == BSF8_DT_BF16 ? 1 : 0;
+  h->aligned16 = (K % 16) == 0;
+  int64_t col = 0, srow = 0;
+  for (int i = 0; i < n_members; ++i) {
+    const int64_t rows = members[i].weight.shape[0];
+    h->dev.m[i].w = static_cast<const uint8_t*>(members[i].weight.data);
+    h->dev.m[i].s = members[i].scale_inv->data;
+    h->dev.m[i].rows = static_cast<int32_t>(rows);
+    h->dev.m[i].col0 = static_cast<int32_t>(col);
+    h->rows[i] = rows;
+    h->col0[i] = col;
+    h->srow0[i] = srow;
+    col += rows;
+    srow += ceil_div(rows, kBlock);
+  }
+  h->n_total = total;
+  *out = h;
+  return BSF8_OK;
+}
+
+void bsf8_weight_destroy(bsf8_weight* w) { delete w; }
+
+bsf8_status bsf8_weight_geometry(const bsf8_weight* w, int64_t* n_total, int64_t* k, int32_t* n_members) {
+  if (w == nullptr) return fail(BSF8_E_INVALID_ARG, "null handle");
+  if (n_total) *n_total = w->n_total;
+  if (k) *k = w->dev.K;
+  if (n_members) *n_members = w->dev.n_members;
+  return BSF8_OK;
+}
+
+bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* member, int64_t* local_row,
+                                  int64_t* stacked_row) {
+  if (w == nullptr) return fail(BSF8_E_INVALID_ARG, "null handle");
+  if (n < 0 || n >= w->n_total) return fail(BSF8_E_INVALID_ARG, "row %lld outside [0,%lld)", (long long)n, (long long)w->n_total);
+  for (int i = w->dev.n_members - 1; i >= 0; --i) {
+    if (n >= w->col0[i]) {
+      const int64_t r = (n - w->col0[i]) / kBlock;
+      if (member) *member = i;
+      if (local_row) *local_row = r;
+      if (stacked_row) *stacked_row = w->srow0[i] + r;
+      return BSF8_OK;
+    }
+  }
+  return fail(BSF8_E_INVALID_ARG, "row not found");
+}
+
+bsf8_status bsf8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                           int64_t ldq, float* xs, int64_t ldxs, void* stream) {
+  if (M < 0 || K < 0) return fail(BSF8_E_INVALID_ARG, "negative size");
+  if (!dtype_ok(x_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "x dtype %d (F32 or BF16)", x_dtype);
+  if (M == 0 || K == 0) return BSF8_OK;
+  if (x == nullptr || xq == nullptr || xs == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (ldx < K || ldq < K || ldxs < ceil_div(K, kBlock)) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (M > INT32_MAX || K > INT32_MAX / 2) return fail(BSF8_E_UNSUPPORTED, "M or K too large");
+  const size_t esz = x_dtype == BSF8_DT_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(x) % esz || reinterpret_cast<uintptr_t>(xs) % 4)
+    return fail(BSF8_E_ALIGNMENT, "x or xs not element aligned");
+  return launch_quant_act(x, x_dtype == BSF8_DT_BF16, M, K, ldx, xq, ldq, xs, ldxs,
+                          static_cast<hipStream_t>(stream));
+}
+
+bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, size_t* bytes) {
+  if (w == nullptr || bytes == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");
+  if (arm == BSF8_ARM_W8A16) *bytes = M ? w8a16_workspace_bytes(w->dev, M) : 0;
+  else if (arm == BSF8_ARM_W8A8) *bytes = M ? w8a8_workspace_bytes(w->dev, M) : 0;
+  else return fail(BSF8_E_INVALID_ARG, "arm %d", arm);
+  return BSF8_OK;
+}
+
+bsf8_status bsf8_linear_w8a16(const bsf8_weight* w, const void* x, int32_t x_dtype, int64_t M, int64_t ldx,
+                              void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (w == nullptr) return fail(BSF8_E_INVALID_ARG, "null handle");
+  if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");
+  if (!dtype_ok(x_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "x dtype %d (F32 or BF16)", x_dtype);
+  if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
+  if (M == 0) return BSF8_OK;
+  if (x == nullptr || y == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (ldx < w->dev.K || ldy < w->n_total) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (M > INT32_MAX / 2) return fail(BSF8_E_UNSUPPORTED, "M too large");
+  const size_t xe = x_dtype == BSF8_DT_F32 ? 4 : 2, ye = y_dtype == BSF8_DT_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(x) % xe || reinterpret_cast<uintptr_t>(y) % ye)
+    return fail(BSF8_E_ALIGNMENT, "x or y not element aligned");
+  const size_t need = w8a16_workspace_bytes(w->dev, M);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(BSF8_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(BSF8_E_ALIGNMENT, "workspace not 256-byte aligned");
+  const bool aligned = w->aligned16 && (reinterpret_cast<uintptr_t>(x) % 16 == 0) && ((ldx * xe) % 16 == 0);
+  return launch_w8a16(w->dev, aligned, x, x_dtype == BSF8_DT_BF16, M, ldx, y, y_dtype == BSF8_DT_BF16, ldy,
+                      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t ldxs,
+                             int64_t M, void* y, int32_t y_dtype, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (w == nullptr) return fail(BSF8_E_INVALID_ARG, "null handle");
+  if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");
+  if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
+  if (M == 0) return BSF8_OK;
+  if (xq == nullptr || xs == nullptr || y == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (ldq < w->dev.K || ldxs < w->dev.Kb || ldy < w->n_total) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (M > INT32_MAX / 2) return fail(BSF8_E_UNSUPPORTED, "M too large");
+  const size_t ye = y_dtype == BSF8_DT_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(xs) % 4 || reinterpret_cast<uintptr_t>(y) % ye)
+    return fail(BSF8_E_ALIGNMENT, "xs or y not element aligned");
+  const size_t need = w8a8_workspace_bytes(w->dev, M);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(BSF8_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  const bool aligned = w->aligned16 && (reinterpret_cast<uintptr_t>(xq) % 16 == 0) && (ldq % 16 == 0);
+  return launch_w8a8(w->dev, aligned, xq, ldq, xs, ldxs, M, y, y_dtype == BSF8_DT_BF16, ldy, workspace,
+                     workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M) {
+  if (w == nullptr) return nullptr;
+  char geo[256];
+  snprintf(geo, sizeof(geo), " | weight N=%lld K=%d members=%d scales=%s", (long long)w->n_total, w->dev.K,
+           w->dev.n_members, w->dev.scale_bf16 ? "bf16" : "f32");
+  if (arm == BSF8_ARM_W8A16) g_describe = describe_w8a16(w->dev, w->aligned16, M) + geo;
+  else if (arm == BSF8_ARM_W8A8) g_describe = describe_w8a8(w->dev, w->aligned16, M) + geo;
+  else g_describe = "unknown arm";
+  return g_describe.c_str();
+}
+
+}  // extern "C"

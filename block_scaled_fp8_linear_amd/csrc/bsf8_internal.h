@@ -1,0 +1,69 @@
+// Internal declarations shared by the host side and the kernel launchers of libbsf8.
+// Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "bsf8.h"
+
+namespace bsf8 {
+
+constexpr int kBlock = 128;       // weight_block_size and activation group width
+constexpr int kMaxMembers = BSF8_MAX_MEMBERS;
+
+// One grouped member as the kernels see it (passed by value in kernel args).
+struct MemberDev {
+  const uint8_t* w;   // [rows, K] E4M3 bytes, row stride K
+  const void* s;      // [ceil(rows/128), Kb] BF16 or F32 scales, row stride Kb
+  int32_t rows;       // N_i
+  int32_t col0;       // R_i: first output feature of this member in Y
+};
+
+struct WeightDev {
+  MemberDev m[kMaxMembers];
+  int32_t n_members;
+  int32_t K;
+  int32_t Kb;          // ceil(K/128)
+  int32_t scale_bf16;  // 1: BF16 scales, 0: F32 scales
+};
+
+// Per-launch tile table: member i owns tiles [tile0[i], tile0[i+1]).
+struct TileMap {
+  int32_t tile0[kMaxMembers + 1];
+  int32_t n_tiles[kMaxMembers];  // row tiles of member i
+};
+
+void set_error(const char* fmt, ...);
+bsf8_status device_status(hipError_t e, const char* what);
+
+// Kernel launchers (one per .hip translation unit).
+bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
+                             uint8_t* xq, int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream);
+
+size_t w8a16_workspace_bytes(const WeightDev& w, int64_t M);
+bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x_bf16, int64_t M,
+                         int64_t ldx, void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M);
+
+size_t w8a8_workspace_bytes(const WeightDev& w, int64_t M);
+bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,
+                        int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M);
+
+}  // namespace bsf8
+
+// The opaque handle of the ABI.
+struct bsf8_weight {
+  bsf8::WeightDev dev;
+  int64_t n_total;
+  int64_t rows[bsf8::kMaxMembers];
+  int64_t col0[bsf8::kMaxMembers];
+  int64_t srow0[bsf8::kMaxMembers];  // B_i: origin of member i in the stacked grids
+  bool aligned16;                    // K % 16 == 0 and every weight pointer 16-byte aligned
+};

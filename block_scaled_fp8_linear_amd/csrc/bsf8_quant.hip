@@ -1,0 +1,111 @@
+// Per-token 1x128 activation quantization to OCP E4M3 (gfx950).
+//
+// ("Module w8a8_prefill", section "WHY (#917 / #928)": per-token F32 scales over
+//  groups of 128 channels; "FP8 Native Serving", section "FP8 E4M3: range and
+//  quirks": finite range +-448, no infinity.)
+//
+// One group of 128 channels is handled by 32 lanes (half a wave), 4 channels per
+// lane, so a wave covers 256 contiguous channels of one token and every global
+// access is a coalesced 16-byte (F32) or 8-byte (BF16) load and a 4-byte store.
+// The group amax is a 5-step butterfly inside the half-wave.  The arithmetic is
+// the defined one, in F32: s = max(amax, 1e-10) / 448 and f = x / s with IEEE
+// division (hipcc's default division is correctly rounded), clamp to +-448, then
+// the hardware RNE conversion v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950), which keeps
+// the sign of zero.  The kernel is HBM-bound: 4 (or 2) bytes in and 1 byte out
+// per channel, plus 4 bytes per group.
+#include <hip/hip_runtime.h>
+
+#include "bsf8_internal.h"
+
+namespace bsf8 {
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr float kE4M3Max = 448.0f;
+constexpr float kAmaxFloor = 1e-10f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* x, int64_t off, int valid, bool vec_ok, float v[4]) {
+  if (BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+    if (valid == 4 && vec_ok) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      v[0] = __uint_as_float(u.x << 16);
+      v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(u.y << 16);
+      v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = j < valid ? bf16_to_f32(p[j]) : 0.0f;
+    }
+  } else {
+    const float* p = static_cast<const float*>(x) + off;
+    if (valid == 4 && vec_ok) {
+      const float4 u = *reinterpret_cast<const float4*>(p);
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = j < valid ? p[j] : 0.0f;
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int32_t M, int32_t K,
+                                                                  int64_t ldx, uint8_t* __restrict__ xq, int64_t ldq,
+                                                                  float* __restrict__ xs, int64_t ldxs, int32_t Kb,
+                                                                  int32_t x_vec, int32_t q_vec) {
+  const int lane32 = threadIdx.x & 31;
+  const int64_t n_groups = int64_t(M) * Kb;
+  const int64_t stride = int64_t(gridDim.x) * (kQuantThreads / 32);
+  for (int64_t gi = int64_t(blockIdx.x) * (kQuantThreads / 32) + (threadIdx.x >> 5); gi < n_groups; gi += stride) {
+    const int64_t m = gi / Kb;
+    const int32_t g = int32_t(gi - m * Kb);
+    const int32_t k = g * kBlock + lane32 * 4;
+    const int valid = max(0, min(4, K - k));
+    float v[4];
+    load4<BF16>(x, m * ldx + k, valid, x_vec != 0, v);
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 32));
+    const float s = fmaxf(amax, kAmaxFloor) / kE4M3Max;
+    float f[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = fminf(fmaxf(v[j] / s, -kE4M3Max), kE4M3Max);
+    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
+    uint8_t* q = xq + m * ldq + k;
+    if (valid == 4 && q_vec) {
+      *reinterpret_cast<int*>(q) = packed;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < valid) q[j] = uint8_t(uint32_t(packed) >> (8 * j));
+    }
+    if (lane32 == 0) xs[m * ldxs + g] = s;
+  }
+}
+
+}  // namespace
+
+bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
+  const int32_t Kb = int32_t((K + kBlock - 1) / kBlock);
+  const int64_t n_groups = M * Kb;
+  const int64_t want = (n_groups + (kQuantThreads / 32) - 1) / (kQuantThreads / 32);
+  const int grid = int(want < 65536 ? want : 65536);
+  const size_t esz = x_bf16 ? 2 : 4;
+  const int x_vec = (reinterpret_cast<uintptr_t>(x) % (4 * esz) == 0) && ((ldx * esz) % (4 * esz) == 0);
+  const int q_vec = (reinterpret_cast<uintptr_t>(xq) % 4 == 0) && (ldq % 4 == 0);
+  if (x_bf16)
+    hipLaunchKernelGGL(quant_act_kernel<true>, dim3(grid), dim3(kQuantThreads), 0, stream, x, int32_t(M), int32_t(K),
+                       ldx, xq, ldq, xs, ldxs, Kb, x_vec, q_vec);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<false>, dim3(grid), dim3(kQuantThreads), 0, stream, x, int32_t(M),
+                       int32_t(K), ldx, xq, ldq, xs, ldxs, Kb, x_vec, q_vec);
+  return device_status(hipGetLastError(), "quant_act launch");
+}
+
+}  // namespace bsf8

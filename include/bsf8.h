@@ -1,0 +1,261 @@
+/*
+ * bsf8.h -- C ABI of libbsf8: the block-scaled FP8 linear projection Y = X . W^T
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources cited by page title and section):
+ *   - Weights are E4M3 bytes of shape [N,K] (row n = output feature, K contiguous),
+ *     kept exactly as the checkpoint stores them, with one scale per 128x128 block
+ *     on a ceil-divided grid [ceil(N/128), ceil(K/128)].  The scale multiplies the
+ *     decoded value; it is not a reciprocal.  BF16 scales widen exactly to F32.
+ *     ("Qwen checkpoints with block FP8 weights", layout and operator paragraphs;
+ *      "th#1803 ... hf.fp8-blockwise@1", section "What lands".)
+ *   - W8A16/F32 arm: F32 activations and F32 accumulation, the block multiplier
+ *     applied inside the reduction, neither operand requantized.
+ *     ("Qwen checkpoints with block FP8 weights", block-path paragraph.)
+ *   - W8A8 arm: activations quantized per token in 1x128 groups to E4M3 with an
+ *     F32 scale each; FP8 x FP8 products accumulated in F32; every 128-wide K
+ *     slice rescaled by activation scale x weight scale in an F32 epilogue.
+ *     ("Module w8a8_prefill", section "WHY (#917 / #928)".)
+ *   - Grouped tensors (fused QKV, gate/up) keep each member's own block-row
+ *     origin; the output concatenates the members along N.
+ *     ("Qwen checkpoints with block FP8 weights", operator paragraph.)
+ *
+ * Conventions for every call:
+ *   - Pointers named x, xq, xs, y, workspace and the tensor descriptors' data are
+ *     DEVICE addresses on the current HIP device.  Descriptors themselves live
+ *     in host memory and are read during the call only.
+ *   - The caller owns all memory.  A weight handle BORROWS the weight and scale
+ *     device pointers it was created from; they must stay valid and unchanged
+ *     until bsf8_weight_destroy.  The library never copies, repacks, rescales or
+ *     quantizes weights.
+ *   - No call allocates device memory, frees it or synchronizes the device.
+ *     Compute calls are asynchronous and ordered on the given stream
+ *     (a hipStream_t passed as void*; NULL = the default stream).
+ *   - Errors are returned as bsf8_status; nothing is thrown across the ABI.
+ *     bsf8_last_error() gives a thread-local sentence for the last failure.
+ *   - Element layouts are row-major with a leading dimension counted in
+ *     elements (ldx, ldq, ldxs, ldy).
+ *   - M == 0 is a successful no-op for every compute call.
+ */
+#ifndef BSF8_H
+#define BSF8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSF8_ABI_VERSION 1
+#define BSF8_MAX_MEMBERS 8
+
+typedef enum bsf8_status {
+  BSF8_OK = 0,
+  BSF8_E_INVALID_ARG = 1,       /* null pointer, negative size, bad dtype/arm enum, ld too small */
+  BSF8_E_GROUP = 2,             /* 0 or more than 8 members; members disagree on K or scale dtype */
+  BSF8_E_DECL = 3,              /* declaration is not quant_method fp8 with weight_block_size [128,128] */
+  BSF8_E_WEIGHT_E5M2 = 4,       /* E5M2 weight encoding */
+  BSF8_E_WEIGHT_DTYPE = 5,      /* weight is not F8_E4M3 (e.g. a dense BF16 tree) */
+  BSF8_E_WEIGHT_RANK = 6,       /* weight is not rank 2 */
+  BSF8_E_WEIGHT_EMPTY = 7,      /* a weight dimension is zero */
+  BSF8_E_SCALE_MISSING = 8,     /* FP8 weight with neither scale leaf */
+  BSF8_E_SCALE_AMBIGUOUS = 9,   /* both a block grid and a row/tensor scale leaf */
+  BSF8_E_SCALE_ROWWISE = 10,    /* a rank-1 scale (one scale per row) */
+  BSF8_E_SCALE_PER_TENSOR = 11, /* a rank-0 weight_scale (per-tensor layout, not this format) */
+  BSF8_E_SCALE_RANK = 12,       /* any other scale rank than 2 */
+  BSF8_E_SCALE_DTYPE = 13,      /* scale grid is not BF16 or F32 */
+  BSF8_E_SCALE_TRANSPOSED = 14, /* grid shaped [Kb,Nb] instead of [Nb,Kb] */
+  BSF8_E_SCALE_GRID = 15,       /* any other grid shape (mis-blocked, floor-divided, ...) */
+  BSF8_E_ALIGNMENT = 16,        /* weight address not 16-byte aligned, scale not element aligned,
+                                   or an activation/output address or ld not aligned as a call needs */
+  BSF8_E_UNSUPPORTED = 17,      /* a dtype combination this build does not implement */
+  BSF8_E_WORKSPACE = 18,        /* workspace missing or smaller than bsf8_workspace_size reports */
+  BSF8_E_DEVICE = 19            /* HIP error at launch; see bsf8_last_error() */
+} bsf8_status;
+
+typedef enum bsf8_dtype {
+  BSF8_DT_INVALID = 0,
+  BSF8_DT_F8_E4M3 = 1,
+  BSF8_DT_F8_E5M2 = 2,
+  BSF8_DT_BF16 = 3,
+  BSF8_DT_F16 = 4,
+  BSF8_DT_F32 = 5,
+  BSF8_DT_U8 = 6,
+  BSF8_DT_OTHER = 7
+} bsf8_dtype;
+
+typedef enum bsf8_arm {
+  BSF8_ARM_W8A16 = 0,  /* F32 activations, F32 accumulation */
+  BSF8_ARM_W8A8 = 1    /* per-token 1x128 E4M3 activations, F32 epilogue */
+} bsf8_arm;
+
+/* Header-level description of one tensor.  data may be NULL for a header-only
+ * check (bsf8_validate); bsf8_weight_create needs device addresses. */
+typedef struct bsf8_tensor_desc {
+  int32_t dtype;      /* bsf8_dtype */
+  int32_t rank;       /* 0..4 */
+  int64_t shape[4];   /* first `rank` entries used */
+  const void* data;   /* device address or NULL */
+} bsf8_tensor_desc;
+
+/* One member of a (possibly grouped) weight.  scale_inv is the block-grid leaf
+ * (weight_scale_inv); scale is the row-wise / per-tensor leaf (weight_scale)
+ * that other FP8 layouts use.  Either may be NULL. */
+typedef struct bsf8_member_desc {
+  bsf8_tensor_desc weight;
+  const bsf8_tensor_desc* scale_inv;
+  const bsf8_tensor_desc* scale;
+} bsf8_member_desc;
+
+/* The checkpoint's quantization_config as declared. */
+typedef struct bsf8_decl {
+  int32_t quant_method_fp8;  /* nonzero when quant_method is "fp8" */
+  int32_t block_n;           /* weight_block_size[0] */
+  int32_t block_k;           /* weight_block_size[1] */
+} bsf8_decl;
+
+typedef struct bsf8_weight bsf8_weight;
+
+/* ABI version of the loaded library (BSF8_ABI_VERSION it was built with). */
+int32_t bsf8_abi_version(void);
+
+/* Stable upper-case name of a status ("OK", "SCALE_TRANSPOSED", ...). Never NULL. */
+const char* bsf8_status_name(bsf8_status s);
+
+/* Thread-local sentence describing the last non-OK status of this thread. */
+const char* bsf8_last_error(void);
+
+/*
+ * bsf8_validate -- geometry validation from headers alone, before any weight
+ * byte is read or uploaded.
+ * ("Qwen checkpoints with block FP8 weights", operator paragraph: E5M2,
+ *  ambiguous row/block scales, malformed grids and incompatible declarations
+ *  are refused before upload; "th#1803", sections "What lands" (headers only)
+ *  and "Why the refusals matter more than the load" (row-wise trees,
+ *  transposed or mis-blocked grids, FP8 without a scale, rank-1 scales,
+ *  configs that disagree with the bytes are refused by name).)
+ *
+ * decl, members: host pointers; n_members in 1..8.  Reads no device memory.
+ * Returns exactly one status; the precedence is
+ *   GROUP (member count) > DECL > per member in index order
+ *   [WEIGHT_E5M2 > WEIGHT_DTYPE > WEIGHT_RANK > WEIGHT_EMPTY > SCALE_MISSING >
+ *    SCALE_AMBIGUOUS > SCALE_ROWWISE > SCALE_PER_TENSOR > SCALE_RANK >
+ *    SCALE_DTYPE > SCALE_TRANSPOSED > SCALE_GRID]
+ *   > GROUP (K or scale dtype differ across members) > ALIGNMENT (non-NULL data
+ *   not 16-byte aligned for weights, not element aligned for scales).
+ * A square grid (Nb == Kb) given transposed has the right shape and cannot be
+ * detected from headers; it is accepted.
+ */
+bsf8_status bsf8_validate(const bsf8_decl* decl, const bsf8_member_desc* members, int32_t n_members);
+
+/*
+ * bsf8_weight_create -- validate (as bsf8_validate) and build an immutable
+ * handle over borrowed device pointers.  Every weight and scale_inv data
+ * pointer must be non-NULL.  Host-only: no device access.
+ * Member i owns output rows [R_i, R_i + N_i) with R_i = sum_{j<i} N_j; its
+ * scale grid is its own [ceil(N_i/128), ceil(K/128)] array (member-local
+ * origin).  On failure *out is set to NULL.
+ */
+bsf8_status bsf8_weight_create(const bsf8_decl* decl, const bsf8_member_desc* members,
+                               int32_t n_members, bsf8_weight** out);
+
+/* Release a handle (host memory only).  NULL is ignored. */
+void bsf8_weight_destroy(bsf8_weight* w);
+
+/* Geometry of a handle: total output features N = sum N_i, K, member count. */
+bsf8_status bsf8_weight_geometry(const bsf8_weight* w, int64_t* n_total, int64_t* k, int32_t* n_members);
+
+/*
+ * bsf8_weight_scale_row -- for output feature n in [0, N), the member index and
+ * the row of that member's scale grid the kernels use: (n - R_i) / 128.
+ * Also returns the row of the members' grids stacked in member order,
+ * B_i + (n - R_i) / 128 with B_i = sum_{j<i} ceil(N_j/128).  Host-only.
+ */
+bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* member,
+                                  int64_t* local_row, int64_t* stacked_row);
+
+/*
+ * bsf8_quant_act -- per-token 1x128 group quantization of activations.
+ * ("Module w8a8_prefill", section "WHY (#917 / #928)": per-token FP32 scales
+ *  over 1x128 groups; "FP8 Native Serving", section "FP8 E4M3: range and
+ *  quirks": E4M3 range +-448, no infinity.)
+ *
+ * x   : [M, K] with leading dimension ldx (elements), dtype F32 or BF16.
+ * xq  : [M, K] E4M3 bytes out, leading dimension ldq (bytes).
+ * xs  : [M, ceil(K/128)] F32 scales out, leading dimension ldxs (elements),
+ *       token-major (row m holds token m's group scales).
+ * For token m and group g (channels 128g .. min(128g+128, K) - 1):
+ *   amax = max |x|;  s = amax' / 448 with amax' = max(amax, 1e-10f) (IEEE F32);
+ *   q = round-to-nearest-even E4M3 of clamp(x / s, -448, 448) (IEEE F32
+ *   division), sign of zero kept.  xs holds s, the dequantization multiplier.
+ * Results are bit-exact: one byte pattern and one scale per input.
+ * Non-finite inputs are outside the defined domain.
+ * Errors: INVALID_ARG (null, negative, ld < K, ldxs < ceil(K/128), bad dtype),
+ *         DEVICE.
+ */
+bsf8_status bsf8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                           uint8_t* xq, int64_t ldq, float* xs, int64_t ldxs, void* stream);
+
+/*
+ * bsf8_workspace_size -- device workspace bytes a compute call of this handle
+ * needs for M tokens on the given arm (0 when none).  The workspace holds
+ * split-K partial sums and arrival counters.  Contract: zero-fill it once before
+ * its first use; every call returns its counters to zero, so it can be reused
+ * by later calls on the same stream.  Calls that overlap in time must not share
+ * a workspace.
+ */
+bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, size_t* bytes);
+
+/*
+ * bsf8_linear_w8a16 -- Y[m, R_i + r] = sum_kb S_i[r/128, kb] * sum_{k in kb} x[m,k] * dec(W_i[r,k])
+ * with F32 activations (BF16 accepted and widened exactly) and F32
+ * accumulation; weights used as stored, no operand requantized.
+ * ("Qwen checkpoints with block FP8 weights", block-path and operator
+ *  paragraphs; "th#1803", section "What lands": the resident=False arm.)
+ *
+ * x : [M, K] F32 or BF16, leading dimension ldx (elements), 16-byte aligned
+ *     rows when K allows.
+ * y : [M, N] F32 or BF16 (RNE), leading dimension ldy (elements).
+ * workspace: device buffer of at least bsf8_workspace_size(w, W8A16, M) bytes
+ *     (may be NULL when that size is 0).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.
+ */
+bsf8_status bsf8_linear_w8a16(const bsf8_weight* w, const void* x, int32_t x_dtype, int64_t M, int64_t ldx,
+                              void* y, int32_t y_dtype, int64_t ldy,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsf8_linear_w8a8 -- for each 128-wide K slice kb:
+ *   P = sum_{k in kb} dec(xq[m,k]) * dec(W_i[r,k])   (products exact, F32 sum)
+ *   acc += P * (xs[m,kb] * S_i[r/128, kb])          (F32 epilogue)
+ * then Y[m, R_i + r] = acc rounded to y_dtype (F32, or BF16 with RNE).
+ * ("Module w8a8_prefill", section "WHY (#917 / #928)"; "FP8 Native Serving",
+ *  section "Native FP8 vs dequant-to-BF16": FP8 operands through the matrix
+ *  unit, BF16 only when results are written back.)
+ *
+ * xq, xs: exactly what bsf8_quant_act writes (ldq bytes, ldxs elements).
+ * y : [M, N] BF16 or F32, leading dimension ldy (elements).
+ * workspace: as for bsf8_linear_w8a16 with arm W8A8.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.
+ */
+bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs,
+                             int64_t ldxs, int64_t M, void* y, int32_t y_dtype, int64_t ldy,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsf8_describe -- one line naming the arithmetic and kernel configuration a
+ * call with this handle, arm and M would run, with the handle's geometry.
+ * ("Qwen checkpoints with block FP8 weights", block-path paragraph: report the
+ *  compute path next to the checkpoint identity; "Module w8a8_prefill",
+ *  section "ACCURACY": make visible which arithmetic ran.)
+ * Returns a pointer to thread-local storage valid until the next call on the
+ * same thread; NULL only for a NULL handle.
+ */
+const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSF8_H */

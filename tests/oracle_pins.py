@@ -285,6 +285,31 @@ def pin_brute_force(O):
     return True, ""
 
 
+def pin_sampled_rows(O):
+    """P9b: sampled-row helpers equal the corresponding columns of the full computation."""
+    x, members = tiny_case(seed=4, M=3, K=300, rows=(130, 7, 129))
+    rows = [0, 1, 127, 128, 129, 130, 136, 137, 200, 265]
+    # (BLAS may sum in another order for a sub-matrix, hence 1e-13 and not bit equality)
+    close = lambda a, b: np.allclose(a, b, rtol=1e-13, atol=0)
+    y = O.linear_w8a16(x, members)
+    if not close(O.linear_w8a16_rows(x, members, rows), y[:, rows]):
+        return False, "w8a16 rows"
+    if not np.array_equal(O.dequantize_rows(members, rows), O.dequantize_members(members)[rows]):
+        return False, "dequantized rows"
+    xq, xs = O.quant_act(x)
+    y8 = O.linear_w8a8(xq, xs, members)
+    if not close(O.linear_w8a8_rows(xq, xs, members, rows), y8[:, rows]):
+        return False, "w8a8 rows"
+    if not close(O.abs_bound_w8a8_rows(xq, xs, members, rows), O.abs_bound_w8a8(xq, xs, members)[:, rows]):
+        return False, "bound rows"
+    try:
+        O.dequantize_rows(members, [266])
+        return False, "row past the end accepted"
+    except IndexError:
+        pass
+    return True, ""
+
+
 def pin_int_partials(O, seed=9):
     """P10: float64 block sums of code products equal the exact integer sums."""
     g = np.random.default_rng(seed)

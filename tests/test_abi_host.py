@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+* the library loads and exports every function include/bsf8.h declares;
+* the C++ validator returns the oracle's status on every validator case;
+* handles over placeholder addresses report the geometry and the member-local
+  scale rows the oracle derives;
+* argument errors are refused before any launch, and M == 0 is a no-op.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_linear_amd as B
+import oracle as O
+from test_oracle_validate import to_oracle
+from validator_cases import CASES
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "bsf8.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsf8_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = B.lib()
+    names = header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == {e[0] for e in B.EXPORTS}
+
+
+def test_abi_version_and_status_names():
+    L = B.lib()
+    assert L.bsf8_abi_version() == 1
+    want = ["OK", "INVALID_ARG", "GROUP", "DECL", "WEIGHT_E5M2", "WEIGHT_DTYPE", "WEIGHT_RANK", "WEIGHT_EMPTY",
+            "SCALE_MISSING", "SCALE_AMBIGUOUS", "SCALE_ROWWISE", "SCALE_PER_TENSOR", "SCALE_RANK", "SCALE_DTYPE",
+            "SCALE_TRANSPOSED", "SCALE_GRID", "ALIGNMENT", "UNSUPPORTED", "WORKSPACE", "DEVICE"]
+    assert [B.status_name(i) for i in range(len(want))] == want
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_validator_matches_oracle(case):
+    _, qm, block, members, want = case
+    assert B.validate(qm, block, members) == want
+    assert O.validate(qm, block, to_oracle(members)) == want
+
+
+def _handle(rows, K, sdt="BF16", base=1 << 40):
+    members, addr = [], base
+    for r in rows:
+        nb, kb = O.scale_grid_shape(r, K)
+        members.append(dict(weight=dict(dtype="F8_E4M3", shape=(r, K), addr=addr),
+                            scale_inv=dict(dtype=sdt, shape=(nb, kb), addr=addr + (1 << 32))))
+        addr += 1 << 33
+    decl = B._decl()
+    arr, keep = B._members_array(members)
+    h = ctypes.c_void_p()
+    st = B.lib().bsf8_weight_create(ctypes.byref(decl), arr, len(members), ctypes.byref(h))
+    return st, h
+
+
+def test_handle_geometry_and_member_local_rows():
+    rows = [6144, 1000, 1000]
+    st, h = _handle(rows, 5120)
+    assert st == 0
+    L = B.lib()
+    try:
+        n, k, nm = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        assert L.bsf8_weight_geometry(h, ctypes.byref(n), ctypes.byref(k), ctypes.byref(nm)) == 0
+        assert (n.value, k.value, nm.value) == (8144, 5120, 3)
+        R, Bo = O.member_table(rows)
+        for row in [0, 127, 128, 6143, 6144, 7143, 7144, 7167, 7271, 7272, 8143]:
+            mi, lr, sr = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+            assert L.bsf8_weight_scale_row(h, row, ctypes.byref(mi), ctypes.byref(lr), ctypes.byref(sr)) == 0
+            assert sr.value == O.stacked_scale_row(row, rows)
+            assert lr.value == (row - R[mi.value]) // 128
+        # V's first row sits on stacked scale row 56, where a global n/128 grid would say 55
+        mi, lr, sr = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+        L.bsf8_weight_scale_row(h, 7144, ctypes.byref(mi), ctypes.byref(lr), ctypes.byref(sr))
+        assert (mi.value, lr.value, sr.value) == (2, 0, 56) and 7144 // 128 == 55
+        assert L.bsf8_weight_scale_row(h, 8144, ctypes.byref(mi), ctypes.byref(lr), ctypes.byref(sr)) == 1
+        d = L.bsf8_describe(h, 0, 1).decode()
+        assert "w8a16" in d and "K=5120" in d and "members=3" in d
+        d = L.bsf8_describe(h, 1, 512).decode()
+        assert "w8a8" in d and "e4m3" in d
+    finally:
+        L.bsf8_weight_destroy(h)
+
+
+def test_workspace_sizes():
+    L = B.lib()
+    st, h = _handle([5120], 5120)
+    assert st == 0
+    try:
+        b = ctypes.c_size_t()
+        assert L.bsf8_workspace_size(h, 0, 8, ctypes.byref(b)) == 0 and b.value > 0
+        assert L.bsf8_workspace_size(h, 0, 0, ctypes.byref(b)) == 0 and b.value == 0
+        assert L.bsf8_workspace_size(h, 1, 1024, ctypes.byref(b)) == 0
+        assert L.bsf8_workspace_size(h, 7, 8, ctypes.byref(b)) == 1
+    finally:
+        L.bsf8_weight_destroy(h)
+
+
+def test_compute_calls_refuse_bad_arguments_without_launching():
+    L = B.lib()
+    st, h = _handle([128], 256)
+    assert st == 0
+    try:
+        fake = ctypes.c_void_p(1 << 40)
+        # M == 0: success, nothing launched
+        assert L.bsf8_linear_w8a16(h, fake, B.DT_F32, 0, 256, fake, B.DT_F32, 128, None, 0, None) == 0
+        assert L.bsf8_linear_w8a8(h, fake, 256, fake, 2, 0, fake, B.DT_BF16, 128, None, 0, None) == 0
+        assert L.bsf8_quant_act(fake, B.DT_F32, 0, 256, 256, fake, 256, fake, 2, None) == 0
+        # refusals
+        assert B.status_name(L.bsf8_linear_w8a16(h, fake, B.DT_F32, -1, 256, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_linear_w8a16(h, fake, B.DT_F16, 4, 256, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_linear_w8a16(h, fake, B.DT_F32, 4, 255, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_linear_w8a16(h, fake, B.DT_F32, 4, 256, fake, B.DT_F32, 128, None, 0, None)) == "WORKSPACE"
+        assert B.status_name(L.bsf8_linear_w8a8(h, fake, 256, fake, 1, 4, fake, B.DT_BF16, 128, None, 0, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_linear_w8a8(h, None, 256, fake, 2, 4, fake, B.DT_BF16, 128, None, 0, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_quant_act(fake, B.DT_F32, 4, 256, 100, fake, 256, fake, 2, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_quant_act(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 4, 256, 256, fake, 256, fake, 2, None)) == "ALIGNMENT"
+        assert B.status_name(L.bsf8_linear_w8a16(None, fake, B.DT_F32, 4, 256, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
+        assert "INVALID_ARG" in L.bsf8_last_error().decode()
+    finally:
+        L.bsf8_weight_destroy(h)
+
+
+def test_create_needs_device_addresses():
+    members = [dict(weight=dict(dtype="F8_E4M3", shape=(128, 256)), scale_inv=dict(dtype="BF16", shape=(1, 2)))]
+    decl = B._decl()
+    arr, keep = B._members_array(members)
+    h = ctypes.c_void_p()
+    assert B.status_name(B.lib().bsf8_weight_create(ctypes.byref(decl), arr, 1, ctypes.byref(h))) == "INVALID_ARG"
+    assert not h.value
