@@ -38,7 +38,8 @@ __all__ = [
     "e4m3_table", "e4m3_decode", "e4m3_encode", "e4m3_encode_scalar",
     "bf16_bits_to_f32", "f32_to_bf16_bits", "f32_to_bf16",
     "scale_grid_shape", "member_table", "stacked_scale_row",
-    "dequantize_block_scaled", "dequantize_members",
+    "dequantize_block_scaled", "dequantize_members", "dequantize_rows",
+    "linear_w8a16_rows", "linear_w8a8_rows", "abs_bound_w8a16_rows", "abs_bound_w8a8_rows",
     "linear_w8a16", "quant_act", "dequantize_act", "linear_w8a8",
     "linear_w8a16_loops", "linear_w8a8_loops", "w8a8_block_partial_int",
     "abs_bound_w8a16", "abs_bound_w8a8", "round_output", "within_bound",
@@ -222,6 +223,27 @@ def dequantize_members(members: Iterable[Tuple[np.ndarray, np.ndarray]]) -> np.n
     return np.concatenate([dequantize_block_scaled(c, s) for c, s in members], axis=0)
 
 
+def dequantize_rows(members: Sequence[Tuple[np.ndarray, np.ndarray]], rows: Sequence[int]) -> np.ndarray:
+    """Dequantized weight rows for global output indices ``rows`` (float64 [len(rows), K]).
+
+    Row n belongs to the member i with R_i <= n < R_i + N_i and uses row
+    (n - R_i) // 128 of that member's own grid (member-local origin).
+    """
+    sizes = [c.shape[0] for c, _ in members]
+    R, _ = member_table(sizes)
+    K = members[0][0].shape[1]
+    kcol = np.arange(K) // BLOCK
+    out = np.empty((len(rows), K), np.float64)
+    for j, n in enumerate(rows):
+        i = max(ii for ii in range(len(sizes)) if R[ii] <= n)
+        r = int(n) - R[i]
+        if r >= sizes[i]:
+            raise IndexError(n)
+        codes, scale = members[i]
+        out[j] = e4m3_decode(codes[r]) * np.asarray(scale, np.float32)[r // BLOCK].astype(np.float64)[kcol]
+    return out
+
+
 # ------------------------------------------------------------------ W8A16/F32
 
 def linear_w8a16(x: np.ndarray, members: Sequence[Tuple[np.ndarray, np.ndarray]]) -> np.ndarray:
@@ -288,6 +310,24 @@ def linear_w8a8(xq: np.ndarray, xs: np.ndarray,
     epilogue.  Exactly, that sum is sum_kb sa*sw*sum_k dec(a)dec(w) = A . Wd^T.
     """
     return dequantize_act(xq, xs) @ dequantize_members(members).T
+
+
+def linear_w8a16_rows(x, members, rows) -> np.ndarray:
+    """Columns ``rows`` of ``linear_w8a16`` (float64 [M, len(rows)])."""
+    return np.asarray(x, np.float32).astype(np.float64) @ dequantize_rows(members, rows).T
+
+
+def linear_w8a8_rows(xq, xs, members, rows) -> np.ndarray:
+    """Columns ``rows`` of ``linear_w8a8`` (float64 [M, len(rows)])."""
+    return dequantize_act(xq, xs) @ dequantize_rows(members, rows).T
+
+
+def abs_bound_w8a16_rows(x, members, rows) -> np.ndarray:
+    return np.abs(np.asarray(x, np.float32).astype(np.float64)) @ np.abs(dequantize_rows(members, rows)).T
+
+
+def abs_bound_w8a8_rows(xq, xs, members, rows) -> np.ndarray:
+    return np.abs(dequantize_act(xq, xs)) @ np.abs(dequantize_rows(members, rows)).T
 
 
 # ---------------------------------------------- brute force (tiny inputs only)
