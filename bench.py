@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Throughput of the block-scaled FP8 linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu] [--copy-calibration]
+
+One step is the dense-FFN prefill pass on M = 1024 synthetic tokens:
+quantize X_gate_up -> W8A8 GEMM on the fused gate/up weight (two members of
+[17408, 5120]) -> quantize X_down -> W8A8 GEMM on the down weight
+[5120, 17408], BF16 outputs.  ``value`` is the step's algorithmic FLOP rate,
+2*M*N*K summed over both GEMMs, over the step time (quantization included).
+
+The same JSON line also carries:
+* ``roofline``: the gate/up GEMM, FLOPs per launch over its mean launch time
+  (HIP events on the launching stream), against the dense FP8 MFMA peak;
+* ``decode_gemv``: the W8A16/F32 arm at M in {1, 4, 8} on W [5120, 5120],
+  rotating through >= 512 MiB of weight copies so the 256 MB Infinity Cache
+  cannot serve them, with an HBM roofline on algorithmic bytes;
+* ``large_prefill``: the W8A8 GEMM at M=8192, K=7168, N=18432;
+* ``cpu_baseline``: the oracle (NumPy) on the host cores, on a bounded sample of
+  the same prefill workload.
+
+Inputs are seeded synthetic data (``synth``) already resident in HBM before
+timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+ROTATE_BYTES = 640 << 20     # > 512 MiB of distinct weight copies for the GEMV
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-cpu", action="store_true", help="leave out the oracle's CPU baseline")
+    ap.add_argument("--skip-extra", action="store_true", help="leave out the decode and large-prefill lines")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+class KernelTimer:
+    """Mean duration of each named launch, from HIP event pairs on the current stream.
+
+    With ``pad`` the launch is preceded by a device-side spin, so the host has
+    queued the start event, the kernel and the stop event before the GPU gets to
+    them: the pair then brackets the kernel alone, not the host's launch latency
+    (which exceeds a few-microsecond kernel).
+    """
+
+    def __init__(self, torch, pad_cycles=0):
+        self.t = torch
+        self.pad = pad_cycles
+        self.pairs = {}
+
+    def run(self, name, fn):
+        if self.pad:
+            self.t.cuda._sleep(self.pad)
+        s = self.t.cuda.Event(enable_timing=True)
+        e = self.t.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return out
+
+    def mean_ms(self, name):
+        ps = self.pairs.get(name, [])
+        return float(np.mean([s.elapsed_time(e) for s, e in ps])) if ps else float("nan")
+
+    def reset(self):
+        self.pairs = {}
+
+
+def to_device_member(torch, m, dev):
+    w = torch.from_numpy(np.ascontiguousarray(m.codes)).to(dev)
+    s = torch.from_numpy(np.ascontiguousarray(m.scale_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    return w, s
+
+
+def bench_prefill(torch, B, synth, steps, warmup, dev):
+    log("prefill: generating dense-FFN inputs (M=1024)")
+    gu = synth.config3_gate_up()
+    dn = synth.config3_down()
+    w_gu = B.BlockFP8Weight([to_device_member(torch, m, dev) for m in gu.members])
+    w_dn = B.BlockFP8Weight([to_device_member(torch, m, dev) for m in dn.members])
+    x_gu = torch.from_numpy(gu.x).to(dev)
+    x_dn = torch.from_numpy(dn.x).to(dev)
+    M = gu.x.shape[0]
+    y_gu = torch.empty((M, w_gu.n_total), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((M, w_dn.n_total), dtype=torch.bfloat16, device=dev)
+    xq_gu = torch.empty((M, w_gu.K), dtype=torch.uint8, device=dev)
+    xs_gu = torch.empty((M, -(-w_gu.K // 128)), dtype=torch.float32, device=dev)
+    xq_dn = torch.empty((M, w_dn.K), dtype=torch.uint8, device=dev)
+    xs_dn = torch.empty((M, -(-w_dn.K // 128)), dtype=torch.float32, device=dev)
+    kt = KernelTimer(torch)
+
+    def step():
+        kt.run("quant_gate_up", lambda: B.quant_act(x_gu, xq_gu, xs_gu))
+        kt.run("gemm_gate_up", lambda: B.linear_w8a8(w_gu, xq_gu, xs_gu, out=y_gu))
+        kt.run("quant_down", lambda: B.quant_act(x_dn, xq_dn, xs_dn))
+        kt.run("gemm_down", lambda: B.linear_w8a8(w_dn, xq_dn, xs_dn, out=y_dn))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    kt.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / steps
+    flop_gu = 2.0 * M * w_gu.n_total * w_gu.K
+    flop_dn = 2.0 * M * w_dn.n_total * w_dn.K
+    kms = {k: kt.mean_ms(k) for k in ("quant_gate_up", "gemm_gate_up", "quant_down", "gemm_down")}
+    res = dict(
+        ms_per_step=ms_step, wall_s=wall, flop_per_step=flop_gu + flop_dn,
+        tflops=(flop_gu + flop_dn) / (ms_step * 1e-3) / 1e12,
+        kernels_ms=kms,
+        gemm_gate_up_tflops=flop_gu / (kms["gemm_gate_up"] * 1e-3) / 1e12,
+        gemm_down_tflops=flop_dn / (kms["gemm_down"] * 1e-3) / 1e12,
+        quant_gate_up_gbs=(M * w_gu.K * 5 + M * (-(-w_gu.K // 128)) * 4) / (kms["quant_gate_up"] * 1e-3) / 1e9,
+        quant_down_gbs=(M * w_dn.K * 5 + M * (-(-w_dn.K // 128)) * 4) / (kms["quant_down"] * 1e-3) / 1e9,
+        flop_gate_up=flop_gu, M=M,
+        describe_gate_up=w_gu.describe(B.ARM_W8A8, M), describe_down=w_dn.describe(B.ARM_W8A8, M),
+        fixture_sha256=synth.sha256_of(*(m.codes for m in gu.members), gu.x),
+    )
+    del w_gu, w_dn
+    return res
+
+
+def bench_decode(torch, B, synth, steps, dev):
+    out = {}
+    N = K = 5120
+    base = synth.config2(8)
+    m = base.members[0]
+    per_copy = m.codes.nbytes + m.scale_bits.nbytes
+    copies = max(2, -(-ROTATE_BYTES // per_copy))
+    log(f"decode: {copies} weight copies of {per_copy / 2**20:.1f} MiB")
+    w0, s0 = to_device_member(torch, m, dev)
+    handles = []
+    for _ in range(copies):
+        handles.append(B.BlockFP8Weight([(w0.clone(), s0.clone())]))
+    Kb = -(-K // 128)
+    for M in (1, 4, 8):
+        x = torch.from_numpy(base.x[:M].copy()).to(dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = [h.workspace(B.ARM_W8A16, M) for h in handles]
+        for i in range(copies):
+            B.linear_w8a16(handles[i], x, out=y, workspace=ws[i])
+        torch.cuda.synchronize()
+        # One graph holds `copies` back-to-back launches, each on another weight
+        # copy; replays are bracketed by events, so the per-launch time is the
+        # device's own launch-to-launch time (host launch latency would
+        # otherwise exceed these few-microsecond kernels).
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(copies):
+                B.linear_w8a16(handles[i], x, out=y, workspace=ws[i])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(4, steps)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * copies)
+        alg_bytes = N * K + 2 * (N // 128) * Kb + 4 * M * K + 4 * M * N
+        out[f"M{M}"] = dict(us=ms * 1e3, gbs=alg_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=alg_bytes,
+                            describe=handles[0].describe(B.ARM_W8A16, M))
+        del g
+    del handles
+    return out
+
+
+def bench_large(torch, B, synth, steps, dev):
+    log("large prefill: generating M=8192, K=7168, N=18432")
+    wl = synth.config5()
+    w = B.BlockFP8Weight([to_device_member(torch, m, dev) for m in wl.members])
+    x = torch.from_numpy(wl.x).to(dev)
+    M = wl.x.shape[0]
+    xq, xs = B.quant_act(x)
+    y = torch.empty((M, w.n_total), dtype=torch.bfloat16, device=dev)
+    kt = KernelTimer(torch)
+    for _ in range(2):
+        B.linear_w8a8(w, xq, xs, out=y)
+    torch.cuda.synchronize()
+    for _ in range(max(3, steps // 2)):
+        kt.run("gemm", lambda: B.linear_w8a8(w, xq, xs, out=y))
+        kt.run("quant", lambda: B.quant_act(x, xq, xs))
+    torch.cuda.synchronize()
+    flop = 2.0 * M * w.n_total * w.K
+    ms = kt.mean_ms("gemm")
+    return dict(gemm_us=ms * 1e3, tflops=flop / (ms * 1e-3) / 1e12, frac=flop / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+                quant_us=kt.mean_ms("quant") * 1e3, describe=w.describe(B.ARM_W8A8, M))
+
+
+def copy_calibration(torch, dev):
+    """A plain device copy of 1 GiB, run a few times, so an HBM counter run can scale FETCH/WRITE_SIZE."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return dict(bytes_read_per_copy=n, bytes_written_per_copy=n, copies=3)
+
+
+def cpu_baseline(synth, budget_s=12.0):
+    """The oracle on the host cores: quantization + W8A8 GEMM of the prefill gate/up step on a row sample."""
+    import oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    gu = synth.config3_gate_up()
+    members = [(m.codes, m.scale_f32()) for m in gu.members]
+    t0 = time.perf_counter()
+    xq, xs = O.quant_act(gu.x)
+    t_quant = time.perf_counter() - t0
+    rows_total = sum(m.codes.shape[0] for m in gu.members)
+    done = 0
+    t1 = time.perf_counter()
+    chunk = 1024
+    while done < rows_total and time.perf_counter() - t1 < budget_s:
+        rows = list(range(done, min(rows_total, done + chunk)))
+        O.linear_w8a8_rows(xq, xs, members, rows)
+        done += len(rows)
+    t_gemm = time.perf_counter() - t1
+    M, K = gu.x.shape
+    flop = 2.0 * M * done * K
+    # scale the sampled rows to the whole step of this GEMM: time = quant + gemm(rows) * total/rows
+    t_full = t_quant + t_gemm * rows_total / done
+    return {"value": 2.0 * M * rows_total * K / t_full / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"gate/up W8A8 of the M=1024 prefill: full activation quantization ({t_quant:.1f} s) + "
+                      f"{done} of {rows_total} output rows in float64 NumPy ({t_gemm:.1f} s, {flop / 1e9:.0f} GFLOP), "
+                      f"scaled to all rows"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported"}))
+        sys.exit(2)
+    import torch
+    import block_scaled_fp8_linear_amd as B
+    import synth
+    B.lib()  # fail loudly when the HIP library is missing: there is no CPU path
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
+
+    pre = bench_prefill(torch, B, synth, a.steps, a.warmup, dev)
+    log(f"prefill {pre['tflops']:.1f} TFLOP/s/step, kernels {pre['kernels_ms']}")
+    extra = {}
+    if not a.skip_extra:
+        extra["decode_gemv"] = bench_decode(torch, B, synth, a.steps, dev)
+        log(f"decode {extra['decode_gemv']}")
+        torch.cuda.empty_cache()
+        extra["large_prefill"] = bench_large(torch, B, synth, a.steps, dev)
+        log(f"large {extra['large_prefill']}")
+    if a.copy_calibration:
+        extra["copy_calibration"] = copy_calibration(torch, dev)
+    cpu = None if a.skip_cpu else cpu_baseline(synth)
+
+    gu_ms = pre["kernels_ms"]["gemm_gate_up"]
+    achieved = pre["flop_gate_up"] / (gu_ms * 1e-3) / 1e12
+    line = {
+        "metric": "W8A8 block-FP8 prefill GEMM TFLOP/s (% FP8 MFMA peak); decode GEMV HBM GB/s",
+        "value": round(pre["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": "dense_ffn_prefill: quant + W8A8 gate/up [2x17408,5120] + quant + W8A8 down "
+                               "[5120,17408], M=1024 tokens, bf16 out",
+                   "M": pre["M"], "global_batch": pre["M"], "parallelism": "single_gpu"},
+        "roofline": {"bound": "mfma", "kernel": "w8a8_gemm (gate/up)", "achieved": round(achieved, 2),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "kernels_ms": {k: round(v, 5) for k, v in pre["kernels_ms"].items()},
+        "gemm_down_tflops": round(pre["gemm_down_tflops"], 2),
+        "quant_gbs": {"gate_up": round(pre["quant_gate_up_gbs"], 1), "down": round(pre["quant_down_gbs"], 1)},
+        "path": {"gate_up": pre["describe_gate_up"], "down": pre["describe_down"]},
+        "fixture_sha256": pre["fixture_sha256"],
+    }
+    if "decode_gemv" in extra:
+        d = extra["decode_gemv"]
+        line["decode_gemv"] = {
+            "workload": "W8A16/F32 decode GEMV, W [5120,5120] + bf16 grid [40,40], f32 x/y, rotating "
+                        f">= {ROTATE_BYTES >> 20} MiB of weight copies",
+            "unit": "GB/s", "by_M": {k: round(v["gbs"], 1) for k, v in d.items()},
+            "us_by_M": {k: round(v["us"], 2) for k, v in d.items()},
+            "roofline": {"bound": "hbm", "kernel": "w8a16 (M=8)", "achieved": round(d["M8"]["gbs"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d["M8"]["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": None},
+            "path": d["M8"]["describe"],
+        }
+    if "large_prefill" in extra:
+        l = extra["large_prefill"]
+        line["large_prefill"] = {"workload": "W8A8 GEMM M=8192 K=7168 N=18432, bf16 out",
+                                 "tflops": round(l["tflops"], 2), "frac": round(l["frac"], 4),
+                                 "gemm_us": round(l["gemm_us"], 1), "quant_us": round(l["quant_us"], 1),
+                                 "path": l["describe"]}
+    if "copy_calibration" in extra:
+        line["copy_calibration"] = extra["copy_calibration"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,20 +20,20 @@
 //  accumulation, as the pages state, at about three BF16 MFMAs per 16x16x32 step.
 //  (Inputs below ~2^-100 in magnitude may lose their lowest remainder bits.)
 //
-// Work decomposition:
-//  * A block (8 waves) owns one 128-row group of one member (exactly one row of
-//    that member's scale grid, so the weight scale is a block-uniform scalar per
-//    128-wide K chunk), 16 tokens, and a range of K chunks.
-//  * Per chunk, the block splits its 16x128 activation slice once into LDS
-//    (shared by all 8 waves); each wave streams its own 16 weight rows x 128
-//    bytes straight from HBM into registers (two 16-byte loads per lane),
-//    converts them and issues 12 MFMAs (4 K-steps x 3 terms); the chunk partial
-//    is scaled by the block's weight scale into the F32 accumulator.
-//  * Decode shapes have too few 128-row groups to fill 256 CUs, so K is split
-//    across blocks.  Each block writes its partial tile to the workspace; the
-//    last block to arrive (device-scope counter) adds the partials in split
-//    order and stores Y, so the result does not depend on arrival order, and
-//    resets the counter to zero for the next call.
+// Work decomposition (no inter-block traffic):
+//  * A block owns 32 consecutive rows of one member (two 16-row MFMA tiles,
+//    member-local, so each tile lies in one row of that member's scale grid
+//    and its weight scale is one scalar per 128-wide K chunk), up to 16 tokens,
+//    and all of K.  Its 8 waves split K: wave w takes a contiguous run of
+//    128-wide chunks.  Per chunk a lane loads its two 16-byte pieces of each of
+//    the two row tiles and 32 activations, splits the activations into three
+//    BF16 B fragments in registers (shared by both row tiles), converts the
+//    weights and issues 24 MFMAs; the chunk partial is scaled by the tile's
+//    weight scale into the F32 accumulator.  Loads run one chunk ahead.
+//  * The 8 per-wave partial tiles are added in LDS in wave order (a fixed
+//    order, so results are reproducible) and stored.
+//  * Decode shapes give about one block per CU (N = 8144 rows -> 256 blocks),
+//    and the weight stream is the only HBM traffic.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -41,42 +41,58 @@
 
 #include "bsf8_internal.h"
 
+// Raw buffer load of 16 bytes; an offset past the resource's size reads zeros.
+typedef int bsf8_w16_v4i __attribute__((ext_vector_type(4)));
+__device__ bsf8_w16_v4i bsf8_raw_buffer_load_b128(bsf8_w16_v4i rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+
 namespace bsf8 {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef bsf8_w16_v4i v4i;
+
+__device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32)));
+  r[2] = __builtin_amdgcn_readfirstlane(int(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint4 as_u4(v4i v) { return make_uint4(uint32_t(v[0]), uint32_t(v[1]), uint32_t(v[2]), uint32_t(v[3])); }
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
-constexpr int ROWS = 128;        // weight rows per block (one scale-grid row)
+constexpr int RT = 2;            // 16-row MFMA tiles per block (and per wave)
+constexpr int ROWS = 16 * RT;    // weight rows per block
 constexpr int COLS = 16;         // tokens per block
 constexpr int CHUNK = 128;       // K per chunk (one scale block)
 constexpr int TERMS = 3;
-constexpr int STEPS = CHUNK / 32;                        // MFMA K-steps per chunk
-constexpr int SPLIT_BYTES = TERMS * STEPS * 64 * 16;     // 12 KiB of BF16 fragments per chunk
-constexpr int TARGET_BLOCKS = 512;
+constexpr int STEPS = CHUNK / 32;  // MFMA K-steps per chunk
+constexpr int MAX_KB = 1024;       // K up to 131072 (scale row staged in LDS)
 
 struct Args {
   WeightDev w;
-  TileMap tm;          // row groups per member, tiles = groups x col tiles
+  TileMap tm;          // 32-row tiles per member; tiles = row tiles x token tiles
   const void* x;
   void* y;
-  float* partial;      // [tiles][splits][ROWS][COLS]
-  uint32_t* counter;   // [tiles]
   int64_t ldx;
   int64_t ldy;
   int32_t M;
   int32_t col_tiles;
-  int32_t splits;
-  int32_t chunks_per_split;
+  int32_t chunks_per_wave;
   int32_t x_bf16;
   int32_t y_bf16;
 };
 
-__device__ __forceinline__ float load_scale(const void* s, int64_t idx, int bf16) {
-  if (bf16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(s)[idx]) << 16);
+template <bool SBF16>
+__device__ __forceinline__ float load_scale(const void* s, int64_t idx) {
+  if (SBF16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(s)[idx]) << 16);
   return static_cast<const float*>(s)[idx];
 }
 
@@ -86,39 +102,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// K offset (within a chunk) of element j of K-step s held by lane group gq.
-// Both MFMA operands use this same map, so the dot product covers every k once.
-__device__ __forceinline__ int kmap(int s, int gq, int j) { return (s >> 1) * 64 + gq * 16 + (s & 1) * 8 + j; }
-
-// Four activations (k .. k+3 of one token) as F32; zeros past K or past M.
-template <bool ALIGNED>
-__device__ __forceinline__ void load_x4(const Args& a, int m, int k, int K, float v[4]) {
-  v[0] = v[1] = v[2] = v[3] = 0.f;
-  if (m >= a.M) return;
-  const int n = K - k;
-  if (n <= 0) return;
-  const int64_t off = int64_t(m) * a.ldx + k;
-  if (a.x_bf16) {
-    const uint16_t* p = static_cast<const uint16_t*>(a.x) + off;
-    if (ALIGNED && n >= 4) {
-      const uint2 u = *reinterpret_cast<const uint2*>(p);
-      v[0] = __uint_as_float(u.x << 16);
-      v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-      v[2] = __uint_as_float(u.y << 16);
-      v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    } else {
-      for (int j = 0; j < 4 && j < n; ++j) v[j] = __uint_as_float(uint32_t(p[j]) << 16);
-    }
-  } else {
-    const float* p = static_cast<const float*>(a.x) + off;
-    if (ALIGNED && n >= 4) {
-      const float4 u = *reinterpret_cast<const float4*>(p);
-      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-    } else {
-      for (int j = 0; j < 4 && j < n; ++j) v[j] = p[j];
-    }
-  }
-}
+// K offsets held by lane group gq within a 128-wide chunk: two runs of 16,
+// [16 gq, 16 gq + 16) and [64 + 16 gq, 64 + 16 gq + 16).  K-step s uses
+// elements (s >> 1) * 64 + 16 gq + (s & 1) * 8 + j, j < 8, on BOTH operands,
+// so every k is covered once whatever order the MFMA sums in.
 
 // 16 weight bytes of one row at K offset k; zeros past K or for a missing row.
 template <bool ALIGNED>
@@ -137,36 +124,66 @@ __device__ __forceinline__ uint4 load_w16(const uint8_t* row, int k, int K, bool
   return v;
 }
 
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
+// 16 activations of one token starting at K offset k, as F32; zeros past K or for a missing token.
+template <bool ALIGNED, bool bf16>
+__device__ __forceinline__ void load_x16(const void* x, int64_t off, int n, bool ok, float v[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = 0.f;
+  if (!ok || n <= 0) return;
+  if (ALIGNED && n < 16) return;   // K % 16 == 0: a 16-run is either whole or past K
+  if (bf16) {
+    const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+    if (ALIGNED) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 u = reinterpret_cast<const uint4*>(p)[q];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[q * 8 + 2 * h] = __uint_as_float(w[h] << 16);
+          v[q * 8 + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+        }
+      }
+    } else {
+      for (int j = 0; j < 16 && j < n; ++j) v[j] = __uint_as_float(uint32_t(p[j]) << 16);
+    }
+  } else {
+    const float* p = static_cast<const float*>(x) + off;
+    if (ALIGNED) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 u = reinterpret_cast<const float4*>(p)[q];
+        v[4 * q] = u.x; v[4 * q + 1] = u.y; v[4 * q + 2] = u.z; v[4 * q + 3] = u.w;
+      }
+    } else {
+      for (int j = 0; j < 16 && j < n; ++j) v[j] = p[j];
+    }
+  }
 }
 
-// Split 4 activations into three BF16 terms and store them into the fragment
-// layout: lane (token c, group gq) of K-step s owns 16 bytes at
-// ((t * STEPS + s) * 64 + gq * 16 + c) * 16.
-__device__ __forceinline__ void split_store(uint8_t* buf, int c, int k4, const float v[4]) {
-  uint32_t t0[4], t1[4], t2[4];
+// x = hi + mid + lo exactly, each a BF16 (top 16 bits of an F32); returns the
+// three terms of 8 activations packed as BF16 pairs.
+__device__ __forceinline__ void split8(const float* v, v8bf& t0, v8bf& t1, v8bf& t2) {
+  uint32_t h[8], m[8], l[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t xb = __float_as_uint(v[j]);
-    const uint32_t hb = xb & 0xFFFF0000u;
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t hb = __float_as_uint(v[j]) & 0xFFFF0000u;
     const float r1 = v[j] - __uint_as_float(hb);
     const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
-    const float r2 = r1 - __uint_as_float(mb);
-    t0[j] = hb;
-    t1[j] = mb;
-    t2[j] = __float_as_uint(r2);
+    h[j] = hb;
+    m[j] = mb;
+    l[j] = __float_as_uint(r1 - __uint_as_float(mb));
   }
-  const int s = ((k4 >> 6) << 1) | ((k4 >> 3) & 1);
-  const int gq = (k4 >> 4) & 3;
-  const int jbyte = (k4 & 7) * 2;  // 0 or 8
-  const int slot = (gq * 16 + c) * 16 + jbyte;
-  uint2 w0 = make_uint2(pack_hi16(t0[0], t0[1]), pack_hi16(t0[2], t0[3]));
-  uint2 w1 = make_uint2(pack_hi16(t1[0], t1[1]), pack_hi16(t1[2], t1[3]));
-  uint2 w2 = make_uint2(pack_hi16(t2[0], t2[1]), pack_hi16(t2[2], t2[3]));
-  *reinterpret_cast<uint2*>(buf + (0 * STEPS + s) * 1024 + slot) = w0;
-  *reinterpret_cast<uint2*>(buf + (1 * STEPS + s) * 1024 + slot) = w1;
-  *reinterpret_cast<uint2*>(buf + (2 * STEPS + s) * 1024 + slot) = w2;
+  uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    p0[q] = (h[2 * q] >> 16) | (h[2 * q + 1] & 0xFFFF0000u);
+    p1[q] = (m[2 * q] >> 16) | (m[2 * q + 1] & 0xFFFF0000u);
+    p2[q] = (l[2 * q] >> 16) | (l[2 * q + 1] & 0xFFFF0000u);
+  }
+  t0 = __builtin_bit_cast(v8bf, make_uint4(p0[0], p0[1], p0[2], p0[3]));
+  t1 = __builtin_bit_cast(v8bf, make_uint4(p1[0], p1[1], p1[2], p1[3]));
+  t2 = __builtin_bit_cast(v8bf, make_uint4(p2[0], p2[1], p2[2], p2[3]));
 }
 
 __device__ __forceinline__ v8bf cvt8(uint32_t lo, uint32_t hi) {
@@ -177,135 +194,163 @@ __device__ __forceinline__ v8bf cvt8(uint32_t lo, uint32_t hi) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <bool ALIGNED>
+template <bool ALIGNED, bool XBF16, bool SBF16>
 __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t xsplit[2][SPLIT_BYTES];
-  __shared__ int last_flag;
+  __shared__ __attribute__((aligned(16))) float red[WAVES][RT][64][4];
+  __shared__ float srow[MAX_KB];   // this block's row of the scale grid
 
-  // ---- block -> (member, row group, token tile, K split)
-  const int splits = a.splits;
-  const int bid = blockIdx.x;
-  const int ks = bid % splits;
-  const int tile = bid / splits;
+  // ---- block -> (member, 32-row tile, token tile)
+  const int tile = blockIdx.x;
   int mi = 0;
   while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
   const int local = tile - a.tm.tile0[mi];
-  const int rg = local % a.tm.n_tiles[mi];
+  const int rtile = local % a.tm.n_tiles[mi];
   const int ct = local / a.tm.n_tiles[mi];
   const MemberDev mem = a.w.m[mi];
   const int K = a.w.K, Kb = a.w.Kb;
-  const int c_begin = ks * a.chunks_per_split;
-  const int c_end = min(Kb, c_begin + a.chunks_per_split);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so the chunk loop is scalar
   const int l16 = lane & 15, gq = lane >> 4;
-
-  // splitter role: thread -> (token c, 4 consecutive k)
-  const int sc = tid >> 5;             // 0..15
-  const int sk4 = (tid & 31) * 4;      // 0..124
-  const int sm = ct * COLS + sc;
-
-  // weight role: wave -> 16 rows; lane -> row l16, two 16-byte pieces
-  const int row = rg * ROWS + wave * 16 + l16;
-  const bool row_ok = row < mem.rows;
-  const uint8_t* wrow = mem.w + int64_t(row_ok ? row : 0) * K;
-  const int64_t s_base = int64_t(rg) * Kb;
-
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-
-  float xv[4];
-  uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-  if (c_begin < c_end) {
-    load_x4<ALIGNED>(a, sm, c_begin * CHUNK + sk4, K, xv);
-    w0 = load_w16<ALIGNED>(wrow, c_begin * CHUNK + gq * 16, K, row_ok);
-    w1 = load_w16<ALIGNED>(wrow, c_begin * CHUNK + 64 + gq * 16, K, row_ok);
+  // Both 16-row tiles of a 32-row block lie in the same 128-row block, so the
+  // block uses one row of the member's scale grid: stage it in LDS once.
+  {
+    const int64_t sr = int64_t((rtile * ROWS) >> 7) * Kb;
+    for (int i = tid; i < Kb; i += THREADS) srow[i] = load_scale<SBF16>(mem.s, sr + i);
   }
-  for (int c = c_begin; c < c_end; ++c) {
-    uint8_t* buf = xsplit[c & 1];
-    split_store(buf, sc, sk4, xv);
-    const bool more = c + 1 < c_end;
-    if (more) load_x4<ALIGNED>(a, sm, (c + 1) * CHUNK + sk4, K, xv);
-    __syncthreads();
-    const uint4 p0 = w0, p1 = w1;
-    if (more) {
-      w0 = load_w16<ALIGNED>(wrow, (c + 1) * CHUNK + gq * 16, K, row_ok);
-      w1 = load_w16<ALIGNED>(wrow, (c + 1) * CHUNK + 64 + gq * 16, K, row_ok);
-    }
-    const float sw = load_scale(mem.s, s_base + c, a.w.scale_bf16);
-    const v8bf af[STEPS] = {cvt8(p0.x, p0.y), cvt8(p0.z, p0.w), cvt8(p1.x, p1.y), cvt8(p1.z, p1.w)};
-    v4f pt[TERMS];
-#pragma unroll
-    for (int t = 0; t < TERMS; ++t) pt[t] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-#pragma unroll
-      for (int t = 0; t < TERMS; ++t) {
-        const v8bf bfr = *reinterpret_cast<const v8bf*>(buf + ((t * STEPS + s) * 64 + lane) * 16);
-        pt[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bfr, pt[t], 0, 0, 0);
-      }
-    }
-    acc += (pt[0] + pt[1] + pt[2]) * sw;
-  }
+  __syncthreads();
+  const int c_begin = min(Kb, wave * a.chunks_per_wave);
+  const int c_end = min(Kb, c_begin + a.chunks_per_wave);
 
-  // ---- output: lane holds rows 4*gq + r of the wave's 16, token l16
-  const int out_row0 = rg * ROWS + wave * 16 + 4 * gq;   // member-local
+  // weight rows of this lane in the two row tiles, and their scale rows
+  // (A lane's weight row l16 and the outputs it accumulates, rows 4*gq + r for
+  // token l16, are different things; the scale belongs to the whole block.)
+  const uint8_t* wrow[RT];
+  bool row_ok[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int r0 = rtile * ROWS + t * 16;
+    row_ok[t] = r0 + l16 < mem.rows;
+    wrow[t] = mem.w + int64_t(row_ok[t] ? r0 + l16 : 0) * K;
+  }
+  // activations of this lane's token
   const int m = ct * COLS + l16;
-  auto store_y = [&](const v4f& v) {
-    if (m >= a.M) return;
-    const int nvalid = mem.rows - out_row0;
-    if (nvalid <= 0) return;
-    const int64_t off = int64_t(m) * a.ldy + mem.col0 + out_row0;
-    if (a.y_bf16) {
-      uint16_t* y = static_cast<uint16_t*>(a.y) + off;
-      for (int r = 0; r < 4 && r < nvalid; ++r) y[r] = f32_to_bf16_rne(v[r]);
+  const bool m_ok = m < a.M;
+  const int64_t x_base = int64_t(m_ok ? m : 0) * a.ldx;
+
+  v4f acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wv[RT][2];
+  float xv[2][16];
+  // Aligned path: buffer loads whose out-of-range offsets (missing rows, tokens
+  // past M, K past the end) read zeros, so no load sits behind a branch and the
+  // compiler can count the one-chunk-ahead prefetch instead of draining it.
+  const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
+  const uint32_t x_esz = XBF16 ? 2u : 4u;
+  const uint32_t x_bytes = uint32_t(a.M) * uint32_t(a.ldx) * x_esz;
+  const v4i rw = make_rsrc(mem.w, w_bytes);
+  const v4i rx = make_rsrc(a.x, x_bytes);
+  auto load_chunk = [&](int c) {
+    const int k0 = c * CHUNK + gq * 16, k1 = k0 + 64;
+    if (ALIGNED) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int rb = (rtile * ROWS + t * 16 + l16) * K;
+        wv[t][0] = as_u4(bsf8_raw_buffer_load_b128(rw, (row_ok[t] && k0 < K) ? rb + k0 : int(w_bytes), 0, 0));
+        wv[t][1] = as_u4(bsf8_raw_buffer_load_b128(rw, (row_ok[t] && k1 < K) ? rb + k1 : int(w_bytes), 0, 0));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = h ? k1 : k0;
+        const int xo = int((x_base + kk) * x_esz);
+        const bool ok = m_ok && kk < K;
+        if (XBF16) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint4 u = as_u4(bsf8_raw_buffer_load_b128(rx, ok ? xo + 16 * q : int(x_bytes), 0, 0));
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              xv[h][q * 8 + 2 * e] = __uint_as_float(w4[e] << 16);
+              xv[h][q * 8 + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 u = as_u4(bsf8_raw_buffer_load_b128(rx, ok ? xo + 16 * q : int(x_bytes), 0, 0));
+            xv[h][4 * q] = __uint_as_float(u.x);
+            xv[h][4 * q + 1] = __uint_as_float(u.y);
+            xv[h][4 * q + 2] = __uint_as_float(u.z);
+            xv[h][4 * q + 3] = __uint_as_float(u.w);
+          }
+        }
+      }
     } else {
-      float* y = static_cast<float*>(a.y) + off;
-      if (nvalid >= 4 && (reinterpret_cast<uintptr_t>(y) & 15) == 0)
-        *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
-      else
-        for (int r = 0; r < 4 && r < nvalid; ++r) y[r] = v[r];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        wv[t][0] = load_w16<ALIGNED>(wrow[t], k0, K, row_ok[t]);
+        wv[t][1] = load_w16<ALIGNED>(wrow[t], k1, K, row_ok[t]);
+      }
+      load_x16<ALIGNED, XBF16>(a.x, x_base + k0, K - k0, m_ok, xv[0]);
+      load_x16<ALIGNED, XBF16>(a.x, x_base + k1, K - k1, m_ok, xv[1]);
     }
   };
 
-  if (splits == 1) {
-    store_y(acc);
-    return;
+  if (c_begin < c_end) load_chunk(c_begin);
+  for (int c = c_begin; c < c_end; ++c) {
+    uint4 cw[RT][2];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) { cw[t][0] = wv[t][0]; cw[t][1] = wv[t][1]; }
+    const float sw = srow[c];
+    v8bf b[TERMS][STEPS];
+    split8(&xv[0][0], b[0][0], b[1][0], b[2][0]);
+    split8(&xv[0][8], b[0][1], b[1][1], b[2][1]);
+    split8(&xv[1][0], b[0][2], b[1][2], b[2][2]);
+    split8(&xv[1][8], b[0][3], b[1][3], b[2][3]);
+    if (c + 1 < c_end) load_chunk(c + 1);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const v8bf af[STEPS] = {cvt8(cw[t][0].x, cw[t][0].y), cvt8(cw[t][0].z, cw[t][0].w),
+                              cvt8(cw[t][1].x, cw[t][1].y), cvt8(cw[t][1].z, cw[t][1].w)};
+      v4f pt[TERMS];
+#pragma unroll
+      for (int u = 0; u < TERMS; ++u) pt[u] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+        for (int u = 0; u < TERMS; ++u) pt[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], b[u][s], pt[u], 0, 0, 0);
+      acc[t] += (pt[0] + pt[1] + pt[2]) * sw;
+    }
   }
 
-  // ---- split-K: publish the partial, the last block to arrive reduces in order
-  float* part = a.partial + (int64_t(tile) * splits + ks) * (ROWS * COLS);
+  // ---- add the 8 waves' partial tiles in wave order and store
 #pragma unroll
-  for (int r = 0; r < 4; ++r) part[(wave * 16 + 4 * gq + r) * COLS + l16] = acc[r];
-  __threadfence();
+  for (int t = 0; t < RT; ++t) *reinterpret_cast<v4f*>(&red[wave][t][lane][0]) = acc[t];
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.counter + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (prev == uint32_t(splits - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  v4f sum = {0.f, 0.f, 0.f, 0.f};
-  const float* base = a.partial + int64_t(tile) * splits * (ROWS * COLS);
-  for (int s = 0; s < splits; ++s) {
-    const float* p = base + int64_t(s) * (ROWS * COLS);
+  const int t = tid >> 8;             // row tile
+  const int ln = (tid >> 2) & 63;     // lane of that tile
+  const int r = tid & 3;              // element
+  float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sum[r] += __builtin_nontemporal_load(p + (wave * 16 + 4 * gq + r) * COLS + l16);
+  for (int w = 0; w < WAVES; ++w) sum += red[w][t][ln][r];
+  const int row = rtile * ROWS + t * 16 + 4 * (ln >> 4) + r;   // member-local output feature
+  const int mo = ct * COLS + (ln & 15);
+  if (row < mem.rows && mo < a.M) {
+    const int64_t off = int64_t(mo) * a.ldy + mem.col0 + row;
+    if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
+    else static_cast<float*>(a.y)[off] = sum;
   }
-  store_y(sum);
-  if (tid == 0) __hip_atomic_store(a.counter + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct Plan {
   TileMap tm;
   int col_tiles;
   int tiles;
-  int splits;
-  int chunks_per_split;
-  int blocks;
-  size_t counter_bytes;
-  size_t partial_bytes;
+  int chunks_per_wave;
 };
 
 Plan make_plan(const WeightDev& w, int64_t M) {
@@ -319,41 +364,37 @@ Plan make_plan(const WeightDev& w, int64_t M) {
   }
   p.tm.tile0[w.n_members] = t;
   p.tiles = t;
-  const int want = (TARGET_BLOCKS + t - 1) / t;
-  const int cps = want <= 1 ? w.Kb : (w.Kb + want - 1) / want;
-  p.chunks_per_split = cps < 1 ? 1 : cps;
-  p.splits = (w.Kb + p.chunks_per_split - 1) / p.chunks_per_split;
-  p.blocks = p.tiles * p.splits;
-  if (p.splits > 1) {
-    p.counter_bytes = ((size_t(p.tiles) * 4 + 255) / 256) * 256;
-    p.partial_bytes = size_t(p.tiles) * p.splits * ROWS * COLS * sizeof(float);
-  }
+  p.chunks_per_wave = (w.Kb + WAVES - 1) / WAVES;
   return p;
 }
 
 }  // namespace
 
-size_t w8a16_workspace_bytes(const WeightDev& w, int64_t M) {
-  const Plan p = make_plan(w, M);
-  return p.counter_bytes + p.partial_bytes;
-}
+size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
 
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   const Plan p = make_plan(w, M > 0 ? M : 1);
   char buf[320];
   snprintf(buf, sizeof(buf),
            "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
-           "mfma_f32_16x16x32_bf16 | kernel=w8a16 rows=%d tokens=%d waves=%d k_splits=%d chunks_per_split=%d "
+           "mfma_f32_16x16x32_bf16 | kernel=w8a16 rows=%d tokens=%d waves=%d (in-block split-K, %d chunks/wave) "
            "path=%s | M=%lld blocks=%d",
-           ROWS, COLS, WAVES, p.splits, p.chunks_per_split, aligned ? "aligned16" : "bytewise", (long long)M,
-           p.blocks);
+           ROWS, COLS, WAVES, p.chunks_per_wave, aligned ? "aligned16" : "bytewise", (long long)M, p.tiles);
   return buf;
 }
 
 bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x_bf16, int64_t M, int64_t ldx,
-                         void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
+                         void* y, bool y_bf16, int64_t ldy, void*, size_t, hipStream_t stream) {
   const Plan p = make_plan(w, M);
-  if (p.blocks == 0) return BSF8_OK;
+  if (w.Kb > MAX_KB) {
+    set_error("UNSUPPORTED: K above %d", MAX_KB * CHUNK);
+    return BSF8_E_UNSUPPORTED;
+  }
+  // buffer offsets are 32-bit: operands of 2 GiB or more take the byte-wise path
+  if (M * ldx * (x_bf16 ? 2 : 4) >= (int64_t(1) << 31)) aligned = false;
+  for (int i = 0; i < w.n_members; ++i)
+    if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) aligned = false;
+  if (p.tiles == 0) return BSF8_OK;
   Args a{};
   a.w = w;
   a.tm = p.tm;
@@ -363,22 +404,19 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   a.ldy = ldy;
   a.M = int32_t(M);
   a.col_tiles = p.col_tiles;
-  a.splits = p.splits;
-  a.chunks_per_split = p.chunks_per_split;
+  a.chunks_per_wave = p.chunks_per_wave;
   a.x_bf16 = x_bf16 ? 1 : 0;
   a.y_bf16 = y_bf16 ? 1 : 0;
-  if (p.splits > 1) {
-    if (ws == nullptr || ws_bytes < p.counter_bytes + p.partial_bytes) {
-      set_error("WORKSPACE: %zu bytes needed", p.counter_bytes + p.partial_bytes);
-      return BSF8_E_WORKSPACE;
-    }
-    a.counter = static_cast<uint32_t*>(ws);
-    a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.counter_bytes);
+  auto kern = w8a16_kernel<true, false, true>;
+  const bool sb = w.scale_bf16 != 0;
+  if (aligned) {
+    if (x_bf16) kern = sb ? w8a16_kernel<true, true, true> : w8a16_kernel<true, true, false>;
+    else kern = sb ? w8a16_kernel<true, false, true> : w8a16_kernel<true, false, false>;
+  } else {
+    if (x_bf16) kern = sb ? w8a16_kernel<false, true, true> : w8a16_kernel<false, true, false>;
+    else kern = sb ? w8a16_kernel<false, false, true> : w8a16_kernel<false, false, false>;
   }
-  if (aligned)
-    hipLaunchKernelGGL(w8a16_kernel<true>, dim3(p.blocks), dim3(THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(w8a16_kernel<false>, dim3(p.blocks), dim3(THREADS), 0, stream, a);
+  hipLaunchKernelGGL(kern, dim3(p.tiles), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a16 launch");
 }
 

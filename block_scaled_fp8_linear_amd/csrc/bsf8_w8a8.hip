@@ -31,9 +31,17 @@
 
 #include "bsf8_internal.h"
 
+// buffer_load ... lds: each lane's 16 bytes land at lds + 16 * lane (the LLVM intrinsic).
+typedef int bsf8_v4i __attribute__((ext_vector_type(4)));
+__device__ void bsf8_raw_buffer_load_lds(bsf8_v4i rsrc, __attribute__((address_space(3))) uint32_t* lds, int size,
+                                         int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 namespace bsf8 {
 namespace {
 
+typedef bsf8_v4i v4i;
+typedef uint32_t __attribute__((address_space(3)))* lds_u32_ptr;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -70,6 +78,12 @@ __device__ __forceinline__ float load_scale(const void* s, int64_t idx, int bf16
   return static_cast<const float*>(s)[idx];
 }
 
+template <bool SBF16>
+__device__ __forceinline__ float load_scale_t(const void* s, int64_t idx) {
+  if (SBF16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(s)[idx]) << 16);
+  return static_cast<const float*>(s)[idx];
+}
+
 // 16 bytes of one row starting at K offset k (bytes past K are zero).
 template <bool ALIGNED>
 __device__ __forceinline__ uint4 load_chunk(const uint8_t* row, int k, int K, bool row_ok) {
@@ -91,6 +105,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+
+// Four consecutive outputs of one token (nvalid of them exist) as F32 or BF16 (RNE).
+__device__ __forceinline__ void store4(void* yv, int bf16, int64_t off, int nvalid, const v4f& v) {
+  if (bf16) {
+    uint16_t* y = static_cast<uint16_t*>(yv) + off;
+    const uint16_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
+    const uint16_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
+    if (nvalid >= 4 && (reinterpret_cast<uintptr_t>(y) & 7) == 0) {
+      *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(b0) | (uint32_t(b1) << 16), uint32_t(b2) | (uint32_t(b3) << 16));
+    } else {
+      y[0] = b0;
+      if (nvalid > 1) y[1] = b1;
+      if (nvalid > 2) y[2] = b2;
+      if (nvalid > 3) y[3] = b3;
+    }
+  } else {
+    float* y = static_cast<float*>(yv) + off;
+    if (nvalid >= 4 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+      *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      y[0] = v[0];
+      if (nvalid > 1) y[1] = v[1];
+      if (nvalid > 2) y[2] = v[2];
+      if (nvalid > 3) y[3] = v[3];
+    }
+  }
 }
 
 template <bool ALIGNED>
@@ -233,44 +275,246 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int n = n0 + wn * WN + 16 * i + 4 * g;
-      const int64_t off = int64_t(m) * a.ldy + mem.col0 + n;
       const int nvalid = mem.rows - n;
       if (nvalid <= 0) continue;
-      if (a.y_bf16) {
-        uint16_t* y = static_cast<uint16_t*>(a.y) + off;
-        const uint16_t b0 = f32_to_bf16_rne(acc[i][j][0]), b1 = f32_to_bf16_rne(acc[i][j][1]);
-        const uint16_t b2 = f32_to_bf16_rne(acc[i][j][2]), b3 = f32_to_bf16_rne(acc[i][j][3]);
-        if (nvalid >= 4 && (reinterpret_cast<uintptr_t>(y) & 7) == 0) {
-          *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(b0) | (uint32_t(b1) << 16), uint32_t(b2) | (uint32_t(b3) << 16));
-        } else {
-          y[0] = b0;
-          if (nvalid > 1) y[1] = b1;
-          if (nvalid > 2) y[2] = b2;
-          if (nvalid > 3) y[3] = b3;
-        }
-      } else {
-        float* y = static_cast<float*>(a.y) + off;
-        if (nvalid >= 4 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
-          *reinterpret_cast<float4*>(y) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        } else {
-          y[0] = acc[i][j][0];
-          if (nvalid > 1) y[1] = acc[i][j][1];
-          if (nvalid > 2) y[2] = acc[i][j][2];
-          if (nvalid > 3) y[3] = acc[i][j][3];
-        }
+      store4(a.y, a.y_bf16, int64_t(m) * a.ldy + mem.col0 + n, nvalid, acc[i][j]);
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Fast path (K % 16 == 0, 16-byte aligned operands): 512 threads, 256 x 256
+// block tile, eight waves of 128 x 64 (two per SIMD, so one wave's epilogue and
+// LDS traffic overlap the other's MFMAs), operands copied HBM -> LDS by
+// buffer_load ... lds without passing through registers.  Out-of-range rows,
+// tokens and K bytes are given an offset past the buffer's end, which the
+// buffer unit returns as zeros.
+// ---------------------------------------------------------------------------
+
+constexpr int FBN = 256, FBM = 256, FTHREADS = 512;
+constexpr int F_SA = FBN * KBYTES + FBM * KBYTES;  // offset of the token scales in a stage
+constexpr int F_STAGE = F_SA + FBM * 4;           // 64 KiB of operands + 1 KiB of scales
+constexpr int F_A_LOADS = FBN * KBYTES / 1024 / 8;  // 1 KiB wave loads per wave per stage: 4
+constexpr int F_B_LOADS = FBM * KBYTES / 1024 / 8;  // 4
+constexpr int XCDS = 8;
+constexpr int GROUP_ROWS = 8;   // row tiles per L2 group
+
+struct FastArgs {
+  WeightDev w;
+  int32_t rt0[kMaxMembers + 1];   // first 256-row tile of each member
+  const uint8_t* xq;
+  const float* xs;
+  void* y;
+  int64_t ldq;
+  int64_t ldxs;
+  int64_t ldy;
+  int32_t M;
+  int32_t m_tiles;
+  int32_t rt_total;
+  int32_t y_bf16;
+};
+
+__device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32)));
+  r[2] = __builtin_amdgcn_readfirstlane(int(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+template <bool SBF16>
+__global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F_STAGE];
+
+  // ---- XCD-aware tile order: blocks are dealt to the 8 XCDs round robin; give
+  // every XCD a contiguous run of tiles, walked in groups of GROUP_ROWS row
+  // tiles x all token tiles so that concurrently running blocks share operands
+  // in that XCD's L2.
+  const int nblk = gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b % XCDS;
+  int v = b / XCDS;
+  for (int y = 0; y < xcd; ++y) v += (nblk - y + XCDS - 1) / XCDS;
+  const int gsz = GROUP_ROWS * a.m_tiles;
+  const int grp = v / gsz;
+  const int in_grp = v - grp * gsz;
+  const int g_rows = min(GROUP_ROWS, a.rt_total - grp * GROUP_ROWS);
+  const int R = grp * GROUP_ROWS + in_grp % g_rows;
+  const int mt = in_grp / g_rows;
+  int mi = 0;
+  while (mi + 1 < a.w.n_members && R >= a.rt0[mi + 1]) ++mi;
+  const MemberDev mem = a.w.m[mi];
+  const int n0 = (R - a.rt0[mi]) * FBN;
+  const int m0 = mt * FBM;
+  const int K = a.w.K, Kb = a.w.Kb, M = a.M;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  // ---- buffer resources and per-lane copy offsets (fixed per K block but for kb*128)
+  const uint32_t a_bytes = uint32_t(mem.rows) * uint32_t(K);
+  const uint32_t b_bytes = uint32_t(M) * uint32_t(a.ldq);
+  const v4i ra = make_rsrc(mem.w, a_bytes);
+  const v4i rb = make_rsrc(a.xq, b_bytes);
+  const uint32_t s_bytes = uint32_t(M) * uint32_t(a.ldxs) * 4u;
+  const v4i rs = make_rsrc(a.xs, s_bytes);
+  // waves 0..3 each copy the scales of 64 tokens (one 4-byte element per lane)
+  const bool s_wave = wave < FBM / 64;
+  const bool s_ok = s_wave && (m0 + wave * 64 + lane) < M;
+  const int s_off = (m0 + wave * 64 + lane) * int(a.ldxs) * 4;
+  const int crow = lane >> 3;                    // row within a 1 KiB wave load
+  const int cchunk = (lane & 7) ^ crow;          // logical 16-byte chunk this lane fetches
+  int a_off[F_A_LOADS], b_off[F_B_LOADS];
+  bool a_ok[F_A_LOADS], b_ok[F_B_LOADS];
+#pragma unroll
+  for (int i = 0; i < F_A_LOADS; ++i) {
+    const int row = (wave * F_A_LOADS + i) * 8 + crow;
+    a_ok[i] = n0 + row < mem.rows;
+    a_off[i] = (n0 + row) * K + cchunk * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < F_B_LOADS; ++i) {
+    const int row = (wave * F_B_LOADS + i) * 8 + crow;
+    b_ok[i] = m0 + row < M;
+    b_off[i] = (m0 + row) * int(a.ldq) + cchunk * 16;
+  }
+  auto issue = [&](int kb, int stage) {
+    const int kk = kb * KBYTES + cchunk * 16;
+    const bool k_ok = kk < K;
+    uint8_t* base = smem + stage * F_STAGE;
+#pragma unroll
+    for (int i = 0; i < F_A_LOADS; ++i) {
+      const int off = (a_ok[i] && k_ok) ? a_off[i] + kb * KBYTES : int(a_bytes);
+      bsf8_raw_buffer_load_lds(ra, (lds_u32_ptr)(base + (wave * F_A_LOADS + i) * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < F_B_LOADS; ++i) {
+      const int off = (b_ok[i] && k_ok) ? b_off[i] + kb * KBYTES : int(b_bytes);
+      bsf8_raw_buffer_load_lds(rb, (lds_u32_ptr)(base + FBN * KBYTES + (wave * F_B_LOADS + i) * 1024), 16, off, 0, 0,
+                          0);
+    }
+    if (s_wave) {
+      const int off = s_ok ? s_off + kb * 4 : int(s_bytes);
+      bsf8_raw_buffer_load_lds(rs, (lds_u32_ptr)(base + F_SA + wave * 256), 4, off, 0, 0, 0);
+    }
+  };
+
+  // ---- scales
+  const int srow = (n0 + wn * WN) >> 7;
+  const int nb = (mem.rows + 127) >> 7;
+  const bool srow_ok = srow < nb;
+  const int64_t s_base = int64_t(srow_ok ? srow : 0) * Kb;
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  float sw_next = srow_ok ? load_scale_t<SBF16>(mem.s, s_base) : 0.f;
+
+  issue(0, 0);
+  for (int kb = 0; kb < Kb; ++kb) {
+    const int stage = kb & 1;
+    // this wave's copies into `stage` have landed; after the barrier everyone's
+    // have, and every wave is done reading the other stage
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < Kb) issue(kb + 1, stage ^ 1);
+
+    const float sw = sw_next;
+    if (kb + 1 < Kb) sw_next = srow_ok ? load_scale_t<SBF16>(mem.s, s_base + kb + 1) : 0.f;
+    const float* sa = reinterpret_cast<const float*>(smem + stage * F_STAGE + F_SA);
+    float s[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) s[j] = sa[wm * WM + 16 * j + l16] * sw;
+
+    const uint8_t* As = smem + stage * F_STAGE;
+    const uint8_t* Bs = As + FBN * KBYTES;
+    v8i bf[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int r = wm * WM + 16 * j + l16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g));
+      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g + 1));
+      bf[j] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    }
+    // Software pipeline over the 8 row tiles: the A fragment of tile i+1 is read
+    // from LDS and the MFMAs of tile i are issued into one partial buffer while
+    // the epilogue FMAs drain tile i-1's buffer.
+    auto read_a = [&](int i) {
+      const int r = wn * WN + 16 * i + l16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g));
+      const uint4 hi = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g + 1));
+      return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    };
+    v8i af[2];
+    v4f pp[2][TJ];
+    af[0] = read_a(0);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      if (i + 1 < TI) af[(i + 1) & 1] = read_a(i + 1);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        pp[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                        0, 0, 0, 0, 0, 0);
+      if (i > 0) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i - 1][j] += pp[(i - 1) & 1][j] * s[j];
       }
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[TI - 1][j] += pp[(TI - 1) & 1][j] * s[j];
+  }
+
+  // ---- store: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int m = m0 + wm * WM + 16 * j + l16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int n = n0 + wn * WN + 16 * i + 4 * g;
+      const int nvalid = mem.rows - n;
+      if (nvalid <= 0) continue;
+      store4(a.y, a.y_bf16, int64_t(m) * a.ldy + mem.col0 + n, nvalid, acc[i][j]);
     }
   }
 }
 
 struct Plan {
-  TileMap tm;
+  bool fast;
+  TileMap tm;         // register-staged kernel: member tiles
+  int32_t rt0[kMaxMembers + 1];
+  int rt_total;
   int m_tiles;
   int blocks;
 };
 
-Plan make_plan(const WeightDev& w, int64_t M) {
+// The direct-copy kernel addresses each operand with 32-bit byte offsets from
+// its base, so every member and the activation block must stay below 2^31 bytes.
+Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
   Plan p{};
+  bool fits = M * ldq < (int64_t(1) << 31);
+  for (int i = 0; i < w.n_members; ++i) fits = fits && int64_t(w.m[i].rows) * w.K < (int64_t(1) << 31);
+  p.fast = aligned && fits;
+  if (p.fast) {
+    p.m_tiles = int((M + FBM - 1) / FBM);
+    int r = 0;
+    for (int i = 0; i < w.n_members; ++i) {
+      p.rt0[i] = r;
+      r += (w.m[i].rows + FBN - 1) / FBN;
+    }
+    for (int i = w.n_members; i <= kMaxMembers; ++i) p.rt0[i] = r;
+    p.rt_total = r;
+    p.blocks = r * p.m_tiles;
+    return p;
+  }
   p.m_tiles = int((M + BM - 1) / BM);
   int t = 0;
   for (int i = 0; i < w.n_members; ++i) {
@@ -288,20 +532,46 @@ Plan make_plan(const WeightDev& w, int64_t M) {
 size_t w8a8_workspace_bytes(const WeightDev&, int64_t) { return 0; }
 
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
-  const Plan p = make_plan(w, M > 0 ? M : 1);
-  char buf[256];
-  snprintf(buf, sizeof(buf),
-           "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | kernel=w8a8_gemm "
-           "tile=%dx%d waves=4 lds=2x%dKiB path=%s | M=%lld blocks=%d",
-           BN, BM, STAGE_BYTES / 1024, aligned ? "aligned16" : "bytewise", (long long)M, p.blocks);
+  const Plan p = make_plan(w, aligned, M > 0 ? M : 1, w.K);
+  char buf[320];
+  if (p.fast)
+    snprintf(buf, sizeof(buf),
+             "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
+             "kernel=w8a8_gemm_fast tile=%dx%d waves=8 lds=2x%dKiB buffer_load_lds xcd_groups=%d | M=%lld blocks=%d",
+             FBN, FBM, F_STAGE / 1024, GROUP_ROWS, (long long)M, p.blocks);
+  else
+    snprintf(buf, sizeof(buf),
+             "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
+             "kernel=w8a8_gemm tile=%dx%d waves=4 lds=2x%dKiB path=%s | M=%lld blocks=%d",
+             BN, BM, STAGE_BYTES / 1024, aligned ? "aligned16" : "bytewise", (long long)M, p.blocks);
   return buf;
 }
 
 bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,
                         int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void*, size_t,
                         hipStream_t stream) {
-  const Plan p = make_plan(w, M);
+  const Plan p = make_plan(w, aligned, M, ldq);
   if (p.blocks == 0) return BSF8_OK;
+  if (p.fast) {
+    FastArgs a{};
+    a.w = w;
+    for (int i = 0; i <= kMaxMembers; ++i) a.rt0[i] = p.rt0[i];
+    a.xq = xq;
+    a.xs = xs;
+    a.y = y;
+    a.ldq = ldq;
+    a.ldxs = ldxs;
+    a.ldy = ldy;
+    a.M = int32_t(M);
+    a.m_tiles = p.m_tiles;
+    a.rt_total = p.rt_total;
+    a.y_bf16 = y_bf16 ? 1 : 0;
+    if (w.scale_bf16)
+      hipLaunchKernelGGL(w8a8_gemm_fast_kernel<true>, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL(w8a8_gemm_fast_kernel<false>, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
+    return device_status(hipGetLastError(), "w8a8_gemm_fast launch");
+  }
   GemmArgs a{};
   a.w = w;
   a.tm = p.tm;
