@@ -106,6 +106,20 @@ class KernelTimer:
         self.pairs = {}
 
 
+def settle(torch, fn, seconds=1.0):
+    """Run ``fn`` back to back for about ``seconds`` before anything is timed.
+
+    The GPU raises its clock only under sustained load: the first milliseconds
+    after an idle period run measurably slower (more than 20 % on the large
+    GEMM), which would make the timed steps depend on what ran before them.
+    """
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def to_device_member(torch, m, dev):
     w = torch.from_numpy(np.ascontiguousarray(m.codes)).to(dev)
     s = torch.from_numpy(np.ascontiguousarray(m.scale_bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -135,6 +149,7 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
         kt.run("quant_down", lambda: B.quant_act(x_dn, xq_dn, xs_dn))
         kt.run("gemm_down", lambda: B.linear_w8a8(w_dn, xq_dn, xs_dn, out=y_dn))
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -197,8 +212,7 @@ def bench_decode(torch, B, synth, steps, dev):
         with torch.cuda.graph(g):
             for i in range(copies):
                 B.linear_w8a16(handles[i], x, out=y, workspace=ws[i])
-        g.replay()
-        torch.cuda.synchronize()
+        settle(torch, g.replay, 0.3)
         reps = max(4, steps)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -225,9 +239,7 @@ def bench_large(torch, B, synth, steps, dev):
     xq, xs = B.quant_act(x)
     y = torch.empty((M, w.n_total), dtype=torch.bfloat16, device=dev)
     kt = KernelTimer(torch)
-    for _ in range(2):
-        B.linear_w8a8(w, xq, xs, out=y)
-    torch.cuda.synchronize()
+    settle(torch, lambda: B.linear_w8a8(w, xq, xs, out=y))
     for _ in range(max(3, steps // 2)):
         kt.run("gemm", lambda: B.linear_w8a8(w, xq, xs, out=y))
         kt.run("quant", lambda: B.quant_act(x, xq, xs))

@@ -36,6 +36,9 @@ typedef int bsf8_v4i __attribute__((ext_vector_type(4)));
 __device__ void bsf8_raw_buffer_load_lds(bsf8_v4i rsrc, __attribute__((address_space(3))) uint32_t* lds, int size,
                                          int voffset, int soffset, int offset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Raw buffer load of 16 bytes into registers; an offset past the resource's size reads zeros.
+__device__ bsf8_v4i bsf8_raw_buffer_load_b128(bsf8_v4i rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 
 namespace bsf8 {
 namespace {
@@ -71,7 +74,13 @@ struct GemmArgs {
   int32_t y_bf16;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * KBYTES + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of row r lives at chunk position c ^ ((r >> 1) & 7).  The LDS
+// serves a ds_read_b128 16 lanes at a time over 64 four-byte banks; a row is
+// 128 bytes, so the bank half is set by the row's parity and the 4-bank group
+// by the chunk position.  The 16 rows an MFMA fragment read touches at once
+// (same logical chunk) thus land on 16 distinct (parity, position) pairs.
+__device__ __forceinline__ int swz_pos(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * KBYTES + (swz_pos(row, chunk) << 4); }
 
 __device__ __forceinline__ float load_scale(const void* s, int64_t idx, int bf16) {
   if (bf16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(s)[idx]) << 16);
@@ -299,6 +308,7 @@ constexpr int F_A_LOADS = FBN * KBYTES / 1024 / 8;  // 1 KiB wave loads per wave
 constexpr int F_B_LOADS = FBM * KBYTES / 1024 / 8;  // 4
 constexpr int XCDS = 8;
 constexpr int GROUP_ROWS = 8;   // row tiles per L2 group
+constexpr int F_MAX_KB = 1024;  // K up to 131072 on the fast path
 
 struct FastArgs {
   WeightDev w;
@@ -313,6 +323,7 @@ struct FastArgs {
   int32_t m_tiles;
   int32_t rt_total;
   int32_t y_bf16;
+  int32_t y_vec;   // y, ldy and every member's column offset allow 16-byte stores
 };
 
 __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
@@ -325,9 +336,71 @@ __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
   return r;
 }
 
+constexpr int F_OUT_PITCH = 144;  // bytes per token row of the store staging (128 + 16: no bank conflicts)
+
+// Writes a wave's 128 x 64 result tile through LDS so that each lane stores 16
+// contiguous bytes of one token row (8 lanes fill a 128-byte line).  In the
+// MFMA layout a lane holds 4 consecutive outputs of one token, and 16 lanes of
+// one instruction touch 16 rows, which turns into many small partial-line
+// writes.  `buf` is this wave's 64 x F_OUT_PITCH staging area; the tile goes
+// out in rounds of 128 bytes per token row (4 row tiles of bf16, 2 of f32).
+template <bool YBF16>
+__device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uint8_t* buf, void* y, int64_t ldy,
+                                                   int64_t col0, int n_base, int n_end, int m_base, int M, int lane) {
+  constexpr int ESZ = YBF16 ? 2 : 4;
+  constexpr int PER_ROUND = 128 / (16 * ESZ);  // row tiles per round
+  constexpr int EPC = 16 / ESZ;                // elements per 16-byte chunk
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i0 = 0; i0 < TI; i0 += PER_ROUND) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+      for (int ii = 0; ii < PER_ROUND; ++ii) {
+        const v4f& v = acc[i0 + ii][j];
+        uint8_t* dst = buf + (16 * j + l16) * F_OUT_PITCH + (ii * 16 + 4 * g) * ESZ;
+        if (YBF16) {
+          *reinterpret_cast<uint2*>(dst) =
+              make_uint2(uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16),
+                         uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16));
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int row = 8 * t + (lane >> 3), ch = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(buf + row * F_OUT_PITCH + ch * 16);
+      const int m = m_base + row;
+      const int n = n_base + i0 * 16 + ch * EPC;
+      const int nvalid = n_end - n;
+      if (m >= M || nvalid <= 0) continue;
+      uint8_t* out = static_cast<uint8_t*>(y) + (int64_t(m) * ldy + col0 + n) * ESZ;
+      if (nvalid >= EPC) {
+        *reinterpret_cast<uint4*>(out) = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int e = 0; e < nvalid; ++e) {
+          if (YBF16)
+            reinterpret_cast<uint16_t*>(out)[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+          else
+            reinterpret_cast<uint32_t*>(out)[e] = w[e];
+        }
+      }
+    }
+  }
+}
+
 template <bool SBF16>
 __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * F_STAGE];
+  // Two separate stage arrays (not one array indexed by stage): the compiler
+  // must wait for in-flight LDS copies before any LDS read it cannot prove
+  // disjoint from them, and distinct objects let it see that reading stage 0
+  // does not touch the copy landing in stage 1.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[F_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[F_STAGE];
+  __shared__ float wscale[2][F_MAX_KB];   // the block's two rows of the weight scale grid
 
   // ---- XCD-aware tile order: blocks are dealt to the 8 XCDs round robin; give
   // every XCD a contiguous run of tiles, walked in groups of GROUP_ROWS row
@@ -364,78 +437,87 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   const v4i rb = make_rsrc(a.xq, b_bytes);
   const uint32_t s_bytes = uint32_t(M) * uint32_t(a.ldxs) * 4u;
   const v4i rs = make_rsrc(a.xs, s_bytes);
-  // waves 0..3 each copy the scales of 64 tokens (one 4-byte element per lane)
+  // waves 0..3 each copy the scales of 64 tokens (one 4-byte element per
+  // lane).  Lane L fetches token 16 (L & 3) + (L >> 2) of its wave's 64, so the
+  // four scales a compute lane needs (tokens l16 + 16 j, j = 0..3) sit in one
+  // 16-byte LDS word.
   const bool s_wave = wave < FBM / 64;
-  const bool s_ok = s_wave && (m0 + wave * 64 + lane) < M;
-  const int s_off = (m0 + wave * 64 + lane) * int(a.ldxs) * 4;
-  const int crow = lane >> 3;                    // row within a 1 KiB wave load
-  const int cchunk = (lane & 7) ^ crow;          // logical 16-byte chunk this lane fetches
-  int a_off[F_A_LOADS], b_off[F_B_LOADS];
-  bool a_ok[F_A_LOADS], b_ok[F_B_LOADS];
-#pragma unroll
-  for (int i = 0; i < F_A_LOADS; ++i) {
-    const int row = (wave * F_A_LOADS + i) * 8 + crow;
-    a_ok[i] = n0 + row < mem.rows;
-    a_off[i] = (n0 + row) * K + cchunk * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < F_B_LOADS; ++i) {
-    const int row = (wave * F_B_LOADS + i) * 8 + crow;
-    b_ok[i] = m0 + row < M;
-    b_off[i] = (m0 + row) * int(a.ldq) + cchunk * 16;
-  }
-  auto issue = [&](int kb, int stage) {
-    const int kk = kb * KBYTES + cchunk * 16;
-    const bool k_ok = kk < K;
-    uint8_t* base = smem + stage * F_STAGE;
-#pragma unroll
-    for (int i = 0; i < F_A_LOADS; ++i) {
-      const int off = (a_ok[i] && k_ok) ? a_off[i] + kb * KBYTES : int(a_bytes);
+  const int s_tok = m0 + wave * 64 + 16 * (lane & 3) + (lane >> 2);
+  const bool s_ok = s_wave && s_tok < M;
+  const int s_off = s_tok * int(a.ldxs) * 4;
+  // Lane L of a 1 KiB wave copy fills chunk position L & 7 of row L >> 3 of its
+  // 8-row slab q; since (row >> 1) & 7 = 4 (q & 1) + (L >> 4), the logical chunk
+  // it fetches depends only on the slab's parity.
+  const int crow = lane >> 3;
+  const int ch_even = swz_pos(crow, lane & 7) * 16;
+  const int ch_odd = swz_pos(crow + 8, lane & 7) * 16;
+  const int a_row0 = n0 + wave * F_A_LOADS * 8 + crow;   // row of slab i is a_row0 + 8 i
+  const int b_row0 = m0 + wave * F_B_LOADS * 8 + crow;
+  // Copy number c (0 .. F_A_LOADS + F_B_LOADS - 1) of K block kb into a stage:
+  // the first F_A_LOADS are weight slabs, the rest token slabs.  With
+  // live == false every lane gets the past-the-end offset, so the copy moves
+  // no data (it fills the unused stage with zeros) and needs no branch.
+  auto issue_one = [&](int kb, uint8_t* base, int c, bool live) {
+    if (c < F_A_LOADS) {
+      const int i = c;
+      const int ch = ((wave * F_A_LOADS + i) & 1) ? ch_odd : ch_even;
+      const bool ok = live && (a_row0 + 8 * i < mem.rows) && (kb * KBYTES + ch < K);
+      const int off = ok ? (a_row0 + 8 * i) * K + kb * KBYTES + ch : int(a_bytes);
       bsf8_raw_buffer_load_lds(ra, (lds_u32_ptr)(base + (wave * F_A_LOADS + i) * 1024), 16, off, 0, 0, 0);
+    } else {
+      const int i = c - F_A_LOADS;
+      const int ch = ((wave * F_B_LOADS + i) & 1) ? ch_odd : ch_even;
+      const bool ok = live && (b_row0 + 8 * i < M) && (kb * KBYTES + ch < K);
+      const int off = ok ? (b_row0 + 8 * i) * int(a.ldq) + kb * KBYTES + ch : int(b_bytes);
+      bsf8_raw_buffer_load_lds(rb, (lds_u32_ptr)(base + FBN * KBYTES + (wave * F_B_LOADS + i) * 1024), 16, off, 0,
+                               0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < F_B_LOADS; ++i) {
-      const int off = (b_ok[i] && k_ok) ? b_off[i] + kb * KBYTES : int(b_bytes);
-      bsf8_raw_buffer_load_lds(rb, (lds_u32_ptr)(base + FBN * KBYTES + (wave * F_B_LOADS + i) * 1024), 16, off, 0, 0,
-                          0);
-    }
+  };
+  auto issue_scales = [&](int kb, uint8_t* base) {
     if (s_wave) {
       const int off = s_ok ? s_off + kb * 4 : int(s_bytes);
       bsf8_raw_buffer_load_lds(rs, (lds_u32_ptr)(base + F_SA + wave * 256), 4, off, 0, 0, 0);
     }
   };
+  auto issue = [&](int kb, uint8_t* base) {
+#pragma unroll
+    for (int c = 0; c < F_A_LOADS + F_B_LOADS; ++c) issue_one(kb, base, c, true);
+    issue_scales(kb, base);
+  };
 
-  // ---- scales
-  const int srow = (n0 + wn * WN) >> 7;
-  const int nb = (mem.rows + 127) >> 7;
-  const bool srow_ok = srow < nb;
-  const int64_t s_base = int64_t(srow_ok ? srow : 0) * Kb;
+  // ---- weight scales: rows (n0 >> 7) and (n0 >> 7) + 1 of the member's grid
+  // (one per wave half), staged in LDS once; a missing row reads as zero
+  {
+    const int nb = (mem.rows + 127) >> 7;
+    for (int i = tid; i < 2 * Kb; i += FTHREADS) {
+      const int h = i >= Kb, kb = i - h * Kb;
+      const int srow = (n0 >> 7) + h;
+      wscale[h][kb] = srow < nb ? load_scale_t<SBF16>(mem.s, int64_t(srow) * Kb + kb) : 0.f;
+    }
+  }
+
   v4f acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  float sw_next = srow_ok ? load_scale_t<SBF16>(mem.s, s_base) : 0.f;
 
-  issue(0, 0);
-  for (int kb = 0; kb < Kb; ++kb) {
-    const int stage = kb & 1;
-    // this wave's copies into `stage` have landed; after the barrier everyone's
-    // have, and every wave is done reading the other stage
+  // One K block: wait for its copies, start the next block's copies into the
+  // other stage, then run the MFMAs and the per-block epilogue.
+  auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt) {
+    // this wave's copies into `cur` have landed; after the barrier everyone's
+    // have, and every wave is done reading `nxt`
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kb + 1 < Kb) issue(kb + 1, stage ^ 1);
+    const bool more = kb + 1 < Kb;
+    if (more) issue_scales(kb + 1, nxt);
 
-    const float sw = sw_next;
-    if (kb + 1 < Kb) sw_next = srow_ok ? load_scale_t<SBF16>(mem.s, s_base + kb + 1) : 0.f;
-    const float* sa = reinterpret_cast<const float*>(smem + stage * F_STAGE + F_SA);
-    float s[TJ];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) s[j] = sa[wm * WM + 16 * j + l16] * sw;
+    const float sw = wscale[wn][kb];
+    const float4 sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
 
-    const uint8_t* As = smem + stage * F_STAGE;
-    const uint8_t* Bs = As + FBN * KBYTES;
+    const uint8_t* As = cur;
+    const uint8_t* Bs = cur + FBN * KBYTES;
     v8i bf[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
@@ -444,9 +526,6 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
       const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g + 1));
       bf[j] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
     }
-    // Software pipeline over the 8 row tiles: the A fragment of tile i+1 is read
-    // from LDS and the MFMAs of tile i are issued into one partial buffer while
-    // the epilogue FMAs drain tile i-1's buffer.
     auto read_a = [&](int i) {
       const int r = wn * WN + 16 * i + l16;
       const uint4 lo = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g));
@@ -454,25 +533,58 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
       return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
     };
     v8i af[2];
-    v4f pp[2][TJ];
     af[0] = read_a(0);
+    const float s[TJ] = {sa.x * sw, sa.y * sw, sa.z * sw, sa.w * sw};
+    // The 32 MFMAs of the K block run as one rotated chain: the epilogue FMAs
+    // that consume MFMA q's partial are issued after MFMA q + 2 (three
+    // 4-register partial buffers), far enough behind for its result to be ready
+    // without wait states, and the A fragment of row tile i + 1 is read from LDS
+    // while tile i's MFMAs run.
+    constexpr int LAG = 2;
+    constexpr int COPY_EVERY = 2;
+    v4f part[LAG + 1];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      if (i + 1 < TI) af[(i + 1) & 1] = read_a(i + 1);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        pp[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                        0, 0, 0, 0, 0, 0);
-      if (i > 0) {
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i - 1][j] += pp[(i - 1) & 1][j] * s[j];
+    for (int q = 0; q < TI * TJ + LAG; ++q) {
+      if (q < TI * TJ) {
+        const int i = q / TJ, j = q % TJ;
+        if (j == 0 && i + 1 < TI) af[(i + 1) & 1] = read_a(i + 1);
+        part[q % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j],
+                                                                             v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (q >= LAG) {
+        const int c = q - LAG, ci = c / TJ, cj = c % TJ;
+        acc[ci][cj] += part[c % (LAG + 1)] * s[cj];
+      }
+      // the next K block's copies go out one per COPY_EVERY MFMAs: issued in one
+      // burst they queue in the vector memory unit and hold the wave there
+      // before its first MFMA
+      if (q % COPY_EVERY == 0 && q / COPY_EVERY < F_A_LOADS + F_B_LOADS) issue_one(kb + 1, nxt, q / COPY_EVERY, more);
+      // (the scheduling barriers keep each MFMA ahead of the FMAs issued after it)
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[TI - 1][j] += pp[(TI - 1) & 1][j] * s[j];
+  };
+
+  issue(0, stage0);
+  for (int kb = 0; kb < Kb; kb += 2) {
+    step(kb, stage0, stage1);
+    if (kb + 1 < Kb) step(kb + 1, stage1, stage0);
   }
 
-  // ---- store: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
+  // ---- store
+  if (a.y_vec) {
+    // the last step's (empty) copies have landed and every wave is done
+    // reading both stages
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint8_t* buf = (wave < 4 ? stage0 : stage1) + (wave & 3) * (64 * F_OUT_PITCH);
+    if (a.y_bf16)
+      store_tile_via_lds<true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+    else
+      store_tile_via_lds<false>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+    return;
+  }
+  // unaligned output: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int m = m0 + wm * WM + 16 * j + l16;
@@ -502,7 +614,7 @@ Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
   Plan p{};
   bool fits = M * ldq < (int64_t(1) << 31);
   for (int i = 0; i < w.n_members; ++i) fits = fits && int64_t(w.m[i].rows) * w.K < (int64_t(1) << 31);
-  p.fast = aligned && fits;
+  p.fast = aligned && fits && w.Kb <= F_MAX_KB;
   if (p.fast) {
     p.m_tiles = int((M + FBM - 1) / FBM);
     int r = 0;
@@ -537,7 +649,8 @@ std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
   if (p.fast)
     snprintf(buf, sizeof(buf),
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
-             "kernel=w8a8_gemm_fast tile=%dx%d waves=8 lds=2x%dKiB buffer_load_lds xcd_groups=%d | M=%lld blocks=%d",
+             "kernel=w8a8_gemm_fast tile=%dx%d waves=8 lds=2x%dKiB (two stage arrays) buffer_load_lds "
+             "xcd_groups=%d | M=%lld blocks=%d",
              FBN, FBM, F_STAGE / 1024, GROUP_ROWS, (long long)M, p.blocks);
   else
     snprintf(buf, sizeof(buf),
@@ -566,6 +679,10 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
     a.m_tiles = p.m_tiles;
     a.rt_total = p.rt_total;
     a.y_bf16 = y_bf16 ? 1 : 0;
+    const int64_t esz = y_bf16 ? 2 : 4;
+    bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (ldy * esz) % 16 == 0;
+    for (int i = 0; i < w.n_members; ++i) vec = vec && (w.m[i].col0 * esz) % 16 == 0;
+    a.y_vec = vec ? 1 : 0;
     if (w.scale_bf16)
       hipLaunchKernelGGL(w8a8_gemm_fast_kernel<true>, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
     else

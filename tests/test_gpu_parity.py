@@ -399,3 +399,25 @@ def test_cross_arm_gate(name, hard_rms):
     assert abs(rel_s - rel_o) <= 5e-4, (rel_s, rel_o)
     if hard_rms:
         assert rel <= 0.02, rel
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_w8a8_aligned_padded_output_with_ragged_tail(out):
+    """A 16-byte multiple output row pitch takes the staged 16-byte store; the
+    member's 261 rows end inside a store chunk, 70 tokens end inside a tile, and
+    the padding around the written block keeps its canaries."""
+    t = torch()
+    m = synth.random_code_weight(105, "vec_W", 261, 384)
+    x = synth.gaussian_activations(105, "vec_X", 70, 384)
+    w = B.BlockFP8Weight([member_to_device(m)])
+    dt = t.float32 if out == "f32" else t.bfloat16
+    ld = 272 if out == "bf16" else 264  # row pitch a multiple of 16 bytes
+    buf = t.full((72, ld), 12288.0, dtype=dt, device=device())
+    y = buf[:70, :261]
+    xq, xs = O.quant_act(x)
+    banner(f"w8a8 padded output {out} ld={ld} {w.describe(B.ARM_W8A8, 70)}")
+    B.linear_w8a8(w, t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device()), out_dtype=dt, out=y)
+    b = buf.float().cpu().numpy()
+    assert np.all(b[:70, 261:] == 12288.0) and np.all(b[70:] == 12288.0)
+    om = oracle_members([m])
+    assert_within(to_np(y), O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), out == "bf16", "padded out")
