@@ -271,6 +271,8 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
   const size_t need = w8a8_workspace_bytes(w->dev, M);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(BSF8_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(BSF8_E_ALIGNMENT, "workspace not 256-byte aligned");
   const bool aligned = w->aligned16 && (reinterpret_cast<uintptr_t>(xq) % 16 == 0) && (ldq % 16 == 0);
   return launch_w8a8(w->dev, aligned, xq, ldq, xs, ldxs, M, y, y_dtype == BSF8_DT_BF16, ldy, workspace,
                      workspace_bytes, static_cast<hipStream_t>(stream));

@@ -324,6 +324,14 @@ struct FastArgs {
   int32_t rt_total;
   int32_t y_bf16;
   int32_t y_vec;   // y, ldy and every member's column offset allow 16-byte stores
+  // split-K: K blocks are cut into `splits` ranges of kb_per_split; split s of
+  // a tile writes its F32 partial tile to ws + s * M * ldws at member column
+  // wcol0[member] (multiples of 4), and a second kernel adds the partials
+  int32_t splits;
+  int32_t kb_per_split;
+  float* ws;
+  int64_t ldws;
+  int32_t wcol0[kMaxMembers];
 };
 
 __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
@@ -411,18 +419,25 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   const int xcd = b % XCDS;
   int v = b / XCDS;
   for (int y = 0; y < xcd; ++y) v += (nblk - y + XCDS - 1) / XCDS;
+  // With split-K the "rows" walked are (split, row tile) pairs, split-major,
+  // so a group's row tiles read the same K range of the same token tiles.
+  const int vr_total = a.rt_total * a.splits;
   const int gsz = GROUP_ROWS * a.m_tiles;
   const int grp = v / gsz;
   const int in_grp = v - grp * gsz;
-  const int g_rows = min(GROUP_ROWS, a.rt_total - grp * GROUP_ROWS);
-  const int R = grp * GROUP_ROWS + in_grp % g_rows;
+  const int g_rows = min(GROUP_ROWS, vr_total - grp * GROUP_ROWS);
+  const int VR = grp * GROUP_ROWS + in_grp % g_rows;
   const int mt = in_grp / g_rows;
+  const int split = VR / a.rt_total;
+  const int R = VR - split * a.rt_total;
   int mi = 0;
   while (mi + 1 < a.w.n_members && R >= a.rt0[mi + 1]) ++mi;
   const MemberDev mem = a.w.m[mi];
   const int n0 = (R - a.rt0[mi]) * FBN;
   const int m0 = mt * FBM;
   const int K = a.w.K, Kb = a.w.Kb, M = a.M;
+  const int kb_begin = split * a.kb_per_split;
+  const int kb_end = min(Kb, kb_begin + a.kb_per_split);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -510,7 +525,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     // have, and every wave is done reading `nxt`
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const bool more = kb + 1 < Kb;
+    const bool more = kb + 1 < kb_end;
     if (more) issue_scales(kb + 1, nxt);
 
     const float sw = wscale[wn][kb];
@@ -565,20 +580,23 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     }
   };
 
-  issue(0, stage0);
-  for (int kb = 0; kb < Kb; kb += 2) {
+  issue(kb_begin, stage0);
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
     step(kb, stage0, stage1);
-    if (kb + 1 < Kb) step(kb + 1, stage1, stage0);
+    if (kb + 1 < kb_end) step(kb + 1, stage1, stage0);
   }
 
   // ---- store
-  if (a.y_vec) {
+  if (a.splits > 1 || a.y_vec) {
     // the last step's (empty) copies have landed and every wave is done
     // reading both stages
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     uint8_t* buf = (wave < 4 ? stage0 : stage1) + (wave & 3) * (64 * F_OUT_PITCH);
-    if (a.y_bf16)
+    if (a.splits > 1)
+      store_tile_via_lds<false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws, a.wcol0[mi], n0 + wn * WN,
+                                mem.rows, m0 + wm * WM, M, lane);
+    else if (a.y_bf16)
       store_tile_via_lds<true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
     else
       store_tile_via_lds<false>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
@@ -599,6 +617,46 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   }
 }
 
+// Split-K partial sums: y[m, col0_i + n] = sum over s = 0 .. S-1, in that
+// order, of ws[s][m][wcol0_i + n].  One thread per 4 workspace columns.
+struct ReduceArgs {
+  const float* ws;
+  int64_t ldws;
+  int64_t split_stride;  // M * ldws
+  void* y;
+  int64_t ldy;
+  int32_t M;
+  int32_t splits;
+  int32_t y_bf16;
+  int32_t n_members;
+  int32_t wcol0[kMaxMembers + 1];  // wcol0[n_members] = ldws
+  int32_t rows[kMaxMembers];
+  int32_t col0[kMaxMembers];
+};
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
+  const int64_t c4_per_row = a.ldws / 4;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(a.M) * c4_per_row) return;
+  const int m = int(idx / c4_per_row);
+  const int wc = int(idx - int64_t(m) * c4_per_row) * 4;
+  int i = 0;
+  while (i + 1 < a.n_members && wc >= a.wcol0[i + 1]) ++i;
+  const int n = wc - a.wcol0[i];
+  const int nvalid = a.rows[i] - n;
+  if (nvalid <= 0) return;
+  const float* p = a.ws + int64_t(m) * a.ldws + wc;
+  float4 t = *reinterpret_cast<const float4*>(p);
+  for (int sp = 1; sp < a.splits; ++sp) {
+    const float4 u = *reinterpret_cast<const float4*>(p + sp * a.split_stride);
+    t.x += u.x;
+    t.y += u.y;
+    t.z += u.z;
+    t.w += u.w;
+  }
+  store4(a.y, a.y_bf16, int64_t(m) * a.ldy + a.col0[i] + n, nvalid, v4f{t.x, t.y, t.z, t.w});
+}
+
 struct Plan {
   bool fast;
   TileMap tm;         // register-staged kernel: member tiles
@@ -606,7 +664,45 @@ struct Plan {
   int rt_total;
   int m_tiles;
   int blocks;
+  int splits;         // fast kernel: K ranges per tile (1: no split)
+  int kb_per_split;
+  int64_t ldws;       // split workspace row pitch (floats)
+  int32_t wcol0[kMaxMembers + 1];
+  size_t ws_bytes;
 };
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// Split-K when the tile grid leaves compute units idle.  Cost model in units
+// of one tile-K-block step (about a microsecond on a 256x256 tile): the grid
+// runs ceil(tiles * S / CUs) rounds of ceil(Kb / S) steps, and the partials
+// cost about 0.1 step per tile and split to write and read back.
+int choose_splits(int tiles, int Kb, int cus) {
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= 8; ++sp) {
+    const int kps = (Kb + sp - 1) / sp;
+    if (sp > 1 && kps < 4) break;
+    const double rounds = double((int64_t(tiles) * sp + cus - 1) / cus);
+    const double cost = rounds * kps + (sp > 1 ? 0.1 * sp * tiles : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
 
 // The direct-copy kernel addresses each operand with 32-bit byte offsets from
 // its base, so every member and the activation block must stay below 2^31 bytes.
@@ -624,9 +720,21 @@ Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
     }
     for (int i = w.n_members; i <= kMaxMembers; ++i) p.rt0[i] = r;
     p.rt_total = r;
-    p.blocks = r * p.m_tiles;
+    p.splits = choose_splits(r * p.m_tiles, w.Kb, device_cus());
+    p.kb_per_split = (w.Kb + p.splits - 1) / p.splits;
+    p.splits = (w.Kb + p.kb_per_split - 1) / p.kb_per_split;  // no empty split
+    p.blocks = r * p.m_tiles * p.splits;
+    int64_t c = 0;
+    for (int i = 0; i < w.n_members; ++i) {
+      p.wcol0[i] = int32_t(c);
+      c += (w.m[i].rows + 3) / 4 * 4;
+    }
+    p.wcol0[w.n_members] = int32_t(c);
+    p.ldws = c;
+    p.ws_bytes = p.splits > 1 ? size_t(p.splits) * size_t(M) * size_t(c) * sizeof(float) : 0;
     return p;
   }
+  p.splits = 1;
   p.m_tiles = int((M + BM - 1) / BM);
   int t = 0;
   for (int i = 0; i < w.n_members; ++i) {
@@ -641,7 +749,12 @@ Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
 
 }  // namespace
 
-size_t w8a8_workspace_bytes(const WeightDev&, int64_t) { return 0; }
+// An upper bound over the paths a call may take: the split plan of the fast
+// kernel for packed activations (the register-staged kernel needs none).
+size_t w8a8_workspace_bytes(const WeightDev& w, int64_t M) {
+  if (M <= 0) return 0;
+  return make_plan(w, true, M, w.K).ws_bytes;
+}
 
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
   const Plan p = make_plan(w, aligned, M > 0 ? M : 1, w.K);
@@ -650,8 +763,8 @@ std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
     snprintf(buf, sizeof(buf),
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
              "kernel=w8a8_gemm_fast tile=%dx%d waves=8 lds=2x%dKiB (two stage arrays) buffer_load_lds "
-             "xcd_groups=%d | M=%lld blocks=%d",
-             FBN, FBM, F_STAGE / 1024, GROUP_ROWS, (long long)M, p.blocks);
+             "xcd_groups=%d split_k=%d | M=%lld blocks=%d",
+             FBN, FBM, F_STAGE / 1024, GROUP_ROWS, p.splits, (long long)M, p.blocks);
   else
     snprintf(buf, sizeof(buf),
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
@@ -661,7 +774,7 @@ std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
 }
 
 bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,
-                        int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void*, size_t,
+                        int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
   const Plan p = make_plan(w, aligned, M, ldq);
   if (p.blocks == 0) return BSF8_OK;
@@ -683,11 +796,41 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
     bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (ldy * esz) % 16 == 0;
     for (int i = 0; i < w.n_members; ++i) vec = vec && (w.m[i].col0 * esz) % 16 == 0;
     a.y_vec = vec ? 1 : 0;
+    a.splits = p.splits;
+    a.kb_per_split = p.kb_per_split;
+    a.ldws = p.ldws;
+    for (int i = 0; i < kMaxMembers; ++i) a.wcol0[i] = p.wcol0[i];
+    if (p.splits > 1) {
+      if (ws == nullptr || ws_bytes < p.ws_bytes || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
+        set_error("WORKSPACE: split-K needs %zu bytes of 256-byte aligned workspace", p.ws_bytes);
+        return BSF8_E_WORKSPACE;
+      }
+      a.ws = static_cast<float*>(ws);
+    }
     if (w.scale_bf16)
       hipLaunchKernelGGL(w8a8_gemm_fast_kernel<true>, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
     else
       hipLaunchKernelGGL(w8a8_gemm_fast_kernel<false>, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
-    return device_status(hipGetLastError(), "w8a8_gemm_fast launch");
+    bsf8_status st = device_status(hipGetLastError(), "w8a8_gemm_fast launch");
+    if (st != BSF8_OK || p.splits == 1) return st;
+    ReduceArgs r{};
+    r.ws = a.ws;
+    r.ldws = p.ldws;
+    r.split_stride = M * p.ldws;
+    r.y = y;
+    r.ldy = ldy;
+    r.M = int32_t(M);
+    r.splits = p.splits;
+    r.y_bf16 = y_bf16 ? 1 : 0;
+    r.n_members = w.n_members;
+    for (int i = 0; i <= kMaxMembers; ++i) r.wcol0[i] = p.wcol0[i];
+    for (int i = 0; i < w.n_members; ++i) {
+      r.rows[i] = w.m[i].rows;
+      r.col0[i] = w.m[i].col0;
+    }
+    const int64_t threads = M * (p.ldws / 4);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, r);
+    return device_status(hipGetLastError(), "splitk_reduce launch");
   }
   GemmArgs a{};
   a.w = w;

@@ -199,11 +199,15 @@ bsf8_status bsf8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K,
 
 /*
  * bsf8_workspace_size -- device workspace bytes a compute call of this handle
- * needs for M tokens on the given arm (0 when none).  The workspace holds
- * split-K partial sums and arrival counters.  Contract: zero-fill it once before
- * its first use; every call returns its counters to zero, so it can be reused
- * by later calls on the same stream.  Calls that overlap in time must not share
- * a workspace.
+ * needs for M tokens on the given arm (0 when none).  The W8A8 arm uses one
+ * when its tile grid is too small to occupy the device (few tokens against few
+ * output features, long K): K is then cut into S ranges, each range's F32
+ * partial tile goes to the workspace (S x M x N floats, N rounded up per member
+ * to a multiple of 4), and a second kernel adds them in range order, so results
+ * do not depend on timing.  The size depends on the device's compute-unit count
+ * (the current device).  No initialization is needed; every call overwrites
+ * what it reads.  Calls that overlap in time must not share a workspace.  The
+ * buffer must be 256-byte aligned.
  */
 bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, size_t* bytes);
 

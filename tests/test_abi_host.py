@@ -102,6 +102,10 @@ def test_workspace_sizes():
         assert L.bsf8_workspace_size(h, 0, 8, ctypes.byref(b)) == 0 and b.value == 0
         assert L.bsf8_workspace_size(h, 0, 0, ctypes.byref(b)) == 0 and b.value == 0
         assert L.bsf8_workspace_size(h, 1, 1024, ctypes.byref(b)) == 0
+        # 20 row tiles x 4 token tiles on 256 compute units (the count assumed
+        # when no device is present) with 40 K blocks: two K ranges of partials
+        assert b.value == 2 * 1024 * 5120 * 4
+        assert L.bsf8_workspace_size(h, 1, 8192, ctypes.byref(b)) == 0 and b.value == 0
         assert L.bsf8_workspace_size(h, 7, 8, ctypes.byref(b)) == 1
     finally:
         L.bsf8_weight_destroy(h)

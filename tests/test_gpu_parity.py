@@ -421,3 +421,24 @@ def test_w8a8_aligned_padded_output_with_ragged_tail(out):
     assert np.all(b[:70, 261:] == 12288.0) and np.all(b[70:] == 12288.0)
     om = oracle_members([m])
     assert_within(to_np(y), O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), out == "bf16", "padded out")
+
+
+def test_w8a8_split_k_is_deterministic():
+    """Two 256-row tiles against K = 8192 leave the GPU idle, so K is cut into
+    ranges summed by a second kernel in fixed order: repeated calls agree bit for
+    bit and stay within the oracle's bound."""
+    t = torch()
+    m = synth.random_code_weight(106, "splitk_W", 512, 8192)
+    x = synth.gaussian_activations(106, "splitk_X", 64, 8192)
+    w = B.BlockFP8Weight([member_to_device(m)])
+    d = w.describe(B.ARM_W8A8, 64)
+    assert "split_k=" in d and "split_k=1 " not in d, d
+    assert w.workspace_size(B.ARM_W8A8, 64) > 0
+    xq, xs = O.quant_act(x)
+    xqd, xsd = t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device())
+    banner(f"w8a8 split-K {d}")
+    ys = [B.linear_w8a8(w, xqd, xsd, out_dtype=t.float32).cpu().numpy() for _ in range(3)]
+    for y in ys[1:]:
+        assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+    om = oracle_members([m])
+    assert_within(ys[0], O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), False, "split-K")
