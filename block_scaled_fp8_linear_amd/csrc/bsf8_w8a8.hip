@@ -304,8 +304,16 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
 constexpr int FBN = 256, FBM = 256, FTHREADS = 512;
 constexpr int F_SA = FBN * KBYTES + FBM * KBYTES;  // offset of the token scales in a stage
 constexpr int F_STAGE = F_SA + FBM * 4;           // 64 KiB of operands + 1 KiB of scales
-constexpr int F_A_LOADS = FBN * KBYTES / 1024 / 8;  // 1 KiB wave loads per wave per stage: 4
-constexpr int F_B_LOADS = FBM * KBYTES / 1024 / 8;  // 4
+// Operand copies: 1 KiB wave copies (8 rows x 128 bytes) per stage, 32 weight
+// slabs and 32 token slabs, all issued by waves 0-3 in one burst at the start
+// of a K block.  Waves 0-3 share their SIMDs with waves 4-7; while a copying
+// wave waits in the vector memory queue its partner has the matrix unit to
+// itself.  (Copies spread over every wave's MFMA chain went out late: the
+// older wave of a SIMD pair takes most MFMA issue slots, so the younger one's
+// chain, and the copies in it, lag behind.)
+constexpr int F_COPIERS = 4;
+constexpr int F_A_LOADS = FBN / 8 / F_COPIERS;  // weight slabs per copying wave
+constexpr int F_B_LOADS = FBM / 8 / F_COPIERS;  // token slabs per copying wave
 constexpr int XCDS = 8;
 constexpr int GROUP_ROWS = 8;   // row tiles per L2 group
 constexpr int F_MAX_KB = 1024;  // K up to 131072 on the fast path
@@ -324,14 +332,16 @@ struct FastArgs {
   int32_t rt_total;
   int32_t y_bf16;
   int32_t y_vec;   // y, ldy and every member's column offset allow 16-byte stores
-  // split-K: K blocks are cut into `splits` ranges of kb_per_split; split s of
-  // a tile writes its F32 partial tile to ws + s * M * ldws at member column
-  // wcol0[member] (multiples of 4), and a second kernel adds the partials
+  // split-K for the row tiles from rt_split0 on: their K blocks are cut into
+  // `splits` ranges of kb_per_split; split s of tile (R, mt) writes its F32
+  // partial tile to ws + s * M * ldws, columns (R - rt_split0) * FBN + [0, FBN),
+  // and a second kernel adds the partials.  Row tiles below rt_split0 run
+  // whole and write y.
   int32_t splits;
   int32_t kb_per_split;
+  int32_t rt_split0;
   float* ws;
   int64_t ldws;
-  int32_t wcol0[kMaxMembers];
 };
 
 __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
@@ -410,34 +420,45 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[F_STAGE];
   __shared__ float wscale[2][F_MAX_KB];   // the block's two rows of the weight scale grid
 
-  // ---- XCD-aware tile order: blocks are dealt to the 8 XCDs round robin; give
-  // every XCD a contiguous run of tiles, walked in groups of GROUP_ROWS row
-  // tiles x all token tiles so that concurrently running blocks share operands
-  // in that XCD's L2.
+  // ---- XCD-aware tile order.  Blocks are dealt to the 8 XCDs round robin, and
+  // each XCD runs its blocks in order.  Two kinds of work are dealt evenly to
+  // every XCD, whole tiles first and split tiles (K ranges of the last row
+  // tiles) after them; within each kind an XCD walks a contiguous run of
+  // tiles in groups of GROUP_ROWS row tiles x all token tiles, so blocks that
+  // run together share operands in that XCD's L2.  Split work walks
+  // (split, row tile) pairs split-major: a group shares one K range.
   const int nblk = gridDim.x;
   const int b = blockIdx.x;
   const int xcd = b % XCDS;
-  int v = b / XCDS;
-  for (int y = 0; y < xcd; ++y) v += (nblk - y + XCDS - 1) / XCDS;
-  // With split-K the "rows" walked are (split, row tile) pairs, split-major,
-  // so a group's row tiles read the same K range of the same token tiles.
-  const int vr_total = a.rt_total * a.splits;
+  const int l = b / XCDS;
+  const int split_rows = a.rt_total - a.rt_split0;
+  const int n_whole = a.rt_split0 * a.m_tiles;
+  int start_whole = 0, start_split = 0;
+  for (int y = 0; y < xcd; ++y) {
+    const int ny = (nblk - y + XCDS - 1) / XCDS, nwy = (n_whole - y + XCDS - 1) / XCDS;
+    start_whole += nwy;
+    start_split += ny - nwy;
+  }
+  const int n_whole_here = (n_whole - xcd + XCDS - 1) / XCDS;
+  const bool whole = l < n_whole_here;
+  const int v = whole ? start_whole + l : start_split + (l - n_whole_here);
+  const int vr_total = whole ? a.rt_split0 : split_rows * a.splits;
   const int gsz = GROUP_ROWS * a.m_tiles;
   const int grp = v / gsz;
   const int in_grp = v - grp * gsz;
   const int g_rows = min(GROUP_ROWS, vr_total - grp * GROUP_ROWS);
   const int VR = grp * GROUP_ROWS + in_grp % g_rows;
   const int mt = in_grp / g_rows;
-  const int split = VR / a.rt_total;
-  const int R = VR - split * a.rt_total;
+  const int split = whole ? 0 : VR / split_rows;
+  const int R = whole ? VR : a.rt_split0 + (VR - split * split_rows);
   int mi = 0;
   while (mi + 1 < a.w.n_members && R >= a.rt0[mi + 1]) ++mi;
   const MemberDev mem = a.w.m[mi];
   const int n0 = (R - a.rt0[mi]) * FBN;
   const int m0 = mt * FBM;
   const int K = a.w.K, Kb = a.w.Kb, M = a.M;
-  const int kb_begin = split * a.kb_per_split;
-  const int kb_end = min(Kb, kb_begin + a.kb_per_split);
+  const int kb_begin = whole ? 0 : split * a.kb_per_split;
+  const int kb_end = whole ? Kb : min(Kb, kb_begin + a.kb_per_split);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -466,25 +487,25 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   const int crow = lane >> 3;
   const int ch_even = swz_pos(crow, lane & 7) * 16;
   const int ch_odd = swz_pos(crow + 8, lane & 7) * 16;
-  const int a_row0 = n0 + wave * F_A_LOADS * 8 + crow;   // row of slab i is a_row0 + 8 i
-  const int b_row0 = m0 + wave * F_B_LOADS * 8 + crow;
+  const int cw = wave;              // copier index (valid when copier)
+  const bool copier = wave < F_COPIERS;
+  const int a_row0 = n0 + cw * F_A_LOADS * 8 + crow;   // row of slab i is a_row0 + 8 i
+  const int b_row0 = m0 + cw * F_B_LOADS * 8 + crow;
   // Copy number c (0 .. F_A_LOADS + F_B_LOADS - 1) of K block kb into a stage:
-  // the first F_A_LOADS are weight slabs, the rest token slabs.  With
-  // live == false every lane gets the past-the-end offset, so the copy moves
-  // no data (it fills the unused stage with zeros) and needs no branch.
-  auto issue_one = [&](int kb, uint8_t* base, int c, bool live) {
+  // the first F_A_LOADS are weight slabs, the rest token slabs.
+  auto issue_one = [&](int kb, uint8_t* base, int c) {
     if (c < F_A_LOADS) {
       const int i = c;
-      const int ch = ((wave * F_A_LOADS + i) & 1) ? ch_odd : ch_even;
-      const bool ok = live && (a_row0 + 8 * i < mem.rows) && (kb * KBYTES + ch < K);
+      const int ch = ((cw * F_A_LOADS + i) & 1) ? ch_odd : ch_even;
+      const bool ok = (a_row0 + 8 * i < mem.rows) && (kb * KBYTES + ch < K);
       const int off = ok ? (a_row0 + 8 * i) * K + kb * KBYTES + ch : int(a_bytes);
-      bsf8_raw_buffer_load_lds(ra, (lds_u32_ptr)(base + (wave * F_A_LOADS + i) * 1024), 16, off, 0, 0, 0);
+      bsf8_raw_buffer_load_lds(ra, (lds_u32_ptr)(base + (cw * F_A_LOADS + i) * 1024), 16, off, 0, 0, 0);
     } else {
       const int i = c - F_A_LOADS;
-      const int ch = ((wave * F_B_LOADS + i) & 1) ? ch_odd : ch_even;
-      const bool ok = live && (b_row0 + 8 * i < M) && (kb * KBYTES + ch < K);
+      const int ch = ((cw * F_B_LOADS + i) & 1) ? ch_odd : ch_even;
+      const bool ok = (b_row0 + 8 * i < M) && (kb * KBYTES + ch < K);
       const int off = ok ? (b_row0 + 8 * i) * int(a.ldq) + kb * KBYTES + ch : int(b_bytes);
-      bsf8_raw_buffer_load_lds(rb, (lds_u32_ptr)(base + FBN * KBYTES + (wave * F_B_LOADS + i) * 1024), 16, off, 0,
+      bsf8_raw_buffer_load_lds(rb, (lds_u32_ptr)(base + FBN * KBYTES + (cw * F_B_LOADS + i) * 1024), 16, off, 0,
                                0, 0);
     }
   };
@@ -495,8 +516,10 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     }
   };
   auto issue = [&](int kb, uint8_t* base) {
+    if (copier) {
 #pragma unroll
-    for (int c = 0; c < F_A_LOADS + F_B_LOADS; ++c) issue_one(kb, base, c, true);
+      for (int c = 0; c < F_A_LOADS + F_B_LOADS; ++c) issue_one(kb, base, c);
+    }
     issue_scales(kb, base);
   };
 
@@ -527,6 +550,10 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     __syncthreads();
     const bool more = kb + 1 < kb_end;
     if (more) issue_scales(kb + 1, nxt);
+    if (copier && more) {
+#pragma unroll
+      for (int c = 0; c < F_A_LOADS + F_B_LOADS; ++c) issue_one(kb + 1, nxt, c);
+    }
 
     const float sw = wscale[wn][kb];
     const float4 sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
@@ -556,7 +583,6 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     // without wait states, and the A fragment of row tile i + 1 is read from LDS
     // while tile i's MFMAs run.
     constexpr int LAG = 2;
-    constexpr int COPY_EVERY = 2;
     v4f part[LAG + 1];
 #pragma unroll
     for (int q = 0; q < TI * TJ + LAG; ++q) {
@@ -571,10 +597,6 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
         const int c = q - LAG, ci = c / TJ, cj = c % TJ;
         acc[ci][cj] += part[c % (LAG + 1)] * s[cj];
       }
-      // the next K block's copies go out one per COPY_EVERY MFMAs: issued in one
-      // burst they queue in the vector memory unit and hold the wave there
-      // before its first MFMA
-      if (q % COPY_EVERY == 0 && q / COPY_EVERY < F_A_LOADS + F_B_LOADS) issue_one(kb + 1, nxt, q / COPY_EVERY, more);
       // (the scheduling barriers keep each MFMA ahead of the FMAs issued after it)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -587,15 +609,14 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   }
 
   // ---- store
-  if (a.splits > 1 || a.y_vec) {
-    // the last step's (empty) copies have landed and every wave is done
-    // reading both stages
+  if (!whole || a.y_vec) {
+    // every wave is done reading both stages
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     uint8_t* buf = (wave < 4 ? stage0 : stage1) + (wave & 3) * (64 * F_OUT_PITCH);
-    if (a.splits > 1)
-      store_tile_via_lds<false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws, a.wcol0[mi], n0 + wn * WN,
-                                mem.rows, m0 + wm * WM, M, lane);
+    if (!whole)
+      store_tile_via_lds<false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws,
+                                int64_t(R - a.rt_split0) * FBN - n0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
     else if (a.y_bf16)
       store_tile_via_lds<true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
     else
@@ -617,8 +638,9 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   }
 }
 
-// Split-K partial sums: y[m, col0_i + n] = sum over s = 0 .. S-1, in that
-// order, of ws[s][m][wcol0_i + n].  One thread per 4 workspace columns.
+// Split-K partial sums: for workspace column c (row tile R = rt_split0 +
+// c / FBN, member i holding R, row n of member i), y[m, col0_i + n] = sum over
+// s = 0 .. S-1, in that order, of ws[s][m][c].  One thread per 4 columns.
 struct ReduceArgs {
   const float* ws;
   int64_t ldws;
@@ -629,7 +651,8 @@ struct ReduceArgs {
   int32_t splits;
   int32_t y_bf16;
   int32_t n_members;
-  int32_t wcol0[kMaxMembers + 1];  // wcol0[n_members] = ldws
+  int32_t rt_split0;
+  int32_t rt0[kMaxMembers + 1];
   int32_t rows[kMaxMembers];
   int32_t col0[kMaxMembers];
 };
@@ -639,13 +662,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= int64_t(a.M) * c4_per_row) return;
   const int m = int(idx / c4_per_row);
-  const int wc = int(idx - int64_t(m) * c4_per_row) * 4;
+  const int c = int(idx - int64_t(m) * c4_per_row) * 4;
+  const int R = a.rt_split0 + c / FBN;
   int i = 0;
-  while (i + 1 < a.n_members && wc >= a.wcol0[i + 1]) ++i;
-  const int n = wc - a.wcol0[i];
+  while (i + 1 < a.n_members && R >= a.rt0[i + 1]) ++i;
+  const int n = (R - a.rt0[i]) * FBN + c % FBN;
   const int nvalid = a.rows[i] - n;
   if (nvalid <= 0) return;
-  const float* p = a.ws + int64_t(m) * a.ldws + wc;
+  const float* p = a.ws + int64_t(m) * a.ldws + c;
   float4 t = *reinterpret_cast<const float4*>(p);
   for (int sp = 1; sp < a.splits; ++sp) {
     const float4 u = *reinterpret_cast<const float4*>(p + sp * a.split_stride);
@@ -664,10 +688,10 @@ struct Plan {
   int rt_total;
   int m_tiles;
   int blocks;
-  int splits;         // fast kernel: K ranges per tile (1: no split)
+  int splits;         // fast kernel: K ranges of each split row tile (1: none)
   int kb_per_split;
+  int rt_split0;      // first split row tile (rt_total when none)
   int64_t ldws;       // split workspace row pitch (floats)
-  int32_t wcol0[kMaxMembers + 1];
   size_t ws_bytes;
 };
 
@@ -684,21 +708,35 @@ int device_cus() {
   return cache[dev];
 }
 
-// Split-K when the tile grid leaves compute units idle.  Cost model in units
-// of one tile-K-block step (about a microsecond on a 256x256 tile): the grid
-// runs ceil(tiles * S / CUs) rounds of ceil(Kb / S) steps, and the partials
-// cost about 0.1 step per tile and split to write and read back.
-int choose_splits(int tiles, int Kb, int cus) {
-  int best = 1;
-  double best_cost = 1e30;
-  for (int sp = 1; sp <= 8; ++sp) {
+// Split-K where the tile grid leaves compute units idle: every tile when there
+// are fewer tiles than compute units, else the row tiles of the last, partly
+// filled round.  Cost model in units of one tile-K-block step (about 1.7 us of
+// GPU time at full occupancy): whole tiles run ceil(n / CUs) rounds of Kb
+// steps, split tiles ceil(n * S / CUs) rounds of ceil(Kb / S) steps, and each
+// split partial tile costs about 0.06 step to write and read back, plus two
+// steps for the second kernel.
+struct SplitChoice {
+  int splits;
+  int split_rows;
+};
+
+SplitChoice choose_splits(int rt_total, int m_tiles, int Kb, int cus) {
+  const int tiles = rt_total * m_tiles;
+  const int tail = tiles <= cus ? tiles : tiles % cus;
+  SplitChoice best{1, 0};
+  if (tail == 0) return best;
+  const int split_rows = tiles <= cus ? rt_total : (tail + m_tiles - 1) / m_tiles;
+  const int whole = (rt_total - split_rows) * m_tiles;
+  const int split_tiles = split_rows * m_tiles;
+  double best_cost = double((tiles + cus - 1) / cus) * Kb;
+  for (int sp = 2; sp <= 8; ++sp) {
     const int kps = (Kb + sp - 1) / sp;
-    if (sp > 1 && kps < 4) break;
-    const double rounds = double((int64_t(tiles) * sp + cus - 1) / cus);
-    const double cost = rounds * kps + (sp > 1 ? 0.1 * sp * tiles : 0.0);
+    if (kps < 4) break;
+    const double cost = double((whole + cus - 1) / cus) * Kb +
+                        double((int64_t(split_tiles) * sp + cus - 1) / cus) * kps + 0.06 * sp * split_tiles + 2.0;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
-      best = sp;
+      best = SplitChoice{sp, split_rows};
     }
   }
   return best;
@@ -720,18 +758,14 @@ Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
     }
     for (int i = w.n_members; i <= kMaxMembers; ++i) p.rt0[i] = r;
     p.rt_total = r;
-    p.splits = choose_splits(r * p.m_tiles, w.Kb, device_cus());
-    p.kb_per_split = (w.Kb + p.splits - 1) / p.splits;
+    const SplitChoice sc = choose_splits(r, p.m_tiles, w.Kb, device_cus());
+    p.kb_per_split = (w.Kb + sc.splits - 1) / sc.splits;
     p.splits = (w.Kb + p.kb_per_split - 1) / p.kb_per_split;  // no empty split
-    p.blocks = r * p.m_tiles * p.splits;
-    int64_t c = 0;
-    for (int i = 0; i < w.n_members; ++i) {
-      p.wcol0[i] = int32_t(c);
-      c += (w.m[i].rows + 3) / 4 * 4;
-    }
-    p.wcol0[w.n_members] = int32_t(c);
-    p.ldws = c;
-    p.ws_bytes = p.splits > 1 ? size_t(p.splits) * size_t(M) * size_t(c) * sizeof(float) : 0;
+    const int split_rows = p.splits > 1 ? sc.split_rows : 0;
+    p.rt_split0 = r - split_rows;
+    p.ldws = int64_t(split_rows) * FBN;
+    p.blocks = p.rt_split0 * p.m_tiles + split_rows * p.m_tiles * p.splits;
+    p.ws_bytes = p.splits > 1 ? size_t(p.splits) * size_t(M) * size_t(p.ldws) * sizeof(float) : 0;
     return p;
   }
   p.splits = 1;
@@ -763,8 +797,8 @@ std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
     snprintf(buf, sizeof(buf),
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
              "kernel=w8a8_gemm_fast tile=%dx%d waves=8 lds=2x%dKiB (two stage arrays) buffer_load_lds "
-             "xcd_groups=%d split_k=%d | M=%lld blocks=%d",
-             FBN, FBM, F_STAGE / 1024, GROUP_ROWS, p.splits, (long long)M, p.blocks);
+             "xcd_groups=%d split_k=%d split_row_tiles=%d | M=%lld blocks=%d",
+             FBN, FBM, F_STAGE / 1024, GROUP_ROWS, p.splits, p.rt_total - p.rt_split0, (long long)M, p.blocks);
   else
     snprintf(buf, sizeof(buf),
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
@@ -798,8 +832,8 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
     a.y_vec = vec ? 1 : 0;
     a.splits = p.splits;
     a.kb_per_split = p.kb_per_split;
+    a.rt_split0 = p.rt_split0;
     a.ldws = p.ldws;
-    for (int i = 0; i < kMaxMembers; ++i) a.wcol0[i] = p.wcol0[i];
     if (p.splits > 1) {
       if (ws == nullptr || ws_bytes < p.ws_bytes || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
         set_error("WORKSPACE: split-K needs %zu bytes of 256-byte aligned workspace", p.ws_bytes);
@@ -823,7 +857,8 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
     r.splits = p.splits;
     r.y_bf16 = y_bf16 ? 1 : 0;
     r.n_members = w.n_members;
-    for (int i = 0; i <= kMaxMembers; ++i) r.wcol0[i] = p.wcol0[i];
+    r.rt_split0 = p.rt_split0;
+    for (int i = 0; i <= kMaxMembers; ++i) r.rt0[i] = p.rt0[i];
     for (int i = 0; i < w.n_members; ++i) {
       r.rows[i] = w.m[i].rows;
       r.col0[i] = w.m[i].col0;

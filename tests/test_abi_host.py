@@ -101,11 +101,17 @@ def test_workspace_sizes():
         b = ctypes.c_size_t()
         assert L.bsf8_workspace_size(h, 0, 8, ctypes.byref(b)) == 0 and b.value == 0
         assert L.bsf8_workspace_size(h, 0, 0, ctypes.byref(b)) == 0 and b.value == 0
-        assert L.bsf8_workspace_size(h, 1, 1024, ctypes.byref(b)) == 0
-        # 20 row tiles x 4 token tiles on 256 compute units (the count assumed
-        # when no device is present) with 40 K blocks: two K ranges of partials
-        assert b.value == 2 * 1024 * 5120 * 4
-        assert L.bsf8_workspace_size(h, 1, 8192, ctypes.byref(b)) == 0 and b.value == 0
+        # W8A8 split-K: the workspace holds S partial tiles of every split row
+        # tile; its size agrees with the plan the handle describes (256 compute
+        # units are assumed when no device is present)
+        for M in (1024, 8192, 4):
+            assert L.bsf8_workspace_size(h, 1, M, ctypes.byref(b)) == 0
+            d = L.bsf8_describe(h, 1, M).decode()
+            sk = int(re.search(r"split_k=(\d+)", d).group(1))
+            rows = int(re.search(r"split_row_tiles=(\d+)", d).group(1))
+            assert b.value == (sk * M * rows * 256 * 4 if sk > 1 else 0), (M, d)
+        # 20 row tiles x 4 token tiles < 256 units: every tile is split
+        assert "split_k=3 split_row_tiles=20" in L.bsf8_describe(h, 1, 1024).decode()
         assert L.bsf8_workspace_size(h, 7, 8, ctypes.byref(b)) == 1
     finally:
         L.bsf8_weight_destroy(h)
