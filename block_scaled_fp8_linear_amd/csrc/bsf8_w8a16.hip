@@ -45,6 +45,10 @@
 typedef int bsf8_w16_v4i __attribute__((ext_vector_type(4)));
 __device__ bsf8_w16_v4i bsf8_raw_buffer_load_b128(bsf8_w16_v4i rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ int bsf8_raw_buffer_load_b32(bsf8_w16_v4i rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.i32");
+__device__ short bsf8_raw_buffer_load_b16(bsf8_w16_v4i rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.i16");
 
 namespace bsf8 {
 namespace {
@@ -346,6 +350,232 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Few tokens (M <= 8, 16-byte aligned operands): the decode-size kernel.  The
+// general kernel's loads put each lane on one weight row (16 rows x 64 bytes
+// per instruction) and its activation loads fill 16 token lanes even when
+// most are past M; at decode sizes those load patterns, not the arithmetic,
+// set its speed.  Here, per wave and K chunk:
+//  * weights are loaded by 8 lanes per 128-byte row (full cache lines per
+//    instruction), written to a wave-private LDS buffer when their chunk comes
+//    up and read back in the MFMA layout;
+//  * activations are loaded compactly (32 lanes per F32 token, 16 per BF16
+//    token), each lane splits only what it loaded, and the BF16 terms go to a
+//    wave-private LDS scratch in fragment order; tokens past M read a zero row;
+//  * a ring of SM_DEPTH chunks of both operands is in flight in registers;
+//    loads retire in issue order, so each slot's loads are issued together and
+//    slots in chunk order (scheduling barriers keep them grouped), and chunks
+//    past the wave's range get past-the-end offsets (zeros, no traffic).
+//    (Copies straight into LDS would save the registers, but the compiler then
+//    waits for every copy in flight before any other LDS access of the wave.)
+//  * the chunk scales of the wave's range are loaded once, first.
+// In a chunk, lane group gq owns the 32 contiguous K bytes [32 gq, 32 gq + 32)
+// of both operands, and K-step s of the 16x16x32 MFMA the 8 at 32 gq + 8 s.
+// LDS layouts (16-byte pieces, bank-conflict free for the fragment reads):
+//  weight buffer: row r of the wave's 32 at r * 128, piece p at p ^ ((r >> 1) & 7);
+//  activation scratch: term u, token t at u * SM_TERM_BYTES + t * 256, piece p at p ^ t.
+// The MFMA sequence, per-chunk scaling and the wave-order reduction are those
+// of the general kernel.
+// ---------------------------------------------------------------------------
+constexpr int SM_MAXM = 8;
+constexpr int SM_ZERO_ROW = SM_MAXM;           // scratch row that stays zero
+constexpr int SM_ROW_BYTES = CHUNK * 2;        // one token's chunk as BF16
+constexpr int SM_TERM_BYTES = (SM_MAXM + 1) * SM_ROW_BYTES;
+constexpr int SM_DEPTH = 3;
+constexpr int SM_SCALE_REGS = 2;               // chunk scales per wave: up to 128 (K up to 131072 with 8 waves)
+constexpr int SM_WBUF = ROWS * CHUNK;          // a wave's weight bytes per chunk: 4 KiB
+
+template <bool XBF16, bool SBF16, int NXI>
+__global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
+  constexpr int NT = XBF16 ? 1 : TERMS;          // a BF16 activation is its own single term
+  constexpr int LPT = XBF16 ? 16 : 32;           // lanes per token in a compact load
+  constexpr int EPL = XBF16 ? 8 : 4;             // activations per lane in a compact load
+  __shared__ __attribute__((aligned(1024))) uint8_t wbuf[WAVES][SM_WBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t scratch[WAVES][NT * SM_TERM_BYTES];
+  static_assert(sizeof(float) * WAVES * RT * 64 * 4 <= sizeof(uint8_t) * WAVES * SM_WBUF, "reduction fits the buffers");
+
+  const int tile = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
+  const int rtile = tile - a.tm.tile0[mi];
+  const MemberDev mem = a.w.m[mi];
+  const int K = a.w.K, Kb = a.w.Kb, M = a.M;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int c_begin = min(Kb, wave * a.chunks_per_wave);
+  const int c_end = min(Kb, c_begin + a.chunks_per_wave);
+  const int64_t srow0 = int64_t((rtile * ROWS) >> 7) * Kb;   // both row tiles share one scale row
+
+  uint8_t* sc = scratch[wave];
+  for (int i = lane; i < NT * SM_TERM_BYTES / 16; i += 64) reinterpret_cast<uint4*>(sc)[i] = make_uint4(0, 0, 0, 0);
+
+  const int xt = lane / LPT;                     // token within a compact load
+  const int xk = (lane % LPT) * EPL;             // first K element of the lane in the chunk
+  const int frow = l16 < M ? l16 : SM_ZERO_ROW;  // scratch row read for this lane's token
+  // weight loads: lane L takes piece L & 7 of row (L >> 3) + 8 q of the wave's 32
+  const int crow = lane >> 3;
+  const int cpiece = lane & 7;
+  uint8_t* const wb = wbuf[wave];
+
+  v4f acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 xr[SM_DEPTH][NXI];
+  uint4 wr[SM_DEPTH][2 * RT];
+  const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
+  const uint32_t x_esz = XBF16 ? 2u : 4u;
+  const uint32_t x_bytes = uint32_t(M) * uint32_t(a.ldx) * x_esz;
+  const uint32_t s_esz = SBF16 ? 2u : 4u;
+  const uint32_t s_bytes = uint32_t((mem.rows + 127) >> 7) * uint32_t(Kb) * s_esz;
+  const v4i rw = make_rsrc(mem.w, w_bytes);
+  const v4i rx = make_rsrc(a.x, x_bytes);
+  const v4i rs = make_rsrc(mem.s, s_bytes);
+
+  // The weight scales of this wave's chunks, one per lane (chunk c_begin +
+  // 64 h + lane), loaded first: as the oldest loads, waiting for them never
+  // waits for a ring slot.  Raw bits; converted where used.
+  uint32_t sraw[SM_SCALE_REGS];
+#pragma unroll
+  for (int h = 0; h < SM_SCALE_REGS; ++h) {
+    const int c = c_begin + 64 * h + lane;
+    const int so = c < c_end ? int((srow0 + c) * s_esz) : int(s_bytes);
+    sraw[h] = SBF16 ? uint32_t(uint16_t(bsf8_raw_buffer_load_b16(rs, so, 0, 0)))
+                    : uint32_t(bsf8_raw_buffer_load_b32(rs, so, 0, 0));
+  }
+  auto chunk_scale = [&](int c) {   // c - c_begin is wave-uniform
+    const int i = c - c_begin;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int h = 0; h < SM_SCALE_REGS; ++h)
+      if ((i >> 6) == h) bits = __builtin_amdgcn_readlane(sraw[h], i & 63);
+    return c < c_end ? __uint_as_float(SBF16 ? bits << 16 : bits) : 0.f;
+  };
+
+  auto issue = [&](int c, int d) {
+    const bool live = c < c_end;
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) {
+      const int t = i * (64 / LPT) + xt;
+      const int k = c * CHUNK + xk;
+      const bool ok = live && t < M && k < K;
+      xr[d][i] = as_u4(bsf8_raw_buffer_load_b128(rx, ok ? int((int64_t(t) * a.ldx + k) * x_esz) : int(x_bytes), 0, 0));
+    }
+#pragma unroll
+    for (int q = 0; q < 2 * RT; ++q) {
+      const int row = rtile * ROWS + 8 * q + crow;
+      const int k = c * CHUNK + 16 * cpiece;
+      const bool ok = live && row < mem.rows && k < K;
+      wr[d][q] = as_u4(bsf8_raw_buffer_load_b128(rw, ok ? row * K + k : int(w_bytes), 0, 0));
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < SM_DEPTH; ++d) {
+    issue(c_begin + d, d);
+    __builtin_amdgcn_sched_barrier(0);   // keep the slots in chunk order
+  }
+  for (int c0 = c_begin; c0 < c_end; c0 += SM_DEPTH) {
+#pragma unroll
+    for (int d = 0; d < SM_DEPTH; ++d) {
+      const int c = c0 + d;
+      const float sw = chunk_scale(c);
+      // split this lane's activations and write the terms in fragment order
+#pragma unroll
+      for (int i = 0; i < NXI; ++i) {
+        const int t = i * (64 / LPT) + xt;
+        const int pos = ((xk >> 3) ^ t) * 16 + (xk & 7) * 2;
+        uint8_t* dst = sc + t * SM_ROW_BYTES + pos;
+        if (XBF16) {
+          *reinterpret_cast<uint4*>(dst) = xr[d][i];
+        } else {
+          const float v[4] = {__uint_as_float(xr[d][i].x), __uint_as_float(xr[d][i].y), __uint_as_float(xr[d][i].z),
+                              __uint_as_float(xr[d][i].w)};
+          uint32_t h[4], m[4], l[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t hb = __float_as_uint(v[j]) & 0xFFFF0000u;
+            const float r1 = v[j] - __uint_as_float(hb);
+            const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+            h[j] = hb;
+            m[j] = mb;
+            l[j] = __float_as_uint(r1 - __uint_as_float(mb));
+          }
+          *reinterpret_cast<uint2*>(dst) = make_uint2((h[0] >> 16) | (h[1] & 0xFFFF0000u), (h[2] >> 16) | (h[3] & 0xFFFF0000u));
+          *reinterpret_cast<uint2*>(dst + SM_TERM_BYTES) =
+              make_uint2((m[0] >> 16) | (m[1] & 0xFFFF0000u), (m[2] >> 16) | (m[3] & 0xFFFF0000u));
+          *reinterpret_cast<uint2*>(dst + 2 * SM_TERM_BYTES) =
+              make_uint2((l[0] >> 16) | (l[1] & 0xFFFF0000u), (l[2] >> 16) | (l[3] & 0xFFFF0000u));
+        }
+      }
+      // B fragments: K-step st holds K = 32 gq + 8 st + j
+      v8bf b[NT][STEPS];
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        const int kc = 4 * gq + st;
+        const uint8_t* srcp = sc + frow * SM_ROW_BYTES + ((kc ^ frow) * 16);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) b[u][st] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(srcp + u * SM_TERM_BYTES));
+      }
+      // weights: to LDS in rows, back in the MFMA layout
+#pragma unroll
+      for (int q = 0; q < 2 * RT; ++q) {
+        const int rr = 8 * q + crow;
+        *reinterpret_cast<uint4*>(wb + rr * CHUNK + ((cpiece ^ ((rr >> 1) & 7)) * 16)) = wr[d][q];
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int rr = 16 * t + l16;
+        const int sw8 = (rr >> 1) & 7;
+        const uint4 lo = *reinterpret_cast<const uint4*>(wb + rr * CHUNK + (((2 * gq) ^ sw8) * 16));
+        const uint4 hi = *reinterpret_cast<const uint4*>(wb + rr * CHUNK + (((2 * gq + 1) ^ sw8) * 16));
+        const v8bf af[STEPS] = {cvt8(lo.x, lo.y), cvt8(lo.z, lo.w), cvt8(hi.x, hi.y), cvt8(hi.z, hi.w)};
+        v4f pt[NT];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) pt[u] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+          for (int u = 0; u < NT; ++u) pt[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], b[u][st], pt[u], 0, 0, 0);
+        v4f tsum = pt[0];
+#pragma unroll
+        for (int u = 1; u < NT; ++u) tsum += pt[u];
+        acc[t] += tsum * sw;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(c + SM_DEPTH, d);   // refill this slot
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // the ring's last refills (chunks past the range) are still in flight, and
+  // the reduction reuses the weight buffers once every wave is done with them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // ---- add the 8 waves' partial tiles in wave order and store
+  float(*red)[RT][64][4] = reinterpret_cast<float(*)[RT][64][4]>(&wbuf[0][0]);
+#pragma unroll
+  for (int t = 0; t < RT; ++t) *reinterpret_cast<v4f*>(&red[wave][t][lane][0]) = acc[t];
+  __syncthreads();
+  const int t = tid >> 8;
+  const int ln = (tid >> 2) & 63;
+  const int r = tid & 3;
+  float sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) sum += red[w][t][ln][r];
+  const int row = rtile * ROWS + t * 16 + 4 * (ln >> 4) + r;
+  const int mo = ln & 15;
+  if (row < mem.rows && mo < M) {
+    const int64_t off = int64_t(mo) * a.ldy + mem.col0 + row;
+    if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
+    else static_cast<float*>(a.y)[off] = sum;
+  }
+}
+
 struct Plan {
   TileMap tm;
   int col_tiles;
@@ -375,11 +605,14 @@ size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   const Plan p = make_plan(w, M > 0 ? M : 1);
   char buf[320];
+  const bool small = aligned && M >= 1 && M <= SM_MAXM;
   snprintf(buf, sizeof(buf),
            "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
-           "mfma_f32_16x16x32_bf16 | kernel=w8a16 rows=%d tokens=%d waves=%d (in-block split-K, %d chunks/wave) "
+           "mfma_f32_16x16x32_bf16 | kernel=%s rows=%d tokens=%d waves=%d (in-block split-K, %d chunks/wave%s) "
            "path=%s | M=%lld blocks=%d",
-           ROWS, COLS, WAVES, p.chunks_per_wave, aligned ? "aligned16" : "bytewise", (long long)M, p.tiles);
+           small ? "w8a16_small_m" : "w8a16", ROWS, small ? SM_MAXM : COLS, WAVES, p.chunks_per_wave,
+           small ? ", 3-chunk load ring, compact activations split in LDS" : "", aligned ? "aligned16" : "bytewise",
+           (long long)M, p.tiles);
   return buf;
 }
 
@@ -409,7 +642,17 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   a.y_bf16 = y_bf16 ? 1 : 0;
   auto kern = w8a16_kernel<true, false, true>;
   const bool sb = w.scale_bf16 != 0;
-  if (aligned) {
+  if (aligned && M <= SM_MAXM) {
+    // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load
+    if (x_bf16) {
+      if (M <= 4) kern = sb ? w8a16_small_m_kernel<true, true, 1> : w8a16_small_m_kernel<true, false, 1>;
+      else kern = sb ? w8a16_small_m_kernel<true, true, 2> : w8a16_small_m_kernel<true, false, 2>;
+    } else {
+      if (M <= 2) kern = sb ? w8a16_small_m_kernel<false, true, 1> : w8a16_small_m_kernel<false, false, 1>;
+      else if (M <= 4) kern = sb ? w8a16_small_m_kernel<false, true, 2> : w8a16_small_m_kernel<false, false, 2>;
+      else kern = sb ? w8a16_small_m_kernel<false, true, 4> : w8a16_small_m_kernel<false, false, 4>;
+    }
+  } else if (aligned) {
     if (x_bf16) kern = sb ? w8a16_kernel<true, true, true> : w8a16_kernel<true, true, false>;
     else kern = sb ? w8a16_kernel<true, false, true> : w8a16_kernel<true, false, false>;
   } else {
