@@ -8,16 +8,19 @@ quantize X_gate_up -> W8A8 GEMM on the fused gate/up weight (two members of
 [17408, 5120]) -> quantize X_down -> W8A8 GEMM on the down weight
 [5120, 17408], BF16 outputs.  ``value`` is the step's algorithmic FLOP rate,
 2*M*N*K summed over both GEMMs, over the step time (quantization included).
+The step runs as one HIP graph of its four calls, replayed back to back; the
+timed region is bracketed by HIP events on the replay stream.
 
 The same JSON line also carries:
-* ``roofline``: the gate/up GEMM, FLOPs per launch over its mean launch time
-  (HIP events on the launching stream), against the dense FP8 MFMA peak;
+* ``roofline``: the gate/up GEMM, FLOPs per launch over its mean device time
+  (a graph of 20 back-to-back launches, timed with HIP events on the
+  replaying stream), against the dense FP8 MFMA peak;
 * ``decode_gemv``: the W8A16/F32 arm at M in {1, 4, 8} on W [5120, 5120],
   rotating through >= 512 MiB of weight copies so the 256 MB Infinity Cache
   cannot serve them, with an HBM roofline on algorithmic bytes;
 * ``large_prefill``: the W8A8 GEMM at M=8192, K=7168, N=18432;
-* ``cpu_baseline``: the oracle (NumPy) on the host cores, on a bounded sample of
-  the same prefill workload.
+* ``cpu_baseline``: the oracle (NumPy) on the host cores, running the same
+  prefill step for about ten seconds.
 
 Inputs are seeded synthetic data (``synth``) already resident in HBM before
 timing starts.
@@ -73,37 +76,34 @@ def parse():
     return ap.parse_args()
 
 
-class KernelTimer:
-    """Mean duration of each named launch, from HIP event pairs on the current stream.
+def graph_of(torch, fn, reps=1):
+    """A HIP graph of ``reps`` back-to-back calls of ``fn``.
 
-    With ``pad`` the launch is preceded by a device-side spin, so the host has
-    queued the start event, the kernel and the stop event before the GPU gets to
-    them: the pair then brackets the kernel alone, not the host's launch latency
-    (which exceeds a few-microsecond kernel).
+    Every buffer, workspaces included, is allocated before capture; the call is
+    made once eagerly first.  Replaying a graph launches its kernels back to
+    back, so the time of a replay is device time, without the host's launch
+    latency (which exceeds the shorter kernels here).
     """
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
 
-    def __init__(self, torch, pad_cycles=0):
-        self.t = torch
-        self.pad = pad_cycles
-        self.pairs = {}
 
-    def run(self, name, fn):
-        if self.pad:
-            self.t.cuda._sleep(self.pad)
-        s = self.t.cuda.Event(enable_timing=True)
-        e = self.t.cuda.Event(enable_timing=True)
-        s.record()
-        out = fn()
-        e.record()
-        self.pairs.setdefault(name, []).append((s, e))
-        return out
-
-    def mean_ms(self, name):
-        ps = self.pairs.get(name, [])
-        return float(np.mean([s.elapsed_time(e) for s, e in ps])) if ps else float("nan")
-
-    def reset(self):
-        self.pairs = {}
+def replay_ms(torch, g, n):
+    """Mean time of one replay of ``g`` over ``n`` back-to-back replays, from HIP events on the replay stream."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def settle(torch, fn, seconds=1.0):
@@ -141,33 +141,37 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
     xs_gu = torch.empty((M, -(-w_gu.K // 128)), dtype=torch.float32, device=dev)
     xq_dn = torch.empty((M, w_dn.K), dtype=torch.uint8, device=dev)
     xs_dn = torch.empty((M, -(-w_dn.K // 128)), dtype=torch.float32, device=dev)
-    kt = KernelTimer(torch)
+    ws_gu = w_gu.workspace(B.ARM_W8A8, M)
+    ws_dn = w_dn.workspace(B.ARM_W8A8, M)
+    calls = {
+        "quant_gate_up": lambda: B.quant_act(x_gu, xq_gu, xs_gu),
+        "gemm_gate_up": lambda: B.linear_w8a8(w_gu, xq_gu, xs_gu, out=y_gu, workspace=ws_gu),
+        "quant_down": lambda: B.quant_act(x_dn, xq_dn, xs_dn),
+        "gemm_down": lambda: B.linear_w8a8(w_dn, xq_dn, xs_dn, out=y_dn, workspace=ws_dn),
+    }
 
     def step():
-        kt.run("quant_gate_up", lambda: B.quant_act(x_gu, xq_gu, xs_gu))
-        kt.run("gemm_gate_up", lambda: B.linear_w8a8(w_gu, xq_gu, xs_gu, out=y_gu))
-        kt.run("quant_down", lambda: B.quant_act(x_dn, xq_dn, xs_dn))
-        kt.run("gemm_down", lambda: B.linear_w8a8(w_dn, xq_dn, xs_dn, out=y_dn))
+        for f in calls.values():
+            f()
 
-    settle(torch, step)
+    # One step = one replay of a graph of the four calls.
+    g_step = graph_of(torch, step)
+    settle(torch, g_step.replay)
     for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    kt.reset()
+        g_step.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
+    ms_step = replay_ms(torch, g_step, steps)
     wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / steps
+    # Device time of each call: a graph of 20 back-to-back launches, replayed.
+    kms = {}
+    for name, f in calls.items():
+        g = graph_of(torch, f, 20)
+        g.replay()
+        kms[name] = replay_ms(torch, g, 5) / 20
+        del g
     flop_gu = 2.0 * M * w_gu.n_total * w_gu.K
     flop_dn = 2.0 * M * w_dn.n_total * w_dn.K
-    kms = {k: kt.mean_ms(k) for k in ("quant_gate_up", "gemm_gate_up", "quant_down", "gemm_down")}
     res = dict(
         ms_per_step=ms_step, wall_s=wall, flop_per_step=flop_gu + flop_dn,
         tflops=(flop_gu + flop_dn) / (ms_step * 1e-3) / 1e12,
@@ -180,7 +184,7 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
         describe_gate_up=w_gu.describe(B.ARM_W8A8, M), describe_down=w_dn.describe(B.ARM_W8A8, M),
         fixture_sha256=synth.sha256_of(*(m.codes for m in gu.members), gu.x),
     )
-    del w_gu, w_dn
+    del g_step, w_gu, w_dn
     return res
 
 
@@ -238,16 +242,16 @@ def bench_large(torch, B, synth, steps, dev):
     M = wl.x.shape[0]
     xq, xs = B.quant_act(x)
     y = torch.empty((M, w.n_total), dtype=torch.bfloat16, device=dev)
-    kt = KernelTimer(torch)
-    settle(torch, lambda: B.linear_w8a8(w, xq, xs, out=y))
-    for _ in range(max(3, steps // 2)):
-        kt.run("gemm", lambda: B.linear_w8a8(w, xq, xs, out=y))
-        kt.run("quant", lambda: B.quant_act(x, xq, xs))
-    torch.cuda.synchronize()
+    ws = w.workspace(B.ARM_W8A8, M)
+    g_gemm = graph_of(torch, lambda: B.linear_w8a8(w, xq, xs, out=y, workspace=ws), 4)
+    g_quant = graph_of(torch, lambda: B.quant_act(x, xq, xs), 4)
+    settle(torch, g_gemm.replay)
+    ms = replay_ms(torch, g_gemm, max(3, steps // 4)) / 4
+    q_ms = replay_ms(torch, g_quant, 5) / 4
     flop = 2.0 * M * w.n_total * w.K
-    ms = kt.mean_ms("gemm")
+    del g_gemm, g_quant
     return dict(gemm_us=ms * 1e3, tflops=flop / (ms * 1e-3) / 1e12, frac=flop / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-                quant_us=kt.mean_ms("quant") * 1e3, describe=w.describe(B.ARM_W8A8, M))
+                quant_us=q_ms * 1e3, describe=w.describe(B.ARM_W8A8, M))
 
 
 def copy_calibration(torch, dev):
@@ -263,8 +267,9 @@ def copy_calibration(torch, dev):
                 launches=3)
 
 
-def cpu_baseline(synth, budget_s=12.0):
-    """The oracle on the host cores: quantization + W8A8 GEMM of the prefill gate/up step on a row sample."""
+def cpu_baseline(synth, budget_s=10.0):
+    """The oracle on the host cores: the whole prefill step (both quantizations and
+    both W8A8 GEMMs, NumPy float64), repeated until about ``budget_s`` seconds."""
     import oracle as O
     try:
         import threadpoolctl
@@ -273,28 +278,30 @@ def cpu_baseline(synth, budget_s=12.0):
     except Exception:
         threads = os.cpu_count() or 1
     gu = synth.config3_gate_up()
-    members = [(m.codes, m.scale_f32()) for m in gu.members]
-    t0 = time.perf_counter()
-    xq, xs = O.quant_act(gu.x)
-    t_quant = time.perf_counter() - t0
-    rows_total = sum(m.codes.shape[0] for m in gu.members)
-    done = 0
-    t1 = time.perf_counter()
-    chunk = 1024
-    while done < rows_total and time.perf_counter() - t1 < budget_s:
-        rows = list(range(done, min(rows_total, done + chunk)))
-        O.linear_w8a8_rows(xq, xs, members, rows)
-        done += len(rows)
-    t_gemm = time.perf_counter() - t1
-    M, K = gu.x.shape
-    flop = 2.0 * M * done * K
-    # scale the sampled rows to the whole step of this GEMM: time = quant + gemm(rows) * total/rows
-    t_full = t_quant + t_gemm * rows_total / done
-    return {"value": 2.0 * M * rows_total * K / t_full / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"gate/up W8A8 of the M=1024 prefill: full activation quantization ({t_quant:.1f} s) + "
-                      f"{done} of {rows_total} output rows in float64 NumPy ({t_gemm:.1f} s, {flop / 1e9:.0f} GFLOP), "
-                      f"scaled to all rows"}
+    dn = synth.config3_down()
+    m_gu = [(m.codes, m.scale_f32()) for m in gu.members]
+    m_dn = [(m.codes, m.scale_f32()) for m in dn.members]
+    M, K_gu = gu.x.shape
+    K_dn = dn.x.shape[1]
+    flop = 2.0 * M * (sum(m.codes.shape[0] for m in gu.members) * K_gu + sum(m.codes.shape[0] for m in dn.members) * K_dn)
+    def gemm(xq, xs, members):
+        # every output row, 1024 rows at a time (the oracle's row form keeps the
+        # dequantized weight block small)
+        total = sum(m[0].shape[0] for m in members)
+        for r0 in range(0, total, 1024):
+            O.linear_w8a8_rows(xq, xs, members, list(range(r0, min(total, r0 + 1024))))
+
+    reps, t0 = 0, time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < budget_s:
+        xq, xs = O.quant_act(gu.x)
+        gemm(xq, xs, m_gu)
+        xq, xs = O.quant_act(dn.x)
+        gemm(xq, xs, m_dn)
+        reps += 1
+    t = (time.perf_counter() - t0) / reps
+    return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole prefill step (quantize + W8A8 gate/up + quantize + W8A8 down, M=1024) in float64 "
+                      f"NumPy, {reps} repetition(s), {t:.2f} s each"}
 
 
 def main():
@@ -350,6 +357,7 @@ def main():
         "gemm_down_tflops": round(pre["gemm_down_tflops"], 2),
         "quant_gbs": {"gate_up": round(pre["quant_gate_up_gbs"], 1), "down": round(pre["quant_down_gbs"], 1)},
         "path": {"gate_up": pre["describe_gate_up"], "down": pre["describe_down"]},
+        "timing": "HIP graph replays: one replay per step; kernel times from graphs of 20 back-to-back launches",
         "fixture_sha256": pre["fixture_sha256"],
     }
     if "decode_gemv" in extra:
