@@ -7,6 +7,8 @@
 // One group of 128 channels is handled by 32 lanes (half a wave), 4 channels per
 // lane, so a wave covers 256 contiguous channels of one token and every global
 // access is a coalesced 16-byte (F32) or 8-byte (BF16) load and a 4-byte store.
+// A half-wave takes four consecutive groups and issues all four loads before
+// processing any, so each lane has several loads in flight.
 // The group amax is a 5-step butterfly inside the half-wave.  The arithmetic is
 // the defined one, in F32: s = max(amax, 1e-10) / 448 and f = x / s with IEEE
 // division (hipcc's default division is correctly rounded), clamp to +-448, then
@@ -23,6 +25,7 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr float kE4M3Max = 448.0f;
 constexpr float kAmaxFloor = 1e-10f;
+constexpr int kGroupsPerHalf = 4;   // 128-element groups per 32-lane half-wave
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -57,34 +60,44 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
                                                                   int64_t ldx, uint8_t* __restrict__ xq, int64_t ldq,
                                                                   float* __restrict__ xs, int64_t ldxs, int32_t Kb,
                                                                   int32_t x_vec, int32_t q_vec) {
+  // Each 32-lane half-wave quantizes kGroupsPerHalf consecutive groups
+  // (row-major over tokens and groups), loading all of them before any is
+  // processed so that several loads per lane are in flight.
   const int lane32 = threadIdx.x & 31;
   const int64_t n_groups = int64_t(M) * Kb;
-  const int64_t stride = int64_t(gridDim.x) * (kQuantThreads / 32);
-  for (int64_t gi = int64_t(blockIdx.x) * (kQuantThreads / 32) + (threadIdx.x >> 5); gi < n_groups; gi += stride) {
-    const int64_t m = gi / Kb;
-    const int32_t g = int32_t(gi - m * Kb);
-    const int32_t k = g * kBlock + lane32 * 4;
-    const int valid = max(0, min(4, K - k));
-    float v[4];
-    load4<BF16>(x, m * ldx + k, valid, x_vec != 0, v);
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  const int64_t g0 = (int64_t(blockIdx.x) * (kQuantThreads / 32) + (threadIdx.x >> 5)) * kGroupsPerHalf;
+  float v[kGroupsPerHalf][4];
+  int64_t mrow[kGroupsPerHalf];
+  int32_t gcol[kGroupsPerHalf], kk[kGroupsPerHalf], valid[kGroupsPerHalf];
+#pragma unroll
+  for (int j = 0; j < kGroupsPerHalf; ++j) {
+    const int64_t gi = g0 + j;
+    const bool live = gi < n_groups;
+    mrow[j] = live ? gi / Kb : 0;
+    gcol[j] = live ? int32_t(gi - mrow[j] * Kb) : 0;
+    kk[j] = gcol[j] * kBlock + lane32 * 4;
+    valid[j] = live ? max(0, min(4, K - kk[j])) : 0;
+    load4<BF16>(x, mrow[j] * ldx + kk[j], valid[j], x_vec != 0, v[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kGroupsPerHalf; ++j) {
+    if (g0 + j >= n_groups) break;
+    float amax = fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3])));
 #pragma unroll
     for (int d = 16; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 32));
     const float s = fmaxf(amax, kAmaxFloor) / kE4M3Max;
     float f[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f[j] = fminf(fmaxf(v[j] / s, -kE4M3Max), kE4M3Max);
+    for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(v[j][e] / s, -kE4M3Max), kE4M3Max);
     int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
     packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
-    uint8_t* q = xq + m * ldq + k;
-    if (valid == 4 && q_vec) {
+    uint8_t* q = xq + mrow[j] * ldq + kk[j];
+    if (valid[j] == 4 && q_vec) {
       *reinterpret_cast<int*>(q) = packed;
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < valid) q[j] = uint8_t(uint32_t(packed) >> (8 * j));
+      for (int e = 0; e < valid[j]; ++e) q[e] = uint8_t(uint32_t(packed) >> (8 * e));
     }
-    if (lane32 == 0) xs[m * ldxs + g] = s;
+    if (lane32 == 0) xs[mrow[j] * ldxs + gcol[j]] = s;
   }
 }
 
@@ -94,8 +107,13 @@ bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, i
                              int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
   const int32_t Kb = int32_t((K + kBlock - 1) / kBlock);
   const int64_t n_groups = M * Kb;
-  const int64_t want = (n_groups + (kQuantThreads / 32) - 1) / (kQuantThreads / 32);
-  const int grid = int(want < 65536 ? want : 65536);
+  const int64_t per_block = int64_t(kQuantThreads / 32) * kGroupsPerHalf;
+  const int64_t grid64 = (n_groups + per_block - 1) / per_block;
+  if (grid64 > INT32_MAX) {
+    set_error("UNSUPPORTED: %lld activation groups", (long long)n_groups);
+    return BSF8_E_UNSUPPORTED;
+  }
+  const int grid = int(grid64);
   const size_t esz = x_bf16 ? 2 : 4;
   const int x_vec = (reinterpret_cast<uintptr_t>(x) % (4 * esz) == 0) && ((ldx * esz) % (4 * esz) == 0);
   const int q_vec = (reinterpret_cast<uintptr_t>(xq) % 4 == 0) && (ldq % 4 == 0);
