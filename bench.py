@@ -15,9 +15,13 @@ The same JSON line also carries:
 * ``roofline``: the gate/up GEMM, FLOPs per launch over its mean device time
   (a graph of 20 back-to-back launches, timed with HIP events on the
   replaying stream), against the dense FP8 MFMA peak;
-* ``decode_gemv``: the W8A16/F32 arm at M in {1, 4, 8} on W [5120, 5120],
-  rotating through >= 512 MiB of weight copies so the 256 MB Infinity Cache
-  cannot serve them, with an HBM roofline on algorithmic bytes;
+* ``decode_gemv`` (and ``decode_gemv_5000x4000``, ``qkv_decode``): the W8A16/F32
+  arm at M in {1, 4, 8} on W [5120, 5120] (W [5000, 4000]; grouped Q/K/V at
+  M = 1), rotating through >= 512 MiB of weight copies so the 256 MB Infinity
+  Cache cannot serve them, per-launch median / p10 / p90 over 100 replays,
+  with an HBM roofline on algorithmic bytes and a plain read of the same bytes
+  (``bsf8_read_stream``) as context;
+* ``qkv_prefill``: grouped Q/K/V W8A8 at M = 512;
 * ``large_prefill``: the W8A8 GEMM at M=8192, K=7168, N=18432;
 * ``cpu_baseline``: the oracle (NumPy) on the host cores, running the same
   prefill step for about ten seconds.
@@ -71,6 +75,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the oracle's CPU baseline")
     ap.add_argument("--skip-extra", action="store_true", help="leave out the decode and large-prefill lines")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="do not run rocm-smi for the clock under load (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -104,6 +110,51 @@ def replay_ms(torch, g, n):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def under_profiler():
+    """True when this process runs under rocprofv3 (its variables are in the environment)."""
+    return any(k.startswith("ROCPROF") for k in os.environ)
+
+
+def replay_stats(torch, g, n, per):
+    """Per-launch device time from ``n`` replays of ``g`` (``per`` launches each),
+    each replay between its own pair of HIP events; replays are queued back to
+    back, so the device never waits for the host.  Milliseconds.  Under a
+    profiler (counter runs) only a few replays are queued: its per-dispatch
+    bookkeeping is not meant for thousands of queued graph launches."""
+    if under_profiler():
+        n = min(n, 5)
+    pairs = []
+    for _ in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) / per for a, b in pairs])
+    return dict(median=float(np.median(t)), p10=float(np.percentile(t, 10)), p90=float(np.percentile(t, 90)),
+                mean=float(t.mean()), launches=int(n * per))
+
+
+def sample_sclk(torch, g, replays):
+    """The shader clock as rocm-smi reports it while ``replays`` replays of ``g`` run
+    (best effort: the tool's own text, or None when it is not available).  Not
+    under a profiler: the tool would be a second process on the profiled GPU."""
+    if under_profiler() or os.environ.get("BSF8_BENCH_NO_CLOCK_SAMPLE"):
+        return None
+    import subprocess
+    for _ in range(replays):
+        g.replay()
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [l.strip() for l in r.stdout.splitlines() if "sclk" in l.lower()]
+    except Exception:
+        lines = None
+    torch.cuda.synchronize()
+    return lines or None
 
 
 def settle(torch, fn, seconds=1.0):
@@ -163,19 +214,23 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
     t0 = time.perf_counter()
     ms_step = replay_ms(torch, g_step, steps)
     wall = time.perf_counter() - t0
-    # Device time of each call: a graph of 20 back-to-back launches, replayed.
-    kms = {}
+    sclk = sample_sclk(torch, g_step, 2000)
+    # Device time of each call: a graph of 20 back-to-back launches, replayed
+    # 50 times (1000 launches), each replay timed on its own.
+    kms, kstats = {}, {}
     for name, f in calls.items():
         g = graph_of(torch, f, 20)
         g.replay()
-        kms[name] = replay_ms(torch, g, 5) / 20
+        st = replay_stats(torch, g, 50, 20)
+        kms[name] = st["mean"]
+        kstats[name] = {k: (round(v * 1e3, 2) if k != "launches" else v) for k, v in st.items()}
         del g
     flop_gu = 2.0 * M * w_gu.n_total * w_gu.K
     flop_dn = 2.0 * M * w_dn.n_total * w_dn.K
     res = dict(
         ms_per_step=ms_step, wall_s=wall, flop_per_step=flop_gu + flop_dn,
         tflops=(flop_gu + flop_dn) / (ms_step * 1e-3) / 1e12,
-        kernels_ms=kms,
+        kernels_ms=kms, kernels_us_stats=kstats, sclk=sclk,
         gemm_gate_up_tflops=flop_gu / (kms["gemm_gate_up"] * 1e-3) / 1e12,
         gemm_down_tflops=flop_dn / (kms["gemm_down"] * 1e-3) / 1e12,
         quant_gate_up_gbs=(M * w_gu.K * 5 + M * (-(-w_gu.K // 128)) * 4) / (kms["quant_gate_up"] * 1e-3) / 1e9,
@@ -188,50 +243,81 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
     return res
 
 
-def bench_decode(torch, B, synth, steps, dev):
-    out = {}
-    N = K = 5120
-    base = synth.config2(8)
-    m = base.members[0]
-    per_copy = m.codes.nbytes + m.scale_bits.nbytes
+def bench_w8a16_rotating(torch, B, members, x_np, Ms, dev, label):
+    """W8A16/F32 at small M on ``members``, rotating through >= ROTATE_BYTES of
+    weight copies (beyond the Infinity Cache): one HIP graph holds one launch per
+    copy; 100 replays give the per-launch median / p10 / p90.  Also times a plain
+    read of the same weight bytes (a torch int32 sum over each copy) as the
+    achievable-bandwidth context."""
+    per_copy = sum(m.codes.nbytes + m.scale_bits.nbytes for m in members)
     copies = max(2, -(-ROTATE_BYTES // per_copy))
-    log(f"decode: {copies} weight copies of {per_copy / 2**20:.1f} MiB")
-    w0, s0 = to_device_member(torch, m, dev)
-    handles = []
-    for _ in range(copies):
-        handles.append(B.BlockFP8Weight([(w0.clone(), s0.clone())]))
+    log(f"{label}: {copies} weight copies of {per_copy / 2**20:.1f} MiB")
+    base = [to_device_member(torch, m, dev) for m in members]
+    copies_t = [[(w.clone(), sc.clone()) for w, sc in base] for _ in range(copies)]
+    handles = [B.BlockFP8Weight(c) for c in copies_t]
+    N = sum(m.codes.shape[0] for m in members)
+    K = members[0].codes.shape[1]
     Kb = -(-K // 128)
-    for M in (1, 4, 8):
-        x = torch.from_numpy(base.x[:M].copy()).to(dev)
+    grid_elems = sum(-(-m.codes.shape[0] // 128) for m in members) * Kb
+    out = {"workload": f"{label}: W [{N},{K}] ({len(members)} member(s)) + bf16 grid, f32 x/y, "
+                       f"rotating {copies} copies ({copies * per_copy >> 20} MiB)", "by_M": {}}
+    for M in Ms:
+        x = torch.from_numpy(np.ascontiguousarray(x_np[:M])).to(dev)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         ws = [h.workspace(B.ARM_W8A16, M) for h in handles]
-        for i in range(copies):
-            B.linear_w8a16(handles[i], x, out=y, workspace=ws[i])
-        torch.cuda.synchronize()
-        # One graph holds `copies` back-to-back launches, each on another weight
-        # copy; replays are bracketed by events, so the per-launch time is the
-        # device's own launch-to-launch time (host launch latency would
-        # otherwise exceed these few-microsecond kernels).
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+
+        def run():
             for i in range(copies):
                 B.linear_w8a16(handles[i], x, out=y, workspace=ws[i])
+
+        g = graph_of(torch, run)
         settle(torch, g.replay, 0.3)
-        reps = max(4, steps)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (reps * copies)
-        alg_bytes = N * K + 2 * (N // 128) * Kb + 4 * M * K + 4 * M * N
-        out[f"M{M}"] = dict(us=ms * 1e3, gbs=alg_bytes / (ms * 1e-3) / 1e9, algorithmic_bytes=alg_bytes,
-                            describe=handles[0].describe(B.ARM_W8A16, M))
+        st = replay_stats(torch, g, 100, copies)
+        alg = N * K + 2 * grid_elems + 4 * M * K + 4 * M * N
+        out["by_M"][f"M{M}"] = dict(us=st["median"] * 1e3, us_p10=st["p10"] * 1e3, us_p90=st["p90"] * 1e3,
+                                    launches=st["launches"], gbs=alg / (st["median"] * 1e-3) / 1e9,
+                                    algorithmic_bytes=alg, describe=handles[0].describe(B.ARM_W8A16, M))
         del g
-    del handles
+    # read-stream context: a plain read of each copy's weight bytes, same rotation
+    sink = torch.zeros(B.READ_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+
+    def read_all():
+        for c in copies_t:
+            for w, _ in c:
+                B.read_stream(w, sink)
+
+    g = graph_of(torch, read_all)
+    settle(torch, g.replay, 0.2)
+    st = replay_stats(torch, g, 50, copies)
+    wbytes = sum(m.codes.nbytes for m in members)
+    out["read_stream_context"] = dict(us=st["median"] * 1e3, gbs=wbytes / (st["median"] * 1e-3) / 1e9,
+                                      kernel="bsf8_read_stream over the same weight bytes, same rotation")
+    del g, handles, copies_t
+    torch.cuda.empty_cache()
     return out
+
+
+def bench_qkv_prefill(torch, B, synth, dev):
+    """Grouped Q/K/V (members of 6144, 1000 and 1000 rows, K = 5120) at M = 512,
+    W8A8 with its quantization; graphs of 20 back-to-back calls, warm."""
+    wl = synth.config4(512)
+    w = B.BlockFP8Weight([to_device_member(torch, m, dev) for m in wl.members])
+    x = torch.from_numpy(wl.x).to(dev)
+    M = wl.x.shape[0]
+    xq, xs = B.quant_act(x)
+    y = torch.empty((M, w.n_total), dtype=torch.bfloat16, device=dev)
+    ws = w.workspace(B.ARM_W8A8, M)
+    g = graph_of(torch, lambda: B.linear_w8a8(w, xq, xs, out=y, workspace=ws), 20)
+    gq = graph_of(torch, lambda: B.quant_act(x, xq, xs), 20)
+    settle(torch, g.replay, 0.3)
+    st = replay_stats(torch, g, 20, 20)
+    sq = replay_stats(torch, gq, 20, 20)
+    flop = 2.0 * M * w.n_total * w.K
+    del g, gq
+    return dict(workload="grouped QKV W8A8, members [6144|1000|1000, 5120], M=512, bf16 out",
+                gemm_us=st["median"] * 1e3, gemm_us_p10=st["p10"] * 1e3, gemm_us_p90=st["p90"] * 1e3,
+                tflops=flop / (st["median"] * 1e-3) / 1e12, quant_us=sq["median"] * 1e3,
+                describe=w.describe(B.ARM_W8A8, M))
 
 
 def bench_large(torch, B, synth, steps, dev):
@@ -306,6 +392,8 @@ def cpu_baseline(synth, budget_s=10.0):
 
 def main():
     a = parse()
+    if a.no_clock_sample:
+        os.environ["BSF8_BENCH_NO_CLOCK_SAMPLE"] = "1"
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported"}))
         sys.exit(2)
@@ -322,8 +410,15 @@ def main():
     log(f"prefill {pre['tflops']:.1f} TFLOP/s/step, kernels {pre['kernels_ms']}")
     extra = {}
     if not a.skip_extra:
-        extra["decode_gemv"] = bench_decode(torch, B, synth, a.steps, dev)
-        log(f"decode {extra['decode_gemv']}")
+        c2 = synth.config2(8)
+        extra["decode_gemv"] = bench_w8a16_rotating(torch, B, c2.members, c2.x, (1, 4, 8), dev, "decode 5120x5120")
+        log(f"decode {extra['decode_gemv']['by_M']}")
+        c2b = synth.config2(8, shape=(5000, 4000))
+        extra["decode_gemv_5000x4000"] = bench_w8a16_rotating(torch, B, c2b.members, c2b.x, (1, 4, 8), dev,
+                                                              "decode 5000x4000")
+        c4 = synth.config4(1)
+        extra["qkv_decode"] = bench_w8a16_rotating(torch, B, c4.members, c4.x, (1,), dev, "grouped QKV decode")
+        extra["qkv_prefill"] = bench_qkv_prefill(torch, B, synth, dev)
         torch.cuda.empty_cache()
         extra["large_prefill"] = bench_large(torch, B, synth, a.steps, dev)
         log(f"large {extra['large_prefill']}")
@@ -354,24 +449,35 @@ def main():
                      "traffic": profiled_traffic("w8a8_gemm_gate_up_m1024")},
         "cpu_baseline": cpu,
         "kernels_ms": {k: round(v, 5) for k, v in pre["kernels_ms"].items()},
+        "kernels_us_stats": pre["kernels_us_stats"],
+        "device": {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+                   "sclk_under_load": pre["sclk"]},
         "gemm_down_tflops": round(pre["gemm_down_tflops"], 2),
         "quant_gbs": {"gate_up": round(pre["quant_gate_up_gbs"], 1), "down": round(pre["quant_down_gbs"], 1)},
         "path": {"gate_up": pre["describe_gate_up"], "down": pre["describe_down"]},
         "timing": "HIP graph replays: one replay per step; kernel times from graphs of 20 back-to-back launches",
         "fixture_sha256": pre["fixture_sha256"],
     }
+    def decode_line(d, roofline_traffic=None):
+        bm = d["by_M"]
+        last = sorted(bm)[-1]
+        r = {"workload": d["workload"], "unit": "GB/s", "by_M": {k: round(v["gbs"], 1) for k, v in bm.items()},
+             "us_by_M": {k: {"median": round(v["us"], 2), "p10": round(v["us_p10"], 2), "p90": round(v["us_p90"], 2),
+                             "launches": v["launches"]} for k, v in bm.items()},
+             "read_stream_context": {k: round(v, 1) for k, v in d["read_stream_context"].items() if k != "kernel"},
+             "path": bm[last]["describe"]}
+        if roofline_traffic is not False:
+            r["roofline"] = {"bound": "hbm", "kernel": f"w8a16 ({last})", "achieved": round(bm[last]["gbs"], 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(bm[last]["gbs"] / HBM_PEAK_GBS, 4),
+                             "traffic": roofline_traffic}
+        return r
+
     if "decode_gemv" in extra:
-        d = extra["decode_gemv"]
-        line["decode_gemv"] = {
-            "workload": "W8A16/F32 decode GEMV, W [5120,5120] + bf16 grid [40,40], f32 x/y, rotating "
-                        f">= {ROTATE_BYTES >> 20} MiB of weight copies",
-            "unit": "GB/s", "by_M": {k: round(v["gbs"], 1) for k, v in d.items()},
-            "us_by_M": {k: round(v["us"], 2) for k, v in d.items()},
-            "roofline": {"bound": "hbm", "kernel": "w8a16 (M=8)", "achieved": round(d["M8"]["gbs"], 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d["M8"]["gbs"] / HBM_PEAK_GBS, 4),
-                         "traffic": profiled_traffic("w8a16_decode_5120x5120")},
-            "path": d["M8"]["describe"],
-        }
+        line["decode_gemv"] = decode_line(extra["decode_gemv"], profiled_traffic("w8a16_decode_5120x5120"))
+        line["decode_gemv_5000x4000"] = decode_line(extra["decode_gemv_5000x4000"], None)
+        line["qkv_decode"] = decode_line(extra["qkv_decode"], None)
+        q = extra["qkv_prefill"]
+        line["qkv_prefill"] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in q.items()}
     if "large_prefill" in extra:
         l = extra["large_prefill"]
         line["large_prefill"] = {"workload": "W8A8 GEMM M=8192 K=7168 N=18432, bf16 out",

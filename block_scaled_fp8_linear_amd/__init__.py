@@ -77,6 +77,7 @@ EXPORTS = [
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("bsf8_describe", ctypes.c_char_p, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]),
+    ("bsf8_read_stream", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
 ]
 
 
@@ -289,3 +290,17 @@ def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=N
 
 __all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "linear_w8a16", "linear_w8a8", "lib",
            "status_name", "ARM_W8A16", "ARM_W8A8", "EXPORTS", "LIB_PATH", "MAX_MEMBERS"]
+
+
+READ_STREAM_SINK_WORDS = 2048  # BSF8_READ_STREAM_SINK_WORDS in include/bsf8.h
+
+
+def read_stream(buf, sink):
+    """Measurement aid: a plain read of ``buf``'s bytes on the current stream.
+
+    ``sink``: int32 device tensor of at least READ_STREAM_SINK_WORDS words; the
+    launch overwrites its leading words with per-block XORs of what it read."""
+    if sink.numel() * sink.element_size() < 4 * READ_STREAM_SINK_WORDS:
+        raise ValueError(f"read_stream sink needs {READ_STREAM_SINK_WORDS} 4-byte words")
+    _check(lib().bsf8_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                  _stream_ptr(buf.device)), "read_stream")

@@ -278,6 +278,15 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
                      workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+bsf8_status bsf8_read_stream(const void* p, int64_t bytes, uint32_t* sink, void* stream) {
+  if (p == nullptr || sink == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (bytes < 0) return fail(BSF8_E_INVALID_ARG, "negative size");
+  if (reinterpret_cast<uintptr_t>(p) % 16 || bytes % 16 || reinterpret_cast<uintptr_t>(sink) % 4)
+    return fail(BSF8_E_ALIGNMENT, "read_stream needs a 16-byte aligned pointer and size");
+  if (bytes == 0) return BSF8_OK;
+  return launch_read_stream(p, bytes, sink, static_cast<hipStream_t>(stream));
+}
+
 const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M) {
   if (w == nullptr) return nullptr;
   char geo[256];

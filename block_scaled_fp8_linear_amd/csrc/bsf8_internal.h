@@ -56,6 +56,8 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
                         size_t ws_bytes, hipStream_t stream);
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M);
 
+bsf8_status launch_read_stream(const void* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace bsf8
 
 // The opaque handle of the ABI.

@@ -523,6 +523,10 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     issue_scales(kb, base);
   };
 
+  // The first K block's copies go out before the weight scales are staged, so
+  // the two memory latencies overlap (the first step's barrier covers both).
+  issue(kb_begin, stage0);
+
   // ---- weight scales: rows (n0 >> 7) and (n0 >> 7) + 1 of the member's grid
   // (one per wave half), staged in LDS once; a missing row reads as zero
   {
@@ -602,7 +606,6 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     }
   };
 
-  issue(kb_begin, stage0);
   for (int kb = kb_begin; kb < kb_end; kb += 2) {
     step(kb, stage0, stage1);
     if (kb + 1 < kb_end) step(kb + 1, stage1, stage0);

@@ -258,6 +258,22 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
  */
 const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M);
 
+/*
+ * bsf8_read_stream -- measurement aid, not part of the projection: reads
+ * `bytes` bytes at `p` as a plain coalesced stream.  Timed on a GEMV's weight
+ * bytes it gives the achievable read rate the GEMV is judged against.
+ * p: device pointer, 16-byte aligned; bytes: a multiple of 16, >= 0.
+ * sink: device array of BSF8_READ_STREAM_SINK_WORDS 4-byte words the caller
+ * owns.  The launch uses min(ceil(bytes / 16 KiB), BSF8_READ_STREAM_SINK_WORDS)
+ * blocks; block b overwrites sink[b] with the XOR of the 4-byte words it read
+ * and words past the last block are left as they were, so the XOR of a sink
+ * zeroed beforehand equals the XOR of the buffer's words.  Stream-ordered;
+ * allocates nothing.  Errors: INVALID_ARG (null pointer, negative size),
+ * ALIGNMENT, DEVICE.
+ */
+#define BSF8_READ_STREAM_SINK_WORDS 2048
+bsf8_status bsf8_read_stream(const void* p, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

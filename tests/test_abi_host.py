@@ -148,3 +148,19 @@ def test_create_needs_device_addresses():
     h = ctypes.c_void_p()
     assert B.status_name(B.lib().bsf8_weight_create(ctypes.byref(decl), arr, 1, ctypes.byref(h))) == "INVALID_ARG"
     assert not h.value
+
+
+def test_read_stream_refusals():
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 40)
+    assert B.status_name(L.bsf8_read_stream(None, 16, fake, None)) == "INVALID_ARG"
+    assert B.status_name(L.bsf8_read_stream(fake, -16, fake, None)) == "INVALID_ARG"
+    assert B.status_name(L.bsf8_read_stream(fake, 24, fake, None)) == "ALIGNMENT"
+    assert B.status_name(L.bsf8_read_stream(ctypes.c_void_p((1 << 40) + 8), 16, fake, None)) == "ALIGNMENT"
+    assert L.bsf8_read_stream(fake, 0, fake, None) == 0
+
+
+def test_read_stream_sink_size_matches_header():
+    with open(os.path.join(ROOT, "include", "bsf8.h")) as f:
+        hdr = f.read()
+    assert int(re.search(r"#define BSF8_READ_STREAM_SINK_WORDS (\d+)", hdr).group(1)) == B.READ_STREAM_SINK_WORDS

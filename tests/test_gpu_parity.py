@@ -442,3 +442,18 @@ def test_w8a8_split_k_is_deterministic():
         assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
     om = oracle_members([m])
     assert_within(ys[0], O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), False, "split-K")
+
+
+
+def test_read_stream_reads_every_byte():
+    """The measurement aid's per-block sink words XOR to the XOR of all 4-byte words read."""
+    t = torch()
+    g = np.random.default_rng(107)
+    for n in (16, 4096, 5 * 1024 * 1024 + 48, 64 * 1024 * 1024 + 16):
+        host = g.integers(0, 2**32, n // 4, dtype=np.uint64).astype(np.uint32)
+        buf = t.from_numpy(host.view(np.int32)).to(device())
+        sink = t.zeros(B.READ_STREAM_SINK_WORDS, dtype=t.int32, device=device())
+        banner(f"read_stream {n} bytes")
+        B.read_stream(buf, sink)
+        want = np.bitwise_xor.reduce(host) if n else np.uint32(0)
+        assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want
