@@ -363,37 +363,46 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //  * activations are loaded compactly (32 lanes per F32 token, 16 per BF16
 //    token), each lane splits only what it loaded, and the BF16 terms go to a
 //    wave-private LDS scratch in fragment order; tokens past M read a zero row;
-//  * a ring of SM_DEPTH chunks of both operands is in flight in registers;
+//  * a ring of SM_DEPTH chunks of both operands is in flight in registers
+//    (as many as a wave has chunks, up to 5, so decode K <= 5120 issues all of
+//    a wave's loads at once; 3 for F32 at M > 4, where registers run out);
 //    loads retire in issue order, so each slot's loads are issued together and
 //    slots in chunk order (scheduling barriers keep them grouped), and chunks
 //    past the wave's range get past-the-end offsets (zeros, no traffic).
 //    (Copies straight into LDS would save the registers, but the compiler then
 //    waits for every copy in flight before any other LDS access of the wave.)
-//  * the chunk scales of the wave's range are loaded once, first.
+//  * the chunk scales of the wave's range are loaded once, first;
+//  * the three BF16 terms of F32 activations are not three MFMA passes: they
+//    fill the MFMA's otherwise idle token columns.  Column g holds term g / M of
+//    token g % M, so M <= 5 takes one 16-column pass and M <= 8 two (a third
+//    and a sixth of the general kernel's MFMAs).  Each column keeps its own F32
+//    accumulator over the chunks, and a token's three columns are added once,
+//    when the waves' partial tiles are reduced.
 // In a chunk, lane group gq owns the 32 contiguous K bytes [32 gq, 32 gq + 32)
 // of both operands, and K-step s of the 16x16x32 MFMA the 8 at 32 gq + 8 s.
 // LDS layouts (16-byte pieces, bank-conflict free for the fragment reads):
 //  weight buffer: row r of the wave's 32 at r * 128, piece p at p ^ ((r >> 1) & 7);
 //  activation scratch: term u, token t at u * SM_TERM_BYTES + t * 256, piece p at p ^ t.
-// The MFMA sequence, per-chunk scaling and the wave-order reduction are those
-// of the general kernel.
+// Per-chunk scaling and the wave-order reduction are those of the general
+// kernel.
 // ---------------------------------------------------------------------------
 constexpr int SM_MAXM = 8;
 constexpr int SM_ZERO_ROW = SM_MAXM;           // scratch row that stays zero
 constexpr int SM_ROW_BYTES = CHUNK * 2;        // one token's chunk as BF16
 constexpr int SM_TERM_BYTES = (SM_MAXM + 1) * SM_ROW_BYTES;
-constexpr int SM_DEPTH = 3;
+constexpr int SM_MAX_DEPTH = 5;               // ring depth for M <= 4 (F32) / 8 (BF16); 3 at F32 M > 4 (registers)
 constexpr int SM_SCALE_REGS = 2;               // chunk scales per wave: up to 128 (K up to 131072 with 8 waves)
 constexpr int SM_WBUF = ROWS * CHUNK;          // a wave's weight bytes per chunk: 4 KiB
 
-template <bool XBF16, bool SBF16, int NXI>
+template <bool XBF16, bool SBF16, int NXI, int NP, int SM_DEPTH>
 __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   constexpr int NT = XBF16 ? 1 : TERMS;          // a BF16 activation is its own single term
+  static_assert(NP == 1 || NP == 2, "one or two 16-column MFMA passes");
   constexpr int LPT = XBF16 ? 16 : 32;           // lanes per token in a compact load
   constexpr int EPL = XBF16 ? 8 : 4;             // activations per lane in a compact load
   __shared__ __attribute__((aligned(1024))) uint8_t wbuf[WAVES][SM_WBUF];
   __shared__ __attribute__((aligned(16))) uint8_t scratch[WAVES][NT * SM_TERM_BYTES];
-  static_assert(sizeof(float) * WAVES * RT * 64 * 4 <= sizeof(uint8_t) * WAVES * SM_WBUF, "reduction fits the buffers");
+  static_assert(sizeof(float) * WAVES * RT * NP * 64 * 4 <= sizeof(uint8_t) * WAVES * SM_WBUF, "reduction fits the buffers");
 
   const int tile = blockIdx.x;
   int mi = 0;
@@ -415,15 +424,28 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 
   const int xt = lane / LPT;                     // token within a compact load
   const int xk = (lane % LPT) * EPL;             // first K element of the lane in the chunk
-  const int frow = l16 < M ? l16 : SM_ZERO_ROW;  // scratch row read for this lane's token
+  // B operand column of this lane in pass p: g = 16 p + l16 is term g / M of
+  // token g % M; columns past the last read the zero row of term 0
+  int boff[NP], bkey[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int g = 16 * p + l16;
+    const int u = g / M;
+    const int tk = g - u * M;
+    const bool ok = u < NT;
+    boff[p] = ok ? u * SM_TERM_BYTES + tk * SM_ROW_BYTES : SM_ZERO_ROW * SM_ROW_BYTES;
+    bkey[p] = ok ? tk : SM_ZERO_ROW;
+  }
   // weight loads: lane L takes piece L & 7 of row (L >> 3) + 8 q of the wave's 32
   const int crow = lane >> 3;
   const int cpiece = lane & 7;
   uint8_t* const wb = wbuf[wave];
 
-  v4f acc[RT];
+  v4f acc[RT][NP];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) acc[t][p] = v4f{0.f, 0.f, 0.f, 0.f};
 
   uint4 xr[SM_DEPTH][NXI];
   uint4 wr[SM_DEPTH][2 * RT];
@@ -513,13 +535,13 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
         }
       }
       // B fragments: K-step st holds K = 32 gq + 8 st + j
-      v8bf b[NT][STEPS];
+      v8bf b[NP][STEPS];
 #pragma unroll
       for (int st = 0; st < STEPS; ++st) {
         const int kc = 4 * gq + st;
-        const uint8_t* srcp = sc + frow * SM_ROW_BYTES + ((kc ^ frow) * 16);
 #pragma unroll
-        for (int u = 0; u < NT; ++u) b[u][st] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(srcp + u * SM_TERM_BYTES));
+        for (int p = 0; p < NP; ++p)
+          b[p][st] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(sc + boff[p] + ((kc ^ bkey[p]) * 16)));
       }
       // weights: to LDS in rows, back in the MFMA layout
 #pragma unroll
@@ -534,17 +556,15 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
         const uint4 lo = *reinterpret_cast<const uint4*>(wb + rr * CHUNK + (((2 * gq) ^ sw8) * 16));
         const uint4 hi = *reinterpret_cast<const uint4*>(wb + rr * CHUNK + (((2 * gq + 1) ^ sw8) * 16));
         const v8bf af[STEPS] = {cvt8(lo.x, lo.y), cvt8(lo.z, lo.w), cvt8(hi.x, hi.y), cvt8(hi.z, hi.w)};
-        v4f pt[NT];
+        v4f pt[NP];
 #pragma unroll
-        for (int u = 0; u < NT; ++u) pt[u] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < NP; ++p) pt[p] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < STEPS; ++st)
 #pragma unroll
-          for (int u = 0; u < NT; ++u) pt[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], b[u][st], pt[u], 0, 0, 0);
-        v4f tsum = pt[0];
+          for (int p = 0; p < NP; ++p) pt[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], b[p][st], pt[p], 0, 0, 0);
 #pragma unroll
-        for (int u = 1; u < NT; ++u) tsum += pt[u];
-        acc[t] += tsum * sw;
+        for (int p = 0; p < NP; ++p) acc[t][p] += pt[p] * sw;
       }
       __builtin_amdgcn_sched_barrier(0);
       issue(c + SM_DEPTH, d);   // refill this slot
@@ -556,23 +576,38 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // ---- add the 8 waves' partial tiles in wave order and store
-  float(*red)[RT][64][4] = reinterpret_cast<float(*)[RT][64][4]>(&wbuf[0][0]);
+  // ---- add the 8 waves' partial tiles in wave order, then a token's term
+  // columns (smallest first), and store
+  float(*red)[RT * NP][64][4] = reinterpret_cast<float(*)[RT * NP][64][4]>(&wbuf[0][0]);
 #pragma unroll
-  for (int t = 0; t < RT; ++t) *reinterpret_cast<v4f*>(&red[wave][t][lane][0]) = acc[t];
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) *reinterpret_cast<v4f*>(&red[wave][t * NP + p][lane][0]) = acc[t][p];
   __syncthreads();
-  const int t = tid >> 8;
-  const int ln = (tid >> 2) & 63;
-  const int r = tid & 3;
-  float sum = 0.f;
+  const int rr = tid & 31;             // row of the block
+  const int tok = tid >> 5;            // token (16 slots, M <= 8 used)
+  const int t = rr >> 4, i = rr & 15;  // row tile, row within the MFMA tile
+  if (tok < M) {
+    float part[NT];
 #pragma unroll
-  for (int w = 0; w < WAVES; ++w) sum += red[w][t][ln][r];
-  const int row = rtile * ROWS + t * 16 + 4 * (ln >> 4) + r;
-  const int mo = ln & 15;
-  if (row < mem.rows && mo < M) {
-    const int64_t off = int64_t(mo) * a.ldy + mem.col0 + row;
-    if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
-    else static_cast<float*>(a.y)[off] = sum;
+    for (int u = 0; u < NT; ++u) {
+      const int g = u * M + tok;       // column of term u
+      const int p = g >> 4;
+      const int ln = 16 * (i >> 2) + (g & 15);
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) s += red[w][t * NP + p][ln][i & 3];
+      part[u] = s;
+    }
+    float sum = part[NT - 1];
+#pragma unroll
+    for (int u = NT - 2; u >= 0; --u) sum += part[u];
+    const int row = rtile * ROWS + rr;
+    if (row < mem.rows) {
+      const int64_t off = int64_t(tok) * a.ldy + mem.col0 + row;
+      if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
+      else static_cast<float*>(a.y)[off] = sum;
+    }
   }
 }
 
@@ -602,17 +637,25 @@ Plan make_plan(const WeightDev& w, int64_t M) {
 
 size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
 
+// load-ring depth of the few-token kernel: a wave's chunk count, within [3, SM_MAX_DEPTH]
+int small_depth(int chunks_per_wave) {
+  return chunks_per_wave <= 3 ? 3 : chunks_per_wave >= SM_MAX_DEPTH ? SM_MAX_DEPTH : chunks_per_wave;
+}
+
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   const Plan p = make_plan(w, M > 0 ? M : 1);
-  char buf[320];
   const bool small = aligned && M >= 1 && M <= SM_MAXM;
+  char ring[160] = "";
+  if (small)
+    snprintf(ring, sizeof(ring), ", %d-chunk load ring%s, compact activations split in LDS, F32 terms in MFMA columns",
+             small_depth(p.chunks_per_wave), M > 4 ? " (3 for F32 activations)" : "");
+  char buf[512];
   snprintf(buf, sizeof(buf),
            "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
            "mfma_f32_16x16x32_bf16 | kernel=%s rows=%d tokens=%d waves=%d (in-block split-K, %d chunks/wave%s) "
            "path=%s | M=%lld blocks=%d",
-           small ? "w8a16_small_m" : "w8a16", ROWS, small ? SM_MAXM : COLS, WAVES, p.chunks_per_wave,
-           small ? ", 3-chunk load ring, compact activations split in LDS" : "", aligned ? "aligned16" : "bytewise",
-           (long long)M, p.tiles);
+           small ? "w8a16_small_m" : "w8a16", ROWS, small ? SM_MAXM : COLS, WAVES, p.chunks_per_wave, ring,
+           aligned ? "aligned16" : "bytewise", (long long)M, p.tiles);
   return buf;
 }
 
@@ -643,15 +686,21 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   auto kern = w8a16_kernel<true, false, true>;
   const bool sb = w.scale_bf16 != 0;
   if (aligned && M <= SM_MAXM) {
-    // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load
+    // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load,
+    // and 3 M term columns of F32 tokens in one 16-column MFMA pass up to M = 5
+    const int depth = small_depth(p.chunks_per_wave);
+#define BSF8_SMALL(XB, NXI, NP)                                                                                   \
+  (depth == 3   ? (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, 3> : w8a16_small_m_kernel<XB, false, NXI, NP, 3>)   \
+   : depth == 4 ? (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, 4> : w8a16_small_m_kernel<XB, false, NXI, NP, 4>)   \
+                : (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, 5> : w8a16_small_m_kernel<XB, false, NXI, NP, 5>))
     if (x_bf16) {
-      if (M <= 4) kern = sb ? w8a16_small_m_kernel<true, true, 1> : w8a16_small_m_kernel<true, false, 1>;
-      else kern = sb ? w8a16_small_m_kernel<true, true, 2> : w8a16_small_m_kernel<true, false, 2>;
+      kern = M <= 4 ? BSF8_SMALL(true, 1, 1) : BSF8_SMALL(true, 2, 1);
+    } else if (M <= 4) {
+      kern = M <= 2 ? BSF8_SMALL(false, 1, 1) : BSF8_SMALL(false, 2, 1);
     } else {
-      if (M <= 2) kern = sb ? w8a16_small_m_kernel<false, true, 1> : w8a16_small_m_kernel<false, false, 1>;
-      else if (M <= 4) kern = sb ? w8a16_small_m_kernel<false, true, 2> : w8a16_small_m_kernel<false, false, 2>;
-      else kern = sb ? w8a16_small_m_kernel<false, true, 4> : w8a16_small_m_kernel<false, false, 4>;
+      kern = sb ? w8a16_small_m_kernel<false, true, 4, 2, 3> : w8a16_small_m_kernel<false, false, 4, 2, 3>;
     }
+#undef BSF8_SMALL
   } else if (aligned) {
     if (x_bf16) kern = sb ? w8a16_kernel<true, true, true> : w8a16_kernel<true, true, false>;
     else kern = sb ? w8a16_kernel<true, false, true> : w8a16_kernel<true, false, false>;

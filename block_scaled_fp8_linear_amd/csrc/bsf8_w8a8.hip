@@ -28,6 +28,7 @@
 
 #include <cstdio>
 #include <string>
+#include <type_traits>
 
 #include "bsf8_internal.h"
 
@@ -305,15 +306,19 @@ constexpr int FBN = 256, FBM = 256, FTHREADS = 512;
 constexpr int F_SA = FBN * KBYTES + FBM * KBYTES;  // offset of the token scales in a stage
 constexpr int F_STAGE = F_SA + FBM * 4;           // 64 KiB of operands + 1 KiB of scales
 // Operand copies: 1 KiB wave copies (8 rows x 128 bytes) per stage, 32 weight
-// slabs and 32 token slabs, all issued by waves 0-3 in one burst at the start
-// of a K block.  Waves 0-3 share their SIMDs with waves 4-7; while a copying
-// wave waits in the vector memory queue its partner has the matrix unit to
-// itself.  (Copies spread over every wave's MFMA chain went out late: the
-// older wave of a SIMD pair takes most MFMA issue slots, so the younger one's
-// chain, and the copies in it, lag behind.)
+// slabs and 32 token slabs, issued by waves 0-3 one after every second MFMA
+// of their chains.  The vector memory unit takes a 1 KiB copy about as fast
+// as it moves it, so a wave that issues its sixteen copies in one burst
+// stalls for most of a K block (as long as its chain); spread over the chain,
+// the stalls overlap MFMAs of both waves of the SIMD.  Waves 0-3 are the
+// older wave of each SIMD pair and win most MFMA issue slots, so their chains,
+// and the copies in them, run early.  (Copies spread over all eight waves go
+// out late: the younger waves' chains lag behind.)
 constexpr int F_COPIERS = 4;
 constexpr int F_A_LOADS = FBN / 8 / F_COPIERS;  // weight slabs per copying wave
 constexpr int F_B_LOADS = FBM / 8 / F_COPIERS;  // token slabs per copying wave
+constexpr int F_IL = TI * TJ / (F_A_LOADS + F_B_LOADS);  // MFMAs per copy in a copying wave's chain
+static_assert(F_IL >= 1 && F_IL * (F_A_LOADS + F_B_LOADS) <= TI * TJ, "copies fit the chain");
 constexpr int XCDS = 8;
 constexpr int GROUP_ROWS = 8;   // row tiles per L2 group
 constexpr int F_MAX_KB = 1024;  // K up to 131072 on the fast path
@@ -410,7 +415,8 @@ __device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uin
   }
 }
 
-template <bool SBF16>
+// KFULL: K is a multiple of 128, so no copy needs the ragged-K test.
+template <bool SBF16, bool KFULL>
 __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   // Two separate stage arrays (not one array indexed by stage): the compiler
   // must wait for in-flight LDS copies before any LDS read it cannot prove
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int l16 = lane & 15, g = lane >> 4;
 
@@ -488,24 +494,31 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   const int ch_even = swz_pos(crow, lane & 7) * 16;
   const int ch_odd = swz_pos(crow + 8, lane & 7) * 16;
   const int cw = wave;              // copier index (valid when copier)
-  const bool copier = wave < F_COPIERS;
+  const bool copier = F_COPIERS * 64 >= FTHREADS || wave < F_COPIERS;
   const int a_row0 = n0 + cw * F_A_LOADS * 8 + crow;   // row of slab i is a_row0 + 8 i
   const int b_row0 = m0 + cw * F_B_LOADS * 8 + crow;
   // Copy number c (0 .. F_A_LOADS + F_B_LOADS - 1) of K block kb into a stage:
   // the first F_A_LOADS are weight slabs, the rest token slabs.
+  // Row parts of the copy offsets, per lane; a row past the operand's end
+  // lands past the buffer's end (zeros), so only a ragged K needs a test.
+  // The K block's part goes through a scalar register, which keeps the
+  // compiler from holding every copy's offset in its own vector register.
+  const uint32_t a_lane = uint32_t(a_row0) * uint32_t(K);
+  const uint32_t b_lane = uint32_t(b_row0) * uint32_t(a.ldq);
   auto issue_one = [&](int kb, uint8_t* base, int c) {
+    const uint32_t kbo = uint32_t(kb) * KBYTES;
     if (c < F_A_LOADS) {
       const int i = c;
-      const int ch = ((cw * F_A_LOADS + i) & 1) ? ch_odd : ch_even;
-      const bool ok = (a_row0 + 8 * i < mem.rows) && (kb * KBYTES + ch < K);
-      const int off = ok ? (a_row0 + 8 * i) * K + kb * KBYTES + ch : int(a_bytes);
-      bsf8_raw_buffer_load_lds(ra, (lds_u32_ptr)(base + (cw * F_A_LOADS + i) * 1024), 16, off, 0, 0, 0);
+      const uint32_t ch = ((cw * F_A_LOADS + i) & 1) ? ch_odd : ch_even;
+      const uint32_t sc = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(8 * i) * uint32_t(K) + kbo)));
+      const uint32_t off = KFULL || kbo + ch < uint32_t(K) ? a_lane + ch + sc : a_bytes;
+      bsf8_raw_buffer_load_lds(ra, (lds_u32_ptr)(base + (cw * F_A_LOADS + i) * 1024), 16, int(off), 0, 0, 0);
     } else {
       const int i = c - F_A_LOADS;
-      const int ch = ((cw * F_B_LOADS + i) & 1) ? ch_odd : ch_even;
-      const bool ok = (b_row0 + 8 * i < M) && (kb * KBYTES + ch < K);
-      const int off = ok ? (b_row0 + 8 * i) * int(a.ldq) + kb * KBYTES + ch : int(b_bytes);
-      bsf8_raw_buffer_load_lds(rb, (lds_u32_ptr)(base + FBN * KBYTES + (cw * F_B_LOADS + i) * 1024), 16, off, 0,
+      const uint32_t ch = ((cw * F_B_LOADS + i) & 1) ? ch_odd : ch_even;
+      const uint32_t sc = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(8 * i) * uint32_t(a.ldq) + kbo)));
+      const uint32_t off = KFULL || kbo + ch < uint32_t(K) ? b_lane + ch + sc : b_bytes;
+      bsf8_raw_buffer_load_lds(rb, (lds_u32_ptr)(base + FBN * KBYTES + (cw * F_B_LOADS + i) * 1024), 16, int(off), 0,
                                0, 0);
     }
   };
@@ -545,42 +558,48 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
 
-  // One K block: wait for its copies, start the next block's copies into the
-  // other stage, then run the MFMAs and the per-block epilogue.
-  auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt) {
+  // One K block: wait for its copies, then run the MFMAs and the per-block
+  // epilogue; a copying wave (COPY) issues the next block's copies into the
+  // other stage between its MFMAs, one every F_IL MFMAs.
+  auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt, auto copy_tag) __attribute__((always_inline)) {
+    constexpr bool COPY = decltype(copy_tag)::value;
     // this wave's copies into `cur` have landed; after the barrier everyone's
     // have, and every wave is done reading `nxt`
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const bool more = kb + 1 < kb_end;
-    if (more) issue_scales(kb + 1, nxt);
-    if (copier && more) {
-#pragma unroll
-      for (int c = 0; c < F_A_LOADS + F_B_LOADS; ++c) issue_one(kb + 1, nxt, c);
-    }
-
-    const float sw = wscale[wn][kb];
-    const float4 sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
+    if (kb + 1 < kb_end) issue_scales(kb + 1, nxt);
+    // the next block's copies; the last block copies itself again (in bounds,
+    // never read), so the chain needs no test
+    const int kcopy = min(kb + 1, kb_end - 1);
 
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + FBN * KBYTES;
-    v8i bf[TJ];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
+    auto read_b = [&](int j) {
       const int r = wm * WM + 16 * j + l16;
       const uint4 lo = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g));
       const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g + 1));
-      bf[j] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-    }
+      return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    };
     auto read_a = [&](int i) {
       const int r = wn * WN + 16 * i + l16;
       const uint4 lo = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g));
       const uint4 hi = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g + 1));
       return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
     };
+    // Reads in the order the chain needs them: the first MFMA waits only for
+    // its own two fragments while the other B fragments and the scales
+    // (needed two MFMAs later) are still on their way.
+    v8i bf[TJ];
     v8i af[2];
+    bf[0] = read_b(0);
     af[0] = read_a(0);
-    const float s[TJ] = {sa.x * sw, sa.y * sw, sa.z * sw, sa.w * sw};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 1; j < TJ; ++j) bf[j] = read_b(j);
+    __builtin_amdgcn_sched_barrier(0);
+    const float sw = wscale[wn][kb];
+    const float4 sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
+    float s[TJ];
     // The 32 MFMAs of the K block run as one rotated chain: the epilogue FMAs
     // that consume MFMA q's partial are issued after MFMA q + 2 (three
     // 4-register partial buffers), far enough behind for its result to be ready
@@ -596,7 +615,16 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
         part[q % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j],
                                                                              v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
       }
+      if constexpr (COPY) {
+        if (q % F_IL == F_IL - 1 && q / F_IL < F_A_LOADS + F_B_LOADS) issue_one(kcopy, nxt, q / F_IL);
+      }
       __builtin_amdgcn_sched_barrier(0);
+      if (q == LAG) {   // the scale products, first needed here
+        s[0] = sa.x * sw;
+        s[1] = sa.y * sw;
+        s[2] = sa.z * sw;
+        s[3] = sa.w * sw;
+      }
       if (q >= LAG) {
         const int c = q - LAG, ci = c / TJ, cj = c % TJ;
         acc[ci][cj] += part[c % (LAG + 1)] * s[cj];
@@ -606,39 +634,46 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     }
   };
 
-  for (int kb = kb_begin; kb < kb_end; kb += 2) {
-    step(kb, stage0, stage1);
-    if (kb + 1 < kb_end) step(kb + 1, stage1, stage0);
-  }
-
-  // ---- store
-  if (!whole || a.y_vec) {
-    // every wave is done reading both stages
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    uint8_t* buf = (wave < 4 ? stage0 : stage1) + (wave & 3) * (64 * F_OUT_PITCH);
-    if (!whole)
-      store_tile_via_lds<false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws,
-                                int64_t(R - a.rt_split0) * FBN - n0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
-    else if (a.y_bf16)
-      store_tile_via_lds<true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
-    else
-      store_tile_via_lds<false>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
-    return;
-  }
-  // unaligned output: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int m = m0 + wm * WM + 16 * j + l16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int n = n0 + wn * WN + 16 * i + 4 * g;
-      const int nvalid = mem.rows - n;
-      if (nvalid <= 0) continue;
-      store4(a.y, a.y_bf16, int64_t(m) * a.ldy + mem.col0 + n, nvalid, acc[i][j]);
+  // Copying waves and the others run separate copies of the main loop and
+  // the store, so no MFMA chain holds a branch (a branch in the chain costs
+  // the register allocator dearly).
+  auto finish = [&](auto copy_tag) __attribute__((always_inline)) {
+    for (int kb = kb_begin; kb < kb_end; kb += 2) {
+      step(kb, stage0, stage1, copy_tag);
+      if (kb + 1 < kb_end) step(kb + 1, stage1, stage0, copy_tag);
     }
-  }
+
+    // ---- store
+    if (!whole || a.y_vec) {
+      // every wave is done reading both stages
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      uint8_t* buf = (wave < 4 ? stage0 : stage1) + (wave & 3) * (64 * F_OUT_PITCH);
+      if (!whole)
+        store_tile_via_lds<false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws,
+                                  int64_t(R - a.rt_split0) * FBN - n0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+      else if (a.y_bf16)
+        store_tile_via_lds<true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+      else
+        store_tile_via_lds<false>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+      return;
+    }
+    // unaligned output: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
+  #pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * WM + 16 * j + l16;
+      if (m >= M) continue;
+  #pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int n = n0 + wn * WN + 16 * i + 4 * g;
+        const int nvalid = mem.rows - n;
+        if (nvalid <= 0) continue;
+        store4(a.y, a.y_bf16, int64_t(m) * a.ldy + mem.col0 + n, nvalid, acc[i][j]);
+      }
+    }
+  };
+  if (copier) finish(std::true_type{});
+  else finish(std::false_type{});
 }
 
 // Split-K partial sums: for workspace column c (row tile R = rt_split0 +
@@ -844,10 +879,10 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
       }
       a.ws = static_cast<float*>(ws);
     }
-    if (w.scale_bf16)
-      hipLaunchKernelGGL(w8a8_gemm_fast_kernel<true>, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL(w8a8_gemm_fast_kernel<false>, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
+    const bool kfull = w.K % KBYTES == 0;
+    auto kern = w.scale_bf16 ? (kfull ? w8a8_gemm_fast_kernel<true, true> : w8a8_gemm_fast_kernel<true, false>)
+                             : (kfull ? w8a8_gemm_fast_kernel<false, true> : w8a8_gemm_fast_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
     bsf8_status st = device_status(hipGetLastError(), "w8a8_gemm_fast launch");
     if (st != BSF8_OK || p.splits == 1) return st;
     ReduceArgs r{};

@@ -236,6 +236,29 @@ def test_w8a16_bf16_activations_and_f32_scales():
     assert_within(to_np(y8), O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), True, "f32 scales w8a8")
 
 
+@pytest.mark.parametrize("K", [384, 3072, 4000, 4224])
+def test_w8a16_few_tokens_sweep(K):
+    """M = 1..8 with F32 and BF16 activations, on K that give the few-token
+    kernel 1, 3, 4 and 5 chunks per wave (4000: a partial last chunk; 4224: 33
+    chunks, so the last wave has none), 200 rows (a ragged last row tile)."""
+    t = torch()
+    cfg = 131
+    m = synth.random_code_weight(cfg, f"sweep_W{K}", 200, K, scale_log2=(-9, -3))
+    w, _keep = weight_on_device([m])
+    om = oracle_members([m])
+    x_all = synth.gaussian_activations(cfg, f"sweep_X{K}", 8, K)
+    for M in range(1, 9):
+        x = x_all[:M]
+        banner(f"w8a16 sweep K={K} M={M} f32 {w.describe(B.ARM_W8A16, M)}")
+        y = B.linear_w8a16(w, t.from_numpy(x).to(device()))
+        assert_within(to_np(y), O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"K={K} M={M} f32")
+        xb = t.from_numpy(x).to(t.bfloat16)
+        x_exact = xb.float().numpy()
+        banner(f"w8a16 sweep K={K} M={M} bf16")
+        yb = B.linear_w8a16(w, xb.to(device()), out_dtype=t.bfloat16)
+        assert_within(to_np(yb), O.linear_w8a16(x_exact, om), O.abs_bound_w8a16(x_exact, om), True, f"K={K} M={M} bf16")
+
+
 def test_nan_weight_code_propagates_only_to_its_row():
     t = torch()
     m = synth.random_code_weight(103, "nan_W", 130, 256)
