@@ -306,19 +306,17 @@ constexpr int FBN = 256, FBM = 256, FTHREADS = 512;
 constexpr int F_SA = FBN * KBYTES + FBM * KBYTES;  // offset of the token scales in a stage
 constexpr int F_STAGE = F_SA + FBM * 4;           // 64 KiB of operands + 1 KiB of scales
 // Operand copies: 1 KiB wave copies (8 rows x 128 bytes) per stage, 32 weight
-// slabs and 32 token slabs, issued by waves 0-3 one after every second MFMA
-// of their chains.  The vector memory unit takes a 1 KiB copy about as fast
-// as it moves it, so a wave that issues its sixteen copies in one burst
-// stalls for most of a K block (as long as its chain); spread over the chain,
-// the stalls overlap MFMAs of both waves of the SIMD.  Waves 0-3 are the
-// older wave of each SIMD pair and win most MFMA issue slots, so their chains,
-// and the copies in them, run early.  (Copies spread over all eight waves go
-// out late: the younger waves' chains lag behind.)
+// slabs and 32 token slabs, issued by waves 0-3 between the MFMAs of their
+// chains.  The vector memory unit takes a 1 KiB copy about as fast as it
+// moves it, so a wave that issues its sixteen copies in one burst stalls for
+// most of a K block; spread over the chain, the stalls overlap MFMAs of both
+// waves of the SIMD.  Waves 0-3 are the older wave of each SIMD pair and win
+// most MFMA issue slots, so their chains, and the copies in them, run early.
+// (Copies spread over all eight waves go out late: the younger waves' chains
+// lag behind.)
 constexpr int F_COPIERS = 4;
 constexpr int F_A_LOADS = FBN / 8 / F_COPIERS;  // weight slabs per copying wave
 constexpr int F_B_LOADS = FBM / 8 / F_COPIERS;  // token slabs per copying wave
-constexpr int F_IL = TI * TJ / (F_A_LOADS + F_B_LOADS);  // MFMAs per copy in a copying wave's chain
-static_assert(F_IL >= 1 && F_IL * (F_A_LOADS + F_B_LOADS) <= TI * TJ, "copies fit the chain");
 constexpr int XCDS = 8;
 constexpr int GROUP_ROWS = 8;   // row tiles per L2 group
 constexpr int F_MAX_KB = 1024;  // K up to 131072 on the fast path
@@ -558,45 +556,57 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
 
-  // One K block: wait for its copies, then run the MFMAs and the per-block
-  // epilogue; a copying wave (COPY) issues the next block's copies into the
-  // other stage between its MFMAs, one every F_IL MFMAs.
-  auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt, auto copy_tag) __attribute__((always_inline)) {
-    constexpr bool COPY = decltype(copy_tag)::value;
-    // this wave's copies into `cur` have landed; after the barrier everyone's
-    // have, and every wave is done reading `nxt`
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 1 < kb_end) issue_scales(kb + 1, nxt);
-    // the next block's copies; the last block copies itself again (in bounds,
-    // never read), so the chain needs no test
-    const int kcopy = min(kb + 1, kb_end - 1);
-
-    const uint8_t* As = cur;
-    const uint8_t* Bs = cur + FBN * KBYTES;
-    auto read_b = [&](int j) {
-      const int r = wm * WM + 16 * j + l16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g));
-      const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g + 1));
-      return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-    };
-    auto read_a = [&](int i) {
-      const int r = wn * WN + 16 * i + l16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g));
-      const uint4 hi = *reinterpret_cast<const uint4*>(As + swz(r, 2 * g + 1));
-      return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-    };
-    // Reads in the order the chain needs them: the first MFMA waits only for
-    // its own two fragments while the other B fragments and the scales
-    // (needed two MFMAs later) are still on their way.
-    v8i bf[TJ];
-    v8i af[2];
-    bf[0] = read_b(0);
-    af[0] = read_a(0);
+  // LDS fragment reads of a stage (swizzled 128-byte rows).
+  auto read_b = [&](const uint8_t* st, int j) {
+    const uint8_t* Bs = st + FBN * KBYTES;
+    const int r = wm * WM + 16 * j + l16;
+    const uint4 lo = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(Bs + swz(r, 2 * g + 1));
+    return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+  };
+  auto read_a = [&](const uint8_t* st, int i) {
+    const int r = wn * WN + 16 * i + l16;
+    const uint4 lo = *reinterpret_cast<const uint4*>(st + swz(r, 2 * g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(st + swz(r, 2 * g + 1));
+    return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+  };
+  // A block's B fragments and first A fragment, in the order its chain needs
+  // them.
+  auto read_head = [&](const uint8_t* st, v8i(&bfx)[TJ], v8i& a0) __attribute__((always_inline)) {
+    bfx[0] = read_b(st, 0);
+    a0 = read_a(st, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 1; j < TJ; ++j) bf[j] = read_b(j);
+    for (int j = 1; j < TJ; ++j) bfx[j] = read_b(st, j);
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One K block, kb, in stage `cur`; block kb + 1 lands in `nxt`.  Its B
+  // fragments (bf) and first A fragment (af[0]) were read before it started.
+  // The block barrier sits at MFMA BARQ of the chain, the first MFMA of the
+  // last row tile, when every read of `cur` has been made: past it `cur` may
+  // be refilled (with block kb + 2), and the copies of block kb + 1 have
+  // landed, so the next block's first A fragment is read at once and each of
+  // its B fragments right after the last MFMA that uses the current one; the
+  // last row tile's MFMAs cover those reads and the next chain starts without
+  // waiting on a burst of LDS reads.  A copying wave issues two copies per
+  // MFMA: block kb + 2's first NTAIL right after the barrier (into `cur`),
+  // the rest over the next chain's first MFMAs, so every copy has most of a K
+  // block to land.  (One copy per MFMA over the chain's first MFMAs was slower
+  // on weights streamed from HBM; all sixteen at once stall the copying wave.)
+  // Near the end of the range the copies repeat the last block (in bounds,
+  // never read), so the chain needs no test.
+  constexpr int BARQ = (TI - 1) * TJ;
+  constexpr int NCOPY = F_A_LOADS + F_B_LOADS;
+  constexpr int CPM = 2;
+  constexpr int NTAIL = (TI * TJ - BARQ) * CPM;
+  static_assert(NTAIL <= NCOPY && (NCOPY - NTAIL) % CPM == 0 && (NCOPY - NTAIL) / CPM <= BARQ, "copies fit the chain");
+  auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt, v8i(&bf)[TJ], v8i(&af)[2],
+                  auto copy_tag) __attribute__((always_inline)) {
+    constexpr bool COPY = decltype(copy_tag)::value;
+    const int k1 = min(kb + 1, kb_end - 1);
+    const int k2 = min(kb + 2, kb_end - 1);
+    if (kb + 1 < kb_end) issue_scales(kb + 1, nxt);   // the next block's token scales
     const float sw = wscale[wn][kb];
     const float4 sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
     float s[TJ];
@@ -611,12 +621,27 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     for (int q = 0; q < TI * TJ + LAG; ++q) {
       if (q < TI * TJ) {
         const int i = q / TJ, j = q % TJ;
-        if (j == 0 && i + 1 < TI) af[(i + 1) & 1] = read_a(i + 1);
+        if (q == BARQ) {
+          // this wave's copies into `nxt` have landed and its reads of `cur`
+          // are done; after the barrier everyone's are
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          af[0] = read_a(nxt, 0);
+        }
+        if (j == 0 && i + 1 < TI) af[(i + 1) & 1] = read_a(cur, i + 1);
         part[q % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j],
                                                                              v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if (q >= BARQ) bf[j] = read_b(nxt, j);   // its last use in this block was the MFMA above
       }
       if constexpr (COPY) {
-        if (q % F_IL == F_IL - 1 && q / F_IL < F_A_LOADS + F_B_LOADS) issue_one(kcopy, nxt, q / F_IL);
+        if (q >= BARQ && q < TI * TJ) {
+#pragma unroll
+          for (int t = 0; t < CPM; ++t) issue_one(k2, const_cast<uint8_t*>(cur), CPM * (q - BARQ) + t);
+        }
+        if (q < (NCOPY - NTAIL) / CPM) {
+#pragma unroll
+          for (int t = 0; t < CPM; ++t) issue_one(k1, nxt, NTAIL + CPM * q + t);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (q == LAG) {   // the scale products, first needed here
@@ -634,13 +659,25 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     }
   };
 
+  // The second block's first copies (the ones a chain issues after its
+  // barrier), then the first block's head fragments.
+  if (copier) {
+    const int k1 = min(kb_begin + 1, kb_end - 1);
+#pragma unroll
+    for (int c = 0; c < NTAIL; ++c) issue_one(k1, stage1, c);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  v8i bf[TJ], af[2];
+  read_head(stage0, bf, af[0]);
+
   // Copying waves and the others run separate copies of the main loop and
   // the store, so no MFMA chain holds a branch (a branch in the chain costs
   // the register allocator dearly).
   auto finish = [&](auto copy_tag) __attribute__((always_inline)) {
     for (int kb = kb_begin; kb < kb_end; kb += 2) {
-      step(kb, stage0, stage1, copy_tag);
-      if (kb + 1 < kb_end) step(kb + 1, stage1, stage0, copy_tag);
+      step(kb, stage0, stage1, bf, af, copy_tag);
+      if (kb + 1 < kb_end) step(kb + 1, stage1, stage0, bf, af, copy_tag);
     }
 
     // ---- store
