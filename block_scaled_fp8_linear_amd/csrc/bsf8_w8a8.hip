@@ -111,10 +111,12 @@ __device__ __forceinline__ uint4 load_chunk(const uint8_t* row, int k, int K, bo
   return v;
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// F32 -> BF16 with round-to-nearest-even: gfx950's v_cvt_pk_bf16_f32 (one
+// instruction per pair; NaN stays NaN).
+typedef __bf16 bsf8_v2bf16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const bsf8_v2bf16 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 
@@ -122,15 +124,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ void store4(void* yv, int bf16, int64_t off, int nvalid, const v4f& v) {
   if (bf16) {
     uint16_t* y = static_cast<uint16_t*>(yv) + off;
-    const uint16_t b0 = f32_to_bf16_rne(v[0]), b1 = f32_to_bf16_rne(v[1]);
-    const uint16_t b2 = f32_to_bf16_rne(v[2]), b3 = f32_to_bf16_rne(v[3]);
+    const uint32_t p01 = bf16_pair(v[0], v[1]), p23 = bf16_pair(v[2], v[3]);
     if (nvalid >= 4 && (reinterpret_cast<uintptr_t>(y) & 7) == 0) {
-      *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(b0) | (uint32_t(b1) << 16), uint32_t(b2) | (uint32_t(b3) << 16));
+      *reinterpret_cast<uint2*>(y) = make_uint2(p01, p23);
     } else {
-      y[0] = b0;
-      if (nvalid > 1) y[1] = b1;
-      if (nvalid > 2) y[2] = b2;
-      if (nvalid > 3) y[3] = b3;
+      y[0] = uint16_t(p01);
+      if (nvalid > 1) y[1] = uint16_t(p01 >> 16);
+      if (nvalid > 2) y[2] = uint16_t(p23);
+      if (nvalid > 3) y[3] = uint16_t(p23 >> 16);
     }
   } else {
     float* y = static_cast<float*>(yv) + off;
@@ -381,9 +382,7 @@ __device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uin
         const v4f& v = acc[i0 + ii][j];
         uint8_t* dst = buf + (16 * j + l16) * F_OUT_PITCH + (ii * 16 + 4 * g) * ESZ;
         if (YBF16) {
-          *reinterpret_cast<uint2*>(dst) =
-              make_uint2(uint32_t(f32_to_bf16_rne(v[0])) | (uint32_t(f32_to_bf16_rne(v[1])) << 16),
-                         uint32_t(f32_to_bf16_rne(v[2])) | (uint32_t(f32_to_bf16_rne(v[3])) << 16));
+          *reinterpret_cast<uint2*>(dst) = make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
         } else {
           *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         }
