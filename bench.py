@@ -21,10 +21,14 @@ The same JSON line also carries:
   Cache cannot serve them, per-launch median / p10 / p90 over 100 replays,
   with an HBM roofline on algorithmic bytes and a plain read of the same bytes
   (``bsf8_read_stream``) as context;
+* ``rotated``: the same step and GEMM calls with two copies of both weights
+  used in turn, so the weights come from HBM rather than the Infinity Cache
+  (the headline figures above are warm: one copy, reused every step);
 * ``qkv_prefill``: grouped Q/K/V W8A8 at M = 512;
-* ``large_prefill``: the W8A8 GEMM at M=8192, K=7168, N=18432;
+* ``large_prefill``: the W8A8 GEMM at M=8192, K=7168, N=18432, warm and
+  rotated over three weight copies;
 * ``cpu_baseline``: the oracle (NumPy) on the host cores, running the same
-  prefill step for about ten seconds.
+  prefill step for about ten seconds, with the median time of each part.
 
 Inputs are seeded synthetic data (``synth``) already resident in HBM before
 timing starts.
@@ -32,6 +36,7 @@ timing starts.
 from __future__ import annotations
 
 import argparse
+import statistics
 import json
 import os
 import sys
@@ -227,7 +232,42 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
         del g
     flop_gu = 2.0 * M * w_gu.n_total * w_gu.K
     flop_dn = 2.0 * M * w_dn.n_total * w_dn.K
-    res = dict(
+    # Rotated: a second copy of both weights, and graphs that alternate the
+    # copies, so each call's weights (178 + 89 MB per copy) were last touched a
+    # copy ago and the 256 MB Infinity Cache cannot hold them between uses.
+    w_gu2 = B.BlockFP8Weight([(t.clone(), sc.clone()) for t, sc in w_gu.members])
+    w_dn2 = B.BlockFP8Weight([(t.clone(), sc.clone()) for t, sc in w_dn.members])
+    ws_gu2 = w_gu2.workspace(B.ARM_W8A8, M)
+    ws_dn2 = w_dn2.workspace(B.ARM_W8A8, M)
+
+    def step2():
+        step()
+        B.quant_act(x_gu, xq_gu, xs_gu)
+        B.linear_w8a8(w_gu2, xq_gu, xs_gu, out=y_gu, workspace=ws_gu2)
+        B.quant_act(x_dn, xq_dn, xs_dn)
+        B.linear_w8a8(w_dn2, xq_dn, xs_dn, out=y_dn, workspace=ws_dn2)
+
+    g_rot = graph_of(torch, step2)
+    settle(torch, g_rot.replay, 0.5)
+    ms_step_rot = replay_ms(torch, g_rot, max(5, steps // 2)) / 2
+    del g_rot
+    rot_stats = {}
+    for name, wa, wsa, wb, wsb, xq_, xs_, y_ in (("gemm_gate_up", w_gu, ws_gu, w_gu2, ws_gu2, xq_gu, xs_gu, y_gu),
+                                                 ("gemm_down", w_dn, ws_dn, w_dn2, ws_dn2, xq_dn, xs_dn, y_dn)):
+        def alt(wa=wa, wsa=wsa, wb=wb, wsb=wsb, xq_=xq_, xs_=xs_, y_=y_):
+            B.linear_w8a8(wa, xq_, xs_, out=y_, workspace=wsa)
+            B.linear_w8a8(wb, xq_, xs_, out=y_, workspace=wsb)
+        g = graph_of(torch, alt, 10)
+        g.replay()
+        st = replay_stats(torch, g, 20, 20)
+        rot_stats[name] = {k: (round(v * 1e3, 2) if k != "launches" else v) for k, v in st.items()}
+        del g
+    rotated = dict(ms_per_step=ms_step_rot, tflops=(flop_gu + flop_dn) / (ms_step_rot * 1e-3) / 1e12,
+                   kernels_us_stats=rot_stats,
+                   gemm_gate_up_tflops=flop_gu / (rot_stats["gemm_gate_up"]["mean"] * 1e-6) / 1e12,
+                   gemm_down_tflops=flop_dn / (rot_stats["gemm_down"]["mean"] * 1e-6) / 1e12)
+    del w_gu2, w_dn2
+    res = dict(rotated=rotated,
         ms_per_step=ms_step, wall_s=wall, flop_per_step=flop_gu + flop_dn,
         tflops=(flop_gu + flop_dn) / (ms_step * 1e-3) / 1e12,
         kernels_ms=kms, kernels_us_stats=kstats, sclk=sclk,
@@ -336,7 +376,20 @@ def bench_large(torch, B, synth, steps, dev):
     q_ms = replay_ms(torch, g_quant, 5) / 4
     flop = 2.0 * M * w.n_total * w.K
     del g_gemm, g_quant
+    # rotated: three copies of the 132 MB weight, called in turn (396 MB > the
+    # 256 MB Infinity Cache)
+    copies = [w] + [B.BlockFP8Weight([(t.clone(), sc.clone()) for t, sc in w.members]) for _ in range(2)]
+    wss = [c.workspace(B.ARM_W8A8, M) for c in copies]
+
+    def rot():
+        for c, wsc in zip(copies, wss):
+            B.linear_w8a8(c, xq, xs, out=y, workspace=wsc)
+    g_rot = graph_of(torch, rot)
+    settle(torch, g_rot.replay, 0.5)
+    ms_rot = replay_ms(torch, g_rot, max(3, steps // 4)) / len(copies)
+    del g_rot, copies
     return dict(gemm_us=ms * 1e3, tflops=flop / (ms * 1e-3) / 1e12, frac=flop / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+                rotated_gemm_us=ms_rot * 1e3, rotated_tflops=flop / (ms_rot * 1e-3) / 1e12,
                 quant_us=q_ms * 1e3, describe=w.describe(B.ARM_W8A8, M))
 
 
@@ -377,17 +430,34 @@ def cpu_baseline(synth, budget_s=10.0):
         for r0 in range(0, total, 1024):
             O.linear_w8a8_rows(xq, xs, members, list(range(r0, min(total, r0 + 1024))))
 
+    parts = {"quant_gate_up": [], "gemm_gate_up": [], "quant_down": [], "gemm_down": []}
     reps, t0 = 0, time.perf_counter()
     while reps == 0 or time.perf_counter() - t0 < budget_s:
+        ta = time.perf_counter()
         xq, xs = O.quant_act(gu.x)
+        tb = time.perf_counter()
         gemm(xq, xs, m_gu)
+        tc = time.perf_counter()
         xq, xs = O.quant_act(dn.x)
+        td = time.perf_counter()
         gemm(xq, xs, m_dn)
+        te = time.perf_counter()
+        for k, v in zip(parts, (tb - ta, tc - tb, td - tc, te - td)):
+            parts[k].append(v)
         reps += 1
     t = (time.perf_counter() - t0) / reps
+    blas = "unknown"
+    try:
+        import threadpoolctl
+        blas = ",".join(sorted({d.get("internal_api", "?") for d in threadpoolctl.threadpool_info()
+                                if d.get("user_api") == "blas"})) or "none"
+    except Exception:
+        pass
     return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"the whole prefill step (quantize + W8A8 gate/up + quantize + W8A8 down, M=1024) in float64 "
-                      f"NumPy, {reps} repetition(s), {t:.2f} s each"}
+                      f"NumPy, {reps} repetition(s), {t:.2f} s each",
+            "parts_s_median": {k: round(statistics.median(v), 3) for k, v in parts.items()},
+            "blas": blas, "host_cpus": os.cpu_count()}
 
 
 def main():
@@ -455,6 +525,12 @@ def main():
         "gemm_down_tflops": round(pre["gemm_down_tflops"], 2),
         "quant_gbs": {"gate_up": round(pre["quant_gate_up_gbs"], 1), "down": round(pre["quant_down_gbs"], 1)},
         "path": {"gate_up": pre["describe_gate_up"], "down": pre["describe_down"]},
+        "rotated": {"note": "two copies of both weights, used in turn (534 MB > the 256 MB Infinity Cache)",
+                    "ms_per_step": round(pre["rotated"]["ms_per_step"], 4),
+                    "tflops": round(pre["rotated"]["tflops"], 2),
+                    "gemm_gate_up_tflops": round(pre["rotated"]["gemm_gate_up_tflops"], 2),
+                    "gemm_down_tflops": round(pre["rotated"]["gemm_down_tflops"], 2),
+                    "kernels_us_stats": pre["rotated"]["kernels_us_stats"]},
         "timing": "HIP graph replays: one replay per step; kernel times from graphs of 20 back-to-back launches",
         "fixture_sha256": pre["fixture_sha256"],
     }
@@ -483,6 +559,9 @@ def main():
         line["large_prefill"] = {"workload": "W8A8 GEMM M=8192 K=7168 N=18432, bf16 out",
                                  "tflops": round(l["tflops"], 2), "frac": round(l["frac"], 4),
                                  "gemm_us": round(l["gemm_us"], 1), "quant_us": round(l["quant_us"], 1),
+                                 "rotated": {"note": "three weight copies used in turn (396 MB)",
+                                             "gemm_us": round(l["rotated_gemm_us"], 1),
+                                             "tflops": round(l["rotated_tflops"], 2)},
                                  "path": l["describe"]}
     if "copy_calibration" in extra:
         line["copy_calibration"] = extra["copy_calibration"]

@@ -198,6 +198,11 @@ class BlockFP8Weight:
     def handle(self):
         return self._h
 
+    @property
+    def members(self):
+        """The borrowed (weight, scale_inv) device tensors, in member order."""
+        return [(self._tensors[i], self._tensors[i + 1]) for i in range(0, len(self._tensors), 2)]
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and _lib is not None:
