@@ -381,12 +381,16 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 // In a chunk, lane group gq owns the 32 contiguous K bytes [32 gq, 32 gq + 32)
 // of both operands, and K-step s of the 16x16x32 MFMA the 8 at 32 gq + 8 s.
 // LDS layouts (16-byte pieces, bank-conflict free for the fragment reads):
-//  weight buffer: row r of the wave's 32 at r * 128, piece p at p ^ ((r >> 1) & 7);
+//  weight buffer: row r of the wave's 32 at r * 128, piece p at p ^ s(r), with s
+//  the permutation of r & 7 that puts even rows on {0, 1, 4, 5} and odd rows on
+//  {2, 3, 6, 7}, so a fragment read's 16 lanes over two lane groups hit all 64
+//  banks once (with s(r) = (r >> 1) & 7 they collide in pairs);
 //  activation scratch: term u, token t at u * SM_TERM_BYTES + t * 256, piece p at p ^ t.
 // Per-chunk scaling and the wave-order reduction are those of the general
 // kernel.
 // ---------------------------------------------------------------------------
 constexpr int SM_MAXM = 8;
+__device__ __forceinline__ int sm_swz(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
 constexpr int SM_ZERO_ROW = SM_MAXM;           // scratch row that stays zero
 constexpr int SM_ROW_BYTES = CHUNK * 2;        // one token's chunk as BF16
 constexpr int SM_TERM_BYTES = (SM_MAXM + 1) * SM_ROW_BYTES;
@@ -547,12 +551,12 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 #pragma unroll
       for (int q = 0; q < 2 * RT; ++q) {
         const int rr = 8 * q + crow;
-        *reinterpret_cast<uint4*>(wb + rr * CHUNK + ((cpiece ^ ((rr >> 1) & 7)) * 16)) = wr[d][q];
+        *reinterpret_cast<uint4*>(wb + rr * CHUNK + ((cpiece ^ sm_swz(rr)) * 16)) = wr[d][q];
       }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int rr = 16 * t + l16;
-        const int sw8 = (rr >> 1) & 7;
+        const int sw8 = sm_swz(rr);
         const uint4 lo = *reinterpret_cast<const uint4*>(wb + rr * CHUNK + (((2 * gq) ^ sw8) * 16));
         const uint4 hi = *reinterpret_cast<const uint4*>(wb + rr * CHUNK + (((2 * gq + 1) ^ sw8) * 16));
         const v8bf af[STEPS] = {cvt8(lo.x, lo.y), cvt8(lo.z, lo.w), cvt8(hi.x, hi.y), cvt8(hi.z, hi.w)};
