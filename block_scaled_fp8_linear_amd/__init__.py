@@ -168,20 +168,25 @@ class BlockFP8Weight:
 
     ``members``: list of (weight, scale_inv) device tensors; weight is uint8 or
     float8_e4m3fn [N_i, K] (contiguous), scale_inv is bfloat16 or float32
-    [ceil(N_i/128), ceil(K/128)] (contiguous).  The tensors are borrowed: this
-    object keeps references so they stay alive, and never modifies them.
+    [ceil(N_i/128), ceil(K/128)] (contiguous).  With ``block=(0, 0)`` the
+    weight is per-tensor scaled instead: each member's scale is its single
+    ``weight_scale`` value (a 0-d or one-element tensor), read as one block that
+    covers the whole member.  The tensors are borrowed: this object keeps
+    references so they stay alive, and never modifies them.
     """
 
     def __init__(self, members: Sequence[Tuple[object, object]], quant_method: str = "fp8", block=(BLOCK, BLOCK)):
         L = lib()
         descs = []
         self._tensors = []
+        leaf = "scale" if tuple(int(b) for b in block) == (0, 0) else "scale_inv"
+        self.per_tensor = leaf == "scale"
         for w, s in members:
             if not (w.is_contiguous() and s.is_contiguous()):
                 raise ValueError("weights and scale grids must be contiguous")
             wdt = DT_F8_E4M3 if _dt_of(w) in (DT_U8, DT_F8_E4M3) else _dt_of(w)
-            descs.append(dict(weight=dict(dtype=wdt, shape=tuple(w.shape), addr=w.data_ptr()),
-                              scale_inv=dict(dtype=_dt_of(s), shape=tuple(s.shape), addr=s.data_ptr())))
+            descs.append({"weight": dict(dtype=wdt, shape=tuple(w.shape), addr=w.data_ptr()),
+                          leaf: dict(dtype=_dt_of(s), shape=tuple(s.shape), addr=s.data_ptr())})
             self._tensors += [w, s]
         decl = _decl(quant_method, block)
         arr, keep = _members_array(descs)

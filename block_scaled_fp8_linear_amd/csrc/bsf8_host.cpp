@@ -40,6 +40,9 @@ static bsf8_status fail(bsf8_status s, const char* fmt, ...) {
   return s;
 }
 
+// The member's scale leaf: the block grid, or the per-tensor weight_scale.
+static const bsf8_tensor_desc* scale_leaf(const bsf8_member_desc& m) { return m.scale_inv ? m.scale_inv : m.scale; }
+
 static bool shape_is(const bsf8_tensor_desc* t, int64_t a, int64_t b) {
   return t->rank == 2 && t->shape[0] == a && t->shape[1] == b;
 }
@@ -49,8 +52,10 @@ static bool shape_is(const bsf8_tensor_desc* t, int64_t a, int64_t b) {
 static bsf8_status validate_impl(const bsf8_decl* decl, const bsf8_member_desc* members, int32_t n) {
   if (decl == nullptr || (members == nullptr && n > 0)) return fail(BSF8_E_INVALID_ARG, "null descriptor");
   if (n < 1 || n > kMaxMembers) return fail(BSF8_E_GROUP, "%d members (1..%d allowed)", n, kMaxMembers);
-  if (!decl->quant_method_fp8 || decl->block_n != kBlock || decl->block_k != kBlock)
-    return fail(BSF8_E_DECL, "declaration is not quant_method fp8 with weight_block_size [128,128] (got fp8=%d, [%d,%d])",
+  const bool per_tensor = decl->quant_method_fp8 && decl->block_n == 0 && decl->block_k == 0;
+  if (!decl->quant_method_fp8 || (!per_tensor && (decl->block_n != kBlock || decl->block_k != kBlock)))
+    return fail(BSF8_E_DECL,
+                "declaration is not quant_method fp8 with weight_block_size [128,128] or per-tensor (got fp8=%d, [%d,%d])",
                 decl->quant_method_fp8, decl->block_n, decl->block_k);
   for (int i = 0; i < n; ++i) {
     const bsf8_member_desc& m = members[i];
@@ -66,6 +71,16 @@ static bsf8_status validate_impl(const bsf8_decl* decl, const bsf8_member_desc* 
       return fail(BSF8_E_SCALE_AMBIGUOUS, "member %d: both a block grid and a row/tensor scale", i);
     const bsf8_tensor_desc* leaf = m.scale_inv ? m.scale_inv : m.scale;
     if (leaf->rank < 0 || leaf->rank > 4) return fail(BSF8_E_INVALID_ARG, "member %d: scale rank %d", i, leaf->rank);
+    if (per_tensor) {
+      // one weight_scale value for the whole tensor (rank 0, or rank 1 of one element)
+      if (m.scale_inv != nullptr)
+        return fail(BSF8_E_DECL, "member %d: a weight_scale_inv grid under a per-tensor declaration", i);
+      if (leaf->rank == 1 && leaf->shape[0] != 1) return fail(BSF8_E_SCALE_ROWWISE, "member %d: rank-1 (row-wise) scale", i);
+      if (leaf->rank > 1) return fail(BSF8_E_SCALE_RANK, "member %d: per-tensor scale of rank %d", i, leaf->rank);
+      if (leaf->dtype != BSF8_DT_BF16 && leaf->dtype != BSF8_DT_F32)
+        return fail(BSF8_E_SCALE_DTYPE, "member %d: scale dtype %d is not BF16/F32", i, leaf->dtype);
+      continue;
+    }
     if (leaf->rank == 1) return fail(BSF8_E_SCALE_ROWWISE, "member %d: rank-1 (row-wise) scale", i);
     if (leaf->rank == 0 && m.scale != nullptr) return fail(BSF8_E_SCALE_PER_TENSOR, "member %d: per-tensor scale", i);
     if (leaf->rank != 2) return fail(BSF8_E_SCALE_RANK, "member %d: scale rank %d", i, leaf->rank);
@@ -82,16 +97,16 @@ static bsf8_status validate_impl(const bsf8_decl* decl, const bsf8_member_desc* 
       return fail(BSF8_E_SCALE_GRID, "member %d: a block-shaped weight_scale leaf is not a weight_scale_inv grid", i);
   }
   const int64_t k0 = members[0].weight.shape[1];
-  const int32_t dt0 = members[0].scale_inv->dtype;
+  const int32_t dt0 = scale_leaf(members[0])->dtype;
   for (int i = 1; i < n; ++i) {
     if (members[i].weight.shape[1] != k0) return fail(BSF8_E_GROUP, "member %d: K differs from member 0", i);
-    if (members[i].scale_inv->dtype != dt0) return fail(BSF8_E_GROUP, "member %d: scale dtype differs from member 0", i);
+    if (scale_leaf(members[i])->dtype != dt0) return fail(BSF8_E_GROUP, "member %d: scale dtype differs from member 0", i);
   }
   for (int i = 0; i < n; ++i) {
     const uintptr_t wa = reinterpret_cast<uintptr_t>(members[i].weight.data);
     if (wa % 16 != 0) return fail(BSF8_E_ALIGNMENT, "member %d: weight address not 16-byte aligned", i);
-    const uintptr_t sa = reinterpret_cast<uintptr_t>(members[i].scale_inv->data);
-    const uintptr_t esz = members[i].scale_inv->dtype == BSF8_DT_BF16 ? 2 : 4;
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_leaf(members[i])->data);
+    const uintptr_t esz = scale_leaf(members[i])->dtype == BSF8_DT_BF16 ? 2 : 4;
     if (sa % esz != 0) return fail(BSF8_E_ALIGNMENT, "member %d: scale address not element aligned", i);
   }
   return BSF8_OK;
@@ -150,7 +165,7 @@ bsf8_status bsf8_weight_create(const bsf8_decl* decl, const bsf8_member_desc* me
   const int64_t K = members[0].weight.shape[1];
   int64_t total = 0;
   for (int i = 0; i < n_members; ++i) {
-    if (members[i].weight.data == nullptr || members[i].scale_inv->data == nullptr)
+    if (members[i].weight.data == nullptr || scale_leaf(members[i])->data == nullptr)
       return fail(BSF8_E_INVALID_ARG, "member %d: a handle needs device addresses", i);
     total += members[i].weight.shape[0];
   }
@@ -161,20 +176,23 @@ bsf8_status bsf8_weight_create(const bsf8_decl* decl, const bsf8_member_desc* me
   h->dev.n_members = n_members;
   h->dev.K = static_cast<int32_t>(K);
   h->dev.Kb = static_cast<int32_t>(ceil_div(K, kBlock));
-  h->dev.scale_bf16 = members[0].scale_inv->dtype == BSF8_DT_BF16 ? 1 : 0;
+  h->dev.scale_bf16 = scale_leaf(members[0])->dtype == BSF8_DT_BF16 ? 1 : 0;
+  h->per_tensor = members[0].scale_inv == nullptr;
+  h->dev.s_rs = h->per_tensor ? 0 : h->dev.Kb;
+  h->dev.s_cs = h->per_tensor ? 0 : 1;
   h->aligned16 = (K % 16) == 0;
   int64_t col = 0, srow = 0;
   for (int i = 0; i < n_members; ++i) {
     const int64_t rows = members[i].weight.shape[0];
     h->dev.m[i].w = static_cast<const uint8_t*>(members[i].weight.data);
-    h->dev.m[i].s = members[i].scale_inv->data;
+    h->dev.m[i].s = scale_leaf(members[i])->data;
     h->dev.m[i].rows = static_cast<int32_t>(rows);
     h->dev.m[i].col0 = static_cast<int32_t>(col);
     h->rows[i] = rows;
     h->col0[i] = col;
     h->srow0[i] = srow;
     col += rows;
-    srow += ceil_div(rows, kBlock);
+    srow += h->per_tensor ? 1 : ceil_div(rows, kBlock);
   }
   h->n_total = total;
   *out = h;
@@ -197,7 +215,7 @@ bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* memb
   if (n < 0 || n >= w->n_total) return fail(BSF8_E_INVALID_ARG, "row %lld outside [0,%lld)", (long long)n, (long long)w->n_total);
   for (int i = w->dev.n_members - 1; i >= 0; --i) {
     if (n >= w->col0[i]) {
-      const int64_t r = (n - w->col0[i]) / kBlock;
+      const int64_t r = w->per_tensor ? 0 : (n - w->col0[i]) / kBlock;
       if (member) *member = i;
       if (local_row) *local_row = r;
       if (stacked_row) *stacked_row = w->srow0[i] + r;
@@ -290,8 +308,8 @@ bsf8_status bsf8_read_stream(const void* p, int64_t bytes, uint32_t* sink, void*
 const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M) {
   if (w == nullptr) return nullptr;
   char geo[256];
-  snprintf(geo, sizeof(geo), " | weight N=%lld K=%d members=%d scales=%s", (long long)w->n_total, w->dev.K,
-           w->dev.n_members, w->dev.scale_bf16 ? "bf16" : "f32");
+  snprintf(geo, sizeof(geo), " | weight N=%lld K=%d members=%d scales=%s%s", (long long)w->n_total, w->dev.K,
+           w->dev.n_members, w->dev.scale_bf16 ? "bf16" : "f32", w->per_tensor ? " per-tensor" : "");
   if (arm == BSF8_ARM_W8A16) g_describe = describe_w8a16(w->dev, w->aligned16, M) + geo;
   else if (arm == BSF8_ARM_W8A8) g_describe = describe_w8a8(w->dev, w->aligned16, M) + geo;
   else g_describe = "unknown arm";

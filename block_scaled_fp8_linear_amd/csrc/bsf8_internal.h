@@ -18,7 +18,7 @@ constexpr int kMaxMembers = BSF8_MAX_MEMBERS;
 // One grouped member as the kernels see it (passed by value in kernel args).
 struct MemberDev {
   const uint8_t* w;   // [rows, K] E4M3 bytes, row stride K
-  const void* s;      // [ceil(rows/128), Kb] BF16 or F32 scales, row stride Kb
+  const void* s;      // BF16 or F32 scales: the [ceil(rows/128), Kb] grid, or one per-tensor value
   int32_t rows;       // N_i
   int32_t col0;       // R_i: first output feature of this member in Y
 };
@@ -29,6 +29,11 @@ struct WeightDev {
   int32_t K;
   int32_t Kb;          // ceil(K/128)
   int32_t scale_bf16;  // 1: BF16 scales, 0: F32 scales
+  // Scale of (128-row block r, 128-wide K block kb) is s[r * s_rs + kb * s_cs]:
+  // (Kb, 1) for a block grid, (0, 0) for a per-tensor scale (the degenerate
+  // block that covers the whole tensor).
+  int32_t s_rs;
+  int32_t s_cs;
 };
 
 // Per-launch tile table: member i owns tiles [tile0[i], tile0[i+1]).
@@ -68,4 +73,5 @@ struct bsf8_weight {
   int64_t col0[bsf8::kMaxMembers];
   int64_t srow0[bsf8::kMaxMembers];  // B_i: origin of member i in the stacked grids
   bool aligned16;                    // K % 16 == 0 and every weight pointer 16-byte aligned
+  bool per_tensor;                   // one scale per member (per-tensor layout) instead of a block grid
 };

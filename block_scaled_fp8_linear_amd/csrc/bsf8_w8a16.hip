@@ -220,8 +220,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
   // Both 16-row tiles of a 32-row block lie in the same 128-row block, so the
   // block uses one row of the member's scale grid: stage it in LDS once.
   {
-    const int64_t sr = int64_t((rtile * ROWS) >> 7) * Kb;
-    for (int i = tid; i < Kb; i += THREADS) srow[i] = load_scale<SBF16>(mem.s, sr + i);
+    const int64_t sr = int64_t((rtile * ROWS) >> 7) * a.w.s_rs;
+    for (int i = tid; i < Kb; i += THREADS) srow[i] = load_scale<SBF16>(mem.s, sr + int64_t(i) * a.w.s_cs);
   }
   __syncthreads();
   const int c_begin = min(Kb, wave * a.chunks_per_wave);
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   const int l16 = lane & 15, gq = lane >> 4;
   const int c_begin = min(Kb, wave * a.chunks_per_wave);
   const int c_end = min(Kb, c_begin + a.chunks_per_wave);
-  const int64_t srow0 = int64_t((rtile * ROWS) >> 7) * Kb;   // both row tiles share one scale row
+  const int64_t srow0 = int64_t((rtile * ROWS) >> 7) * a.w.s_rs;   // both row tiles share one scale row
 
   uint8_t* sc = scratch[wave];
   for (int i = lane; i < NT * SM_TERM_BYTES / 16; i += 64) reinterpret_cast<uint4*>(sc)[i] = make_uint4(0, 0, 0, 0);
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   const uint32_t x_esz = XBF16 ? 2u : 4u;
   const uint32_t x_bytes = uint32_t(M) * uint32_t(a.ldx) * x_esz;
   const uint32_t s_esz = SBF16 ? 2u : 4u;
-  const uint32_t s_bytes = uint32_t((mem.rows + 127) >> 7) * uint32_t(Kb) * s_esz;
+  const uint32_t s_bytes = (a.w.s_rs ? uint32_t((mem.rows + 127) >> 7) * uint32_t(Kb) : 1u) * s_esz;
   const v4i rw = make_rsrc(mem.w, w_bytes);
   const v4i rx = make_rsrc(a.x, x_bytes);
   const v4i rs = make_rsrc(mem.s, s_bytes);
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 #pragma unroll
   for (int h = 0; h < SM_SCALE_REGS; ++h) {
     const int c = c_begin + 64 * h + lane;
-    const int so = c < c_end ? int((srow0 + c) * s_esz) : int(s_bytes);
+    const int so = c < c_end ? int((srow0 + int64_t(c) * a.w.s_cs) * s_esz) : int(s_bytes);
     sraw[h] = SBF16 ? uint32_t(uint16_t(bsf8_raw_buffer_load_b16(rs, so, 0, 0)))
                     : uint32_t(bsf8_raw_buffer_load_b32(rs, so, 0, 0));
   }

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
   const int srow = (n0 + wn * WN) >> 7;
   const int nb = (mem.rows + 127) >> 7;
   const bool srow_ok = srow < nb;
-  const int64_t s_base = int64_t(srow_ok ? srow : 0) * Kb;
+  const int64_t s_base = int64_t(srow_ok ? srow : 0) * a.w.s_rs;
   const float* xs_row[TJ];
   bool m_ok[TJ];
 #pragma unroll
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) s[j] = sa_next[j] * sw;
     if (more) {
-      sw_next = srow_ok ? load_scale(mem.s, s_base + kb + 1, a.w.scale_bf16) : 0.f;
+      sw_next = srow_ok ? load_scale(mem.s, s_base + int64_t(kb + 1) * a.w.s_cs, a.w.scale_bf16) : 0.f;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) sa_next[j] = m_ok[j] ? xs_row[j][kb + 1] : 0.f;
     }
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     for (int i = tid; i < 2 * Kb; i += FTHREADS) {
       const int h = i >= Kb, kb = i - h * Kb;
       const int srow = (n0 >> 7) + h;
-      wscale[h][kb] = srow < nb ? load_scale_t<SBF16>(mem.s, int64_t(srow) * Kb + kb) : 0.f;
+      wscale[h][kb] = srow < nb ? load_scale_t<SBF16>(mem.s, int64_t(srow) * a.w.s_rs + int64_t(kb) * a.w.s_cs) : 0.f;
     }
   }
 

@@ -108,11 +108,14 @@ typedef struct bsf8_member_desc {
   const bsf8_tensor_desc* scale;
 } bsf8_member_desc;
 
-/* The checkpoint's quantization_config as declared. */
+/* The checkpoint's quantization_config as declared.  block_n = block_k = 0
+ * declares the per-tensor layout (no weight_block_size: one weight_scale per
+ * tensor, read as the degenerate block that covers the whole tensor; "FP8
+ * Native Serving", section "The two FP8 checkpoint shapes"). */
 typedef struct bsf8_decl {
   int32_t quant_method_fp8;  /* nonzero when quant_method is "fp8" */
-  int32_t block_n;           /* weight_block_size[0] */
-  int32_t block_k;           /* weight_block_size[1] */
+  int32_t block_n;           /* weight_block_size[0], or 0 for per-tensor */
+  int32_t block_k;           /* weight_block_size[1], or 0 for per-tensor */
 } bsf8_decl;
 
 typedef struct bsf8_weight bsf8_weight;
@@ -146,16 +149,22 @@ const char* bsf8_last_error(void);
  *   not 16-byte aligned for weights, not element aligned for scales).
  * A square grid (Nb == Kb) given transposed has the right shape and cannot be
  * detected from headers; it is accepted.
+ * Under a per-tensor declaration (block 0 x 0) each member needs a scale
+ * (weight_scale) leaf holding one BF16 or F32 value (rank 0, or rank 1 of
+ * shape [1]); a scale_inv grid disagrees with the declaration (DECL), a
+ * longer rank-1 leaf is SCALE_ROWWISE and a higher rank SCALE_RANK.  A rank-0
+ * scale under the [128,128] declaration stays SCALE_PER_TENSOR.
  */
 bsf8_status bsf8_validate(const bsf8_decl* decl, const bsf8_member_desc* members, int32_t n_members);
 
 /*
  * bsf8_weight_create -- validate (as bsf8_validate) and build an immutable
- * handle over borrowed device pointers.  Every weight and scale_inv data
- * pointer must be non-NULL.  Host-only: no device access.
+ * handle over borrowed device pointers.  Every weight and scale data pointer
+ * must be non-NULL.  Host-only: no device access.
  * Member i owns output rows [R_i, R_i + N_i) with R_i = sum_{j<i} N_j; its
  * scale grid is its own [ceil(N_i/128), ceil(K/128)] array (member-local
- * origin).  On failure *out is set to NULL.
+ * origin), or, per-tensor, its own single value used for every block.  On
+ * failure *out is set to NULL.
  */
 bsf8_status bsf8_weight_create(const bsf8_decl* decl, const bsf8_member_desc* members,
                                int32_t n_members, bsf8_weight** out);
@@ -170,7 +179,9 @@ bsf8_status bsf8_weight_geometry(const bsf8_weight* w, int64_t* n_total, int64_t
  * bsf8_weight_scale_row -- for output feature n in [0, N), the member index and
  * the row of that member's scale grid the kernels use: (n - R_i) / 128.
  * Also returns the row of the members' grids stacked in member order,
- * B_i + (n - R_i) / 128 with B_i = sum_{j<i} ceil(N_j/128).  Host-only.
+ * B_i + (n - R_i) / 128 with B_i = sum_{j<i} ceil(N_j/128).  For a
+ * per-tensor weight the local row is 0 and the stacked row is i (one value
+ * per member).  Host-only.
  */
 bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* member,
                                   int64_t* local_row, int64_t* stacked_row);

@@ -38,7 +38,7 @@ __all__ = [
     "e4m3_table", "e4m3_decode", "e4m3_encode", "e4m3_encode_scalar",
     "bf16_bits_to_f32", "f32_to_bf16_bits", "f32_to_bf16",
     "scale_grid_shape", "member_table", "stacked_scale_row",
-    "dequantize_block_scaled", "dequantize_members", "dequantize_rows",
+    "dequantize_block_scaled", "dequantize_per_tensor", "dequantize_members", "dequantize_rows",
     "linear_w8a16_rows", "linear_w8a8_rows", "abs_bound_w8a16_rows", "abs_bound_w8a8_rows",
     "linear_w8a16", "quant_act", "dequantize_act", "linear_w8a8",
     "linear_w8a16_loops", "linear_w8a8_loops", "w8a8_block_partial_int",
@@ -218,9 +218,31 @@ def dequantize_block_scaled(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return e4m3_decode(codes) * s_full
 
 
+def dequantize_per_tensor(codes: np.ndarray, scale) -> np.ndarray:
+    """Wd[r,k] = dec(codes[r,k]) * scale, float64 (exact), for one per-tensor scale.
+
+    [FP8 "The two FP8 checkpoint shapes"]: the per-tensor layout pairs the E4M3
+    weight with a single weight_scale for the whole tensor, and reads as the
+    degenerate block case: one block covering every element.  ``scale`` is a
+    float32 scalar (a 0-d or one-element array).
+    """
+    codes = np.asarray(codes, np.uint8)
+    sv = np.asarray(scale, np.float32)
+    if sv.size != 1 or sv.ndim > 1:
+        raise ValueError(f"per-tensor scale must hold one value, got shape {sv.shape}")
+    return e4m3_decode(codes) * float(sv.reshape(()))
+
+
+def _is_per_tensor(scale) -> bool:
+    sv = np.asarray(scale)
+    return sv.ndim == 0 or (sv.ndim == 1 and sv.size == 1)
+
+
 def dequantize_members(members: Iterable[Tuple[np.ndarray, np.ndarray]]) -> np.ndarray:
-    """Concatenate the dequantized members along N, each with its own grid."""
-    return np.concatenate([dequantize_block_scaled(c, s) for c, s in members], axis=0)
+    """Concatenate the dequantized members along N, each with its own grid (or
+    its own per-tensor scale)."""
+    return np.concatenate([dequantize_per_tensor(c, s) if _is_per_tensor(s) else dequantize_block_scaled(c, s)
+                           for c, s in members], axis=0)
 
 
 def dequantize_rows(members: Sequence[Tuple[np.ndarray, np.ndarray]], rows: Sequence[int]) -> np.ndarray:
@@ -240,7 +262,10 @@ def dequantize_rows(members: Sequence[Tuple[np.ndarray, np.ndarray]], rows: Sequ
         if r >= sizes[i]:
             raise IndexError(n)
         codes, scale = members[i]
-        out[j] = e4m3_decode(codes[r]) * np.asarray(scale, np.float32)[r // BLOCK].astype(np.float64)[kcol]
+        if _is_per_tensor(scale):
+            out[j] = e4m3_decode(codes[r]) * float(np.asarray(scale, np.float32).reshape(()))
+        else:
+            out[j] = e4m3_decode(codes[r]) * np.asarray(scale, np.float32)[r // BLOCK].astype(np.float64)[kcol]
     return out
 
 
@@ -513,11 +538,23 @@ def validate(quant_method: str, block: Sequence[int], members: Sequence[MemberDe
          scale element (scale)                           -> ALIGNMENT
     Reading: when Nb == Kb a transposed grid has the right shape and cannot be
     told apart from headers; it is accepted.
+
+    Per-tensor layout ([FP8 "The two FP8 checkpoint shapes"]: E4M3 weight plus
+    one weight_scale per tensor, read as the degenerate block case).  Reading:
+    the pages do not say how such a checkpoint declares itself; it is taken to
+    be quant_method fp8 without a weight_block_size, written block (0, 0).
+    Under that declaration each member needs a ``weight_scale`` leaf holding
+    one value (rank 0, or rank 1 of shape [1]); a ``weight_scale_inv`` grid
+    disagrees with the declaration (DECL), a rank-1 leaf of more than one
+    value is row-wise (SCALE_ROWWISE), a higher rank is SCALE_RANK, and the
+    dtype must be BF16 or F32.  The weight checks are the same.
     """
     S = Status
     if len(members) < 1 or len(members) > max_members:
         return S.GROUP
-    if quant_method != "fp8" or tuple(int(b) for b in block) != (BLOCK, BLOCK):
+    blk = tuple(int(b) for b in block)
+    per_tensor = quant_method == "fp8" and blk == (0, 0)
+    if quant_method != "fp8" or (blk != (BLOCK, BLOCK) and not per_tensor):
         return S.DECL
     for m in members:
         w = m.weight
@@ -535,6 +572,16 @@ def validate(quant_method: str, block: Sequence[int], members: Sequence[MemberDe
             return S.SCALE_AMBIGUOUS
         leaf = m.scale_inv if m.scale_inv is not None else m.scale
         rank = len(leaf.shape)
+        if per_tensor:
+            if m.scale_inv is not None:
+                return S.DECL
+            if rank == 1 and leaf.shape[0] != 1:
+                return S.SCALE_ROWWISE
+            if rank > 1:
+                return S.SCALE_RANK
+            if leaf.dtype not in ("BF16", "F32"):
+                return S.SCALE_DTYPE
+            continue
         if rank == 1:
             return S.SCALE_ROWWISE
         if rank == 0 and m.scale is not None:
@@ -548,15 +595,17 @@ def validate(quant_method: str, block: Sequence[int], members: Sequence[MemberDe
             return S.SCALE_TRANSPOSED
         if leaf.shape != (nb, kb) or m.scale is not None:
             return S.SCALE_GRID
+    def leaf_of(m):
+        return m.scale_inv if m.scale_inv is not None else m.scale
     k0 = members[0].weight.shape[1]
-    dt0 = members[0].scale_inv.dtype
+    dt0 = leaf_of(members[0]).dtype
     for m in members[1:]:
-        if m.weight.shape[1] != k0 or m.scale_inv.dtype != dt0:
+        if m.weight.shape[1] != k0 or leaf_of(m).dtype != dt0:
             return S.GROUP
     for m in members:
         if m.weight.addr is not None and m.weight.addr % 16 != 0:
             return S.ALIGNMENT
-        esz = 2 if m.scale_inv.dtype == "BF16" else 4
-        if m.scale_inv.addr is not None and m.scale_inv.addr % esz != 0:
+        esz = 2 if leaf_of(m).dtype == "BF16" else 4
+        if leaf_of(m).addr is not None and leaf_of(m).addr % esz != 0:
             return S.ALIGNMENT
     return S.OK

@@ -285,6 +285,44 @@ def pin_brute_force(O):
     return True, ""
 
 
+def pin_per_tensor(O, seed=21):
+    """P9c: a per-tensor scale is the degenerate block ([FP8] 'The two FP8 checkpoint
+    shapes'): elementwise dec(code) * s by pure-Python loops on a slice, equal to
+    the block path with a grid filled with s, through both arms and the row helper."""
+    g = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    K = 300
+    members = [(finite[g.integers(0, finite.size, (r, K))], np.float32(np.exp2(e)))
+               for r, e in ((130, -7.5), (7, 3.25))]
+    for codes, sv in members:
+        d = O.dequantize_per_tensor(codes, sv)
+        for r in sorted({0, 1, min(64, codes.shape[0] - 1), codes.shape[0] - 1}):
+            for k in (0, 1, 127, 128, 299):
+                c = int(codes[r, k])
+                sgn, e, m = -1.0 if c >> 7 else 1.0, (c >> 3) & 15, c & 7
+                v = sgn * (m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))   # E4M3 closed form
+                if d[r, k] != v * float(sv):
+                    return False, f"dequant [{r},{k}]"
+        full = np.full(O.scale_grid_shape(*codes.shape), sv, np.float32)
+        if not np.array_equal(d, O.dequantize_block_scaled(codes, full)):
+            return False, "block path with a constant grid"
+        if not np.array_equal(O.dequantize_per_tensor(codes, np.array([sv], np.float32)), d):
+            return False, "one-element scale"
+    grids = [(c, np.full(O.scale_grid_shape(*c.shape), sv, np.float32)) for c, sv in members]
+    x = g.standard_normal((4, K)).astype(np.float32)
+    if not np.array_equal(O.linear_w8a16(x, members), O.linear_w8a16(x, grids)):
+        return False, "w8a16"
+    if not np.allclose(O.linear_w8a16(x, members), O.linear_w8a16_loops(x, grids), rtol=1e-12, atol=1e-300):
+        return False, "w8a16 loops"
+    xq, xs = O.quant_act(x)
+    if not np.array_equal(O.linear_w8a8(xq, xs, members), O.linear_w8a8(xq, xs, grids)):
+        return False, "w8a8"
+    rows = [0, 129, 130, 136]
+    if not np.array_equal(O.dequantize_rows(members, rows), O.dequantize_members(grids)[rows]):
+        return False, "rows"
+    return True, ""
+
+
 def pin_sampled_rows(O):
     """P9b: sampled-row helpers equal the corresponding columns of the full computation."""
     x, members = tiny_case(seed=4, M=3, K=300, rows=(130, 7, 129))

@@ -259,6 +259,36 @@ def test_w8a16_few_tokens_sweep(K):
         assert_within(to_np(yb), O.linear_w8a16(x_exact, om), O.abs_bound_w8a16(x_exact, om), True, f"K={K} M={M} bf16")
 
 
+@pytest.mark.parametrize("K", [384, 300])
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_per_tensor_scaled_weights(K, sdt):
+    """Per-tensor FP8 (one weight_scale per member, the degenerate block of FP8
+    Native Serving, 'The two FP8 checkpoint shapes'): both arms against the
+    oracle, on two members (130 and 300 rows), few and many tokens; K = 384 runs
+    the aligned kernels, K = 300 the byte-wise ones."""
+    t = torch()
+    g = np.random.default_rng(151 + K)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes = [finite[g.integers(0, finite.size, (r, K))] for r in (130, 300)]
+    svals = [np.float32(2.0 ** -7.25), np.float32(2.0 ** -4.5)]
+    if sdt == "bf16":   # values exact in BF16
+        svals = [np.float32(2.0 ** -7), np.float32(1.5 * 2.0 ** -5)]
+    dev = [(t.from_numpy(c).to(device()),
+            t.tensor(float(sv), dtype=t.float32 if sdt == "f32" else t.bfloat16, device=device()))
+           for c, sv in zip(codes, svals)]
+    w = B.BlockFP8Weight(dev, block=(0, 0))
+    om = list(zip(codes, svals))
+    x_all = synth.gaussian_activations(151, f"pt_X{K}", 300, K)
+    for M in (1, 5, 17, 300):
+        x = x_all[:M]
+        banner(f"per-tensor K={K} {sdt} M={M} {w.describe(B.ARM_W8A16, M)}")
+        y = B.linear_w8a16(w, t.from_numpy(x).to(device()))
+        assert_within(to_np(y), O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"w8a16 M={M}")
+        xq, xs = O.quant_act(x)
+        y8 = B.linear_w8a8(w, t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device()))
+        assert_within(to_np(y8), O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), True, f"w8a8 M={M}")
+
+
 def test_nan_weight_code_propagates_only_to_its_row():
     t = torch()
     m = synth.random_code_weight(103, "nan_W", 130, 256)

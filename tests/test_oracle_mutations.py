@@ -35,6 +35,16 @@ def test_mutation_divide_instead_of_multiply(monkeypatch):
     assert not _fails(P.pin_scale_direction, OM)
 
 
+def test_mutation_per_tensor_reciprocal(monkeypatch):
+    """A per-tensor scale used as a reciprocal fails the per-tensor pin."""
+    orig = OM.dequantize_per_tensor
+    monkeypatch.setattr(OM, "dequantize_per_tensor",
+                        lambda codes, scale: OM.e4m3_decode(codes) / float(np.asarray(scale, np.float32).reshape(())))
+    assert _fails(P.pin_per_tensor, OM)
+    monkeypatch.setattr(OM, "dequantize_per_tensor", orig)
+    assert not _fails(P.pin_per_tensor, OM)
+
+
 def test_mutation_wrong_bias(monkeypatch):
     t = OM.e4m3_table() * 2.0
     monkeypatch.setattr(OM, "e4m3_table", lambda: t.copy())

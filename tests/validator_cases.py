@@ -63,4 +63,19 @@ CASES = [
     ("scale_misaligned", "fp8", (128, 128), [mem(sinv=T("F32", (1, 2), 4098), waddr=4096)], "ALIGNMENT"),
     ("aligned_addresses_ok", "fp8", (128, 128), [mem(sinv=T("BF16", (1, 2), 4098), waddr=8192)], "OK"),
     ("grid_before_alignment", "fp8", (128, 128), [mem(sinv=T("BF16", (1, 3), 4096), waddr=4104)], "SCALE_GRID"),
+    # Per-tensor layout (FP8 Native Serving, 'The two FP8 checkpoint shapes': one
+    # weight_scale per tensor, the degenerate block), declared as block (0, 0).
+    ("per_tensor_f32_scalar_ok", "fp8", (0, 0), [mem(s=T("F32", ()))], "OK"),
+    ("per_tensor_one_element_ok", "fp8", (0, 0), [mem(s=T("F32", (1,)))], "OK"),
+    ("per_tensor_bf16_scalar_ok", "fp8", (0, 0), [mem(s=T("BF16", ()))], "OK"),
+    ("per_tensor_group_ok", "fp8", (0, 0), [mem(s=T("F32", ())), mem((1000, 256), s=T("F32", ()))], "OK"),
+    ("per_tensor_decl_with_grid", "fp8", (0, 0), [mem(sinv=T("BF16", (1, 2)))], "DECL"),
+    ("per_tensor_decl_rowwise", "fp8", (0, 0), [mem(s=T("F32", (128,)))], "SCALE_ROWWISE"),
+    ("per_tensor_decl_rank2", "fp8", (0, 0), [mem(s=T("F32", (1, 1)))], "SCALE_RANK"),
+    ("per_tensor_decl_f16", "fp8", (0, 0), [mem(s=T("F16", ()))], "SCALE_DTYPE"),
+    ("per_tensor_decl_missing", "fp8", (0, 0), [mem()], "SCALE_MISSING"),
+    ("per_tensor_decl_e5m2", "fp8", (0, 0), [mem(wdt="F8_E5M2", s=T("F32", ()))], "WEIGHT_E5M2"),
+    ("per_tensor_group_dtype_mismatch", "fp8", (0, 0), [mem(s=T("F32", ())), mem(s=T("BF16", ()))], "GROUP"),
+    ("per_tensor_scale_misaligned", "fp8", (0, 0), [mem(s=T("F32", (), 4098), waddr=4096)], "ALIGNMENT"),
+    ("decl_half_zero_block", "fp8", (0, 128), [mem(s=T("F32", ()))], "DECL"),
 ]
