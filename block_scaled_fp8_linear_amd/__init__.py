@@ -50,6 +50,13 @@ class Decl(ctypes.Structure):
     _fields_ = [("quant_method_fp8", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32)]
 
 
+class Unit(ctypes.Structure):
+    _fields_ = [("prefix", ctypes.c_char * 256), ("prefix_truncated", ctypes.c_int32), ("status", ctypes.c_int32),
+                ("weight", TensorDesc), ("scale_inv", TensorDesc), ("scale", TensorDesc),
+                ("has_scale_inv", ctypes.c_int32), ("has_scale", ctypes.c_int32),
+                ("weight_offset", ctypes.c_int64), ("scale_offset", ctypes.c_int64)]
+
+
 _lib = None
 
 # (name, restype, argtypes) of every entry point the header declares.
@@ -78,6 +85,9 @@ EXPORTS = [
                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("bsf8_describe", ctypes.c_char_p, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]),
     ("bsf8_read_stream", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    ("bsf8_parse_quant_config", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl)]),
+    ("bsf8_inspect_safetensors", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl), ctypes.POINTER(Unit),
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
 ]
 
 
@@ -143,6 +153,46 @@ def validate(quant_method: str, block, members: Sequence[dict]) -> str:
     decl = _decl(quant_method, block)
     arr, _keep = _members_array(members)
     return status_name(lib().bsf8_validate(ctypes.byref(decl), arr, len(members)))
+
+
+# ------------------------------------------------------- checkpoint headers
+
+_DT_NAME = {v: k for k, v in DTYPE_NAMES.items()}
+
+
+def parse_quant_config(json_text: str) -> Tuple[str, Tuple[int, int]]:
+    """(quant_method as 'fp8' or 'other', weight_block_size) from a config's JSON text;
+    the block is (0, 0) when no weight_block_size is declared (per-tensor reading)."""
+    d = Decl()
+    _check(lib().bsf8_parse_quant_config(json_text.encode(), ctypes.byref(d)), "parse_quant_config")
+    return ("fp8" if d.quant_method_fp8 else "other"), (d.block_n, d.block_k)
+
+
+def _desc_dict(t: TensorDesc) -> dict:
+    return dict(dtype=_DT_NAME.get(t.dtype, "OTHER"), shape=tuple(t.shape[i] for i in range(t.rank)))
+
+
+def inspect_safetensors(path: str, quant_method: str = "fp8", block=(BLOCK, BLOCK)):
+    """Header-only inspection of one safetensors file (no tensor byte is read).
+
+    Returns (status name of the whole file, list of units); each unit is a dict
+    with prefix, weight / scale_inv / scale descriptors, data offsets and its
+    own status name."""
+    L = lib()
+    decl = _decl(quant_method, block)
+    n = ctypes.c_int32()
+    st = L.bsf8_inspect_safetensors(path.encode(), ctypes.byref(decl), None, 0, ctypes.byref(n))
+    if status_name(st) == "INVALID_ARG":
+        _check(st, "inspect_safetensors")
+    units = (Unit * max(1, n.value))()
+    st = L.bsf8_inspect_safetensors(path.encode(), ctypes.byref(decl), units, n.value, ctypes.byref(n))
+    out = []
+    for u in units[:n.value]:
+        out.append(dict(prefix=u.prefix.decode(), status=status_name(u.status), weight=_desc_dict(u.weight),
+                        scale_inv=_desc_dict(u.scale_inv) if u.has_scale_inv else None,
+                        scale=_desc_dict(u.scale) if u.has_scale else None,
+                        weight_offset=u.weight_offset, scale_offset=u.scale_offset))
+    return status_name(st), out
 
 
 # ------------------------------------------------------------------ torch glue

@@ -270,6 +270,56 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
 const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M);
 
 /*
+ * Header-only checkpoint inspection ("th#1803: the consumer half of the layout
+ * gate", sections "What lands": verification from safetensors headers alone,
+ * before any weight byte is read; "Why the refusals matter more than the
+ * load" and "Proof": row-wise, transposed-grid, scale-less and dense trees are
+ * refused by name.  "Qwen checkpoints with block FP8 weights", layout
+ * paragraph: the declaration and the weight / weight_scale_inv leaves.)
+ *
+ * bsf8_parse_quant_config -- read quant_method and weight_block_size from a
+ * checkpoint config: json_text is a NUL-terminated JSON object, either the
+ * model config holding a "quantization_config" object or that object itself.
+ * out->quant_method_fp8 = (quant_method == "fp8"); block_n / block_k from
+ * weight_block_size, or 0 / 0 when it is absent or null (the per-tensor
+ * reading).  Host-only.  Errors: INVALID_ARG (null argument, malformed JSON,
+ * not an object), DECL (no quant_method string, or a weight_block_size that is
+ * not a pair of positive integers).
+ *
+ * bsf8_inspect_safetensors -- read the 8-byte header length and the JSON
+ * header of the safetensors file at `path` (nothing after the header) and
+ * list its linear units: every "<prefix>.weight" tensor stored as F8_E4M3 /
+ * F8_E5M2, or with a "<prefix>.weight_scale_inv" or "<prefix>.weight_scale"
+ * sibling.  Other tensors (dense BF16/F16 weights such as the output head,
+ * norms, biases) keep their own representation and are not units.  Each unit
+ * carries header descriptors (data = NULL), the file offsets of its bytes and
+ * the status bsf8_validate gives it alone under *decl.  units: caller array of
+ * `capacity` records (may be NULL when capacity is 0); *n_units = the number
+ * of units in the file (records past `capacity` are not written).  Host-only.
+ * Returns OK when every unit validates; else the first refusing unit's status
+ * in header order (bsf8_last_error names the unit); WEIGHT_DTYPE when the file
+ * has two-dimensional weights but no unit (a dense tree).  Errors also:
+ * INVALID_ARG (null argument, unreadable file, header length outside
+ * [2, BSF8_SAFETENSORS_MAX_HEADER], malformed header JSON).
+ */
+#define BSF8_SAFETENSORS_MAX_HEADER 100000000
+typedef struct bsf8_unit {
+  char prefix[256];            /* tensor name without ".weight" (NUL-terminated) */
+  int32_t prefix_truncated;    /* 1 when the name did not fit */
+  int32_t status;              /* bsf8_status of this unit alone */
+  bsf8_tensor_desc weight;
+  bsf8_tensor_desc scale_inv;  /* valid when has_scale_inv */
+  bsf8_tensor_desc scale;      /* valid when has_scale */
+  int32_t has_scale_inv;
+  int32_t has_scale;
+  int64_t weight_offset;       /* byte offset of the weight's data in the file */
+  int64_t scale_offset;        /* of the scale leaf present (scale_inv first), -1 when none */
+} bsf8_unit;
+bsf8_status bsf8_parse_quant_config(const char* json_text, bsf8_decl* out);
+bsf8_status bsf8_inspect_safetensors(const char* path, const bsf8_decl* decl, bsf8_unit* units, int32_t capacity,
+                                     int32_t* n_units);
+
+/*
  * bsf8_read_stream -- measurement aid, not part of the projection: reads
  * `bytes` bytes at `p` as a plain coalesced stream.  Timed on a GEMV's weight
  * bytes it gives the achievable read rate the GEMV is judged against.
