@@ -44,6 +44,7 @@ __all__ = [
     "linear_w8a16_loops", "linear_w8a8_loops", "w8a8_block_partial_int",
     "abs_bound_w8a16", "abs_bound_w8a8", "round_output", "within_bound",
     "cross_arm_metrics", "Status", "TensorDesc", "MemberDesc", "validate",
+    "upcast_members", "linear_dense", "abs_bound_dense", "linear_dense_loops",
 ]
 
 BLOCK = 128            # weight_block_size [128,128]  [QWEN layout paragraph]
@@ -280,6 +281,61 @@ def linear_w8a16(x: np.ndarray, members: Sequence[Tuple[np.ndarray, np.ndarray]]
     """
     x64 = np.asarray(x, np.float32).astype(np.float64)
     return x64 @ dequantize_members(members).T
+
+
+# ----------------------------------------------- upcast at load (dense arm)
+
+def upcast_members(members: Sequence[Tuple[np.ndarray, np.ndarray]], dtype: str) -> np.ndarray:
+    """Dense copy [N_total, K] of a (grouped) weight, as the resident=False arm
+    loads it: 'f32' -> float32 values; 'bf16' -> BF16 bit patterns (uint16).
+
+    [TH1803 "What lands"]: with resident=False the loader upcasts the weight
+    ahead of time instead of keeping the FP8 bytes; [FP8 "Native FP8 vs
+    dequant-to-BF16"]: the dequantized operand the matrix unit then reads is
+    BF16.  Members stay in order along N, each with its own grid.
+    Reading: an element is dec(q) * s formed as one float32 product (the exact
+    float64 product rounded once to float32, which is what an F32 multiply
+    returns; exact whenever the scale is BF16, since 4 + 8 significant bits fit
+    in 24), and a BF16 copy rounds that float32 value to nearest-even.
+    """
+    w32 = dequantize_members(members).astype(np.float32)
+    if dtype == "f32":
+        return w32
+    if dtype == "bf16":
+        return f32_to_bf16_bits(w32)
+    raise ValueError(dtype)
+
+
+def linear_dense(x: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """Y = X . Wd^T in float64 for dense operands given as float32 values
+    (BF16 operands widened with ``bf16_bits_to_f32``).
+
+    [FP8 "Native FP8 vs dequant-to-BF16"]: after the upcast the projection is
+    an ordinary BF16 matrix product accumulated in F32, whose exact value is
+    this sum.
+    """
+    return np.asarray(x, np.float32).astype(np.float64) @ np.asarray(wd, np.float32).astype(np.float64).T
+
+
+def abs_bound_dense(x: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """sum_k |x_k * w_k| per output (float64), the scale of the dense arm's error bound."""
+    return np.abs(np.asarray(x, np.float32).astype(np.float64)) @ np.abs(np.asarray(wd, np.float32).astype(np.float64)).T
+
+
+def linear_dense_loops(x, wd) -> np.ndarray:
+    """The dense product by plain Python loops (tiny inputs only)."""
+    x = np.asarray(x, np.float32)
+    wd = np.asarray(wd, np.float32)
+    M, K = x.shape
+    N = wd.shape[0]
+    y = np.zeros((M, N), np.float64)
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(x[m, k]) * float(wd[n, k])
+            y[m, n] = acc
+    return y
 
 
 # ------------------------------------------------------- activation quantizer

@@ -464,3 +464,95 @@ def pin_quant_brute_force(O, seed=17, M=6, K=300):
                 if int(q[m, k]) != O.e4m3_encode_scalar(f):
                     return False, f"code {m},{k}"
     return True, ""
+
+
+# ------------------------------------------------------------- P13 / P14
+
+def _torch_upcast(members, dtype):
+    """The dense copy built with PyTorch's own casts: float8_e4m3fn -> float32,
+    an F32 multiply by the expanded grid, then (for BF16) PyTorch's RNE cast."""
+    import torch
+    parts = []
+    for codes, scale in members:
+        w = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float32)
+        s = torch.from_numpy(np.asarray(scale, np.float32).reshape(-1, np.asarray(scale).shape[-1])
+                             if np.asarray(scale).ndim == 2 else np.asarray(scale, np.float32).reshape(1, 1))
+        N, K = w.shape
+        s_full = s.repeat_interleave(128, 0)[:N].repeat_interleave(128, 1)[:, :K] if s.numel() > 1 else s
+        parts.append(w * s_full)
+    d = torch.cat(parts, 0)
+    if dtype == "f32":
+        return d.numpy()
+    return d.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_upcast(O, seed=23):
+    """P13: the dense copy of the resident=False arm.
+
+    * equals PyTorch's casts (float8_e4m3fn decode, F32 multiply, BF16 RNE cast)
+      on grouped members with F32 and with BF16-valued grids and ragged tails;
+    * closed form: codes 0x38 (1.0) give the grid itself in every block;
+    * with BF16-valued scales the F32 copy is exact (equals the float64 dequantization);
+    * the reading 'F32 product, then BF16' is the one taken where it matters:
+      products whose F32 rounding lands on a BF16 tie that the exact product
+      does not, so one rounding and two differ.
+    """
+    import torch
+    x, members = tiny_case(seed=seed, M=1, K=300, rows=(130, 7, 129))
+    bf_members = [(c, O.f32_to_bf16(s)) for c, s in members]
+    for mem in (members, bf_members):
+        for dt in ("f32", "bf16"):
+            ours = O.upcast_members(mem, dt)
+            ref = _torch_upcast(mem, dt)
+            if ours.shape != ref.shape or not np.array_equal(ours.view(np.uint32 if dt == "f32" else np.uint16),
+                                                             ref.view(np.uint32 if dt == "f32" else np.uint16)):
+                return False, f"torch casts ({dt})"
+    exact = O.upcast_members(bf_members, "f32").astype(np.float64)
+    if not np.array_equal(exact, O.dequantize_members(bf_members)):
+        return False, "BF16 grid: F32 copy not exact"
+    ones = [(np.full_like(c, 0x38), s) for c, s in members]
+    d = O.upcast_members(ones, "f32")
+    r0 = 0
+    for c, s in members:
+        N, K = c.shape
+        for r in (0, N - 1):
+            for k in (0, K - 1):
+                if d[r0 + r, k] != s[r // 128, k // 128]:
+                    return False, f"closed form [{r0 + r},{k}]"
+        r0 += N
+    # double rounding: dec = 1.125 (code 0x39); scales near tie/1.125 for BF16 ties T
+    cases = 0
+    for t in range(1, 256, 2):
+        T = 1.0 + t * 2.0 ** -8                      # odd multiple of 2^-8: a BF16 tie in [1, 2)
+        s32 = np.float32(T / 1.125)
+        for sv in (s32, np.nextafter(s32, np.float32(2)), np.nextafter(s32, np.float32(0))):
+            p = 1.125 * float(sv)                     # exact in float64
+            f32 = np.float32(p)
+            if float(f32) != T or p == T:
+                continue
+            # one rounding of the exact product to BF16's 8 significant bits, ties to even
+            m, e = math.frexp(p)
+            once = float(round(m * 256.0)) * 2.0 ** (e - 8)
+            twice = torch.tensor([float(f32)], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)[0]
+            if once == float(O.bf16_bits_to_f32(np.array([twice], np.uint16))[0]):
+                continue
+            cases += 1
+            got = O.upcast_members([(np.array([[0x39]], np.uint8), np.array([[sv]], np.float32))], "bf16")[0, 0]
+            if got != twice:
+                return False, f"double rounding at T={T}"
+    if cases == 0:
+        return False, "no double-rounding case found"
+    return True, f"{cases} double-rounding cases"
+
+
+def pin_dense_brute_force(O, seed=29):
+    """P14: the dense product equals pure-Python loops on a tiny BF16 case with a ragged K."""
+    g = np.random.default_rng(seed)
+    x = O.f32_to_bf16(g.standard_normal((3, 70)).astype(np.float32))
+    wd = O.f32_to_bf16(g.standard_normal((5, 70)).astype(np.float32) * np.float32(0.02))
+    y = O.linear_dense(x, wd)
+    if not np.allclose(y, O.linear_dense_loops(x, wd), rtol=1e-12, atol=1e-300):
+        return False, "loops"
+    if not np.allclose(O.abs_bound_dense(x, wd), O.linear_dense_loops(np.abs(x), np.abs(wd)), rtol=1e-12, atol=1e-300):
+        return False, "bound"
+    return True, ""

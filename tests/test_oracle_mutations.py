@@ -139,3 +139,37 @@ def test_mutation_bf16_truncation(monkeypatch):
 def test_mutation_scale_grid_floor(monkeypatch):
     monkeypatch.setattr(OM, "scale_grid_shape", lambda n, k, block=(128, 128): (n // 128, k // 128))
     assert _fails(P.pin_grids, OM)
+
+
+def test_mutation_upcast_single_rounding(monkeypatch):
+    """A BF16 copy rounded once from the exact product fails the upcast pin."""
+    orig = OM.upcast_members
+
+    def once(members, dtype):
+        if dtype != "bf16":
+            return orig(members, dtype)
+        m, e = np.frexp(OM.dequantize_members(members))
+        v = (np.round(m * 256.0) * np.exp2(e - 8.0)).astype(np.float32)   # exact: 8 significant bits
+        return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    monkeypatch.setattr(OM, "upcast_members", once)
+    assert _fails(P.pin_upcast, OM)
+    monkeypatch.setattr(OM, "upcast_members", orig)
+    assert not _fails(P.pin_upcast, OM)
+
+
+def test_mutation_upcast_member_grid(monkeypatch):
+    """A dense copy that scales every member with the first member's grid fails the upcast pin."""
+    orig = OM.upcast_members
+
+    def shared(members, dtype):
+        s0 = members[0][1]
+        fixed = [(c, s0[:-(-c.shape[0] // 128)]) if s0.shape[0] >= -(-c.shape[0] // 128) else (c, s) for c, s in members]
+        return orig(fixed, dtype)
+    monkeypatch.setattr(OM, "upcast_members", shared)
+    assert _fails(P.pin_upcast, OM)
+
+
+def test_mutation_dense_transposed(monkeypatch):
+    """Summing over the wrong weight index fails the dense brute-force pin."""
+    monkeypatch.setattr(OM, "linear_dense", lambda x, wd: np.asarray(x, np.float64) @ np.asarray(wd, np.float64)[:, ::-1].T)
+    assert _fails(P.pin_dense_brute_force, OM)
