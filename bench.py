@@ -27,6 +27,10 @@ The same JSON line also carries:
 * ``qkv_prefill``: grouped Q/K/V W8A8 at M = 512;
 * ``large_prefill``: the W8A8 GEMM at M=8192, K=7168, N=18432, warm and
   rotated over three weight copies;
+* ``dense_arm``: the resident=False arm on the grouped Q/K/V weight: the
+  upcast to a dense BF16 copy (rotated over three weight copies, HBM roofline
+  on its algorithmic bytes) and the dense BF16 product at M = 128 and 512
+  (BF16 MFMA roofline);
 * ``cpu_baseline``: the oracle (NumPy) on the host cores, running the same
   prefill step for about ten seconds, with the median time of each part.
 
@@ -49,6 +53,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense BF16 MFMA
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 ROTATE_BYTES = 640 << 20     # > 512 MiB of distinct weight copies for the GEMV
 
@@ -393,6 +398,48 @@ def bench_large(torch, B, synth, steps, dev):
                 quant_us=q_ms * 1e3, describe=w.describe(B.ARM_W8A8, M))
 
 
+def bench_dense_arm(torch, B, synth, dev):
+    """The resident=False arm on grouped Q/K/V [6144|1000|1000, 5120]: the upcast
+    (BF16 copy; three weight copies and three outputs used in turn, 375 MB, so
+    HBM rather than the Infinity Cache serves them) and the dense product over
+    the copy with BF16 activations at M = 128 and 512 (graphs of 20 calls)."""
+    wl = synth.config4(512)
+    w = B.BlockFP8Weight([to_device_member(torch, m, dev) for m in wl.members])
+    N, K = w.n_total, w.K
+    copies = [w] + [B.BlockFP8Weight([(t.clone(), sc.clone()) for t, sc in w.members]) for _ in range(2)]
+    outs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in copies]
+
+    def up():
+        for c, o in zip(copies, outs):
+            B.upcast(c, out=o)
+    g_up = graph_of(torch, up, 7)
+    settle(torch, g_up.replay, 0.3)
+    su = replay_stats(torch, g_up, 20, 7 * len(copies))
+    grid = sum(-(-m.codes.shape[0] // 128) * -(-K // 128) for m in wl.members)
+    up_bytes = N * K * 3 + 2 * grid
+    del g_up
+    wd = outs[0]
+    x = torch.from_numpy(wl.x).to(dev).to(torch.bfloat16)
+    gemm = {}
+    for M in (128, 512):
+        xm = x[:M]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        need = B.dense_workspace_size(N, K, M)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        g = graph_of(torch, lambda: B.linear_dense(wd, xm, out_dtype=torch.bfloat16, out=y, workspace=ws), 20)
+        settle(torch, g.replay, 0.3)
+        st = replay_stats(torch, g, 20, 20)
+        flop = 2.0 * M * N * K
+        gemm[f"M{M}"] = dict(us=st["median"] * 1e3, us_p10=st["p10"] * 1e3, us_p90=st["p90"] * 1e3,
+                             launches=st["launches"], tflops=flop / (st["median"] * 1e-3) / 1e12,
+                             describe=w.describe(B.ARM_DENSE, M))
+        del g
+    del copies, outs
+    return dict(upcast_us=su["median"] * 1e3, upcast_us_p10=su["p10"] * 1e3, upcast_us_p90=su["p90"] * 1e3,
+                upcast_launches=su["launches"], upcast_gbs=up_bytes / (su["median"] * 1e-3) / 1e9,
+                upcast_bytes=up_bytes, gemm=gemm)
+
+
 def copy_calibration(torch, dev):
     """A plain streaming kernel of known traffic, run three times, so an HBM counter run can scale
     FETCH_SIZE / WRITE_SIZE: y = 2 * x over 2^28 float32 (reads 1 GiB, writes 1 GiB per launch)."""
@@ -492,6 +539,9 @@ def main():
         torch.cuda.empty_cache()
         extra["large_prefill"] = bench_large(torch, B, synth, a.steps, dev)
         log(f"large {extra['large_prefill']}")
+        torch.cuda.empty_cache()
+        extra["dense_arm"] = bench_dense_arm(torch, B, synth, dev)
+        log(f"dense arm {extra['dense_arm']}")
     if a.copy_calibration:
         extra["copy_calibration"] = copy_calibration(torch, dev)
     cpu = None if a.skip_cpu else cpu_baseline(synth)
@@ -563,6 +613,23 @@ def main():
                                              "gemm_us": round(l["rotated_gemm_us"], 1),
                                              "tflops": round(l["rotated_tflops"], 2)},
                                  "path": l["describe"]}
+    if "dense_arm" in extra:
+        d = extra["dense_arm"]
+        g512 = d["gemm"]["M512"]
+        line["dense_arm"] = {
+            "workload": "resident=False arm, grouped QKV [6144|1000|1000, 5120]: upcast to BF16, then BF16 x BF16 "
+                        "product with BF16 activations, bf16 out",
+            "upcast": {"us": round(d["upcast_us"], 2), "p10": round(d["upcast_us_p10"], 2),
+                       "p90": round(d["upcast_us_p90"], 2), "launches": d["upcast_launches"],
+                       "gbs": round(d["upcast_gbs"], 1), "bytes": d["upcast_bytes"],
+                       "frac_hbm": round(d["upcast_gbs"] / HBM_PEAK_GBS, 4),
+                       "note": "1 B read + 2 B written per element (+ grid); three weight copies used in turn"},
+            "gemm": {k: {"us": round(v["us"], 2), "p10": round(v["us_p10"], 2), "p90": round(v["us_p90"], 2),
+                         "launches": v["launches"], "tflops": round(v["tflops"], 2), "path": v["describe"]}
+                     for k, v in d["gemm"].items()},
+            "roofline": {"bound": "mfma", "kernel": "dense_gemm (M512)", "achieved": round(g512["tflops"], 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(g512["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None}}
     if "copy_calibration" in extra:
         line["copy_calibration"] = extra["copy_calibration"]
     print(json.dumps(line), flush=True)

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsf8.so")
 
 DT_INVALID, DT_F8_E4M3, DT_F8_E5M2, DT_BF16, DT_F16, DT_F32, DT_U8, DT_OTHER = range(8)
-ARM_W8A16, ARM_W8A8 = 0, 1
+ARM_W8A16, ARM_W8A8, ARM_DENSE = 0, 1, 2
 DTYPE_NAMES = {"F8_E4M3": DT_F8_E4M3, "F8_E5M2": DT_F8_E5M2, "BF16": DT_BF16, "F16": DT_F16,
                "F32": DT_F32, "U8": DT_U8}
 MAX_MEMBERS = 8
@@ -88,6 +88,12 @@ EXPORTS = [
     ("bsf8_parse_quant_config", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl)]),
     ("bsf8_inspect_safetensors", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl), ctypes.POINTER(Unit),
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+    ("bsf8_upcast", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
+    ("bsf8_dense_workspace_size", ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    ("bsf8_linear_dense", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 ]
 
 
@@ -348,8 +354,51 @@ def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=N
     return y
 
 
-__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "linear_w8a16", "linear_w8a8", "lib",
-           "status_name", "ARM_W8A16", "ARM_W8A8", "EXPORTS", "LIB_PATH", "MAX_MEMBERS"]
+def upcast(w: BlockFP8Weight, out_dtype=None, out=None):
+    """Dense copy [N, K] of the weight (bfloat16 unless out_dtype says float32): the resident=False load step."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((w.n_total, w.K), dtype=out_dtype, device=w.device)
+    if out.dtype != out_dtype or out.dim() != 2 or out.shape[0] != w.n_total or out.shape[1] < w.K \
+            or out.stride(1) != 1:
+        raise ValueError("out must be [N, >=K] with unit column stride and the requested dtype")
+    _check(lib().bsf8_upcast(w.handle, out.data_ptr(), _dt_of(out), out.stride(0), _stream_ptr(out.device)), "upcast")
+    return out
+
+
+def dense_workspace_size(N: int, K: int, M: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().bsf8_dense_workspace_size(N, K, M, ctypes.byref(b)), "dense_workspace_size")
+    return b.value
+
+
+def linear_dense(wd, x, out_dtype=None, out=None, workspace=None):
+    """Dense arm: y [M, N] = x . wd^T for bfloat16 wd [N, K] (contiguous) and bfloat16 x [M, K]
+    (float32 output unless out_dtype says bfloat16).  ``workspace``: a uint8 device tensor of at
+    least dense_workspace_size bytes, allocated here when omitted."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    if wd.dim() != 2 or not wd.is_contiguous() or wd.dtype != torch.bfloat16:
+        raise ValueError("wd must be a contiguous bfloat16 [N, K] tensor")
+    N, K = wd.shape
+    if x.dim() != 2 or x.stride(1) != 1 or x.shape[1] != K or x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16 [M, K] with unit column stride")
+    M = x.shape[0]
+    y = _out(out, M, N, out_dtype, x.device)
+    need = dense_workspace_size(N, K, M)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().bsf8_linear_dense(wd.data_ptr(), N, K, x.data_ptr(), M, x.stride(0), y.data_ptr(), _dt_of(y),
+                                   y.stride(0), workspace.data_ptr() if workspace is not None else None,
+                                   workspace.numel() if workspace is not None else 0, _stream_ptr(x.device)),
+           "linear_dense")
+    return y
+
+
+__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "linear_w8a16", "linear_w8a8", "upcast",
+           "linear_dense", "dense_workspace_size", "lib", "status_name", "ARM_W8A16", "ARM_W8A8", "ARM_DENSE",
+           "EXPORTS", "LIB_PATH", "MAX_MEMBERS"]
 
 
 READ_STREAM_SINK_WORDS = 2048  # BSF8_READ_STREAM_SINK_WORDS in include/bsf8.h

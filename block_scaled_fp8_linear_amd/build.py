@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsf8.so")
 
-SOURCES = ["bsf8_host.cpp", "bsf8_inspect.cpp", "bsf8_quant.hip", "bsf8_w8a16.hip", "bsf8_w8a8.hip", "bsf8_stream.hip"]
+SOURCES = ["bsf8_host.cpp", "bsf8_inspect.cpp", "bsf8_quant.hip", "bsf8_w8a16.hip", "bsf8_w8a8.hip", "bsf8_dense.hip",
+           "bsf8_stream.hip"]
 ARCH = "gfx950"
 
 

@@ -245,8 +245,52 @@ bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, si
   if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");
   if (arm == BSF8_ARM_W8A16) *bytes = M ? w8a16_workspace_bytes(w->dev, M) : 0;
   else if (arm == BSF8_ARM_W8A8) *bytes = M ? w8a8_workspace_bytes(w->dev, M) : 0;
+  else if (arm == BSF8_ARM_DENSE) *bytes = M ? dense_workspace_bytes(w->n_total, w->dev.K, M) : 0;
   else return fail(BSF8_E_INVALID_ARG, "arm %d", arm);
   return BSF8_OK;
+}
+
+bsf8_status bsf8_upcast(const bsf8_weight* w, void* out, int32_t out_dtype, int64_t ldo, void* stream) {
+  if (w == nullptr || out == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (!dtype_ok(out_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "out dtype %d (F32 or BF16)", out_dtype);
+  if (ldo < w->dev.K) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  const size_t esz = out_dtype == BSF8_DT_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(out) % esz) return fail(BSF8_E_ALIGNMENT, "out not element aligned");
+  const bool vec = w->aligned16 && reinterpret_cast<uintptr_t>(out) % 16 == 0 && (ldo * int64_t(esz)) % 16 == 0;
+  return launch_upcast(w->dev, w->n_total, vec, out, out_dtype == BSF8_DT_BF16, ldo, static_cast<hipStream_t>(stream));
+}
+
+bsf8_status bsf8_dense_workspace_size(int64_t N, int64_t K, int64_t M, size_t* bytes) {
+  if (bytes == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (N <= 0 || K <= 0 || M < 0) return fail(BSF8_E_INVALID_ARG, "sizes N=%lld K=%lld M=%lld", (long long)N,
+                                             (long long)K, (long long)M);
+  *bytes = dense_workspace_bytes(N, K, M);
+  return BSF8_OK;
+}
+
+bsf8_status bsf8_linear_dense(const uint16_t* wd, int64_t N, int64_t K, const uint16_t* x, int64_t M, int64_t ldx,
+                              void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (N <= 0 || K <= 0 || M < 0) return fail(BSF8_E_INVALID_ARG, "sizes N=%lld K=%lld M=%lld", (long long)N,
+                                             (long long)K, (long long)M);
+  if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
+  if (M == 0) return BSF8_OK;
+  if (wd == nullptr || x == nullptr || y == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (ldx < K || ldy < N) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  const size_t ye = y_dtype == BSF8_DT_F32 ? 4 : 2;
+  if (K % 8 || ldx % 8 || reinterpret_cast<uintptr_t>(wd) % 16 || reinterpret_cast<uintptr_t>(x) % 16)
+    return fail(BSF8_E_ALIGNMENT, "dense GEMM needs K and ldx multiples of 8 and 16-byte aligned wd and x");
+  if (reinterpret_cast<uintptr_t>(y) % ye) return fail(BSF8_E_ALIGNMENT, "y not element aligned");
+  if (!dense_supported(N, K, M, ldx))
+    return fail(BSF8_E_UNSUPPORTED, "dense GEMM shape N=%lld K=%lld M=%lld ldx=%lld (K <= 65536 and operands "
+                "below 2 GiB)", (long long)N, (long long)K, (long long)M, (long long)ldx);
+  const size_t need = dense_workspace_bytes(N, K, M);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(BSF8_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(BSF8_E_ALIGNMENT, "workspace not 256-byte aligned");
+  return launch_dense(wd, N, K, x, M, ldx, y, y_dtype == BSF8_DT_BF16, ldy, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream));
 }
 
 bsf8_status bsf8_linear_w8a16(const bsf8_weight* w, const void* x, int32_t x_dtype, int64_t M, int64_t ldx,
@@ -312,6 +356,7 @@ const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M) {
            w->dev.n_members, w->dev.scale_bf16 ? "bf16" : "f32", w->per_tensor ? " per-tensor" : "");
   if (arm == BSF8_ARM_W8A16) g_describe = describe_w8a16(w->dev, w->aligned16, M) + geo;
   else if (arm == BSF8_ARM_W8A8) g_describe = describe_w8a8(w->dev, w->aligned16, M) + geo;
+  else if (arm == BSF8_ARM_DENSE) g_describe = describe_dense(w->n_total, w->dev.K, M) + geo;
   else g_describe = "unknown arm";
   return g_describe.c_str();
 }

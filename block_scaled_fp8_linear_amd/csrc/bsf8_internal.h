@@ -61,6 +61,16 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
                         size_t ws_bytes, hipStream_t stream);
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M);
 
+// Dense arm: the upcast copy and the BF16 GEMM over it (the fast W8A8 kernel's
+// dense instance).
+bsf8_status launch_upcast(const WeightDev& w, int64_t n_total, bool vec, void* out, bool out_bf16, int64_t ldo,
+                          hipStream_t stream);
+bool dense_supported(int64_t N, int64_t K, int64_t M, int64_t ldx);
+size_t dense_workspace_bytes(int64_t N, int64_t K, int64_t M);
+std::string describe_dense(int64_t N, int64_t K, int64_t M);
+bsf8_status launch_dense(const uint16_t* wd, int64_t N, int64_t K, const uint16_t* x, int64_t M, int64_t ldx,
+                         void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
+
 bsf8_status launch_read_stream(const void* p, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace bsf8

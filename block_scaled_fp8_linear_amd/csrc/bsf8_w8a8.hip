@@ -419,8 +419,25 @@ __device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uin
   }
 }
 
-// KFULL: K is a multiple of 128, so no copy needs the ragged-K test.
-template <bool SBF16, bool KFULL>
+// Dense arm: two BF16 MFMAs per 32-byte fragment pair.  A fragment holds 16
+// BF16 values of one row (chunks 2g and 2g + 1 of its 128-byte K block); the
+// first MFMA takes chunk 2g as its K group g and the second chunk 2g + 1, on
+// both operands alike, so the pair sums every K element of the block once.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void mfma_bf16_pair(v4f& c, const v8i& a, const v8i& b) {
+  const v8bf a0 = __builtin_bit_cast(v8bf, __builtin_shufflevector(a, a, 0, 1, 2, 3));
+  const v8bf a1 = __builtin_bit_cast(v8bf, __builtin_shufflevector(a, a, 4, 5, 6, 7));
+  const v8bf b0 = __builtin_bit_cast(v8bf, __builtin_shufflevector(b, b, 0, 1, 2, 3));
+  const v8bf b1 = __builtin_bit_cast(v8bf, __builtin_shufflevector(b, b, 4, 5, 6, 7));
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, c, 0, 0, 0);
+}
+
+// KFULL: K is a multiple of 128 bytes, so no copy needs the ragged-K test.
+// DENSE: BF16 operands without scales (the upcast weight of the resident=False
+// arm times BF16 activations): w.K counts bytes (2 per element), the MFMAs
+// accumulate in place, and there are no scales to stage or apply.
+template <bool SBF16, bool KFULL, bool DENSE>
 __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   // Two separate stage arrays (not one array indexed by stage): the compiler
   // must wait for in-flight LDS copies before any LDS read it cannot prove
@@ -526,9 +543,11 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     }
   };
   auto issue_scales = [&](int kb, uint8_t* base) {
-    if (s_wave) {
-      const int off = s_ok ? s_off + kb * 4 : int(s_bytes);
-      bsf8_raw_buffer_load_lds(rs, (lds_u32_ptr)(base + F_SA + wave * 256), 4, off, 0, 0, 0);
+    if constexpr (!DENSE) {
+      if (s_wave) {
+        const int off = s_ok ? s_off + kb * 4 : int(s_bytes);
+        bsf8_raw_buffer_load_lds(rs, (lds_u32_ptr)(base + F_SA + wave * 256), 4, off, 0, 0, 0);
+      }
     }
   };
   auto issue = [&](int kb, uint8_t* base) {
@@ -545,7 +564,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
 
   // ---- weight scales: rows (n0 >> 7) and (n0 >> 7) + 1 of the member's grid
   // (one per wave half), staged in LDS once; a missing row reads as zero
-  {
+  if constexpr (!DENSE) {
     const int nb = (mem.rows + 127) >> 7;
     for (int i = tid; i < 2 * Kb; i += FTHREADS) {
       const int h = i >= Kb, kb = i - h * Kb;
@@ -612,8 +631,12 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     const int k1 = min(kb + 1, kb_end - 1);
     const int k2 = min(kb + 2, kb_end - 1);
     if (kb + 1 < kb_end) issue_scales(kb + 1, nxt);   // the next block's token scales
-    const float sw = wscale[wn][kb];
-    const float4 sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
+    float sw = 0.f;
+    float4 sa = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (!DENSE) {
+      sw = wscale[wn][kb];
+      sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
+    }
     float s[TJ];
     // The 32 MFMAs of the K block run as one rotated chain: the epilogue FMAs
     // that consume MFMA q's partial are issued after MFMA q + 2 (three
@@ -634,8 +657,11 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
           af[0] = read_a(nxt, 0);
         }
         if (j == 0 && i + 1 < TI) af[(i + 1) & 1] = read_a(cur, i + 1);
-        part[q % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j],
-                                                                             v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if constexpr (DENSE)
+          mfma_bf16_pair(acc[i][j], af[i & 1], bf[j]);
+        else
+          part[q % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j],
+                                                                               v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
         if (q >= BARQ) bf[j] = read_b(nxt, j);   // its last use in this block was the MFMA above
       }
       if constexpr (COPY) {
@@ -649,15 +675,17 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (q == LAG) {   // the scale products, first needed here
-        s[0] = sa.x * sw;
-        s[1] = sa.y * sw;
-        s[2] = sa.z * sw;
-        s[3] = sa.w * sw;
-      }
-      if (q >= LAG) {
-        const int c = q - LAG, ci = c / TJ, cj = c % TJ;
-        acc[ci][cj] += part[c % (LAG + 1)] * s[cj];
+      if constexpr (!DENSE) {
+        if (q == LAG) {   // the scale products, first needed here
+          s[0] = sa.x * sw;
+          s[1] = sa.y * sw;
+          s[2] = sa.z * sw;
+          s[3] = sa.w * sw;
+        }
+        if (q >= LAG) {
+          const int c = q - LAG, ci = c / TJ, cj = c % TJ;
+          acc[ci][cj] += part[c % (LAG + 1)] * s[cj];
+        }
       }
       // (the scheduling barriers keep each MFMA ahead of the FMAs issued after it)
       __builtin_amdgcn_sched_barrier(0);
@@ -887,66 +915,132 @@ std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
   return buf;
 }
 
+namespace {
+
+// Fast-kernel launch (and the split-K reduction when the plan splits).
+bsf8_status launch_fast(const Plan& p, const WeightDev& w, bool dense, const uint8_t* xq, int64_t ldq,
+                        const float* xs, int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  FastArgs a{};
+  a.w = w;
+  for (int i = 0; i <= kMaxMembers; ++i) a.rt0[i] = p.rt0[i];
+  a.xq = xq;
+  a.xs = xs;
+  a.y = y;
+  a.ldq = ldq;
+  a.ldxs = ldxs;
+  a.ldy = ldy;
+  a.M = int32_t(M);
+  a.m_tiles = p.m_tiles;
+  a.rt_total = p.rt_total;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  const int64_t esz = y_bf16 ? 2 : 4;
+  bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (ldy * esz) % 16 == 0;
+  for (int i = 0; i < w.n_members; ++i) vec = vec && (w.m[i].col0 * esz) % 16 == 0;
+  a.y_vec = vec ? 1 : 0;
+  a.splits = p.splits;
+  a.kb_per_split = p.kb_per_split;
+  a.rt_split0 = p.rt_split0;
+  a.ldws = p.ldws;
+  if (p.splits > 1) {
+    if (ws == nullptr || ws_bytes < p.ws_bytes || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
+      set_error("WORKSPACE: split-K needs %zu bytes of 256-byte aligned workspace", p.ws_bytes);
+      return BSF8_E_WORKSPACE;
+    }
+    a.ws = static_cast<float*>(ws);
+  }
+  const bool kfull = w.K % KBYTES == 0;
+  using Kern = void (*)(FastArgs);
+  Kern kern;
+  if (dense)
+    kern = kfull ? w8a8_gemm_fast_kernel<false, true, true> : w8a8_gemm_fast_kernel<false, false, true>;
+  else if (w.scale_bf16)
+    kern = kfull ? w8a8_gemm_fast_kernel<true, true, false> : w8a8_gemm_fast_kernel<true, false, false>;
+  else
+    kern = kfull ? w8a8_gemm_fast_kernel<false, true, false> : w8a8_gemm_fast_kernel<false, false, false>;
+  hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
+  bsf8_status st = device_status(hipGetLastError(), dense ? "dense_gemm launch" : "w8a8_gemm_fast launch");
+  if (st != BSF8_OK || p.splits == 1) return st;
+  ReduceArgs r{};
+  r.ws = a.ws;
+  r.ldws = p.ldws;
+  r.split_stride = M * p.ldws;
+  r.y = y;
+  r.ldy = ldy;
+  r.M = int32_t(M);
+  r.splits = p.splits;
+  r.y_bf16 = y_bf16 ? 1 : 0;
+  r.n_members = w.n_members;
+  r.rt_split0 = p.rt_split0;
+  for (int i = 0; i <= kMaxMembers; ++i) r.rt0[i] = p.rt0[i];
+  for (int i = 0; i < w.n_members; ++i) {
+    r.rows[i] = w.m[i].rows;
+    r.col0[i] = w.m[i].col0;
+  }
+  const int64_t threads = M * (p.ldws / 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, r);
+  return device_status(hipGetLastError(), "splitk_reduce launch");
+}
+
+// The dense BF16 weight [N, K] as the fast kernel's single member: rows of
+// 2K bytes, no scales.
+WeightDev dense_weight(const uint16_t* wd, int64_t N, int64_t K) {
+  WeightDev w{};
+  w.m[0].w = reinterpret_cast<const uint8_t*>(wd);
+  w.m[0].s = nullptr;
+  w.m[0].rows = int32_t(N);
+  w.m[0].col0 = 0;
+  w.n_members = 1;
+  w.K = int32_t(2 * K);
+  w.Kb = int32_t((2 * K + KBYTES - 1) / KBYTES);
+  return w;
+}
+
+}  // namespace
+
+bool dense_supported(int64_t N, int64_t K, int64_t M, int64_t ldx) {
+  if (N <= 0 || K <= 0 || N > INT32_MAX || 2 * K > int64_t(F_MAX_KB) * KBYTES) return false;
+  return make_plan(dense_weight(nullptr, N, K), true, M > 0 ? M : 1, 2 * ldx).fast;
+}
+
+size_t dense_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  if (M <= 0 || !dense_supported(N, K, M, K)) return 0;
+  return make_plan(dense_weight(nullptr, N, K), true, M, 2 * K).ws_bytes;
+}
+
+std::string describe_dense(int64_t N, int64_t K, int64_t M) {
+  const int64_t m = M > 0 ? M : 1;
+  if (!dense_supported(N, K, m, K)) return "arm=dense unsupported shape";
+  const Plan p = make_plan(dense_weight(nullptr, N, K), true, m, 2 * K);
+  char buf[320];
+  snprintf(buf, sizeof(buf),
+           "arm=dense arithmetic=bf16xbf16 mfma_f32_16x16x32_bf16 (two per 128-byte K block), f32 accumulate | "
+           "kernel=w8a8_gemm_fast<dense> tile=%dx%d waves=8 buffer_load_lds xcd_groups=%d split_k=%d "
+           "split_row_tiles=%d | M=%lld blocks=%d | dense weight N=%lld K=%lld bf16",
+           FBN, FBM, GROUP_ROWS, p.splits, p.rt_total - p.rt_split0, (long long)m, p.blocks, (long long)N,
+           (long long)K);
+  return buf;
+}
+
+bsf8_status launch_dense(const uint16_t* wd, int64_t N, int64_t K, const uint16_t* x, int64_t M, int64_t ldx,
+                         void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const WeightDev w = dense_weight(wd, N, K);
+  const Plan p = make_plan(w, true, M, 2 * ldx);
+  if (!p.fast) {
+    set_error("UNSUPPORTED: dense GEMM shape N=%lld K=%lld M=%lld", (long long)N, (long long)K, (long long)M);
+    return BSF8_E_UNSUPPORTED;
+  }
+  if (p.blocks == 0) return BSF8_OK;
+  return launch_fast(p, w, true, reinterpret_cast<const uint8_t*>(x), 2 * ldx, nullptr, 0, M, y, y_bf16, ldy, ws,
+                     ws_bytes, stream);
+}
+
 bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,
                         int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
   const Plan p = make_plan(w, aligned, M, ldq);
   if (p.blocks == 0) return BSF8_OK;
-  if (p.fast) {
-    FastArgs a{};
-    a.w = w;
-    for (int i = 0; i <= kMaxMembers; ++i) a.rt0[i] = p.rt0[i];
-    a.xq = xq;
-    a.xs = xs;
-    a.y = y;
-    a.ldq = ldq;
-    a.ldxs = ldxs;
-    a.ldy = ldy;
-    a.M = int32_t(M);
-    a.m_tiles = p.m_tiles;
-    a.rt_total = p.rt_total;
-    a.y_bf16 = y_bf16 ? 1 : 0;
-    const int64_t esz = y_bf16 ? 2 : 4;
-    bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (ldy * esz) % 16 == 0;
-    for (int i = 0; i < w.n_members; ++i) vec = vec && (w.m[i].col0 * esz) % 16 == 0;
-    a.y_vec = vec ? 1 : 0;
-    a.splits = p.splits;
-    a.kb_per_split = p.kb_per_split;
-    a.rt_split0 = p.rt_split0;
-    a.ldws = p.ldws;
-    if (p.splits > 1) {
-      if (ws == nullptr || ws_bytes < p.ws_bytes || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
-        set_error("WORKSPACE: split-K needs %zu bytes of 256-byte aligned workspace", p.ws_bytes);
-        return BSF8_E_WORKSPACE;
-      }
-      a.ws = static_cast<float*>(ws);
-    }
-    const bool kfull = w.K % KBYTES == 0;
-    auto kern = w.scale_bf16 ? (kfull ? w8a8_gemm_fast_kernel<true, true> : w8a8_gemm_fast_kernel<true, false>)
-                             : (kfull ? w8a8_gemm_fast_kernel<false, true> : w8a8_gemm_fast_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
-    bsf8_status st = device_status(hipGetLastError(), "w8a8_gemm_fast launch");
-    if (st != BSF8_OK || p.splits == 1) return st;
-    ReduceArgs r{};
-    r.ws = a.ws;
-    r.ldws = p.ldws;
-    r.split_stride = M * p.ldws;
-    r.y = y;
-    r.ldy = ldy;
-    r.M = int32_t(M);
-    r.splits = p.splits;
-    r.y_bf16 = y_bf16 ? 1 : 0;
-    r.n_members = w.n_members;
-    r.rt_split0 = p.rt_split0;
-    for (int i = 0; i <= kMaxMembers; ++i) r.rt0[i] = p.rt0[i];
-    for (int i = 0; i < w.n_members; ++i) {
-      r.rows[i] = w.m[i].rows;
-      r.col0[i] = w.m[i].col0;
-    }
-    const int64_t threads = M * (p.ldws / 4);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, stream, r);
-    return device_status(hipGetLastError(), "splitk_reduce launch");
-  }
+  if (p.fast) return launch_fast(p, w, false, xq, ldq, xs, ldxs, M, y, y_bf16, ldy, ws, ws_bytes, stream);
   GemmArgs a{};
   a.w = w;
   a.tm = p.tm;

@@ -27,7 +27,8 @@
  *   - The caller owns all memory.  A weight handle BORROWS the weight and scale
  *     device pointers it was created from; they must stay valid and unchanged
  *     until bsf8_weight_destroy.  The library never copies, repacks, rescales or
- *     quantizes weights.
+ *     quantizes weights on its own; bsf8_upcast writes a dense copy into caller
+ *     memory when asked.
  *   - No call allocates device memory, frees it or synchronizes the device.
  *     Compute calls are asynchronous and ordered on the given stream
  *     (a hipStream_t passed as void*; NULL = the default stream).
@@ -87,7 +88,9 @@ typedef enum bsf8_dtype {
 
 typedef enum bsf8_arm {
   BSF8_ARM_W8A16 = 0,  /* F32 activations, F32 accumulation */
-  BSF8_ARM_W8A8 = 1    /* per-token 1x128 E4M3 activations, F32 epilogue */
+  BSF8_ARM_W8A8 = 1,   /* per-token 1x128 E4M3 activations, F32 epilogue */
+  BSF8_ARM_DENSE = 2   /* the handle's upcast dense BF16 copy times BF16 activations (bsf8_linear_dense);
+                          for bsf8_workspace_size and bsf8_describe */
 } bsf8_arm;
 
 /* Header-level description of one tensor.  data may be NULL for a header-only
@@ -268,6 +271,39 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
  * same thread; NULL only for a NULL handle.
  */
 const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M);
+
+/*
+ * The resident=False arm: upcast at load, then a dense BF16 product.
+ * ("th#1803: the consumer half of the layout gate", section "What lands": with
+ *  resident=False the loader upcasts the weight ahead of time instead of
+ *  keeping the FP8 bytes; "FP8 Native Serving", section "Native FP8 vs
+ *  dequant-to-BF16": the dequantized operand is BF16 and the product runs on
+ *  BF16 matrix units.)
+ *
+ * bsf8_upcast -- write the dense copy of the handle's weight:
+ *   out[R_i + r, k] = dec(W_i[r, k]) * S_i[r/128, k/128]   (per-tensor: * s_i)
+ * for every member i (rows in member order, as the output features of the other
+ * arms).  Each value is one F32 product (exact for BF16 scales) written as F32,
+ * or rounded to nearest-even BF16 (out_dtype BSF8_DT_BF16).  out: device
+ * [n_total, ldo] of out_dtype, ldo >= K, caller-owned; columns K..ldo-1 are not
+ * written.  One pass over the weight bytes (HBM-bound), asynchronous on
+ * `stream`.  Errors: INVALID_ARG (null, dtype, ldo), ALIGNMENT (out not element
+ * aligned), UNSUPPORTED (more than 2^32 16-element pieces).
+ *
+ * bsf8_linear_dense -- Y[m, n] = sum_k x[m, k] * wd[n, k] for BF16 wd [N, K]
+ * (row-major, row pitch K: bsf8_upcast's output with ldo = K) and BF16 x [M, K]
+ * with row pitch ldx; BF16 x BF16 products accumulated in F32 on the BF16
+ * matrix cores; y F32 or BF16 (RNE) [M, ldy].  Needs K and ldx multiples of 8,
+ * wd and x 16-byte aligned (ALIGNMENT otherwise), K <= 65536 and each operand
+ * below 2 GiB (UNSUPPORTED otherwise).  A workspace of
+ * bsf8_dense_workspace_size bytes (256-byte aligned) is needed when the tile
+ * grid is split over K, as for the W8A8 arm; M == 0 is a no-op.
+ */
+bsf8_status bsf8_upcast(const bsf8_weight* w, void* out, int32_t out_dtype, int64_t ldo, void* stream);
+bsf8_status bsf8_dense_workspace_size(int64_t N, int64_t K, int64_t M, size_t* bytes);
+bsf8_status bsf8_linear_dense(const uint16_t* wd, int64_t N, int64_t K, const uint16_t* x, int64_t M, int64_t ldx,
+                              void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Header-only checkpoint inspection ("th#1803: the consumer half of the layout

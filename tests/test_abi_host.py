@@ -164,3 +164,44 @@ def test_read_stream_sink_size_matches_header():
     with open(os.path.join(ROOT, "include", "bsf8.h")) as f:
         hdr = f.read()
     assert int(re.search(r"#define BSF8_READ_STREAM_SINK_WORDS (\d+)", hdr).group(1)) == B.READ_STREAM_SINK_WORDS
+
+
+def test_dense_arm_refuses_bad_arguments_without_launching():
+    L = B.lib()
+    st, h = _handle([128, 300], 256)
+    assert st == 0
+    fake = ctypes.c_void_p(1 << 40)
+    name = lambda s: B.status_name(s)
+    try:
+        # upcast: dtype, leading dimension, null, element alignment
+        assert name(L.bsf8_upcast(h, fake, B.DT_F16, 256, None)) == "INVALID_ARG"
+        assert name(L.bsf8_upcast(h, fake, B.DT_BF16, 255, None)) == "INVALID_ARG"
+        assert name(L.bsf8_upcast(h, None, B.DT_BF16, 256, None)) == "INVALID_ARG"
+        assert name(L.bsf8_upcast(None, fake, B.DT_BF16, 256, None)) == "INVALID_ARG"
+        assert name(L.bsf8_upcast(h, ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 256, None)) == "ALIGNMENT"
+        # dense product
+        args = lambda N=512, K=256, x=fake, M=4, ldx=256, ydt=B.DT_F32, ldy=512, ws=None, wsb=0: \
+            L.bsf8_linear_dense(fake, N, K, x, M, ldx, fake, ydt, ldy, ws, wsb, None)
+        assert args(M=0) == 0
+        assert name(args(M=-1)) == "INVALID_ARG"
+        assert name(args(ydt=B.DT_F16)) == "INVALID_ARG"
+        assert name(args(ldx=255)) == "INVALID_ARG"
+        assert name(args(ldy=511)) == "INVALID_ARG"
+        assert name(args(x=None)) == "INVALID_ARG"
+        assert name(args(K=250, ldx=256)) == "ALIGNMENT"
+        assert name(args(ldx=260)) == "ALIGNMENT"
+        assert name(args(x=ctypes.c_void_p((1 << 40) + 8))) == "ALIGNMENT"
+        assert name(args(K=65544, ldx=65544)) == "UNSUPPORTED"
+        # one row tile, four token rows: the plan splits K, so a workspace is required
+        b = ctypes.c_size_t()
+        assert L.bsf8_dense_workspace_size(512, 4096, 4, ctypes.byref(b)) == 0 and b.value > 0
+        assert name(args(K=4096, ldx=4096)) == "WORKSPACE"
+        assert name(L.bsf8_dense_workspace_size(0, 4096, 4, ctypes.byref(b))) == "INVALID_ARG"
+        # the handle's dense arm describes and sizes the product over its dense copy (N = 428)
+        assert L.bsf8_workspace_size(h, B.ARM_DENSE, 4, ctypes.byref(b)) == 0
+        w2 = ctypes.c_size_t()
+        assert L.bsf8_dense_workspace_size(428, 256, 4, ctypes.byref(w2)) == 0 and w2.value == b.value
+        d = L.bsf8_describe(h, B.ARM_DENSE, 4).decode()
+        assert "arm=dense" in d and "N=428 K=256" in d
+    finally:
+        L.bsf8_weight_destroy(h)
