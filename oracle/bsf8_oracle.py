@@ -45,6 +45,7 @@ __all__ = [
     "abs_bound_w8a16", "abs_bound_w8a8", "round_output", "within_bound",
     "cross_arm_metrics", "Status", "TensorDesc", "MemberDesc", "validate",
     "upcast_members", "linear_dense", "abs_bound_dense", "linear_dense_loops",
+    "silu_glu", "glu_quant",
 ]
 
 BLOCK = 128            # weight_block_size [128,128]  [QWEN layout paragraph]
@@ -370,6 +371,42 @@ def quant_act(x: np.ndarray, eps: np.float32 = ACT_EPS) -> Tuple[np.ndarray, np.
         codes[:, k0:k1] = e4m3_encode(f)
         scales[:, g] = s
     return codes, scales
+
+
+def silu_glu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u = g * sigmoid(g) * u as float32.
+
+    [W8A8 "Module w8a8_prefill" preamble]: the arm is the dense FFN's
+    gate/up/down prefill, in which the gate/up output reaches the down
+    projection through the gated activation and the per-token quantizer.
+    Reading: the pages do not name the activation; the gated SiLU of the
+    Qwen dense FFN is taken.  Its steps are fixed so that the quantized codes
+    (decided in float32) are reproducible, in the overflow-free form:
+    e = exp(-|g|) evaluated in float64 and rounded to float32 (in (0, 1]),
+    t = 1 + e, then q = g / t for g >= 0 and q = (g * e) / t for g < 0, and
+    h = q * u, each an IEEE float32 operation.
+    """
+    g = np.asarray(g, np.float32)
+    u = np.asarray(u, np.float32)
+    e = np.exp(-np.abs(g.astype(np.float64))).astype(np.float32)
+    t = np.float32(1.0) + e
+    q = np.where(g >= 0, g / t, (g * e) / t).astype(np.float32)
+    return q * u
+
+
+def glu_quant(y_gu: np.ndarray, F: int, eps: np.float32 = ACT_EPS) -> Tuple[np.ndarray, np.ndarray]:
+    """The gate/up -> activation -> quantization step that feeds the down
+    projection: y_gu [M, 2F] holds the gate outputs in columns [0, F) and the up
+    outputs in [F, 2F) (the fused gate/up weight's member order); returns the
+    down projection's quantized input (codes uint8 [M, F], scales f32 [M, ceil(F/128)]).
+
+    [W8A8 "WHY (#917 / #928)"]: the down GEMM consumes per-token 1x128 E4M3
+    activations; the activation values are ``silu_glu`` of the two halves.
+    """
+    y = np.asarray(y_gu, np.float32)
+    if y.ndim != 2 or y.shape[1] < 2 * F:
+        raise ValueError(f"y_gu {y.shape} does not hold 2F = {2 * F} columns")
+    return quant_act(silu_glu(y[:, :F], y[:, F:2 * F]), eps)
 
 
 def dequantize_act(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

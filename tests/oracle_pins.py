@@ -556,3 +556,55 @@ def pin_dense_brute_force(O, seed=29):
     if not np.allclose(O.abs_bound_dense(x, wd), O.linear_dense_loops(np.abs(x), np.abs(wd)), rtol=1e-12, atol=1e-300):
         return False, "bound"
     return True, ""
+
+
+# ------------------------------------------------------------------- P15
+
+def _f32(v: float) -> float:
+    import struct
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def pin_silu_glu(O, seed=31):
+    """P15: the gated activation feeding the down projection.
+
+    * PyTorch's SiLU (float64) times u agrees within 4 float32 ulps where
+      exp(-|g|) is a normal float32 (|g| < 80), over values spanning 2^-6..2^6;
+    * closed forms: g = 0 gives signed zeros, g = 100 gives g*u exactly,
+      g = -200 gives -0 * u (exp(-200) rounds to zero);
+    * brute force with Python's float64 exp and float32 rounding after each step
+      equals it bit for bit, tails included;
+    * glu_quant is quant_act of it over the gate/up halves, in that order.
+    """
+    import math
+    import torch
+    g = np.random.default_rng(seed)
+    gate = (g.standard_normal(4000) * np.exp2(g.uniform(-6, 6, 4000))).astype(np.float32)
+    up = (g.standard_normal(4000) * np.exp2(g.uniform(-6, 6, 4000))).astype(np.float32)
+    h = O.silu_glu(gate, up)
+    ref = (torch.nn.functional.silu(torch.from_numpy(gate).double()) * torch.from_numpy(up).double()).numpy()
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    keep = np.abs(gate) < 80
+    if not np.all((np.abs(h.astype(np.float64) - ref) <= 4 * ulp)[keep]):
+        return False, "torch silu"
+    for gv, uv in ((0.0, 3.0), (0.0, -3.0), (100.0, 1.5), (-200.0, 2.0), (-200.0, -2.0)):
+        hv = float(O.silu_glu(np.float32(gv), np.float32(uv)))
+        want = {0.0: 0.0 * uv, 100.0: gv * uv, -200.0: -0.0 * uv}[gv]
+        if hv != want or math.copysign(1, hv) != math.copysign(1, want):
+            return False, f"closed form g={gv} u={uv}: {hv}"
+    for gv, uv in list(zip(gate[:300], up[:300])) + [(np.float32(-95.5), np.float32(3.0)),
+                                                     (np.float32(-150.25), np.float32(-1.0))]:
+        ev = _f32(math.exp(-abs(float(gv))))
+        tv = _f32(1.0 + ev)
+        qv = _f32(float(gv) / tv) if gv >= 0 else _f32(_f32(float(gv) * ev) / tv)
+        hv = _f32(qv * float(uv))
+        ov = float(O.silu_glu(gv, uv))
+        if hv != ov or math.copysign(1, hv) != math.copysign(1, ov):
+            return False, f"brute force g={gv} u={uv}"
+    M, F = 3, 200
+    y = np.concatenate([gate[:M * F].reshape(M, F), up[:M * F].reshape(M, F)], axis=1)
+    q, s = O.glu_quant(y, F)
+    q2, s2 = O.quant_act(O.silu_glu(y[:, :F], y[:, F:]))
+    if not (np.array_equal(q, q2) and np.array_equal(s, s2)):
+        return False, "glu_quant composition"
+    return True, ""

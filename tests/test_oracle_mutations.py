@@ -173,3 +173,36 @@ def test_mutation_dense_transposed(monkeypatch):
     """Summing over the wrong weight index fails the dense brute-force pin."""
     monkeypatch.setattr(OM, "linear_dense", lambda x, wd: np.asarray(x, np.float64) @ np.asarray(wd, np.float64)[:, ::-1].T)
     assert _fails(P.pin_dense_brute_force, OM)
+
+
+def test_mutation_silu_sign_of_exponent(monkeypatch):
+    """exp(+|g|) in place of exp(-|g|) fails the activation pin."""
+    orig = OM.silu_glu
+
+    def wrong(g, u):
+        g = np.asarray(g, np.float32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            e = np.exp(np.abs(g.astype(np.float64))).astype(np.float32)
+            t = np.float32(1) + e
+            return np.where(g >= 0, g / t, (g * e) / t).astype(np.float32) * np.asarray(u, np.float32)
+    monkeypatch.setattr(OM, "silu_glu", wrong)
+    assert _fails(P.pin_silu_glu, OM)
+    monkeypatch.setattr(OM, "silu_glu", orig)
+    assert not _fails(P.pin_silu_glu, OM)
+
+
+def test_mutation_silu_negative_branch(monkeypatch):
+    """Using g / t for negative g as well (sigmoid of |g|) fails the activation pin."""
+    def wrong(g, u):
+        g = np.asarray(g, np.float32)
+        e = np.exp(-np.abs(g.astype(np.float64))).astype(np.float32)
+        return g / (np.float32(1) + e) * np.asarray(u, np.float32)
+    monkeypatch.setattr(OM, "silu_glu", wrong)
+    assert _fails(P.pin_silu_glu, OM)
+
+
+def test_mutation_glu_halves_swapped(monkeypatch):
+    """The gate taken from the up half (silu applied to the wrong operand) fails the activation pin."""
+    orig = OM.silu_glu
+    monkeypatch.setattr(OM, "silu_glu", lambda g, u: orig(u, g))
+    assert _fails(P.pin_silu_glu, OM)
