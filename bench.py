@@ -31,6 +31,8 @@ The same JSON line also carries:
   upcast to a dense BF16 copy (rotated over three weight copies, HBM roofline
   on its algorithmic bytes) and the dense BF16 product at M = 128 and 512
   (BF16 MFMA roofline);
+* ``ffn_chain``: the same FFN with the down projection fed by the gate/up
+  output through ``quant_glu`` (gated SiLU and quantization in one pass);
 * ``cpu_baseline``: the oracle (NumPy) on the host cores, running the same
   prefill step for about ten seconds, with the median time of each part.
 
@@ -284,6 +286,28 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
         describe_gate_up=w_gu.describe(B.ARM_W8A8, M), describe_down=w_dn.describe(B.ARM_W8A8, M),
         fixture_sha256=synth.sha256_of(*(m.codes for m in gu.members), gu.x),
     )
+    # Chained FFN: the down projection's input is the gate/up output taken
+    # through the gated activation and the quantizer in one pass (quant_glu),
+    # instead of a separate activation tensor.
+    def chain():
+        B.quant_act(x_gu, xq_gu, xs_gu)
+        B.linear_w8a8(w_gu, xq_gu, xs_gu, out=y_gu, workspace=ws_gu)
+        B.quant_glu(y_gu, xq_dn, xs_dn)
+        B.linear_w8a8(w_dn, xq_dn, xs_dn, out=y_dn, workspace=ws_dn)
+    g_chain = graph_of(torch, chain)
+    settle(torch, g_chain.replay, 0.3)
+    ms_chain = replay_ms(torch, g_chain, steps)
+    del g_chain
+    g_glu = graph_of(torch, lambda: B.quant_glu(y_gu, xq_dn, xs_dn), 20)
+    g_glu.replay()
+    sg = replay_stats(torch, g_glu, 50, 20)
+    del g_glu
+    F = w_dn.K
+    glu_bytes = M * 2 * F * 2 + M * F + M * (-(-F // 128)) * 4
+    res["ffn_chain"] = dict(ms_per_step=ms_chain, tflops=(flop_gu + flop_dn) / (ms_chain * 1e-3) / 1e12,
+                            glu_us=sg["median"] * 1e3, glu_us_p10=sg["p10"] * 1e3, glu_us_p90=sg["p90"] * 1e3,
+                            glu_launches=sg["launches"], glu_gbs=glu_bytes / (sg["median"] * 1e-3) / 1e9,
+                            glu_bytes=glu_bytes)
     del g_step, w_gu, w_dn
     return res
 
@@ -581,6 +605,17 @@ def main():
                     "gemm_gate_up_tflops": round(pre["rotated"]["gemm_gate_up_tflops"], 2),
                     "gemm_down_tflops": round(pre["rotated"]["gemm_down_tflops"], 2),
                     "kernels_us_stats": pre["rotated"]["kernels_us_stats"]},
+        "ffn_chain": {"note": "quant -> W8A8 gate/up -> quant_glu (silu(gate)*up quantized in one pass) -> W8A8 down: "
+                              "the down input is the gate/up output",
+                      "ms_per_step": round(pre["ffn_chain"]["ms_per_step"], 4),
+                      "tflops": round(pre["ffn_chain"]["tflops"], 2),
+                      "quant_glu": {"us": round(pre["ffn_chain"]["glu_us"], 2),
+                                    "p10": round(pre["ffn_chain"]["glu_us_p10"], 2),
+                                    "p90": round(pre["ffn_chain"]["glu_us_p90"], 2),
+                                    "launches": pre["ffn_chain"]["glu_launches"],
+                                    "gbs": round(pre["ffn_chain"]["glu_gbs"], 1),
+                                    "bytes": pre["ffn_chain"]["glu_bytes"],
+                                    "frac_hbm": round(pre["ffn_chain"]["glu_gbs"] / HBM_PEAK_GBS, 4)}},
         "timing": "HIP graph replays: one replay per step; kernel times from graphs of 20 back-to-back launches",
         "fixture_sha256": pre["fixture_sha256"],
     }

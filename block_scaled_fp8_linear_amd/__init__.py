@@ -88,6 +88,9 @@ EXPORTS = [
     ("bsf8_parse_quant_config", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl)]),
     ("bsf8_inspect_safetensors", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl), ctypes.POINTER(Unit),
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+    ("bsf8_quant_glu", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_upcast", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_dense_workspace_size", ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -323,6 +326,23 @@ def quant_act(x, xq=None, xs=None):
     return xq, xs
 
 
+def quant_glu(y, xq=None, xs=None):
+    """Gate/up output y [M, 2F] (gate then up; float32 or bfloat16) -> the down projection's
+    quantized input for silu(gate) * up: (xq uint8 [M, F], xs f32 [M, ceil(F/128)])."""
+    torch = _torch()
+    if y.dim() != 2 or y.stride(1) != 1 or y.shape[1] % 2:
+        raise ValueError("y must be 2-D with an even number of columns and unit column stride")
+    M, F = y.shape[0], y.shape[1] // 2
+    Fb = -(-F // BLOCK)
+    if xq is None:
+        xq = torch.empty((M, F), dtype=torch.uint8, device=y.device)
+    if xs is None:
+        xs = torch.empty((M, Fb), dtype=torch.float32, device=y.device)
+    _check(lib().bsf8_quant_glu(y.data_ptr(), _dt_of(y), M, F, y.stride(0), xq.data_ptr(), xq.stride(0),
+                                xs.data_ptr(), xs.stride(0), _stream_ptr(y.device)), "quant_glu")
+    return xq, xs
+
+
 def linear_w8a16(w: BlockFP8Weight, x, out_dtype=None, out=None, workspace=None):
     """F32-activation arm: y [M, N] = x . dequant(W)^T (float32 output unless out_dtype says bfloat16)."""
     torch = _torch()
@@ -396,7 +416,7 @@ def linear_dense(wd, x, out_dtype=None, out=None, workspace=None):
     return y
 
 
-__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "linear_w8a16", "linear_w8a8", "upcast",
+__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "quant_glu", "linear_w8a16", "linear_w8a8", "upcast",
            "linear_dense", "dense_workspace_size", "lib", "status_name", "ARM_W8A16", "ARM_W8A8", "ARM_DENSE",
            "EXPORTS", "LIB_PATH", "MAX_MEMBERS"]
 

@@ -49,6 +49,9 @@ bsf8_status device_status(hipError_t e, const char* what);
 bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
                              uint8_t* xq, int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream);
 
+bsf8_status launch_quant_glu(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
+                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream);
+
 size_t w8a16_workspace_bytes(const WeightDev& w, int64_t M);
 bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x_bf16, int64_t M,
                          int64_t ldx, void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes,

@@ -15,6 +15,16 @@
 // the hardware RNE conversion v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950), which keeps
 // the sign of zero.  The kernel is HBM-bound: 4 (or 2) bytes in and 1 byte out
 // per channel, plus 4 bytes per group.
+//
+// The GLU instance is the step between the dense FFN's gate/up GEMM and its
+// down GEMM ("Module w8a8_prefill", preamble: the gate/up/down prefill arm):
+// it reads the gate/up output [M, 2F] (gate in columns [0, F), up in [F, 2F)),
+// forms h = silu(gate) * up in registers and quantizes h, so the activated
+// tensor never goes to memory.  The activation is the gated SiLU of the Qwen
+// dense FFN (the pages do not name one), evaluated in a fixed, overflow-free
+// order so that the codes are reproducible: e = exp(-|g|) in F64 rounded to
+// F32, t = 1 + e, q = g / t (g >= 0) or (g * e) / t, h = q * u, each an IEEE
+// F32 operation.  Per channel: 2 x 4 (or 2 x 2) bytes in, 1 byte out.
 #include <hip/hip_runtime.h>
 
 #include "bsf8_internal.h"
@@ -55,7 +65,17 @@ __device__ __forceinline__ void load4(const void* x, int64_t off, int valid, boo
   }
 }
 
-template <bool BF16>
+// h = silu(g) * u in the fixed order above (no contraction: no product is
+// followed by an add).
+__device__ __forceinline__ float silu_glu(float g, float u) {
+  const float e = static_cast<float>(exp(-fabs(static_cast<double>(g))));
+  const float t = 1.0f + e;
+  const float q = g >= 0.0f ? g / t : (g * e) / t;
+  return q * u;
+}
+
+// GLU: x is the gate/up output; K = F, the up half starts at column K.
+template <bool BF16, bool GLU>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int32_t M, int32_t K,
                                                                   int64_t ldx, uint8_t* __restrict__ xq, int64_t ldq,
                                                                   float* __restrict__ xs, int64_t ldxs, int32_t Kb,
@@ -78,6 +98,12 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
     kk[j] = gcol[j] * kBlock + lane32 * 4;
     valid[j] = live ? max(0, min(4, K - kk[j])) : 0;
     load4<BF16>(x, mrow[j] * ldx + kk[j], valid[j], x_vec != 0, v[j]);
+    if (GLU) {
+      float u[4];
+      load4<BF16>(x, mrow[j] * ldx + K + kk[j], valid[j], x_vec != 0, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = silu_glu(v[j][e], u[e]);   // lanes past K: silu(0) * 0 = 0
+    }
   }
 #pragma unroll
   for (int j = 0; j < kGroupsPerHalf; ++j) {
@@ -103,8 +129,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
 
 }  // namespace
 
-bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
-                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
+namespace {
+
+// glu: x is the gate/up output [M, 2K] and the quantized tensor is silu(gate) * up.
+bsf8_status launch_quant(const void* x, bool x_bf16, bool glu, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                         int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
   const int32_t Kb = int32_t((K + kBlock - 1) / kBlock);
   const int64_t n_groups = M * Kb;
   const int64_t per_block = int64_t(kQuantThreads / 32) * kGroupsPerHalf;
@@ -115,15 +144,29 @@ bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, i
   }
   const int grid = int(grid64);
   const size_t esz = x_bf16 ? 2 : 4;
-  const int x_vec = (reinterpret_cast<uintptr_t>(x) % (4 * esz) == 0) && ((ldx * esz) % (4 * esz) == 0);
+  // 4-element vector loads: the base, every row and (GLU) the up half's offset aligned
+  const int x_vec = (reinterpret_cast<uintptr_t>(x) % (4 * esz) == 0) && ((ldx * esz) % (4 * esz) == 0) &&
+                    (!glu || K % 4 == 0);
   const int q_vec = (reinterpret_cast<uintptr_t>(xq) % 4 == 0) && (ldq % 4 == 0);
-  if (x_bf16)
-    hipLaunchKernelGGL(quant_act_kernel<true>, dim3(grid), dim3(kQuantThreads), 0, stream, x, int32_t(M), int32_t(K),
-                       ldx, xq, ldq, xs, ldxs, Kb, x_vec, q_vec);
-  else
-    hipLaunchKernelGGL(quant_act_kernel<false>, dim3(grid), dim3(kQuantThreads), 0, stream, x, int32_t(M),
-                       int32_t(K), ldx, xq, ldq, xs, ldxs, Kb, x_vec, q_vec);
-  return device_status(hipGetLastError(), "quant_act launch");
+  using Kern = void (*)(const void*, int32_t, int32_t, int64_t, uint8_t*, int64_t, float*, int64_t, int32_t, int32_t,
+                        int32_t);
+  const Kern kern = x_bf16 ? (glu ? quant_act_kernel<true, true> : quant_act_kernel<true, false>)
+                           : (glu ? quant_act_kernel<false, true> : quant_act_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kQuantThreads), 0, stream, x, int32_t(M), int32_t(K), ldx, xq, ldq, xs,
+                     ldxs, Kb, x_vec, q_vec);
+  return device_status(hipGetLastError(), glu ? "quant_glu launch" : "quant_act launch");
+}
+
+}  // namespace
+
+bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
+  return launch_quant(x, x_bf16, false, M, K, ldx, xq, ldq, xs, ldxs, stream);
+}
+
+bsf8_status launch_quant_glu(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
+                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
+  return launch_quant(y, y_bf16, true, M, F, ldy, xq, ldq, xs, ldxs, stream);
 }
 
 }  // namespace bsf8

@@ -212,6 +212,27 @@ bsf8_status bsf8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K,
                            uint8_t* xq, int64_t ldq, float* xs, int64_t ldxs, void* stream);
 
 /*
+ * bsf8_quant_glu -- the step between the dense FFN's gate/up GEMM and its down
+ * GEMM: y [M, >= 2F] (leading dimension ldy, F32 or BF16) holds the gate
+ * outputs in columns [0, F) and the up outputs in [F, 2F) (a gate/up weight
+ * grouped as gate then up gives exactly this); the call writes the down GEMM's
+ * quantized input, xq [M, F] and xs [M, ceil(F/128)], as bsf8_quant_act would
+ * for h = silu(gate) * up, without writing h.
+ * ("Module w8a8_prefill", preamble and section "WHY (#917 / #928)": the
+ *  gate/up/down prefill arm; the down GEMM consumes per-token 1x128 E4M3
+ *  activations.  The pages do not name the activation: this is the gated SiLU
+ *  of the Qwen dense FFN.)
+ * h is formed in F32 in a fixed order, so the codes are reproducible:
+ *   e = exp(-|g|) evaluated in F64 and rounded to F32;  t = 1 + e;
+ *   q = g / t (g >= 0) or (g * e) / t (g < 0);  h = q * u,
+ * each an IEEE F32 operation; then quantized exactly as bsf8_quant_act does.
+ * Errors: INVALID_ARG (null, negative, ldy < 2F, ldq < F, ldxs < ceil(F/128),
+ * bad dtype), ALIGNMENT (y not element aligned), DEVICE.
+ */
+bsf8_status bsf8_quant_glu(const void* y, int32_t y_dtype, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
+                           int64_t ldq, float* xs, int64_t ldxs, void* stream);
+
+/*
  * bsf8_workspace_size -- device workspace bytes a compute call of this handle
  * needs for M tokens on the given arm (0 when none).  The W8A8 arm uses one
  * when its tile grid is too small to occupy the device (few tokens against few

@@ -205,3 +205,19 @@ def test_dense_arm_refuses_bad_arguments_without_launching():
         assert "arm=dense" in d and "N=428 K=256" in d
     finally:
         L.bsf8_weight_destroy(h)
+
+
+def test_quant_glu_refuses_bad_arguments_without_launching():
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 40)
+    name = lambda s: B.status_name(s)
+    assert L.bsf8_quant_glu(fake, B.DT_BF16, 0, 256, 512, fake, 256, fake, 2, None) == 0
+    assert L.bsf8_quant_glu(fake, B.DT_BF16, 4, 0, 512, fake, 256, fake, 2, None) == 0
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, -1, 256, 512, fake, 256, fake, 2, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_F16, 4, 256, 512, fake, 256, fake, 2, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 256, 511, fake, 256, fake, 2, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 256, 512, fake, 255, fake, 2, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 257, 514, fake, 257, fake, 2, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(None, B.DT_BF16, 4, 256, 512, fake, 256, fake, 2, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 4, 256, 512, fake, 256, fake, 2,
+                                 None)) == "ALIGNMENT"
