@@ -510,3 +510,49 @@ def test_read_stream_reads_every_byte():
         B.read_stream(buf, sink)
         want = np.bitwise_xor.reduce(host) if n else np.uint32(0)
         assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want
+
+
+@pytest.mark.parametrize("K", [384, 336])
+@pytest.mark.parametrize("out,pad", [("bf16", 0), ("f32", 0), ("bf16", 3)])
+def test_w8a8_many_work_items(K, out, pad):
+    """More 256x256 work items than compute units (4000 tokens x grouped members of 1000,
+    1000 and 2100 rows: 272 tiles plus a split tail), so each block walks several items
+    and the stores of one overlap the next; K = 336 runs the ragged-K copies; pad = 3
+    gives an output row pitch that is not 16-byte aligned."""
+    t = torch()
+    rows = (1000, 1000, 2100)
+    ms = [synth.random_code_weight(171, f"many_W{i}_{K}", r, K) for i, r in enumerate(rows)]
+    w, _keep = weight_on_device(ms)
+    om = oracle_members(ms)
+    M = 4000
+    x = synth.gaussian_activations(171, f"many_X{K}", M, K)
+    xq_ref, xs_ref = O.quant_act(x)
+    odt = t.bfloat16 if out == "bf16" else t.float32
+    y = t.full((M, w.n_total + pad), 7.0, dtype=odt, device=device())
+    banner(f"many items K={K} out={out} pad={pad}: {w.describe(B.ARM_W8A8, M)}")
+    B.linear_w8a8(w, t.from_numpy(xq_ref).to(device()), t.from_numpy(xs_ref).to(device()), out_dtype=odt, out=y)
+    yn = to_np(y)
+    rs = sample_rows(w.n_total, rows, 40, seed=K)
+    tok = np.unique(np.concatenate([np.arange(4), np.arange(M - 4, M), np.random.default_rng(K).integers(0, M, 60)]))
+    ref = O.linear_w8a8_rows(xq_ref[tok], xs_ref[tok], om, rs)
+    assert_within(yn[np.ix_(tok, rs)], ref, O.abs_bound_w8a8_rows(xq_ref[tok], xs_ref[tok], om, rs), out == "bf16",
+                  "many items")
+    if pad:
+        assert np.all(yn[:, w.n_total:] == 7.0)
+
+
+def test_dense_many_work_items():
+    """The dense instance with more work items than compute units (N = 4100, M = 4000)."""
+    t = torch()
+    g = np.random.default_rng(173)
+    N, K, M = 4100, 512, 4000
+    wd_bits = O.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    x = O.f32_to_bf16(synth.gaussian_activations(173, "dense_many_X", M, K))
+    wd = t.from_numpy(wd_bits.view(np.int16)).to(device()).view(t.bfloat16)
+    xd = t.from_numpy(O.f32_to_bf16_bits(x).view(np.int16)).to(device()).view(t.bfloat16)
+    banner("dense many items N=4100 K=512 M=4000")
+    y = to_np(B.linear_dense(wd, xd, out_dtype=t.float32))
+    rs = sample_rows(N, [N], 40, seed=3)
+    tok = np.unique(np.concatenate([np.arange(4), np.arange(M - 4, M), g.integers(0, M, 60)]))
+    wf = O.bf16_bits_to_f32(wd_bits[rs])
+    assert_within(y[np.ix_(tok, rs)], O.linear_dense(x[tok], wf), O.abs_bound_dense(x[tok], wf), False, "dense many")
