@@ -615,7 +615,10 @@ def main():
                                     "launches": pre["ffn_chain"]["glu_launches"],
                                     "gbs": round(pre["ffn_chain"]["glu_gbs"], 1),
                                     "bytes": pre["ffn_chain"]["glu_bytes"],
-                                    "frac_hbm": round(pre["ffn_chain"]["glu_gbs"] / HBM_PEAK_GBS, 4)}},
+                                    "frac_hbm": round(pre["ffn_chain"]["glu_gbs"] / HBM_PEAK_GBS, 4),
+                                    "traffic": profiled_traffic("quant_glu_ffn_m1024"),
+                                    "note": "bound by the ALU (an F64 exp and two IEEE F32 divisions per channel), "
+                                            "not by HBM"}},
         "timing": "HIP graph replays: one replay per step; kernel times from graphs of 20 back-to-back launches",
         "fixture_sha256": pre["fixture_sha256"],
     }
