@@ -36,6 +36,7 @@
 //    and the weight stream is the only HBM traffic.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <string>
 
@@ -54,6 +55,7 @@ namespace bsf8 {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef bsf8_w16_v4i v4i;
 
 __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
@@ -615,12 +617,208 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// One token (M = 1, 16-byte aligned operands): plain F32 dot products on the
+// vector ALUs.  At one token the matrix unit saves nothing (each weight byte
+// is used once) and its fragment layout costs a transpose of the weights
+// through LDS; here a weight row's 128-byte K chunk is loaded by 8 lanes
+// (16 bytes each, full lines), decoded exactly to F32 in registers
+// (v_cvt_scalef32_pk_f32_fp8, unit scale) and multiplied by the 16
+// activations that lane holds for that chunk, so there is no LDS traffic until
+// the final reduction.  A block owns G groups of 8 rows of one member (G is
+// chosen so that the grid is about one block per compute unit) and all of K;
+// its 8 waves split K into contiguous chunk ranges and every load of a wave is
+// issued before any arithmetic.  The chunk partial of each row is scaled by
+// its block scale (a block's rows span at most two rows of the grid, each
+// lane picks its own) into an F32 accumulator; lanes of a row are added by
+// shuffles and the 8 waves' partials in LDS in wave order (reproducible).
+// ---------------------------------------------------------------------------
+constexpr int M1_MAX_G = 4;
+
+template <bool XBF16, bool SBF16, int G, int CPW>
+__global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
+  __shared__ float red[WAVES][G * 8];
+  const int tile = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
+  const int rtile = tile - a.tm.tile0[mi];
+  const MemberDev mem = a.w.m[mi];
+  const int K = a.w.K, Kb = a.w.Kb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jp = lane & 7;    // 16-byte piece of a 128-byte chunk
+  const int rl = lane >> 3;   // row within an 8-row group
+  const int row0 = rtile * G * 8;
+  const int c_begin = min(Kb, wave * CPW);
+  const int c_end = min(Kb, c_begin + CPW);
+
+  const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
+  const v4i rw = make_rsrc(mem.w, w_bytes);
+  constexpr uint32_t XE = XBF16 ? 2u : 4u;
+  const uint32_t x_bytes = uint32_t(K) * XE;
+  const v4i rx = make_rsrc(a.x, x_bytes);
+  constexpr int XL = XBF16 ? 2 : 4;   // 16-byte activation loads per chunk piece
+
+  // ---- the chunk scales of the (at most two) grid rows the block's rows use,
+  // issued first and without branches, so that waiting for them never waits
+  // for the weight stream behind them (loads retire in order)
+  const int nb = (mem.rows + 127) >> 7;
+  const int srow = row0 >> 7;
+  const int srow1 = min(srow + 1, nb - 1);
+  // raw bits now, widened to F32 at use (a conversion here would wait for the loads)
+  uint32_t sc0[CPW], sc1[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int chunk = min(c_begin + c, Kb - 1);
+    const int64_t i0 = int64_t(srow) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
+    const int64_t i1 = int64_t(srow1) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
+    if (SBF16) {
+      sc0[c] = static_cast<const uint16_t*>(mem.s)[i0];
+      sc1[c] = static_cast<const uint16_t*>(mem.s)[i1];
+    } else {
+      sc0[c] = static_cast<const uint32_t*>(mem.s)[i0];
+      sc1[c] = static_cast<const uint32_t*>(mem.s)[i1];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- every load of the wave: weights, activations (kept ahead of all arithmetic)
+  uint4 wv[CPW][G];
+  uint4 xr[CPW][XL];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int chunk = c_begin + c;
+    const int k = chunk * CHUNK + 16 * jp;
+    const bool live = chunk < c_end && k < K;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int r = row0 + 8 * g + rl;
+      const uint32_t off = live && r < mem.rows ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
+      wv[c][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, 0));
+    }
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const uint32_t off = live ? uint32_t(k) * XE + 16u * q : x_bytes;
+      xr[c][q] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    float xv[16];
+    if (XBF16) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t w4[4] = {xr[c][q].x, xr[c][q].y, xr[c][q].z, xr[c][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[8 * q + 2 * e] = __uint_as_float(w4[e] << 16);
+          xv[8 * q + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[4 * q] = __uint_as_float(xr[c][q].x);
+        xv[4 * q + 1] = __uint_as_float(xr[c][q].y);
+        xv[4 * q + 2] = __uint_as_float(xr[c][q].z);
+        xv[4 * q + 3] = __uint_as_float(xr[c][q].w);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t w4[4] = {wv[c][g].x, wv[c][g].y, wv[c][g].z, wv[c][g].w};
+      float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, true);
+        p[0] = fmaf(xv[4 * e], lo[0], p[0]);
+        p[1] = fmaf(xv[4 * e + 1], lo[1], p[1]);
+        p[2] = fmaf(xv[4 * e + 2], hi[0], p[2]);
+        p[3] = fmaf(xv[4 * e + 3], hi[1], p[3]);
+      }
+      const int r = row0 + 8 * g + rl;
+      const uint32_t sb = (r >> 7) == srow ? sc0[c] : sc1[c];
+      const float sw = __uint_as_float(SBF16 ? sb << 16 : sb);
+      acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), sw, acc[g]);
+    }
+  }
+  // ---- rows: the 8 lanes of a row, then the 8 waves in order
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    acc[g] += __shfl_xor(acc[g], 1);
+    acc[g] += __shfl_xor(acc[g], 2);
+    acc[g] += __shfl_xor(acc[g], 4);
+    if (jp == 0) red[wave][8 * g + rl] = acc[g];
+  }
+  __syncthreads();
+  if (tid < G * 8) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[w][tid];
+    const int row = row0 + tid;
+    if (row < mem.rows) {
+      const int64_t off = mem.col0 + row;
+      if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
+      else static_cast<float*>(a.y)[off] = sum;
+    }
+  }
+}
+
 struct Plan {
   TileMap tm;
   int col_tiles;
   int tiles;
   int chunks_per_wave;
 };
+
+// Compute units of the current device (cached per device).
+int w16_device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// The one-token kernel's shape: 8-row groups per block (about one block per
+// compute unit) and chunks per wave; g = 0 when it does not apply.
+struct M1Shape {
+  int g;
+  int cpw;
+  TileMap tm;
+  int tiles;
+};
+
+M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
+  M1Shape m{};
+  if (!aligned || M != 1 || w.Kb > WAVES * 5) return m;
+  m.cpw = w.Kb <= WAVES * 4 ? 4 : 5;
+  int64_t groups = 0;
+  for (int i = 0; i < w.n_members; ++i) groups += (w.m[i].rows + 7) / 8;
+  const int cus = w16_device_cus();
+  m.g = int(std::min<int64_t>(M1_MAX_G, std::max<int64_t>(2, (groups + cus - 1) / cus)));
+  int t = 0;
+  for (int i = 0; i < w.n_members; ++i) {
+    m.tm.tile0[i] = t;
+    m.tm.n_tiles[i] = (w.m[i].rows + 8 * m.g - 1) / (8 * m.g);
+    t += m.tm.n_tiles[i];
+  }
+  m.tm.tile0[w.n_members] = t;
+  m.tiles = t;
+  return m;
+}
 
 Plan make_plan(const WeightDev& w, int64_t M) {
   Plan p{};
@@ -647,6 +845,16 @@ int small_depth(int chunks_per_wave) {
 }
 
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
+  const M1Shape m1 = m1_shape(w, aligned, M > 0 ? M : 1);
+  if (m1.g) {
+    char b1[384];
+    snprintf(b1, sizeof(b1),
+             "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), f32 fma accumulate | "
+             "kernel=w8a16_m1 rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all loads first, "
+             "8 lanes per 128-byte row piece, no LDS transpose) | M=1 blocks=%d",
+             8 * m1.g, m1.g, WAVES, m1.cpw, m1.tiles);
+    return b1;
+  }
   const Plan p = make_plan(w, M > 0 ? M : 1);
   const bool small = aligned && M >= 1 && M <= SM_MAXM;
   char ring[160] = "";
@@ -675,6 +883,30 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   for (int i = 0; i < w.n_members; ++i)
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) aligned = false;
   if (p.tiles == 0) return BSF8_OK;
+  const M1Shape m1 = m1_shape(w, aligned, M);
+  if (m1.g) {
+    Args a{};
+    a.w = w;
+    a.tm = m1.tm;
+    a.x = x;
+    a.y = y;
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.M = 1;
+    a.col_tiles = 1;
+    a.chunks_per_wave = m1.cpw;
+    a.x_bf16 = x_bf16 ? 1 : 0;
+    a.y_bf16 = y_bf16 ? 1 : 0;
+    const bool sb = w.scale_bf16 != 0;
+#define BSF8_M1(G, C)                                                                                         \
+  (x_bf16 ? (sb ? w8a16_m1_kernel<true, true, G, C> : w8a16_m1_kernel<true, false, G, C>)                     \
+          : (sb ? w8a16_m1_kernel<false, true, G, C> : w8a16_m1_kernel<false, false, G, C>))
+    auto k1 = m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
+                          : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5));
+#undef BSF8_M1
+    hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
+    return device_status(hipGetLastError(), "w8a16_m1 launch");
+  }
   Args a{};
   a.w = w;
   a.tm = p.tm;
