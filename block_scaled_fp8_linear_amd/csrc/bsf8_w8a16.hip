@@ -772,6 +772,193 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Two to four tokens (aligned operands, K <= 5120): the one-token kernel's
+// layout with the activations in LDS.  Each wave copies the slice it uses
+// (MT tokens x its chunk range, widened to F32) into a wave-private LDS
+// region; the loads are issued before the weight stream and written to LDS
+// once the stream is in flight (loads retire in order, so waiting for them
+// never waits for weights).  Per chunk, each lane decodes its 16 weight bytes
+// of every row group to F32 and multiplies them by the row's block scale once
+// (exact for BF16 scales), then runs 16 FMAs per token into that row and
+// token's accumulator; activations are read from LDS (lanes of the same piece
+// position read the same address).  Rows are summed over their 8 lanes by
+// shuffles and over the waves in LDS, in wave order.
+// ---------------------------------------------------------------------------
+template <bool XBF16, bool SBF16, int G, int CPW, int MT>
+__global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
+  constexpr int XS = MT * CPW * CHUNK;   // F32 activations per wave
+  __shared__ __attribute__((aligned(16))) float xl[WAVES * XS];
+  const int tile = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
+  const int rtile = tile - a.tm.tile0[mi];
+  const MemberDev mem = a.w.m[mi];
+  const int K = a.w.K, Kb = a.w.Kb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jp = lane & 7;
+  const int rl = lane >> 3;
+  const int row0 = rtile * G * 8;
+  const int c_begin = min(Kb, wave * CPW);
+  const int c_end = min(Kb, c_begin + CPW);
+  const int k_end = min(K, c_end * CHUNK);
+
+  const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
+  const v4i rw = make_rsrc(mem.w, w_bytes);
+  constexpr uint32_t XE = XBF16 ? 2u : 4u;
+  const uint32_t x_bytes = uint32_t(a.M) * uint32_t(a.ldx) * XE;
+  const v4i rx = make_rsrc(a.x, x_bytes);
+
+  // ---- chunk scales first (raw bits, widened at use)
+  const int nb = (mem.rows + 127) >> 7;
+  const int srow = row0 >> 7;
+  const int srow1 = min(srow + 1, nb - 1);
+  uint32_t sc0[CPW], sc1[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int chunk = min(c_begin + c, Kb - 1);
+    const int64_t i0 = int64_t(srow) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
+    const int64_t i1 = int64_t(srow1) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
+    if (SBF16) {
+      sc0[c] = static_cast<const uint16_t*>(mem.s)[i0];
+      sc1[c] = static_cast<const uint16_t*>(mem.s)[i1];
+    } else {
+      sc0[c] = static_cast<const uint32_t*>(mem.s)[i0];
+      sc1[c] = static_cast<const uint32_t*>(mem.s)[i1];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- the wave's activation slice: MT tokens x CPW chunks, as 16-byte pieces
+  constexpr int PPT = CPW * CHUNK * int(XE) / 16;   // pieces per token
+  constexpr int XPL = (MT * PPT + 63) / 64;         // pieces per lane
+  constexpr int EPP = 16 / int(XE);                 // elements per piece
+  uint4 xr[XPL];
+#pragma unroll
+  for (int i = 0; i < XPL; ++i) {
+    const int piece = lane + 64 * i;
+    const int t = piece / PPT, pp = piece - t * PPT;
+    const int k = c_begin * CHUNK + pp * EPP;
+    const bool ok = piece < MT * PPT && t < a.M && k < k_end;
+    const uint32_t off = ok ? (uint32_t(t) * uint32_t(a.ldx) + uint32_t(k)) * XE : x_bytes;
+    xr[i] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
+  }
+  // ---- the weight stream
+  uint4 wv[CPW][G];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int chunk = c_begin + c;
+    const int k = chunk * CHUNK + 16 * jp;
+    const bool live = chunk < c_end && k < K;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int r = row0 + 8 * g + rl;
+      const uint32_t off = live && r < mem.rows ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
+      wv[c][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, 0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- activations into this wave's LDS region, as F32: token t, element e of the slice at t * CPW*CHUNK + e
+  float* xw = xl + wave * XS;
+#pragma unroll
+  for (int i = 0; i < XPL; ++i) {
+    const int piece = lane + 64 * i;
+    if (piece < MT * PPT) {
+      const int t = piece / PPT, pp = piece - t * PPT;
+      float* dst = xw + t * (CPW * CHUNK) + pp * EPP;
+      if (XBF16) {
+        const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        reinterpret_cast<float4*>(dst)[0] = make_float4(__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xFFFF0000u),
+                                                        __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xFFFF0000u));
+        reinterpret_cast<float4*>(dst)[1] = make_float4(__uint_as_float(w4[2] << 16), __uint_as_float(w4[2] & 0xFFFF0000u),
+                                                        __uint_as_float(w4[3] << 16), __uint_as_float(w4[3] & 0xFFFF0000u));
+      } else {
+        *reinterpret_cast<uint4*>(dst) = xr[i];
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+
+  float acc[G][MT];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[g][t] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    float wd[G][16];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int r = row0 + 8 * g + rl;
+      const uint32_t sb = (r >> 7) == srow ? sc0[c] : sc1[c];
+      const float sw = __uint_as_float(SBF16 ? sb << 16 : sb);
+      const uint32_t w4[4] = {wv[c][g].x, wv[c][g].y, wv[c][g].z, wv[c][g].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, true);
+        wd[g][4 * e] = lo[0] * sw;
+        wd[g][4 * e + 1] = lo[1] * sw;
+        wd[g][4 * e + 2] = hi[0] * sw;
+        wd[g][4 * e + 3] = hi[1] * sw;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float* xp = xw + t * (CPW * CHUNK) + c * CHUNK + 16 * jp;
+      float xv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(xp)[q];
+        xv[4 * q] = v.x;
+        xv[4 * q + 1] = v.y;
+        xv[4 * q + 2] = v.z;
+        xv[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[g][t] = fmaf(xv[e], wd[g][e], acc[g][t]);
+    }
+  }
+  // ---- rows: the 8 lanes of a row by shuffles; the waves through each wave's own region
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      float v = acc[g][t];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      acc[g][t] = v;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  if (jp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) xw[t * (G * 8) + 8 * g + rl] = acc[g][t];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * 8 * MT; i += THREADS) {
+    const int t = i / (G * 8), rr = i - t * (G * 8);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += xl[w * XS + i];
+    const int row = row0 + rr;
+    if (t < a.M && row < mem.rows) {
+      const int64_t off = int64_t(t) * a.ldy + mem.col0 + row;
+      if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
+      else static_cast<float*>(a.y)[off] = sum;
+    }
+  }
+}
+
 struct Plan {
   TileMap tm;
   int col_tiles;
@@ -803,8 +990,10 @@ struct M1Shape {
 
 M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
   M1Shape m{};
-  if (!aligned || M != 1 || w.Kb > WAVES * 5) return m;
-  m.cpw = w.Kb <= WAVES * 4 ? 4 : 5;
+  // (at five to eight tokens the FMAs and activation reads outweigh the MFMA
+  // kernel's transpose: 15.4 against 15.0 us for 8 tokens of W [5120,5120])
+  if (!aligned || M < 1 || M > 4 || w.Kb > WAVES * 5) return m;
+  m.cpw = M == 1 && w.Kb <= WAVES * 4 ? 4 : 5;
   int64_t groups = 0;
   for (int i = 0; i < w.n_members; ++i) groups += (w.m[i].rows + 7) / 8;
   const int cus = w16_device_cus();
@@ -847,12 +1036,14 @@ int small_depth(int chunks_per_wave) {
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   const M1Shape m1 = m1_shape(w, aligned, M > 0 ? M : 1);
   if (m1.g) {
-    char b1[384];
+    char b1[448];
     snprintf(b1, sizeof(b1),
              "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), f32 fma accumulate | "
-             "kernel=w8a16_m1 rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all loads first, "
-             "8 lanes per 128-byte row piece, no LDS transpose) | M=1 blocks=%d",
-             8 * m1.g, m1.g, WAVES, m1.cpw, m1.tiles);
+             "kernel=%s rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all loads first, "
+             "8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
+             M <= 1 ? "w8a16_m1" : "w8a16_mt", 8 * m1.g, m1.g, WAVES, m1.cpw,
+             M <= 1 ? "" : ", 4-token activation slices in LDS",
+             (long long)(M > 0 ? M : 1), m1.tiles);
     return b1;
   }
   const Plan p = make_plan(w, M > 0 ? M : 1);
@@ -892,7 +1083,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     a.y = y;
     a.ldx = ldx;
     a.ldy = ldy;
-    a.M = 1;
+    a.M = int32_t(M);
     a.col_tiles = 1;
     a.chunks_per_wave = m1.cpw;
     a.x_bf16 = x_bf16 ? 1 : 0;
@@ -901,9 +1092,14 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
 #define BSF8_M1(G, C)                                                                                         \
   (x_bf16 ? (sb ? w8a16_m1_kernel<true, true, G, C> : w8a16_m1_kernel<true, false, G, C>)                     \
           : (sb ? w8a16_m1_kernel<false, true, G, C> : w8a16_m1_kernel<false, false, G, C>))
-    auto k1 = m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
-                          : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5));
+#define BSF8_MT(G, T)                                                                                        \
+  (x_bf16 ? (sb ? w8a16_mt_kernel<true, true, G, 5, T> : w8a16_mt_kernel<true, false, G, 5, T>)                 \
+          : (sb ? w8a16_mt_kernel<false, true, G, 5, T> : w8a16_mt_kernel<false, false, G, 5, T>))
+    auto k1 = M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
+                                    : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5)))
+            : (m1.g == 2 ? BSF8_MT(2, 4) : m1.g == 3 ? BSF8_MT(3, 4) : BSF8_MT(4, 4));
 #undef BSF8_M1
+#undef BSF8_MT
     hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
     return device_status(hipGetLastError(), "w8a16_m1 launch");
   }

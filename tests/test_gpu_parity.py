@@ -556,3 +556,24 @@ def test_dense_many_work_items():
     tok = np.unique(np.concatenate([np.arange(4), np.arange(M - 4, M), g.integers(0, M, 60)]))
     wf = O.bf16_bits_to_f32(wd_bits[rs])
     assert_within(y[np.ix_(tok, rs)], O.linear_dense(x[tok], wf), O.abs_bound_dense(x[tok], wf), False, "dense many")
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_w8a16_few_tokens_f32_grids_straddling_blocks(M):
+    """Two to four tokens on grouped members (4000 and 200 rows: 525 groups of 8 rows, so
+    blocks of 24 rows straddle 128-row scale blocks) with F32 grids that are not BF16 values;
+    K = 5120 gives each wave 5 chunks.  Sampled rows, every token."""
+    t = torch()
+    g = np.random.default_rng(181 + M)
+    K = 5120
+    om = []
+    for r in (4000, 200):
+        codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)[g.integers(0, 254, (r, K))]
+        om.append((codes, np.exp2(g.uniform(-10, -3, O.scale_grid_shape(r, K))).astype(np.float32)))
+    w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.from_numpy(s).to(device())) for c, s in om])
+    x = synth.gaussian_activations(181, f"straddle_X{M}", M, K)
+    banner(f"w8a16 M={M} f32 grids straddling: {w.describe(B.ARM_W8A16, M)}")
+    y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
+    rows = sample_rows(w.n_total, [4000, 200], 60, seed=M)
+    assert_within(y[:, rows], O.linear_w8a16_rows(x, om, rows), O.abs_bound_w8a16_rows(x, om, rows), False,
+                  f"M={M} straddling")
