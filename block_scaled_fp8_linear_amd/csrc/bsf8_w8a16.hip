@@ -367,7 +367,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //    wave-private LDS scratch in fragment order; tokens past M read a zero row;
 //  * a ring of SM_DEPTH chunks of both operands is in flight in registers
 //    (as many as a wave has chunks, up to 5, so decode K <= 5120 issues all of
-//    a wave's loads at once; 3 for F32 at M > 4, where registers run out);
+//    a wave's loads at once; 3 for F32 at M > 4, where registers run out, or 4
+//    when that is all of a wave's chunks);
 //    loads retire in issue order, so each slot's loads are issued together and
 //    slots in chunk order (scheduling barriers keep them grouped), and chunks
 //    past the wave's range get past-the-end offsets (zeros, no traffic).
@@ -1051,7 +1052,8 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   char ring[160] = "";
   if (small)
     snprintf(ring, sizeof(ring), ", %d-chunk load ring%s, compact activations split in LDS, F32 terms in MFMA columns",
-             small_depth(p.chunks_per_wave), M > 4 ? " (3 for F32 activations)" : "");
+             small_depth(p.chunks_per_wave),
+             M > 4 ? (p.chunks_per_wave == 4 ? " (4 for F32 activations)" : " (3 for F32 activations)") : "");
   char buf[512];
   snprintf(buf, sizeof(buf),
            "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
@@ -1130,7 +1132,12 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     } else if (M <= 4) {
       kern = M <= 2 ? BSF8_SMALL(false, 1, 1) : BSF8_SMALL(false, 2, 1);
     } else {
-      kern = sb ? w8a16_small_m_kernel<false, true, 4, 2, 3> : w8a16_small_m_kernel<false, false, 4, 2, 3>;
+      // F32 tokens 5-8: a ring of 4 (254 registers) when it holds all of a wave's
+      // chunks (W [5000,4000]: 15.6 -> 14.2 us at M = 8), else 3 (a ring of 4
+      // then 1 chunk measured 18.5 against 15.0 us with 5 chunks)
+      kern = p.chunks_per_wave == 4
+                 ? (sb ? w8a16_small_m_kernel<false, true, 4, 2, 4> : w8a16_small_m_kernel<false, false, 4, 2, 4>)
+                 : (sb ? w8a16_small_m_kernel<false, true, 4, 2, 3> : w8a16_small_m_kernel<false, false, 4, 2, 3>);
     }
 #undef BSF8_SMALL
   } else if (aligned) {
