@@ -8,9 +8,14 @@
 //  own block-row origin.)
 //
 // Design for CDNA4.  At decode sizes this is an HBM stream of the weight bytes.
-// A plain F32 FMA loop needs ~M FMAs per weight byte, which at M = 8 exceeds the
-// FP32 VALU rate before HBM is saturated, so the products run on the BF16
-// matrix cores without losing any activation bit:
+// Kernels by token count (16-byte aligned operands, K <= 5120 for the first two):
+//  * 1 token, and 2 to 4 tokens: F32 FMAs on the vector ALUs against weights
+//    decoded exactly to F32 in registers (w8a16_m1_kernel, w8a16_mt_kernel);
+//  * 5 to 8 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
+//  * more tokens, or any unaligned operand: the general MFMA kernel.
+// A plain F32 FMA loop needs ~M FMAs per weight byte, which beyond four tokens
+// outweighs the stream, so there the products run on the BF16 matrix cores
+// without losing any activation bit:
 //  * every E4M3 value is exact in BF16 (v_cvt_scalef32_pk_bf16_fp8, scale 1.0);
 //  * every F32 activation is split exactly as x = hi + mid + lo with three BF16
 //    values (truncate to the top 16 bits twice; each remainder is exact in F32

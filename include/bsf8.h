@@ -251,7 +251,11 @@ bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, si
  * with F32 activations (BF16 accepted and widened exactly) and F32
  * accumulation; weights used as stored, no operand requantized.
  * ("Qwen checkpoints with block FP8 weights", block-path and operator
- *  paragraphs; "th#1803", section "What lands": the resident=False arm.)
+ *  paragraphs; "FP8 Native Serving", section "Native FP8 vs dequant-to-BF16":
+ *  the weights are decoded where they are consumed, not in a copy.)
+ * Kernels: one token and two to four tokens run F32 FMAs against weights
+ * decoded exactly to F32 (aligned operands, K <= 5120); more tokens run the
+ * BF16 matrix cores on an exact three-term split of each F32 activation.
  *
  * x : [M, K] F32 or BF16, leading dimension ldx (elements), 16-byte aligned
  *     rows when K allows.
