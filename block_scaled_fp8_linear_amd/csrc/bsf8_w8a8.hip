@@ -343,6 +343,7 @@ struct FastArgs {
   int32_t rt_total;
   int32_t y_bf16;
   int32_t y_vec;   // y, ldy and every member's column offset allow 16-byte stores
+  int32_t y_nt;    // the output exceeds half the Infinity Cache: store it non-temporally
   // split-K for the row tiles from rt_split0 on: their K blocks are cut into
   // `splits` ranges of kb_per_split; split s of tile (R, mt) writes its F32
   // partial tile to ws + s * M * ldws, columns (R - rt_split0) * FBN + [0, FBN),
@@ -373,7 +374,12 @@ constexpr int F_OUT_PITCH = 144;  // bytes per token row of the store staging (1
 // one instruction touch 16 rows, which turns into many small partial-line
 // writes.  `buf` is this wave's 64 x F_OUT_PITCH staging area; the tile goes
 // out in rounds of 128 bytes per token row (4 row tiles of bf16, 2 of f32).
-template <bool YBF16>
+//
+// NT: non-temporal stores, for an output too large to stay in the Infinity
+// Cache for its consumer anyway; they keep it from evicting the operands the
+// GEMM is still reading (M = 8192, N = 18432: 302 MB of output, 2-3 % faster).
+typedef unsigned int bsf8_u4v __attribute__((ext_vector_type(4)));
+template <bool YBF16, bool NT = false>
 __device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uint8_t* buf, void* y, int64_t ldy,
                                                    int64_t col0, int n_base, int n_end, int m_base, int M, int lane) {
   constexpr int ESZ = YBF16 ? 2 : 4;
@@ -405,7 +411,10 @@ __device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uin
       if (m >= M || nvalid <= 0) continue;
       uint8_t* out = static_cast<uint8_t*>(y) + (int64_t(m) * ldy + col0 + n) * ESZ;
       if (nvalid >= EPC) {
-        *reinterpret_cast<uint4*>(out) = v;
+        if (NT)
+          __builtin_nontemporal_store(bsf8_u4v{v.x, v.y, v.z, v.w}, reinterpret_cast<bsf8_u4v*>(out));
+        else
+          *reinterpret_cast<uint4*>(out) = v;
       } else {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         for (int e = 0; e < nvalid; ++e) {
@@ -722,8 +731,12 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
       if (!whole)
         store_tile_via_lds<false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws,
                                   int64_t(R - a.rt_split0) * FBN - n0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+      else if (a.y_bf16 && a.y_nt)
+        store_tile_via_lds<true, true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       else if (a.y_bf16)
         store_tile_via_lds<true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+      else if (a.y_nt)
+        store_tile_via_lds<false, true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       else
         store_tile_via_lds<false>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       return;
@@ -938,6 +951,7 @@ bsf8_status launch_fast(const Plan& p, const WeightDev& w, bool dense, const uin
   bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (ldy * esz) % 16 == 0;
   for (int i = 0; i < w.n_members; ++i) vec = vec && (w.m[i].col0 * esz) % 16 == 0;
   a.y_vec = vec ? 1 : 0;
+  a.y_nt = M * int64_t(w.m[w.n_members - 1].col0 + w.m[w.n_members - 1].rows) * esz > (int64_t(128) << 20) ? 1 : 0;
   a.splits = p.splits;
   a.kb_per_split = p.kb_per_split;
   a.rt_split0 = p.rt_split0;
