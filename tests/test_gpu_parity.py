@@ -577,3 +577,62 @@ def test_w8a16_few_tokens_f32_grids_straddling_blocks(M):
     rows = sample_rows(w.n_total, [4000, 200], 60, seed=M)
     assert_within(y[:, rows], O.linear_w8a16_rows(x, om, rows), O.abs_bound_w8a16_rows(x, om, rows), False,
                   f"M={M} straddling")
+
+
+def _bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of BF16 values at |v| (normal range): 2^(e - 8) for |v| = m * 2^e, m in [0.5, 1)."""
+    _, e = np.frexp(np.abs(v.astype(np.float64)))
+    return np.ldexp(1.0, e - 8)
+
+
+AGREE_CASES = {
+    # name: (member rows, K, M)
+    "qkv_384_136_136_k768_m300": ((384, 136, 136), 768, 300),     # Kb = 6: no K split
+    "split_k_2048_k4096_m64": ((2048,), 4096, 64),
+    "ffn_down_shape_512_k17408_m40": ((512,), 17408, 40),
+}
+
+
+@pytest.mark.parametrize("name", list(AGREE_CASES))
+def test_w8a8_kernel_variants_agree(name):
+    """The two W8A8 GEMM kernels on the same quantized activation agree to a BF16 ULP or two
+    ("Module w8a8_prefill", section "WHY (#917 / #928)": the two FP8 GEMMs that consume one
+    quantized activation and one F32 epilogue).  A row pitch of K + 8 bytes for
+    the codes sends the call to the register-staged kernel, K to the direct-copy one.  Both
+    take the same 16x16x128 MFMA per scale block and the same F32 epilogue, so without a
+    K split the F32 outputs are identical; a split only regroups the F32 sum of the Kb
+    block terms (at most Kb * 2^-24 * sum|a w| apart) before the BF16 rounding."""
+    t = torch()
+    rows, K, M = AGREE_CASES[name]
+    ms = [synth.random_code_weight(191, f"agree_W{i}_{name}", r, K) for i, r in enumerate(rows)]
+    w, _keep = weight_on_device(ms)
+    x = synth.gaussian_activations(191, f"agree_X_{name}", M, K)
+    xq, xs = O.quant_act(x)
+    xqd, xsd = t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device())
+    pitched = t.zeros((M, K + 8), dtype=t.uint8, device=device())
+    pitched[:, :K] = xqd
+    xq_pitched = pitched[:, :K]
+    d_fast = w.describe(B.ARM_W8A8, M)
+    assert "kernel=w8a8_gemm_fast" in d_fast, d_fast
+    split = "split_k=1 " not in d_fast
+    om = oracle_members(ms)
+    S = O.abs_bound_w8a8(xq, xs, om)
+    Kb = -(-K // 128)
+    reorder = 2.0 * Kb * 2.0 ** -24 * S
+    for odt in (t.float32, t.bfloat16):
+        banner(f"w8a8 variants {name} {odt}: {d_fast}")
+        y_fast = to_np(B.linear_w8a8(w, xqd, xsd, out_dtype=odt))
+        y_staged = to_np(B.linear_w8a8(w, xq_pitched, xsd, out_dtype=odt))
+        diff = np.abs(y_fast.astype(np.float64) - y_staged.astype(np.float64))
+        if odt == t.float32:
+            if not split:
+                assert np.array_equal(y_fast.view(np.uint32), y_staged.view(np.uint32)), \
+                    f"{int(np.count_nonzero(y_fast != y_staged))} F32 outputs differ without a K split"
+            assert np.all(diff <= reorder), f"worst {float(np.max(diff / reorder)):.3g} of the reorder bound"
+        else:
+            ulp = _bf16_ulp(np.maximum(np.abs(y_fast), np.abs(y_staged)))
+            assert np.all(diff <= 2.0 * ulp + reorder), \
+                f"worst {float(np.max(diff / (2.0 * ulp + reorder))):.3g} of 2 ULP + reorder bound"
+            if not split:
+                assert np.array_equal(y_fast, y_staged)
+        assert_within(y_staged, O.linear_w8a8(xq, xs, om), S, odt == t.bfloat16, f"{name} register-staged")
