@@ -74,15 +74,16 @@ EXPORTS = [
                                              ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
     ("bsf8_quant_act", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                      ctypes.c_int64, ctypes.c_void_p]),
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_workspace_size", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                            ctypes.POINTER(ctypes.c_size_t)]),
     ("bsf8_linear_w8a16", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("bsf8_linear_w8a8", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
-                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]),
     ("bsf8_describe", ctypes.c_char_p, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]),
     ("bsf8_read_stream", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     ("bsf8_parse_quant_config", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl)]),
@@ -90,7 +91,7 @@ EXPORTS = [
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     ("bsf8_quant_glu", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                      ctypes.c_int64, ctypes.c_void_p]),
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_upcast", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_dense_workspace_size", ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -310,8 +311,17 @@ def _out(out, M, N, dtype, device):
     return out
 
 
+def scales_kmajor(M: int, Kb: int, device):
+    """An uninitialised [M, Kb] float32 scale tensor in the K-major layout (token index
+    contiguous: strides (1, M)), the layout the W8A8 product reads fastest."""
+    torch = _torch()
+    return torch.empty((Kb, M), dtype=torch.float32, device=device).t()
+
+
 def quant_act(x, xq=None, xs=None):
-    """Per-token 1x128 E4M3 quantization of x [M,K] (float32 or bfloat16) -> (xq uint8 [M,K], xs f32 [M,Kb])."""
+    """Per-token 1x128 E4M3 quantization of x [M,K] (float32 or bfloat16) -> (xq uint8 [M,K], xs f32 [M,Kb]).
+    xs may be any [M, Kb] float32 view in the token-major or the K-major layout; by default
+    it is a new K-major one."""
     torch = _torch()
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
@@ -320,15 +330,15 @@ def quant_act(x, xq=None, xs=None):
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if xs is None:
-        xs = torch.empty((M, Kb), dtype=torch.float32, device=x.device)
+        xs = scales_kmajor(M, Kb, x.device)
     _check(lib().bsf8_quant_act(x.data_ptr(), _dt_of(x), M, K, x.stride(0), xq.data_ptr(), xq.stride(0),
-                                xs.data_ptr(), xs.stride(0), _stream_ptr(x.device)), "quant_act")
+                                xs.data_ptr(), xs.stride(0), xs.stride(1), _stream_ptr(x.device)), "quant_act")
     return xq, xs
 
 
 def quant_glu(y, xq=None, xs=None):
     """Gate/up output y [M, 2F] (gate then up; float32 or bfloat16) -> the down projection's
-    quantized input for silu(gate) * up: (xq uint8 [M, F], xs f32 [M, ceil(F/128)])."""
+    quantized input for silu(gate) * up: (xq uint8 [M, F], xs f32 [M, ceil(F/128)]; xs as for quant_act)."""
     torch = _torch()
     if y.dim() != 2 or y.stride(1) != 1 or y.shape[1] % 2:
         raise ValueError("y must be 2-D with an even number of columns and unit column stride")
@@ -337,9 +347,9 @@ def quant_glu(y, xq=None, xs=None):
     if xq is None:
         xq = torch.empty((M, F), dtype=torch.uint8, device=y.device)
     if xs is None:
-        xs = torch.empty((M, Fb), dtype=torch.float32, device=y.device)
+        xs = scales_kmajor(M, Fb, y.device)
     _check(lib().bsf8_quant_glu(y.data_ptr(), _dt_of(y), M, F, y.stride(0), xq.data_ptr(), xq.stride(0),
-                                xs.data_ptr(), xs.stride(0), _stream_ptr(y.device)), "quant_glu")
+                                xs.data_ptr(), xs.stride(0), xs.stride(1), _stream_ptr(y.device)), "quant_glu")
     return xq, xs
 
 
@@ -362,12 +372,12 @@ def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=N
     """FP8 x FP8 arm with F32 epilogue: y [M, N] (bfloat16 output unless out_dtype says float32)."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
-    if xq.dim() != 2 or xq.shape[1] != w.K or xq.stride(1) != 1 or xs.stride(1) != 1:
-        raise ValueError("xq must be [M, K] and xs [M, Kb], unit column stride")
+    if xq.dim() != 2 or xq.shape[1] != w.K or xq.stride(1) != 1 or xs.dim() != 2:
+        raise ValueError("xq must be [M, K] with unit column stride and xs [M, Kb]")
     M = xq.shape[0]
     y = _out(out, M, w.n_total, out_dtype, xq.device)
     ws, wsb = workspace if workspace is not None else w.workspace(ARM_W8A8, M)
-    _check(lib().bsf8_linear_w8a8(w.handle, xq.data_ptr(), xq.stride(0), xs.data_ptr(), xs.stride(0), M,
+    _check(lib().bsf8_linear_w8a8(w.handle, xq.data_ptr(), xq.stride(0), xs.data_ptr(), xs.stride(0), xs.stride(1), M,
                                   y.data_ptr(), _dt_of(y), y.stride(0),
                                   ws.data_ptr() if ws is not None else None, wsb, _stream_ptr(xq.device)),
            "linear_w8a8")
@@ -418,7 +428,7 @@ def linear_dense(wd, x, out_dtype=None, out=None, workspace=None):
 
 __all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "quant_glu", "linear_w8a16", "linear_w8a8", "upcast",
            "linear_dense", "dense_workspace_size", "lib", "status_name", "ARM_W8A16", "ARM_W8A8", "ARM_DENSE",
-           "EXPORTS", "LIB_PATH", "MAX_MEMBERS"]
+           "EXPORTS", "LIB_PATH", "MAX_MEMBERS", "scales_kmajor"]
 
 
 READ_STREAM_SINK_WORDS = 2048  # BSF8_READ_STREAM_SINK_WORDS in include/bsf8.h

@@ -225,33 +225,46 @@ bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* memb
   return fail(BSF8_E_INVALID_ARG, "row not found");
 }
 
+// The two accepted activation scale layouts: token-major (xs_sk == 1, rows of
+// at least Kb) and K-major (xs_sm == 1, rows of at least M).
+static bool scale_layout_ok(int64_t M, int64_t Kb, int64_t xs_sm, int64_t xs_sk) {
+  return (xs_sk == 1 && xs_sm >= Kb) || (xs_sm == 1 && xs_sk >= M);
+}
+
 bsf8_status bsf8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
-                           int64_t ldq, float* xs, int64_t ldxs, void* stream) {
+                           int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, void* stream) {
   if (M < 0 || K < 0) return fail(BSF8_E_INVALID_ARG, "negative size");
   if (!dtype_ok(x_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "x dtype %d (F32 or BF16)", x_dtype);
   if (M == 0 || K == 0) return BSF8_OK;
   if (x == nullptr || xq == nullptr || xs == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
-  if (ldx < K || ldq < K || ldxs < ceil_div(K, kBlock)) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (ldx < K || ldq < K) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (!scale_layout_ok(M, ceil_div(K, kBlock), xs_sm, xs_sk))
+    return fail(BSF8_E_INVALID_ARG, "xs strides (%lld, %lld): neither token-major nor K-major", (long long)xs_sm,
+                (long long)xs_sk);
   if (M > INT32_MAX || K > INT32_MAX / 2) return fail(BSF8_E_UNSUPPORTED, "M or K too large");
   const size_t esz = x_dtype == BSF8_DT_F32 ? 4 : 2;
   if (reinterpret_cast<uintptr_t>(x) % esz || reinterpret_cast<uintptr_t>(xs) % 4)
     return fail(BSF8_E_ALIGNMENT, "x or xs not element aligned");
-  return launch_quant_act(x, x_dtype == BSF8_DT_BF16, M, K, ldx, xq, ldq, xs, ldxs,
+  return launch_quant_act(x, x_dtype == BSF8_DT_BF16, M, K, ldx, xq, ldq, xs, xs_sm, xs_sk,
                           static_cast<hipStream_t>(stream));
 }
 
 bsf8_status bsf8_quant_glu(const void* y, int32_t y_dtype, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
-                           int64_t ldq, float* xs, int64_t ldxs, void* stream) {
+                           int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, void* stream) {
   if (M < 0 || F < 0) return fail(BSF8_E_INVALID_ARG, "negative size");
   if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
   if (M == 0 || F == 0) return BSF8_OK;
   if (y == nullptr || xq == nullptr || xs == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
-  if (ldy < 2 * F || ldq < F || ldxs < ceil_div(F, kBlock)) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (ldy < 2 * F || ldq < F) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (!scale_layout_ok(M, ceil_div(F, kBlock), xs_sm, xs_sk))
+    return fail(BSF8_E_INVALID_ARG, "xs strides (%lld, %lld): neither token-major nor K-major", (long long)xs_sm,
+                (long long)xs_sk);
   if (M > INT32_MAX || F > INT32_MAX / 4) return fail(BSF8_E_UNSUPPORTED, "M or F too large");
   const size_t esz = y_dtype == BSF8_DT_F32 ? 4 : 2;
   if (reinterpret_cast<uintptr_t>(y) % esz || reinterpret_cast<uintptr_t>(xs) % 4)
     return fail(BSF8_E_ALIGNMENT, "y or xs not element aligned");
-  return launch_quant_glu(y, y_dtype == BSF8_DT_BF16, M, F, ldy, xq, ldq, xs, ldxs, static_cast<hipStream_t>(stream));
+  return launch_quant_glu(y, y_dtype == BSF8_DT_BF16, M, F, ldy, xq, ldq, xs, xs_sm, xs_sk,
+                          static_cast<hipStream_t>(stream));
 }
 
 bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, size_t* bytes) {
@@ -331,7 +344,8 @@ bsf8_status bsf8_linear_w8a16(const bsf8_weight* w, const void* x, int32_t x_dty
                       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
-bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t ldxs,
+bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t xs_sm,
+                             int64_t xs_sk,
                              int64_t M, void* y, int32_t y_dtype, int64_t ldy, void* workspace,
                              size_t workspace_bytes, void* stream) {
   if (w == nullptr) return fail(BSF8_E_INVALID_ARG, "null handle");
@@ -339,7 +353,10 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
   if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
   if (M == 0) return BSF8_OK;
   if (xq == nullptr || xs == nullptr || y == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
-  if (ldq < w->dev.K || ldxs < w->dev.Kb || ldy < w->n_total) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (ldq < w->dev.K || ldy < w->n_total) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (!scale_layout_ok(M, w->dev.Kb, xs_sm, xs_sk))
+    return fail(BSF8_E_INVALID_ARG, "xs strides (%lld, %lld): neither token-major nor K-major", (long long)xs_sm,
+                (long long)xs_sk);
   if (M > INT32_MAX / 2) return fail(BSF8_E_UNSUPPORTED, "M too large");
   const size_t ye = y_dtype == BSF8_DT_F32 ? 4 : 2;
   if (reinterpret_cast<uintptr_t>(xs) % 4 || reinterpret_cast<uintptr_t>(y) % ye)
@@ -350,7 +367,7 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
   if (workspace != nullptr && reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(BSF8_E_ALIGNMENT, "workspace not 256-byte aligned");
   const bool aligned = w->aligned16 && (reinterpret_cast<uintptr_t>(xq) % 16 == 0) && (ldq % 16 == 0);
-  return launch_w8a8(w->dev, aligned, xq, ldq, xs, ldxs, M, y, y_dtype == BSF8_DT_BF16, ldy, workspace,
+  return launch_w8a8(w->dev, aligned, xq, ldq, xs, xs_sm, xs_sk, M, y, y_dtype == BSF8_DT_BF16, ldy, workspace,
                      workspace_bytes, static_cast<hipStream_t>(stream));
 }
 

@@ -46,11 +46,13 @@ void set_error(const char* fmt, ...);
 bsf8_status device_status(hipError_t e, const char* what);
 
 // Kernel launchers (one per .hip translation unit).
+// Activation scales: element (m, kb) at xs[m * xs_sm + kb * xs_sk] (token-major
+// or K-major, checked by the host layer).
 bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx,
-                             uint8_t* xq, int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream);
+                             uint8_t* xq, int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream);
 
 bsf8_status launch_quant_glu(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
-                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream);
+                             int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream);
 
 size_t w8a16_workspace_bytes(const WeightDev& w, int64_t M);
 bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x_bf16, int64_t M,
@@ -60,7 +62,7 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M);
 
 size_t w8a8_workspace_bytes(const WeightDev& w, int64_t M);
 bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,
-                        int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
+                        int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M);
 

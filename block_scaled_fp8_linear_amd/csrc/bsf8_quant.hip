@@ -78,7 +78,8 @@ __device__ __forceinline__ float silu_glu(float g, float u) {
 template <bool BF16, bool GLU>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int32_t M, int32_t K,
                                                                   int64_t ldx, uint8_t* __restrict__ xq, int64_t ldq,
-                                                                  float* __restrict__ xs, int64_t ldxs, int32_t Kb,
+                                                                  float* __restrict__ xs, int64_t xs_sm, int64_t xs_sk,
+                                                                  int32_t Kb,
                                                                   int32_t x_vec, int32_t q_vec) {
   // Each 32-lane half-wave quantizes kGroupsPerHalf consecutive groups
   // (row-major over tokens and groups), loading all of them before any is
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
     } else {
       for (int e = 0; e < valid[j]; ++e) q[e] = uint8_t(uint32_t(packed) >> (8 * e));
     }
-    if (lane32 == 0) xs[mrow[j] * ldxs + gcol[j]] = s;
+    if (lane32 == 0) xs[mrow[j] * xs_sm + gcol[j] * xs_sk] = s;
   }
 }
 
@@ -133,7 +134,7 @@ namespace {
 
 // glu: x is the gate/up output [M, 2K] and the quantized tensor is silu(gate) * up.
 bsf8_status launch_quant(const void* x, bool x_bf16, bool glu, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
-                         int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
+                         int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream) {
   const int32_t Kb = int32_t((K + kBlock - 1) / kBlock);
   const int64_t n_groups = M * Kb;
   const int64_t per_block = int64_t(kQuantThreads / 32) * kGroupsPerHalf;
@@ -148,25 +149,25 @@ bsf8_status launch_quant(const void* x, bool x_bf16, bool glu, int64_t M, int64_
   const int x_vec = (reinterpret_cast<uintptr_t>(x) % (4 * esz) == 0) && ((ldx * esz) % (4 * esz) == 0) &&
                     (!glu || K % 4 == 0);
   const int q_vec = (reinterpret_cast<uintptr_t>(xq) % 4 == 0) && (ldq % 4 == 0);
-  using Kern = void (*)(const void*, int32_t, int32_t, int64_t, uint8_t*, int64_t, float*, int64_t, int32_t, int32_t,
-                        int32_t);
+  using Kern = void (*)(const void*, int32_t, int32_t, int64_t, uint8_t*, int64_t, float*, int64_t, int64_t, int32_t,
+                        int32_t, int32_t);
   const Kern kern = x_bf16 ? (glu ? quant_act_kernel<true, true> : quant_act_kernel<true, false>)
                            : (glu ? quant_act_kernel<false, true> : quant_act_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kQuantThreads), 0, stream, x, int32_t(M), int32_t(K), ldx, xq, ldq, xs,
-                     ldxs, Kb, x_vec, q_vec);
+                     xs_sm, xs_sk, Kb, x_vec, q_vec);
   return device_status(hipGetLastError(), glu ? "quant_glu launch" : "quant_act launch");
 }
 
 }  // namespace
 
 bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
-                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
-  return launch_quant(x, x_bf16, false, M, K, ldx, xq, ldq, xs, ldxs, stream);
+                             int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream) {
+  return launch_quant(x, x_bf16, false, M, K, ldx, xq, ldq, xs, xs_sm, xs_sk, stream);
 }
 
 bsf8_status launch_quant_glu(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
-                             int64_t ldq, float* xs, int64_t ldxs, hipStream_t stream) {
-  return launch_quant(y, y_bf16, true, M, F, ldy, xq, ldq, xs, ldxs, stream);
+                             int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream) {
+  return launch_quant(y, y_bf16, true, M, F, ldy, xq, ldq, xs, xs_sm, xs_sk, stream);
 }
 
 }  // namespace bsf8

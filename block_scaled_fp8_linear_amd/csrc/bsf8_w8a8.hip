@@ -68,7 +68,8 @@ struct GemmArgs {
   const float* xs;
   void* y;
   int64_t ldq;
-  int64_t ldxs;
+  int64_t xs_sm;   // activation scale (m, kb) at xs[m * xs_sm + kb * xs_sk]
+  int64_t xs_sk;
   int64_t ldy;
   int32_t M;
   int32_t m_tiles;
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
   for (int j = 0; j < TJ; ++j) {
     const int m = m0 + wm * WM + 16 * j + l16;
     m_ok[j] = m < M;
-    xs_row[j] = a.xs + int64_t(m_ok[j] ? m : 0) * a.ldxs;
+    xs_row[j] = a.xs + int64_t(m_ok[j] ? m : 0) * a.xs_sm;
   }
 
   v4f acc[TI][TJ];
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
     if (more) {
       sw_next = srow_ok ? load_scale(mem.s, s_base + int64_t(kb + 1) * a.w.s_cs, a.w.scale_bf16) : 0.f;
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) sa_next[j] = m_ok[j] ? xs_row[j][kb + 1] : 0.f;
+      for (int j = 0; j < TJ; ++j) sa_next[j] = m_ok[j] ? xs_row[j][int64_t(kb + 1) * a.xs_sk] : 0.f;
     }
 
     const uint8_t* As = smem + stage * STAGE_BYTES;
@@ -336,7 +337,8 @@ struct FastArgs {
   const float* xs;
   void* y;
   int64_t ldq;
-  int64_t ldxs;
+  int64_t xs_sm;   // activation scale (m, kb) at xs[m * xs_sm + kb * xs_sk]
+  int64_t xs_sk;
   int64_t ldy;
   int32_t M;
   int32_t m_tiles;
@@ -507,16 +509,19 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   const uint32_t b_bytes = uint32_t(M) * uint32_t(a.ldq);
   const v4i ra = make_rsrc(mem.w, a_bytes);
   const v4i rb = make_rsrc(a.xq, b_bytes);
-  const uint32_t s_bytes = uint32_t(M) * uint32_t(a.ldxs) * 4u;
+  // the scales' extent in bytes (below 2^31: the plan checks it)
+  const uint32_t s_bytes = uint32_t(((int64_t(M) - 1) * a.xs_sm + int64_t(Kb - 1) * a.xs_sk + 1) * 4);
   const v4i rs = make_rsrc(a.xs, s_bytes);
   // waves 0..3 each copy the scales of 64 tokens (one 4-byte element per
   // lane).  Lane L fetches token 16 (L & 3) + (L >> 2) of its wave's 64, so the
   // four scales a compute lane needs (tokens l16 + 16 j, j = 0..3) sit in one
-  // 16-byte LDS word.
+  // 16-byte LDS word.  With K-major scales (xs_sm = 1) a wave's copy reads
+  // 256 contiguous bytes; token-major, 64 words a row pitch apart.
   const bool s_wave = wave < FBM / 64;
   const int s_tok = m0 + wave * 64 + 16 * (lane & 3) + (lane >> 2);
   const bool s_ok = s_wave && s_tok < M;
-  const int s_off = s_tok * int(a.ldxs) * 4;
+  const int s_off = s_ok ? s_tok * int(a.xs_sm) * 4 : 0;
+  const int s_kstep = int(a.xs_sk) * 4;
   // Lane L of a 1 KiB wave copy fills chunk position L & 7 of row L >> 3 of its
   // 8-row slab; since the swizzle depends on r & 7 only, the logical chunk it
   // fetches is the same for every slab.
@@ -554,7 +559,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   auto issue_scales = [&](int kb, uint8_t* base) {
     if constexpr (!DENSE) {
       if (s_wave) {
-        const int off = s_ok ? s_off + kb * 4 : int(s_bytes);
+        const int off = s_ok ? s_off + kb * s_kstep : int(s_bytes);
         bsf8_raw_buffer_load_lds(rs, (lds_u32_ptr)(base + F_SA + wave * 256), 4, off, 0, 0, 0);
       }
     }
@@ -864,10 +869,13 @@ SplitChoice choose_splits(int rt_total, int m_tiles, int Kb, int cus) {
 }
 
 // The direct-copy kernel addresses each operand with 32-bit byte offsets from
-// its base, so every member and the activation block must stay below 2^31 bytes.
-Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
+// its base, so every member, the activation block and its scales must stay
+// below 2^31 bytes.
+// (xs_extent: elements spanned by the activation scales; -1: M x Kb.)
+Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq, int64_t xs_extent = -1) {
   Plan p{};
-  bool fits = M * ldq < (int64_t(1) << 31);
+  if (xs_extent < 0) xs_extent = M * w.Kb;
+  bool fits = M * ldq < (int64_t(1) << 31) && xs_extent * 4 < (int64_t(1) << 31);
   for (int i = 0; i < w.n_members; ++i) fits = fits && int64_t(w.m[i].rows) * w.K < (int64_t(1) << 31);
   p.fast = aligned && fits && w.Kb <= F_MAX_KB;
   if (p.fast) {
@@ -932,8 +940,8 @@ namespace {
 
 // Fast-kernel launch (and the split-K reduction when the plan splits).
 bsf8_status launch_fast(const Plan& p, const WeightDev& w, bool dense, const uint8_t* xq, int64_t ldq,
-                        const float* xs, int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+                        const float* xs, int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
   FastArgs a{};
   a.w = w;
   for (int i = 0; i <= kMaxMembers; ++i) a.rt0[i] = p.rt0[i];
@@ -941,7 +949,8 @@ bsf8_status launch_fast(const Plan& p, const WeightDev& w, bool dense, const uin
   a.xs = xs;
   a.y = y;
   a.ldq = ldq;
-  a.ldxs = ldxs;
+  a.xs_sm = xs_sm;
+  a.xs_sk = xs_sk;
   a.ldy = ldy;
   a.M = int32_t(M);
   a.m_tiles = p.m_tiles;
@@ -1045,16 +1054,16 @@ bsf8_status launch_dense(const uint16_t* wd, int64_t N, int64_t K, const uint16_
     return BSF8_E_UNSUPPORTED;
   }
   if (p.blocks == 0) return BSF8_OK;
-  return launch_fast(p, w, true, reinterpret_cast<const uint8_t*>(x), 2 * ldx, nullptr, 0, M, y, y_bf16, ldy, ws,
-                     ws_bytes, stream);
+  return launch_fast(p, w, true, reinterpret_cast<const uint8_t*>(x), 2 * ldx, nullptr, 0, 0, M, y, y_bf16, ldy,
+                     ws, ws_bytes, stream);
 }
 
 bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,
-                        int64_t ldxs, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
-  const Plan p = make_plan(w, aligned, M, ldq);
+                        int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  const Plan p = make_plan(w, aligned, M, ldq, (M - 1) * xs_sm + (w.Kb - 1) * xs_sk + 1);
   if (p.blocks == 0) return BSF8_OK;
-  if (p.fast) return launch_fast(p, w, false, xq, ldq, xs, ldxs, M, y, y_bf16, ldy, ws, ws_bytes, stream);
+  if (p.fast) return launch_fast(p, w, false, xq, ldq, xs, xs_sm, xs_sk, M, y, y_bf16, ldy, ws, ws_bytes, stream);
   GemmArgs a{};
   a.w = w;
   a.tm = p.tm;
@@ -1062,7 +1071,8 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
   a.xs = xs;
   a.y = y;
   a.ldq = ldq;
-  a.ldxs = ldxs;
+  a.xs_sm = xs_sm;
+  a.xs_sk = xs_sk;
   a.ldy = ldy;
   a.M = int32_t(M);
   a.m_tiles = p.m_tiles;

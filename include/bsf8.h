@@ -35,7 +35,8 @@
  *   - Errors are returned as bsf8_status; nothing is thrown across the ABI.
  *     bsf8_last_error() gives a thread-local sentence for the last failure.
  *   - Element layouts are row-major with a leading dimension counted in
- *     elements (ldx, ldq, ldxs, ldy).
+ *     elements (ldx, ldq, ldy), except the activation scales, which take two
+ *     strides (see BSF8 activation scale layout below).
  *   - M == 0 is a successful no-op for every compute call.
  */
 #ifndef BSF8_H
@@ -190,6 +191,22 @@ bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* memb
                                   int64_t* local_row, int64_t* stacked_row);
 
 /*
+ * BSF8 activation scale layout.  The per-token group scales xs are a logical
+ * [M, ceil(K/128)] F32 array whose element (m, kb) sits at
+ * xs[m * xs_sm + kb * xs_sk] (strides in elements).  Two layouts are accepted:
+ *   token-major: xs_sk == 1 and xs_sm >= ceil(K/128)  (row m = token m's scales,
+ *                the layout of the pages' quantizer);
+ *   K-major:     xs_sm == 1 and xs_sk >= M            (row kb = every token's
+ *                scale of block kb, token index contiguous, the layout the
+ *                pages transpose to for their cuBLASLt path: "Module
+ *                w8a8_prefill", section "Reachability").
+ * (When M == 1 or ceil(K/128) == 1 either test may hold.)  Any other pair is
+ * INVALID_ARG.  The W8A8 product reads a K block's 256 token scales at a time:
+ * K-major makes that one contiguous kilobyte, token-major 256 separate words,
+ * so K-major is the faster input; results are identical.
+ */
+
+/*
  * bsf8_quant_act -- per-token 1x128 group quantization of activations.
  * ("Module w8a8_prefill", section "WHY (#917 / #928)": per-token FP32 scales
  *  over 1x128 groups; "FP8 Native Serving", section "FP8 E4M3: range and
@@ -197,26 +214,27 @@ bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* memb
  *
  * x   : [M, K] with leading dimension ldx (elements), dtype F32 or BF16.
  * xq  : [M, K] E4M3 bytes out, leading dimension ldq (bytes).
- * xs  : [M, ceil(K/128)] F32 scales out, leading dimension ldxs (elements),
- *       token-major (row m holds token m's group scales).
+ * xs  : [M, ceil(K/128)] F32 scales out, strides xs_sm, xs_sk (elements; the
+ *       activation scale layout above).
  * For token m and group g (channels 128g .. min(128g+128, K) - 1):
  *   amax = max |x|;  s = amax' / 448 with amax' = max(amax, 1e-10f) (IEEE F32);
  *   q = round-to-nearest-even E4M3 of clamp(x / s, -448, 448) (IEEE F32
  *   division), sign of zero kept.  xs holds s, the dequantization multiplier.
  * Results are bit-exact: one byte pattern and one scale per input.
  * Non-finite inputs are outside the defined domain.
- * Errors: INVALID_ARG (null, negative, ld < K, ldxs < ceil(K/128), bad dtype),
- *         DEVICE.
+ * Errors: INVALID_ARG (null, negative, ld < K, a scale layout other than the
+ *         two above, bad dtype), DEVICE.
  */
 bsf8_status bsf8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
-                           uint8_t* xq, int64_t ldq, float* xs, int64_t ldxs, void* stream);
+                           uint8_t* xq, int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, void* stream);
 
 /*
  * bsf8_quant_glu -- the step between the dense FFN's gate/up GEMM and its down
  * GEMM: y [M, >= 2F] (leading dimension ldy, F32 or BF16) holds the gate
  * outputs in columns [0, F) and the up outputs in [F, 2F) (a gate/up weight
  * grouped as gate then up gives exactly this); the call writes the down GEMM's
- * quantized input, xq [M, F] and xs [M, ceil(F/128)], as bsf8_quant_act would
+ * quantized input, xq [M, F] and xs [M, ceil(F/128)] (strides xs_sm, xs_sk),
+ * as bsf8_quant_act would
  * for h = silu(gate) * up, without writing h.
  * ("Module w8a8_prefill", preamble and section "WHY (#917 / #928)": the
  *  gate/up/down prefill arm; the down GEMM consumes per-token 1x128 E4M3
@@ -226,11 +244,11 @@ bsf8_status bsf8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K,
  *   e = exp(-|g|) evaluated in F64 and rounded to F32;  t = 1 + e;
  *   q = g / t (g >= 0) or (g * e) / t (g < 0);  h = q * u,
  * each an IEEE F32 operation; then quantized exactly as bsf8_quant_act does.
- * Errors: INVALID_ARG (null, negative, ldy < 2F, ldq < F, ldxs < ceil(F/128),
- * bad dtype), ALIGNMENT (y not element aligned), DEVICE.
+ * Errors: INVALID_ARG (null, negative, ldy < 2F, ldq < F, a scale layout other
+ * than the two accepted, bad dtype), ALIGNMENT (y not element aligned), DEVICE.
  */
 bsf8_status bsf8_quant_glu(const void* y, int32_t y_dtype, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
-                           int64_t ldq, float* xs, int64_t ldxs, void* stream);
+                           int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, void* stream);
 
 /*
  * bsf8_workspace_size -- device workspace bytes a compute call of this handle
@@ -277,13 +295,14 @@ bsf8_status bsf8_linear_w8a16(const bsf8_weight* w, const void* x, int32_t x_dty
  *  section "Native FP8 vs dequant-to-BF16": FP8 operands through the matrix
  *  unit, BF16 only when results are written back.)
  *
- * xq, xs: exactly what bsf8_quant_act writes (ldq bytes, ldxs elements).
+ * xq, xs: exactly what bsf8_quant_act writes (ldq bytes; xs in either
+ *         activation scale layout, strides xs_sm, xs_sk).
  * y : [M, N] BF16 or F32, leading dimension ldy (elements).
  * workspace: as for bsf8_linear_w8a16 with arm W8A8.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE.
  */
 bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs,
-                             int64_t ldxs, int64_t M, void* y, int32_t y_dtype, int64_t ldy,
+                             int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, int32_t y_dtype, int64_t ldy,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -125,18 +125,27 @@ def test_compute_calls_refuse_bad_arguments_without_launching():
         fake = ctypes.c_void_p(1 << 40)
         # M == 0: success, nothing launched
         assert L.bsf8_linear_w8a16(h, fake, B.DT_F32, 0, 256, fake, B.DT_F32, 128, None, 0, None) == 0
-        assert L.bsf8_linear_w8a8(h, fake, 256, fake, 2, 0, fake, B.DT_BF16, 128, None, 0, None) == 0
-        assert L.bsf8_quant_act(fake, B.DT_F32, 0, 256, 256, fake, 256, fake, 2, None) == 0
+        assert L.bsf8_linear_w8a8(h, fake, 256, fake, 2, 1, 0, fake, B.DT_BF16, 128, None, 0, None) == 0
+        assert L.bsf8_quant_act(fake, B.DT_F32, 0, 256, 256, fake, 256, fake, 2, 1, None) == 0
         # refusals
         assert B.status_name(L.bsf8_linear_w8a16(h, fake, B.DT_F32, -1, 256, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
         assert B.status_name(L.bsf8_linear_w8a16(h, fake, B.DT_F16, 4, 256, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
         assert B.status_name(L.bsf8_linear_w8a16(h, fake, B.DT_F32, 4, 255, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
-        assert B.status_name(L.bsf8_linear_w8a8(h, fake, 256, fake, 1, 4, fake, B.DT_BF16, 128, None, 0, None)) == "INVALID_ARG"
-        assert B.status_name(L.bsf8_linear_w8a8(h, None, 256, fake, 2, 4, fake, B.DT_BF16, 128, None, 0, None)) == "INVALID_ARG"
-        assert B.status_name(L.bsf8_quant_act(fake, B.DT_F32, 4, 256, 100, fake, 256, fake, 2, None)) == "INVALID_ARG"
-        assert B.status_name(L.bsf8_quant_act(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 4, 256, 256, fake, 256, fake, 2, None)) == "ALIGNMENT"
+        assert B.status_name(L.bsf8_linear_w8a8(h, fake, 256, fake, 1, 1, 4, fake, B.DT_BF16, 128, None, 0, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_linear_w8a8(h, None, 256, fake, 2, 1, 4, fake, B.DT_BF16, 128, None, 0, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_quant_act(fake, B.DT_F32, 4, 256, 100, fake, 256, fake, 2, 1, None)) == "INVALID_ARG"
+        assert B.status_name(L.bsf8_quant_act(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 4, 256, 256, fake, 256, fake, 2, 1, None)) == "ALIGNMENT"
         assert B.status_name(L.bsf8_linear_w8a16(None, fake, B.DT_F32, 4, 256, fake, B.DT_F32, 128, None, 0, None)) == "INVALID_ARG"
         assert "INVALID_ARG" in L.bsf8_last_error().decode()
+        # activation scale layouts: only token-major (sk = 1, sm >= Kb) and K-major (sm = 1, sk >= M)
+        for sm, sk in ((3, 2), (1, 3), (2, 0), (0, 1), (-2, 1)):
+            assert B.status_name(L.bsf8_linear_w8a8(h, fake, 256, fake, sm, sk, 4, fake, B.DT_BF16, 128, None, 0,
+                                                    None)) == "INVALID_ARG", (sm, sk)
+            assert B.status_name(L.bsf8_quant_act(fake, B.DT_F32, 4, 256, 256, fake, 256, fake, sm, sk,
+                                                  None)) == "INVALID_ARG", (sm, sk)
+            assert B.status_name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 256, 512, fake, 256, fake, sm, sk,
+                                                  None)) == "INVALID_ARG", (sm, sk)
+        assert "neither token-major nor K-major" in L.bsf8_last_error().decode()
     finally:
         L.bsf8_weight_destroy(h)
 
@@ -211,13 +220,13 @@ def test_quant_glu_refuses_bad_arguments_without_launching():
     L = B.lib()
     fake = ctypes.c_void_p(1 << 40)
     name = lambda s: B.status_name(s)
-    assert L.bsf8_quant_glu(fake, B.DT_BF16, 0, 256, 512, fake, 256, fake, 2, None) == 0
-    assert L.bsf8_quant_glu(fake, B.DT_BF16, 4, 0, 512, fake, 256, fake, 2, None) == 0
-    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, -1, 256, 512, fake, 256, fake, 2, None)) == "INVALID_ARG"
-    assert name(L.bsf8_quant_glu(fake, B.DT_F16, 4, 256, 512, fake, 256, fake, 2, None)) == "INVALID_ARG"
-    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 256, 511, fake, 256, fake, 2, None)) == "INVALID_ARG"
-    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 256, 512, fake, 255, fake, 2, None)) == "INVALID_ARG"
-    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 257, 514, fake, 257, fake, 2, None)) == "INVALID_ARG"
-    assert name(L.bsf8_quant_glu(None, B.DT_BF16, 4, 256, 512, fake, 256, fake, 2, None)) == "INVALID_ARG"
-    assert name(L.bsf8_quant_glu(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 4, 256, 512, fake, 256, fake, 2,
+    assert L.bsf8_quant_glu(fake, B.DT_BF16, 0, 256, 512, fake, 256, fake, 2, 1, None) == 0
+    assert L.bsf8_quant_glu(fake, B.DT_BF16, 4, 0, 512, fake, 256, fake, 2, 1, None) == 0
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, -1, 256, 512, fake, 256, fake, 2, 1, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_F16, 4, 256, 512, fake, 256, fake, 2, 1, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 256, 511, fake, 256, fake, 2, 1, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 256, 512, fake, 255, fake, 2, 1, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(fake, B.DT_BF16, 4, 257, 514, fake, 257, fake, 2, 1, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(None, B.DT_BF16, 4, 256, 512, fake, 256, fake, 2, 1, None)) == "INVALID_ARG"
+    assert name(L.bsf8_quant_glu(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 4, 256, 512, fake, 256, fake, 2, 1,
                                  None)) == "ALIGNMENT"

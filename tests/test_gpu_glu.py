@@ -61,7 +61,7 @@ def _call_strided(yd, F, xq, xs):
     M = yd.shape[0]
     Fb = -(-F // 128)
     st = L.bsf8_quant_glu(yd.data_ptr(), B._dt_of(yd), M, F, yd.stride(0), xq.data_ptr(), xq.stride(0),
-                          xs.data_ptr(), xs.stride(0), B._stream_ptr(yd.device))
+                          xs.data_ptr(), xs.stride(0), xs.stride(1), B._stream_ptr(yd.device))
     assert st == 0, B.status_name(st)
 
 

@@ -189,6 +189,29 @@ def test_quant_act_bf16_input_and_strides():
     assert np.all(xq[:, 520:].cpu().numpy() == 0xAB) and np.all(xs[:, 5:].cpu().numpy() == -1.0)
 
 
+def test_quant_act_scale_layouts():
+    """Token-major and K-major scale outputs ("Module w8a8_prefill", section "Reachability":
+    the per-token scales and their token-contiguous transpose), each with row padding that
+    must stay untouched: the same bits in both, bit-exact against the oracle."""
+    t = torch()
+    M, K = 37, 1000
+    Kb = -(-K // 128)
+    x = synth.gaussian_activations(109, "layout_X", M, K)
+    xd = t.from_numpy(x).to(device())
+    q_ref, s_ref = O.quant_act(x)
+    tm = t.full((M, Kb + 3), -1.0, dtype=t.float32, device=device())           # token-major, pitch Kb + 3
+    km = t.full((Kb, M + 5), -1.0, dtype=t.float32, device=device())           # K-major, pitch M + 5
+    banner("quant_act scale layouts")
+    xq1, _ = B.quant_act(xd, xs=tm[:, :Kb])
+    xq2, _ = B.quant_act(xd, xs=km[:, :M].t())
+    assert np.array_equal(xq1.cpu().numpy(), q_ref) and np.array_equal(xq2.cpu().numpy(), q_ref)
+    assert np.array_equal(tm[:, :Kb].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(km[:, :M].cpu().numpy().T.view(np.uint32), s_ref.view(np.uint32))
+    assert np.all(tm[:, Kb:].cpu().numpy() == -1.0) and np.all(km[:, M:].cpu().numpy() == -1.0)
+    xq3, xs3 = B.quant_act(xd)                                                  # the binding's default: K-major
+    assert xs3.stride() == (1, M) and np.array_equal(xs3.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
 # ------------------------------------------------------------- GEMM parity
 
 @pytest.mark.parametrize("name", TAX)
@@ -636,3 +659,41 @@ def test_w8a8_kernel_variants_agree(name):
             if not split:
                 assert np.array_equal(y_fast, y_staged)
         assert_within(y_staged, O.linear_w8a8(xq, xs, om), S, odt == t.bfloat16, f"{name} register-staged")
+
+
+SCALE_LAYOUT_CASES = {
+    # name: (member rows, K, M)
+    "n512_k1024_m600": ((512,), 1024, 600),
+    "split_k_n512_k8192_m64": ((512,), 8192, 64),
+    "grouped_100_28_130_k300_m9": ((100, 28, 130), 300, 9),     # ragged K: the register-staged kernel
+}
+
+
+@pytest.mark.parametrize("name", list(SCALE_LAYOUT_CASES))
+def test_w8a8_scale_layouts_give_identical_outputs(name):
+    """One quantized activation with its scales token-major (padded rows) and K-major (padded
+    rows), through the direct-copy kernel and through the register-staged one (code pitch
+    K + 8): per kernel, the two layouts give bit-identical outputs, within the oracle's
+    bound.  (The two kernels may differ in the last bit where the direct-copy plan splits K.)"""
+    t = torch()
+    rows, K, M = SCALE_LAYOUT_CASES[name]
+    Kb = -(-K // 128)
+    ms = [synth.random_code_weight(193, f"lay_W{i}_{name}", r, K) for i, r in enumerate(rows)]
+    w, _keep = weight_on_device(ms)
+    x = synth.gaussian_activations(193, f"lay_X_{name}", M, K)
+    xq, xs = O.quant_act(x)
+    xqd = t.from_numpy(xq).to(device())
+    tm = t.full((M, Kb + 2), 3.0, dtype=t.float32, device=device())
+    tm[:, :Kb] = t.from_numpy(xs).to(device())
+    km = t.full((Kb, M + 7), 3.0, dtype=t.float32, device=device())
+    km[:, :M] = t.from_numpy(np.ascontiguousarray(xs.T)).to(device())
+    pitched = t.zeros((M, K + 8), dtype=t.uint8, device=device())
+    pitched[:, :K] = xqd
+    banner(f"w8a8 scale layouts {name}: {w.describe(B.ARM_W8A8, M)}")
+    om = oracle_members(ms)
+    ref, bound = O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om)
+    for codes, kernel in ((xqd, "direct-copy"), (pitched[:, :K], "register-staged")):
+        y_tm = to_np(B.linear_w8a8(w, codes, tm[:, :Kb], out_dtype=t.float32))
+        y_km = to_np(B.linear_w8a8(w, codes, km[:, :M].t(), out_dtype=t.float32))
+        assert np.array_equal(y_km.view(np.uint32), y_tm.view(np.uint32)), kernel
+        assert_within(y_km, ref, bound, False, f"{name} {kernel}")
