@@ -201,9 +201,9 @@ def bench_prefill(torch, B, synth, steps, warmup, dev):
     y_gu = torch.empty((M, w_gu.n_total), dtype=torch.bfloat16, device=dev)
     y_dn = torch.empty((M, w_dn.n_total), dtype=torch.bfloat16, device=dev)
     xq_gu = torch.empty((M, w_gu.K), dtype=torch.uint8, device=dev)
-    xs_gu = torch.empty((M, -(-w_gu.K // 128)), dtype=torch.float32, device=dev)
+    xs_gu = B.scales_kmajor(M, -(-w_gu.K // 128), dev)   # [M, Kb] views, token index contiguous
     xq_dn = torch.empty((M, w_dn.K), dtype=torch.uint8, device=dev)
-    xs_dn = torch.empty((M, -(-w_dn.K // 128)), dtype=torch.float32, device=dev)
+    xs_dn = B.scales_kmajor(M, -(-w_dn.K // 128), dev)
     ws_gu = w_gu.workspace(B.ARM_W8A8, M)
     ws_dn = w_dn.workspace(B.ARM_W8A8, M)
     calls = {
@@ -587,7 +587,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense_ffn_prefill: quant + W8A8 gate/up [2x17408,5120] + quant + W8A8 down "
                                "[5120,17408], M=1024 tokens, bf16 out",
-                   "M": pre["M"], "global_batch": pre["M"], "parallelism": "single_gpu"},
+                   "M": pre["M"], "global_batch": pre["M"], "parallelism": "single_gpu",
+                   "act_scale_layout": "K-major (token index contiguous)"},
         "roofline": {"bound": "mfma", "kernel": "w8a8_gemm (gate/up)", "achieved": round(achieved, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "traffic": profiled_traffic("w8a8_gemm_gate_up_m1024")},
