@@ -99,6 +99,7 @@ struct Args {
   int32_t chunks_per_wave;
   int32_t x_bf16;
   int32_t y_bf16;
+  int32_t rows_per_block;   // few-token VALU kernels: rows of a block (at most 8 G)
 };
 
 template <bool SBF16>
@@ -632,8 +633,9 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 // (16 bytes each, full lines), decoded exactly to F32 in registers
 // (v_cvt_scalef32_pk_f32_fp8, unit scale) and multiplied by the 16
 // activations that lane holds for that chunk, so there is no LDS traffic until
-// the final reduction.  A block owns G groups of 8 rows of one member (G is
-// chosen so that the grid is about one block per compute unit) and all of K;
+// the final reduction.  A block owns rb consecutive rows of one member, taken
+// as G groups of 8 (the last group partly masked when rb < 8 G; rb is chosen
+// so that the grid is about one block per compute unit), and all of K;
 // its 8 waves split K into contiguous chunk ranges and every load of a wave is
 // issued before any arithmetic.  The chunk partial of each row is scaled by
 // its block scale (a block's rows span at most two rows of the grid, each
@@ -656,7 +658,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jp = lane & 7;    // 16-byte piece of a 128-byte chunk
   const int rl = lane >> 3;   // row within an 8-row group
-  const int row0 = rtile * G * 8;
+  const int row0 = rtile * a.rows_per_block;
+  const int rend = min(mem.rows, row0 + a.rows_per_block);   // rows from rend on: masked lanes
   const int c_begin = min(Kb, wave * CPW);
   const int c_end = min(Kb, c_begin + CPW);
 
@@ -701,7 +704,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int r = row0 + 8 * g + rl;
-      const uint32_t off = live && r < mem.rows ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
+      const uint32_t off = live && r < rend ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
       wv[c][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, 0));
     }
 #pragma unroll
@@ -770,7 +773,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += red[w][tid];
     const int row = row0 + tid;
-    if (row < mem.rows) {
+    if (row < rend) {
       const int64_t off = mem.col0 + row;
       if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
       else static_cast<float*>(a.y)[off] = sum;
@@ -807,7 +810,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jp = lane & 7;
   const int rl = lane >> 3;
-  const int row0 = rtile * G * 8;
+  const int row0 = rtile * a.rows_per_block;
+  const int rend = min(mem.rows, row0 + a.rows_per_block);
   const int c_begin = min(Kb, wave * CPW);
   const int c_end = min(Kb, c_begin + CPW);
   const int k_end = min(K, c_end * CHUNK);
@@ -862,7 +866,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int r = row0 + 8 * g + rl;
-      const uint32_t off = live && r < mem.rows ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
+      const uint32_t off = live && r < rend ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
       wv[c][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, 0));
     }
   }
@@ -957,7 +961,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += xl[w * XS + i];
     const int row = row0 + rr;
-    if (t < a.M && row < mem.rows) {
+    if (t < a.M && row < rend) {
       const int64_t off = int64_t(t) * a.ldy + mem.col0 + row;
       if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
       else static_cast<float*>(a.y)[off] = sum;
@@ -985,10 +989,12 @@ int w16_device_cus() {
   return cache[dev];
 }
 
-// The one-token kernel's shape: 8-row groups per block (about one block per
-// compute unit) and chunks per wave; g = 0 when it does not apply.
+// The few-token VALU kernels' shape: rows per block (rb, at most one block per
+// compute unit when 32 rows allow it), 8-row groups per block (g = ceil(rb / 8))
+// and chunks per wave; g = 0 when they do not apply.
 struct M1Shape {
   int g;
+  int rb;
   int cpw;
   TileMap tm;
   int tiles;
@@ -1000,14 +1006,34 @@ M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
   // kernel's transpose: 15.4 against 15.0 us for 8 tokens of W [5120,5120])
   if (!aligned || M < 1 || M > 4 || w.Kb > WAVES * 5) return m;
   m.cpw = M == 1 && w.Kb <= WAVES * 4 ? 4 : 5;
-  int64_t groups = 0;
-  for (int i = 0; i < w.n_members; ++i) groups += (w.m[i].rows + 7) / 8;
+  // One token: the fewest rows in [16, 32] that keep the grid within one
+  // block per compute unit, so every unit streams about the same bytes
+  // (W [5120, 5120]: 20 rows, 256 blocks, 9.3 -> 8.8 us; whole 8-row groups
+  // would give 24 rows and 214 blocks); the last group of a block may be
+  // partly masked.  Two to four tokens: whole groups, about one block per
+  // unit (there the masked lanes' FMAs and the extra blocks' activation
+  // staging cost more than the balance gains: 10.8 -> 11.2 us at M = 2).
   const int cus = w16_device_cus();
-  m.g = int(std::min<int64_t>(M1_MAX_G, std::max<int64_t>(2, (groups + cus - 1) / cus)));
+  if (M == 1) {
+    m.rb = 8 * M1_MAX_G;
+    for (int rb = 16; rb < 8 * M1_MAX_G; ++rb) {
+      int64_t n = 0;
+      for (int i = 0; i < w.n_members; ++i) n += (w.m[i].rows + rb - 1) / rb;
+      if (n <= cus) {
+        m.rb = rb;
+        break;
+      }
+    }
+  } else {
+    int64_t groups = 0;
+    for (int i = 0; i < w.n_members; ++i) groups += (w.m[i].rows + 7) / 8;
+    m.rb = 8 * int(std::min<int64_t>(M1_MAX_G, std::max<int64_t>(2, (groups + cus - 1) / cus)));
+  }
+  m.g = (m.rb + 7) / 8;
   int t = 0;
   for (int i = 0; i < w.n_members; ++i) {
     m.tm.tile0[i] = t;
-    m.tm.n_tiles[i] = (w.m[i].rows + 8 * m.g - 1) / (8 * m.g);
+    m.tm.n_tiles[i] = (w.m[i].rows + m.rb - 1) / m.rb;
     t += m.tm.n_tiles[i];
   }
   m.tm.tile0[w.n_members] = t;
@@ -1047,7 +1073,7 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
              "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), f32 fma accumulate | "
              "kernel=%s rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all loads first, "
              "8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
-             M <= 1 ? "w8a16_m1" : "w8a16_mt", 8 * m1.g, m1.g, WAVES, m1.cpw,
+             M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
              M <= 1 ? "" : ", 4-token activation slices in LDS",
              (long long)(M > 0 ? M : 1), m1.tiles);
     return b1;
@@ -1093,6 +1119,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     a.M = int32_t(M);
     a.col_tiles = 1;
     a.chunks_per_wave = m1.cpw;
+    a.rows_per_block = m1.rb;
     a.x_bf16 = x_bf16 ? 1 : 0;
     a.y_bf16 = y_bf16 ? 1 : 0;
     const bool sb = w.scale_bf16 != 0;

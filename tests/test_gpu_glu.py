@@ -101,3 +101,25 @@ def test_quant_glu_tails(dtype):
     g[5, ::2] = np.float32(3.0)
     u[5, ::2] = np.float32(2.0)                                        # half the channels zero
     _run(y, F, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quant_glu_kmajor_scales_padded(dtype):
+    """K-major scale output (token index contiguous) with a row pitch of M + 5: the same
+    bits as the oracle's token-major scales, the padding untouched."""
+    t = torch()
+    M, F = 11, 640
+    Fb = F // 128
+    y_np = _gate_up(167, M, F)
+    if dtype == "bf16":
+        y_np = O.f32_to_bf16(y_np)
+        yd = t.from_numpy(O.f32_to_bf16_bits(y_np).view(np.int16)).to(device()).view(t.bfloat16)
+    else:
+        yd = t.from_numpy(y_np).to(device())
+    km = t.full((Fb, M + 5), -1.0, dtype=t.float32, device=device())
+    banner(f"quant_glu K-major scales {dtype}")
+    xq, _ = B.quant_glu(yd, xs=km[:, :M].t())
+    q_ref, s_ref = O.glu_quant(y_np, F)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(km[:, :M].cpu().numpy().T.view(np.uint32), s_ref.view(np.uint32))
+    assert np.all(km[:, M:].cpu().numpy() == -1.0)

@@ -406,6 +406,7 @@ FULL = {
     "decode_5120x5120_m4": lambda: synth.config2(4),
     "decode_5120x5120_m8": lambda: synth.config2(8),
     "decode_5000x4000_m8": lambda: synth.config2(8, shape=(5000, 4000)),
+    "decode_5000x4000_m1": lambda: synth.config2(1, shape=(5000, 4000)),
     "ffn_gate_up_m1024": synth.config3_gate_up,
     "ffn_down_m1024": synth.config3_down,
     "qkv_m1": lambda: synth.config4(1),
@@ -414,6 +415,7 @@ FULL = {
 }
 ARMS = {"decode_5120x5120_m1": ("w8a16", "w8a8"), "decode_5120x5120_m4": ("w8a16",),
         "decode_5120x5120_m8": ("w8a16", "w8a8"), "decode_5000x4000_m8": ("w8a16", "w8a8"),
+        "decode_5000x4000_m1": ("w8a16",),
         "ffn_gate_up_m1024": ("w8a8",), "ffn_down_m1024": ("w8a8",), "qkv_m1": ("w8a16", "w8a8"),
         "qkv_m512": ("w8a16", "w8a8"), "large_prefill_m8192": ("w8a8",)}
 
@@ -697,3 +699,31 @@ def test_w8a8_scale_layouts_give_identical_outputs(name):
         y_km = to_np(B.linear_w8a8(w, codes, km[:, :M].t(), out_dtype=t.float32))
         assert np.array_equal(y_km.view(np.uint32), y_tm.view(np.uint32)), kernel
         assert_within(y_km, ref, bound, False, f"{name} {kernel}")
+
+
+@pytest.mark.parametrize("sdt", ["bf16", "f32"])
+def test_w8a16_one_token_blocks_of_odd_row_counts(sdt):
+    """One token on grouped members of 4100 and 700 rows (K = 1024): the one-token kernel
+    balances the grid with 19-row blocks, so blocks start at any row, straddle 128-row scale
+    blocks and leave part of their last 8-row group masked.  Every output against the oracle."""
+    t = torch()
+    g = np.random.default_rng(197)
+    K = 1024
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    om = []
+    for r in (4100, 700):
+        codes = finite[g.integers(0, finite.size, (r, K))]
+        sc = np.exp2(g.uniform(-10, -3, O.scale_grid_shape(r, K))).astype(np.float32)
+        if sdt == "bf16":
+            sc = O.f32_to_bf16(sc)
+        om.append((codes, sc))
+    dt = t.float32 if sdt == "f32" else t.bfloat16
+    w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.from_numpy(np.asarray(s, np.float32)).to(device()).to(dt))
+                          for c, s in om])
+    d = w.describe(B.ARM_W8A16, 1)
+    banner(f"w8a16 one token, odd rows per block: {d}")
+    if t.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert "kernel=w8a16_m1 rows=19 " in d, d
+    x = synth.gaussian_activations(197, "odd_rows_X", 1, K)
+    y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
+    assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"odd rows {sdt}")
