@@ -430,7 +430,15 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   const int l16 = lane & 15, gq = lane >> 4;
   const int c_begin = min(Kb, wave * a.chunks_per_wave);
   const int c_end = min(Kb, c_begin + a.chunks_per_wave);
-  const int64_t srow0 = int64_t((rtile * ROWS) >> 7) * a.w.s_rs;   // both row tiles share one scale row
+  // the block's rows: [row0, rend), at most 32, in two 16-row MFMA tiles (rows
+  // past rend masked); they use at most two rows of the scale grid, the second
+  // from row `split` on
+  const int row0 = rtile * a.rows_per_block;
+  const int rend = min(mem.rows, row0 + a.rows_per_block);
+  const int srow = row0 >> 7;
+  const int split = (srow + 1) << 7;
+  const int64_t soff0 = int64_t(srow) * a.w.s_rs;
+  const int64_t soff1 = int64_t(min(srow + 1, ((mem.rows + 127) >> 7) - 1)) * a.w.s_rs;
 
   uint8_t* sc = scratch[wave];
   for (int i = lane; i < NT * SM_TERM_BYTES / 16; i += 64) reinterpret_cast<uint4*>(sc)[i] = make_uint4(0, 0, 0, 0);
@@ -474,22 +482,32 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   // The weight scales of this wave's chunks, one per lane (chunk c_begin +
   // 64 h + lane), loaded first: as the oldest loads, waiting for them never
   // waits for a ring slot.  Raw bits; converted where used.
-  uint32_t sraw[SM_SCALE_REGS];
+  uint32_t sraw[2][SM_SCALE_REGS];
 #pragma unroll
   for (int h = 0; h < SM_SCALE_REGS; ++h) {
     const int c = c_begin + 64 * h + lane;
-    const int so = c < c_end ? int((srow0 + int64_t(c) * a.w.s_cs) * s_esz) : int(s_bytes);
-    sraw[h] = SBF16 ? uint32_t(uint16_t(bsf8_raw_buffer_load_b16(rs, so, 0, 0)))
-                    : uint32_t(bsf8_raw_buffer_load_b32(rs, so, 0, 0));
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int so = c < c_end ? int(((v ? soff1 : soff0) + int64_t(c) * a.w.s_cs) * s_esz) : int(s_bytes);
+      sraw[v][h] = SBF16 ? uint32_t(uint16_t(bsf8_raw_buffer_load_b16(rs, so, 0, 0)))
+                         : uint32_t(bsf8_raw_buffer_load_b32(rs, so, 0, 0));
+    }
   }
-  auto chunk_scale = [&](int c) {   // c - c_begin is wave-uniform
+  auto chunk_scale = [&](int c, int v) {   // c - c_begin is wave-uniform
     const int i = c - c_begin;
     uint32_t bits = 0;
 #pragma unroll
     for (int h = 0; h < SM_SCALE_REGS; ++h)
-      if ((i >> 6) == h) bits = __builtin_amdgcn_readlane(sraw[h], i & 63);
+      if ((i >> 6) == h) bits = __builtin_amdgcn_readlane(sraw[v][h], i & 63);
     return c < c_end ? __uint_as_float(SBF16 ? bits << 16 : bits) : 0.f;
   };
+  // which of this lane's accumulator rows (16 t + 4 gq + e) use the second grid row
+  uint32_t hi_rows = 0;
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (row0 + 16 * t + 4 * gq + e >= split) hi_rows |= 1u << (4 * t + e);
 
   auto issue = [&](int c, int d) {
     const bool live = c < c_end;
@@ -502,9 +520,9 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
     }
 #pragma unroll
     for (int q = 0; q < 2 * RT; ++q) {
-      const int row = rtile * ROWS + 8 * q + crow;
+      const int row = row0 + 8 * q + crow;
       const int k = c * CHUNK + 16 * cpiece;
-      const bool ok = live && row < mem.rows && k < K;
+      const bool ok = live && row < rend && k < K;
       wr[d][q] = as_u4(bsf8_raw_buffer_load_b128(rw, ok ? row * K + k : int(w_bytes), 0, 0));
     }
   };
@@ -518,7 +536,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 #pragma unroll
     for (int d = 0; d < SM_DEPTH; ++d) {
       const int c = c0 + d;
-      const float sw = chunk_scale(c);
+      const float sw0 = chunk_scale(c, 0), sw1 = chunk_scale(c, 1);
       // split this lane's activations and write the terms in fragment order
 #pragma unroll
       for (int i = 0; i < NXI; ++i) {
@@ -577,7 +595,12 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 #pragma unroll
           for (int p = 0; p < NP; ++p) pt[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[st], b[p][st], pt[p], 0, 0, 0);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) acc[t][p] += pt[p] * sw;
+        for (int p = 0; p < NP; ++p) {
+          v4f s4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s4[e] = (hi_rows >> (4 * t + e)) & 1u ? sw1 : sw0;
+          acc[t][p] += pt[p] * s4;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       issue(c + SM_DEPTH, d);   // refill this slot
@@ -615,8 +638,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
     float sum = part[NT - 1];
 #pragma unroll
     for (int u = NT - 2; u >= 0; --u) sum += part[u];
-    const int row = rtile * ROWS + rr;
-    if (row < mem.rows) {
+    const int row = row0 + rr;
+    if (row < rend) {
       const int64_t off = int64_t(tok) * a.ldy + mem.col0 + row;
       if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
       else static_cast<float*>(a.y)[off] = sum;
@@ -1041,6 +1064,38 @@ M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
   return m;
 }
 
+// The few-token MFMA kernel's rows per block: the fewest in [16, 32] that keep
+// the grid within one block per compute unit (W [5120, 5120]: 20 rows, 256
+// blocks, where 32-row blocks leave 96 units idle), else 32.
+struct SmallShape {
+  int rb;
+  TileMap tm;
+  int tiles;
+};
+
+SmallShape small_shape(const WeightDev& w) {
+  SmallShape sh{};
+  const int cus = w16_device_cus();
+  sh.rb = ROWS;
+  for (int rb = 16; rb < ROWS; ++rb) {
+    int64_t n = 0;
+    for (int i = 0; i < w.n_members; ++i) n += (w.m[i].rows + rb - 1) / rb;
+    if (n <= cus) {
+      sh.rb = rb;
+      break;
+    }
+  }
+  int t = 0;
+  for (int i = 0; i < w.n_members; ++i) {
+    sh.tm.tile0[i] = t;
+    sh.tm.n_tiles[i] = (w.m[i].rows + sh.rb - 1) / sh.rb;
+    t += sh.tm.n_tiles[i];
+  }
+  sh.tm.tile0[w.n_members] = t;
+  sh.tiles = t;
+  return sh;
+}
+
 Plan make_plan(const WeightDev& w, int64_t M) {
   Plan p{};
   p.col_tiles = int((M + COLS - 1) / COLS);
@@ -1090,8 +1145,9 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
            "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
            "mfma_f32_16x16x32_bf16 | kernel=%s rows=%d tokens=%d waves=%d (in-block split-K, %d chunks/wave%s) "
            "path=%s | M=%lld blocks=%d",
-           small ? "w8a16_small_m" : "w8a16", ROWS, small ? SM_MAXM : COLS, WAVES, p.chunks_per_wave, ring,
-           aligned ? "aligned16" : "bytewise", (long long)M, p.tiles);
+           small ? "w8a16_small_m" : "w8a16", small ? small_shape(w).rb : ROWS, small ? SM_MAXM : COLS, WAVES,
+           p.chunks_per_wave, ring, aligned ? "aligned16" : "bytewise", (long long)M,
+           small ? small_shape(w).tiles : p.tiles);
   return buf;
 }
 
@@ -1151,7 +1207,12 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   a.y_bf16 = y_bf16 ? 1 : 0;
   auto kern = w8a16_kernel<true, false, true>;
   const bool sb = w.scale_bf16 != 0;
+  int grid = p.tiles;
   if (aligned && M <= SM_MAXM) {
+    const SmallShape sh = small_shape(w);
+    a.tm = sh.tm;
+    a.rows_per_block = sh.rb;
+    grid = sh.tiles;
     // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load,
     // and 3 M term columns of F32 tokens in one 16-column MFMA pass up to M = 5
     const int depth = small_depth(p.chunks_per_wave);
@@ -1179,7 +1240,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     if (x_bf16) kern = sb ? w8a16_kernel<false, true, true> : w8a16_kernel<false, true, false>;
     else kern = sb ? w8a16_kernel<false, false, true> : w8a16_kernel<false, false, false>;
   }
-  hipLaunchKernelGGL(kern, dim3(p.tiles), dim3(THREADS), 0, stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a16 launch");
 }
 

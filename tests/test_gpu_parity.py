@@ -701,11 +701,13 @@ def test_w8a8_scale_layouts_give_identical_outputs(name):
         assert_within(y_km, ref, bound, False, f"{name} {kernel}")
 
 
+@pytest.mark.parametrize("M", [1, 6, 8])
 @pytest.mark.parametrize("sdt", ["bf16", "f32"])
-def test_w8a16_one_token_blocks_of_odd_row_counts(sdt):
-    """One token on grouped members of 4100 and 700 rows (K = 1024): the one-token kernel
-    balances the grid with 19-row blocks, so blocks start at any row, straddle 128-row scale
-    blocks and leave part of their last 8-row group masked.  Every output against the oracle."""
+def test_w8a16_blocks_of_odd_row_counts(sdt, M):
+    """Grouped members of 4100 and 700 rows (K = 1024): the one-token kernel (M = 1) and the
+    few-token MFMA kernel (M = 6, 8) balance the grid with 19-row blocks, so blocks start at
+    any row, straddle 128-row scale blocks (two grid rows per block) and leave part of their
+    last 8-row group or 16-row tile masked.  Every output against the oracle."""
     t = torch()
     g = np.random.default_rng(197)
     K = 1024
@@ -720,10 +722,10 @@ def test_w8a16_one_token_blocks_of_odd_row_counts(sdt):
     dt = t.float32 if sdt == "f32" else t.bfloat16
     w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.from_numpy(np.asarray(s, np.float32)).to(device()).to(dt))
                           for c, s in om])
-    d = w.describe(B.ARM_W8A16, 1)
-    banner(f"w8a16 one token, odd rows per block: {d}")
+    d = w.describe(B.ARM_W8A16, M)
+    banner(f"w8a16 M={M}, odd rows per block: {d}")
     if t.cuda.get_device_properties(0).multi_processor_count == 256:
-        assert "kernel=w8a16_m1 rows=19 " in d, d
-    x = synth.gaussian_activations(197, "odd_rows_X", 1, K)
+        assert ("kernel=w8a16_m1 rows=19 " if M == 1 else "kernel=w8a16_small_m rows=19 ") in d, d
+    x = synth.gaussian_activations(197, f"odd_rows_X{M}", M, K)
     y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
-    assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"odd rows {sdt}")
+    assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"odd rows {sdt} M={M}")
