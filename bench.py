@@ -630,7 +630,9 @@ def main():
              "us_by_M": {k: {"median": round(v["us"], 2), "p10": round(v["us_p10"], 2), "p90": round(v["us_p90"], 2),
                              "launches": v["launches"]} for k, v in bm.items()},
              "read_stream_context": {k: round(v, 1) for k, v in d["read_stream_context"].items() if k != "kernel"},
-             "path": bm[last]["describe"]}
+             "path": bm[last]["describe"],
+             "frac_hbm_by_M": {k: round(v["gbs"] / HBM_PEAK_GBS, 4) for k, v in bm.items()},
+             "path_by_M": {k: v["describe"].split("|")[1].strip() for k, v in bm.items()}}
         if roofline_traffic is not False:
             r["roofline"] = {"bound": "hbm", "kernel": f"w8a16 ({last})", "achieved": round(bm[last]["gbs"], 1),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(bm[last]["gbs"] / HBM_PEAK_GBS, 4),
