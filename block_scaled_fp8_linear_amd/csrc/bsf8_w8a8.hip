@@ -327,7 +327,11 @@ constexpr int F_COPIERS = 4;
 constexpr int F_A_LOADS = FBN / 8 / F_COPIERS;  // weight slabs per copying wave
 constexpr int F_B_LOADS = FBM / 8 / F_COPIERS;  // token slabs per copying wave
 constexpr int XCDS = 8;
-constexpr int GROUP_ROWS = 8;   // row tiles per L2 group
+// Row tiles per L2 group: 16 when there are at most 4 token tiles (M <= 1024)
+// and more tiles than one round, else 8 (measured: gate/up at M = 1024,
+// 544 tiles, 170 -> 166 us with 16; the M = 8192 prefill keeps 8, 794 -> 798
+// us with 16; the M = 1024 down projection, 80 tiles all split, 92 -> 93 us).
+int group_rows_for(int m_tiles, int tiles, int cus) { return m_tiles <= 4 && tiles > cus ? 16 : 8; }
 constexpr int F_MAX_KB = 1024;  // K up to 131072 on the fast path
 
 struct FastArgs {
@@ -346,6 +350,7 @@ struct FastArgs {
   int32_t y_bf16;
   int32_t y_vec;   // y, ldy and every member's column offset allow 16-byte stores
   int32_t y_nt;    // the output exceeds half the Infinity Cache: store it non-temporally
+  int32_t group_rows;   // row tiles per L2 group
   // split-K for the row tiles from rt_split0 on: their K blocks are cut into
   // `splits` ranges of kb_per_split; split s of tile (R, mt) writes its F32
   // partial tile to ws + s * M * ldws, columns (R - rt_split0) * FBN + [0, FBN),
@@ -462,7 +467,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   // each XCD runs its blocks in order.  Two kinds of work are dealt evenly to
   // every XCD, whole tiles first and split tiles (K ranges of the last row
   // tiles) after them; within each kind an XCD walks a contiguous run of
-  // tiles in groups of GROUP_ROWS row tiles x all token tiles, so blocks that
+  // tiles in groups of group_rows row tiles x all token tiles, so blocks that
   // run together share operands in that XCD's L2.  Split work walks
   // (split, row tile) pairs split-major: a group shares one K range.
   const int nblk = gridDim.x;
@@ -481,6 +486,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   const bool whole = l < n_whole_here;
   const int v = whole ? start_whole + l : start_split + (l - n_whole_here);
   const int vr_total = whole ? a.rt_split0 : split_rows * a.splits;
+  const int GROUP_ROWS = a.group_rows;
   const int gsz = GROUP_ROWS * a.m_tiles;
   const int grp = v / gsz;
   const int in_grp = v - grp * gsz;
@@ -927,7 +933,8 @@ std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
              "kernel=w8a8_gemm_fast tile=%dx%d waves=8 lds=2x%dKiB (two stage arrays) buffer_load_lds "
              "xcd_groups=%d split_k=%d split_row_tiles=%d | M=%lld blocks=%d",
-             FBN, FBM, F_STAGE / 1024, GROUP_ROWS, p.splits, p.rt_total - p.rt_split0, (long long)M, p.blocks);
+             FBN, FBM, F_STAGE / 1024, group_rows_for(p.m_tiles, p.rt_total * p.m_tiles, device_cus()), p.splits,
+             p.rt_total - p.rt_split0, (long long)M, p.blocks);
   else
     snprintf(buf, sizeof(buf),
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
@@ -955,6 +962,7 @@ bsf8_status launch_fast(const Plan& p, const WeightDev& w, bool dense, const uin
   a.M = int32_t(M);
   a.m_tiles = p.m_tiles;
   a.rt_total = p.rt_total;
+  a.group_rows = group_rows_for(p.m_tiles, p.rt_total * p.m_tiles, device_cus());
   a.y_bf16 = y_bf16 ? 1 : 0;
   const int64_t esz = y_bf16 ? 2 : 4;
   bool vec = (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (ldy * esz) % 16 == 0;
@@ -1040,7 +1048,8 @@ std::string describe_dense(int64_t N, int64_t K, int64_t M) {
            "arm=dense arithmetic=bf16xbf16 mfma_f32_16x16x32_bf16 (two per 128-byte K block), f32 accumulate | "
            "kernel=w8a8_gemm_fast<dense> tile=%dx%d waves=8 buffer_load_lds xcd_groups=%d split_k=%d "
            "split_row_tiles=%d | M=%lld blocks=%d | dense weight N=%lld K=%lld bf16",
-           FBN, FBM, GROUP_ROWS, p.splits, p.rt_total - p.rt_split0, (long long)m, p.blocks, (long long)N,
+           FBN, FBM, group_rows_for(p.m_tiles, p.rt_total * p.m_tiles, device_cus()), p.splits,
+           p.rt_total - p.rt_split0, (long long)m, p.blocks, (long long)N,
            (long long)K);
   return buf;
 }
