@@ -360,7 +360,9 @@ def bench_w8a16_rotating(torch, B, members, x_np, Ms, dev, label):
     st = replay_stats(torch, g, 50, copies)
     wbytes = sum(m.codes.nbytes for m in members)
     out["read_stream_context"] = dict(us=st["median"] * 1e3, gbs=wbytes / (st["median"] * 1e-3) / 1e9,
-                                      kernel="bsf8_read_stream over the same weight bytes, same rotation")
+                                      launches_per_copy=len(members),
+                                      kernel="bsf8_read_stream over the same weight bytes, same rotation "
+                                             "(one launch per member buffer)")
     del g, handles, copies_t
     torch.cuda.empty_cache()
     return out
