@@ -7,8 +7,9 @@
 // One group of 128 channels is handled by 32 lanes (half a wave), 4 channels per
 // lane, so a wave covers 256 contiguous channels of one token and every global
 // access is a coalesced 16-byte (F32) or 8-byte (BF16) load and a 4-byte store.
-// A half-wave takes four consecutive groups and issues all four loads before
-// processing any, so each lane has several loads in flight.
+// A half-wave takes two or four consecutive groups (four for large tensors)
+// and issues all their loads before processing any, so each lane has several
+// loads in flight.
 // The group amax is a 5-step butterfly inside the half-wave.  The arithmetic is
 // the defined one, in F32: s = max(amax, 1e-10) / 448 and f = x / s with IEEE
 // division (hipcc's default division is correctly rounded), clamp to +-448, then
@@ -35,7 +36,11 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr float kE4M3Max = 448.0f;
 constexpr float kAmaxFloor = 1e-10f;
-constexpr int kGroupsPerHalf = 4;   // 128-element groups per 32-lane half-wave
+// 128-element groups per 32-lane half-wave: 4 from 2^18 groups on, else 2
+// (more, smaller blocks: X [1024, 17408] 19.1 -> 18.0 us, X [1024, 5120]
+// 7.5 -> 6.9 us, the GLU step 35.1 -> 33.5 us; X [8192, 7168] keeps 4, 56.4
+// against 59.6 us with 2).
+constexpr int64_t kManyGroups = int64_t(1) << 18;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -75,7 +80,7 @@ __device__ __forceinline__ float silu_glu(float g, float u) {
 }
 
 // GLU: x is the gate/up output; K = F, the up half starts at column K.
-template <bool BF16, bool GLU>
+template <bool BF16, bool GLU, int kGroupsPerHalf>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int32_t M, int32_t K,
                                                                   int64_t ldx, uint8_t* __restrict__ xq, int64_t ldq,
                                                                   float* __restrict__ xs, int64_t xs_sm, int64_t xs_sk,
@@ -137,7 +142,8 @@ bsf8_status launch_quant(const void* x, bool x_bf16, bool glu, int64_t M, int64_
                          int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream) {
   const int32_t Kb = int32_t((K + kBlock - 1) / kBlock);
   const int64_t n_groups = M * Kb;
-  const int64_t per_block = int64_t(kQuantThreads / 32) * kGroupsPerHalf;
+  const int gph = n_groups >= kManyGroups ? 4 : 2;
+  const int64_t per_block = int64_t(kQuantThreads / 32) * gph;
   const int64_t grid64 = (n_groups + per_block - 1) / per_block;
   if (grid64 > INT32_MAX) {
     set_error("UNSUPPORTED: %lld activation groups", (long long)n_groups);
@@ -151,8 +157,10 @@ bsf8_status launch_quant(const void* x, bool x_bf16, bool glu, int64_t M, int64_
   const int q_vec = (reinterpret_cast<uintptr_t>(xq) % 4 == 0) && (ldq % 4 == 0);
   using Kern = void (*)(const void*, int32_t, int32_t, int64_t, uint8_t*, int64_t, float*, int64_t, int64_t, int32_t,
                         int32_t, int32_t);
-  const Kern kern = x_bf16 ? (glu ? quant_act_kernel<true, true> : quant_act_kernel<true, false>)
-                           : (glu ? quant_act_kernel<false, true> : quant_act_kernel<false, false>);
+  const Kern kern = gph == 4 ? (x_bf16 ? (glu ? quant_act_kernel<true, true, 4> : quant_act_kernel<true, false, 4>)
+                                       : (glu ? quant_act_kernel<false, true, 4> : quant_act_kernel<false, false, 4>))
+                             : (x_bf16 ? (glu ? quant_act_kernel<true, true, 2> : quant_act_kernel<true, false, 2>)
+                                       : (glu ? quant_act_kernel<false, true, 2> : quant_act_kernel<false, false, 2>));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kQuantThreads), 0, stream, x, int32_t(M), int32_t(K), ldx, xq, ldq, xs,
                      xs_sm, xs_sk, Kb, x_vec, q_vec);
   return device_status(hipGetLastError(), glu ? "quant_glu launch" : "quant_act launch");
