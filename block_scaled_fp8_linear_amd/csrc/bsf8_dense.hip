@@ -14,7 +14,8 @@
 // HBM-bound: each thread turns 16 weight bytes into 16 outputs; consecutive
 // threads take consecutive 16-byte pieces of a row, so reads and writes are
 // contiguous per wave.  The member and scale lookups are a few scalar-cached
-// loads per thread.
+// loads per thread.  The copy is written once and read by a later GEMM, so
+// its stores are non-temporal (Q/K/V, three copies in turn: 28.7 -> 25.9 us).
 #include <hip/hip_runtime.h>
 
 #include "bsf8_internal.h"
@@ -23,6 +24,7 @@ namespace bsf8 {
 namespace {
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
 constexpr int UP_THREADS = 256;
 
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(UP_THREADS) void upcast_kernel(UpcastArgs a) {
     for (int i = 0; i < 8; ++i) p[i] = bf16_pair(v[2 * i], v[2 * i + 1]);
     uint16_t* dst = static_cast<uint16_t*>(a.out) + off;
     if (VEC) {
-      reinterpret_cast<uint4*>(dst)[0] = make_uint4(p[0], p[1], p[2], p[3]);
-      reinterpret_cast<uint4*>(dst)[1] = make_uint4(p[4], p[5], p[6], p[7]);
+      __builtin_nontemporal_store(u4v{p[0], p[1], p[2], p[3]}, reinterpret_cast<u4v*>(dst));
+      __builtin_nontemporal_store(u4v{p[4], p[5], p[6], p[7]}, reinterpret_cast<u4v*>(dst) + 1);
     } else {
       for (int i = 0; i < n; ++i) dst[i] = uint16_t(p[i >> 1] >> (16 * (i & 1)));
     }
@@ -100,7 +102,9 @@ __global__ __launch_bounds__(UP_THREADS) void upcast_kernel(UpcastArgs a) {
     if (VEC) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        reinterpret_cast<float4*>(dst)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        __builtin_nontemporal_store(u4v{__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                                        __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3])},
+                                    reinterpret_cast<u4v*>(dst) + i);
     } else {
       for (int i = 0; i < n; ++i) dst[i] = v[i];
     }
