@@ -195,11 +195,11 @@ bsf8_status bsf8_weight_scale_row(const bsf8_weight* w, int64_t n, int32_t* memb
  * [M, ceil(K/128)] F32 array whose element (m, kb) sits at
  * xs[m * xs_sm + kb * xs_sk] (strides in elements).  Two layouts are accepted:
  *   token-major: xs_sk == 1 and xs_sm >= ceil(K/128)  (row m = token m's scales,
- *                the layout of the pages' quantizer);
+ *                as the quantizer of "Module w8a8_prefill" writes them);
  *   K-major:     xs_sm == 1 and xs_sk >= M            (row kb = every token's
- *                scale of block kb, token index contiguous, the layout the
- *                pages transpose to for their cuBLASLt path: "Module
- *                w8a8_prefill", section "Reachability").
+ *                scale of block kb, token index contiguous: the transposed
+ *                copy that "Module w8a8_prefill", section "Reachability",
+ *                makes for its cuBLASLt path).
  * (When M == 1 or ceil(K/128) == 1 either test may hold.)  Any other pair is
  * INVALID_ARG.  The W8A8 product reads a K block's 256 token scales at a time:
  * K-major makes that one contiguous kilobyte, token-major 256 separate words,
