@@ -331,6 +331,8 @@ def quant_act(x, xq=None, xs=None):
         xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if xs is None:
         xs = scales_kmajor(M, Kb, x.device)
+    if tuple(xq.shape) != (M, K) or tuple(xs.shape) != (M, Kb) or xs.dtype != torch.float32:
+        raise ValueError(f"xq must be [M, K] = [{M}, {K}] and xs float32 [M, Kb] = [{M}, {Kb}]")
     _check(lib().bsf8_quant_act(x.data_ptr(), _dt_of(x), M, K, x.stride(0), xq.data_ptr(), xq.stride(0),
                                 xs.data_ptr(), xs.stride(0), xs.stride(1), _stream_ptr(x.device)), "quant_act")
     return xq, xs
@@ -348,6 +350,8 @@ def quant_glu(y, xq=None, xs=None):
         xq = torch.empty((M, F), dtype=torch.uint8, device=y.device)
     if xs is None:
         xs = scales_kmajor(M, Fb, y.device)
+    if tuple(xq.shape) != (M, F) or tuple(xs.shape) != (M, Fb) or xs.dtype != torch.float32:
+        raise ValueError(f"xq must be [M, F] = [{M}, {F}] and xs float32 [M, Fb] = [{M}, {Fb}]")
     _check(lib().bsf8_quant_glu(y.data_ptr(), _dt_of(y), M, F, y.stride(0), xq.data_ptr(), xq.stride(0),
                                 xs.data_ptr(), xs.stride(0), xs.stride(1), _stream_ptr(y.device)), "quant_glu")
     return xq, xs
@@ -372,8 +376,10 @@ def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=N
     """FP8 x FP8 arm with F32 epilogue: y [M, N] (bfloat16 output unless out_dtype says float32)."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
-    if xq.dim() != 2 or xq.shape[1] != w.K or xq.stride(1) != 1 or xs.dim() != 2:
-        raise ValueError("xq must be [M, K] with unit column stride and xs [M, Kb]")
+    Kb = -(-w.K // BLOCK)
+    if (xq.dim() != 2 or xq.shape[1] != w.K or xq.stride(1) != 1 or tuple(xs.shape) != (xq.shape[0], Kb)
+            or xs.dtype != torch.float32):
+        raise ValueError("xq must be [M, K] with unit column stride and xs float32 [M, ceil(K/128)]")
     M = xq.shape[0]
     y = _out(out, M, w.n_total, out_dtype, xq.device)
     ws, wsb = workspace if workspace is not None else w.workspace(ARM_W8A8, M)
