@@ -608,3 +608,169 @@ def pin_silu_glu(O, seed=31):
     if not (np.array_equal(q, q2) and np.array_equal(s, s2)):
         return False, "glu_quant composition"
     return True, ""
+
+
+# ------------------------------------------------------------ P16 - P18
+# The helpers every GEMM verdict rests on: the per-element error scale
+# sum_k |a_k w_k|, the acceptance test built on it, and the cross-arm metrics
+# of "Module w8a8_prefill", section "ACCURACY".
+
+def _dec_py(c: int) -> float:
+    """E4M3 value of one finite code from its bit fields (sign, exponent bias 7, 3-bit mantissa)."""
+    sgn = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 0xF, c & 7
+    return sgn * (m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+
+
+def _abs_sum_loops(a_rows, members, K):
+    """sum_k |a[m,k]| * |dec(w[n,k]) * s_i[r//128, k//128]| by plain Python loops.
+
+    ``a_rows`` holds float values (lists of floats) per token; the weights are
+    decoded from their bit fields here, so neither the oracle's table nor
+    NumPy's matmul is involved."""
+    dec = _dec_py
+    out = []
+    for a in a_rows:
+        row = []
+        for codes, scale in members:
+            for r in range(codes.shape[0]):
+                acc = 0.0
+                for k in range(K):
+                    acc += abs(a[k]) * abs(dec(int(codes[r, k])) * float(scale[r // 128, k // 128]))
+                row.append(acc)
+        out.append(row)
+    return np.array(out, np.float64)
+
+
+def pin_abs_bounds(O, seed=37):
+    """P16: the error scale sum_k |a_k w_k| of both arms and of their row forms.
+
+    * equals pure-Python loops over the dequantized operands, on grouped
+      members with ragged rows and a ragged K (W8A16: a_k = x_k; W8A8: a_k =
+      dec(q_k) * s_a of the token's group);
+    * closed form: with every operand non-negative there is no cancellation,
+      so the bound equals the output itself;
+    * flipping the sign of activations or weight codes leaves it unchanged,
+      while the output changes, so |sum| in place of sum |.| is caught.
+    """
+    g = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    K = 200
+    members = [(finite[g.integers(0, finite.size, (r, K))],
+                np.exp2(g.uniform(-9, -3, (-(-r // 128), -(-K // 128)))).astype(np.float32)) for r in (130, 5)]
+    x = (g.standard_normal((3, K)) * np.exp2(g.uniform(-3, 3, (3, 1)))).astype(np.float32)
+    b16 = O.abs_bound_w8a16(x, members)
+    loops16 = _abs_sum_loops([[float(v) for v in row] for row in x], members, K)
+    if b16.shape != loops16.shape or not np.allclose(b16, loops16, rtol=1e-12, atol=0):
+        return False, "w8a16 bound vs loops"
+    xq, xs = O.quant_act(x)
+    a = [[_dec_py(int(xq[m, k])) * float(xs[m, k // 128]) for k in range(K)] for m in range(x.shape[0])]
+    b8 = O.abs_bound_w8a8(xq, xs, members)
+    if not np.allclose(b8, _abs_sum_loops(a, members, K), rtol=1e-12, atol=0):
+        return False, "w8a8 bound vs loops"
+    rows = [0, 127, 128, 129, 130, 134]
+    if not np.allclose(O.abs_bound_w8a16_rows(x, members, rows), loops16[:, rows], rtol=1e-12, atol=0):
+        return False, "w8a16 row form"
+    if not np.allclose(O.abs_bound_w8a8_rows(xq, xs, members, rows), b8[:, rows], rtol=1e-12, atol=0):
+        return False, "w8a8 row form"
+    pos = [(c & np.uint8(0x7F), s) for c, s in members]
+    xp = np.abs(x)
+    if not np.array_equal(O.abs_bound_w8a16(xp, pos), O.linear_w8a16(xp, pos)):
+        return False, "non-negative operands: bound != output"
+    qp, sp = O.quant_act(xp)
+    if not np.array_equal(O.abs_bound_w8a8(qp, sp, pos), O.linear_w8a8(qp, sp, pos)):
+        return False, "non-negative operands (w8a8): bound != output"
+    flipped = [(c ^ np.uint8(0x80), s) for c, s in members]
+    if not np.array_equal(O.abs_bound_w8a16(-x, flipped), b16):
+        return False, "sign flips change the bound"
+    y = O.linear_w8a16(x, members)
+    if not (np.all(b16 >= np.abs(y)) and np.any(b16 > 2 * np.abs(y))):
+        return False, "bound does not dominate |y| with room on mixed signs"
+    return True, ""
+
+
+def pin_within_bound(O, seed=41):
+    """P17: the acceptance test |y - y_ref| <= 1e-3 * S (+ 2^-8 |y_ref| for BF16).
+
+    * an error of 0.999 x the bound passes and 1.001 x fails, element by
+      element, for the F32 form and the BF16 form (whose half-ULP term is
+      checked against the F32 form on the same errors);
+    * NaN on either side fails; a zero bound with equal outputs passes;
+    * the reported worst ratio is max(err / bound) computed by a loop.
+    """
+    g = np.random.default_rng(seed)
+    S = np.exp2(g.uniform(-10, 10, (4, 7)))
+    y_ref = g.standard_normal((4, 7)) * S * 0.01
+    sign = np.where(g.random((4, 7)) < 0.5, -1.0, 1.0)
+    for bf16 in (False, True):
+        bound = 1e-3 * S + (2.0 ** -8 * np.abs(y_ref) if bf16 else 0.0)
+        ok, worst = O.within_bound(y_ref + sign * 0.999 * bound, y_ref, S, bf16_out=bf16)
+        if not ok:
+            return False, f"0.999 x bound rejected (bf16={bf16})"
+        loop_worst = max(abs((y_ref[i, j] + sign[i, j] * 0.999 * bound[i, j]) - y_ref[i, j]) / bound[i, j]
+                         for i in range(4) for j in range(7))
+        if abs(worst - loop_worst) > 1e-9:
+            return False, f"worst ratio {worst} vs {loop_worst}"
+        for i, j in ((0, 0), (3, 6), (2, 3)):
+            y = y_ref + sign * 0.5 * bound
+            y[i, j] = y_ref[i, j] + sign[i, j] * 1.001 * bound[i, j]
+            if O.within_bound(y, y_ref, S, bf16_out=bf16)[0]:
+                return False, f"1.001 x bound accepted at {i},{j} (bf16={bf16})"
+    # the BF16 form adds exactly half a BF16 ULP's worth: an error between the two bounds
+    mid = y_ref + sign * (1e-3 * S + 2.0 ** -9 * np.abs(y_ref))
+    if not O.within_bound(mid, y_ref, S, bf16_out=True)[0] or O.within_bound(mid, y_ref, S, bf16_out=False)[0]:
+        return False, "BF16 term"
+    for bad in (np.nan,):
+        y = y_ref.copy()
+        y[1, 2] = bad
+        if O.within_bound(y, y_ref, S)[0]:
+            return False, "NaN output accepted"
+        r = y_ref.copy()
+        r[1, 2] = bad
+        if O.within_bound(y_ref, r, S)[0]:
+            return False, "NaN reference accepted"
+    z = np.zeros((2, 3))
+    if not O.within_bound(z, z, z)[0]:
+        return False, "zero bound, equal outputs rejected"
+    if O.within_bound(z + 1e-30, z, z)[0]:
+        return False, "zero bound, unequal outputs accepted"
+    return True, ""
+
+
+def pin_cross_arm_metrics(O, seed=43):
+    """P18: cosine and relative RMS of the W8A8 output against the W8A16 one.
+
+    Closed forms: identical outputs give (1, 0); orthogonal outputs cos 0;
+    y8 = 1.01 y16 gives rel 0.01 and y16 = 1.01 y8 gives 0.01/1.01 (the W8A16
+    output is the reference, the denominator); y8 = -y16 gives (-1, 2).
+    Brute force: sums written out as Python loops over the flattened output,
+    on a 2-D case whose rows have very different magnitudes (a per-row mean of
+    metrics would differ).
+    """
+    g = np.random.default_rng(seed)
+    y = g.standard_normal((5, 9)) * np.exp2(np.arange(5) * 3.0)[:, None]
+    cos, rel = O.cross_arm_metrics(y, y)
+    if abs(cos - 1.0) > 1e-15 or rel != 0.0:
+        return False, f"identical: {cos} {rel}"
+    a = np.array([1.0, 2.0, 0.0, -3.0])
+    b = np.array([2.0, -1.0, 5.0, 0.0])
+    if abs(O.cross_arm_metrics(a, b)[0]) > 1e-15:
+        return False, "orthogonal"
+    cos, rel = O.cross_arm_metrics(1.01 * y, y)
+    if abs(rel - 0.01) > 1e-12 or abs(cos - 1.0) > 1e-15:
+        return False, f"y8 = 1.01 y16: {cos} {rel}"
+    if abs(O.cross_arm_metrics(y, 1.01 * y)[1] - 0.01 / 1.01) > 1e-12:
+        return False, "denominator is not the W8A16 output"
+    cos, rel = O.cross_arm_metrics(-y, y)
+    if abs(cos + 1.0) > 1e-15 or abs(rel - 2.0) > 1e-12:
+        return False, "opposite"
+    y8 = y + g.standard_normal(y.shape) * 0.05 * np.abs(y)
+    fa, fb = [float(v) for v in y8.ravel()], [float(v) for v in y.ravel()]
+    dot = sum(p * q for p, q in zip(fa, fb))
+    na = math.sqrt(sum(p * p for p in fa))
+    nb = math.sqrt(sum(q * q for q in fb))
+    nd = math.sqrt(sum((p - q) ** 2 for p, q in zip(fa, fb)))
+    cos, rel = O.cross_arm_metrics(y8, y)
+    if abs(cos - dot / (na * nb)) > 1e-12 or abs(rel - nd / nb) > 1e-12:
+        return False, f"loops: {cos} vs {dot / (na * nb)}, {rel} vs {nd / nb}"
+    return True, ""

@@ -206,3 +206,88 @@ def test_mutation_glu_halves_swapped(monkeypatch):
     orig = OM.silu_glu
     monkeypatch.setattr(OM, "silu_glu", lambda g, u: orig(u, g))
     assert _fails(P.pin_silu_glu, OM)
+
+
+# ------------------------------------------- tolerance and metric helpers
+
+def test_mutation_bound_abs_of_sum(monkeypatch):
+    """|sum_k a_k w_k| in place of sum_k |a_k w_k| fails the bound pin."""
+    monkeypatch.setattr(OM, "abs_bound_w8a16", lambda x, members: np.abs(OM.linear_w8a16(x, members)))
+    assert _fails(P.pin_abs_bounds, OM)
+
+
+def test_mutation_bound_missing_activation_abs(monkeypatch):
+    """Dropping |.| on the dequantized activation of the W8A8 bound fails the bound pin."""
+    monkeypatch.setattr(OM, "abs_bound_w8a8",
+                        lambda xq, xs, members: OM.dequantize_act(xq, xs) @ np.abs(OM.dequantize_members(members)).T)
+    assert _fails(P.pin_abs_bounds, OM)
+
+
+def test_mutation_bound_rows_use_global_grid(monkeypatch):
+    """A row form that takes the scale row n // 128 of the stacked grids fails the bound pin."""
+    def rows_global(xq, xs, members, rows):
+        codes = np.concatenate([c for c, _ in members])
+        sc = np.concatenate([s for _, s in members])
+        K = codes.shape[1]
+        w = np.stack([OM.e4m3_decode(codes[n]) * np.repeat(sc[min(n // 128, sc.shape[0] - 1)], 128)[:K] for n in rows])
+        return np.abs(OM.dequantize_act(xq, xs)) @ np.abs(w).T
+    monkeypatch.setattr(OM, "abs_bound_w8a8_rows", rows_global)
+    assert _fails(P.pin_abs_bounds, OM)
+
+
+def test_mutation_within_bound_loose_factor(monkeypatch):
+    """A tolerance of 2e-3 in place of 1e-3 fails the acceptance pin."""
+    orig = OM.within_bound
+    monkeypatch.setattr(OM, "within_bound", lambda y, r, s, rel=1e-3, bf16_out=False: orig(y, r, s, 2e-3, bf16_out))
+    assert _fails(P.pin_within_bound, OM)
+
+
+def test_mutation_within_bound_full_ulp(monkeypatch):
+    """A whole BF16 ULP (2^-7 |y|) in place of half of one fails the acceptance pin."""
+    def loose(y_test, y_ref, abs_sum, rel=1e-3, bf16_out=False):
+        err = np.abs(np.asarray(y_test, np.float64) - y_ref)
+        bound = np.maximum(rel * abs_sum + (2.0 ** -7 * np.abs(y_ref) if bf16_out else 0.0), np.finfo(np.float32).tiny)
+        return bool(np.all(err <= bound)) and not np.isnan(err).any(), float(np.nanmax(err / bound))
+    monkeypatch.setattr(OM, "within_bound", loose)
+    assert _fails(P.pin_within_bound, OM)
+
+
+def test_mutation_within_bound_ignores_nan(monkeypatch):
+    """An acceptance test that skips NaN elements fails the acceptance pin."""
+    def nan_blind(y_test, y_ref, abs_sum, rel=1e-3, bf16_out=False):
+        err = np.abs(np.asarray(y_test, np.float64) - y_ref)
+        bound = np.maximum(rel * abs_sum + (2.0 ** -8 * np.abs(y_ref) if bf16_out else 0.0), np.finfo(np.float32).tiny)
+        keep = ~np.isnan(err)
+        return bool(np.all(err[keep] <= bound[keep])), float(np.nanmax(err / bound))
+    monkeypatch.setattr(OM, "within_bound", nan_blind)
+    assert _fails(P.pin_within_bound, OM)
+
+
+def test_mutation_cross_arm_wrong_denominator(monkeypatch):
+    """Relative RMS over the W8A8 output's norm fails the metrics pin."""
+    def wrong(y8, y16):
+        a, b = np.ravel(y8).astype(np.float64), np.ravel(y16).astype(np.float64)
+        return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b))), float(np.linalg.norm(a - b) / np.linalg.norm(a))
+    monkeypatch.setattr(OM, "cross_arm_metrics", wrong)
+    assert _fails(P.pin_cross_arm_metrics, OM)
+
+
+def test_mutation_cross_arm_mean_of_rows(monkeypatch):
+    """Metrics averaged over rows instead of over the whole output fail the metrics pin."""
+    orig = OM.cross_arm_metrics
+
+    def per_row(y8, y16):
+        y8, y16 = np.atleast_2d(y8), np.atleast_2d(y16)
+        vals = [orig(a, b) for a, b in zip(y8, y16)]
+        return float(np.mean([v[0] for v in vals])), float(np.mean([v[1] for v in vals]))
+    monkeypatch.setattr(OM, "cross_arm_metrics", per_row)
+    assert _fails(P.pin_cross_arm_metrics, OM)
+
+
+def test_mutation_cross_arm_unnormalised_cosine(monkeypatch):
+    """A cosine normalised by the W8A16 norm squared fails the metrics pin."""
+    def wrong(y8, y16):
+        a, b = np.ravel(y8).astype(np.float64), np.ravel(y16).astype(np.float64)
+        return float(a @ b / (b @ b)), float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    monkeypatch.setattr(OM, "cross_arm_metrics", wrong)
+    assert _fails(P.pin_cross_arm_metrics, OM)
