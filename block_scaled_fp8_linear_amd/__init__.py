@@ -218,6 +218,26 @@ def _dt_of(t) -> int:
             torch.float8_e4m3fn: DT_F8_E4M3, torch.float8_e5m2: DT_F8_E5M2}.get(t.dtype, DT_OTHER)
 
 
+def _on_device(device, **tensors):
+    """Refuse, before any library call, a tensor that is not a GPU tensor on ``device``.
+
+    The library takes raw device addresses: a host tensor's address would reach
+    a kernel as if it were device memory, so every tensor argument is checked
+    here (None entries are skipped)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (got one on {t.device})")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _codes_dtype_ok(t) -> bool:
+    torch = _torch()
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
 def _stream_ptr(device) -> int:
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
@@ -241,7 +261,11 @@ class BlockFP8Weight:
         self._tensors = []
         leaf = "scale" if tuple(int(b) for b in block) == (0, 0) else "scale_inv"
         self.per_tensor = leaf == "scale"
-        for w, s in members:
+        if len(members) == 0:
+            raise ValueError("a weight needs at least one member")
+        dev0 = members[0][0].device
+        for i, (w, s) in enumerate(members):
+            _on_device(dev0 if dev0.type == "cuda" else None, **{f"member {i} weight": w, f"member {i} scale": s})
             if not (w.is_contiguous() and s.is_contiguous()):
                 raise ValueError("weights and scale grids must be contiguous")
             wdt = DT_F8_E4M3 if _dt_of(w) in (DT_U8, DT_F8_E4M3) else _dt_of(w)
@@ -323,6 +347,8 @@ def quant_act(x, xq=None, xs=None):
     xs may be any [M, Kb] float32 view in the token-major or the K-major layout; by default
     it is a new K-major one."""
     torch = _torch()
+    _on_device(None, x=x)
+    _on_device(x.device, xq=xq, xs=xs)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     M, K = x.shape
@@ -333,6 +359,8 @@ def quant_act(x, xq=None, xs=None):
         xs = scales_kmajor(M, Kb, x.device)
     if tuple(xq.shape) != (M, K) or tuple(xs.shape) != (M, Kb) or xs.dtype != torch.float32:
         raise ValueError(f"xq must be [M, K] = [{M}, {K}] and xs float32 [M, Kb] = [{M}, {Kb}]")
+    if not _codes_dtype_ok(xq) or xq.stride(1) != 1:
+        raise ValueError("xq must be uint8 or float8_e4m3fn with unit column stride")
     _check(lib().bsf8_quant_act(x.data_ptr(), _dt_of(x), M, K, x.stride(0), xq.data_ptr(), xq.stride(0),
                                 xs.data_ptr(), xs.stride(0), xs.stride(1), _stream_ptr(x.device)), "quant_act")
     return xq, xs
@@ -342,6 +370,8 @@ def quant_glu(y, xq=None, xs=None):
     """Gate/up output y [M, 2F] (gate then up; float32 or bfloat16) -> the down projection's
     quantized input for silu(gate) * up: (xq uint8 [M, F], xs f32 [M, ceil(F/128)]; xs as for quant_act)."""
     torch = _torch()
+    _on_device(None, y=y)
+    _on_device(y.device, xq=xq, xs=xs)
     if y.dim() != 2 or y.stride(1) != 1 or y.shape[1] % 2:
         raise ValueError("y must be 2-D with an even number of columns and unit column stride")
     M, F = y.shape[0], y.shape[1] // 2
@@ -352,6 +382,8 @@ def quant_glu(y, xq=None, xs=None):
         xs = scales_kmajor(M, Fb, y.device)
     if tuple(xq.shape) != (M, F) or tuple(xs.shape) != (M, Fb) or xs.dtype != torch.float32:
         raise ValueError(f"xq must be [M, F] = [{M}, {F}] and xs float32 [M, Fb] = [{M}, {Fb}]")
+    if not _codes_dtype_ok(xq) or xq.stride(1) != 1:
+        raise ValueError("xq must be uint8 or float8_e4m3fn with unit column stride")
     _check(lib().bsf8_quant_glu(y.data_ptr(), _dt_of(y), M, F, y.stride(0), xq.data_ptr(), xq.stride(0),
                                 xs.data_ptr(), xs.stride(0), xs.stride(1), _stream_ptr(y.device)), "quant_glu")
     return xq, xs
@@ -361,6 +393,7 @@ def linear_w8a16(w: BlockFP8Weight, x, out_dtype=None, out=None, workspace=None)
     """F32-activation arm: y [M, N] = x . dequant(W)^T (float32 output unless out_dtype says bfloat16)."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
+    _on_device(w.device, x=x, out=out, workspace=workspace[0] if workspace is not None else None)
     if x.dim() != 2 or x.stride(1) != 1 or x.shape[1] != w.K:
         raise ValueError("x must be [M, K] with unit column stride")
     M = x.shape[0]
@@ -376,10 +409,13 @@ def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=N
     """FP8 x FP8 arm with F32 epilogue: y [M, N] (bfloat16 output unless out_dtype says float32)."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
+    _on_device(w.device, xq=xq, xs=xs, out=out, workspace=workspace[0] if workspace is not None else None)
     Kb = -(-w.K // BLOCK)
     if (xq.dim() != 2 or xq.shape[1] != w.K or xq.stride(1) != 1 or tuple(xs.shape) != (xq.shape[0], Kb)
             or xs.dtype != torch.float32):
         raise ValueError("xq must be [M, K] with unit column stride and xs float32 [M, ceil(K/128)]")
+    if not _codes_dtype_ok(xq):
+        raise ValueError("xq must be uint8 or float8_e4m3fn (the quantizer's E4M3 bytes)")
     M = xq.shape[0]
     y = _out(out, M, w.n_total, out_dtype, xq.device)
     ws, wsb = workspace if workspace is not None else w.workspace(ARM_W8A8, M)
@@ -394,6 +430,7 @@ def upcast(w: BlockFP8Weight, out_dtype=None, out=None):
     """Dense copy [N, K] of the weight (bfloat16 unless out_dtype says float32): the resident=False load step."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
+    _on_device(w.device, out=out)
     if out is None:
         out = torch.empty((w.n_total, w.K), dtype=out_dtype, device=w.device)
     if out.dtype != out_dtype or out.dim() != 2 or out.shape[0] != w.n_total or out.shape[1] < w.K \
@@ -415,6 +452,8 @@ def linear_dense(wd, x, out_dtype=None, out=None, workspace=None):
     least dense_workspace_size bytes, allocated here when omitted."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
+    _on_device(None, wd=wd)
+    _on_device(wd.device, x=x, out=out, workspace=workspace)
     if wd.dim() != 2 or not wd.is_contiguous() or wd.dtype != torch.bfloat16:
         raise ValueError("wd must be a contiguous bfloat16 [N, K] tensor")
     N, K = wd.shape
@@ -445,6 +484,8 @@ def read_stream(buf, sink):
 
     ``sink``: int32 device tensor of at least READ_STREAM_SINK_WORDS words; the
     launch overwrites its leading words with per-block XORs of what it read."""
+    _on_device(None, buf=buf)
+    _on_device(buf.device, sink=sink)
     if sink.numel() * sink.element_size() < 4 * READ_STREAM_SINK_WORDS:
         raise ValueError(f"read_stream sink needs {READ_STREAM_SINK_WORDS} 4-byte words")
     _check(lib().bsf8_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),

@@ -230,3 +230,44 @@ def test_quant_glu_refuses_bad_arguments_without_launching():
     assert name(L.bsf8_quant_glu(None, B.DT_BF16, 4, 256, 512, fake, 256, fake, 2, 1, None)) == "INVALID_ARG"
     assert name(L.bsf8_quant_glu(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 4, 256, 512, fake, 256, fake, 2, 1,
                                  None)) == "ALIGNMENT"
+
+
+def test_binding_refuses_host_tensors_before_any_library_call():
+    """Host (CPU) tensors never reach the library: their addresses are not device
+    memory, so the binding raises ValueError first, for every call that takes a
+    tensor, and also rejects activation codes of any dtype other than E4M3 bytes."""
+    import types
+
+    import torch
+    codes = torch.zeros((256, 256), dtype=torch.uint8)
+    grid = torch.ones((2, 2), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.BlockFP8Weight([(codes, grid)])
+    x = torch.zeros((4, 256), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.quant_act(x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.quant_glu(torch.zeros((4, 512), dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.linear_dense(torch.zeros((8, 64), dtype=torch.bfloat16), torch.zeros((2, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.read_stream(torch.zeros(64, dtype=torch.int32), torch.zeros(B.READ_STREAM_SINK_WORDS, dtype=torch.int32))
+    # A handle that claims a GPU: host activations, outputs and workspaces are refused.
+    fake = types.SimpleNamespace(device=torch.device("cuda", 0), K=256, n_total=256, handle=None,
+                                 workspace=lambda arm, M: (None, 0))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.linear_w8a16(fake, x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.linear_w8a8(fake, torch.zeros((4, 256), dtype=torch.uint8), torch.ones((4, 2), dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.upcast(fake, out=torch.empty((256, 256), dtype=torch.bfloat16))
+
+
+def test_binding_checks_activation_code_dtype():
+    """xq must hold E4M3 bytes (uint8 or float8_e4m3fn): an int8 or float tensor of the
+    right shape is refused by dtype.  The predicate the calls use is checked directly on
+    meta tensors, since no device tensor exists without a GPU."""
+    import torch
+    for dt, ok in ((torch.uint8, True), (torch.float8_e4m3fn, True), (torch.int8, False), (torch.float32, False),
+                   (torch.float8_e5m2, False)):
+        assert B._codes_dtype_ok(torch.empty((2, 2), dtype=dt, device="meta")) == ok, dt
