@@ -20,7 +20,9 @@ import os
 from typing import Dict, List, Optional, Sequence, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsf8.so")
+# BSF8_LIBRARY may name another build of the same library (the host-sanitized
+# build the CPU tests run under); by default the in-tree libbsf8.so is loaded.
+LIB_PATH = os.environ.get("BSF8_LIBRARY") or os.path.join(_HERE, "libbsf8.so")
 
 DT_INVALID, DT_F8_E4M3, DT_F8_E5M2, DT_BF16, DT_F16, DT_F32, DT_U8, DT_OTHER = range(8)
 ARM_W8A16, ARM_W8A8, ARM_DENSE = 0, 1, 2

@@ -13,6 +13,7 @@
 //  weights", layout paragraph: quant_method fp8 with weight_block_size
 //  [128,128], leaves weight and weight_scale_inv; mixed BF16/F16 tensors such
 //  as the output head keep their own representation.)
+#include <cerrno>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -41,7 +42,7 @@ bsf8_status ifail(bsf8_status s, const char* fmt, ...) {
 // ---------------------------------------------------------------- JSON
 // A small recursive-descent reader: objects (key order kept), arrays,
 // strings (escapes decoded; \u escapes to UTF-8), numbers (integers exact
-// up to 2^63, others as double), true / false / null.
+// when they fit int64, others as double only), true / false / null.
 struct Json {
   enum Kind { NUL, BOOL, NUM, STR, ARR, OBJ } kind = NUL;
   bool b = false;
@@ -179,9 +180,15 @@ class Parser {
     const std::string t(s, p_);
     out.kind = Json::NUM;
     out.num = std::strtod(t.c_str(), nullptr);
-    if (!frac && t.size() <= 19) {
-      out.is_int = true;
-      out.inum = std::strtoll(t.c_str(), nullptr, 10);
+    if (!frac) {
+      // an integer is exact only when it fits int64: strtoll reports ERANGE
+      // (and clamps) for anything larger, which then stays a plain number
+      errno = 0;
+      const long long v = std::strtoll(t.c_str(), nullptr, 10);
+      if (errno != ERANGE) {
+        out.is_int = true;
+        out.inum = v;
+      }
     }
     return true;
   }
@@ -252,6 +259,20 @@ int32_t dtype_of(const std::string& s) {
   if (s == "U8") return BSF8_DT_U8;
   return BSF8_DT_OTHER;
 }
+
+// Bytes per element of a safetensors dtype name, 0 when the name is unknown.
+int64_t dtype_bytes(const std::string& s) {
+  static const struct { const char* name; int64_t bytes; } table[] = {
+      {"BOOL", 1}, {"U8", 1}, {"I8", 1}, {"F8_E4M3", 1}, {"F8_E5M2", 1}, {"I16", 2}, {"U16", 2}, {"F16", 2},
+      {"BF16", 2}, {"I32", 4}, {"U32", 4}, {"F32", 4}, {"I64", 8}, {"U64", 8}, {"F64", 8}};
+  for (const auto& e : table)
+    if (s == e.name) return e.bytes;
+  return 0;
+}
+
+// The header's own bounds: every dimension below 2^31 (the validator and the
+// kernels index rows and columns with 32-bit integers).
+constexpr int64_t kMaxDim = int64_t(INT32_MAX);
 
 struct Entry {
   int32_t dtype;
@@ -347,12 +368,30 @@ bsf8_status bsf8_inspect_safetensors(const char* path, const bsf8_decl* decl, bs
     e.dtype = dtype_of(dt->str);
     e.rank = static_cast<int32_t>(sh->arr.size());
     if (e.rank > 4) e.rank = 4 + 1;   // reported as rank 5: refused below like any other bad rank
-    for (int i = 0; i < 4 && i < static_cast<int>(sh->arr.size()); ++i) {
-      if (!sh->arr[i].is_int || sh->arr[i].inum < 0)
-        return ifail(BSF8_E_INVALID_ARG, "%s: tensor '%s' has a bad shape", path, kv.first.c_str());
-      e.shape[i] = sh->arr[i].inum;
+    // every dimension an integer in [0, 2^31); the element count, with
+    // overflow checks, for the span check below
+    int64_t numel = 1;
+    for (size_t i = 0; i < sh->arr.size(); ++i) {
+      const Json& d = sh->arr[i];
+      if (!d.is_int || d.inum < 0 || d.inum > kMaxDim)
+        return ifail(BSF8_E_INVALID_ARG, "%s: tensor '%s' has a bad shape (dimension %zu not an integer in [0, 2^31))",
+                     path, kv.first.c_str(), i);
+      if (i < 4) e.shape[i] = d.inum;
+      if (numel != 0 && d.inum > INT64_MAX / numel)
+        return ifail(BSF8_E_INVALID_ARG, "%s: tensor '%s': element count overflows", path, kv.first.c_str());
+      numel *= d.inum;
     }
-    e.begin = int64_t(8 + hlen) + off->arr[0].inum;
+    // data_offsets [begin, end) relative to the end of the header: 0 <= begin
+    // <= end, and end - begin is the tensor's byte size when its dtype is known
+    const int64_t b0 = off->arr[0].inum, b1 = off->arr[1].inum;
+    if (b0 < 0 || b1 < b0 || b1 > INT64_MAX - int64_t(8 + hlen))
+      return ifail(BSF8_E_INVALID_ARG, "%s: tensor '%s' has data_offsets [%lld, %lld] out of order or range", path,
+                   kv.first.c_str(), (long long)b0, (long long)b1);
+    const int64_t esz = dtype_bytes(dt->str);
+    if (esz > 0 && (numel > INT64_MAX / esz || b1 - b0 != numel * esz))
+      return ifail(BSF8_E_INVALID_ARG, "%s: tensor '%s' spans %lld bytes, its dtype and shape need %lld", path,
+                   kv.first.c_str(), (long long)(b1 - b0), (long long)(numel > INT64_MAX / esz ? -1 : numel * esz));
+    e.begin = int64_t(8 + hlen) + b0;
     byname[kv.first] = e;
     order.push_back(kv.first);
   }

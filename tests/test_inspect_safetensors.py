@@ -190,3 +190,49 @@ def test_quant_config_refusals(text, name):
     with pytest.raises(B.BSF8Error) as e:
         B.parse_quant_config(text)
     assert e.value.name == name
+
+
+def _raw_file(tmp_path, name, header: dict, pad: int = 0):
+    body = json.dumps(header).encode()
+    p = os.path.join(str(tmp_path), name)
+    with open(p, "wb") as f:
+        f.write(struct.pack("<Q", len(body)) + body + b"\0" * pad)
+    return p
+
+
+GOOD_UNIT = {"down.weight": {"dtype": "F8_E4M3", "shape": [128, 256], "data_offsets": [0, 32768]},
+             "down.weight_scale_inv": {"dtype": "BF16", "shape": [1, 2], "data_offsets": [32768, 32772]}}
+
+
+@pytest.mark.parametrize("case,entry", [
+    ("negative_begin", {"dtype": "F8_E4M3", "shape": [128, 256], "data_offsets": [-16, 32752]}),
+    ("begin_after_end", {"dtype": "F8_E4M3", "shape": [128, 256], "data_offsets": [32768, 0]}),
+    ("span_too_short", {"dtype": "F8_E4M3", "shape": [128, 256], "data_offsets": [0, 32767]}),
+    ("span_too_long", {"dtype": "F8_E4M3", "shape": [128, 256], "data_offsets": [0, 65536]}),
+    ("dimension_2_31", {"dtype": "F8_E4M3", "shape": [2 ** 31, 1], "data_offsets": [0, 2 ** 31]}),
+    ("element_count_overflow", {"dtype": "F8_E4M3", "shape": [2 ** 31 - 1] * 3, "data_offsets": [0, 1]}),
+    ("offset_above_int64", {"dtype": "F8_E4M3", "shape": [128, 256], "data_offsets": [0, 10 ** 20]}),
+    ("dimension_above_int64", {"dtype": "F8_E4M3", "shape": [10 ** 19, 1], "data_offsets": [0, 1]}),
+    ("offset_near_int64_max", {"dtype": "U8", "shape": [16],
+                               "data_offsets": [2 ** 63 - 20, 2 ** 63 - 4]}),
+])
+def test_malformed_offsets_and_shapes_are_refused(tmp_path, case, entry):
+    """data_offsets must satisfy 0 <= begin <= end with end - begin = numel x element size,
+    every dimension must be an integer in [0, 2^31), and integers beyond int64 are not
+    integers: each such header is refused as malformed (no offset is ever returned)."""
+    hdr = dict(GOOD_UNIT)
+    hdr["down.weight"] = entry
+    p = _raw_file(tmp_path, f"{case}.safetensors", hdr)
+    with pytest.raises(B.BSF8Error) as e:
+        B.inspect_safetensors(p)
+    assert e.value.name == "INVALID_ARG", e.value
+
+
+def test_hand_written_header_verifies(tmp_path):
+    """The same hand-written header with consistent offsets verifies and reports the offsets."""
+    p = _raw_file(tmp_path, "ok.safetensors", GOOD_UNIT)
+    st, units = B.inspect_safetensors(p)
+    n = len(json.dumps(GOOD_UNIT).encode())
+    assert st == "OK" and len(units) == 1
+    assert units[0]["weight_offset"] == 8 + n and units[0]["scale_offset"] == 8 + n + 32768
+    assert units[0]["weight"]["shape"] == (128, 256) and units[0]["scale_inv"]["shape"] == (1, 2)
