@@ -1,40 +1,43 @@
 #!/usr/bin/env python3
 """Throughput of the block-scaled FP8 linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu] [--copy-calibration]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu] [--skip-extra] [--copy-calibration]
 
-One step is the dense-FFN prefill pass on M = 1024 synthetic tokens:
-quantize X_gate_up -> W8A8 GEMM on the fused gate/up weight (two members of
-[17408, 5120]) -> quantize X_down -> W8A8 GEMM on the down weight
-[5120, 17408], BF16 outputs.  ``value`` is the step's algorithmic FLOP rate,
-2*M*N*K summed over both GEMMs, over the step time (quantization included).
-The step runs as one HIP graph of its four calls, replayed back to back; the
-timed region is bracketed by HIP events on the replay stream.
+One step is the large prefill on M = 8192 synthetic tokens: quantize X
+[8192, 7168] per token in 1x128 groups, then the W8A8 GEMM against the block-FP8
+weight [18432, 7168] (heavy-tailed per-block scales) with its F32 epilogue and
+BF16 output.  ``value`` is the step's algorithmic FLOP rate, 2*M*N*K over the
+step time (quantization included).  The step runs as one HIP graph of its two
+calls, replayed back to back; the timed region is bracketed by HIP events on
+the replay stream, inputs resident in HBM.
+
+``roofline`` is the GEMM kernel alone: FLOPs per launch over its mean device
+time from a graph of back-to-back launches, against the dense FP8 MFMA peak,
+with the HBM traffic the profiled counters measured (profiles/traffic.json,
+reported only while the kernel source matches the hash it was measured on).
+``cpu_baseline`` is the oracle (NumPy) on the host cores, on 1024 of the 8192
+tokens of the same step (median of three).
 
 The same JSON line also carries:
-* ``roofline``: the gate/up GEMM, FLOPs per launch over its mean device time
-  (a graph of 20 back-to-back launches, timed with HIP events on the
-  replaying stream), against the dense FP8 MFMA peak;
+* ``dense_ffn_prefill``: the dense-FFN prefill pass at M = 1024 (quantize ->
+  W8A8 gate/up [2x17408, 5120] -> quantize -> W8A8 down [5120, 17408]) as a
+  graph of four calls, with each GEMM's roofline, the step over two weight
+  copies (``rotated``), and the chained form whose down input comes from the
+  gate/up output through ``quant_glu`` (``ffn_chain``);
 * ``decode_gemv`` (and ``decode_gemv_5000x4000``, ``qkv_decode``): the W8A16/F32
   arm at M in {1, 4, 8} on W [5120, 5120] (W [5000, 4000]; grouped Q/K/V at
   M = 1), rotating through >= 512 MiB of weight copies so the 256 MB Infinity
   Cache cannot serve them, per-launch median / p10 / p90 over 100 replays,
   with an HBM roofline on algorithmic bytes and a plain read of the same bytes
   (``bsf8_read_stream``) as context;
-* ``rotated``: the same step and GEMM calls with two copies of both weights
-  used in turn, so the weights come from HBM rather than the Infinity Cache
-  (the headline figures above are warm: one copy, reused every step);
-* ``qkv_prefill``: grouped Q/K/V W8A8 at M = 512;
-* ``large_prefill``: the W8A8 GEMM at M=8192, K=7168, N=18432, warm and
-  rotated over three weight copies;
+* ``qkv_w8a8_decode``: grouped Q/K/V through the W8A8 arm at M = 1, rotated;
+* ``qkv_prefill`` and ``qkv_w8a16_m512``: grouped Q/K/V at M = 512 through the
+  W8A8 and the W8A16/F32 arm;
+* ``rotated``: the headline GEMM over three weight copies used in turn;
 * ``dense_arm``: the resident=False arm on the grouped Q/K/V weight: the
   upcast to a dense BF16 copy (rotated over three weight copies, HBM roofline
   on its algorithmic bytes) and the dense BF16 product at M = 128 and 512
-  (BF16 MFMA roofline);
-* ``ffn_chain``: the same FFN with the down projection fed by the gate/up
-  output through ``quant_glu`` (gated SiLU and quantization in one pass);
-* ``cpu_baseline``: the oracle (NumPy) on the host cores, running the same
-  prefill step for about ten seconds, with the median time of each part.
+  (BF16 MFMA roofline).
 
 Inputs are seeded synthetic data (``synth``) already resident in HBM before
 timing starts.
@@ -83,10 +86,10 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the oracle's CPU baseline")
-    ap.add_argument("--skip-extra", action="store_true", help="leave out the decode and large-prefill lines")
+    ap.add_argument("--skip-extra", action="store_true", help="leave out every line but the headline step")
     ap.add_argument("--no-clock-sample", action="store_true",
                     help="do not run rocm-smi for the clock under load (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -391,24 +394,42 @@ def bench_qkv_prefill(torch, B, synth, dev):
                 describe=w.describe(B.ARM_W8A8, M))
 
 
-def bench_large(torch, B, synth, steps, dev):
+def bench_large_step(torch, B, synth, steps, warmup, dev):
+    """The headline: one step = quantize X [8192, 7168] -> W8A8 GEMM on W [18432, 7168] (BF16 out),
+    as one HIP graph replayed back to back; per-kernel device times from graphs of
+    back-to-back launches; the GEMM also over three weight copies used in turn."""
     log("large prefill: generating M=8192, K=7168, N=18432")
     wl = synth.config5()
     w = B.BlockFP8Weight([to_device_member(torch, m, dev) for m in wl.members])
     x = torch.from_numpy(wl.x).to(dev)
     M = wl.x.shape[0]
-    xq, xs = B.quant_act(x)
+    Kb = -(-w.K // 128)
+    xq = torch.empty((M, w.K), dtype=torch.uint8, device=dev)
+    xs = B.scales_kmajor(M, Kb, dev)
     y = torch.empty((M, w.n_total), dtype=torch.bfloat16, device=dev)
     ws = w.workspace(B.ARM_W8A8, M)
-    g_gemm = graph_of(torch, lambda: B.linear_w8a8(w, xq, xs, out=y, workspace=ws), 4)
-    g_quant = graph_of(torch, lambda: B.quant_act(x, xq, xs), 4)
-    settle(torch, g_gemm.replay)
-    ms = replay_ms(torch, g_gemm, max(3, steps // 4)) / 4
-    q_ms = replay_ms(torch, g_quant, 5) / 4
+    calls = {"quant": lambda: B.quant_act(x, xq, xs),
+             "gemm": lambda: B.linear_w8a8(w, xq, xs, out=y, workspace=ws)}
+
+    def step():
+        for f in calls.values():
+            f()
+    g_step = graph_of(torch, step)
+    settle(torch, g_step.replay)
+    for _ in range(warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    ms_step = replay_ms(torch, g_step, steps)
+    sclk = sample_sclk(torch, g_step, 400)
+    del g_step
+    stats = {}
+    for name, f, reps, n in (("gemm", calls["gemm"], 4, 10), ("quant", calls["quant"], 20, 20)):
+        g = graph_of(torch, f, reps)
+        settle(torch, g.replay, 0.3)
+        stats[name] = replay_stats(torch, g, n, reps)
+        del g
     flop = 2.0 * M * w.n_total * w.K
-    del g_gemm, g_quant
-    # rotated: three copies of the 132 MB weight, called in turn (396 MB > the
-    # 256 MB Infinity Cache)
+    # rotated: three copies of the 132 MB weight used in turn (396 MB > the 256 MB Infinity Cache)
     copies = [w] + [B.BlockFP8Weight([(t.clone(), sc.clone()) for t, sc in w.members]) for _ in range(2)]
     wss = [c.workspace(B.ARM_W8A8, M) for c in copies]
 
@@ -417,11 +438,116 @@ def bench_large(torch, B, synth, steps, dev):
             B.linear_w8a8(c, xq, xs, out=y, workspace=wsc)
     g_rot = graph_of(torch, rot)
     settle(torch, g_rot.replay, 0.5)
-    ms_rot = replay_ms(torch, g_rot, max(3, steps // 4)) / len(copies)
+    st_rot = replay_stats(torch, g_rot, 5, len(copies))
     del g_rot, copies
-    return dict(gemm_us=ms * 1e3, tflops=flop / (ms * 1e-3) / 1e12, frac=flop / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-                rotated_gemm_us=ms_rot * 1e3, rotated_tflops=flop / (ms_rot * 1e-3) / 1e12,
-                quant_us=q_ms * 1e3, describe=w.describe(B.ARM_W8A8, M))
+    us = lambda st: {k: (round(v * 1e3, 2) if k != "launches" else v) for k, v in st.items()}
+    quant_bytes = M * w.K * 4 + M * w.K + M * Kb * 4
+    return dict(M=M, N=w.n_total, K=w.K, flop=flop, ms_per_step=ms_step, sclk=sclk,
+                gemm_ms=stats["gemm"]["mean"], gemm_us_stats=us(stats["gemm"]), quant_us_stats=us(stats["quant"]),
+                quant_gbs=quant_bytes / (stats["quant"]["mean"] * 1e-3) / 1e9, quant_bytes=quant_bytes,
+                rotated_gemm_us_stats=us(st_rot),
+                describe=w.describe(B.ARM_W8A8, M),
+                fixture_sha256=synth.sha256_of(*(m.codes for m in wl.members), *(m.scale_bits for m in wl.members),
+                                               wl.x))
+
+
+def bench_qkv_w8a16_m512(torch, B, synth, dev):
+    """Grouped Q/K/V through the W8A16/F32 arm at M = 512 (config 4's second token count):
+    graphs of 20 back-to-back calls, F32 activations and output."""
+    wl = synth.config4(512)
+    w = B.BlockFP8Weight([to_device_member(torch, m, dev) for m in wl.members])
+    x = torch.from_numpy(wl.x).to(dev)
+    M = wl.x.shape[0]
+    y = torch.empty((M, w.n_total), dtype=torch.float32, device=dev)
+    g = graph_of(torch, lambda: B.linear_w8a16(w, x, out=y), 20)
+    settle(torch, g.replay, 0.3)
+    st = replay_stats(torch, g, 20, 20)
+    del g
+    flop = 2.0 * M * w.n_total * w.K
+    return dict(workload="grouped QKV W8A16/F32, members [6144|1000|1000, 5120], M=512, f32 x and y",
+                us=st["median"] * 1e3, us_p10=st["p10"] * 1e3, us_p90=st["p90"] * 1e3, us_mean=st["mean"] * 1e3,
+                launches=st["launches"], tflops=flop / (st["mean"] * 1e-3) / 1e12, flop=flop,
+                describe=w.describe(B.ARM_W8A16, M))
+
+
+def bench_w8a8_rotating(torch, B, members, x_np, dev, label):
+    """W8A8 at M = 1 (quantized once; the GEMM and its split-K reduction timed per call),
+    rotating through >= ROTATE_BYTES of weight copies so HBM serves the weights."""
+    per_copy = sum(m.codes.nbytes + m.scale_bits.nbytes for m in members)
+    copies = max(2, -(-ROTATE_BYTES // per_copy))
+    log(f"{label}: {copies} weight copies of {per_copy / 2**20:.1f} MiB")
+    base = [to_device_member(torch, m, dev) for m in members]
+    handles = [B.BlockFP8Weight([(w.clone(), sc.clone()) for w, sc in base]) for _ in range(copies)]
+    N = handles[0].n_total
+    K = handles[0].K
+    Kb = -(-K // 128)
+    M = x_np.shape[0]
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(dev)
+    xq, xs = B.quant_act(x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wss = [h.workspace(B.ARM_W8A8, M) for h in handles]
+
+    def run():
+        for h, wsh in zip(handles, wss):
+            B.linear_w8a8(h, xq, xs, out=y, workspace=wsh)
+    g = graph_of(torch, run)
+    settle(torch, g.replay, 0.3)
+    st = replay_stats(torch, g, 100, copies)
+    del g
+    grid = sum(-(-m.codes.shape[0] // 128) for m in members) * Kb
+    alg = N * K + 2 * grid + M * K + 4 * M * Kb + 2 * M * N
+    out = dict(workload=f"{label}: W [{N},{K}] ({len(members)} member(s)) + bf16 grid, quantized x, bf16 y, "
+                        f"rotating {copies} copies ({copies * per_copy >> 20} MiB)",
+               us=st["median"] * 1e3, us_p10=st["p10"] * 1e3, us_p90=st["p90"] * 1e3, us_mean=st["mean"] * 1e3,
+               launches=st["launches"], algorithmic_bytes=alg, gbs=alg / (st["mean"] * 1e-3) / 1e9,
+               describe=handles[0].describe(B.ARM_W8A8, M))
+    del handles
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline_large(synth, tokens=1024, reps=3):
+    """The oracle on the host cores on a bounded sample of the headline step: the first
+    ``tokens`` of the 8192 tokens quantized (NumPy float32, as defined) and multiplied
+    against all 18432 rows of the weight (float64, the oracle's row-chunked form),
+    ``reps`` times; the median time gives the rate."""
+    import oracle as O
+    wl = synth.config5()
+    om = [(m.codes, m.scale_f32()) for m in wl.members]
+    x = wl.x[:tokens]
+    N = sum(m.codes.shape[0] for m in wl.members)
+    K = x.shape[1]
+    times, parts = [], {"quant": [], "gemm": []}
+    for _ in range(reps):
+        ta = time.perf_counter()
+        xq, xs = O.quant_act(x)
+        tb = time.perf_counter()
+        for r0 in range(0, N, 1024):
+            O.linear_w8a8_rows(xq, xs, om, list(range(r0, min(N, r0 + 1024))))
+        tc = time.perf_counter()
+        times.append(tc - ta)
+        parts["quant"].append(tb - ta)
+        parts["gemm"].append(tc - tb)
+    t = statistics.median(times)
+    flop = 2.0 * tokens * N * K
+    threads, blas = _blas_info()
+    return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{tokens} of the 8192 tokens of the headline step (quantize + W8A8 GEMM over all {N} rows, "
+                      f"K={K}), float32 quantizer and float64 GEMM in NumPy, median of {reps} repetitions "
+                      f"({t:.2f} s each)",
+            "parts_s_median": {k: round(statistics.median(v), 3) for k, v in parts.items()},
+            "blas": blas, "host_cpus": os.cpu_count()}
+
+
+def _blas_info():
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+        blas = ",".join(sorted({d.get("internal_api", "?") for d in info if d.get("user_api") == "blas"})) or "none"
+    except Exception:
+        threads, blas = os.cpu_count() or 1, "unknown"
+    return int(threads), blas
 
 
 def bench_dense_arm(torch, B, synth, dev):
@@ -479,60 +605,6 @@ def copy_calibration(torch, dev):
                 launches=3)
 
 
-def cpu_baseline(synth, budget_s=10.0):
-    """The oracle on the host cores: the whole prefill step (both quantizations and
-    both W8A8 GEMMs, NumPy float64), repeated until about ``budget_s`` seconds."""
-    import oracle as O
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    gu = synth.config3_gate_up()
-    dn = synth.config3_down()
-    m_gu = [(m.codes, m.scale_f32()) for m in gu.members]
-    m_dn = [(m.codes, m.scale_f32()) for m in dn.members]
-    M, K_gu = gu.x.shape
-    K_dn = dn.x.shape[1]
-    flop = 2.0 * M * (sum(m.codes.shape[0] for m in gu.members) * K_gu + sum(m.codes.shape[0] for m in dn.members) * K_dn)
-    def gemm(xq, xs, members):
-        # every output row, 1024 rows at a time (the oracle's row form keeps the
-        # dequantized weight block small)
-        total = sum(m[0].shape[0] for m in members)
-        for r0 in range(0, total, 1024):
-            O.linear_w8a8_rows(xq, xs, members, list(range(r0, min(total, r0 + 1024))))
-
-    parts = {"quant_gate_up": [], "gemm_gate_up": [], "quant_down": [], "gemm_down": []}
-    reps, t0 = 0, time.perf_counter()
-    while reps == 0 or time.perf_counter() - t0 < budget_s:
-        ta = time.perf_counter()
-        xq, xs = O.quant_act(gu.x)
-        tb = time.perf_counter()
-        gemm(xq, xs, m_gu)
-        tc = time.perf_counter()
-        xq, xs = O.quant_act(dn.x)
-        td = time.perf_counter()
-        gemm(xq, xs, m_dn)
-        te = time.perf_counter()
-        for k, v in zip(parts, (tb - ta, tc - tb, td - tc, te - td)):
-            parts[k].append(v)
-        reps += 1
-    t = (time.perf_counter() - t0) / reps
-    blas = "unknown"
-    try:
-        import threadpoolctl
-        blas = ",".join(sorted({d.get("internal_api", "?") for d in threadpoolctl.threadpool_info()
-                                if d.get("user_api") == "blas"})) or "none"
-    except Exception:
-        pass
-    return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole prefill step (quantize + W8A8 gate/up + quantize + W8A8 down, M=1024) in float64 "
-                      f"NumPy, {reps} repetition(s), {t:.2f} s each",
-            "parts_s_median": {k: round(statistics.median(v), 3) for k, v in parts.items()},
-            "blas": blas, "host_cpus": os.cpu_count()}
-
-
 def main():
     a = parse()
     if a.no_clock_sample:
@@ -549,10 +621,14 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
 
-    pre = bench_prefill(torch, B, synth, a.steps, a.warmup, dev)
-    log(f"prefill {pre['tflops']:.1f} TFLOP/s/step, kernels {pre['kernels_ms']}")
+    big = bench_large_step(torch, B, synth, a.steps, a.warmup, dev)
+    log(f"large prefill step {big['ms_per_step']:.4f} ms, gemm {big['gemm_us_stats']}")
+    torch.cuda.empty_cache()
     extra = {}
     if not a.skip_extra:
+        extra["ffn"] = bench_prefill(torch, B, synth, a.steps, a.warmup, dev)
+        log(f"dense FFN step {extra['ffn']['ms_per_step']:.4f} ms, kernels {extra['ffn']['kernels_ms']}")
+        torch.cuda.empty_cache()
         c2 = synth.config2(8)
         extra["decode_gemv"] = bench_w8a16_rotating(torch, B, c2.members, c2.x, (1, 4, 8), dev, "decode 5120x5120")
         log(f"decode {extra['decode_gemv']['by_M']}")
@@ -561,70 +637,94 @@ def main():
                                                               "decode 5000x4000")
         c4 = synth.config4(1)
         extra["qkv_decode"] = bench_w8a16_rotating(torch, B, c4.members, c4.x, (1,), dev, "grouped QKV decode")
+        extra["qkv_w8a8_decode"] = bench_w8a8_rotating(torch, B, c4.members, c4.x, dev, "grouped QKV W8A8 M=1")
         extra["qkv_prefill"] = bench_qkv_prefill(torch, B, synth, dev)
-        torch.cuda.empty_cache()
-        extra["large_prefill"] = bench_large(torch, B, synth, a.steps, dev)
-        log(f"large {extra['large_prefill']}")
+        extra["qkv_w8a16_m512"] = bench_qkv_w8a16_m512(torch, B, synth, dev)
         torch.cuda.empty_cache()
         extra["dense_arm"] = bench_dense_arm(torch, B, synth, dev)
         log(f"dense arm {extra['dense_arm']}")
     if a.copy_calibration:
         extra["copy_calibration"] = copy_calibration(torch, dev)
-    cpu = None if a.skip_cpu else cpu_baseline(synth)
+    cpu = None if a.skip_cpu else cpu_baseline_large(synth)
 
-    gu_ms = pre["kernels_ms"]["gemm_gate_up"]
-    achieved = pre["flop_gate_up"] / (gu_ms * 1e-3) / 1e12
+    achieved = big["flop"] / (big["gemm_ms"] * 1e-3) / 1e12
     line = {
         "metric": "W8A8 block-FP8 prefill GEMM TFLOP/s (% FP8 MFMA peak); decode GEMV HBM GB/s",
-        "value": round(pre["tflops"], 2),
+        "value": round(big["flop"] / (big["ms_per_step"] * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(pre["ms_per_step"], 4),
+        "ms_per_step": round(big["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": "dense_ffn_prefill: quant + W8A8 gate/up [2x17408,5120] + quant + W8A8 down "
-                               "[5120,17408], M=1024 tokens, bf16 out",
-                   "M": pre["M"], "global_batch": pre["M"], "parallelism": "single_gpu",
-                   "act_scale_layout": "K-major (token index contiguous)"},
-        "roofline": {"bound": "mfma", "kernel": "w8a8_gemm (gate/up)", "achieved": round(achieved, 2),
+        "config": {"workload": "large_prefill: quantize X [8192,7168] per token 1x128 + W8A8 GEMM "
+                               "M=8192 K=7168 N=18432 (heavy-tailed block scales), bf16 out",
+                   "M": big["M"], "N": big["N"], "K": big["K"], "global_batch": big["M"],
+                   "parallelism": "single_gpu", "act_scale_layout": "K-major (token index contiguous)"},
+        "roofline": {"bound": "mfma", "kernel": "w8a8_gemm_fast (large prefill)", "achieved": round(achieved, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": profiled_traffic("w8a8_gemm_gate_up_m1024")},
+                     "traffic": profiled_traffic("w8a8_gemm_large_prefill_m8192"),
+                     "algorithmic": "2*M*N*K FLOP per launch over the launch's mean device time"},
         "cpu_baseline": cpu,
-        "kernels_ms": {k: round(v, 5) for k, v in pre["kernels_ms"].items()},
-        "kernels_us_stats": pre["kernels_us_stats"],
+        "kernels_us_stats": {"gemm": big["gemm_us_stats"], "quant": big["quant_us_stats"]},
+        "quant_gbs": round(big["quant_gbs"], 1),
+        "rotated": {"note": "three weight copies used in turn (396 MB > the 256 MB Infinity Cache)",
+                    "gemm_us_stats": big["rotated_gemm_us_stats"],
+                    "tflops": round(big["flop"] / (big["rotated_gemm_us_stats"]["mean"] * 1e-6) / 1e12, 2)},
         "device": {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
-                   "sclk_under_load": pre["sclk"]},
-        "gemm_down_tflops": round(pre["gemm_down_tflops"], 2),
-        "quant_gbs": {"gate_up": round(pre["quant_gate_up_gbs"], 1), "down": round(pre["quant_down_gbs"], 1)},
-        "path": {"gate_up": pre["describe_gate_up"], "down": pre["describe_down"]},
-        "rotated": {"note": "two copies of both weights, used in turn (534 MB > the 256 MB Infinity Cache)",
-                    "ms_per_step": round(pre["rotated"]["ms_per_step"], 4),
-                    "tflops": round(pre["rotated"]["tflops"], 2),
-                    "gemm_gate_up_tflops": round(pre["rotated"]["gemm_gate_up_tflops"], 2),
-                    "gemm_down_tflops": round(pre["rotated"]["gemm_down_tflops"], 2),
-                    "kernels_us_stats": pre["rotated"]["kernels_us_stats"]},
-        "ffn_chain": {"note": "quant -> W8A8 gate/up -> quant_glu (silu(gate)*up quantized in one pass) -> W8A8 down: "
-                              "the down input is the gate/up output",
-                      "ms_per_step": round(pre["ffn_chain"]["ms_per_step"], 4),
-                      "tflops": round(pre["ffn_chain"]["tflops"], 2),
-                      "quant_glu": {"us": round(pre["ffn_chain"]["glu_us"], 2),
-                                    "p10": round(pre["ffn_chain"]["glu_us_p10"], 2),
-                                    "p90": round(pre["ffn_chain"]["glu_us_p90"], 2),
-                                    "launches": pre["ffn_chain"]["glu_launches"],
-                                    "gbs": round(pre["ffn_chain"]["glu_gbs"], 1),
-                                    "bytes": pre["ffn_chain"]["glu_bytes"],
-                                    "frac_hbm": round(pre["ffn_chain"]["glu_gbs"] / HBM_PEAK_GBS, 4),
-                                    "traffic": profiled_traffic("quant_glu_ffn_m1024"),
-                                    "note": "bound by the ALU (an F64 exp and two IEEE F32 divisions per channel), "
-                                            "not by HBM"}},
-        "timing": "HIP graph replays: one replay per step; kernel times from graphs of 20 back-to-back launches",
-        "fixture_sha256": pre["fixture_sha256"],
+                   "sclk_under_load": big["sclk"]},
+        "path": big["describe"],
+        "timing": "HIP graph replays bracketed by HIP events on the replay stream: one replay per step; "
+                  "kernel times from graphs of back-to-back launches",
+        "fixture_sha256": big["fixture_sha256"],
     }
+
+    if "ffn" in extra:
+        pre = extra["ffn"]
+        gu_ms = pre["kernels_ms"]["gemm_gate_up"]
+        dn_ms = pre["kernels_ms"]["gemm_down"]
+        line["dense_ffn_prefill"] = {
+            "workload": "quant + W8A8 gate/up [2x17408,5120] + quant + W8A8 down [5120,17408], M=1024, bf16 out",
+            "ms_per_step": round(pre["ms_per_step"], 4), "tflops": round(pre["tflops"], 2),
+            "kernels_us_stats": pre["kernels_us_stats"],
+            "gemm_gate_up": {"tflops": round(pre["gemm_gate_up_tflops"], 2),
+                             "frac": round(pre["gemm_gate_up_tflops"] / FP8_PEAK_TFLOPS, 4),
+                             "traffic": profiled_traffic("w8a8_gemm_gate_up_m1024")},
+            "gemm_down": {"tflops": round(pre["gemm_down_tflops"], 2),
+                          "frac": round(pre["gemm_down_tflops"] / FP8_PEAK_TFLOPS, 4),
+                          "traffic": profiled_traffic("w8a8_gemm_down_m1024")},
+            "roofline": {"bound": "mfma", "kernel": "w8a8_gemm (gate/up, with its split-K reduction)",
+                         "achieved": round(pre["flop_gate_up"] / (gu_ms * 1e-3) / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pre["flop_gate_up"] / (gu_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                         "traffic": profiled_traffic("w8a8_gemm_gate_up_m1024")},
+            "quant_gbs": {"gate_up": round(pre["quant_gate_up_gbs"], 1), "down": round(pre["quant_down_gbs"], 1)},
+            "path": {"gate_up": pre["describe_gate_up"], "down": pre["describe_down"]},
+            "rotated": {"note": "two copies of both weights, used in turn (534 MB > the 256 MB Infinity Cache)",
+                        "ms_per_step": round(pre["rotated"]["ms_per_step"], 4),
+                        "tflops": round(pre["rotated"]["tflops"], 2),
+                        "gemm_gate_up_tflops": round(pre["rotated"]["gemm_gate_up_tflops"], 2),
+                        "gemm_down_tflops": round(pre["rotated"]["gemm_down_tflops"], 2),
+                        "kernels_us_stats": pre["rotated"]["kernels_us_stats"]},
+            "ffn_chain": {"note": "quant -> W8A8 gate/up -> quant_glu (silu(gate)*up quantized in one pass) -> "
+                                  "W8A8 down: the down input is the gate/up output",
+                          "ms_per_step": round(pre["ffn_chain"]["ms_per_step"], 4),
+                          "tflops": round(pre["ffn_chain"]["tflops"], 2),
+                          "quant_glu": {"us": round(pre["ffn_chain"]["glu_us"], 2),
+                                        "p10": round(pre["ffn_chain"]["glu_us_p10"], 2),
+                                        "p90": round(pre["ffn_chain"]["glu_us_p90"], 2),
+                                        "launches": pre["ffn_chain"]["glu_launches"],
+                                        "gbs": round(pre["ffn_chain"]["glu_gbs"], 1),
+                                        "bytes": pre["ffn_chain"]["glu_bytes"],
+                                        "frac_hbm": round(pre["ffn_chain"]["glu_gbs"] / HBM_PEAK_GBS, 4),
+                                        "traffic": profiled_traffic("quant_glu_ffn_m1024")}},
+            "fixture_sha256": pre["fixture_sha256"],
+        }
+        del gu_ms, dn_ms
+
     def decode_line(d, roofline_traffic=None):
         bm = d["by_M"]
         last = sorted(bm)[-1]
@@ -635,27 +735,38 @@ def main():
              "path": bm[last]["describe"],
              "frac_hbm_by_M": {k: round(v["gbs"] / HBM_PEAK_GBS, 4) for k, v in bm.items()},
              "path_by_M": {k: v["describe"].split("|")[1].strip() for k, v in bm.items()}}
-        if roofline_traffic is not False:
-            r["roofline"] = {"bound": "hbm", "kernel": f"w8a16 ({last})", "achieved": round(bm[last]["gbs"], 1),
-                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(bm[last]["gbs"] / HBM_PEAK_GBS, 4),
-                             "traffic": roofline_traffic}
+        r["roofline"] = {"bound": "hbm", "kernel": f"w8a16 ({last})", "achieved": round(bm[last]["gbs"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(bm[last]["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": roofline_traffic}
         return r
 
     if "decode_gemv" in extra:
         line["decode_gemv"] = decode_line(extra["decode_gemv"], profiled_traffic("w8a16_decode_5120x5120"))
-        line["decode_gemv_5000x4000"] = decode_line(extra["decode_gemv_5000x4000"], None)
-        line["qkv_decode"] = decode_line(extra["qkv_decode"], None)
+        line["decode_gemv_5000x4000"] = decode_line(extra["decode_gemv_5000x4000"],
+                                                    profiled_traffic("w8a16_decode_5000x4000"))
+        line["qkv_decode"] = decode_line(extra["qkv_decode"], profiled_traffic("w8a16_decode_qkv_m1"))
+        d = extra["qkv_w8a8_decode"]
+        line["qkv_w8a8_decode"] = {
+            "workload": d["workload"], "us": round(d["us"], 2), "p10": round(d["us_p10"], 2),
+            "p90": round(d["us_p90"], 2), "launches": d["launches"], "path": d["describe"],
+            "roofline": {"bound": "hbm", "kernel": "w8a8_gemm (M=1, with its split-K reduction)",
+                         "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": profiled_traffic("w8a8_qkv_m1"),
+                         "algorithmic_bytes": d["algorithmic_bytes"]}}
         q = extra["qkv_prefill"]
         line["qkv_prefill"] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in q.items()}
-    if "large_prefill" in extra:
-        l = extra["large_prefill"]
-        line["large_prefill"] = {"workload": "W8A8 GEMM M=8192 K=7168 N=18432, bf16 out",
-                                 "tflops": round(l["tflops"], 2), "frac": round(l["frac"], 4),
-                                 "gemm_us": round(l["gemm_us"], 1), "quant_us": round(l["quant_us"], 1),
-                                 "rotated": {"note": "three weight copies used in turn (396 MB)",
-                                             "gemm_us": round(l["rotated_gemm_us"], 1),
-                                             "tflops": round(l["rotated_tflops"], 2)},
-                                 "path": l["describe"]}
+        line["qkv_prefill"]["roofline"] = {"bound": "mfma", "kernel": "w8a8_gemm (QKV, M=512)",
+                                           "achieved": round(q["tflops"], 2), "peak": FP8_PEAK_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": round(q["tflops"] / FP8_PEAK_TFLOPS, 4),
+                                           "traffic": None}
+        q16 = extra["qkv_w8a16_m512"]
+        line["qkv_w8a16_m512"] = {
+            "workload": q16["workload"], "us": round(q16["us"], 2), "p10": round(q16["us_p10"], 2),
+            "p90": round(q16["us_p90"], 2), "launches": q16["launches"], "path": q16["describe"],
+            "roofline": {"bound": "mfma", "kernel": "w8a16 (general, M=512)", "achieved": round(q16["tflops"], 2),
+                         "peak": round(BF16_PEAK_TFLOPS / 3, 1), "unit": "TFLOP/s",
+                         "frac": round(q16["tflops"] / (BF16_PEAK_TFLOPS / 3), 4), "traffic": None,
+                         "peak_note": "exact F32 activations as three BF16 terms: a third of the BF16 MFMA peak"}}
     if "dense_arm" in extra:
         d = extra["dense_arm"]
         g512 = d["gemm"]["M512"]

@@ -17,8 +17,8 @@ import pytest
 import block_scaled_fp8_linear_amd as B
 import oracle as O
 import synth
-from gpu_util import (assert_within, banner, device, member_to_device, oracle_members, raw_member_to_device,
-                      sample_rows, to_np, torch)
+from gpu_util import (assert_within, banner, device, member_to_device, note_fixture, oracle_members,
+                      raw_member_to_device, record, sample_rows, sample_tokens, to_np, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -165,10 +165,14 @@ def test_quant_act_bit_exact(name):
     t = torch()
     x = quant_inputs(name)
     banner(f"quant_act {name} {x.shape}")
+    note_fixture(x=x)
     xq, xs = B.quant_act(t.from_numpy(x).to(device()))
     q_ref, s_ref = O.quant_act(x)
-    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     got = xq.cpu().numpy()
+    same_s = np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    record(f"quant_act {name}", same_s and np.array_equal(got, q_ref), kind="bit-exact",
+           oracle_sha256=synth.sha256_of(q_ref, s_ref)[:16], codes_differing=int((got != q_ref).sum()))
+    assert same_s
     assert np.array_equal(got, q_ref), f"{int((got != q_ref).sum())} codes differ"
 
 
@@ -219,6 +223,8 @@ def test_quant_act_scale_layouts():
 def test_w8a16_parity(name, out):
     t = torch()
     members, x = tax_case(name)
+    note_fixture(**{f"codes{i}": m.codes for i, m in enumerate(members)},
+                 **{f"scale{i}": m.scale_bits for i, m in enumerate(members)}, x=x)
     w, _keep = weight_on_device(members)
     banner(f"w8a16 {name} out={out} M={x.shape[0]} {w.describe(B.ARM_W8A16, x.shape[0])}")
     y = B.linear_w8a16(w, t.from_numpy(x).to(device()), out_dtype=t.float32 if out == "f32" else t.bfloat16)
@@ -231,6 +237,8 @@ def test_w8a16_parity(name, out):
 def test_w8a8_parity(name, out):
     t = torch()
     members, x = tax_case(name)
+    note_fixture(**{f"codes{i}": m.codes for i, m in enumerate(members)},
+                 **{f"scale{i}": m.scale_bits for i, m in enumerate(members)}, x=x)
     w, _keep = weight_on_device(members)
     xq, xs = O.quant_act(x)  # the GEMM is checked on the oracle's own quantized activations
     banner(f"w8a8 {name} out={out} M={x.shape[0]} {w.describe(B.ARM_W8A8, x.shape[0])}")
@@ -422,17 +430,19 @@ ARMS = {"decode_5120x5120_m1": ("w8a16", "w8a8"), "decode_5120x5120_m4": ("w8a16
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size_sampled(name):
-    """The workload at full size, in the configuration the bench times; outputs checked on sampled rows
-    (all tokens for those rows), quantization checked in full."""
+    """The workload at full size, in the configuration the bench times; outputs checked on sampled
+    rows and tokens (every 256-row tile of every member and every 256-token tile is visited, so
+    every work item of the GEMMs and every XCD group contributes), quantization checked in full."""
     t = torch()
     wl = FULL[name]()
+    note_fixture(**{f"codes{i}": m.codes for i, m in enumerate(wl.members)},
+                 **{f"scale{i}": m.scale_bits for i, m in enumerate(wl.members)}, x=wl.x)
     w, _keep = weight_on_device(wl.members)
     om = oracle_members(wl.members)
     rows = sample_rows(w.n_total, [m.codes.shape[0] for m in wl.members], 48)
     xd = t.from_numpy(wl.x).to(device())
     M = wl.x.shape[0]
-    tok = np.arange(M) if M <= 64 else np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M),
-                                                                  np.random.default_rng(1).integers(0, M, 48)]))
+    tok = sample_tokens(M)
     if "w8a16" in ARMS[name]:
         banner(f"full {name} w8a16: {w.describe(B.ARM_W8A16, M)}")
         y = to_np(B.linear_w8a16(w, xd))[np.ix_(tok, rows)]
@@ -448,35 +458,136 @@ def test_full_size_sampled(name):
         assert_within(y, ref, O.abs_bound_w8a8_rows(q_ref[tok], s_ref[tok], om, rows), True, name)
 
 
-@pytest.mark.parametrize("name,hard_rms", [("decode_5120x5120_m8", True), ("qkv_m1", True),
-                                           ("tiny_config1", False), ("large_prefill_m8192", False)])
+CROSS_ARM = [
+    # (workload, relative RMS <= 2 % required): the gate applies where the inputs carry the
+    # outlier-channel structure; on pure-Gaussian inputs E4M3 rounding alone exceeds 2 %, so
+    # there the GPU's figure must match the oracle's own on the same sample.
+    ("tiny_config1", False),
+    ("decode_5120x5120_m8", True),
+    ("decode_5000x4000_m8", True),
+    ("ffn_gate_up_m1024", True),
+    ("ffn_down_m1024", True),
+    ("qkv_m1", True),
+    ("qkv_m512", True),
+    ("large_prefill_m8192", False),
+]
+
+
+@pytest.mark.parametrize("name,hard_rms", CROSS_ARM, ids=[c[0] for c in CROSS_ARM])
 def test_cross_arm_gate(name, hard_rms):
-    """W8A8 vs W8A16 on the GPU: cosine >= 0.999; relative RMS <= 2% where the inputs carry the
-    outlier-channel structure, and equal to the oracle's own figure otherwise."""
+    """W8A8 against W8A16 on the GPU over the whole output of every workload, at full size
+    ("Module w8a8_prefill", section "ACCURACY"): cosine >= 0.999 everywhere; relative RMS
+    <= 2 % where the inputs carry outlier channels; and on sampled rows and tokens the GPU's
+    relative RMS equals the oracle's own within 5e-4 (the activation bytes are bit-exact, so
+    the two arms' disagreement is the method's, not the kernels')."""
     t = torch()
     if name == "tiny_config1":
         members, x = tax_case(name)
     else:
         wl = FULL[name]()
         members, x = wl.members, wl.x
-    if x.shape[0] > 512:
-        x = x[:512].copy()
+    note_fixture(**{f"codes{i}": m.codes for i, m in enumerate(members)},
+                 **{f"scale{i}": m.scale_bits for i, m in enumerate(members)}, x=x)
     w, _keep = weight_on_device(members)
     xd = t.from_numpy(x).to(device())
-    banner(f"cross-arm {name}")
-    y16 = B.linear_w8a16(w, xd).cpu().numpy()
+    M = x.shape[0]
+    banner(f"cross-arm {name} M={M}: {w.describe(B.ARM_W8A16, M)}")
+    y16 = B.linear_w8a16(w, xd)
     xq, xs = B.quant_act(xd)
-    y8 = B.linear_w8a8(w, xq, xs, out_dtype=t.float32).cpu().numpy()
+    y8 = B.linear_w8a8(w, xq, xs, out_dtype=t.float32)
+    del xd, xq, xs
+    y16 = y16.cpu().numpy()
+    y8 = y8.cpu().numpy()
     cos, rel = O.cross_arm_metrics(y8, y16)
     om = oracle_members(members)
-    q_ref, s_ref = O.quant_act(x)
-    rows = sample_rows(w.n_total, [m.codes.shape[0] for m in members], 256)
-    cos_o, rel_o = O.cross_arm_metrics(O.linear_w8a8_rows(q_ref, s_ref, om, rows), O.linear_w8a16_rows(x, om, rows))
-    cos_s, rel_s = O.cross_arm_metrics(y8[:, rows], y16[:, rows])
+    rows = sample_rows(w.n_total, [m.codes.shape[0] for m in members], 128)
+    tok = sample_tokens(M)
+    q_ref, s_ref = O.quant_act(x[tok])
+    cos_o, rel_o = O.cross_arm_metrics(O.linear_w8a8_rows(q_ref, s_ref, om, rows),
+                                       O.linear_w8a16_rows(x[tok], om, rows))
+    cos_s, rel_s = O.cross_arm_metrics(y8[np.ix_(tok, rows)], y16[np.ix_(tok, rows)])
+    ok = cos >= 0.999 and abs(rel_s - rel_o) <= 5e-4 and (rel <= 0.02 or not hard_rms)
+    record(f"cross-arm {name}", ok, kind="cross-arm", cosine=cos, relative_rms=rel, sample_relative_rms=rel_s,
+           oracle_sample_relative_rms=rel_o, oracle_sample_cosine=cos_o, hard_rms=hard_rms)
     assert cos >= 0.999, cos
     assert abs(rel_s - rel_o) <= 5e-4, (rel_s, rel_o)
     if hard_rms:
         assert rel <= 0.02, rel
+
+
+# ------------------------------------------- BF16 write-back is RNE of the F32 result
+
+def _bf16_bits(y):
+    return y.view(torch().int16).cpu().numpy().view(np.uint16)
+
+
+RNE_W8A16 = [
+    # (name, member rows, K, M): each W8A16 kernel
+    ("one_token", (300, 130), 1024, 1),
+    ("two_to_four_tokens", (300, 130), 1024, 3),
+    ("few_token_mfma", (300, 130), 1024, 6),
+    ("general_mfma", (300, 130), 1024, 40),
+    ("general_bytewise_k1000", (300, 130), 1000, 5),
+]
+
+
+@pytest.mark.parametrize("name,rows,K,M", RNE_W8A16, ids=[c[0] for c in RNE_W8A16])
+def test_w8a16_bf16_output_is_rne_of_f32_output(name, rows, K, M):
+    """The BF16 output of each W8A16 kernel is the F32 output of the same call rounded to
+    nearest-even, bit for bit ("FP8 Native Serving", section "Native FP8 vs dequant-to-BF16":
+    results become BF16 only when written back; the cast rounds to nearest even)."""
+    t = torch()
+    ms = [synth.random_code_weight(211, f"rne16_W{i}_{name}", r, K, scale_log2=(-9, -3)) for i, r in enumerate(rows)]
+    w, _keep = weight_on_device(ms)
+    x = synth.gaussian_activations(211, f"rne16_X_{name}", M, K)
+    xd = t.from_numpy(x).to(device())
+    banner(f"w8a16 RNE {name}: {w.describe(B.ARM_W8A16, M)}")
+    y32 = B.linear_w8a16(w, xd, out_dtype=t.float32).cpu().numpy()
+    y16 = _bf16_bits(B.linear_w8a16(w, xd, out_dtype=t.bfloat16))
+    want = O.f32_to_bf16_bits(y32)
+    differ = int(np.count_nonzero(y16 != want))
+    record(f"w8a16 bf16 rne {name}", differ == 0, kind="bit-exact", outputs=int(y32.size), differing=differ)
+    assert differ == 0, f"{differ} BF16 outputs are not RNE of the F32 output"
+
+
+RNE_W8A8 = [
+    # (name, member rows, K, M, code pitch pad, output pitch pad)
+    ("fast_whole_tiles", (300, 130), 1024, 300, 0, 0),
+    ("fast_split_k", (512,), 8192, 64, 0, 0),
+    ("register_staged", (300, 130), 1024, 300, 8, 0),
+    ("unaligned_output_pitch", (300, 130), 1024, 77, 0, 3),
+    ("nontemporal_stores", (8448,), 256, 8192, 0, 0),
+]
+
+
+@pytest.mark.parametrize("name,rows,K,M,qpad,ypad", RNE_W8A8, ids=[c[0] for c in RNE_W8A8])
+def test_w8a8_bf16_output_is_rne_of_f32_output(name, rows, K, M, qpad, ypad):
+    """Each W8A8 store path (staged 16-byte stores of whole tiles, the split-K reduction, the
+    register-staged kernel, element stores for an unaligned output pitch, and the
+    non-temporal stores of an output above 128 MB) writes BF16 outputs that are the F32
+    outputs of the same call rounded to nearest-even, bit for bit."""
+    t = torch()
+    ms = [synth.random_code_weight(213, f"rne8_W{i}_{name}", r, K) for i, r in enumerate(rows)]
+    w, _keep = weight_on_device(ms)
+    x = synth.gaussian_activations(213, f"rne8_X_{name}", M, K)
+    xq, xs = O.quant_act(x)
+    buf = t.zeros((M, K + qpad), dtype=t.uint8, device=device())
+    buf[:, :K] = t.from_numpy(xq).to(device())
+    xqd, xsd = buf[:, :K], t.from_numpy(xs).to(device())
+    N = w.n_total
+    d = w.describe(B.ARM_W8A8, M)
+    banner(f"w8a8 RNE {name}: {d}")
+    if name == "fast_split_k":
+        assert "split_k=1 " not in d, d
+    y32 = t.empty((M, N + ypad), dtype=t.float32, device=device())[:, :N]
+    y16 = t.empty((M, N + ypad), dtype=t.bfloat16, device=device())[:, :N]
+    B.linear_w8a8(w, xqd, xsd, out_dtype=t.float32, out=y32)
+    B.linear_w8a8(w, xqd, xsd, out_dtype=t.bfloat16, out=y16)
+    want = O.f32_to_bf16_bits(y32.cpu().numpy())
+    got = _bf16_bits(y16.contiguous())
+    differ = int(np.count_nonzero(got != want))
+    record(f"w8a8 bf16 rne {name}", differ == 0, kind="bit-exact", outputs=int(want.size), differing=differ)
+    assert differ == 0, f"{differ} BF16 outputs are not RNE of the F32 output"
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
