@@ -86,6 +86,9 @@ EXPORTS = [
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    ("bsf8_linear_w8a8_noalloc", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_describe", ctypes.c_char_p, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]),
     ("bsf8_read_stream", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     ("bsf8_parse_quant_config", ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Decl)]),
@@ -428,6 +431,31 @@ def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=N
     return y
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20   # BSF8_NOALLOC_SCRATCH_BYTES in include/bsf8.h
+
+
+def linear_w8a8_noalloc(w: BlockFP8Weight, xq, xs, out):
+    """linear_w8a8 for callers that cannot allocate: ``out`` (bfloat16 or float32 [M, >=N])
+    must be given, and split-K partials go to the library's fixed per-device scratch
+    instead of a workspace.  Calls that overlap in time on one device race."""
+    torch = _torch()
+    if out is None:
+        raise ValueError("out must be given: the no-allocation call allocates nothing")
+    _on_device(w.device, xq=xq, xs=xs, out=out)
+    Kb = -(-w.K // BLOCK)
+    if (xq.dim() != 2 or xq.shape[1] != w.K or xq.stride(1) != 1 or tuple(xs.shape) != (xq.shape[0], Kb)
+            or xs.dtype != torch.float32):
+        raise ValueError("xq must be [M, K] with unit column stride and xs float32 [M, ceil(K/128)]")
+    if not _codes_dtype_ok(xq):
+        raise ValueError("xq must be uint8 or float8_e4m3fn (the quantizer's E4M3 bytes)")
+    M = xq.shape[0]
+    y = _out(out, M, w.n_total, out.dtype, xq.device)
+    _check(lib().bsf8_linear_w8a8_noalloc(w.handle, xq.data_ptr(), xq.stride(0), xs.data_ptr(), xs.stride(0),
+                                          xs.stride(1), M, y.data_ptr(), _dt_of(y), y.stride(0),
+                                          _stream_ptr(xq.device)), "linear_w8a8_noalloc")
+    return y
+
+
 def upcast(w: BlockFP8Weight, out_dtype=None, out=None):
     """Dense copy [N, K] of the weight (bfloat16 unless out_dtype says float32): the resident=False load step."""
     torch = _torch()
@@ -473,7 +501,8 @@ def linear_dense(wd, x, out_dtype=None, out=None, workspace=None):
     return y
 
 
-__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "quant_glu", "linear_w8a16", "linear_w8a8", "upcast",
+__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "quant_glu", "linear_w8a16", "linear_w8a8",
+           "linear_w8a8_noalloc", "NOALLOC_SCRATCH_BYTES", "upcast",
            "linear_dense", "dense_workspace_size", "lib", "status_name", "ARM_W8A16", "ARM_W8A8", "ARM_DENSE",
            "EXPORTS", "LIB_PATH", "MAX_MEMBERS", "scales_kmajor"]
 

@@ -371,6 +371,26 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
                      workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+bsf8_status bsf8_linear_w8a8_noalloc(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs,
+                                     int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, int32_t y_dtype, int64_t ldy,
+                                     void* stream) {
+  if (w == nullptr) return fail(BSF8_E_INVALID_ARG, "null handle");
+  if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");
+  if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
+  if (M == 0) return BSF8_OK;
+  const size_t need = w8a8_workspace_bytes(w->dev, M);
+  if (need > size_t(BSF8_NOALLOC_SCRATCH_BYTES))
+    return fail(BSF8_E_WORKSPACE,
+                "this call needs %zu bytes of split-K partials; the no-allocation entry point holds %zu "
+                "(BSF8_NOALLOC_SCRATCH_BYTES): call bsf8_linear_w8a8 with a workspace instead",
+                need, size_t(BSF8_NOALLOC_SCRATCH_BYTES));
+  void* scratch = nullptr;
+  const bsf8_status st = w8a8_noalloc_scratch(&scratch);
+  if (st != BSF8_OK) return st;
+  return bsf8_linear_w8a8(w, xq, ldq, xs, xs_sm, xs_sk, M, y, y_dtype, ldy, scratch,
+                          size_t(BSF8_NOALLOC_SCRATCH_BYTES), stream);
+}
+
 bsf8_status bsf8_read_stream(const void* p, int64_t bytes, uint32_t* sink, void* stream) {
   if (p == nullptr || sink == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
   if (bytes < 0) return fail(BSF8_E_INVALID_ARG, "negative size");

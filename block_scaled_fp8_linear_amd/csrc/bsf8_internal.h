@@ -65,6 +65,9 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
                         int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M);
+// Device address of this device's copy of the no-allocation scratch array
+// (BSF8_NOALLOC_SCRATCH_BYTES bytes), looked up once per device.
+bsf8_status w8a8_noalloc_scratch(void** ptr);
 
 // Dense arm: the upcast copy and the BF16 GEMM over it (the fast W8A8 kernel's
 // dense instance).

@@ -26,7 +26,9 @@
 //    never stored.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1065,6 +1067,50 @@ bsf8_status launch_dense(const uint16_t* wd, int64_t N, int64_t K, const uint16_
   if (p.blocks == 0) return BSF8_OK;
   return launch_fast(p, w, true, reinterpret_cast<const uint8_t*>(x), 2 * ldx, nullptr, 0, 0, M, y, y_bf16, ldy,
                      ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry point (bsf8_linear_w8a8_noalloc): the
+// split-K partial tiles go here instead of a caller workspace.  Each device
+// holds its own copy of this array from the library's load until the process
+// ends.  Its name is only a host-side stand-in: kernels are given the device
+// address hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.  Nothing in it needs to start at zero (every split
+// writes the whole partial tile it later reads), and calls that overlap in
+// time on one device share it, so they race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[BSF8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+bsf8_status w8a8_noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices) {
+    set_error("DEVICE: device index %d beyond the %d the no-allocation scratch table covers", dev, kScratchDevices);
+    return BSF8_E_DEVICE;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+      if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255) != 0) {
+        set_error("DEVICE: the no-allocation scratch has no 256-byte aligned device address");
+        return BSF8_E_DEVICE;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return BSF8_OK;
 }
 
 bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,

@@ -306,6 +306,28 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bsf8_linear_w8a8_noalloc -- bsf8_linear_w8a8 without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, kernels and results as bsf8_linear_w8a8; where
+ * that call would use a workspace (split-K partial tiles), this one uses a
+ * fixed array of BSF8_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * every device it runs on until the process ends (its device address is looked
+ * up once per device, on the first call made with that device current).
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device race and must be ordered by the caller (one stream, or
+ * events).  Nothing in the array needs clearing between calls.
+ * Errors: as bsf8_linear_w8a8, and WORKSPACE when the call would need more than
+ * BSF8_NOALLOC_SCRATCH_BYTES of partials (bsf8_workspace_size with arm W8A8
+ * tells), before anything is launched; DEVICE when the array's address cannot
+ * be obtained.
+ */
+#define BSF8_NOALLOC_SCRATCH_BYTES (64u << 20)
+bsf8_status bsf8_linear_w8a8_noalloc(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs,
+                                     int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, int32_t y_dtype, int64_t ldy,
+                                     void* stream);
+
+/*
  * bsf8_describe -- one line naming the arithmetic and kernel configuration a
  * call with this handle, arm and M would run, with the handle's geometry.
  * ("Qwen checkpoints with block FP8 weights", block-path paragraph: report the
