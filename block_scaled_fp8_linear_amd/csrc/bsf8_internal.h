@@ -65,6 +65,12 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
                         int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M);
+// The W8A8 arm at one to four tokens runs the W8A16 file's streaming kernels
+// with E4M3 activations (no workspace).
+bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldq);
+std::string describe_w8a8_stream(const WeightDev& w, int64_t M);
+bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t xs_sm,
+                               int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
 // Device address of this device's copy of the no-allocation scratch array
 // (BSF8_NOALLOC_SCRATCH_BYTES bytes), looked up once per device.
 bsf8_status w8a8_noalloc_scratch(void** ptr);

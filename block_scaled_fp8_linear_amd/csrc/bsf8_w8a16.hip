@@ -100,7 +100,18 @@ struct Args {
   int32_t x_bf16;
   int32_t y_bf16;
   int32_t rows_per_block;   // few-token VALU kernels: rows of a block (at most 8 G)
+  // E4M3-activation instances (the W8A8 arm at one to four tokens): the
+  // per-token group scales, element (m, kb) at xs[m * xs_sm + kb * xs_sk]
+  const float* xs;
+  int64_t xs_sm;
+  int64_t xs_sk;
 };
+
+// Activation kinds of the few-token VALU kernels: F32 and BF16 activations (the
+// W8A16 arm), or E4M3 codes with per-token 1x128 group scales (the W8A8 arm:
+// the products of decoded codes are exact in F32, each chunk's partial is
+// scaled by activation scale x weight scale).
+constexpr int XK_F32 = 0, XK_BF16 = 1, XK_E4M3 = 2;
 
 template <bool SBF16>
 __device__ __forceinline__ float load_scale(const void* s, int64_t idx) {
@@ -667,8 +678,9 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 // ---------------------------------------------------------------------------
 constexpr int M1_MAX_G = 4;
 
-template <bool XBF16, bool SBF16, int G, int CPW>
+template <int XK, bool SBF16, int G, int CPW>
 __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
+  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
   __shared__ float red[WAVES][G * 8];
   const int tile = blockIdx.x;
   int mi = 0;
@@ -688,10 +700,10 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 
   const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
   const v4i rw = make_rsrc(mem.w, w_bytes);
-  constexpr uint32_t XE = XBF16 ? 2u : 4u;
+  constexpr uint32_t XE = XQ8 ? 1u : XBF16 ? 2u : 4u;
   const uint32_t x_bytes = uint32_t(K) * XE;
   const v4i rx = make_rsrc(a.x, x_bytes);
-  constexpr int XL = XBF16 ? 2 : 4;   // 16-byte activation loads per chunk piece
+  constexpr int XL = XQ8 ? 1 : XBF16 ? 2 : 4;   // 16-byte activation loads per chunk piece
 
   // ---- the chunk scales of the (at most two) grid rows the block's rows use,
   // issued first and without branches, so that waiting for them never waits
@@ -714,6 +726,10 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
       sc1[c] = static_cast<const uint32_t*>(mem.s)[i1];
     }
   }
+  // the token's group scale of each chunk (E4M3 activations)
+  float sa[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) sa[c] = XQ8 ? a.xs[int64_t(min(c_begin + c, Kb - 1)) * a.xs_sk] : 1.f;
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- every load of the wave: weights, activations (kept ahead of all arithmetic)
@@ -744,7 +760,18 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     float xv[16];
-    if (XBF16) {
+    if (XQ8) {
+      const uint32_t x4[4] = {xr[c][0].x, xr[c][0].y, xr[c][0].z, xr[c][0].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, true);
+        xv[4 * e] = lo[0];
+        xv[4 * e + 1] = lo[1];
+        xv[4 * e + 2] = hi[0];
+        xv[4 * e + 3] = hi[1];
+      }
+    } else if (XBF16) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const uint32_t w4[4] = {xr[c][q].x, xr[c][q].y, xr[c][q].z, xr[c][q].w};
@@ -779,7 +806,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
       const int r = row0 + 8 * g + rl;
       const uint32_t sb = (r >> 7) == srow ? sc0[c] : sc1[c];
       const float sw = __uint_as_float(SBF16 ? sb << 16 : sb);
-      acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), sw, acc[g]);
+      acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), XQ8 ? sa[c] * sw : sw, acc[g]);
     }
   }
   // ---- rows: the 8 lanes of a row, then the 8 waves in order
@@ -818,9 +845,16 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 // position read the same address).  Rows are summed over their 8 lanes by
 // shuffles and over the waves in LDS, in wave order.
 // ---------------------------------------------------------------------------
-template <bool XBF16, bool SBF16, int G, int CPW, int MT>
+// Activation slices in LDS carry 4 floats of padding after every 64: a lane
+// reads the 16 activations of its piece (lanes of one piece position read the
+// same address), and unpadded the eight piece positions, 256 bytes apart
+// modulo the 64 banks, met in pairs.
+__device__ __forceinline__ int xpad(int e) { return e + 4 * (e >> 6); }
+
+template <int XK, bool SBF16, int G, int CPW, int MT>
 __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
-  constexpr int XS = MT * CPW * CHUNK;   // F32 activations per wave
+  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
+  constexpr int XS = MT * CPW * CHUNK + 4 * (MT * CPW * CHUNK / 64);   // padded F32 activations per wave
   __shared__ __attribute__((aligned(16))) float xl[WAVES * XS];
   const int tile = blockIdx.x;
   int mi = 0;
@@ -841,7 +875,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
 
   const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
   const v4i rw = make_rsrc(mem.w, w_bytes);
-  constexpr uint32_t XE = XBF16 ? 2u : 4u;
+  constexpr uint32_t XE = XQ8 ? 1u : XBF16 ? 2u : 4u;
   const uint32_t x_bytes = uint32_t(a.M) * uint32_t(a.ldx) * XE;
   const v4i rx = make_rsrc(a.x, x_bytes);
 
@@ -863,6 +897,13 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
       sc1[c] = static_cast<const uint32_t*>(mem.s)[i1];
     }
   }
+  // each token's group scale of each chunk (E4M3 activations; tokens past M read token 0's)
+  float sa[CPW][MT];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      sa[c][t] = XQ8 ? a.xs[int64_t(t < a.M ? t : 0) * a.xs_sm + int64_t(min(c_begin + c, Kb - 1)) * a.xs_sk] : 1.f;
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- the wave's activation slice: MT tokens x CPW chunks, as 16-byte pieces
@@ -894,15 +935,24 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // ---- activations into this wave's LDS region, as F32: token t, element e of the slice at t * CPW*CHUNK + e
+  // ---- activations into this wave's LDS region, as F32: token t, element e of
+  // the slice at xpad(t * CPW*CHUNK + e) (a piece never crosses a padding point)
   float* xw = xl + wave * XS;
 #pragma unroll
   for (int i = 0; i < XPL; ++i) {
     const int piece = lane + 64 * i;
     if (piece < MT * PPT) {
       const int t = piece / PPT, pp = piece - t * PPT;
-      float* dst = xw + t * (CPW * CHUNK) + pp * EPP;
-      if (XBF16) {
+      float* dst = xw + xpad(t * (CPW * CHUNK) + pp * EPP);
+      if (XQ8) {
+        const uint32_t x4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, false);
+          const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, true);
+          reinterpret_cast<float4*>(dst)[e] = make_float4(lo[0], lo[1], hi[0], hi[1]);
+        }
+      } else if (XBF16) {
         const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
         reinterpret_cast<float4*>(dst)[0] = make_float4(__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xFFFF0000u),
                                                         __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xFFFF0000u));
@@ -923,26 +973,28 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
     for (int t = 0; t < MT; ++t) acc[g][t] = 0.f;
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
+    // the lane's 16 weights of each row group, decoded exactly (unscaled)
     float wd[G][16];
+    float sw[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int r = row0 + 8 * g + rl;
       const uint32_t sb = (r >> 7) == srow ? sc0[c] : sc1[c];
-      const float sw = __uint_as_float(SBF16 ? sb << 16 : sb);
+      sw[g] = __uint_as_float(SBF16 ? sb << 16 : sb);
       const uint32_t w4[4] = {wv[c][g].x, wv[c][g].y, wv[c][g].z, wv[c][g].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, false);
         const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, true);
-        wd[g][4 * e] = lo[0] * sw;
-        wd[g][4 * e + 1] = lo[1] * sw;
-        wd[g][4 * e + 2] = hi[0] * sw;
-        wd[g][4 * e + 3] = hi[1] * sw;
+        wd[g][4 * e] = lo[0];
+        wd[g][4 * e + 1] = lo[1];
+        wd[g][4 * e + 2] = hi[0];
+        wd[g][4 * e + 3] = hi[1];
       }
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const float* xp = xw + t * (CPW * CHUNK) + c * CHUNK + 16 * jp;
+      const float* xp = xw + xpad(t * (CPW * CHUNK) + c * CHUNK + 16 * jp);
       float xv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -952,10 +1004,18 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
         xv[4 * q + 2] = v.z;
         xv[4 * q + 3] = v.w;
       }
+      // the chunk partial of each row and token, then its scale (the block
+      // multiplier; times the token's group scale for E4M3 activations)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        float pa = 0.f, pb = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[g][t] = fmaf(xv[e], wd[g][e], acc[g][t]);
+        for (int e = 0; e < 16; e += 2) {
+          pa = fmaf(xv[e], wd[g][e], pa);
+          pb = fmaf(xv[e + 1], wd[g][e + 1], pb);
+        }
+        acc[g][t] = fmaf(pa + pb, XQ8 ? sa[c][t] * sw[g] : sw[g], acc[g][t]);
+      }
     }
   }
   // ---- rows: the 8 lanes of a row by shuffles; the waves through each wave's own region
@@ -1180,11 +1240,11 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     a.y_bf16 = y_bf16 ? 1 : 0;
     const bool sb = w.scale_bf16 != 0;
 #define BSF8_M1(G, C)                                                                                         \
-  (x_bf16 ? (sb ? w8a16_m1_kernel<true, true, G, C> : w8a16_m1_kernel<true, false, G, C>)                     \
-          : (sb ? w8a16_m1_kernel<false, true, G, C> : w8a16_m1_kernel<false, false, G, C>))
+  (x_bf16 ? (sb ? w8a16_m1_kernel<XK_BF16, true, G, C> : w8a16_m1_kernel<XK_BF16, false, G, C>)               \
+          : (sb ? w8a16_m1_kernel<XK_F32, true, G, C> : w8a16_m1_kernel<XK_F32, false, G, C>))
 #define BSF8_MT(G, T)                                                                                        \
-  (x_bf16 ? (sb ? w8a16_mt_kernel<true, true, G, 5, T> : w8a16_mt_kernel<true, false, G, 5, T>)                 \
-          : (sb ? w8a16_mt_kernel<false, true, G, 5, T> : w8a16_mt_kernel<false, false, G, 5, T>))
+  (x_bf16 ? (sb ? w8a16_mt_kernel<XK_BF16, true, G, 5, T> : w8a16_mt_kernel<XK_BF16, false, G, 5, T>)           \
+          : (sb ? w8a16_mt_kernel<XK_F32, true, G, 5, T> : w8a16_mt_kernel<XK_F32, false, G, 5, T>))
     auto k1 = M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
                                     : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5)))
             : (m1.g == 2 ? BSF8_MT(2, 4) : m1.g == 3 ? BSF8_MT(3, 4) : BSF8_MT(4, 4));
@@ -1242,6 +1302,66 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a16 launch");
+}
+
+// The W8A8 arm at one to four tokens: the same weight stream with E4M3
+// activations.  A decoded code times a decoded weight is exact in F32, so a
+// chunk partial is the method's block partial summed in another order, and
+// it is scaled by activation scale x weight scale as the F32 epilogue states.
+// At these token counts the 256 x 256 matrix-core tile would read the weight
+// for 1 to 4 useful columns out of 256.
+bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
+  if (!aligned || M * ldq >= (int64_t(1) << 31)) return false;
+  for (int i = 0; i < w.n_members; ++i)
+    if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) return false;
+  return m1_shape(w, true, M).g != 0;
+}
+
+std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
+  const M1Shape m1 = m1_shape(w, true, M);
+  char b[448];
+  snprintf(b, sizeof(b),
+           "arm=w8a8 arithmetic=e4m3 x e4m3 decoded exactly to f32, f32 fma chunk partials x (act scale x weight "
+           "scale) | kernel=%s<e4m3> rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all "
+           "loads first, 8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
+           M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
+           M <= 1 ? "" : ", 4-token activation slices in LDS", (long long)M, m1.tiles);
+  return b;
+}
+
+bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t xs_sm,
+                               int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
+  const M1Shape m1 = m1_shape(w, true, M);
+  if (m1.g == 0) {
+    set_error("UNSUPPORTED: the streaming W8A8 kernels take 1 to 4 tokens and K up to %d", WAVES * 5 * CHUNK);
+    return BSF8_E_UNSUPPORTED;
+  }
+  Args a{};
+  a.w = w;
+  a.tm = m1.tm;
+  a.x = xq;
+  a.y = y;
+  a.ldx = ldq;
+  a.ldy = ldy;
+  a.M = int32_t(M);
+  a.col_tiles = 1;
+  a.chunks_per_wave = m1.cpw;
+  a.rows_per_block = m1.rb;
+  a.x_bf16 = 0;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.xs = xs;
+  a.xs_sm = xs_sm;
+  a.xs_sk = xs_sk;
+  const bool sb = w.scale_bf16 != 0;
+#define BSF8_Q1(G, C) (sb ? w8a16_m1_kernel<XK_E4M3, true, G, C> : w8a16_m1_kernel<XK_E4M3, false, G, C>)
+#define BSF8_QT(G) (sb ? w8a16_mt_kernel<XK_E4M3, true, G, 5, 4> : w8a16_mt_kernel<XK_E4M3, false, G, 5, 4>)
+  auto k1 = M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_Q1(2, 4) : m1.g == 3 ? BSF8_Q1(3, 4) : BSF8_Q1(4, 4))
+                                  : (m1.g == 2 ? BSF8_Q1(2, 5) : m1.g == 3 ? BSF8_Q1(3, 5) : BSF8_Q1(4, 5)))
+                   : (m1.g == 2 ? BSF8_QT(2) : m1.g == 3 ? BSF8_QT(3) : BSF8_QT(4));
+#undef BSF8_Q1
+#undef BSF8_QT
+  hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
+  return device_status(hipGetLastError(), "w8a8 streaming launch");
 }
 
 }  // namespace bsf8

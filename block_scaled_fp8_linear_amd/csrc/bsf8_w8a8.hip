@@ -928,6 +928,7 @@ size_t w8a8_workspace_bytes(const WeightDev& w, int64_t M) {
 }
 
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
+  if (w8a8_stream_applies(w, aligned, M > 0 ? M : 1, w.K)) return describe_w8a8_stream(w, M > 0 ? M : 1);
   const Plan p = make_plan(w, aligned, M > 0 ? M : 1, w.K);
   char buf[320];
   if (p.fast)
@@ -1116,6 +1117,8 @@ bsf8_status w8a8_noalloc_scratch(void** ptr) {
 bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int64_t ldq, const float* xs,
                         int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
                         size_t ws_bytes, hipStream_t stream) {
+  if (w8a8_stream_applies(w, aligned, M, ldq))
+    return launch_w8a8_stream(w, xq, ldq, xs, xs_sm, xs_sk, M, y, y_bf16, ldy, stream);
   const Plan p = make_plan(w, aligned, M, ldq, (M - 1) * xs_sm + (w.Kb - 1) * xs_sk + 1);
   if (p.blocks == 0) return BSF8_OK;
   if (p.fast) return launch_fast(p, w, false, xq, ldq, xs, xs_sm, xs_sk, M, y, y_bf16, ldy, ws, ws_bytes, stream);

@@ -552,6 +552,8 @@ def test_w8a16_bf16_output_is_rne_of_f32_output(name, rows, K, M):
 
 RNE_W8A8 = [
     # (name, member rows, K, M, code pitch pad, output pitch pad)
+    ("streaming_one_token", (300, 130), 1024, 1, 0, 0),
+    ("streaming_three_tokens", (300, 130), 1024, 3, 0, 0),
     ("fast_whole_tiles", (300, 130), 1024, 300, 0, 0),
     ("fast_split_k", (512,), 8192, 64, 0, 0),
     ("register_staged", (300, 130), 1024, 300, 8, 0),
@@ -840,3 +842,44 @@ def test_w8a16_blocks_of_odd_row_counts(sdt, M):
     x = synth.gaussian_activations(197, f"odd_rows_X{M}", M, K)
     y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
     assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"odd rows {sdt} M={M}")
+
+
+@pytest.mark.parametrize("K", [384, 4000, 5120])
+@pytest.mark.parametrize("sdt", ["bf16", "f32"])
+def test_w8a8_few_tokens_streaming(K, sdt):
+    """The W8A8 arm at one to four tokens runs the streaming kernels with E4M3
+    activations (decoded exactly, chunk partials scaled by activation scale x weight
+    scale).  Grouped members of 200 and 70 rows (blocks straddling 128-row scale
+    blocks, a ragged last member), K with a partial last chunk (4000) and with every
+    wave's five chunks (5120), BF16 and F32 grids, token-major and K-major activation
+    scales: every output against the oracle."""
+    t = torch()
+    g = np.random.default_rng(227 + K)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    om = []
+    for r in (200, 70):
+        codes = finite[g.integers(0, finite.size, (r, K))]
+        sc = np.exp2(g.uniform(-10, -3, O.scale_grid_shape(r, K))).astype(np.float32)
+        if sdt == "bf16":
+            sc = O.f32_to_bf16(sc)
+        om.append((codes, sc))
+    dt = t.float32 if sdt == "f32" else t.bfloat16
+    w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.from_numpy(np.asarray(s, np.float32)).to(device()).to(dt))
+                          for c, s in om])
+    x_all = synth.gaussian_activations(227, f"stream8_X{K}", 4, K)
+    Kb = -(-K // 128)
+    for M in (1, 2, 3, 4):
+        x = x_all[:M]
+        xq, xs = O.quant_act(x)
+        d = w.describe(B.ARM_W8A8, M)
+        assert "<e4m3>" in d, d
+        ref, bound = O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om)
+        xqd = t.from_numpy(xq).to(device())
+        tm = t.from_numpy(xs).to(device())
+        km = t.from_numpy(np.ascontiguousarray(xs.T)).to(device()).t()
+        assert km.shape == (M, Kb) and (M == 1 or tuple(km.stride()) == (1, M))
+        for layout, xsd in (("token-major", tm), ("K-major", km)):
+            banner(f"w8a8 streaming K={K} {sdt} M={M} {layout}: {d}")
+            for odt in (t.float32, t.bfloat16):
+                y = to_np(B.linear_w8a8(w, xqd, xsd, out_dtype=odt))
+                assert_within(y, ref, bound, odt == t.bfloat16, f"w8a8 streaming K={K} M={M} {layout}")
