@@ -217,8 +217,10 @@ __device__ __forceinline__ v8bf cvt8(uint32_t lo, uint32_t hi) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <bool ALIGNED, bool XBF16, bool SBF16>
+template <bool ALIGNED, bool XBF16, bool SBF16, int RTT>
 __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
+  constexpr int RT = RTT;          // 16-row MFMA tiles per block (and per wave)
+  constexpr int ROWS = 16 * RT;    // weight rows per block (32 or 64: within one 128-row scale block)
   __shared__ __attribute__((aligned(16))) float red[WAVES][RT][64][4];
   __shared__ float srow[MAX_KB];   // this block's row of the scale grid
 
@@ -236,8 +238,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so the chunk loop is scalar
   const int l16 = lane & 15, gq = lane >> 4;
-  // Both 16-row tiles of a 32-row block lie in the same 128-row block, so the
-  // block uses one row of the member's scale grid: stage it in LDS once.
+  // The block's 16-row tiles lie in one 128-row block (ROWS divides 128), so
+  // the block uses one row of the member's scale grid: stage it in LDS once.
   {
     const int64_t sr = int64_t((rtile * ROWS) >> 7) * a.w.s_rs;
     for (int i = tid; i < Kb; i += THREADS) srow[i] = load_scale<SBF16>(mem.s, sr + int64_t(i) * a.w.s_cs);
@@ -354,18 +356,21 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 #pragma unroll
   for (int t = 0; t < RT; ++t) *reinterpret_cast<v4f*>(&red[wave][t][lane][0]) = acc[t];
   __syncthreads();
-  const int t = tid >> 8;             // row tile
-  const int ln = (tid >> 2) & 63;     // lane of that tile
-  const int r = tid & 3;              // element
-  float sum = 0.f;
 #pragma unroll
-  for (int w = 0; w < WAVES; ++w) sum += red[w][t][ln][r];
-  const int row = rtile * ROWS + t * 16 + 4 * (ln >> 4) + r;   // member-local output feature
-  const int mo = ct * COLS + (ln & 15);
-  if (row < mem.rows && mo < a.M) {
-    const int64_t off = int64_t(mo) * a.ldy + mem.col0 + row;
-    if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
-    else static_cast<float*>(a.y)[off] = sum;
+  for (int o = tid; o < RT * 256; o += THREADS) {
+    const int t = o >> 8;               // row tile
+    const int ln = (o >> 2) & 63;       // lane of that tile
+    const int r = o & 3;                // element
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[w][t][ln][r];
+    const int row = rtile * ROWS + t * 16 + 4 * (ln >> 4) + r;   // member-local output feature
+    const int mo = ct * COLS + (ln & 15);
+    if (row < mem.rows && mo < a.M) {
+      const int64_t off = int64_t(mo) * a.ldy + mem.col0 + row;
+      if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
+      else static_cast<float*>(a.y)[off] = sum;
+    }
   }
 }
 
@@ -405,7 +410,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //  the permutation of r & 7 that puts even rows on {0, 1, 4, 5} and odd rows on
 //  {2, 3, 6, 7}, so a fragment read's 16 lanes over two lane groups hit all 64
 //  banks once (with s(r) = (r >> 1) & 7 they collide in pairs);
-//  activation scratch: term u, token t at u * SM_TERM_BYTES + t * 256, piece p at p ^ t.
+//  activation scratch: term u, token t at u * SM_TERM_BYTES + t * 256, piece p at
+//  p ^ ((u M + t) & 15) (the column index of that term and token in its pass).
 // Per-chunk scaling and the wave-order reduction are those of the general
 // kernel.
 // ---------------------------------------------------------------------------
@@ -457,7 +463,12 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   const int xt = lane / LPT;                     // token within a compact load
   const int xk = (lane % LPT) * EPL;             // first K element of the lane in the chunk
   // B operand column of this lane in pass p: g = 16 p + l16 is term g / M of
-  // token g % M; columns past the last read the zero row of term 0
+  // token g % M; columns past the last read the zero row of term 0.  The
+  // 16-byte slots of term u's row of token t are permuted by the key
+  // (u M + t) & 15, which differs across the 16 columns of a pass, so a
+  // fragment read never meets two rows on one bank (term rows lie a multiple
+  // of 256 bytes apart); the zero row takes key 15, which no live column of
+  // its pass uses.
   int boff[NP], bkey[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
     const int tk = g - u * M;
     const bool ok = u < NT;
     boff[p] = ok ? u * SM_TERM_BYTES + tk * SM_ROW_BYTES : SM_ZERO_ROW * SM_ROW_BYTES;
-    bkey[p] = ok ? tk : SM_ZERO_ROW;
+    bkey[p] = ok ? g & 15 : 15;
   }
   // weight loads: lane L takes piece L & 7 of row (L >> 3) + 8 q of the wave's 32
   const int crow = lane >> 3;
@@ -552,10 +563,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 #pragma unroll
       for (int i = 0; i < NXI; ++i) {
         const int t = i * (64 / LPT) + xt;
-        const int pos = ((xk >> 3) ^ t) * 16 + (xk & 7) * 2;
-        uint8_t* dst = sc + t * SM_ROW_BYTES + pos;
+        // slot of this lane's 16-byte K piece in term u's row: piece ^ ((u M + t) & 15)
+        auto at = [&](int u) { return sc + u * SM_TERM_BYTES + t * SM_ROW_BYTES +
+                                      ((xk >> 3) ^ ((u * M + t) & 15)) * 16 + (xk & 7) * 2; };
         if (XBF16) {
-          *reinterpret_cast<uint4*>(dst) = xr[d][i];
+          *reinterpret_cast<uint4*>(at(0)) = xr[d][i];
         } else {
           const float v[4] = {__uint_as_float(xr[d][i].x), __uint_as_float(xr[d][i].y), __uint_as_float(xr[d][i].z),
                               __uint_as_float(xr[d][i].w)};
@@ -569,10 +581,10 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
             m[j] = mb;
             l[j] = __float_as_uint(r1 - __uint_as_float(mb));
           }
-          *reinterpret_cast<uint2*>(dst) = make_uint2((h[0] >> 16) | (h[1] & 0xFFFF0000u), (h[2] >> 16) | (h[3] & 0xFFFF0000u));
-          *reinterpret_cast<uint2*>(dst + SM_TERM_BYTES) =
+          *reinterpret_cast<uint2*>(at(0)) = make_uint2((h[0] >> 16) | (h[1] & 0xFFFF0000u), (h[2] >> 16) | (h[3] & 0xFFFF0000u));
+          *reinterpret_cast<uint2*>(at(1)) =
               make_uint2((m[0] >> 16) | (m[1] & 0xFFFF0000u), (m[2] >> 16) | (m[3] & 0xFFFF0000u));
-          *reinterpret_cast<uint2*>(dst + 2 * SM_TERM_BYTES) =
+          *reinterpret_cast<uint2*>(at(2)) =
               make_uint2((l[0] >> 16) | (l[1] & 0xFFFF0000u), (l[2] >> 16) | (l[3] & 0xFFFF0000u));
         }
       }
@@ -1057,7 +1069,13 @@ struct Plan {
   int col_tiles;
   int tiles;
   int chunks_per_wave;
+  int rt;   // general kernel: 16-row tiles per block
 };
+
+// The general kernel re-reads a block's tokens for every row block, so from
+// this many tokens on (aligned operands) it takes 64-row blocks: half the
+// activation traffic per weight byte, twice the matrix work per split.
+constexpr int GEN_WIDE_M = 64;
 
 // Compute units of the current device (cached per device).
 int w16_device_cus() {
@@ -1156,13 +1174,15 @@ SmallShape small_shape(const WeightDev& w) {
   return sh;
 }
 
-Plan make_plan(const WeightDev& w, int64_t M) {
+Plan make_plan(const WeightDev& w, int64_t M, bool aligned = false) {
   Plan p{};
+  p.rt = aligned && M >= GEN_WIDE_M ? 4 : RT;
+  const int rows = 16 * p.rt;
   p.col_tiles = int((M + COLS - 1) / COLS);
   int t = 0;
   for (int i = 0; i < w.n_members; ++i) {
     p.tm.tile0[i] = t;
-    p.tm.n_tiles[i] = (w.m[i].rows + ROWS - 1) / ROWS;
+    p.tm.n_tiles[i] = (w.m[i].rows + rows - 1) / rows;
     t += p.tm.n_tiles[i] * p.col_tiles;
   }
   p.tm.tile0[w.n_members] = t;
@@ -1193,7 +1213,7 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
              (long long)(M > 0 ? M : 1), m1.tiles);
     return b1;
   }
-  const Plan p = make_plan(w, M > 0 ? M : 1);
+  const Plan p = make_plan(w, M > 0 ? M : 1, aligned);
   const bool small = aligned && M >= 1 && M <= SM_MAXM;
   char ring[160] = "";
   if (small)
@@ -1205,7 +1225,7 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
            "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
            "mfma_f32_16x16x32_bf16 | kernel=%s rows=%d tokens=%d waves=%d (in-block split-K, %d chunks/wave%s) "
            "path=%s | M=%lld blocks=%d",
-           small ? "w8a16_small_m" : "w8a16", small ? small_shape(w).rb : ROWS, small ? SM_MAXM : COLS, WAVES,
+           small ? "w8a16_small_m" : "w8a16", small ? small_shape(w).rb : 16 * p.rt, small ? SM_MAXM : COLS, WAVES,
            p.chunks_per_wave, ring, aligned ? "aligned16" : "bytewise", (long long)M,
            small ? small_shape(w).tiles : p.tiles);
   return buf;
@@ -1213,7 +1233,6 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
 
 bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x_bf16, int64_t M, int64_t ldx,
                          void* y, bool y_bf16, int64_t ldy, void*, size_t, hipStream_t stream) {
-  const Plan p = make_plan(w, M);
   if (w.Kb > MAX_KB) {
     set_error("UNSUPPORTED: K above %d", MAX_KB * CHUNK);
     return BSF8_E_UNSUPPORTED;
@@ -1222,6 +1241,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   if (M * ldx * (x_bf16 ? 2 : 4) >= (int64_t(1) << 31)) aligned = false;
   for (int i = 0; i < w.n_members; ++i)
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) aligned = false;
+  const Plan p = make_plan(w, M, aligned);
   if (p.tiles == 0) return BSF8_OK;
   const M1Shape m1 = m1_shape(w, aligned, M);
   if (m1.g) {
@@ -1265,7 +1285,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   a.chunks_per_wave = p.chunks_per_wave;
   a.x_bf16 = x_bf16 ? 1 : 0;
   a.y_bf16 = y_bf16 ? 1 : 0;
-  auto kern = w8a16_kernel<true, false, true>;
+  auto kern = w8a16_kernel<true, false, true, RT>;
   const bool sb = w.scale_bf16 != 0;
   int grid = p.tiles;
   if (aligned && M <= SM_MAXM) {
@@ -1293,12 +1313,15 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
                  : (sb ? w8a16_small_m_kernel<false, true, 4, 2, 3> : w8a16_small_m_kernel<false, false, 4, 2, 3>);
     }
 #undef BSF8_SMALL
+  } else if (aligned && p.rt == 4) {
+    if (x_bf16) kern = sb ? w8a16_kernel<true, true, true, 4> : w8a16_kernel<true, true, false, 4>;
+    else kern = sb ? w8a16_kernel<true, false, true, 4> : w8a16_kernel<true, false, false, 4>;
   } else if (aligned) {
-    if (x_bf16) kern = sb ? w8a16_kernel<true, true, true> : w8a16_kernel<true, true, false>;
-    else kern = sb ? w8a16_kernel<true, false, true> : w8a16_kernel<true, false, false>;
+    if (x_bf16) kern = sb ? w8a16_kernel<true, true, true, RT> : w8a16_kernel<true, true, false, RT>;
+    else kern = sb ? w8a16_kernel<true, false, true, RT> : w8a16_kernel<true, false, false, RT>;
   } else {
-    if (x_bf16) kern = sb ? w8a16_kernel<false, true, true> : w8a16_kernel<false, true, false>;
-    else kern = sb ? w8a16_kernel<false, false, true> : w8a16_kernel<false, false, false>;
+    if (x_bf16) kern = sb ? w8a16_kernel<false, true, true, RT> : w8a16_kernel<false, true, false, RT>;
+    else kern = sb ? w8a16_kernel<false, false, true, RT> : w8a16_kernel<false, false, false, RT>;
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a16 launch");

@@ -527,6 +527,7 @@ RNE_W8A16 = [
     ("two_to_four_tokens", (300, 130), 1024, 3),
     ("few_token_mfma", (300, 130), 1024, 6),
     ("general_mfma", (300, 130), 1024, 40),
+    ("general_mfma_64_row_blocks", (300, 130), 1024, 96),
     ("general_bytewise_k1000", (300, 130), 1000, 5),
 ]
 
