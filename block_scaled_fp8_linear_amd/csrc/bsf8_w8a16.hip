@@ -845,6 +845,196 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 
 
 // ---------------------------------------------------------------------------
+// One token with a long K (more than five chunks per wave, e.g. an FFN down
+// projection at decode, K = 17408): the one-token kernel's layout, but a wave
+// keeps a ring of D chunk slots in flight instead of issuing all of its loads
+// at once.  Each slot's loads (the row groups' 16-byte pieces and the lane's
+// activations) are issued together and slots in chunk order; after a chunk is
+// used its slot is refilled with the chunk D further on (loads retire in
+// issue order, so waiting for one chunk never waits for a later one), and
+// chunks past the wave's range read past-the-end offsets (zeros, no traffic).
+// The weight scales (and the token's activation scales for E4M3 activations)
+// of the wave's chunks are loaded first, one chunk per lane, and picked per
+// chunk with a lane read.
+// ---------------------------------------------------------------------------
+constexpr int M1R_DEPTH = 4;
+
+template <int XK, bool SBF16, int G, int D>
+__global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
+  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
+  __shared__ float red[WAVES][G * 8];
+  const int tile = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
+  const int rtile = tile - a.tm.tile0[mi];
+  const MemberDev mem = a.w.m[mi];
+  const int K = a.w.K, Kb = a.w.Kb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jp = lane & 7;
+  const int rl = lane >> 3;
+  const int row0 = rtile * a.rows_per_block;
+  const int rend = min(mem.rows, row0 + a.rows_per_block);
+  const int c_begin = min(Kb, wave * a.chunks_per_wave);
+  const int c_end = min(Kb, c_begin + a.chunks_per_wave);
+
+  const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
+  const v4i rw = make_rsrc(mem.w, w_bytes);
+  constexpr uint32_t XE = XQ8 ? 1u : XBF16 ? 2u : 4u;
+  const uint32_t x_bytes = uint32_t(K) * XE;
+  const v4i rx = make_rsrc(a.x, x_bytes);
+  constexpr int XL = XQ8 ? 1 : XBF16 ? 2 : 4;
+
+  // ---- scales of the wave's chunks, chunk c_begin + 64 h + lane in register h
+  const int nb = (mem.rows + 127) >> 7;
+  const int srow = row0 >> 7;
+  const int srow1 = min(srow + 1, nb - 1);
+  uint32_t s0[SM_SCALE_REGS], s1[SM_SCALE_REGS];
+  float sav[SM_SCALE_REGS];
+#pragma unroll
+  for (int h = 0; h < SM_SCALE_REGS; ++h) {
+    const int chunk = min(c_begin + 64 * h + lane, Kb - 1);
+    const int64_t i0 = int64_t(srow) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
+    const int64_t i1 = int64_t(srow1) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
+    if (SBF16) {
+      s0[h] = static_cast<const uint16_t*>(mem.s)[i0];
+      s1[h] = static_cast<const uint16_t*>(mem.s)[i1];
+    } else {
+      s0[h] = static_cast<const uint32_t*>(mem.s)[i0];
+      s1[h] = static_cast<const uint32_t*>(mem.s)[i1];
+    }
+    sav[h] = XQ8 ? a.xs[int64_t(chunk) * a.xs_sk] : 1.f;
+  }
+  // raw bits of chunk c's scale for grid row v (c - c_begin is wave-uniform); 0 past the range
+  auto wscale = [&](int c, int v) {
+    const int i = c - c_begin;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int h = 0; h < SM_SCALE_REGS; ++h)
+      if ((i >> 6) == h) bits = __builtin_amdgcn_readlane(v ? s1[h] : s0[h], i & 63);
+    return c < c_end ? __uint_as_float(SBF16 ? bits << 16 : bits) : 0.f;
+  };
+  auto ascale = [&](int c) {
+    const int i = c - c_begin;
+    float v = 1.f;
+#pragma unroll
+    for (int h = 0; h < SM_SCALE_REGS; ++h)
+      if ((i >> 6) == h) v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sav[h]), i & 63));
+    return v;
+  };
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint4 wv[D][G];
+  uint4 xr[D][XL];
+  auto issue = [&](int c, int d) {
+    const int k = c * CHUNK + 16 * jp;
+    const bool live = c < c_end && k < K;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int r = row0 + 8 * g + rl;
+      const uint32_t off = live && r < rend ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
+      wv[d][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, 0));
+    }
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+      const uint32_t off = live ? uint32_t(k) * XE + 16u * q : x_bytes;
+      xr[d][q] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    issue(c_begin + d, d);
+    __builtin_amdgcn_sched_barrier(0);   // keep the slots in chunk order
+  }
+
+  float acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = 0.f;
+  for (int c0 = c_begin; c0 < c_end; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int c = c0 + d;
+      const float sw0 = wscale(c, 0), sw1 = wscale(c, 1);
+      const float sa = XQ8 ? ascale(c) : 1.f;
+      float xv[16];
+      if (XQ8) {
+        const uint32_t x4[4] = {xr[d][0].x, xr[d][0].y, xr[d][0].z, xr[d][0].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, false);
+          const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, true);
+          xv[4 * e] = lo[0];
+          xv[4 * e + 1] = lo[1];
+          xv[4 * e + 2] = hi[0];
+          xv[4 * e + 3] = hi[1];
+        }
+      } else if (XBF16) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t w4[4] = {xr[d][q].x, xr[d][q].y, xr[d][q].z, xr[d][q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xv[8 * q + 2 * e] = __uint_as_float(w4[e] << 16);
+            xv[8 * q + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv[4 * q] = __uint_as_float(xr[d][q].x);
+          xv[4 * q + 1] = __uint_as_float(xr[d][q].y);
+          xv[4 * q + 2] = __uint_as_float(xr[d][q].z);
+          xv[4 * q + 3] = __uint_as_float(xr[d][q].w);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t w4[4] = {wv[d][g].x, wv[d][g].y, wv[d][g].z, wv[d][g].w};
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, false);
+          const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, true);
+          p[0] = fmaf(xv[4 * e], lo[0], p[0]);
+          p[1] = fmaf(xv[4 * e + 1], lo[1], p[1]);
+          p[2] = fmaf(xv[4 * e + 2], hi[0], p[2]);
+          p[3] = fmaf(xv[4 * e + 3], hi[1], p[3]);
+        }
+        const int r = row0 + 8 * g + rl;
+        const float sw = (r >> 7) == srow ? sw0 : sw1;
+        acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), XQ8 ? sa * sw : sw, acc[g]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(c + D, d);   // refill this slot
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // ---- rows: the 8 lanes of a row, then the 8 waves in order
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    acc[g] += __shfl_xor(acc[g], 1);
+    acc[g] += __shfl_xor(acc[g], 2);
+    acc[g] += __shfl_xor(acc[g], 4);
+    if (jp == 0) red[wave][8 * g + rl] = acc[g];
+  }
+  __syncthreads();
+  if (tid < G * 8) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[w][tid];
+    const int row = row0 + tid;
+    if (row < rend) {
+      const int64_t off = mem.col0 + row;
+      if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
+      else static_cast<float*>(a.y)[off] = sum;
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
 // Two to four tokens (aligned operands, K <= 5120): the one-token kernel's
 // layout with the activations in LDS.  Each wave copies the slice it uses
 // (MT tokens x its chunk range, widened to F32) into a wave-private LDS
@@ -1097,6 +1287,7 @@ struct M1Shape {
   int g;
   int rb;
   int cpw;
+  bool ring;   // one token, more than five chunks per wave: the ring kernel
   TileMap tm;
   int tiles;
 };
@@ -1105,8 +1296,13 @@ M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
   M1Shape m{};
   // (at five to eight tokens the FMAs and activation reads outweigh the MFMA
   // kernel's transpose: 15.4 against 15.0 us for 8 tokens of W [5120,5120])
-  if (!aligned || M < 1 || M > 4 || w.Kb > WAVES * 5) return m;
-  m.cpw = M == 1 && w.Kb <= WAVES * 4 ? 4 : 5;
+  if (!aligned || M < 1 || M > 4) return m;
+  // a K of more than five chunks per wave: one token takes the ring kernel,
+  // two to four the few-token MFMA kernel (their activation slices would not
+  // fit the LDS)
+  m.ring = w.Kb > WAVES * 5;
+  if (m.ring && M != 1) return m;
+  m.cpw = m.ring ? (w.Kb + WAVES - 1) / WAVES : M == 1 && w.Kb <= WAVES * 4 ? 4 : 5;
   // One token: the fewest rows in [16, 32] that keep the grid within one
   // block per compute unit, so every unit streams about the same bytes
   // (W [5120, 5120]: 20 rows, 256 blocks, 9.3 -> 8.8 us; whole 8-row groups
@@ -1206,10 +1402,10 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
     char b1[448];
     snprintf(b1, sizeof(b1),
              "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), f32 fma accumulate | "
-             "kernel=%s rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all loads first, "
+             "kernel=%s rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, %s, "
              "8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
-             M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
-             M <= 1 ? "" : ", 4-token activation slices in LDS",
+             m1.ring ? "w8a16_m1_ring" : M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
+             m1.ring ? "4-chunk load ring" : "all loads first", M <= 1 ? "" : ", 4-token activation slices in LDS",
              (long long)(M > 0 ? M : 1), m1.tiles);
     return b1;
   }
@@ -1265,11 +1461,16 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
 #define BSF8_MT(G, T)                                                                                        \
   (x_bf16 ? (sb ? w8a16_mt_kernel<XK_BF16, true, G, 5, T> : w8a16_mt_kernel<XK_BF16, false, G, 5, T>)           \
           : (sb ? w8a16_mt_kernel<XK_F32, true, G, 5, T> : w8a16_mt_kernel<XK_F32, false, G, 5, T>))
-    auto k1 = M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
-                                    : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5)))
-            : (m1.g == 2 ? BSF8_MT(2, 4) : m1.g == 3 ? BSF8_MT(3, 4) : BSF8_MT(4, 4));
+#define BSF8_MR(G)                                                                                              \
+  (x_bf16 ? (sb ? w8a16_m1_ring_kernel<XK_BF16, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_BF16, false, G, M1R_DEPTH>) \
+          : (sb ? w8a16_m1_ring_kernel<XK_F32, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_F32, false, G, M1R_DEPTH>))
+    auto k1 = m1.ring ? (m1.g == 2 ? BSF8_MR(2) : m1.g == 3 ? BSF8_MR(3) : BSF8_MR(4))
+              : M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
+                                      : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5)))
+                       : (m1.g == 2 ? BSF8_MT(2, 4) : m1.g == 3 ? BSF8_MT(3, 4) : BSF8_MT(4, 4));
 #undef BSF8_M1
 #undef BSF8_MT
+#undef BSF8_MR
     hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
     return device_status(hipGetLastError(), "w8a16_m1 launch");
   }
@@ -1345,10 +1546,11 @@ std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
   char b[448];
   snprintf(b, sizeof(b),
            "arm=w8a8 arithmetic=e4m3 x e4m3 decoded exactly to f32, f32 fma chunk partials x (act scale x weight "
-           "scale) | kernel=%s<e4m3> rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all "
-           "loads first, 8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
-           M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
-           M <= 1 ? "" : ", 4-token activation slices in LDS", (long long)M, m1.tiles);
+           "scale) | kernel=%s<e4m3> rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, %s, "
+           "8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
+           m1.ring ? "w8a16_m1_ring" : M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
+           m1.ring ? "4-chunk load ring" : "all loads first", M <= 1 ? "" : ", 4-token activation slices in LDS",
+           (long long)M, m1.tiles);
   return b;
 }
 
@@ -1356,7 +1558,8 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
                                int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
   const M1Shape m1 = m1_shape(w, true, M);
   if (m1.g == 0) {
-    set_error("UNSUPPORTED: the streaming W8A8 kernels take 1 to 4 tokens and K up to %d", WAVES * 5 * CHUNK);
+    set_error("UNSUPPORTED: the streaming W8A8 kernels take one token, or 2 to 4 tokens with K up to %d",
+              WAVES * 5 * CHUNK);
     return BSF8_E_UNSUPPORTED;
   }
   Args a{};
@@ -1378,11 +1581,15 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
   const bool sb = w.scale_bf16 != 0;
 #define BSF8_Q1(G, C) (sb ? w8a16_m1_kernel<XK_E4M3, true, G, C> : w8a16_m1_kernel<XK_E4M3, false, G, C>)
 #define BSF8_QT(G) (sb ? w8a16_mt_kernel<XK_E4M3, true, G, 5, 4> : w8a16_mt_kernel<XK_E4M3, false, G, 5, 4>)
-  auto k1 = M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_Q1(2, 4) : m1.g == 3 ? BSF8_Q1(3, 4) : BSF8_Q1(4, 4))
-                                  : (m1.g == 2 ? BSF8_Q1(2, 5) : m1.g == 3 ? BSF8_Q1(3, 5) : BSF8_Q1(4, 5)))
-                   : (m1.g == 2 ? BSF8_QT(2) : m1.g == 3 ? BSF8_QT(3) : BSF8_QT(4));
+#define BSF8_QR(G) \
+  (sb ? w8a16_m1_ring_kernel<XK_E4M3, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_E4M3, false, G, M1R_DEPTH>)
+  auto k1 = m1.ring ? (m1.g == 2 ? BSF8_QR(2) : m1.g == 3 ? BSF8_QR(3) : BSF8_QR(4))
+            : M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_Q1(2, 4) : m1.g == 3 ? BSF8_Q1(3, 4) : BSF8_Q1(4, 4))
+                                    : (m1.g == 2 ? BSF8_Q1(2, 5) : m1.g == 3 ? BSF8_Q1(3, 5) : BSF8_Q1(4, 5)))
+                     : (m1.g == 2 ? BSF8_QT(2) : m1.g == 3 ? BSF8_QT(3) : BSF8_QT(4));
 #undef BSF8_Q1
 #undef BSF8_QT
+#undef BSF8_QR
   hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a8 streaming launch");
 }

@@ -420,12 +420,13 @@ FULL = {
     "qkv_m1": lambda: synth.config4(1),
     "qkv_m512": lambda: synth.config4(512),
     "large_prefill_m8192": synth.config5,
+    "ffn_down_decode_m1": lambda: synth.config3_down(1),
 }
 ARMS = {"decode_5120x5120_m1": ("w8a16", "w8a8"), "decode_5120x5120_m4": ("w8a16",),
         "decode_5120x5120_m8": ("w8a16", "w8a8"), "decode_5000x4000_m8": ("w8a16", "w8a8"),
         "decode_5000x4000_m1": ("w8a16",),
         "ffn_gate_up_m1024": ("w8a8",), "ffn_down_m1024": ("w8a8",), "qkv_m1": ("w8a16", "w8a8"),
-        "qkv_m512": ("w8a16", "w8a8"), "large_prefill_m8192": ("w8a8",)}
+        "qkv_m512": ("w8a16", "w8a8"), "large_prefill_m8192": ("w8a8",), "ffn_down_decode_m1": ("w8a16", "w8a8")}
 
 
 @pytest.mark.parametrize("name", list(FULL))
@@ -884,3 +885,60 @@ def test_w8a8_few_tokens_streaming(K, sdt):
             for odt in (t.float32, t.bfloat16):
                 y = to_np(B.linear_w8a8(w, xqd, xsd, out_dtype=odt))
                 assert_within(y, ref, bound, odt == t.bfloat16, f"w8a8 streaming K={K} M={M} {layout}")
+
+
+@pytest.mark.parametrize("K", [5248, 6144, 17408])
+@pytest.mark.parametrize("sdt", ["bf16", "f32"])
+def test_one_token_long_k_ring(K, sdt):
+    """One token with more than five chunks per wave runs the ring kernel (both arms):
+    K = 5248 (41 chunks: waves of 6 and a last one of 5), 6144 (6 per wave: one and a half
+    rounds of the 4-slot ring) and 17408 (the FFN down projection: 17 per wave);
+    grouped members of 300 and 130 rows, F32 and BF16 activations, BF16 and F32 grids;
+    every output against the oracle."""
+    t = torch()
+    g = np.random.default_rng(229 + K)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    om = []
+    for r in (300, 130):
+        codes = finite[g.integers(0, finite.size, (r, K))]
+        sc = np.exp2(g.uniform(-10, -3, O.scale_grid_shape(r, K))).astype(np.float32)
+        if sdt == "bf16":
+            sc = O.f32_to_bf16(sc)
+        om.append((codes, sc))
+    dt = t.float32 if sdt == "f32" else t.bfloat16
+    w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.from_numpy(np.asarray(s, np.float32)).to(device()).to(dt))
+                          for c, s in om])
+    x = synth.gaussian_activations(229, f"ring_X{K}", 1, K)
+    d16 = w.describe(B.ARM_W8A16, 1)
+    d8 = w.describe(B.ARM_W8A8, 1)
+    assert "w8a16_m1_ring " in d16 and "w8a16_m1_ring<e4m3>" in d8, (d16, d8)
+    banner(f"ring K={K} {sdt}: {d16}")
+    y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
+    assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"ring w8a16 K={K}")
+    xb = t.from_numpy(x).to(t.bfloat16)
+    xe = xb.float().numpy()
+    yb = to_np(B.linear_w8a16(w, xb.to(device()), out_dtype=t.bfloat16))
+    assert_within(yb, O.linear_w8a16(xe, om), O.abs_bound_w8a16(xe, om), True, f"ring w8a16 bf16 K={K}")
+    xq, xs = O.quant_act(x)
+    y8 = to_np(B.linear_w8a8(w, t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device()), out_dtype=t.float32))
+    assert_within(y8, O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), False, f"ring w8a8 K={K}")
+
+
+def test_one_token_long_k_ring_per_tensor():
+    """The ring kernel with per-tensor scales (strides (0, 0)) on K = 6144."""
+    t = torch()
+    g = np.random.default_rng(233)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    K = 6144
+    codes = [finite[g.integers(0, finite.size, (r, K))] for r in (130, 300)]
+    svals = [np.float32(2.0 ** -7.25), np.float32(2.0 ** -4.5)]
+    w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.tensor(float(v), dtype=t.float32, device=device()))
+                          for c, v in zip(codes, svals)], block=(0, 0))
+    om = list(zip(codes, svals))
+    x = synth.gaussian_activations(233, "ring_pt_X", 1, K)
+    banner(f"ring per-tensor: {w.describe(B.ARM_W8A16, 1)}")
+    y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
+    assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, "ring per-tensor w8a16")
+    xq, xs = O.quant_act(x)
+    y8 = to_np(B.linear_w8a8(w, t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device())))
+    assert_within(y8, O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), True, "ring per-tensor w8a8")
