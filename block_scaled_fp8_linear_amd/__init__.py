@@ -97,6 +97,8 @@ EXPORTS = [
     ("bsf8_quant_glu", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]),
+    ("bsf8_glu_act", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_upcast", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
     ("bsf8_dense_workspace_size", ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -394,6 +396,24 @@ def quant_glu(y, xq=None, xs=None):
     return xq, xs
 
 
+def glu_act(y, out=None):
+    """Gate/up output y [M, 2F] (gate then up; float32 or bfloat16) -> h = silu(gate) * up as float32 [M, F],
+    the same values quant_glu quantizes."""
+    torch = _torch()
+    _on_device(None, y=y)
+    _on_device(y.device, out=out)
+    if y.dim() != 2 or y.stride(1) != 1 or y.shape[1] % 2:
+        raise ValueError("y must be 2-D with an even number of columns and unit column stride")
+    M, F = y.shape[0], y.shape[1] // 2
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.float32, device=y.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or tuple(out.shape) != (M, F) or out.stride(1) != 1:
+        raise ValueError(f"out must be float32 [M, F] = [{M}, {F}] with unit column stride")
+    _check(lib().bsf8_glu_act(y.data_ptr(), _dt_of(y), M, F, y.stride(0), out.data_ptr(), out.stride(0),
+                              _stream_ptr(y.device)), "glu_act")
+    return out
+
+
 def linear_w8a16(w: BlockFP8Weight, x, out_dtype=None, out=None, workspace=None):
     """F32-activation arm: y [M, N] = x . dequant(W)^T (float32 output unless out_dtype says bfloat16)."""
     torch = _torch()
@@ -501,7 +521,7 @@ def linear_dense(wd, x, out_dtype=None, out=None, workspace=None):
     return y
 
 
-__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "quant_glu", "linear_w8a16", "linear_w8a8",
+__all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "quant_glu", "glu_act", "linear_w8a16", "linear_w8a8",
            "linear_w8a8_noalloc", "NOALLOC_SCRATCH_BYTES", "upcast",
            "linear_dense", "dense_workspace_size", "lib", "status_name", "ARM_W8A16", "ARM_W8A8", "ARM_DENSE",
            "EXPORTS", "LIB_PATH", "MAX_MEMBERS", "scales_kmajor"]

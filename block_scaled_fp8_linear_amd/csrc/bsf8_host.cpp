@@ -267,6 +267,20 @@ bsf8_status bsf8_quant_glu(const void* y, int32_t y_dtype, int64_t M, int64_t F,
                           static_cast<hipStream_t>(stream));
 }
 
+bsf8_status bsf8_glu_act(const void* y, int32_t y_dtype, int64_t M, int64_t F, int64_t ldy, float* h, int64_t ldh,
+                         void* stream) {
+  if (M < 0 || F < 0) return fail(BSF8_E_INVALID_ARG, "negative size");
+  if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
+  if (M == 0 || F == 0) return BSF8_OK;
+  if (y == nullptr || h == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (ldy < 2 * F || ldh < F) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (M > INT32_MAX || F > INT32_MAX / 4) return fail(BSF8_E_UNSUPPORTED, "M or F too large");
+  const size_t esz = y_dtype == BSF8_DT_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(y) % esz || reinterpret_cast<uintptr_t>(h) % 4)
+    return fail(BSF8_E_ALIGNMENT, "y or h not element aligned");
+  return launch_glu_act(y, y_dtype == BSF8_DT_BF16, M, F, ldy, h, ldh, static_cast<hipStream_t>(stream));
+}
+
 bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, size_t* bytes) {
   if (w == nullptr || bytes == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
   if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");

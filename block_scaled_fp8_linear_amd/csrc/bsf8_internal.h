@@ -53,6 +53,8 @@ bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, i
 
 bsf8_status launch_quant_glu(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
                              int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream);
+bsf8_status launch_glu_act(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, float* h, int64_t ldh,
+                           hipStream_t stream);
 
 size_t w8a16_workspace_bytes(const WeightDev& w, int64_t M);
 bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x_bf16, int64_t M,

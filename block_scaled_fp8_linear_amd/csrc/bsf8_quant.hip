@@ -11,11 +11,23 @@
 // and issues all their loads before processing any, so each lane has several
 // loads in flight.
 // The group amax is a 5-step butterfly inside the half-wave.  The arithmetic is
-// the defined one, in F32: s = max(amax, 1e-10) / 448 and f = x / s with IEEE
-// division (hipcc's default division is correctly rounded), clamp to +-448, then
-// the hardware RNE conversion v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950), which keeps
-// the sign of zero.  The kernel is HBM-bound: 4 (or 2) bytes in and 1 byte out
-// per channel, plus 4 bytes per group.
+// the defined one: s = max(amax, 1e-10) / 448 in F32 (IEEE division, hipcc's
+// default), f = x / s with the IEEE F32 quotient, clamp to +-448, then the
+// hardware RNE conversion v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950), which keeps
+// the sign of zero.  The quotient is formed as fl32(x * r) in F64 with
+// r = fl64(1 / s) computed once per group, which is exactly the IEEE F32
+// quotient.  Write x = X 2^a and s = S 2^b with integer significands (S below
+// 2^24, s is normal) and let m = (2n + 1) 2^(c-1) be an F32 rounding midpoint
+// next to q = x / s, 2^c the F32 spacing there.  x/s - m equals
+// (X 2^a - (2n + 1) S 2^(b+c-1)) / (S 2^b), which is never zero (a quotient of
+// two 24-bit numbers is not a 25-bit odd significand) and, as q >= 2^(c+23)
+// forces a >= b + c - 1, is a multiple of 2^(b+c-1) / (S 2^b): relative to q
+// at least 2^-25 / S > 2^-49 (for a subnormal q at least 2^-174 in absolute
+// terms).  fl64(x * r) is within 2^-51.9 of x / s relative (below 2^-178
+// absolute for subnormal q), so both round to the same F32 value, zero's sign
+// included.  Per channel that is two conversions and one F64 multiply instead
+// of the F32 division's ten instructions.  The kernel is HBM-bound for plain activations: 4 (or 2)
+// bytes in and 1 byte out per channel, plus 4 bytes per group.
 //
 // The GLU instance is the step between the dense FFN's gate/up GEMM and its
 // down GEMM ("Module w8a8_prefill", preamble: the gate/up/down prefill arm):
@@ -118,9 +130,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
 #pragma unroll
     for (int d = 16; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 32));
     const float s = fmaxf(amax, kAmaxFloor) / kE4M3Max;
+    const double rs = 1.0 / static_cast<double>(s);   // fl64(1 / s), once per group
     float f[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(v[j][e] / s, -kE4M3Max), kE4M3Max);
+    for (int e = 0; e < 4; ++e) {
+      const float qv = static_cast<float>(static_cast<double>(v[j][e]) * rs);   // = the IEEE F32 quotient v / s
+      f[e] = fminf(fmaxf(qv, -kE4M3Max), kE4M3Max);
+    }
     int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
     packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
     uint8_t* q = xq + mrow[j] * ldq + kk[j];
@@ -130,6 +146,33 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
       for (int e = 0; e < valid[j]; ++e) q[e] = uint8_t(uint32_t(packed) >> (8 * e));
     }
     if (lane32 == 0) xs[mrow[j] * xs_sm + gcol[j] * xs_sk] = s;
+  }
+}
+
+// The activation itself, h = silu(g) * u in F32, for callers that need it
+// unquantized (the W8A16 down projection at decode).  One thread per four
+// channels of a token; y is the gate/up output [M, 2F], h is [M, F] (pitch ldh).
+template <bool BF16>
+__global__ __launch_bounds__(kQuantThreads) void glu_act_kernel(const void* __restrict__ y, int32_t M, int32_t F,
+                                                                int64_t ldy, float* __restrict__ h, int64_t ldh,
+                                                                int32_t y_vec, int32_t h_vec) {
+  const int32_t per_row = (F + 3) >> 2;
+  const int64_t i = int64_t(blockIdx.x) * kQuantThreads + threadIdx.x;
+  if (i >= int64_t(M) * per_row) return;
+  const int64_t m = i / per_row;
+  const int32_t f0 = int32_t(i - m * per_row) * 4;
+  const int valid = min(4, F - f0);
+  float g[4], u[4];
+  load4<BF16>(y, m * ldy + f0, valid, y_vec != 0, g);
+  load4<BF16>(y, m * ldy + F + f0, valid, y_vec != 0, u);
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = silu_glu(g[e], u[e]);
+  float* out = h + m * ldh + f0;
+  if (valid == 4 && h_vec) {
+    *reinterpret_cast<float4*>(out) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    for (int e = 0; e < valid; ++e) out[e] = v[e];
   }
 }
 
@@ -176,6 +219,26 @@ bsf8_status launch_quant_act(const void* x, bool x_bf16, int64_t M, int64_t K, i
 bsf8_status launch_quant_glu(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, uint8_t* xq,
                              int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, hipStream_t stream) {
   return launch_quant(y, y_bf16, true, M, F, ldy, xq, ldq, xs, xs_sm, xs_sk, stream);
+}
+
+}  // namespace bsf8
+
+namespace bsf8 {
+
+bsf8_status launch_glu_act(const void* y, bool y_bf16, int64_t M, int64_t F, int64_t ldy, float* h, int64_t ldh,
+                           hipStream_t stream) {
+  const int64_t threads = M * ((F + 3) / 4);
+  const int64_t grid64 = (threads + kQuantThreads - 1) / kQuantThreads;
+  if (grid64 > INT32_MAX || F > INT32_MAX || M > INT32_MAX) {
+    set_error("UNSUPPORTED: %lld x %lld activations", (long long)M, (long long)F);
+    return BSF8_E_UNSUPPORTED;
+  }
+  const size_t esz = y_bf16 ? 2 : 4;
+  const int y_vec = (reinterpret_cast<uintptr_t>(y) % (4 * esz) == 0) && ((ldy * esz) % (4 * esz) == 0) && F % 4 == 0;
+  const int h_vec = (reinterpret_cast<uintptr_t>(h) % 16 == 0) && (ldh % 4 == 0);
+  hipLaunchKernelGGL(y_bf16 ? glu_act_kernel<true> : glu_act_kernel<false>, dim3(unsigned(grid64)),
+                     dim3(kQuantThreads), 0, stream, y, int32_t(M), int32_t(F), ldy, h, ldh, y_vec, h_vec);
+  return device_status(hipGetLastError(), "glu_act launch");
 }
 
 }  // namespace bsf8

@@ -251,6 +251,20 @@ bsf8_status bsf8_quant_glu(const void* y, int32_t y_dtype, int64_t M, int64_t F,
                            int64_t ldq, float* xs, int64_t xs_sm, int64_t xs_sk, void* stream);
 
 /*
+ * bsf8_glu_act -- the same activation as bsf8_quant_glu, written out instead of
+ * quantized: h[m, f] = silu(y[m, f]) * y[m, F + f] as F32, h [M, F] with leading
+ * dimension ldh (elements).  For a down projection that takes F32 activations
+ * (the W8A16 arm at decode, where the activation is not quantized).
+ * ("Module w8a8_prefill", preamble: the gate/up/down dense FFN; "Qwen
+ *  checkpoints with block FP8 weights", block-path paragraph: the W8A16 arm takes
+ *  F32 activations.)  Same evaluation, bit for bit, as bsf8_quant_glu's h.
+ * Errors: INVALID_ARG (null, negative, ldy < 2F, ldh < F, bad dtype), ALIGNMENT
+ * (y or h not element aligned), UNSUPPORTED (M or F too large), DEVICE.
+ */
+bsf8_status bsf8_glu_act(const void* y, int32_t y_dtype, int64_t M, int64_t F, int64_t ldy, float* h, int64_t ldh,
+                         void* stream);
+
+/*
  * bsf8_workspace_size -- device workspace bytes a compute call of this handle
  * needs for M tokens on the given arm (0 when none).  The W8A8 arm uses one
  * when its tile grid is too small to occupy the device (few tokens against few

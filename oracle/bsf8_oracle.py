@@ -45,7 +45,7 @@ __all__ = [
     "abs_bound_w8a16", "abs_bound_w8a8", "round_output", "within_bound",
     "cross_arm_metrics", "Status", "TensorDesc", "MemberDesc", "validate",
     "upcast_members", "linear_dense", "abs_bound_dense", "linear_dense_loops",
-    "silu_glu", "glu_quant",
+    "exp_neg_abs_f32", "silu_glu", "glu_quant",
 ]
 
 BLOCK = 128            # weight_block_size [128,128]  [QWEN layout paragraph]
@@ -373,6 +373,47 @@ def quant_act(x: np.ndarray, eps: np.float32 = ACT_EPS) -> Tuple[np.ndarray, np.
     return codes, scales
 
 
+def exp_neg_abs_f32(g: np.ndarray) -> np.ndarray:
+    """e = exp(-|g|) correctly rounded to float32 (nearest, ties to even), for float32 g.
+
+    float64's exp (within a float64 ulp or two) rounded to float32 is the
+    correctly rounded value unless exp(-|g|) lies near a float32 rounding
+    midpoint; wherever the float64 value is within 2^-45 (relative) of one, the
+    value is recomputed with Python's decimal module at 60 digits (its exp is
+    correctly rounded at that precision) and compared with the midpoints
+    exactly.  exp of a nonzero rational is irrational, so it is never a
+    midpoint itself.
+    """
+    from decimal import Decimal, localcontext
+    g = np.asarray(g, np.float32)
+    a = np.abs(g.astype(np.float64))
+    e64 = np.exp(-a)
+    e32 = e64.astype(np.float32)
+    up = np.nextafter(e32, np.float32(np.inf))
+    dn = np.nextafter(e32, np.float32(0.0))
+    m_up = (e32.astype(np.float64) + up.astype(np.float64)) / 2.0   # exact: both are float32
+    m_dn = (e32.astype(np.float64) + dn.astype(np.float64)) / 2.0
+    tol = 2.0 ** -45 * e64
+    near = ((np.abs(e64 - m_up) <= tol) | ((np.abs(e64 - m_dn) <= tol) & (e32 > 0))) & (a > 0)
+    if np.any(near):
+        e32 = e32.copy()
+        flat_a, flat_e = a.reshape(-1), e32.reshape(-1)
+        flat_up, flat_dn = up.reshape(-1), dn.reshape(-1)
+        with localcontext() as ctx:
+            ctx.prec = 60
+            for i in np.flatnonzero(near.reshape(-1)):
+                ed = (-Decimal(float(flat_a[i]))).exp()
+                c = flat_e[i]
+                hi = (Decimal(float(c)) + Decimal(float(flat_up[i]))) / 2
+                lo = (Decimal(float(c)) + Decimal(float(flat_dn[i]))) / 2
+                if ed > hi:
+                    flat_e[i] = flat_up[i]
+                elif ed < lo and c > 0:
+                    flat_e[i] = flat_dn[i]
+        e32 = flat_e.reshape(e32.shape)
+    return e32
+
+
 def silu_glu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     """h = silu(g) * u = g * sigmoid(g) * u as float32.
 
@@ -381,14 +422,14 @@ def silu_glu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     projection through the gated activation and the per-token quantizer.
     Reading: the pages do not name the activation; the gated SiLU of the
     Qwen dense FFN is taken.  Its steps are fixed so that the quantized codes
-    (decided in float32) are reproducible, in the overflow-free form:
-    e = exp(-|g|) evaluated in float64 and rounded to float32 (in (0, 1]),
-    t = 1 + e, then q = g / t for g >= 0 and q = (g * e) / t for g < 0, and
-    h = q * u, each an IEEE float32 operation.
+    (decided in float32) are reproducible and single-valued, in the
+    overflow-free form: e = exp(-|g|) correctly rounded to float32 (in [0, 1],
+    ``exp_neg_abs_f32``), t = 1 + e, then q = g / t for g >= 0 and
+    q = (g * e) / t for g < 0, and h = q * u, each an IEEE float32 operation.
     """
     g = np.asarray(g, np.float32)
     u = np.asarray(u, np.float32)
-    e = np.exp(-np.abs(g.astype(np.float64))).astype(np.float32)
+    e = exp_neg_abs_f32(g)
     t = np.float32(1.0) + e
     q = np.where(g >= 0, g / t, (g * e) / t).astype(np.float32)
     return q * u

@@ -572,8 +572,9 @@ def pin_silu_glu(O, seed=31):
       exp(-|g|) is a normal float32 (|g| < 80), over values spanning 2^-6..2^6;
     * closed forms: g = 0 gives signed zeros, g = 100 gives g*u exactly,
       g = -200 gives -0 * u (exp(-200) rounds to zero);
-    * brute force with Python's float64 exp and float32 rounding after each step
-      equals it bit for bit, tails included;
+    * brute force with the correctly rounded exp of an 80-digit decimal
+      evaluation and float32 rounding after each step equals it bit for bit,
+      tails included;
     * glu_quant is quant_act of it over the gate/up halves, in that order.
     """
     import math
@@ -594,7 +595,7 @@ def pin_silu_glu(O, seed=31):
             return False, f"closed form g={gv} u={uv}: {hv}"
     for gv, uv in list(zip(gate[:300], up[:300])) + [(np.float32(-95.5), np.float32(3.0)),
                                                      (np.float32(-150.25), np.float32(-1.0))]:
-        ev = _f32(math.exp(-abs(float(gv))))
+        ev = _exp_rn32_decimal(abs(float(gv)))
         tv = _f32(1.0 + ev)
         qv = _f32(float(gv) / tv) if gv >= 0 else _f32(_f32(float(gv) * ev) / tv)
         hv = _f32(qv * float(uv))
@@ -774,3 +775,61 @@ def pin_cross_arm_metrics(O, seed=43):
     if abs(cos - dot / (na * nb)) > 1e-12 or abs(rel - nd / nb) > 1e-12:
         return False, f"loops: {cos} vs {dot / (na * nb)}, {rel} vs {nd / nb}"
     return True, ""
+
+
+# ------------------------------------------------------------------- P19
+
+def _exp_rn32_decimal(a: float) -> float:
+    """exp(-a) correctly rounded to float32, from an 80-digit decimal evaluation
+    compared exactly with the float32 midpoints around it."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 80
+        ed = (-Decimal(a)).exp()
+        c = np.float32(float(ed))
+        for _ in range(2):
+            up = np.nextafter(c, np.float32(np.inf))
+            dn = np.nextafter(c, np.float32(0.0))
+            if ed > (Decimal(float(c)) + Decimal(float(up))) / 2:
+                c = up
+            elif c > 0 and ed < (Decimal(float(c)) + Decimal(float(dn))) / 2:
+                c = dn
+    return float(c)
+
+
+def pin_exp_correctly_rounded(O, seed=47, n_random=20000, n_search=4_000_000):
+    """P19: the activation's e = exp(-|g|) is the float32 nearest to the exact value.
+
+    * equals an independent 80-digit decimal evaluation on random float32
+      arguments over [0, 110] (both signs of g) and on every argument, among a
+      few million random ones, whose exp lies within 2^-42 of a float32 rounding
+      midpoint (where a float64 evaluation rounded once more could differ);
+    * closed forms: exp(0) = 1; arguments beyond 103.98 round to 0; the value
+      stays in [0, 1].
+    """
+    g = np.random.default_rng(seed)
+    x = (g.integers(0, 0x42DC0000, n_random, dtype=np.int64).astype(np.uint32)).view(np.float32)
+    x = x * np.where(g.random(n_random) < 0.5, np.float32(-1), np.float32(1))
+    e = O.exp_neg_abs_f32(x)
+    for xi, ei in zip(x, e):
+        if float(ei) != _exp_rn32_decimal(abs(float(xi))):
+            return False, f"random argument {float(xi)!r}"
+    cand = (g.integers(0, 0x42D00000, n_search, dtype=np.int64).astype(np.uint32)).view(np.float32)
+    e64 = np.exp(-cand.astype(np.float64))
+    c32 = e64.astype(np.float32)
+    mids = [(c32.astype(np.float64) + np.nextafter(c32, np.float32(np.inf)).astype(np.float64)) / 2,
+            (c32.astype(np.float64) + np.nextafter(c32, np.float32(0)).astype(np.float64)) / 2]
+    dist = np.minimum(np.abs(e64 - mids[0]), np.abs(e64 - mids[1])) / e64
+    hard = cand[dist <= 2.0 ** -42]
+    if hard.size == 0:
+        return False, "no near-midpoint argument found"
+    eh = O.exp_neg_abs_f32(hard)
+    for xi, ei in zip(hard, eh):
+        if float(ei) != _exp_rn32_decimal(float(xi)):
+            return False, f"near-midpoint argument {float(xi)!r}"
+    edge = O.exp_neg_abs_f32(np.array([0.0, -0.0, 104.0, -200.0, 1e30], np.float32))
+    if not (edge[0] == 1.0 and edge[1] == 1.0 and edge[2] == 0.0 and edge[3] == 0.0 and edge[4] == 0.0):
+        return False, f"closed forms {edge}"
+    if not (np.all(e >= 0) and np.all(e <= 1)):
+        return False, "range"
+    return True, f"{hard.size} near-midpoint arguments"

@@ -123,3 +123,61 @@ def test_quant_glu_kmajor_scales_padded(dtype):
     assert np.array_equal(xq.cpu().numpy(), q_ref)
     assert np.array_equal(km[:, :M].cpu().numpy().T.view(np.uint32), s_ref.view(np.uint32))
     assert np.all(km[:, M:].cpu().numpy() == -1.0)
+
+
+# ----------------------------------------------------- the activation itself
+
+def _glu_act(y_np, F, dtype, ld_pad=0):
+    t = torch()
+    M = y_np.shape[0]
+    if dtype == "bf16":
+        y_np = O.f32_to_bf16(y_np)
+        yd = t.from_numpy(O.f32_to_bf16_bits(y_np).view(np.int16)).to(device()).view(t.bfloat16)
+    else:
+        yd = t.from_numpy(np.ascontiguousarray(y_np)).to(device())
+    h = t.full((M, F + ld_pad), 7.0, dtype=t.float32, device=device())
+    banner(f"glu_act M={M} F={F} {dtype} ldh_pad={ld_pad}")
+    B.glu_act(yd, h[:, :F])
+    hn = h.cpu().numpy()
+    ref = O.silu_glu(y_np[:, :F], y_np[:, F:2 * F])
+    differ = int(np.count_nonzero(hn[:, :F].view(np.uint32) != ref.view(np.uint32)))
+    assert differ == 0, f"{differ} activations differ"
+    if ld_pad:
+        assert np.all(hn[:, F:] == 7.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,F", [(1, 17408), (7, 202), (300, 1000)])
+def test_glu_act_bit_exact(M, F, dtype):
+    """bsf8_glu_act writes the activation bsf8_quant_glu quantizes: bit for bit the oracle's
+    silu(g) * u (e = exp(-|g|) correctly rounded to F32), ragged widths and a padded pitch."""
+    _glu_act(_gate_up(171, M, F, scale=2.0), F, dtype, ld_pad=3 if F % 2 else 0)
+
+
+def test_glu_act_over_the_gate_domain():
+    """Every 251st float32 gate value with |g| in [2^-26, 104] (both signs; u = 1), plus the
+    arguments among a few million whose exp lies within 2^-42 of a float32 rounding
+    midpoint, plus values beyond the range (exp rounds to 1 or to 0): the device's
+    activation equals the oracle's correctly rounded definition bit for bit.  (Run over
+    every value of the domain, 547 356 674 of them, the same comparison finds no
+    difference.)"""
+    lo = int(np.float32(2.0 ** -26).view(np.uint32))
+    hi = int(np.float32(104.0).view(np.uint32))
+    bits = np.arange(lo, hi + 1, 251, dtype=np.uint64).astype(np.uint32)
+    g = np.concatenate([bits.view(np.float32), -bits.view(np.float32)])
+    rng = np.random.default_rng(239)
+    cand = (rng.integers(lo, hi, 4_000_000, dtype=np.int64).astype(np.uint32)).view(np.float32)
+    e64 = np.exp(-cand.astype(np.float64))
+    c32 = e64.astype(np.float32)
+    up = (c32.astype(np.float64) + np.nextafter(c32, np.float32(np.inf)).astype(np.float64)) / 2
+    dn = (c32.astype(np.float64) + np.nextafter(c32, np.float32(0)).astype(np.float64)) / 2
+    hard = cand[np.minimum(np.abs(e64 - up), np.abs(e64 - dn)) <= 2.0 ** -42 * e64]
+    extra = np.array([0.0, -0.0, 2.0 ** -30, -2.0 ** -30, 103.9, -103.9, 104.5, -104.5, 1e6, -1e6, 87.3, -87.3],
+                     np.float32)
+    g = np.concatenate([g, hard, -hard, extra]).astype(np.float32)
+    F = 4096
+    pad = (-g.size) % F
+    gp = np.concatenate([g, np.zeros(pad, np.float32)]).reshape(-1, F)
+    y = np.concatenate([gp, np.ones_like(gp)], axis=1)
+    banner(f"glu_act gate domain: {g.size} values ({hard.size} near-midpoint)")
+    _glu_act(y, F, "f32")

@@ -291,3 +291,19 @@ def test_mutation_cross_arm_unnormalised_cosine(monkeypatch):
         return float(a @ b / (b @ b)), float(np.linalg.norm(a - b) / np.linalg.norm(b))
     monkeypatch.setattr(OM, "cross_arm_metrics", wrong)
     assert _fails(P.pin_cross_arm_metrics, OM)
+
+
+def test_mutation_exp_in_float32(monkeypatch):
+    """exp evaluated in float32 (a float32 library exp, not correctly rounded) fails the exp pin."""
+    monkeypatch.setattr(OM, "exp_neg_abs_f32", lambda g: np.exp(-np.abs(np.asarray(g, np.float32))))
+    assert _fails(P.pin_exp_correctly_rounded, OM)
+
+
+def test_mutation_exp_rounded_down(monkeypatch):
+    """exp rounded toward zero instead of to nearest fails the exp pin."""
+    def trunc(g):
+        e64 = np.exp(-np.abs(np.asarray(g, np.float32).astype(np.float64)))
+        e32 = e64.astype(np.float32)
+        return np.where(e32.astype(np.float64) > e64, np.nextafter(e32, np.float32(0)), e32).astype(np.float32)
+    monkeypatch.setattr(OM, "exp_neg_abs_f32", trunc)
+    assert _fails(P.pin_exp_correctly_rounded, OM)

@@ -11,7 +11,7 @@ import oracle_pins as P
     P.pin_encode_vs_torch, P.pin_bf16, P.pin_grids, P.pin_scale_direction,
     P.pin_quant_invariants, P.pin_brute_force, P.pin_per_tensor, P.pin_sampled_rows, P.pin_int_partials, P.pin_special_cases,
     P.pin_cross_arm, P.pin_upcast, P.pin_dense_brute_force, P.pin_silu_glu,
-    P.pin_abs_bounds, P.pin_within_bound, P.pin_cross_arm_metrics,
+    P.pin_abs_bounds, P.pin_within_bound, P.pin_cross_arm_metrics, P.pin_exp_correctly_rounded,
 ], ids=lambda f: f.__name__)
 def test_pin(pin):
     ok, detail = pin(O)
