@@ -31,6 +31,8 @@ The same JSON line also carries:
   with an HBM roofline on algorithmic bytes and a plain read of the same bytes
   (``bsf8_read_stream``) as context;
 * ``qkv_w8a8_decode``: grouped Q/K/V through the W8A8 arm at M = 1, rotated;
+* ``ffn_down_decode`` and ``ffn_down_w8a8_decode``: the FFN down projection
+  [5120, 17408] at one token through both arms, rotated;
 * ``qkv_prefill`` and ``qkv_w8a16_m512``: grouped Q/K/V at M = 512 through the
   W8A8 and the W8A16/F32 arm;
 * ``rotated``: the headline GEMM over three weight copies used in turn;
@@ -94,6 +96,8 @@ def parse():
                     help="do not run rocm-smi for the clock under load (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="only time two plain read kernels over buffer sizes from 8 MB to 416 MB and print that line")
     return ap.parse_args()
 
 
@@ -592,6 +596,49 @@ def bench_dense_arm(torch, B, synth, dev):
                 upcast_bytes=up_bytes, gemm=gemm)
 
 
+def read_sweep(torch, B, dev):
+    """What a single launch that only reads N bytes achieves, for N from 8 MB to 416 MB:
+    bsf8_read_stream (all loads of a block issued at once) and PyTorch's own int32 sum
+    (its reduction kernel), each over enough distinct copies (>= 640 MiB in rotation) that
+    the Infinity Cache cannot serve them; per-launch device time from graphs of
+    back-to-back launches.  A fit t = t0 + N / R separates the fixed cost of a launch
+    from the streaming rate."""
+    sizes_mb = (8, 16, 26.2144, 52.4288, 104.8576, 209.7152, 419.4304)
+    sink = torch.zeros(B.READ_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+    res = {}
+    for kname in ("bsf8_read_stream", "torch_int32_sum"):
+        pts = []
+        for mb in sizes_mb:
+            n = int(mb * 1e6) // 16 * 16
+            copies = max(2, -(-ROTATE_BYTES // n))
+            bufs = [torch.empty(n // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(copies)]
+            outs = torch.empty(copies, dtype=torch.int64, device=dev)
+            if kname == "bsf8_read_stream":
+                def run():
+                    for b in bufs:
+                        B.read_stream(b, sink)
+            else:
+                def run():
+                    for i, b in enumerate(bufs):
+                        torch.sum(b, dtype=torch.int64, out=outs[i])
+            g = graph_of(torch, run)
+            settle(torch, g.replay, 0.2)
+            st = replay_stats(torch, g, 30, copies)
+            pts.append((n, st["median"] * 1e-3))
+            del g, bufs
+            torch.cuda.empty_cache()
+        # least-squares fit of t = t0 + n / R
+        xs = np.array([p[0] for p in pts], np.float64)
+        ts = np.array([p[1] for p in pts], np.float64)
+        A = np.vstack([np.ones_like(xs), xs]).T
+        (t0, inv_r), *_ = np.linalg.lstsq(A, ts, rcond=None)
+        res[kname] = {"points": [{"mb": round(n / 1e6, 2), "us": round(t * 1e6, 2), "gbs": round(n / t / 1e9, 1),
+                                  "frac_hbm": round(n / t / 1e9 / HBM_PEAK_GBS, 4)} for n, t in pts],
+                      "fit_t0_us": round(t0 * 1e6, 2), "fit_rate_gbs": round(1.0 / inv_r / 1e9, 1)}
+        log(f"read sweep {kname}: {res[kname]}")
+    return res
+
+
 def copy_calibration(torch, dev):
     """A plain streaming kernel of known traffic, run three times, so an HBM counter run can scale
     FETCH_SIZE / WRITE_SIZE: y = 2 * x over 2^28 float32 (reads 1 GiB, writes 1 GiB per launch)."""
@@ -620,6 +667,9 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} {props.gcnArchName} CUs={props.multi_processor_count}")
+    if a.read_sweep:
+        print(json.dumps({"read_sweep": read_sweep(torch, B, dev), "device": props.gcnArchName}), flush=True)
+        return
 
     big = bench_large_step(torch, B, synth, a.steps, a.warmup, dev)
     log(f"large prefill step {big['ms_per_step']:.4f} ms, gemm {big['gemm_us_stats']}")
@@ -638,6 +688,10 @@ def main():
         c4 = synth.config4(1)
         extra["qkv_decode"] = bench_w8a16_rotating(torch, B, c4.members, c4.x, (1,), dev, "grouped QKV decode")
         extra["qkv_w8a8_decode"] = bench_w8a8_rotating(torch, B, c4.members, c4.x, dev, "grouped QKV W8A8 M=1")
+        dn = synth.config3_down(1)
+        extra["down_decode"] = bench_w8a16_rotating(torch, B, dn.members, dn.x, (1,), dev, "FFN down decode")
+        extra["down_w8a8_decode"] = bench_w8a8_rotating(torch, B, dn.members, dn.x, dev, "FFN down W8A8 M=1")
+        del dn
         extra["qkv_prefill"] = bench_qkv_prefill(torch, B, synth, dev)
         extra["qkv_w8a16_m512"] = bench_qkv_w8a16_m512(torch, B, synth, dev)
         torch.cuda.empty_cache()
@@ -753,6 +807,14 @@ def main():
                          "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": profiled_traffic("w8a8_qkv_m1"),
                          "algorithmic_bytes": d["algorithmic_bytes"]}}
+        line["ffn_down_decode"] = decode_line(extra["down_decode"], profiled_traffic("w8a16_decode_down_m1"))
+        d = extra["down_w8a8_decode"]
+        line["ffn_down_w8a8_decode"] = {
+            "workload": d["workload"], "us": round(d["us"], 2), "p10": round(d["us_p10"], 2),
+            "p90": round(d["us_p90"], 2), "launches": d["launches"], "path": d["describe"],
+            "roofline": {"bound": "hbm", "kernel": "w8a8 streaming (M=1)", "achieved": round(d["gbs"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": profiled_traffic("w8a8_decode_down_m1"), "algorithmic_bytes": d["algorithmic_bytes"]}}
         q = extra["qkv_prefill"]
         line["qkv_prefill"] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in q.items()}
         line["qkv_prefill"]["roofline"] = {"bound": "mfma", "kernel": "w8a8_gemm (QKV, M=512)",
