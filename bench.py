@@ -597,34 +597,42 @@ def bench_dense_arm(torch, B, synth, dev):
 
 
 def read_sweep(torch, B, dev):
-    """What a single launch that only reads N bytes achieves, for N from 8 MB to 416 MB:
-    bsf8_read_stream (all loads of a block issued at once) and PyTorch's own int32 sum
-    (its reduction kernel), each over enough distinct copies (>= 640 MiB in rotation) that
+    """What a single launch that moves N bytes achieves, for N from 8 MB to 416 MB read:
+    bsf8_read_stream (all loads of a block issued at once), PyTorch's float32 sum (its
+    reduction kernel) and a device copy (N read + N written, counted as 2N), each over
+    enough distinct copies (>= 640 MiB in rotation) that
     the Infinity Cache cannot serve them; per-launch device time from graphs of
     back-to-back launches.  A fit t = t0 + N / R separates the fixed cost of a launch
     from the streaming rate."""
     sizes_mb = (8, 16, 26.2144, 52.4288, 104.8576, 209.7152, 419.4304)
     sink = torch.zeros(B.READ_STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
     res = {}
-    for kname in ("bsf8_read_stream", "torch_int32_sum"):
+    for kname in ("bsf8_read_stream", "torch_float32_sum", "torch_copy_read_plus_write"):
         pts = []
         for mb in sizes_mb:
             n = int(mb * 1e6) // 16 * 16
             copies = max(2, -(-ROTATE_BYTES // n))
-            bufs = [torch.empty(n // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(copies)]
-            outs = torch.empty(copies, dtype=torch.int64, device=dev)
+            bufs = [torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(i * 1e-3) for i in range(copies)]
+            outs = torch.empty(copies, dtype=torch.float32, device=dev)
             if kname == "bsf8_read_stream":
                 def run():
                     for b in bufs:
                         B.read_stream(b, sink)
-            else:
+            elif kname == "torch_float32_sum":
                 def run():
                     for i, b in enumerate(bufs):
-                        torch.sum(b, dtype=torch.int64, out=outs[i])
+                        torch.sum(b, dim=0, out=outs[i])
+            else:
+                # a device copy reads n and writes n bytes: timed per n read (the rate counts both)
+                dst = torch.empty_like(bufs[0])
+
+                def run():
+                    for b in bufs:
+                        dst.copy_(b)
             g = graph_of(torch, run)
             settle(torch, g.replay, 0.2)
             st = replay_stats(torch, g, 30, copies)
-            pts.append((n, st["median"] * 1e-3))
+            pts.append((n * (2 if kname == "torch_copy_read_plus_write" else 1), st["median"] * 1e-3))
             del g, bufs
             torch.cuda.empty_cache()
         # least-squares fit of t = t0 + n / R
