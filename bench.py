@@ -510,7 +510,7 @@ def bench_w8a8_rotating(torch, B, members, x_np, dev, label):
     return out
 
 
-def cpu_baseline_large(synth, tokens=1024, reps=3):
+def cpu_baseline_large(synth, tokens=4096, reps=3):
     """The oracle on the host cores on a bounded sample of the headline step: the first
     ``tokens`` of the 8192 tokens quantized (NumPy float32, as defined) and multiplied
     against all 18432 rows of the weight (float64, the oracle's row-chunked form),
