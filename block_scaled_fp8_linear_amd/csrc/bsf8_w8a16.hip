@@ -8,10 +8,14 @@
 //  own block-row origin.)
 //
 // Design for CDNA4.  At decode sizes this is an HBM stream of the weight bytes.
-// Kernels by token count (16-byte aligned operands, K <= 5120 for the first two):
-//  * 1 token, and 2 to 4 tokens: F32 FMAs on the vector ALUs against weights
-//    decoded exactly to F32 in registers (w8a16_m1_kernel, w8a16_mt_kernel);
-//  * 5 to 8 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
+// Kernels by token count (16-byte aligned operands):
+//  * 1 token: F32 FMAs on the vector ALUs against weights decoded exactly to
+//    F32 in registers (w8a16_m1_kernel; w8a16_m1_ring_kernel beyond five chunks
+//    per wave);
+//  * 2 to 4 tokens, K <= 5120: the same weight stream with the F32 products
+//    summed on the matrix cores (w8a16_mf_kernel, v_mfma_f32_4x4x1f32);
+//  * 5 to 8 tokens, and 2 to 4 with a longer K: the few-token MFMA kernel
+//    (w8a16_small_m_kernel);
 //  * more tokens, or any unaligned operand: the general MFMA kernel.
 // A plain F32 FMA loop needs ~M FMAs per weight byte, which beyond four tokens
 // outweighs the stream, so there the products run on the BF16 matrix cores
@@ -1045,16 +1049,32 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
 
 // ---------------------------------------------------------------------------
 // Two to four tokens (aligned operands, K <= 5120): the one-token kernel's
-// layout with the activations in LDS.  Each wave copies the slice it uses
-// (MT tokens x its chunk range, widened to F32) into a wave-private LDS
-// region; the loads are issued before the weight stream and written to LDS
-// once the stream is in flight (loads retire in order, so waiting for them
-// never waits for weights).  Per chunk, each lane decodes its 16 weight bytes
-// of every row group to F32 and multiplies them by the row's block scale once
-// (exact for BF16 scales), then runs 16 FMAs per token into that row and
-// token's accumulator; activations are read from LDS (lanes of the same piece
-// position read the same address).  Rows are summed over their 8 lanes by
-// shuffles and over the waves in LDS, in wave order.
+// weight stream with the products on the matrix cores, in F32.
+// v_mfma_f32_4x4x1f32 treats a wave as 16 blocks of four lanes: lane 4b + i
+// supplies row i of block b's 4 x 1 A operand and column i of its 1 x 4 B
+// operand, and lane 4b + j receives column j of block b's 4 x 4 product, one
+// register per row.  Lane (s, p, j) = (lane >> 5, (lane >> 2) & 7, lane & 3)
+// therefore loads the 16 weight bytes of row 4s + j of an 8-row group at piece
+// p of a chunk (one load instruction still covers 8 rows x 128 contiguous
+// bytes) and reads from LDS the 16 activations of token j at the same K
+// positions; one MFMA per K position adds w[row 4s + i][k] x[token j][k] into
+// block (s, p)'s product for every i and j.  Each wave copies its activation
+// slice (4 tokens x its chunks, widened to F32) into a wave-private LDS
+// region; those loads go out before the weight stream and are written to LDS
+// once the stream is in flight (loads retire in order, so that wait never
+// covers weights).  After a chunk's 16 positions each product register is one
+// row's and one token's partial over the piece; it is scaled by the chunk's
+// block scale (times the token's group scale for E4M3 activations) into an
+// F32 accumulator.  At the end the 8 pieces of a row and token are added
+// across lanes and the waves in LDS, in wave order.  The product of an E4M3
+// weight and an F32 activation is rounded to F32 once, as an FMA's would be;
+// the matrix core's F32 sum takes the place of the FMA chain, and the vector
+// ALU keeps the decoding and the scaling.  Against the same kernel with 16
+// FMAs per weight byte and token on the vector ALU: 9.8-10.2 -> 9.5-9.7 us at
+// two to four tokens of W [5120, 5120].  Five to eight tokens do not fit the
+// LDS as F32 slices; taken in two passes over the wave's chunks (weights kept
+// in registers, the second slice copied in between) they measured 15.1-15.3
+// us against the MFMA few-token kernel's 13.1-13.8 us, so those stay there.
 // ---------------------------------------------------------------------------
 // Activation slices in LDS carry 4 floats of padding after every 64: a lane
 // reads the 16 activations of its piece (lanes of one piece position read the
@@ -1062,8 +1082,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
 // modulo the 64 banks, met in pairs.
 __device__ __forceinline__ int xpad(int e) { return e + 4 * (e >> 6); }
 
-template <int XK, bool SBF16, int G, int CPW, int MT>
-__global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
+typedef float mf_v4f __attribute__((ext_vector_type(4)));
+
+template <int XK, bool SBF16, int G, int CPW>
+__global__ __launch_bounds__(THREADS) void w8a16_mf_kernel(Args a) {
+  constexpr int MT = 4;
   constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
   constexpr int XS = MT * CPW * CHUNK + 4 * (MT * CPW * CHUNK / 64);   // padded F32 activations per wave
   __shared__ __attribute__((aligned(16))) float xl[WAVES * XS];
@@ -1076,10 +1099,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jp = lane & 7;
-  const int rl = lane >> 3;
+  const int j = lane & 3;          // row of the lane's loads within its half group; its token
+  const int p = (lane >> 2) & 7;   // 16-byte piece of a 128-byte chunk
+  const int s = lane >> 5;         // half of the 8-row group
   const int row0 = rtile * a.rows_per_block;
-  const int rend = min(mem.rows, row0 + a.rows_per_block);
+  const int rend = min(mem.rows, row0 + a.rows_per_block);   // rows from rend on: zeros
   const int c_begin = min(Kb, wave * CPW);
   const int c_end = min(Kb, c_begin + CPW);
   const int k_end = min(K, c_end * CHUNK);
@@ -1108,13 +1132,17 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
       sc1[c] = static_cast<const uint32_t*>(mem.s)[i1];
     }
   }
-  // each token's group scale of each chunk (E4M3 activations; tokens past M read token 0's)
-  float sa[CPW][MT];
+  // the lane's token's group scale of each chunk (E4M3 activations; tokens past M read token 0's)
+  float sa[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c)
+    sa[c] = XQ8 ? a.xs[int64_t(j < a.M ? j : 0) * a.xs_sm + int64_t(min(c_begin + c, Kb - 1)) * a.xs_sk] : 1.f;
+  // the scale-grid row of each result register i (row 8 g + 4 s + i of the block)
+  bool second[G][4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-      sa[c][t] = XQ8 ? a.xs[int64_t(t < a.M ? t : 0) * a.xs_sm + int64_t(min(c_begin + c, Kb - 1)) * a.xs_sk] : 1.f;
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) second[g][i] = ((row0 + 8 * g + 4 * s + i) >> 7) != srow;
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- the wave's activation slice: MT tokens x CPW chunks, as 16-byte pieces
@@ -1136,11 +1164,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int chunk = c_begin + c;
-    const int k = chunk * CHUNK + 16 * jp;
+    const int k = chunk * CHUNK + 16 * p;
     const bool live = chunk < c_end && k < K;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int r = row0 + 8 * g + rl;
+      const int r = row0 + 8 * g + 4 * s + j;
       const uint32_t off = live && r < rend ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
       wv[c][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, kStreamLoadAux));
     }
@@ -1177,76 +1205,76 @@ __global__ __launch_bounds__(THREADS) void w8a16_mt_kernel(Args a) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
 
-  float acc[G][MT];
+  float acc[G][4];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[g][t] = 0.f;
+    for (int i = 0; i < 4; ++i) acc[g][i] = 0.f;
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
+    // the lane's token's 16 activations at its piece
+    const float* xp = xw + xpad(j * (CPW * CHUNK) + c * CHUNK + 16 * p);
+    float xv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(xp)[q];
+      xv[4 * q] = v.x;
+      xv[4 * q + 1] = v.y;
+      xv[4 * q + 2] = v.z;
+      xv[4 * q + 3] = v.w;
+    }
     // the lane's 16 weights of each row group, decoded exactly (unscaled)
-    float wd[G][16];
-    float sw[G];
+    float wf[G][16];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int r = row0 + 8 * g + rl;
-      const uint32_t sb = (r >> 7) == srow ? sc0[c] : sc1[c];
-      sw[g] = __uint_as_float(SBF16 ? sb << 16 : sb);
       const uint32_t w4[4] = {wv[c][g].x, wv[c][g].y, wv[c][g].z, wv[c][g].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, false);
         const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, true);
-        wd[g][4 * e] = lo[0];
-        wd[g][4 * e + 1] = lo[1];
-        wd[g][4 * e + 2] = hi[0];
-        wd[g][4 * e + 3] = hi[1];
+        wf[g][4 * e] = lo[0];
+        wf[g][4 * e + 1] = lo[1];
+        wf[g][4 * e + 2] = hi[0];
+        wf[g][4 * e + 3] = hi[1];
       }
     }
+    // one MFMA per K position and row group; the groups' chains interleaved
+    mf_v4f pr[G];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const float* xp = xw + xpad(t * (CPW * CHUNK) + c * CHUNK + 16 * jp);
-      float xv[16];
+    for (int g = 0; g < G; ++g) pr[g] = mf_v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = reinterpret_cast<const float4*>(xp)[q];
-        xv[4 * q] = v.x;
-        xv[4 * q + 1] = v.y;
-        xv[4 * q + 2] = v.z;
-        xv[4 * q + 3] = v.w;
-      }
-      // the chunk partial of each row and token, then its scale (the block
-      // multiplier; times the token's group scale for E4M3 activations)
+    for (int e = 0; e < 16; ++e)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float pa = 0.f, pb = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          pa = fmaf(xv[e], wd[g][e], pa);
-          pb = fmaf(xv[e + 1], wd[g][e + 1], pb);
-        }
-        acc[g][t] = fmaf(pa + pb, XQ8 ? sa[c][t] * sw[g] : sw[g], acc[g][t]);
-      }
-    }
-  }
-  // ---- rows: the 8 lanes of a row by shuffles; the waves through each wave's own region
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      float v = acc[g][t];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 4);
-      acc[g][t] = v;
-    }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  if (jp == 0) {
+      for (int g = 0; g < G; ++g) pr[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[g][e], xv[e], pr[g], 0, 0, 0);
+    // the piece partials, scaled by the chunk's multipliers
+    const float sw0 = __uint_as_float(SBF16 ? sc0[c] << 16 : sc0[c]);
+    const float sw1 = __uint_as_float(SBF16 ? sc1[c] << 16 : sc1[c]);
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) xw[t * (G * 8) + 8 * g + rl] = acc[g][t];
+      for (int i = 0; i < 4; ++i) {
+        const float sw = second[g][i] ? sw1 : sw0;
+        acc[g][i] = fmaf(pr[g][i], XQ8 ? sw * sa[c] : sw, acc[g][i]);
+      }
+  }
+  // ---- the 8 pieces of a row and token (lanes 4 apart within each half), then the waves in order
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[g][i];
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 16);
+      acc[g][i] = v;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  if (p == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xw[j * (G * 8) + 8 * g + 4 * s + i] = acc[g][i];
   }
   __syncthreads();
   for (int i = tid; i < G * 8 * MT; i += THREADS) {
@@ -1289,53 +1317,77 @@ int w16_device_cus() {
   return cache[dev];
 }
 
-// The few-token VALU kernels' shape: rows per block (rb, at most one block per
-// compute unit when 32 rows allow it), 8-row groups per block (g = ceil(rb / 8))
-// and chunks per wave; g = 0 when they do not apply.
+// The one-token kernels' shape: rows per block (rb), 8-row groups per block
+// (g = ceil(rb / 8)) and chunks per wave; g = 0 when they do not apply.
 struct M1Shape {
   int g;
   int rb;
   int cpw;
-  bool ring;   // one token, more than five chunks per wave: the ring kernel
+  bool ring;   // more than five chunks per wave: the ring kernel
   TileMap tm;
   int tiles;
 };
 
 M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
   M1Shape m{};
-  // (at five to eight tokens the FMAs and activation reads outweigh the MFMA
-  // kernel's transpose: 15.4 against 15.0 us for 8 tokens of W [5120,5120])
-  if (!aligned || M < 1 || M > 4) return m;
-  // a K of more than five chunks per wave: one token takes the ring kernel,
-  // two to four the few-token MFMA kernel (their activation slices would not
-  // fit the LDS)
+  if (!aligned || M != 1) return m;
   m.ring = w.Kb > WAVES * 5;
-  if (m.ring && M != 1) return m;
-  m.cpw = m.ring ? (w.Kb + WAVES - 1) / WAVES : M == 1 && w.Kb <= WAVES * 4 ? 4 : 5;
-  // One token: the fewest rows in [16, 32] that keep the grid within one
-  // block per compute unit, so every unit streams about the same bytes
-  // (W [5120, 5120]: 20 rows, 256 blocks, 9.3 -> 8.8 us; whole 8-row groups
-  // would give 24 rows and 214 blocks); the last group of a block may be
-  // partly masked.  Two to four tokens: whole groups, about one block per
-  // unit (there the masked lanes' FMAs and the extra blocks' activation
-  // staging cost more than the balance gains: 10.8 -> 11.2 us at M = 2).
+  m.cpw = m.ring ? (w.Kb + WAVES - 1) / WAVES : w.Kb <= WAVES * 4 ? 4 : 5;
+  // the fewest rows in [16, 32] that keep the grid within one block per
+  // compute unit, so every unit streams about the same bytes (W [5120, 5120]:
+  // 20 rows, 256 blocks, 9.3 -> 8.8 us; whole 8-row groups would give 24 rows
+  // and 214 blocks); the last group of a block may be partly masked
   const int cus = w16_device_cus();
-  if (M == 1) {
-    m.rb = 8 * M1_MAX_G;
-    for (int rb = 16; rb < 8 * M1_MAX_G; ++rb) {
-      int64_t n = 0;
-      for (int i = 0; i < w.n_members; ++i) n += (w.m[i].rows + rb - 1) / rb;
-      if (n <= cus) {
-        m.rb = rb;
-        break;
-      }
+  m.rb = 8 * M1_MAX_G;
+  for (int rb = 16; rb < 8 * M1_MAX_G; ++rb) {
+    int64_t n = 0;
+    for (int i = 0; i < w.n_members; ++i) n += (w.m[i].rows + rb - 1) / rb;
+    if (n <= cus) {
+      m.rb = rb;
+      break;
     }
-  } else {
-    int64_t groups = 0;
-    for (int i = 0; i < w.n_members; ++i) groups += (w.m[i].rows + 7) / 8;
-    m.rb = 8 * int(std::min<int64_t>(M1_MAX_G, std::max<int64_t>(2, (groups + cus - 1) / cus)));
   }
   m.g = (m.rb + 7) / 8;
+  int t = 0;
+  for (int i = 0; i < w.n_members; ++i) {
+    m.tm.tile0[i] = t;
+    m.tm.n_tiles[i] = (w.m[i].rows + m.rb - 1) / m.rb;
+    t += m.tm.n_tiles[i];
+  }
+  m.tm.tile0[w.n_members] = t;
+  m.tiles = t;
+  return m;
+}
+
+// The F32-MFMA few-token kernel's shape (two to four tokens, aligned
+// operands, at most five chunks per wave): rows per block balanced like the
+// one-token kernel's (the fewest in [16, 32] that keep the grid within one
+// block per compute unit; a block's last 8-row group may be partly masked),
+// G = ceil(rows / 8) row groups and chunks per wave; g = 0 when it does not
+// apply.
+struct MfShape {
+  int g;
+  int rb;
+  int cpw;
+  TileMap tm;
+  int tiles;
+};
+
+MfShape mf_shape(const WeightDev& w, bool aligned, int64_t M) {
+  MfShape m{};
+  if (!aligned || M < 2 || M > 4 || w.Kb > WAVES * 5) return m;
+  const int cus = w16_device_cus();
+  m.rb = 8 * M1_MAX_G;
+  for (int rb = 16; rb < 8 * M1_MAX_G; ++rb) {
+    int64_t n = 0;
+    for (int i = 0; i < w.n_members; ++i) n += (w.m[i].rows + rb - 1) / rb;
+    if (n <= cus) {
+      m.rb = rb;
+      break;
+    }
+  }
+  m.g = (m.rb + 7) / 8;
+  m.cpw = w.Kb <= WAVES * 4 ? 4 : 5;
   int t = 0;
   for (int i = 0; i < w.n_members; ++i) {
     m.tm.tile0[i] = t;
@@ -1396,6 +1448,54 @@ Plan make_plan(const WeightDev& w, int64_t M, bool aligned = false) {
   return p;
 }
 
+typedef void (*KernelFn)(Args);
+
+template <int XK, bool SB, int C>
+KernelFn mf_kernel_for(int g) {
+  return g == 2 ? w8a16_mf_kernel<XK, SB, 2, C> : g == 3 ? w8a16_mf_kernel<XK, SB, 3, C> : w8a16_mf_kernel<XK, SB, 4, C>;
+}
+
+template <int XK>
+KernelFn mf_kernel_for(bool sb, int g, int cpw) {
+  if (sb) return cpw == 4 ? mf_kernel_for<XK, true, 4>(g) : mf_kernel_for<XK, true, 5>(g);
+  return cpw == 4 ? mf_kernel_for<XK, false, 4>(g) : mf_kernel_for<XK, false, 5>(g);
+}
+
+bsf8_status launch_mf(const WeightDev& w, const MfShape& m, int xk, const void* x, int64_t ldx, const float* xs,
+                      int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
+  Args a{};
+  a.w = w;
+  a.tm = m.tm;
+  a.x = x;
+  a.y = y;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = int32_t(M);
+  a.col_tiles = 1;
+  a.chunks_per_wave = m.cpw;
+  a.rows_per_block = m.rb;
+  a.x_bf16 = xk == XK_BF16 ? 1 : 0;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.xs = xs;
+  a.xs_sm = xs_sm;
+  a.xs_sk = xs_sk;
+  const bool sb = w.scale_bf16 != 0;
+  const KernelFn k = xk == XK_E4M3 ? mf_kernel_for<XK_E4M3>(sb, m.g, m.cpw)
+                     : xk == XK_BF16 ? mf_kernel_for<XK_BF16>(sb, m.g, m.cpw)
+                                     : mf_kernel_for<XK_F32>(sb, m.g, m.cpw);
+  hipLaunchKernelGGL(k, dim3(m.tiles), dim3(THREADS), 0, stream, a);
+  return device_status(hipGetLastError(), "w8a16_mf launch");
+}
+
+char* describe_mf(char* b, size_t n, const MfShape& m, const char* arm, int64_t M) {
+  snprintf(b, n,
+           "%s | kernel=w8a16_mf rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all weight "
+           "loads first, 4-token activation slices in LDS, mfma_f32_4x4x1f32: a lane block is 4 rows x 4 tokens, "
+           "8 rows x 128 bytes per load, no LDS transpose) | M=%lld blocks=%d",
+           arm, m.rb, m.g, WAVES, m.cpw, (long long)M, m.tiles);
+  return b;
+}
+
 }  // namespace
 
 size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
@@ -1406,16 +1506,23 @@ int small_depth(int chunks_per_wave) {
 }
 
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
+  const MfShape mf = mf_shape(w, aligned, M);
+  if (mf.g) {
+    char b[512];
+    return describe_mf(b, sizeof(b), mf,
+                       "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), "
+                       "f32 products summed on the matrix cores per 16-K piece, f32 accumulate",
+                       M);
+  }
   const M1Shape m1 = m1_shape(w, aligned, M > 0 ? M : 1);
   if (m1.g) {
     char b1[448];
     snprintf(b1, sizeof(b1),
              "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), f32 fma accumulate | "
              "kernel=%s rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, %s, "
-             "8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
-             m1.ring ? "w8a16_m1_ring" : M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
-             m1.ring ? "4-chunk load ring" : "all loads first", M <= 1 ? "" : ", 4-token activation slices in LDS",
-             (long long)(M > 0 ? M : 1), m1.tiles);
+             "8 lanes per 128-byte row piece, no LDS transpose) | M=%lld blocks=%d",
+             m1.ring ? "w8a16_m1_ring" : "w8a16_m1", m1.rb, m1.g, WAVES, m1.cpw,
+             m1.ring ? "4-chunk load ring" : "all loads first", (long long)(M > 0 ? M : 1), m1.tiles);
     return b1;
   }
   const Plan p = make_plan(w, M > 0 ? M : 1, aligned);
@@ -1448,6 +1555,8 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) aligned = false;
   const Plan p = make_plan(w, M, aligned);
   if (p.tiles == 0) return BSF8_OK;
+  const MfShape mf = mf_shape(w, aligned, M);
+  if (mf.g) return launch_mf(w, mf, x_bf16 ? XK_BF16 : XK_F32, x, ldx, nullptr, 0, 0, M, y, y_bf16, ldy, stream);
   const M1Shape m1 = m1_shape(w, aligned, M);
   if (m1.g) {
     Args a{};
@@ -1467,18 +1576,13 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
 #define BSF8_M1(G, C)                                                                                         \
   (x_bf16 ? (sb ? w8a16_m1_kernel<XK_BF16, true, G, C> : w8a16_m1_kernel<XK_BF16, false, G, C>)               \
           : (sb ? w8a16_m1_kernel<XK_F32, true, G, C> : w8a16_m1_kernel<XK_F32, false, G, C>))
-#define BSF8_MT(G, T)                                                                                        \
-  (x_bf16 ? (sb ? w8a16_mt_kernel<XK_BF16, true, G, 5, T> : w8a16_mt_kernel<XK_BF16, false, G, 5, T>)           \
-          : (sb ? w8a16_mt_kernel<XK_F32, true, G, 5, T> : w8a16_mt_kernel<XK_F32, false, G, 5, T>))
 #define BSF8_MR(G)                                                                                              \
   (x_bf16 ? (sb ? w8a16_m1_ring_kernel<XK_BF16, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_BF16, false, G, M1R_DEPTH>) \
           : (sb ? w8a16_m1_ring_kernel<XK_F32, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_F32, false, G, M1R_DEPTH>))
     auto k1 = m1.ring ? (m1.g == 2 ? BSF8_MR(2) : m1.g == 3 ? BSF8_MR(3) : BSF8_MR(4))
-              : M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
-                                      : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5)))
-                       : (m1.g == 2 ? BSF8_MT(2, 4) : m1.g == 3 ? BSF8_MT(3, 4) : BSF8_MT(4, 4));
+              : m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
+                            : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5));
 #undef BSF8_M1
-#undef BSF8_MT
 #undef BSF8_MR
     hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
     return device_status(hipGetLastError(), "w8a16_m1 launch");
@@ -1547,28 +1651,36 @@ bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ld
   if (!aligned || M * ldq >= (int64_t(1) << 31)) return false;
   for (int i = 0; i < w.n_members; ++i)
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) return false;
-  return m1_shape(w, true, M).g != 0;
+  return m1_shape(w, true, M).g != 0 || mf_shape(w, true, M).g != 0;
 }
 
 std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
+  const MfShape mf = mf_shape(w, true, M);
+  if (mf.g) {
+    char b[512];
+    return describe_mf(b, sizeof(b), mf,
+                       "arm=w8a8 arithmetic=e4m3 x e4m3 decoded exactly to f32, products summed on the matrix cores "
+                       "per 16-K piece, piece partials x (act scale x weight scale)",
+                       M);
+  }
   const M1Shape m1 = m1_shape(w, true, M);
   char b[448];
   snprintf(b, sizeof(b),
            "arm=w8a8 arithmetic=e4m3 x e4m3 decoded exactly to f32, f32 fma chunk partials x (act scale x weight "
            "scale) | kernel=%s<e4m3> rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, %s, "
            "8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
-           m1.ring ? "w8a16_m1_ring" : M <= 1 ? "w8a16_m1" : "w8a16_mt", m1.rb, m1.g, WAVES, m1.cpw,
-           m1.ring ? "4-chunk load ring" : "all loads first", M <= 1 ? "" : ", 4-token activation slices in LDS",
-           (long long)M, m1.tiles);
+           m1.ring ? "w8a16_m1_ring" : "w8a16_m1", m1.rb, m1.g, WAVES, m1.cpw,
+           m1.ring ? "4-chunk load ring" : "all loads first", "", (long long)M, m1.tiles);
   return b;
 }
 
 bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t xs_sm,
                                int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
+  const MfShape mf = mf_shape(w, true, M);
+  if (mf.g) return launch_mf(w, mf, XK_E4M3, xq, ldq, xs, xs_sm, xs_sk, M, y, y_bf16, ldy, stream);
   const M1Shape m1 = m1_shape(w, true, M);
   if (m1.g == 0) {
-    set_error("UNSUPPORTED: the streaming W8A8 kernels take one token, or 2 to 4 tokens with K up to %d",
-              WAVES * 5 * CHUNK);
+    set_error("UNSUPPORTED: the streaming W8A8 kernels take one to eight tokens");
     return BSF8_E_UNSUPPORTED;
   }
   Args a{};
@@ -1589,15 +1701,12 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
   a.xs_sk = xs_sk;
   const bool sb = w.scale_bf16 != 0;
 #define BSF8_Q1(G, C) (sb ? w8a16_m1_kernel<XK_E4M3, true, G, C> : w8a16_m1_kernel<XK_E4M3, false, G, C>)
-#define BSF8_QT(G) (sb ? w8a16_mt_kernel<XK_E4M3, true, G, 5, 4> : w8a16_mt_kernel<XK_E4M3, false, G, 5, 4>)
 #define BSF8_QR(G) \
   (sb ? w8a16_m1_ring_kernel<XK_E4M3, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_E4M3, false, G, M1R_DEPTH>)
   auto k1 = m1.ring ? (m1.g == 2 ? BSF8_QR(2) : m1.g == 3 ? BSF8_QR(3) : BSF8_QR(4))
-            : M == 1 ? (m1.cpw == 4 ? (m1.g == 2 ? BSF8_Q1(2, 4) : m1.g == 3 ? BSF8_Q1(3, 4) : BSF8_Q1(4, 4))
-                                    : (m1.g == 2 ? BSF8_Q1(2, 5) : m1.g == 3 ? BSF8_Q1(3, 5) : BSF8_Q1(4, 5)))
-                     : (m1.g == 2 ? BSF8_QT(2) : m1.g == 3 ? BSF8_QT(3) : BSF8_QT(4));
+            : m1.cpw == 4 ? (m1.g == 2 ? BSF8_Q1(2, 4) : m1.g == 3 ? BSF8_Q1(3, 4) : BSF8_Q1(4, 4))
+                          : (m1.g == 2 ? BSF8_Q1(2, 5) : m1.g == 3 ? BSF8_Q1(3, 5) : BSF8_Q1(4, 5));
 #undef BSF8_Q1
-#undef BSF8_QT
 #undef BSF8_QR
   hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a8 streaming launch");

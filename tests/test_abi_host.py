@@ -114,8 +114,12 @@ def test_workspace_sizes():
         assert "split_k=3 split_row_tiles=20" in L.bsf8_describe(h, 1, 1024).decode()
         # one to four tokens stream the weight with E4M3 activations and use no
         # workspace; the size reported stays an upper bound over the paths
-        assert "<e4m3>" in L.bsf8_describe(h, 1, 4).decode()
-        assert L.bsf8_workspace_size(h, 1, 4, ctypes.byref(b)) == 0
+        assert "w8a16_m1<e4m3>" in L.bsf8_describe(h, 1, 1).decode()
+        for M in (2, 4):
+            d = L.bsf8_describe(h, 1, M).decode()
+            assert "kernel=w8a16_mf" in d and "e4m3 x e4m3 decoded exactly" in d, d
+            assert L.bsf8_workspace_size(h, 1, M, ctypes.byref(b)) == 0
+        assert "w8a8_gemm" in L.bsf8_describe(h, 1, 5).decode()
         assert L.bsf8_workspace_size(h, 7, 8, ctypes.byref(b)) == 1
     finally:
         L.bsf8_weight_destroy(h)

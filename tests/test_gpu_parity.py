@@ -850,8 +850,9 @@ def test_w8a16_blocks_of_odd_row_counts(sdt, M):
 @pytest.mark.parametrize("sdt", ["bf16", "f32"])
 def test_w8a8_few_tokens_streaming(K, sdt):
     """The W8A8 arm at one to four tokens runs the streaming kernels with E4M3
-    activations (decoded exactly, chunk partials scaled by activation scale x weight
-    scale).  Grouped members of 200 and 70 rows (blocks straddling 128-row scale
+    activations (decoded exactly; one token: chunk partials on the vector ALU, two to
+    four: piece partials on the F32 matrix cores; each scaled by activation scale x
+    weight scale).  Grouped members of 200 and 70 rows (blocks straddling 128-row scale
     blocks, a ragged last member), K with a partial last chunk (4000) and with every
     wave's five chunks (5120), BF16 and F32 grids, token-major and K-major activation
     scales: every output against the oracle."""
@@ -874,7 +875,7 @@ def test_w8a8_few_tokens_streaming(K, sdt):
         x = x_all[:M]
         xq, xs = O.quant_act(x)
         d = w.describe(B.ARM_W8A8, M)
-        assert "<e4m3>" in d, d
+        assert "e4m3 x e4m3 decoded exactly" in d, d
         ref, bound = O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om)
         xqd = t.from_numpy(xq).to(device())
         tm = t.from_numpy(xs).to(device())
@@ -922,6 +923,44 @@ def test_one_token_long_k_ring(K, sdt):
     xq, xs = O.quant_act(x)
     y8 = to_np(B.linear_w8a8(w, t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device()), out_dtype=t.float32))
     assert_within(y8, O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), False, f"ring w8a8 K={K}")
+
+
+@pytest.mark.parametrize("K", [5248, 17408])
+@pytest.mark.parametrize("sdt", ["bf16", "f32"])
+def test_few_tokens_long_k(K, sdt):
+    """Two to eight tokens with more than five chunks per wave, where the activation
+    slices no longer fit the LDS: K = 5248 (waves of 6 chunks and a last one of 5) and
+    17408 (the FFN down projection, 17 per wave); grouped members of 300 and 130 rows
+    (blocks straddling 128-row scale blocks, a ragged last member), M = 2, 5, 8; F32 and
+    BF16 activations, E4M3 activations through the W8A8 arm; every output against the
+    oracle."""
+    t = torch()
+    g = np.random.default_rng(239 + K)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    om = []
+    for r in (300, 130):
+        codes = finite[g.integers(0, finite.size, (r, K))]
+        sc = np.exp2(g.uniform(-10, -3, O.scale_grid_shape(r, K))).astype(np.float32)
+        if sdt == "bf16":
+            sc = O.f32_to_bf16(sc)
+        om.append((codes, sc))
+    dt = t.float32 if sdt == "f32" else t.bfloat16
+    w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.from_numpy(np.asarray(s, np.float32)).to(device()).to(dt))
+                          for c, s in om])
+    x_all = synth.gaussian_activations(239, f"mf_X{K}", 8, K)
+    for M in (2, 5, 8):
+        x = x_all[:M]
+        banner(f"few tokens long K={K} {sdt} M={M}: {w.describe(B.ARM_W8A16, M)} / {w.describe(B.ARM_W8A8, M)}")
+        y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
+        assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"long K w8a16 K={K} M={M}")
+        xb = t.from_numpy(x).to(t.bfloat16)
+        xe = xb.float().numpy()
+        yb = to_np(B.linear_w8a16(w, xb.to(device()), out_dtype=t.bfloat16))
+        assert_within(yb, O.linear_w8a16(xe, om), O.abs_bound_w8a16(xe, om), True, f"long K w8a16 bf16 K={K} M={M}")
+        xq, xs = O.quant_act(x)
+        y8 = to_np(B.linear_w8a8(w, t.from_numpy(xq).to(device()), t.from_numpy(xs).to(device()),
+                                 out_dtype=t.float32))
+        assert_within(y8, O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om), False, f"long K w8a8 K={K} M={M}")
 
 
 def test_one_token_long_k_ring_per_tensor():
