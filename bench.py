@@ -2,6 +2,7 @@
 """Throughput of the block-scaled FP8 linear on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu] [--skip-extra] [--copy-calibration]
+    python bench.py --read-sweep     # what single reads of 8 to 419 MB reach (no projection timed)
 
 One step is the large prefill on M = 8192 synthetic tokens: quantize X
 [8192, 7168] per token in 1x128 groups, then the W8A8 GEMM against the block-FP8
@@ -15,8 +16,8 @@ the replay stream, inputs resident in HBM.
 time from a graph of back-to-back launches, against the dense FP8 MFMA peak,
 with the HBM traffic the profiled counters measured (profiles/traffic.json,
 reported only while the kernel source matches the hash it was measured on).
-``cpu_baseline`` is the oracle (NumPy) on the host cores, on 1024 of the 8192
-tokens of the same step (median of three).
+``cpu_baseline`` is the oracle (NumPy) on the host cores, on the whole step
+(all 8192 tokens; median of three repetitions of about five seconds each).
 
 The same JSON line also carries:
 * ``dense_ffn_prefill``: the dense-FFN prefill pass at M = 1024 (quantize ->
@@ -510,11 +511,11 @@ def bench_w8a8_rotating(torch, B, members, x_np, dev, label):
     return out
 
 
-def cpu_baseline_large(synth, tokens=4096, reps=3):
-    """The oracle on the host cores on a bounded sample of the headline step: the first
-    ``tokens`` of the 8192 tokens quantized (NumPy float32, as defined) and multiplied
-    against all 18432 rows of the weight (float64, the oracle's row-chunked form),
-    ``reps`` times; the median time gives the rate."""
+def cpu_baseline_large(synth, tokens=8192, reps=3):
+    """The oracle on the host cores on the headline step: the first ``tokens`` of the
+    8192 tokens (all of them by default) quantized (NumPy float32, as defined) and
+    multiplied against all 18432 rows of the weight (float64, the oracle's row-chunked
+    form), ``reps`` times; the median time gives the rate."""
     import oracle as O
     wl = synth.config5()
     om = [(m.codes, m.scale_f32()) for m in wl.members]
@@ -536,7 +537,7 @@ def cpu_baseline_large(synth, tokens=4096, reps=3):
     flop = 2.0 * tokens * N * K
     threads, blas = _blas_info()
     return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{tokens} of the 8192 tokens of the headline step (quantize + W8A8 GEMM over all {N} rows, "
+            "sample": f"{tokens} of the {wl.x.shape[0]} tokens of the headline step (quantize + W8A8 GEMM over all {N} rows, "
                       f"K={K}), float32 quantizer and float64 GEMM in NumPy, median of {reps} repetitions "
                       f"({t:.2f} s each)",
             "parts_s_median": {k: round(statistics.median(v), 3) for k, v in parts.items()},
