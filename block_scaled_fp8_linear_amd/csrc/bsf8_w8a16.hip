@@ -48,6 +48,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <string>
+#include <type_traits>
 
 #include "bsf8_internal.h"
 
@@ -1291,6 +1292,224 @@ __global__ __launch_bounds__(THREADS) void w8a16_mf_kernel(Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many tokens (aligned operands): an LDS-staged tile of 256 weight rows x 64
+// tokens per block, so each weight byte is read once per 64 tokens and each
+// activation once per 256 rows.  Per 128-wide K chunk the block copies the
+// chunk's weight bytes (256 rows x 128 bytes) and activations (64 tokens x 128,
+// F32 or BF16) through registers into one of two LDS stages; a chunk's loads go
+// out two chunks before its use.  Its 8 waves split the tile 2
+// (row halves of 128) x 4 (token quarters of 16); per 32-wide K step a wave
+// reads 8 weight fragments (decoded exactly to BF16) and one token fragment,
+// splits the 8 F32 activations of each lane into three BF16 terms (exact, as
+// in the general kernel) and issues 8 x 3 MFMAs.  A wave's 128 rows lie in one
+// 128-row block of its member's scale grid (tiles start at member-local
+// multiples of 256), so after the chunk's 4 steps each 16x16 partial is scaled
+// by one multiplier into the F32 accumulator: the arithmetic is the block
+// operator's, per-chunk partial then block scale.
+//
+// LDS layouts (16-byte units XOR-swizzled so fragment reads are
+// conflict-free): weight row r at r * 128, unit u at (u ^ ((r >> 1) & 7)) * 16
+// (16 lanes reading 8 bytes of 16 consecutive rows meet 32 distinct 8-byte
+// slots of the 256 bytes the 64 banks span); token t at t * 128 * XE, unit u at
+// (u ^ (t & 15)) * 16 (16 lanes reading 16 bytes of 16 consecutive tokens meet
+// 16 distinct units).
+// ---------------------------------------------------------------------------
+constexpr int GW_ROWS = 256;
+constexpr int GW_TOKS = 64;
+constexpr int GW_THREADS = 512;
+
+struct GemmArgs {
+  WeightDev w;
+  int32_t rt0[kMaxMembers + 1];   // first 256-row tile of each member; rt0[n_members] = row tiles
+  int32_t m_tiles;                // 64-token tiles
+  const void* x;
+  void* y;
+  int64_t ldx;
+  int64_t ldy;
+  int32_t M;
+  int32_t y_bf16;
+  int32_t y_vec;                  // 16-byte (F32) / 8-byte (BF16) output stores allowed
+};
+
+template <bool XBF16, bool SBF16>
+__global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
+  constexpr int XE = XBF16 ? 2 : 4;
+  constexpr int A_BYTES = GW_ROWS * CHUNK;              // 32 KiB
+  constexpr int B_BYTES = GW_TOKS * CHUNK * XE;         // 32 KiB (F32) / 16 KiB (BF16)
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_PER = A_BYTES / 16 / GW_THREADS;      // 16-byte pieces per thread: 4
+  constexpr int B_PER = B_BYTES / 16 / GW_THREADS;      // 4 (F32) / 2 (BF16)
+  constexpr int B_UNITS = CHUNK * XE / 16;              // 16-byte units per token row: 32 / 16
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+
+  const int R = blockIdx.x / a.m_tiles, T = blockIdx.x - R * a.m_tiles;
+  int mi = 0;
+  while (mi + 1 < a.w.n_members && R >= a.rt0[mi + 1]) ++mi;
+  const MemberDev mem = a.w.m[mi];
+  const int K = a.w.K, Kb = a.w.Kb;
+  const int r0 = (R - a.rt0[mi]) * GW_ROWS;   // member-local first row
+  const int t0 = T * GW_TOKS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave & 1, wc = wave >> 1;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  // ---- copies of chunk kb into a register slot, then into a stage.  Buffer loads:
+  // a piece past a member's rows, past K or past M reads an offset beyond the
+  // resource (zeros, no traffic), so every chunk issues the same loads.
+  const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
+  const v4i rw = make_rsrc(mem.w, w_bytes);
+  const uint32_t x_bytes = uint32_t(a.M) * uint32_t(a.ldx) * XE;
+  const v4i rx = make_rsrc(a.x, x_bytes);
+  uint4 ra[A_PER], rb[B_PER];
+  // per piece, its byte offset in chunk 0 (past the resource for rows past the
+  // member's end and tokens past M) and the first K element it holds; chunk kb
+  // adds kb * 128 elements through the instruction's scalar offset
+  uint32_t aoff[A_PER], boff[B_PER];
+  int ak[A_PER], bk[B_PER];
+#pragma unroll
+  for (int j = 0; j < A_PER; ++j) {
+    const int pc = tid + GW_THREADS * j;
+    const int row = pc >> 3, u = pc & 7;
+    ak[j] = u * 16;
+    aoff[j] = r0 + row < mem.rows ? uint32_t(r0 + row) * uint32_t(K) + uint32_t(ak[j]) : w_bytes;
+  }
+#pragma unroll
+  for (int j = 0; j < B_PER; ++j) {
+    const int pc = tid + GW_THREADS * j;
+    const int t = pc / B_UNITS, u = pc - t * B_UNITS;
+    bk[j] = u * (16 / XE);
+    boff[j] = t0 + t < a.M ? (uint32_t(t0 + t) * uint32_t(a.ldx) + uint32_t(bk[j])) * uint32_t(XE) : x_bytes;
+  }
+  auto load = [&](int kb) {
+    const int kt = K - kb * CHUNK;   // K elements left from this chunk on (<= 0 past the last)
+    const int sa = __builtin_amdgcn_readfirstlane(kb * CHUNK), sx = __builtin_amdgcn_readfirstlane(kb * CHUNK * XE);
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j)
+      ra[j] = as_u4(bsf8_raw_buffer_load_b128(rw, ak[j] < kt ? int(aoff[j]) : int(w_bytes), sa, kReuseLoadAux));
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j)
+      rb[j] = as_u4(bsf8_raw_buffer_load_b128(rx, bk[j] < kt ? int(boff[j]) : int(x_bytes), sx, 0));
+  };
+  auto store = [&](uint8_t* st) {
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j) {
+      const int pc = tid + GW_THREADS * j;
+      const int row = pc >> 3, u = pc & 7;
+      *reinterpret_cast<uint4*>(st + row * CHUNK + ((u ^ ((row >> 1) & 7)) << 4)) = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j) {
+      const int pc = tid + GW_THREADS * j;
+      const int t = pc / B_UNITS, u = pc - t * B_UNITS;
+      *reinterpret_cast<uint4*>(st + A_BYTES + t * (CHUNK * XE) + ((u ^ (t & 15)) << 4)) = rb[j];
+    }
+  };
+
+  // the wave's scale-grid row (its 128 rows lie in one block row; a half past the
+  // member's last row reads the last grid row, its rows being zeros)
+  const int srow = min((r0 + wr * 128) >> 7, (mem.rows - 1) >> 7);
+  auto wscale = [&](int kb) {
+    const int64_t i = int64_t(srow) * a.w.s_rs + int64_t(kb) * a.w.s_cs;
+    return SBF16 ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(mem.s)[i]) << 16)
+                 : static_cast<const float*>(mem.s)[i];
+  };
+
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // chunk k goes through stage k & 1: loaded into registers two chunks before its
+  // use and stored into its stage one chunk before
+  load(0);
+  store(lds);
+  load(1);
+  const int tw = wc * 16 + l16;   // the lane's token within the tile (B fragments)
+  // the fragments of K step st: 8 weight fragments decoded to BF16, the token
+  // fragment split into three BF16 terms (one for BF16 activations)
+  constexpr int NT = XBF16 ? 1 : 3;
+  auto frag = [&](const uint8_t* cur, int st, v8bf (&af)[8], v8bf (&bt)[3]) {
+    if (XBF16) {
+      const int u = 4 * st + g;   // a 16-byte unit holds 8 BF16
+      const uint4 q = *reinterpret_cast<const uint4*>(cur + A_BYTES + tw * (CHUNK * XE) + ((u ^ (tw & 15)) << 4));
+      bt[0] = __builtin_bit_cast(v8bf, q);
+    } else {
+      const int u0 = 8 * st + 2 * g;
+      const uint4 q0 = *reinterpret_cast<const uint4*>(cur + A_BYTES + tw * (CHUNK * XE) + ((u0 ^ (tw & 15)) << 4));
+      const uint4 q1 =
+          *reinterpret_cast<const uint4*>(cur + A_BYTES + tw * (CHUNK * XE) + (((u0 + 1) ^ (tw & 15)) << 4));
+      const float xv[8] = {__uint_as_float(q0.x), __uint_as_float(q0.y), __uint_as_float(q0.z), __uint_as_float(q0.w),
+                           __uint_as_float(q1.x), __uint_as_float(q1.y), __uint_as_float(q1.z), __uint_as_float(q1.w)};
+      split8(xv, bt[0], bt[1], bt[2]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // row 16 i + l16 of the wave's half, K bytes 32 st + 8 g
+      const int row = wr * 128 + 16 * i + l16;
+      const int u = 2 * st + (g >> 1);
+      const uint2 wq =
+          *reinterpret_cast<const uint2*>(cur + row * CHUNK + ((u ^ ((row >> 1) & 7)) << 4) + ((g & 1) << 3));
+      af[i] = cvt8(wq.x, wq.y);
+    }
+  };
+  // a chunk: per K step the fragments, then its MFMAs with the terms outermost,
+  // so 8 independent MFMAs sit between two that share an accumulator
+  auto compute = [&](const uint8_t* cur, int kb) {
+    const float sw = wscale(kb);
+    v4f pr[8];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      v8bf af[8], bt[3];
+      frag(cur, st, af, bt);
+#pragma unroll
+      for (int tm = 0; tm < NT; ++tm)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pr[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bt[tm],
+                                                          (st == 0 && tm == 0) ? v4f{0.f, 0.f, 0.f, 0.f} : pr[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][r] = fmaf(pr[i][r], sw, acc[i][r]);
+  };
+  for (int kb = 0; kb < Kb; ++kb) {
+    __syncthreads();   // chunk kb's stage is complete; chunk kb - 1's reads are done
+    if (kb + 1 < Kb) store(lds + ((kb + 1) & 1) * STAGE);
+    load(kb + 2);   // past the last chunk: zeros, no traffic
+    compute(lds + (kb & 1) * STAGE, kb);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- store: lane holds rows 16 i + 4 g + r (r < 4) of the wave's half, token l16 of its quarter
+  const int t = t0 + wc * 16 + l16;
+  if (t >= a.M) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = r0 + wr * 128 + 16 * i + 4 * g;   // member-local row of register 0
+    const int nvalid = mem.rows - n;
+    if (nvalid <= 0) continue;
+    const int64_t off = int64_t(t) * a.ldy + mem.col0 + n;
+    if (a.y_bf16) {
+      uint16_t* yp = static_cast<uint16_t*>(a.y) + off;
+      if (nvalid >= 4 && a.y_vec) {
+        *reinterpret_cast<uint2*>(yp) = make_uint2(uint32_t(f32_to_bf16_rne(acc[i][0])) | (uint32_t(f32_to_bf16_rne(acc[i][1])) << 16),
+                                                   uint32_t(f32_to_bf16_rne(acc[i][2])) | (uint32_t(f32_to_bf16_rne(acc[i][3])) << 16));
+      } else {
+        for (int r = 0; r < 4 && r < nvalid; ++r) yp[r] = f32_to_bf16_rne(acc[i][r]);
+      }
+    } else {
+      float* yp = static_cast<float*>(a.y) + off;
+      if (nvalid >= 4 && a.y_vec) {
+        *reinterpret_cast<float4*>(yp) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+      } else {
+        for (int r = 0; r < 4 && r < nvalid; ++r) yp[r] = acc[i][r];
+      }
+    }
+  }
+}
+
 struct Plan {
   TileMap tm;
   int col_tiles;
@@ -1496,6 +1715,60 @@ char* describe_mf(char* b, size_t n, const MfShape& m, const char* arm, int64_t 
   return b;
 }
 
+int gemm_row_tiles(const WeightDev& w, int32_t* rt0);
+
+// The LDS-staged GEMM kernel runs for aligned operands when its grid fills at
+// least half the compute units: a block takes about the same time whatever
+// the grid (grouped Q/K/V: 121-130 us from 64 to 512 tokens), so with fewer
+// blocks the general kernel, which splits K inside many small blocks, is
+// faster (44 / 84 us at 64 / 128 tokens against 121 us; at 256 tokens 164
+// against 122 us, at 512 325 against 129 us).
+bool gemm_applies(const WeightDev& w, bool aligned, int64_t M) {
+  if (!aligned || M < GW_TOKS) return false;
+  const int64_t blocks = int64_t(gemm_row_tiles(w, nullptr)) * ((M + GW_TOKS - 1) / GW_TOKS);
+  return 2 * blocks >= w16_device_cus();
+}
+
+int gemm_row_tiles(const WeightDev& w, int32_t* rt0) {
+  int t = 0;
+  for (int i = 0; i < w.n_members; ++i) {
+    if (rt0) rt0[i] = t;
+    t += (w.m[i].rows + GW_ROWS - 1) / GW_ROWS;
+  }
+  if (rt0) rt0[w.n_members] = t;
+  return t;
+}
+
+bsf8_status launch_gemm(const WeightDev& w, const void* x, bool x_bf16, int64_t M, int64_t ldx, void* y, bool y_bf16,
+                        int64_t ldy, hipStream_t stream) {
+  GemmArgs a{};
+  a.w = w;
+  const int rt = gemm_row_tiles(w, a.rt0);
+  a.m_tiles = int32_t((M + GW_TOKS - 1) / GW_TOKS);
+  a.x = x;
+  a.y = y;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = int32_t(M);
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  // vector stores of 4 outputs need every member's 4-row runs to start aligned
+  const int ye = y_bf16 ? 2 : 4;
+  bool vec = reinterpret_cast<uintptr_t>(y) % (4 * ye) == 0 && ldy % 4 == 0;
+  for (int i = 0; i < w.n_members; ++i) vec = vec && w.m[i].col0 % 4 == 0;
+  a.y_vec = vec ? 1 : 0;
+  const int64_t blocks = int64_t(rt) * a.m_tiles;
+  if (blocks == 0) return BSF8_OK;
+  if (blocks >= (int64_t(1) << 31)) {
+    set_error("UNSUPPORTED: %lld blocks", (long long)blocks);
+    return BSF8_E_UNSUPPORTED;
+  }
+  const bool sb = w.scale_bf16 != 0;
+  auto k = x_bf16 ? (sb ? w8a16_gemm_kernel<true, true> : w8a16_gemm_kernel<true, false>)
+                  : (sb ? w8a16_gemm_kernel<false, true> : w8a16_gemm_kernel<false, false>);
+  hipLaunchKernelGGL(k, dim3(unsigned(blocks)), dim3(GW_THREADS), 0, stream, a);
+  return device_status(hipGetLastError(), "w8a16_gemm launch");
+}
+
 }  // namespace
 
 size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
@@ -1506,6 +1779,16 @@ int small_depth(int chunks_per_wave) {
 }
 
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
+  if (gemm_applies(w, aligned, M)) {
+    char b[448];
+    const int rt = gemm_row_tiles(w, nullptr);
+    snprintf(b, sizeof(b),
+             "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
+             "mfma_f32_16x16x32_bf16 | kernel=w8a16_gemm tile=%dx%d waves=8 lds=2 stages (register-staged copies) | "
+             "M=%lld blocks=%lld",
+             GW_ROWS, GW_TOKS, (long long)M, (long long)rt * ((M + GW_TOKS - 1) / GW_TOKS));
+    return b;
+  }
   const MfShape mf = mf_shape(w, aligned, M);
   if (mf.g) {
     char b[512];
@@ -1557,6 +1840,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   if (p.tiles == 0) return BSF8_OK;
   const MfShape mf = mf_shape(w, aligned, M);
   if (mf.g) return launch_mf(w, mf, x_bf16 ? XK_BF16 : XK_F32, x, ldx, nullptr, 0, 0, M, y, y_bf16, ldy, stream);
+  if (gemm_applies(w, aligned, M)) return launch_gemm(w, x, x_bf16, M, ldx, y, y_bf16, ldy, stream);
   const M1Shape m1 = m1_shape(w, aligned, M);
   if (m1.g) {
     Args a{};

@@ -530,7 +530,8 @@ RNE_W8A16 = [
     ("two_to_four_tokens", (300, 130), 1024, 3),
     ("few_token_mfma", (300, 130), 1024, 6),
     ("general_mfma", (300, 130), 1024, 40),
-    ("general_mfma_64_row_blocks", (300, 130), 1024, 96),
+    ("lds_staged_gemm", (4100, 700), 1024, 448),
+    ("lds_staged_gemm_element_stores", (4101, 700), 1024, 400),
     ("general_bytewise_k1000", (300, 130), 1000, 5),
 ]
 
@@ -552,6 +553,49 @@ def test_w8a16_bf16_output_is_rne_of_f32_output(name, rows, K, M):
     differ = int(np.count_nonzero(y16 != want))
     record(f"w8a16 bf16 rne {name}", differ == 0, kind="bit-exact", outputs=int(y32.size), differing=differ)
     assert differ == 0, f"{differ} BF16 outputs are not RNE of the F32 output"
+
+
+@pytest.mark.parametrize("sdt", ["bf16", "f32", "per_tensor"])
+def test_w8a16_lds_gemm(sdt):
+    """Many tokens through the LDS-staged W8A16 kernel (256-row x 64-token tiles, taken
+    when its grid fills at least half the compute units): grouped members of 4101, 700 and
+    77 rows (a last tile past each member's end, a member shorter than one scale block, a
+    first column that is not a multiple of 4 so outputs go out element by element),
+    K = 1040 (eight whole 128-wide blocks and a 16-wide tail), M = 385 and 448 (a last
+    token tile with one token, and whole tiles); F32 and BF16 activations; BF16, F32 and
+    per-tensor scales.  Every output against the oracle."""
+    t = torch()
+    g = np.random.default_rng(241)
+    K = 1040
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    om, dev_members = [], []
+    for r in (4101, 700, 77):
+        codes = finite[g.integers(0, finite.size, (r, K))]
+        if sdt == "per_tensor":
+            sc = np.float32(2.0 ** g.uniform(-9, -3))
+            om.append((codes, sc))
+            dev_members.append((t.from_numpy(codes).to(device()), t.tensor(float(sc), dtype=t.float32, device=device())))
+        else:
+            sc = np.exp2(g.uniform(-10, -3, O.scale_grid_shape(r, K))).astype(np.float32)
+            if sdt == "bf16":
+                sc = O.f32_to_bf16(sc)
+            om.append((codes, sc))
+            dt = t.float32 if sdt == "f32" else t.bfloat16
+            dev_members.append((t.from_numpy(codes).to(device()), t.from_numpy(np.asarray(sc, np.float32)).to(device()).to(dt)))
+    w = B.BlockFP8Weight(dev_members, block=(0, 0) if sdt == "per_tensor" else (128, 128))
+    x_all = synth.gaussian_activations(241, f"gemm16_X_{sdt}", 448, K)
+    for M in (385, 448):
+        x = x_all[:M]
+        d = w.describe(B.ARM_W8A16, M)
+        if t.cuda.get_device_properties(0).multi_processor_count <= 256:
+            assert "kernel=w8a16_gemm" in d, d
+        banner(f"w8a16 lds gemm {sdt} M={M}: {d}")
+        y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
+        assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"lds gemm {sdt} M={M}")
+        xb = t.from_numpy(x).to(t.bfloat16)
+        xe = xb.float().numpy()
+        yb = to_np(B.linear_w8a16(w, xb.to(device()), out_dtype=t.bfloat16))
+        assert_within(yb, O.linear_w8a16(xe, om), O.abs_bound_w8a16(xe, om), True, f"lds gemm bf16 {sdt} M={M}")
 
 
 RNE_W8A8 = [
