@@ -16,7 +16,9 @@
 //    summed on the matrix cores (w8a16_mf_kernel, v_mfma_f32_4x4x1f32);
 //  * 5 to 8 tokens, and 2 to 4 with a longer K: the few-token MFMA kernel
 //    (w8a16_small_m_kernel);
-//  * more tokens, or any unaligned operand: the general MFMA kernel.
+//  * many tokens, once 256-row x 64-token tiles fill half the compute units:
+//    the LDS-staged GEMM (w8a16_gemm_kernel);
+//  * the tokens in between, or any unaligned operand: the general MFMA kernel.
 // A plain F32 FMA loop needs ~M FMAs per weight byte, which beyond four tokens
 // outweighs the stream, so there the products run on the BF16 matrix cores
 // without losing any activation bit:
