@@ -1302,9 +1302,13 @@ __global__ __launch_bounds__(THREADS) void w8a16_mf_kernel(Args a) {
 // F32 or BF16) through registers into one of two LDS stages; a chunk's loads go
 // out two chunks before its use.  Its 8 waves split the tile 2
 // (row halves of 128) x 4 (token quarters of 16); per 32-wide K step a wave
-// reads 8 weight fragments (decoded exactly to BF16) and one token fragment,
-// splits the 8 F32 activations of each lane into three BF16 terms (exact, as
-// in the general kernel) and issues 8 x 3 MFMAs.  A wave's 128 rows lie in one
+// reads 8 weight fragments (decoded exactly to BF16) and the token fragment's
+// three BF16 terms and issues 8 x 3 MFMAs.  F32 activations are split into the
+// three exact terms (as in the general kernel) once per value and block, when
+// the chunk is stored: three BF16 planes, so a stage holds 32 KiB of weights
+// and 48 KiB of activations and the two stages fill the 160 KiB LDS (splitting
+// per wave instead, each token fragment being split by both row halves, cost
+// 134 against 112 us at M = 512 in a timing variant without the split).  A wave's 128 rows lie in one
 // 128-row block of its member's scale grid (tiles start at member-local
 // multiples of 256), so after the chunk's 4 steps each 16x16 partial is scaled
 // by one multiplier into the F32 accumulator: the arithmetic is the block
@@ -1313,9 +1317,9 @@ __global__ __launch_bounds__(THREADS) void w8a16_mf_kernel(Args a) {
 // LDS layouts (16-byte units XOR-swizzled so fragment reads are
 // conflict-free): weight row r at r * 128, unit u at (u ^ ((r >> 1) & 7)) * 16
 // (16 lanes reading 8 bytes of 16 consecutive rows meet 32 distinct 8-byte
-// slots of the 256 bytes the 64 banks span); token t at t * 128 * XE, unit u at
-// (u ^ (t & 15)) * 16 (16 lanes reading 16 bytes of 16 consecutive tokens meet
-// 16 distinct units).
+// slots of the 256 bytes the 64 banks span); in each activation plane, token t
+// at t * 256, unit u (8 BF16) at (u ^ (t & 15)) * 16 (16 lanes reading 16 bytes
+// of 16 consecutive tokens meet 16 distinct units).
 // ---------------------------------------------------------------------------
 constexpr int GW_ROWS = 256;
 constexpr int GW_TOKS = 64;
@@ -1337,12 +1341,12 @@ struct GemmArgs {
 template <bool XBF16, bool SBF16>
 __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
   constexpr int XE = XBF16 ? 2 : 4;
+  constexpr int NT = XBF16 ? 1 : 3;                     // BF16 planes of the activations
+  constexpr int PLANE = GW_TOKS * CHUNK * 2;            // 16 KiB: 64 tokens x 128 BF16
   constexpr int A_BYTES = GW_ROWS * CHUNK;              // 32 KiB
-  constexpr int B_BYTES = GW_TOKS * CHUNK * XE;         // 32 KiB (F32) / 16 KiB (BF16)
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int STAGE = A_BYTES + NT * PLANE;           // 80 KiB (F32: two stages fill the LDS) / 48 KiB
   constexpr int A_PER = A_BYTES / 16 / GW_THREADS;      // 16-byte pieces per thread: 4
-  constexpr int B_PER = B_BYTES / 16 / GW_THREADS;      // 4 (F32) / 2 (BF16)
-  constexpr int B_UNITS = CHUNK * XE / 16;              // 16-byte units per token row: 32 / 16
+  constexpr int B_PER = GW_TOKS * CHUNK * XE / 16 / GW_THREADS;   // 4 (F32: 16 consecutive values) / 2
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
 
   const int R = blockIdx.x / a.m_tiles, T = blockIdx.x - R * a.m_tiles;
@@ -1377,12 +1381,14 @@ __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
     ak[j] = u * 16;
     aoff[j] = r0 + row < mem.rows ? uint32_t(r0 + row) * uint32_t(K) + uint32_t(ak[j]) : w_bytes;
   }
+  // activations: F32, thread (t, q) = (tid / 8, tid % 8) holds elements [16 q, 16 q + 16)
+  // of token t (4 pieces); BF16, the thread holds elements [8 u, 8 u + 8) of token
+  // t for u = 2 (tid % 8) and u + 1
+  const int bt_t = tid >> 3, bt_q = tid & 7;
 #pragma unroll
   for (int j = 0; j < B_PER; ++j) {
-    const int pc = tid + GW_THREADS * j;
-    const int t = pc / B_UNITS, u = pc - t * B_UNITS;
-    bk[j] = u * (16 / XE);
-    boff[j] = t0 + t < a.M ? (uint32_t(t0 + t) * uint32_t(a.ldx) + uint32_t(bk[j])) * uint32_t(XE) : x_bytes;
+    bk[j] = XBF16 ? (2 * bt_q + j) * 8 : 16 * bt_q + 4 * j;
+    boff[j] = t0 + bt_t < a.M ? (uint32_t(t0 + bt_t) * uint32_t(a.ldx) + uint32_t(bk[j])) * uint32_t(XE) : x_bytes;
   }
   auto load = [&](int kb) {
     const int kt = K - kb * CHUNK;   // K elements left from this chunk on (<= 0 past the last)
@@ -1401,11 +1407,26 @@ __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
       const int row = pc >> 3, u = pc & 7;
       *reinterpret_cast<uint4*>(st + row * CHUNK + ((u ^ ((row >> 1) & 7)) << 4)) = ra[j];
     }
+    // activation plane p, token t: 16 units of 8 BF16, unit u at (u ^ (t & 15)) * 16
+    uint8_t* bp = st + A_BYTES + bt_t * (CHUNK * 2);
+    if (XBF16) {
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j) {
-      const int pc = tid + GW_THREADS * j;
-      const int t = pc / B_UNITS, u = pc - t * B_UNITS;
-      *reinterpret_cast<uint4*>(st + A_BYTES + t * (CHUNK * XE) + ((u ^ (t & 15)) << 4)) = rb[j];
+      for (int j = 0; j < B_PER; ++j)
+        *reinterpret_cast<uint4*>(bp + (((2 * bt_q + j) ^ (bt_t & 15)) << 4)) = rb[j];
+    } else {
+      // the exact three-term split, once per value and block
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float xv[8] = {__uint_as_float(rb[2 * h].x), __uint_as_float(rb[2 * h].y), __uint_as_float(rb[2 * h].z),
+                             __uint_as_float(rb[2 * h].w), __uint_as_float(rb[2 * h + 1].x),
+                             __uint_as_float(rb[2 * h + 1].y), __uint_as_float(rb[2 * h + 1].z),
+                             __uint_as_float(rb[2 * h + 1].w)};
+        v8bf t3[3];
+        split8(xv, t3[0], t3[1], t3[2]);
+        const int pos = ((2 * bt_q + h) ^ (bt_t & 15)) << 4;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) *reinterpret_cast<v8bf*>(bp + p * PLANE + pos) = t3[p];
+      }
     }
   };
 
@@ -1428,23 +1449,13 @@ __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
   store(lds);
   load(1);
   const int tw = wc * 16 + l16;   // the lane's token within the tile (B fragments)
-  // the fragments of K step st: 8 weight fragments decoded to BF16, the token
-  // fragment split into three BF16 terms (one for BF16 activations)
-  constexpr int NT = XBF16 ? 1 : 3;
+  // the fragments of K step st: 8 weight fragments decoded to BF16 and the token
+  // fragment's BF16 terms (one per plane)
   auto frag = [&](const uint8_t* cur, int st, v8bf (&af)[8], v8bf (&bt)[3]) {
-    if (XBF16) {
-      const int u = 4 * st + g;   // a 16-byte unit holds 8 BF16
-      const uint4 q = *reinterpret_cast<const uint4*>(cur + A_BYTES + tw * (CHUNK * XE) + ((u ^ (tw & 15)) << 4));
-      bt[0] = __builtin_bit_cast(v8bf, q);
-    } else {
-      const int u0 = 8 * st + 2 * g;
-      const uint4 q0 = *reinterpret_cast<const uint4*>(cur + A_BYTES + tw * (CHUNK * XE) + ((u0 ^ (tw & 15)) << 4));
-      const uint4 q1 =
-          *reinterpret_cast<const uint4*>(cur + A_BYTES + tw * (CHUNK * XE) + (((u0 + 1) ^ (tw & 15)) << 4));
-      const float xv[8] = {__uint_as_float(q0.x), __uint_as_float(q0.y), __uint_as_float(q0.z), __uint_as_float(q0.w),
-                           __uint_as_float(q1.x), __uint_as_float(q1.y), __uint_as_float(q1.z), __uint_as_float(q1.w)};
-      split8(xv, bt[0], bt[1], bt[2]);
-    }
+    const int ub = 4 * st + g;   // K elements [32 st + 8 g, + 8): one unit of each plane
+#pragma unroll
+    for (int p = 0; p < NT; ++p)
+      bt[p] = *reinterpret_cast<const v8bf*>(cur + A_BYTES + p * PLANE + tw * (CHUNK * 2) + ((ub ^ (tw & 15)) << 4));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // row 16 i + l16 of the wave's half, K bytes 32 st + 8 g
