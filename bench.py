@@ -834,9 +834,10 @@ def main():
         line["qkv_w8a16_m512"] = {
             "workload": q16["workload"], "us": round(q16["us"], 2), "p10": round(q16["us_p10"], 2),
             "p90": round(q16["us_p90"], 2), "launches": q16["launches"], "path": q16["describe"],
-            "roofline": {"bound": "mfma", "kernel": "w8a16 (general, M=512)", "achieved": round(q16["tflops"], 2),
-                         "peak": round(BF16_PEAK_TFLOPS / 3, 1), "unit": "TFLOP/s",
-                         "frac": round(q16["tflops"] / (BF16_PEAK_TFLOPS / 3), 4), "traffic": None,
+            "roofline": {"bound": "mfma", "kernel": "w8a16_gemm (LDS-staged 256x64 tiles, M=512)",
+                         "achieved": round(q16["tflops"], 2), "peak": round(BF16_PEAK_TFLOPS / 3, 1), "unit": "TFLOP/s",
+                         "frac": round(q16["tflops"] / (BF16_PEAK_TFLOPS / 3), 4),
+                         "traffic": profiled_traffic("w8a16_gemm_qkv_m512"),
                          "peak_note": "exact F32 activations as three BF16 terms: a third of the published BF16 MFMA "
                                       "peak; v_mfma_f32_16x16x32_bf16 itself issues once per 28-32 cycles per SIMD "
                                       "(1.1-1.27 PFLOP/s measured), half the published rate"}}
