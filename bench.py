@@ -66,19 +66,28 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 ROTATE_BYTES = 640 << 20     # > 512 MiB of distinct weight copies for the GEMV
 
 
+def code_digest(path):
+    """sha256[:16] of a C++/HIP source with its comments and whitespace removed: a change to the code
+    changes it, a change to a comment does not."""
+    import hashlib, re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def profiled_traffic(key):
     """Bytes per launch moved between L2 and memory for ``key``, from the committed counter runs in
-    profiles/traffic.json, or None when the kernel source has changed since those counters were taken."""
-    import hashlib
+    profiles/traffic.json, or None when the kernel's source code has changed since those counters were
+    taken."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             entry = json.load(f)[key]
-        src = os.path.join(ROOT, "block_scaled_fp8_linear_amd", "csrc", entry["source"])
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()[:16]
+        digest = code_digest(os.path.join(ROOT, "block_scaled_fp8_linear_amd", "csrc", entry["source"]))
     except (OSError, KeyError, ValueError):
         return None
-    return entry["traffic_bytes"] if digest == entry["source_sha256_16"] else None
+    return entry["traffic_bytes"] if digest == entry["code_sha256_16"] else None
 
 
 def log(msg):

@@ -31,7 +31,8 @@
 //  accumulation, as the pages state, at about three BF16 MFMAs per 16x16x32 step.
 //  (Inputs below ~2^-100 in magnitude may lose their lowest remainder bits.)
 //
-// Work decomposition (no inter-block traffic):
+// Work decomposition of the general kernel (the others, described where they
+// are defined, follow the same pattern; no inter-block traffic):
 //  * A block owns 32 consecutive rows of one member (two 16-row MFMA tiles,
 //    member-local, so each tile lies in one row of that member's scale grid
 //    and its weight scale is one scalar per 128-wide K chunk), up to 16 tokens,
@@ -43,8 +44,8 @@
 //    weight scale into the F32 accumulator.  Loads run one chunk ahead.
 //  * The 8 per-wave partial tiles are added in LDS in wave order (a fixed
 //    order, so results are reproducible) and stored.
-//  * Decode shapes give about one block per CU (N = 8144 rows -> 256 blocks),
-//    and the weight stream is the only HBM traffic.
+//  * At decode shapes (N = 8144 rows -> 256 blocks of 32 rows) that is about
+//    one block per CU, and the weight stream is the only HBM traffic.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

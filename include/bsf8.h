@@ -285,9 +285,11 @@ bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, si
  * ("Qwen checkpoints with block FP8 weights", block-path and operator
  *  paragraphs; "FP8 Native Serving", section "Native FP8 vs dequant-to-BF16":
  *  the weights are decoded where they are consumed, not in a copy.)
- * Kernels: one token and two to four tokens run F32 FMAs against weights
- * decoded exactly to F32 (aligned operands, K <= 5120); more tokens run the
- * BF16 matrix cores on an exact three-term split of each F32 activation.
+ * Kernels (aligned operands): one token runs F32 FMAs on the vector ALUs
+ * against weights decoded exactly to F32 (any K); two to four tokens with
+ * K <= 5120 form the same F32 products on the F32 matrix cores; other token
+ * counts and shapes run the BF16 matrix cores on an exact three-term split of
+ * each F32 activation (an LDS-staged GEMM for hundreds of tokens).
  *
  * x : [M, K] F32 or BF16, leading dimension ldx (elements), 16-byte aligned
  *     rows when K allows.
