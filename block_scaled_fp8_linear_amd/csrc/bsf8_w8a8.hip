@@ -313,9 +313,7 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
 // buffer unit returns as zeros.
 // ---------------------------------------------------------------------------
 
-constexpr int FBN = 256, FBM = 256, FTHREADS = 512;
-constexpr int F_SA = FBN * KBYTES + FBM * KBYTES;  // offset of the token scales in a stage
-constexpr int F_STAGE = F_SA + FBM * 4;           // 64 KiB of operands + 1 KiB of scales
+constexpr int FTHREADS = 512;
 // Operand copies: 1 KiB wave copies (8 rows x 128 bytes) per stage, 32 weight
 // slabs and 32 token slabs, issued by waves 0-3 between the MFMAs of their
 // chains.  The vector memory unit takes a 1 KiB copy about as fast as it
@@ -326,8 +324,23 @@ constexpr int F_STAGE = F_SA + FBM * 4;           // 64 KiB of operands + 1 KiB 
 // (Copies spread over all eight waves go out late: the younger waves' chains
 // lag behind.)
 constexpr int F_COPIERS = 4;
-constexpr int F_A_LOADS = FBN / 8 / F_COPIERS;  // weight slabs per copying wave
-constexpr int F_B_LOADS = FBM / 8 / F_COPIERS;  // token slabs per copying wave
+// The block tile: T weight rows x T tokens over 2 x 4 waves.  T = 256 is the
+// main tile; T = 128 serves grids that 256 x 256 tiles would leave mostly to
+// split-K (Q/K/V [8144, 5120] at M = 512: 64 tiles split 4 ways, 43.9 us,
+// against 256 whole 128 x 128 tiles, 34.7 us).  A 128 x 128 K block reads
+// 12 KiB of fragments per wave for an eighth of the MFMAs, so per FLOP it is
+// slower (about 0.55 of a 256 x 256 step for a quarter of the work); the plan
+// takes whichever its cost model finds cheaper.
+template <int T>
+struct FTile {
+  static constexpr int BN = T, BM = T;                // weight rows and tokens per block tile
+  static constexpr int WN = BN / 2, WM = BM / 4;      // per wave
+  static constexpr int TI = WN / 16, TJ = WM / 16;    // 16 x 16 MFMA tiles per wave
+  static constexpr int SA = BN * KBYTES + BM * KBYTES;  // offset of the token scales in a stage
+  static constexpr int STAGE = SA + BM * 4;             // operands + token scales
+  static constexpr int A_LOADS = BN / 8 / F_COPIERS;    // weight slabs per copying wave
+  static constexpr int B_LOADS = BM / 8 / F_COPIERS;    // token slabs per copying wave
+};
 constexpr int XCDS = 8;
 // Row tiles per L2 group: 16 when there are at most 4 token tiles (M <= 1024)
 // and more tiles than one round, else 8 (measured: gate/up at M = 1024,
@@ -338,7 +351,7 @@ constexpr int F_MAX_KB = 1024;  // K up to 131072 on the fast path
 
 struct FastArgs {
   WeightDev w;
-  int32_t rt0[kMaxMembers + 1];   // first 256-row tile of each member
+  int32_t rt0[kMaxMembers + 1];   // first row tile (T rows) of each member
   const uint8_t* xq;
   const float* xs;
   void* y;
@@ -355,7 +368,7 @@ struct FastArgs {
   int32_t group_rows;   // row tiles per L2 group
   // split-K for the row tiles from rt_split0 on: their K blocks are cut into
   // `splits` ranges of kb_per_split; split s of tile (R, mt) writes its F32
-  // partial tile to ws + s * M * ldws, columns (R - rt_split0) * FBN + [0, FBN),
+  // partial tile to ws + s * M * ldws, columns (R - rt_split0) * T + [0, T),
   // and a second kernel adds the partials.  Row tiles below rt_split0 run
   // whole and write y.
   int32_t splits;
@@ -377,28 +390,28 @@ __device__ __forceinline__ v4i make_rsrc(const void* p, uint32_t bytes) {
 
 constexpr int F_OUT_PITCH = 144;  // bytes per token row of the store staging (128 + 16: no bank conflicts)
 
-// Writes a wave's 128 x 64 result tile through LDS so that each lane stores 16
+// Writes a wave's 16 STI x 16 STJ result tile through LDS so that each lane stores 16
 // contiguous bytes of one token row (8 lanes fill a 128-byte line).  In the
 // MFMA layout a lane holds 4 consecutive outputs of one token, and 16 lanes of
 // one instruction touch 16 rows, which turns into many small partial-line
-// writes.  `buf` is this wave's 64 x F_OUT_PITCH staging area; the tile goes
+// writes.  `buf` is this wave's 16 STJ x F_OUT_PITCH staging area; the tile goes
 // out in rounds of 128 bytes per token row (4 row tiles of bf16, 2 of f32).
 //
 // NT: non-temporal stores, for an output too large to stay in the Infinity
 // Cache for its consumer anyway; they keep it from evicting the operands the
 // GEMM is still reading (M = 8192, N = 18432: 302 MB of output, 2-3 % faster).
 typedef unsigned int bsf8_u4v __attribute__((ext_vector_type(4)));
-template <bool YBF16, bool NT = false>
-__device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uint8_t* buf, void* y, int64_t ldy,
+template <int STI, int STJ, bool YBF16, bool NT = false>
+__device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[STI][STJ], uint8_t* buf, void* y, int64_t ldy,
                                                    int64_t col0, int n_base, int n_end, int m_base, int M, int lane) {
   constexpr int ESZ = YBF16 ? 2 : 4;
   constexpr int PER_ROUND = 128 / (16 * ESZ);  // row tiles per round
   constexpr int EPC = 16 / ESZ;                // elements per 16-byte chunk
   const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int i0 = 0; i0 < TI; i0 += PER_ROUND) {
+  for (int i0 = 0; i0 < STI; i0 += PER_ROUND) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
+    for (int j = 0; j < STJ; ++j) {
 #pragma unroll
       for (int ii = 0; ii < PER_ROUND; ++ii) {
         const v4f& v = acc[i0 + ii][j];
@@ -411,7 +424,7 @@ __device__ __forceinline__ void store_tile_via_lds(const v4f (&acc)[TI][TJ], uin
       }
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 2 * STJ; ++t) {   // the wave's 16 STJ token rows, 8 at a time
       const int row = 8 * t + (lane >> 3), ch = lane & 7;
       const uint4 v = *reinterpret_cast<const uint4*>(buf + row * F_OUT_PITCH + ch * 16);
       const int m = m_base + row;
@@ -455,8 +468,12 @@ __device__ __forceinline__ void mfma_bf16_pair(v4f& c, const v8i& a, const v8i& 
 // DENSE: BF16 operands without scales (the upcast weight of the resident=False
 // arm times BF16 activations): w.K counts bytes (2 per element), the MFMAs
 // accumulate in place, and there are no scales to stage or apply.
-template <bool SBF16, bool KFULL, bool DENSE>
+template <int T, bool SBF16, bool KFULL, bool DENSE>
 __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
+  using C = FTile<T>;
+  constexpr int FBN = C::BN, FBM = C::BM, F_SA = C::SA, F_STAGE = C::STAGE;
+  constexpr int F_A_LOADS = C::A_LOADS, F_B_LOADS = C::B_LOADS;
+  constexpr int WN = C::WN, WM = C::WM, TI = C::TI, TJ = C::TJ;
   // Two separate stage arrays (not one array indexed by stage): the compiler
   // must wait for in-flight LDS copies before any LDS read it cannot prove
   // disjoint from them, and distinct objects let it see that reading stage 0
@@ -656,8 +673,15 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
     float sw = 0.f;
     float4 sa = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (!DENSE) {
-      sw = wscale[wn][kb];
-      sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
+      sw = wscale[WN >= 128 ? wn : 0][kb];   // a 128-row tile lies in one scale row
+      if constexpr (TJ == 4) {
+        sa = *reinterpret_cast<const float4*>(cur + F_SA + wm * 256 + 16 * l16);
+      } else {
+        // 32 tokens per wave: tokens 32 wm + 16 j + l16, j = 0, 1, sit at
+        // positions 4 l16 + 2 (wm & 1) + j of their 64-token copy group
+        const float2 s2 = *reinterpret_cast<const float2*>(cur + F_SA + (wm >> 1) * 256 + 16 * l16 + 8 * (wm & 1));
+        sa = make_float4(s2.x, s2.y, 0.f, 0.f);
+      }
     }
     float s[TJ];
     // The 32 MFMAs of the K block run as one rotated chain: the epilogue FMAs
@@ -701,8 +725,10 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
         if (q == LAG) {   // the scale products, first needed here
           s[0] = sa.x * sw;
           s[1] = sa.y * sw;
-          s[2] = sa.z * sw;
-          s[3] = sa.w * sw;
+          if constexpr (TJ == 4) {
+            s[2] = sa.z * sw;
+            s[3] = sa.w * sw;
+          }
         }
         if (q >= LAG) {
           const int c = q - LAG, ci = c / TJ, cj = c % TJ;
@@ -740,18 +766,18 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
       // every wave is done reading both stages
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      uint8_t* buf = (wave < 4 ? stage0 : stage1) + (wave & 3) * (64 * F_OUT_PITCH);
+      uint8_t* buf = (wave < 4 ? stage0 : stage1) + (wave & 3) * (WM * F_OUT_PITCH);
       if (!whole)
-        store_tile_via_lds<false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws,
+        store_tile_via_lds<TI, TJ, false>(acc, buf, a.ws + int64_t(split) * M * a.ldws, a.ldws,
                                   int64_t(R - a.rt_split0) * FBN - n0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       else if (a.y_bf16 && a.y_nt)
-        store_tile_via_lds<true, true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+        store_tile_via_lds<TI, TJ, true, true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       else if (a.y_bf16)
-        store_tile_via_lds<true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+        store_tile_via_lds<TI, TJ, true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       else if (a.y_nt)
-        store_tile_via_lds<false, true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+        store_tile_via_lds<TI, TJ, false, true>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       else
-        store_tile_via_lds<false>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
+        store_tile_via_lds<TI, TJ, false>(acc, buf, a.y, a.ldy, mem.col0, n0 + wn * WN, mem.rows, m0 + wm * WM, M, lane);
       return;
     }
     // unaligned output: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16
@@ -773,7 +799,7 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
 }
 
 // Split-K partial sums: for workspace column c (row tile R = rt_split0 +
-// c / FBN, member i holding R, row n of member i), y[m, col0_i + n] = sum over
+// c / T, member i holding R, row n of member i), y[m, col0_i + n] = sum over
 // s = 0 .. S-1, in that order, of ws[s][m][c].  One thread per 4 columns.
 struct ReduceArgs {
   const float* ws;
@@ -786,6 +812,7 @@ struct ReduceArgs {
   int32_t y_bf16;
   int32_t n_members;
   int32_t rt_split0;
+  int32_t tile_n;       // weight rows per block tile (T)
   int32_t rt0[kMaxMembers + 1];
   int32_t rows[kMaxMembers];
   int32_t col0[kMaxMembers];
@@ -797,10 +824,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
   if (idx >= int64_t(a.M) * c4_per_row) return;
   const int m = int(idx / c4_per_row);
   const int c = int(idx - int64_t(m) * c4_per_row) * 4;
-  const int R = a.rt_split0 + c / FBN;
+  const int R = a.rt_split0 + c / a.tile_n;
   int i = 0;
   while (i + 1 < a.n_members && R >= a.rt0[i + 1]) ++i;
-  const int n = (R - a.rt0[i]) * FBN + c % FBN;
+  const int n = (R - a.rt0[i]) * a.tile_n + c % a.tile_n;
   const int nvalid = a.rows[i] - n;
   if (nvalid <= 0) return;
   const float* p = a.ws + int64_t(m) * a.ldws + c;
@@ -817,6 +844,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
 
 struct Plan {
   bool fast;
+  int tile;           // fast kernel: the block tile T (T x T)
   TileMap tm;         // register-staged kernel: member tiles
   int32_t rt0[kMaxMembers + 1];
   int rt_total;
@@ -844,34 +872,34 @@ int device_cus() {
 
 // Split-K where the tile grid leaves compute units idle: every tile when there
 // are fewer tiles than compute units, else the row tiles of the last, partly
-// filled round.  Cost model in units of one tile-K-block step (about 1.7 us of
-// GPU time at full occupancy): whole tiles run ceil(n / CUs) rounds of Kb
-// steps, split tiles ceil(n * S / CUs) rounds of ceil(Kb / S) steps, and each
-// split partial tile costs about 0.06 step to write and read back, plus two
-// steps for the second kernel.
+// filled round.  Cost model in units of one 256 x 256 tile-K-block step (about
+// 1.6 us of GPU time at full occupancy): whole tiles run ceil(n / CUs) rounds
+// of Kb steps, split tiles ceil(n * S / CUs) rounds of ceil(Kb / S) steps, and
+// each split partial tile costs `part` (0.06 step for 256 x 256) to write and
+// read back, plus two steps for the second kernel.  A 128 x 128 K block costs
+// `step` = 0.555 of a 256 x 256 one.  (Measured on Q/K/V [8144, 5120] at M =
+// 128 / 256 / 512 / 1024: the model gives 23 / 31 / 43 / 58 us for 256 x 256
+// tiles against 25 / 31 / 44 / 59 measured.)
 struct SplitChoice {
   int splits;
   int split_rows;
+  double cost;
 };
 
-SplitChoice choose_splits(int rt_total, int m_tiles, int Kb, int cus) {
+SplitChoice choose_splits(int rt_total, int m_tiles, int Kb, int cus, double step, double part) {
   const int tiles = rt_total * m_tiles;
   const int tail = tiles <= cus ? tiles : tiles % cus;
-  SplitChoice best{1, 0};
+  SplitChoice best{1, 0, double((tiles + cus - 1) / cus) * Kb * step};
   if (tail == 0) return best;
   const int split_rows = tiles <= cus ? rt_total : (tail + m_tiles - 1) / m_tiles;
   const int whole = (rt_total - split_rows) * m_tiles;
   const int split_tiles = split_rows * m_tiles;
-  double best_cost = double((tiles + cus - 1) / cus) * Kb;
   for (int sp = 2; sp <= 8; ++sp) {
     const int kps = (Kb + sp - 1) / sp;
     if (kps < 4) break;
-    const double cost = double((whole + cus - 1) / cus) * Kb +
-                        double((int64_t(split_tiles) * sp + cus - 1) / cus) * kps + 0.06 * sp * split_tiles + 2.0;
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = SplitChoice{sp, split_rows};
-    }
+    const double cost = double((whole + cus - 1) / cus) * Kb * step +
+                        double((int64_t(split_tiles) * sp + cus - 1) / cus) * kps * step + part * sp * split_tiles + 2.0;
+    if (cost < best.cost - 1e-9) best = SplitChoice{sp, split_rows, cost};
   }
   return best;
 }
@@ -887,20 +915,33 @@ Plan make_plan(const WeightDev& w, bool aligned, int64_t M, int64_t ldq, int64_t
   for (int i = 0; i < w.n_members; ++i) fits = fits && int64_t(w.m[i].rows) * w.K < (int64_t(1) << 31);
   p.fast = aligned && fits && w.Kb <= F_MAX_KB;
   if (p.fast) {
-    p.m_tiles = int((M + FBM - 1) / FBM);
+    // the tile (256 or 128) with the lower modelled cost, 256 on a tie
+    SplitChoice sc{};
+    for (const int T : {256, 128}) {
+      const int m_tiles = int((M + T - 1) / T);
+      int r = 0;
+      for (int i = 0; i < w.n_members; ++i) r += (w.m[i].rows + T - 1) / T;
+      const SplitChoice c = T == 256 ? choose_splits(r, m_tiles, w.Kb, device_cus(), 1.0, 0.06)
+                                     : choose_splits(r, m_tiles, w.Kb, device_cus(), 0.555, 0.015);
+      if (T == 256 || c.cost < sc.cost - 1e-9) {
+        sc = c;
+        p.tile = T;
+      }
+    }
+    const int T = p.tile;
+    p.m_tiles = int((M + T - 1) / T);
     int r = 0;
     for (int i = 0; i < w.n_members; ++i) {
       p.rt0[i] = r;
-      r += (w.m[i].rows + FBN - 1) / FBN;
+      r += (w.m[i].rows + T - 1) / T;
     }
     for (int i = w.n_members; i <= kMaxMembers; ++i) p.rt0[i] = r;
     p.rt_total = r;
-    const SplitChoice sc = choose_splits(r, p.m_tiles, w.Kb, device_cus());
     p.kb_per_split = (w.Kb + sc.splits - 1) / sc.splits;
     p.splits = (w.Kb + p.kb_per_split - 1) / p.kb_per_split;  // no empty split
     const int split_rows = p.splits > 1 ? sc.split_rows : 0;
     p.rt_split0 = r - split_rows;
-    p.ldws = int64_t(split_rows) * FBN;
+    p.ldws = int64_t(split_rows) * T;
     p.blocks = p.rt_split0 * p.m_tiles + split_rows * p.m_tiles * p.splits;
     p.ws_bytes = p.splits > 1 ? size_t(p.splits) * size_t(M) * size_t(p.ldws) * sizeof(float) : 0;
     return p;
@@ -936,7 +977,8 @@ std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M) {
              "arm=w8a8 arithmetic=e4m3xe4m3 mfma_f32_16x16x128_f8f6f4, f32 per-128-K epilogue | "
              "kernel=w8a8_gemm_fast tile=%dx%d waves=8 lds=2x%dKiB (two stage arrays) buffer_load_lds "
              "xcd_groups=%d split_k=%d split_row_tiles=%d | M=%lld blocks=%d",
-             FBN, FBM, F_STAGE / 1024, group_rows_for(p.m_tiles, p.rt_total * p.m_tiles, device_cus()), p.splits,
+             p.tile, p.tile, (p.tile == 256 ? FTile<256>::STAGE : FTile<128>::STAGE) / 1024,
+             group_rows_for(p.m_tiles, p.rt_total * p.m_tiles, device_cus()), p.splits,
              p.rt_total - p.rt_split0, (long long)M, p.blocks);
   else
     snprintf(buf, sizeof(buf),
@@ -986,12 +1028,12 @@ bsf8_status launch_fast(const Plan& p, const WeightDev& w, bool dense, const uin
   const bool kfull = w.K % KBYTES == 0;
   using Kern = void (*)(FastArgs);
   Kern kern;
-  if (dense)
-    kern = kfull ? w8a8_gemm_fast_kernel<false, true, true> : w8a8_gemm_fast_kernel<false, false, true>;
-  else if (w.scale_bf16)
-    kern = kfull ? w8a8_gemm_fast_kernel<true, true, false> : w8a8_gemm_fast_kernel<true, false, false>;
-  else
-    kern = kfull ? w8a8_gemm_fast_kernel<false, true, false> : w8a8_gemm_fast_kernel<false, false, false>;
+#define BSF8_FAST(T)                                                                                          \
+  (dense ? (kfull ? w8a8_gemm_fast_kernel<T, false, true, true> : w8a8_gemm_fast_kernel<T, false, false, true>) \
+   : w.scale_bf16 ? (kfull ? w8a8_gemm_fast_kernel<T, true, true, false> : w8a8_gemm_fast_kernel<T, true, false, false>) \
+                  : (kfull ? w8a8_gemm_fast_kernel<T, false, true, false> : w8a8_gemm_fast_kernel<T, false, false, false>))
+  kern = p.tile == 256 ? BSF8_FAST(256) : BSF8_FAST(128);
+#undef BSF8_FAST
   hipLaunchKernelGGL(kern, dim3(p.blocks), dim3(FTHREADS), 0, stream, a);
   bsf8_status st = device_status(hipGetLastError(), dense ? "dense_gemm launch" : "w8a8_gemm_fast launch");
   if (st != BSF8_OK || p.splits == 1) return st;
@@ -1006,6 +1048,7 @@ bsf8_status launch_fast(const Plan& p, const WeightDev& w, bool dense, const uin
   r.y_bf16 = y_bf16 ? 1 : 0;
   r.n_members = w.n_members;
   r.rt_split0 = p.rt_split0;
+  r.tile_n = p.tile;
   for (int i = 0; i <= kMaxMembers; ++i) r.rt0[i] = p.rt0[i];
   for (int i = 0; i < w.n_members; ++i) {
     r.rows[i] = w.m[i].rows;
@@ -1051,7 +1094,7 @@ std::string describe_dense(int64_t N, int64_t K, int64_t M) {
            "arm=dense arithmetic=bf16xbf16 mfma_f32_16x16x32_bf16 (two per 128-byte K block), f32 accumulate | "
            "kernel=w8a8_gemm_fast<dense> tile=%dx%d waves=8 buffer_load_lds xcd_groups=%d split_k=%d "
            "split_row_tiles=%d | M=%lld blocks=%d | dense weight N=%lld K=%lld bf16",
-           FBN, FBM, group_rows_for(p.m_tiles, p.rt_total * p.m_tiles, device_cus()), p.splits,
+           p.tile, p.tile, group_rows_for(p.m_tiles, p.rt_total * p.m_tiles, device_cus()), p.splits,
            p.rt_total - p.rt_split0, (long long)m, p.blocks, (long long)N,
            (long long)K);
   return buf;

@@ -109,7 +109,8 @@ def test_workspace_sizes():
             d = L.bsf8_describe(h, 1, M).decode()
             sk = int(re.search(r"split_k=(\d+)", d).group(1))
             rows = int(re.search(r"split_row_tiles=(\d+)", d).group(1))
-            assert b.value == (sk * M * rows * 256 * 4 if sk > 1 else 0), (M, d)
+            tile = int(re.search(r"tile=(\d+)x", d).group(1))
+            assert b.value == (sk * M * rows * tile * 4 if sk > 1 else 0), (M, d)
         # 20 row tiles x 4 token tiles < 256 units: every tile is split
         assert "split_k=3 split_row_tiles=20" in L.bsf8_describe(h, 1, 1024).decode()
         # one to four tokens stream the weight with E4M3 activations and use no
