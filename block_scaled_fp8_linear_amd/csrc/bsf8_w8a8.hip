@@ -876,10 +876,14 @@ int device_cus() {
 // 1.6 us of GPU time at full occupancy): whole tiles run ceil(n / CUs) rounds
 // of Kb steps, split tiles ceil(n * S / CUs) rounds of ceil(Kb / S) steps, and
 // each split partial tile costs `part` (0.06 step for 256 x 256) to write and
-// read back, plus two steps for the second kernel.  A 128 x 128 K block costs
-// `step` = 0.555 of a 256 x 256 one.  (Measured on Q/K/V [8144, 5120] at M =
-// 128 / 256 / 512 / 1024: the model gives 23 / 31 / 43 / 58 us for 256 x 256
-// tiles against 25 / 31 / 44 / 59 measured.)
+// read back, plus two steps for the second kernel; every round of blocks adds
+// four steps of start-up and result stores.  A 128 x 128 K block costs `step`
+// = 0.555 of a 256 x 256 one and its partial tile 0.015.  (Without the round
+// term the model gives 23 / 31 / 43 / 58 us for Q/K/V [8144, 5120] at M =
+// 128 / 256 / 512 / 1024 on 256 x 256 tiles, against 25 / 31 / 44 / 59
+// measured; the round term only weighs plans with different round counts,
+// and with it the cheaper tile was picked on all 18 shapes timed both ways.)
+constexpr double kRoundSteps = 4.0;
 struct SplitChoice {
   int splits;
   int split_rows;
@@ -889,7 +893,8 @@ struct SplitChoice {
 SplitChoice choose_splits(int rt_total, int m_tiles, int Kb, int cus, double step, double part) {
   const int tiles = rt_total * m_tiles;
   const int tail = tiles <= cus ? tiles : tiles % cus;
-  SplitChoice best{1, 0, double((tiles + cus - 1) / cus) * Kb * step};
+  const int rounds = (tiles + cus - 1) / cus;
+  SplitChoice best{1, 0, double(rounds) * (Kb * step + kRoundSteps)};
   if (tail == 0) return best;
   const int split_rows = tiles <= cus ? rt_total : (tail + m_tiles - 1) / m_tiles;
   const int whole = (rt_total - split_rows) * m_tiles;
@@ -897,8 +902,10 @@ SplitChoice choose_splits(int rt_total, int m_tiles, int Kb, int cus, double ste
   for (int sp = 2; sp <= 8; ++sp) {
     const int kps = (Kb + sp - 1) / sp;
     if (kps < 4) break;
-    const double cost = double((whole + cus - 1) / cus) * Kb * step +
-                        double((int64_t(split_tiles) * sp + cus - 1) / cus) * kps * step + part * sp * split_tiles + 2.0;
+    const int r_whole = (whole + cus - 1) / cus;
+    const int r_split = int((int64_t(split_tiles) * sp + cus - 1) / cus);
+    const double cost = r_whole * (Kb * step + kRoundSteps) + r_split * (kps * step + kRoundSteps) +
+                        part * sp * split_tiles + 2.0;
     if (cost < best.cost - 1e-9) best = SplitChoice{sp, split_rows, cost};
   }
   return best;
