@@ -305,8 +305,9 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Fast path (K % 16 == 0, 16-byte aligned operands): 512 threads, 256 x 256
-// block tile, eight waves of 128 x 64 (two per SIMD, so one wave's epilogue and
+// Fast path (K % 16 == 0, 16-byte aligned operands): 512 threads, a T x T
+// block tile (T = 256, or 128 for small grids), eight waves of T/2 x T/4 (two
+// per SIMD, so one wave's epilogue and
 // LDS traffic overlap the other's MFMAs), operands copied HBM -> LDS by
 // buffer_load ... lds without passing through registers.  Out-of-range rows,
 // tokens and K bytes are given an offset past the buffer's end, which the
@@ -314,8 +315,8 @@ __global__ __launch_bounds__(THREADS) void w8a8_gemm_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int FTHREADS = 512;
-// Operand copies: 1 KiB wave copies (8 rows x 128 bytes) per stage, 32 weight
-// slabs and 32 token slabs, issued by waves 0-3 between the MFMAs of their
+// Operand copies: 1 KiB wave copies (8 rows x 128 bytes) per stage, T/8 weight
+// slabs and T/8 token slabs, issued by waves 0-3 between the MFMAs of their
 // chains.  The vector memory unit takes a 1 KiB copy about as fast as it
 // moves it, so a wave that issues its sixteen copies in one burst stalls for
 // most of a K block; spread over the chain, the stalls overlap MFMAs of both
@@ -537,10 +538,10 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   // the scales' extent in bytes (below 2^31: the plan checks it)
   const uint32_t s_bytes = uint32_t(((int64_t(M) - 1) * a.xs_sm + int64_t(Kb - 1) * a.xs_sk + 1) * 4);
   const v4i rs = make_rsrc(a.xs, s_bytes);
-  // waves 0..3 each copy the scales of 64 tokens (one 4-byte element per
+  // waves 0..T/64-1 each copy the scales of 64 tokens (one 4-byte element per
   // lane).  Lane L fetches token 16 (L & 3) + (L >> 2) of its wave's 64, so the
-  // four scales a compute lane needs (tokens l16 + 16 j, j = 0..3) sit in one
-  // 16-byte LDS word.  With K-major scales (xs_sm = 1) a wave's copy reads
+  // four scales a compute lane of a 64-token wave needs (tokens l16 + 16 j,
+  // j = 0..3) sit in one 16-byte LDS word (a 32-token wave's two, in 8 bytes).  With K-major scales (xs_sm = 1) a wave's copy reads
   // 256 contiguous bytes; token-major, 64 words a row pitch apart.
   const bool s_wave = wave < FBM / 64;
   const int s_tok = m0 + wave * 64 + 16 * (lane & 3) + (lane >> 2);
@@ -602,7 +603,8 @@ __global__ __launch_bounds__(FTHREADS) void w8a8_gemm_fast_kernel(FastArgs a) {
   issue(kb_begin, stage0);
 
   // ---- weight scales: rows (n0 >> 7) and (n0 >> 7) + 1 of the member's grid
-  // (one per wave half), staged in LDS once; a missing row reads as zero
+  // (one per wave half of a 256-row tile; a 128-row tile uses the first),
+  // staged in LDS once; a missing row reads as zero
   if constexpr (!DENSE) {
     const int nb = (mem.rows + 127) >> 7;
     for (int i = tid; i < 2 * Kb; i += FTHREADS) {
