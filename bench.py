@@ -838,7 +838,7 @@ def main():
         line["qkv_prefill"]["roofline"] = {"bound": "mfma", "kernel": "w8a8_gemm (QKV, M=512)",
                                            "achieved": round(q["tflops"], 2), "peak": FP8_PEAK_TFLOPS,
                                            "unit": "TFLOP/s", "frac": round(q["tflops"] / FP8_PEAK_TFLOPS, 4),
-                                           "traffic": None}
+                                           "traffic": profiled_traffic("w8a8_gemm_qkv_m512")}
         q16 = extra["qkv_w8a16_m512"]
         line["qkv_w8a16_m512"] = {
             "workload": q16["workload"], "us": round(q16["us"], 2), "p10": round(q16["us_p10"], 2),
@@ -864,9 +864,11 @@ def main():
             "gemm": {k: {"us": round(v["us"], 2), "p10": round(v["us_p10"], 2), "p90": round(v["us_p90"], 2),
                          "launches": v["launches"], "tflops": round(v["tflops"], 2), "path": v["describe"]}
                      for k, v in d["gemm"].items()},
-            "roofline": {"bound": "mfma", "kernel": "dense_gemm (M512)", "achieved": round(g512["tflops"], 2),
+            "roofline": {"bound": "mfma", "kernel": "dense_gemm (M512; traffic of the GEMM kernel, its split-K "
+                                                    "reduction not included)", "achieved": round(g512["tflops"], 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(g512["tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "frac": round(g512["tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "traffic": profiled_traffic("dense_gemm_qkv_m512")}}
     if "copy_calibration" in extra:
         line["copy_calibration"] = extra["copy_calibration"]
     print(json.dumps(line), flush=True)
