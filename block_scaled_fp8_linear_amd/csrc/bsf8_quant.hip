@@ -104,6 +104,20 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   const int lane32 = threadIdx.x & 31;
   const int64_t n_groups = int64_t(M) * Kb;
   const int64_t g0 = (int64_t(blockIdx.x) * (kQuantThreads / 32) + (threadIdx.x >> 5)) * kGroupsPerHalf;
+  // Token row and group column of the half-wave's first group: one division,
+  // in 32 bits whenever the group count allows (a 64-bit division is about a
+  // hundred instructions, as many as the arithmetic of the group's channels);
+  // the following groups step along the row and wrap to the next ones.
+  int64_t mrow0;
+  int32_t gcol0;
+  if (n_groups <= int64_t(INT32_MAX)) {
+    const uint32_t gg = uint32_t(g0), q = gg / uint32_t(Kb);
+    mrow0 = q;
+    gcol0 = int32_t(gg - q * uint32_t(Kb));
+  } else {
+    mrow0 = g0 / Kb;
+    gcol0 = int32_t(g0 - mrow0 * Kb);
+  }
   float v[kGroupsPerHalf][4];
   int64_t mrow[kGroupsPerHalf];
   int32_t gcol[kGroupsPerHalf], kk[kGroupsPerHalf], valid[kGroupsPerHalf];
@@ -111,8 +125,16 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
   for (int j = 0; j < kGroupsPerHalf; ++j) {
     const int64_t gi = g0 + j;
     const bool live = gi < n_groups;
-    mrow[j] = live ? gi / Kb : 0;
-    gcol[j] = live ? int32_t(gi - mrow[j] * Kb) : 0;
+    int32_t gc = gcol0 + j;
+    int64_t mr = mrow0;
+#pragma unroll
+    for (int t = 0; t < j; ++t)   // at most j rows further on (when Kb < j + 1)
+      if (gc >= Kb) {
+        gc -= Kb;
+        ++mr;
+      }
+    mrow[j] = live ? mr : 0;
+    gcol[j] = live ? gc : 0;
     kk[j] = gcol[j] * kBlock + lane32 * 4;
     valid[j] = live ? max(0, min(4, K - kk[j])) : 0;
     load4<BF16>(x, mrow[j] * ldx + kk[j], valid[j], x_vec != 0, v[j]);
