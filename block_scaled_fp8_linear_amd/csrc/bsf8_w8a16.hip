@@ -873,8 +873,16 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 // The weight scales (and the token's activation scales for E4M3 activations)
 // of the wave's chunks are loaded first, one chunk per lane, and picked per
 // chunk with a lane read.
+// Ring depth: a slot holds about 3 KiB of weights per wave plus the lane's
+// activations (4 KiB per wave for F32, 2 for BF16, 1 for E4M3), and the
+// fastest depth is the one that keeps about 14-16 MB in flight over the
+// chip, beyond which requests only queue: FFN down [5120, 17408] at one token
+// with F32 activations took 22.5 / 20.2 / 19.7 / 19.1 us at depth 4 / 3 / 2 /
+// 1, with E4M3 activations 20.4 / 18.3 / 17.3 / 19.4 us (the plain read of
+// the same bytes 17.3 us).
 // ---------------------------------------------------------------------------
-constexpr int M1R_DEPTH = 4;
+template <int XK>
+constexpr int m1r_depth() { return XK == XK_F32 ? 1 : 2; }
 
 template <int XK, bool SBF16, int G, int D>
 __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
@@ -1819,7 +1827,8 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
              "kernel=%s rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, %s, "
              "8 lanes per 128-byte row piece, no LDS transpose) | M=%lld blocks=%d",
              m1.ring ? "w8a16_m1_ring" : "w8a16_m1", m1.rb, m1.g, WAVES, m1.cpw,
-             m1.ring ? "4-chunk load ring" : "all loads first", (long long)(M > 0 ? M : 1), m1.tiles);
+             m1.ring ? "load ring of 1 chunk (F32 activations) or 2 (BF16)" : "all loads first",
+             (long long)(M > 0 ? M : 1), m1.tiles);
     return b1;
   }
   const Plan p = make_plan(w, M > 0 ? M : 1, aligned);
@@ -1875,8 +1884,10 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   (x_bf16 ? (sb ? w8a16_m1_kernel<XK_BF16, true, G, C> : w8a16_m1_kernel<XK_BF16, false, G, C>)               \
           : (sb ? w8a16_m1_kernel<XK_F32, true, G, C> : w8a16_m1_kernel<XK_F32, false, G, C>))
 #define BSF8_MR(G)                                                                                              \
-  (x_bf16 ? (sb ? w8a16_m1_ring_kernel<XK_BF16, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_BF16, false, G, M1R_DEPTH>) \
-          : (sb ? w8a16_m1_ring_kernel<XK_F32, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_F32, false, G, M1R_DEPTH>))
+  (x_bf16 ? (sb ? w8a16_m1_ring_kernel<XK_BF16, true, G, m1r_depth<XK_BF16>()>                           \
+                 : w8a16_m1_ring_kernel<XK_BF16, false, G, m1r_depth<XK_BF16>()>)                          \
+          : (sb ? w8a16_m1_ring_kernel<XK_F32, true, G, m1r_depth<XK_F32>()>                               \
+                : w8a16_m1_ring_kernel<XK_F32, false, G, m1r_depth<XK_F32>()>))
     auto k1 = m1.ring ? (m1.g == 2 ? BSF8_MR(2) : m1.g == 3 ? BSF8_MR(3) : BSF8_MR(4))
               : m1.cpw == 4 ? (m1.g == 2 ? BSF8_M1(2, 4) : m1.g == 3 ? BSF8_M1(3, 4) : BSF8_M1(4, 4))
                             : (m1.g == 2 ? BSF8_M1(2, 5) : m1.g == 3 ? BSF8_M1(3, 5) : BSF8_M1(4, 5));
@@ -1968,7 +1979,7 @@ std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
            "scale) | kernel=%s<e4m3> rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, %s, "
            "8 lanes per 128-byte row piece, no LDS transpose%s) | M=%lld blocks=%d",
            m1.ring ? "w8a16_m1_ring" : "w8a16_m1", m1.rb, m1.g, WAVES, m1.cpw,
-           m1.ring ? "4-chunk load ring" : "all loads first", "", (long long)M, m1.tiles);
+           m1.ring ? "2-chunk load ring" : "all loads first", "", (long long)M, m1.tiles);
   return b;
 }
 
@@ -2000,7 +2011,8 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
   const bool sb = w.scale_bf16 != 0;
 #define BSF8_Q1(G, C) (sb ? w8a16_m1_kernel<XK_E4M3, true, G, C> : w8a16_m1_kernel<XK_E4M3, false, G, C>)
 #define BSF8_QR(G) \
-  (sb ? w8a16_m1_ring_kernel<XK_E4M3, true, G, M1R_DEPTH> : w8a16_m1_ring_kernel<XK_E4M3, false, G, M1R_DEPTH>)
+  (sb ? w8a16_m1_ring_kernel<XK_E4M3, true, G, m1r_depth<XK_E4M3>()>                                     \
+      : w8a16_m1_ring_kernel<XK_E4M3, false, G, m1r_depth<XK_E4M3>()>)
   auto k1 = m1.ring ? (m1.g == 2 ? BSF8_QR(2) : m1.g == 3 ? BSF8_QR(3) : BSF8_QR(4))
             : m1.cpw == 4 ? (m1.g == 2 ? BSF8_Q1(2, 4) : m1.g == 3 ? BSF8_Q1(3, 4) : BSF8_Q1(4, 4))
                           : (m1.g == 2 ? BSF8_Q1(2, 5) : m1.g == 3 ? BSF8_Q1(3, 5) : BSF8_Q1(4, 5));
