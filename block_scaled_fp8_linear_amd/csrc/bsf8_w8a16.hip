@@ -12,10 +12,10 @@
 //  * 1 token: F32 FMAs on the vector ALUs against weights decoded exactly to
 //    F32 in registers (w8a16_m1_kernel; w8a16_m1_ring_kernel beyond five chunks
 //    per wave);
-//  * 2 to 4 tokens, K <= 5120: the same weight stream with the F32 products
-//    summed on the matrix cores (w8a16_mf_kernel, v_mfma_f32_4x4x1f32);
-//  * 5 to 8 tokens, and 2 to 4 with a longer K: the few-token MFMA kernel
-//    (w8a16_small_m_kernel);
+//  * 2 to 8 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
+//  * (E4M3 activations at 2 to 4 tokens, the W8A8 arm's few-token path: the
+//    one-token weight stream with the F32 products summed on the matrix
+//    cores, w8a16_mf_kernel, v_mfma_f32_4x4x1f32);
 //  * many tokens, once 256-row x 64-token tiles fill half the compute units:
 //    the LDS-staged GEMM (w8a16_gemm_kernel);
 //  * the tokens in between, or any unaligned operand: the general MFMA kernel.
@@ -404,10 +404,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //  * activations are loaded compactly (32 lanes per F32 token, 16 per BF16
 //    token), each lane splits only what it loaded, and the BF16 terms go to a
 //    wave-private LDS scratch in fragment order; tokens past M read a zero row;
-//  * a ring of SM_DEPTH chunks of both operands is in flight in registers
-//    (as many as a wave has chunks, up to 5, so decode K <= 5120 issues all of
-//    a wave's loads at once; 3 for F32 at M > 4, where registers run out, or 4
-//    when that is all of a wave's chunks);
+//  * SM_RING chunks of both operands are in flight per wave in registers, one
+//    chunk: each chunk is about 8 KiB per wave (weights and activations), and
+//    with more in flight the memory system only queues the requests (W
+//    [5120, 5120] at M = 8: 13.9 us with 3 chunks, 13.0 with 2, 11.0 with 1;
+//    Q/K/V at M = 8 with BF16 activations 10.9 -> 8.6 us);
 //    loads retire in issue order, so each slot's loads are issued together and
 //    slots in chunk order (scheduling barriers keep them grouped), and chunks
 //    past the wave's range get past-the-end offsets (zeros, no traffic).
@@ -437,7 +438,7 @@ __device__ __forceinline__ int sm_swz(int r) { return ((r & 1) << 1) | ((r >> 1)
 constexpr int SM_ZERO_ROW = SM_MAXM;           // scratch row that stays zero
 constexpr int SM_ROW_BYTES = CHUNK * 2;        // one token's chunk as BF16
 constexpr int SM_TERM_BYTES = (SM_MAXM + 1) * SM_ROW_BYTES;
-constexpr int SM_MAX_DEPTH = 5;               // ring depth for M <= 4 (F32) / 8 (BF16); 3 at F32 M > 4 (registers)
+constexpr int SM_RING = 1;                    // chunks in flight per wave (the kernel takes any depth)
 constexpr int SM_SCALE_REGS = 2;               // chunk scales per wave: up to 128 (K up to 131072 with 8 waves)
 constexpr int SM_WBUF = ROWS * CHUNK;          // a wave's weight bytes per chunk: 4 KiB
 
@@ -1060,8 +1061,12 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
 
 
 // ---------------------------------------------------------------------------
-// Two to four tokens (aligned operands, K <= 5120): the one-token kernel's
-// weight stream with the products on the matrix cores, in F32.
+// Two to four tokens of E4M3 activations (the W8A8 arm's few-token path;
+// aligned operands, K <= 5120): the one-token kernel's weight stream with the
+// products on the matrix cores, in F32.  (The template also takes F32 and
+// BF16 activations; the W8A16 arm no longer uses it, since the few-token MFMA
+// kernel with one chunk in flight per wave is faster there: W [5120, 5120] at
+// M = 2 / 4 9.3 / 9.5 -> 8.6 / 9.1 us, Q/K/V at M = 4 12.6 -> 10.4 us.)
 // v_mfma_f32_4x4x1f32 treats a wave as 16 blocks of four lanes: lane 4b + i
 // supplies row i of block b's 4 x 1 A operand and column i of its 1 x 4 B
 // operand, and lane 4b + j receives column j of block b's 4 x 4 product, one
@@ -1083,10 +1088,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
 // the matrix core's F32 sum takes the place of the FMA chain, and the vector
 // ALU keeps the decoding and the scaling.  Against the same kernel with 16
 // FMAs per weight byte and token on the vector ALU: 9.8-10.2 -> 9.5-9.7 us at
-// two to four tokens of W [5120, 5120].  Five to eight tokens do not fit the
-// LDS as F32 slices; taken in two passes over the wave's chunks (weights kept
-// in registers, the second slice copied in between) they measured 15.1-15.3
-// us against the MFMA few-token kernel's 13.1-13.8 us, so those stay there.
+// two to four F32 tokens of W [5120, 5120].
 // ---------------------------------------------------------------------------
 // Activation slices in LDS carry 4 floats of padding after every 64: a lane
 // reads the 16 activations of its piece (lanes of one piece position read the
@@ -1721,9 +1723,11 @@ bsf8_status launch_mf(const WeightDev& w, const MfShape& m, int xk, const void* 
   a.xs_sm = xs_sm;
   a.xs_sk = xs_sk;
   const bool sb = w.scale_bf16 != 0;
-  const KernelFn k = xk == XK_E4M3 ? mf_kernel_for<XK_E4M3>(sb, m.g, m.cpw)
-                     : xk == XK_BF16 ? mf_kernel_for<XK_BF16>(sb, m.g, m.cpw)
-                                     : mf_kernel_for<XK_F32>(sb, m.g, m.cpw);
+  if (xk != XK_E4M3) {
+    set_error("UNSUPPORTED: the F32-matrix-core few-token kernel is built for E4M3 activations only");
+    return BSF8_E_UNSUPPORTED;
+  }
+  const KernelFn k = mf_kernel_for<XK_E4M3>(sb, m.g, m.cpw);
   hipLaunchKernelGGL(k, dim3(m.tiles), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a16_mf launch");
 }
@@ -1795,11 +1799,6 @@ bsf8_status launch_gemm(const WeightDev& w, const void* x, bool x_bf16, int64_t 
 
 size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
 
-// load-ring depth of the few-token kernel: a wave's chunk count, within [3, SM_MAX_DEPTH]
-int small_depth(int chunks_per_wave) {
-  return chunks_per_wave <= 3 ? 3 : chunks_per_wave >= SM_MAX_DEPTH ? SM_MAX_DEPTH : chunks_per_wave;
-}
-
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   if (gemm_applies(w, aligned, M)) {
     char b[448];
@@ -1810,14 +1809,6 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
              "M=%lld blocks=%lld",
              GW_ROWS, GW_TOKS, (long long)M, (long long)rt * ((M + GW_TOKS - 1) / GW_TOKS));
     return b;
-  }
-  const MfShape mf = mf_shape(w, aligned, M);
-  if (mf.g) {
-    char b[512];
-    return describe_mf(b, sizeof(b), mf,
-                       "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), "
-                       "f32 products summed on the matrix cores per 16-K piece, f32 accumulate",
-                       M);
   }
   const M1Shape m1 = m1_shape(w, aligned, M > 0 ? M : 1);
   if (m1.g) {
@@ -1835,9 +1826,8 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   const bool small = aligned && M >= 1 && M <= SM_MAXM;
   char ring[160] = "";
   if (small)
-    snprintf(ring, sizeof(ring), ", %d-chunk load ring%s, compact activations split in LDS, F32 terms in MFMA columns",
-             small_depth(p.chunks_per_wave),
-             M > 4 ? (p.chunks_per_wave == 4 ? " (4 for F32 activations)" : " (3 for F32 activations)") : "");
+    snprintf(ring, sizeof(ring), ", %d-chunk load ring, compact activations split in LDS, F32 terms in MFMA columns",
+             SM_RING);
   char buf[512];
   snprintf(buf, sizeof(buf),
            "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
@@ -1861,8 +1851,6 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) aligned = false;
   const Plan p = make_plan(w, M, aligned);
   if (p.tiles == 0) return BSF8_OK;
-  const MfShape mf = mf_shape(w, aligned, M);
-  if (mf.g) return launch_mf(w, mf, x_bf16 ? XK_BF16 : XK_F32, x, ldx, nullptr, 0, 0, M, y, y_bf16, ldy, stream);
   if (gemm_applies(w, aligned, M)) return launch_gemm(w, x, x_bf16, M, ldx, y, y_bf16, ldy, stream);
   const M1Shape m1 = m1_shape(w, aligned, M);
   if (m1.g) {
@@ -1918,22 +1906,14 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     grid = sh.tiles;
     // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load,
     // and 3 M term columns of F32 tokens in one 16-column MFMA pass up to M = 5
-    const int depth = small_depth(p.chunks_per_wave);
-#define BSF8_SMALL(XB, NXI, NP)                                                                                   \
-  (depth == 3   ? (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, 3> : w8a16_small_m_kernel<XB, false, NXI, NP, 3>)   \
-   : depth == 4 ? (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, 4> : w8a16_small_m_kernel<XB, false, NXI, NP, 4>)   \
-                : (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, 5> : w8a16_small_m_kernel<XB, false, NXI, NP, 5>))
+#define BSF8_SMALL(XB, NXI, NP) \
+  (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, SM_RING> : w8a16_small_m_kernel<XB, false, NXI, NP, SM_RING>)
     if (x_bf16) {
       kern = M <= 4 ? BSF8_SMALL(true, 1, 1) : BSF8_SMALL(true, 2, 1);
     } else if (M <= 4) {
       kern = M <= 2 ? BSF8_SMALL(false, 1, 1) : BSF8_SMALL(false, 2, 1);
     } else {
-      // F32 tokens 5-8: a ring of 4 (254 registers) when it holds all of a wave's
-      // chunks (W [5000,4000]: 15.6 -> 14.2 us at M = 8), else 3 (a ring of 4
-      // then 1 chunk measured 18.5 against 15.0 us with 5 chunks)
-      kern = p.chunks_per_wave == 4
-                 ? (sb ? w8a16_small_m_kernel<false, true, 4, 2, 4> : w8a16_small_m_kernel<false, false, 4, 2, 4>)
-                 : (sb ? w8a16_small_m_kernel<false, true, 4, 2, 3> : w8a16_small_m_kernel<false, false, 4, 2, 3>);
+      kern = BSF8_SMALL(false, 4, 2);
     }
 #undef BSF8_SMALL
   } else if (aligned && p.rt == 4) {

@@ -286,10 +286,9 @@ bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, si
  *  paragraphs; "FP8 Native Serving", section "Native FP8 vs dequant-to-BF16":
  *  the weights are decoded where they are consumed, not in a copy.)
  * Kernels (aligned operands): one token runs F32 FMAs on the vector ALUs
- * against weights decoded exactly to F32 (any K); two to four tokens with
- * K <= 5120 form the same F32 products on the F32 matrix cores; other token
- * counts and shapes run the BF16 matrix cores on an exact three-term split of
- * each F32 activation (an LDS-staged GEMM for hundreds of tokens).
+ * against weights decoded exactly to F32 (any K); more tokens run the BF16
+ * matrix cores on an exact three-term split of each F32 activation (a
+ * weight-streaming kernel up to eight tokens, an LDS-staged GEMM for hundreds).
  *
  * x : [M, K] F32 or BF16, leading dimension ldx (elements), 16-byte aligned
  *     rows when K allows.
