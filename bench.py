@@ -32,8 +32,12 @@ The same JSON line also carries:
   with an HBM roofline on algorithmic bytes and a plain read of the same bytes
   (``bsf8_read_stream``) as context;
 * ``qkv_w8a8_decode``: grouped Q/K/V through the W8A8 arm at M = 1, rotated;
+* ``qkv_w8a8_dynamic_decode``: the same at M = 1 and 4 on F32 activations with
+  the quantization inside the step: the dynamic call (quantized inside the
+  streaming kernels) against quant_act followed by linear_w8a8, rotated;
 * ``ffn_down_decode`` and ``ffn_down_w8a8_decode``: the FFN down projection
-  [5120, 17408] at one token through both arms, rotated;
+  [5120, 17408] at one token through both arms, rotated, and
+  ``ffn_down_w8a8_dynamic_decode`` with the quantization inside the step;
 * ``qkv_prefill`` and ``qkv_w8a16_m512``: grouped Q/K/V at M = 512 through the
   W8A8 and the W8A16/F32 arm;
 * ``rotated``: the headline GEMM over three weight copies used in turn;
@@ -520,6 +524,56 @@ def bench_w8a8_rotating(torch, B, members, x_np, dev, label):
     return out
 
 
+def bench_w8a8_dynamic_rotating(torch, B, members, x_np, Ms, dev, label):
+    """The W8A8 arm on F32 activations at a few tokens, rotating through >= ROTATE_BYTES
+    of weight copies: one step is the projection including the activation quantization,
+    timed two ways, each as one HIP graph of one step per copy: the dynamic call (the
+    streaming kernels quantize in registers) and the two calls it replaces
+    (quant_act, then linear_w8a8)."""
+    per_copy = sum(m.codes.nbytes + m.scale_bits.nbytes for m in members)
+    copies = max(2, -(-ROTATE_BYTES // per_copy))
+    log(f"{label}: {copies} weight copies of {per_copy / 2**20:.1f} MiB")
+    base = [to_device_member(torch, m, dev) for m in members]
+    handles = [B.BlockFP8Weight([(w.clone(), sc.clone()) for w, sc in base]) for _ in range(copies)]
+    N, K = handles[0].n_total, handles[0].K
+    Kb = -(-K // 128)
+    grid = sum(-(-m.codes.shape[0] // 128) for m in members) * Kb
+    out = {"workload": f"{label}: W [{N},{K}] ({len(members)} member(s)) + bf16 grid, f32 x quantized in the step, "
+                       f"bf16 y, rotating {copies} copies ({copies * per_copy >> 20} MiB)", "by_M": {}}
+    for M in Ms:
+        x = torch.from_numpy(np.ascontiguousarray(x_np[:M])).to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        xq, xs = B.quant_act(x)
+        wsd = [h.workspace(B.ARM_W8A8_DYNAMIC, M) for h in handles]
+        ws8 = [h.workspace(B.ARM_W8A8, M) for h in handles]
+
+        def run_dynamic():
+            for h, wsh in zip(handles, wsd):
+                B.linear_w8a8_dynamic(h, x, out=y, workspace=wsh)
+
+        def run_two():
+            for h, wsh in zip(handles, ws8):
+                B.quant_act(x, xq=xq, xs=xs)
+                B.linear_w8a8(h, xq, xs, out=y, workspace=wsh)
+
+        res = {}
+        for key, fn in (("dynamic", run_dynamic), ("two_calls", run_two)):
+            g = graph_of(torch, fn)
+            settle(torch, g.replay, 0.3)
+            st = replay_stats(torch, g, 100, copies)
+            res[key] = st
+            del g
+        alg = N * K + 2 * grid + 4 * M * K + 2 * M * N
+        out["by_M"][f"M{M}"] = dict(
+            dynamic_us=res["dynamic"]["median"] * 1e3, dynamic_p10=res["dynamic"]["p10"] * 1e3,
+            dynamic_p90=res["dynamic"]["p90"] * 1e3, two_calls_us=res["two_calls"]["median"] * 1e3,
+            launches=res["dynamic"]["launches"], algorithmic_bytes=alg,
+            gbs=alg / (res["dynamic"]["mean"] * 1e-3) / 1e9, describe=handles[0].describe(B.ARM_W8A8_DYNAMIC, M))
+    del handles
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline_large(synth, tokens=8192, reps=3):
     """The oracle on the host cores on the headline step: the first ``tokens`` of the
     8192 tokens (all of them by default) quantized (NumPy float32, as defined) and
@@ -706,9 +760,15 @@ def main():
         c4 = synth.config4(1)
         extra["qkv_decode"] = bench_w8a16_rotating(torch, B, c4.members, c4.x, (1,), dev, "grouped QKV decode")
         extra["qkv_w8a8_decode"] = bench_w8a8_rotating(torch, B, c4.members, c4.x, dev, "grouped QKV W8A8 M=1")
+        c4d = synth.config4(4)
+        extra["qkv_w8a8_dynamic"] = bench_w8a8_dynamic_rotating(torch, B, c4d.members, c4d.x, (1, 4), dev,
+                                                                "grouped QKV W8A8 dynamic")
+        del c4d
         dn = synth.config3_down(1)
         extra["down_decode"] = bench_w8a16_rotating(torch, B, dn.members, dn.x, (1,), dev, "FFN down decode")
         extra["down_w8a8_decode"] = bench_w8a8_rotating(torch, B, dn.members, dn.x, dev, "FFN down W8A8 M=1")
+        extra["down_w8a8_dynamic"] = bench_w8a8_dynamic_rotating(torch, B, dn.members, dn.x, (1,), dev,
+                                                                 "FFN down W8A8 dynamic")
         del dn
         extra["qkv_prefill"] = bench_qkv_prefill(torch, B, synth, dev)
         extra["qkv_w8a16_m512"] = bench_qkv_w8a16_m512(torch, B, synth, dev)
@@ -825,7 +885,27 @@ def main():
                          "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": profiled_traffic("w8a8_qkv_m1"),
                          "algorithmic_bytes": d["algorithmic_bytes"]}}
+        d = extra["qkv_w8a8_dynamic"]
+        d1 = d["by_M"]["M1"]
+        line["qkv_w8a8_dynamic_decode"] = {
+            "workload": d["workload"],
+            "by_M": {k: {"dynamic_us": round(v["dynamic_us"], 2), "p10": round(v["dynamic_p10"], 2),
+                         "p90": round(v["dynamic_p90"], 2), "two_calls_us": round(v["two_calls_us"], 2),
+                         "launches": v["launches"], "path": v["describe"]} for k, v in d["by_M"].items()},
+            "roofline": {"bound": "hbm", "kernel": "w8a16_m1<quantizing> (M=1, quantization inside)",
+                         "achieved": round(d1["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(d1["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes": d1["algorithmic_bytes"]}}
         line["ffn_down_decode"] = decode_line(extra["down_decode"], profiled_traffic("w8a16_decode_down_m1"))
+        d = extra["down_w8a8_dynamic"]["by_M"]["M1"]
+        line["ffn_down_w8a8_dynamic_decode"] = {
+            "workload": extra["down_w8a8_dynamic"]["workload"], "dynamic_us": round(d["dynamic_us"], 2),
+            "p10": round(d["dynamic_p10"], 2), "p90": round(d["dynamic_p90"], 2),
+            "two_calls_us": round(d["two_calls_us"], 2), "launches": d["launches"], "path": d["describe"],
+            "roofline": {"bound": "hbm", "kernel": "w8a16_m1_ring<quantizing> (M=1, quantization inside)",
+                         "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes": d["algorithmic_bytes"]}}
         d = extra["down_w8a8_decode"]
         line["ffn_down_w8a8_decode"] = {
             "workload": d["workload"], "us": round(d["us"], 2), "p10": round(d["us_p10"], 2),

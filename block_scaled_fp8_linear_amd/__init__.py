@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("BSF8_LIBRARY") or os.path.join(_HERE, "libbsf8.so")
 
 DT_INVALID, DT_F8_E4M3, DT_F8_E5M2, DT_BF16, DT_F16, DT_F32, DT_U8, DT_OTHER = range(8)
-ARM_W8A16, ARM_W8A8, ARM_DENSE = 0, 1, 2
+ARM_W8A16, ARM_W8A8, ARM_DENSE, ARM_W8A8_DYNAMIC = 0, 1, 2, 3
 DTYPE_NAMES = {"F8_E4M3": DT_F8_E4M3, "F8_E5M2": DT_F8_E5M2, "BF16": DT_BF16, "F16": DT_F16,
                "F32": DT_F32, "U8": DT_U8}
 MAX_MEMBERS = 8
@@ -86,6 +86,9 @@ EXPORTS = [
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    ("bsf8_linear_w8a8_dynamic", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("bsf8_linear_w8a8_noalloc", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                                 ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
@@ -451,6 +454,25 @@ def linear_w8a8(w: BlockFP8Weight, xq, xs, out_dtype=None, out=None, workspace=N
     return y
 
 
+def linear_w8a8_dynamic(w: BlockFP8Weight, x, out_dtype=None, out=None, workspace=None):
+    """W8A8 arm on unquantized activations: x (float32 or bfloat16 [M, K]) is quantized per
+    token in 1x128 groups as quant_act does and multiplied as linear_w8a8 does, bit for bit,
+    in one call (bfloat16 output unless out_dtype says float32).  One aligned token is
+    quantized inside the weight-streaming kernels; more go through the workspace."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _on_device(w.device, x=x, out=out, workspace=workspace[0] if workspace is not None else None)
+    if x.dim() != 2 or x.stride(1) != 1 or x.shape[1] != w.K:
+        raise ValueError("x must be [M, K] with unit column stride")
+    M = x.shape[0]
+    y = _out(out, M, w.n_total, out_dtype, x.device)
+    ws, wsb = workspace if workspace is not None else w.workspace(ARM_W8A8_DYNAMIC, M)
+    _check(lib().bsf8_linear_w8a8_dynamic(w.handle, x.data_ptr(), _dt_of(x), M, x.stride(0), y.data_ptr(),
+                                          _dt_of(y), y.stride(0), ws.data_ptr() if ws is not None else None, wsb,
+                                          _stream_ptr(x.device)), "linear_w8a8_dynamic")
+    return y
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20   # BSF8_NOALLOC_SCRATCH_BYTES in include/bsf8.h
 
 
@@ -522,8 +544,9 @@ def linear_dense(wd, x, out_dtype=None, out=None, workspace=None):
 
 
 __all__ = ["BSF8Error", "BlockFP8Weight", "validate", "quant_act", "quant_glu", "glu_act", "linear_w8a16", "linear_w8a8",
-           "linear_w8a8_noalloc", "NOALLOC_SCRATCH_BYTES", "upcast",
+           "linear_w8a8_dynamic", "linear_w8a8_noalloc", "NOALLOC_SCRATCH_BYTES", "upcast",
            "linear_dense", "dense_workspace_size", "lib", "status_name", "ARM_W8A16", "ARM_W8A8", "ARM_DENSE",
+           "ARM_W8A8_DYNAMIC",
            "EXPORTS", "LIB_PATH", "MAX_MEMBERS", "scales_kmajor"]
 
 

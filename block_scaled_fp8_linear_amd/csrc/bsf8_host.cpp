@@ -281,12 +281,31 @@ bsf8_status bsf8_glu_act(const void* y, int32_t y_dtype, int64_t M, int64_t F, i
   return launch_glu_act(y, y_dtype == BSF8_DT_BF16, M, F, ldy, h, ldh, static_cast<hipStream_t>(stream));
 }
 
+// Workspace of the two-step form of bsf8_linear_w8a8_dynamic: the codes (row
+// pitch K rounded up to 16 bytes), the K-major scales, then the W8A8 call's own
+// workspace, each from a 256-byte boundary.
+struct DynLayout {
+  int64_t ldq;
+  size_t xs_off, gemm_off, gemm_bytes, total;
+};
+static size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+static DynLayout dyn_layout(const WeightDev& d, int64_t M) {
+  DynLayout L{};
+  L.ldq = (int64_t(d.K) + 15) & ~int64_t(15);
+  L.xs_off = round256(size_t(M) * size_t(L.ldq));
+  L.gemm_off = L.xs_off + round256(size_t(M) * size_t(d.Kb) * sizeof(float));
+  L.gemm_bytes = w8a8_workspace_bytes(d, M);
+  L.total = L.gemm_off + L.gemm_bytes;
+  return L;
+}
+
 bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, size_t* bytes) {
   if (w == nullptr || bytes == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
   if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");
   if (arm == BSF8_ARM_W8A16) *bytes = M ? w8a16_workspace_bytes(w->dev, M) : 0;
   else if (arm == BSF8_ARM_W8A8) *bytes = M ? w8a8_workspace_bytes(w->dev, M) : 0;
   else if (arm == BSF8_ARM_DENSE) *bytes = M ? dense_workspace_bytes(w->n_total, w->dev.K, M) : 0;
+  else if (arm == BSF8_ARM_W8A8_DYNAMIC) *bytes = M ? dyn_layout(w->dev, M).total : 0;
   else return fail(BSF8_E_INVALID_ARG, "arm %d", arm);
   return BSF8_OK;
 }
@@ -385,6 +404,39 @@ bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ld
                      workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+bsf8_status bsf8_linear_w8a8_dynamic(const bsf8_weight* w, const void* x, int32_t x_dtype, int64_t M, int64_t ldx,
+                                     void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  if (w == nullptr) return fail(BSF8_E_INVALID_ARG, "null handle");
+  if (M < 0) return fail(BSF8_E_INVALID_ARG, "negative M");
+  if (!dtype_ok(x_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "x dtype %d (F32 or BF16)", x_dtype);
+  if (!dtype_ok(y_dtype, true, true)) return fail(BSF8_E_INVALID_ARG, "y dtype %d (F32 or BF16)", y_dtype);
+  if (M == 0) return BSF8_OK;
+  if (x == nullptr || y == nullptr) return fail(BSF8_E_INVALID_ARG, "null pointer");
+  if (ldx < w->dev.K || ldy < w->n_total) return fail(BSF8_E_INVALID_ARG, "leading dimension too small");
+  if (M > INT32_MAX / 2) return fail(BSF8_E_UNSUPPORTED, "M too large");
+  const size_t xe = x_dtype == BSF8_DT_F32 ? 4 : 2, ye = y_dtype == BSF8_DT_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(x) % xe || reinterpret_cast<uintptr_t>(y) % ye)
+    return fail(BSF8_E_ALIGNMENT, "x or y not element aligned");
+  const bool x_bf16 = x_dtype == BSF8_DT_BF16, y_bf16 = y_dtype == BSF8_DT_BF16;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool aligned = w->aligned16 && (reinterpret_cast<uintptr_t>(x) % 16 == 0) && ((ldx * int64_t(xe)) % 16 == 0);
+  if (w8a8_dyn_stream_applies(w->dev, aligned, M, ldx * int64_t(xe)))
+    return launch_w8a8_dyn_stream(w->dev, x, x_bf16, M, ldx, y, y_bf16, ldy, st);
+  // two steps: the quantizer into the workspace, then the W8A8 kernels
+  const DynLayout L = dyn_layout(w->dev, M);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(BSF8_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, workspace ? workspace_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(BSF8_E_ALIGNMENT, "workspace not 256-byte aligned");
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  uint8_t* xq = base;
+  float* xs = reinterpret_cast<float*>(base + L.xs_off);
+  const bsf8_status s1 = launch_quant_act(x, x_bf16, M, w->dev.K, ldx, xq, L.ldq, xs, 1, M, st);
+  if (s1 != BSF8_OK) return s1;
+  return launch_w8a8(w->dev, w->aligned16, xq, L.ldq, xs, 1, M, M, y, y_bf16, ldy,
+                     L.gemm_bytes ? base + L.gemm_off : nullptr, L.gemm_bytes, st);
+}
+
 bsf8_status bsf8_linear_w8a8_noalloc(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs,
                                      int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, int32_t y_dtype, int64_t ldy,
                                      void* stream) {
@@ -422,6 +474,11 @@ const char* bsf8_describe(const bsf8_weight* w, int32_t arm, int64_t M) {
   if (arm == BSF8_ARM_W8A16) g_describe = describe_w8a16(w->dev, w->aligned16, M) + geo;
   else if (arm == BSF8_ARM_W8A8) g_describe = describe_w8a8(w->dev, w->aligned16, M) + geo;
   else if (arm == BSF8_ARM_DENSE) g_describe = describe_dense(w->n_total, w->dev.K, M) + geo;
+  else if (arm == BSF8_ARM_W8A8_DYNAMIC)
+    g_describe = (w8a8_dyn_stream_applies(w->dev, w->aligned16, M > 0 ? M : 1, int64_t(w->dev.K) * 4)
+                      ? describe_w8a8_dyn_stream(w->dev, M > 0 ? M : 1)
+                      : "quant_act into the workspace (K-major scales), then " + describe_w8a8(w->dev, w->aligned16, M)) +
+                  geo;
   else g_describe = "unknown arm";
   return g_describe.c_str();
 }

@@ -73,6 +73,13 @@ bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ld
 std::string describe_w8a8_stream(const WeightDev& w, int64_t M);
 bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t xs_sm,
                                int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream);
+// The one-token kernels quantizing F32 or BF16 activations themselves (the
+// W8A8 arm with the activation quantization in the same call; ldx_bytes is the
+// activations' row pitch in bytes).
+bool w8a8_dyn_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldx_bytes);
+std::string describe_w8a8_dyn_stream(const WeightDev& w, int64_t M);
+bsf8_status launch_w8a8_dyn_stream(const WeightDev& w, const void* x, bool x_bf16, int64_t M, int64_t ldx, void* y,
+                                   bool y_bf16, int64_t ldy, hipStream_t stream);
 // Device address of this device's copy of the no-allocation scratch array
 // (BSF8_NOALLOC_SCRATCH_BYTES bytes), looked up once per device.
 bsf8_status w8a8_noalloc_scratch(void** ptr);

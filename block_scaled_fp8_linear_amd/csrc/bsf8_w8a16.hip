@@ -127,8 +127,104 @@ struct Args {
 // Activation kinds of the few-token VALU kernels: F32 and BF16 activations (the
 // W8A16 arm), or E4M3 codes with per-token 1x128 group scales (the W8A8 arm:
 // the products of decoded codes are exact in F32, each chunk's partial is
-// scaled by activation scale x weight scale).
-constexpr int XK_F32 = 0, XK_BF16 = 1, XK_E4M3 = 2;
+// scaled by activation scale x weight scale), or one token of F32 / BF16
+// activations that the one-token kernels quantize to those codes and scales
+// themselves (the W8A8 arm with the activation quantization in the same call).
+constexpr int XK_F32 = 0, XK_BF16 = 1, XK_E4M3 = 2, XK_F32Q = 3, XK_BF16Q = 4;
+template <int XK>
+constexpr bool xk_quantize() { return XK == XK_F32Q || XK == XK_BF16Q; }
+// bytes per activation element in memory
+template <int XK>
+constexpr uint32_t xk_bytes() { return XK == XK_E4M3 ? 1u : XK == XK_BF16 || XK == XK_BF16Q ? 2u : 4u; }
+// 16-byte activation loads per lane and chunk in the one-token kernels' main loop
+// (a quantizing instance reads the codes it staged, one 16-byte piece)
+template <int XK>
+constexpr int xk_loads() { return XK == XK_E4M3 || xk_quantize<XK>() ? 1 : XK == XK_BF16 ? 2 : 4; }
+
+// ---- Per-token 1x128 activation quantization inside the one-token kernels
+// ("Module w8a8_prefill", WHY: amax / 448 per 128-wide group of a token, E4M3
+// with round-to-nearest-even, saturating).  A wave quantizes its own K range
+// once before it streams weights: lane slot q of a round takes 16-byte piece
+// q % 8 (16 activations) of chunk q / 8, so the 8 lanes of a chunk hold its
+// group, and writes the 16 codes and, from its first lane, the group's scale
+// to the wave's LDS region; the main loop then reads them as it would read
+// quantized activations from memory.  The arithmetic is the activation
+// quantizer's, step for step, so codes and scales are bit-identical to its
+// output: s = max(amax, 1e-10) / 448 as an IEEE F32 division, the quotient x / s
+// formed exactly as fl32(x * fl64(1 / s)) (the quantizer's comments show why
+// that is the IEEE F32 quotient), clamped to +-448 in the same order, rounded
+// by v_cvt_pk_fp8_f32.  Values past K load as zeros, as there.
+constexpr int QROUND_MAX = 8;                        // 64 slots per round: up to 64 chunks per wave
+constexpr int QCHUNKS_MAX = QROUND_MAX * 64 / 8;
+
+// Issues the loads of RB rounds of slots from slot r0 (16 activations of one
+// piece per lane and round, raw); zeros past the range or past K.
+template <int XK, int RB>
+__device__ __forceinline__ void quant_issue(v4i rx, uint32_t x_bytes, int K, int c_begin, int nch, int lane, int r0,
+                                            uint4 (&raw)[RB][4]) {
+  constexpr uint32_t XE = xk_bytes<XK>();
+  constexpr int NL = XE == 4 ? 4 : 2;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int slot = r0 + 64 * b + lane;
+    const int cl = slot >> 3, pc = slot & 7;
+    const uint32_t k = uint32_t(c_begin + cl) * CHUNK + 16u * pc;
+    const bool ok = cl < nch && int(k) < K;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) raw[b][q] = as_u4(bsf8_raw_buffer_load_b128(rx, int(ok ? k * XE + 16u * q : x_bytes), 0, 0));
+  }
+}
+
+// Quantizes the slots whose loads quant_issue made: a lane's 16 values are an
+// eighth of its chunk's group (8 aligned lanes); the codes and the group's
+// scale go to the wave's LDS region, codes[slot] and scales[chunk], for the
+// region's cap chunks.
+template <int XK, int RB>
+__device__ __forceinline__ void quant_store(int nch, int cap, int lane, int r0, const uint4 (&raw)[RB][4],
+                                            uint4* codes, float* scales) {
+  constexpr bool W4 = xk_bytes<XK>() == 4;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < (W4 ? 4 : 2); ++q) {
+      const uint32_t w4[4] = {raw[b][q].x, raw[b][q].y, raw[b][q].z, raw[b][q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (W4) {
+          v[4 * q + e] = __uint_as_float(w4[e]);
+        } else {
+          v[8 * q + 2 * e] = __uint_as_float(w4[e] << 16);
+          v[8 * q + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+        }
+      }
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) am = fmaxf(am, fabsf(v[e]));
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1) am = fmaxf(am, __shfl_xor(am, d));
+    const float s = fmaxf(am, 1e-10f) / 448.0f;
+    const double rs = 1.0 / static_cast<double>(s);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        f[e] = fminf(fmaxf(static_cast<float>(static_cast<double>(v[4 * q + e]) * rs), -448.0f), 448.0f);
+      int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
+      w[q] = uint32_t(packed);
+    }
+    // slots past the range hold zero codes, so a chunk read past it adds nothing
+    const int slot = r0 + 64 * b + lane;
+    if (slot < cap * 8) {
+      codes[slot] = make_uint4(w[0], w[1], w[2], w[3]);
+      if ((slot & 7) == 0) scales[slot >> 3] = s;
+    }
+  }
+}
 
 template <bool SBF16>
 __device__ __forceinline__ float load_scale(const void* s, int64_t idx) {
@@ -710,8 +806,11 @@ constexpr int M1_MAX_G = 4;
 
 template <int XK, bool SBF16, int G, int CPW>
 __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
-  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
+  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3, XQD = xk_quantize<XK>();
+  static_assert(!XQD || CPW * 8 <= 64, "a quantizing wave's range is one round of slots");
   __shared__ float red[WAVES][G * 8];
+  __shared__ uint4 qcodes[WAVES][XQD ? CPW * 8 : 1];   // quantizing instances: the wave's codes and scales
+  __shared__ float qscl[WAVES][XQD ? CPW : 1];
   const int tile = blockIdx.x;
   int mi = 0;
   while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
@@ -730,10 +829,10 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 
   const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
   const v4i rw = make_rsrc(mem.w, w_bytes);
-  constexpr uint32_t XE = XQ8 ? 1u : XBF16 ? 2u : 4u;
+  constexpr uint32_t XE = xk_bytes<XK>();
   const uint32_t x_bytes = uint32_t(K) * XE;
   const v4i rx = make_rsrc(a.x, x_bytes);
-  constexpr int XL = XQ8 ? 1 : XBF16 ? 2 : 4;   // 16-byte activation loads per chunk piece
+  constexpr int XL = xk_loads<XK>();   // 16-byte activation loads per chunk piece
 
   // ---- the chunk scales of the (at most two) grid rows the block's rows use,
   // issued first and without branches, so that waiting for them never waits
@@ -762,6 +861,13 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
   for (int c = 0; c < CPW; ++c) sa[c] = XQ8 ? a.xs[int64_t(min(c_begin + c, Kb - 1)) * a.xs_sk] : 1.f;
   __builtin_amdgcn_sched_barrier(0);
 
+  // ---- a quantizing instance's activations go out first: they arrive long
+  // before the weights and are quantized while the weight stream is in flight
+  // (loads retire in order, so a wait for them never covers weights)
+  uint4 qraw[1][4];
+  if constexpr (XQD) quant_issue<XK, 1>(rx, x_bytes, K, c_begin, c_end - c_begin, lane, 0, qraw);
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- every load of the wave: weights, activations (kept ahead of all arithmetic)
   uint4 wv[CPW][G];
   uint4 xr[CPW][XL];
@@ -776,13 +882,25 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
       const uint32_t off = live && r < rend ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
       wv[c][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, kStreamLoadAux));
     }
+    if (!XQD) {
 #pragma unroll
-    for (int q = 0; q < XL; ++q) {
-      const uint32_t off = live ? uint32_t(k) * XE + 16u * q : x_bytes;
-      xr[c][q] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
+      for (int q = 0; q < XL; ++q) {
+        const uint32_t off = live ? uint32_t(k) * XE + 16u * q : x_bytes;
+        xr[c][q] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XQD) {
+    quant_store<XK, 1>(c_end - c_begin, CPW, lane, 0, qraw, qcodes[wave], qscl[wave]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      xr[c][0] = qcodes[wave][8 * c + jp];
+      sa[c] = qscl[wave][c];
+    }
+  }
 
   float acc[G];
 #pragma unroll
@@ -790,7 +908,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     float xv[16];
-    if (XQ8) {
+    if (XQ8 || XQD) {
       const uint32_t x4[4] = {xr[c][0].x, xr[c][0].y, xr[c][0].z, xr[c][0].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -836,7 +954,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
       const int r = row0 + 8 * g + rl;
       const uint32_t sb = (r >> 7) == srow ? sc0[c] : sc1[c];
       const float sw = __uint_as_float(SBF16 ? sb << 16 : sb);
-      acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), XQ8 ? sa[c] * sw : sw, acc[g]);
+      acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), XQ8 || XQD ? sa[c] * sw : sw, acc[g]);
     }
   }
   // ---- rows: the 8 lanes of a row, then the 8 waves in order
@@ -882,13 +1000,19 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_kernel(Args a) {
 // 1, with E4M3 activations 20.4 / 18.3 / 17.3 / 19.4 us (the plain read of
 // the same bytes 17.3 us).
 // ---------------------------------------------------------------------------
+// (a quantizing instance's slot holds weights only: its activations are staged
+// in LDS before the stream starts, so it takes the E4M3 depth)
 template <int XK>
 constexpr int m1r_depth() { return XK == XK_F32 ? 1 : 2; }
+constexpr int QRB = 4;   // rounds of quantization slots issued together by the ring kernel (32 chunks)
 
 template <int XK, bool SBF16, int G, int D>
 __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
-  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
+  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3, XQD = xk_quantize<XK>();
   __shared__ float red[WAVES][G * 8];
+  // quantizing instances: the wave's codes and scales (at most QCHUNKS_MAX chunks per wave)
+  __shared__ uint4 qcodes[WAVES][XQD ? QCHUNKS_MAX * 8 : 1];
+  __shared__ float qscl[WAVES][XQD ? QCHUNKS_MAX : 1];
   const int tile = blockIdx.x;
   int mi = 0;
   while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
@@ -907,10 +1031,10 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
 
   const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
   const v4i rw = make_rsrc(mem.w, w_bytes);
-  constexpr uint32_t XE = XQ8 ? 1u : XBF16 ? 2u : 4u;
+  constexpr uint32_t XE = xk_bytes<XK>();
   const uint32_t x_bytes = uint32_t(K) * XE;
   const v4i rx = make_rsrc(a.x, x_bytes);
-  constexpr int XL = XQ8 ? 1 : XBF16 ? 2 : 4;
+  constexpr int XL = XQD ? 1 : xk_loads<XK>();
 
   // ---- scales of the wave's chunks, chunk c_begin + 64 h + lane in register h
   const int nb = (mem.rows + 127) >> 7;
@@ -951,6 +1075,13 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
   };
   __builtin_amdgcn_sched_barrier(0);
 
+  // ---- a quantizing instance's first QRB rounds of activations go out before
+  // the weight stream (quantized while it is in flight; loads retire in order)
+  const int nch = c_end - c_begin;
+  uint4 qraw[XQD ? QRB : 1][4];
+  if constexpr (XQD) quant_issue<XK, QRB>(rx, x_bytes, K, c_begin, nch, lane, 0, qraw);
+  __builtin_amdgcn_sched_barrier(0);
+
   uint4 wv[D][G];
   uint4 xr[D][XL];
   auto issue = [&](int c, int d) {
@@ -962,16 +1093,29 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
       const uint32_t off = live && r < rend ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
       wv[d][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, kStreamLoadAux));
     }
+    if (!XQD) {
 #pragma unroll
-    for (int q = 0; q < XL; ++q) {
-      const uint32_t off = live ? uint32_t(k) * XE + 16u * q : x_bytes;
-      xr[d][q] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
+      for (int q = 0; q < XL; ++q) {
+        const uint32_t off = live ? uint32_t(k) * XE + 16u * q : x_bytes;
+        xr[d][q] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
+      }
     }
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     issue(c_begin + d, d);
     __builtin_amdgcn_sched_barrier(0);   // keep the slots in chunk order
+  }
+  if constexpr (XQD) {
+    quant_store<XK, QRB>(nch, QCHUNKS_MAX, lane, 0, qraw, qcodes[wave], qscl[wave]);
+    // a range beyond QRB rounds (more than 32 chunks per wave): the rest in
+    // further batches, whose loads wait behind the first weight slots
+    for (int r0 = 64 * QRB; r0 < nch * 8; r0 += 64 * QRB) {
+      quant_issue<XK, QRB>(rx, x_bytes, K, c_begin, nch, lane, r0, qraw);
+      quant_store<XK, QRB>(nch, QCHUNKS_MAX, lane, r0, qraw, qcodes[wave], qscl[wave]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
   }
 
   float acc[G];
@@ -982,10 +1126,14 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
     for (int d = 0; d < D; ++d) {
       const int c = c0 + d;
       const float sw0 = wscale(c, 0), sw1 = wscale(c, 1);
-      const float sa = XQ8 ? ascale(c) : 1.f;
+      // a quantizing instance's codes and scale of chunk c, from LDS (zeros past the range)
+      const int cq = min(c - c_begin, QCHUNKS_MAX - 1);
+      const uint4 qc = XQD && c < c_end ? qcodes[wave][8 * cq + jp] : make_uint4(0, 0, 0, 0);
+      const float sa = XQ8 ? ascale(c) : XQD ? (c < c_end ? qscl[wave][cq] : 0.f) : 1.f;
       float xv[16];
-      if (XQ8) {
-        const uint32_t x4[4] = {xr[d][0].x, xr[d][0].y, xr[d][0].z, xr[d][0].w};
+      if (XQ8 || XQD) {
+        const uint4 cx = XQD ? qc : xr[d][0];
+        const uint32_t x4[4] = {cx.x, cx.y, cx.z, cx.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, false);
@@ -1029,7 +1177,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
         }
         const int r = row0 + 8 * g + rl;
         const float sw = (r >> 7) == srow ? sw0 : sw1;
-        acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), XQ8 ? sa * sw : sw, acc[g]);
+        acc[g] = fmaf((p[0] + p[1]) + (p[2] + p[3]), XQ8 || XQD ? sa * sw : sw, acc[g]);
       }
       __builtin_amdgcn_sched_barrier(0);
       issue(c + D, d);   // refill this slot
@@ -2000,6 +2148,70 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
 #undef BSF8_QR
   hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
   return device_status(hipGetLastError(), "w8a8 streaming launch");
+}
+
+// The W8A8 arm with the activation quantization in the same call, at one token:
+// the one-token kernels (and their load-ring form) quantize each wave's K range
+// of the token into LDS before the weight stream lands (see quant_issue) and
+// then run as on quantized activations, so codes, scales and results are those
+// of bsf8_quant_act followed by bsf8_linear_w8a8, bit for bit, and the codes
+// never go to memory.  More tokens do not pay: every block would quantize all
+// of them again (two to four tokens measured 1.5-1.8 us slower than the
+// quantizer followed by the few-token kernel on grouped Q/K/V).
+bool w8a8_dyn_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldx_bytes) {
+  if (M != 1 || !w8a8_stream_applies(w, aligned, M, ldx_bytes)) return false;
+  const M1Shape m1 = m1_shape(w, true, M);
+  return m1.g != 0 && (!m1.ring || m1.cpw <= QCHUNKS_MAX);
+}
+
+std::string describe_w8a8_dyn_stream(const WeightDev& w, int64_t M) {
+  const M1Shape m1 = m1_shape(w, true, M);
+  char b[640];
+  snprintf(b, sizeof(b),
+           "arm=w8a8-dynamic arithmetic=f32/bf16 activations quantized per token 1x128 to e4m3 by each wave for "
+           "its K range into LDS (codes never stored), e4m3 x e4m3 decoded exactly to f32, f32 fma chunk partials "
+           "x (act scale x weight scale) | kernel=%s<quantizing> rows=%d (8-row groups=%d) waves=%d (in-block "
+           "split-K, %d chunks/wave, %s, 8 lanes per 128-byte row piece) | M=%lld blocks=%d",
+           m1.ring ? "w8a16_m1_ring" : "w8a16_m1", m1.rb, m1.g, WAVES, m1.cpw,
+           m1.ring ? "2-chunk load ring" : "all loads first", (long long)M, m1.tiles);
+  return b;
+}
+
+bsf8_status launch_w8a8_dyn_stream(const WeightDev& w, const void* x, bool x_bf16, int64_t M, int64_t ldx, void* y,
+                                   bool y_bf16, int64_t ldy, hipStream_t stream) {
+  const M1Shape m1 = m1_shape(w, true, M);
+  if (M != 1 || m1.g == 0 || (m1.ring && m1.cpw > QCHUNKS_MAX)) {
+    set_error("UNSUPPORTED: the quantizing streaming kernels take one token and at most %d chunks per wave",
+              QCHUNKS_MAX);
+    return BSF8_E_UNSUPPORTED;
+  }
+  Args a{};
+  a.w = w;
+  a.tm = m1.tm;
+  a.x = x;
+  a.y = y;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = 1;
+  a.col_tiles = 1;
+  a.chunks_per_wave = m1.cpw;
+  a.rows_per_block = m1.rb;
+  a.x_bf16 = x_bf16 ? 1 : 0;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  const bool sb = w.scale_bf16 != 0;
+#define BSF8_D1(XK, G, C) (sb ? w8a16_m1_kernel<XK, true, G, C> : w8a16_m1_kernel<XK, false, G, C>)
+#define BSF8_DR(XK, G) \
+  (sb ? w8a16_m1_ring_kernel<XK, true, G, m1r_depth<XK>()> : w8a16_m1_ring_kernel<XK, false, G, m1r_depth<XK>()>)
+#define BSF8_DSEL(XK)                                                                                    \
+  (m1.ring ? (m1.g == 2 ? BSF8_DR(XK, 2) : m1.g == 3 ? BSF8_DR(XK, 3) : BSF8_DR(XK, 4))                \
+   : m1.cpw == 4 ? (m1.g == 2 ? BSF8_D1(XK, 2, 4) : m1.g == 3 ? BSF8_D1(XK, 3, 4) : BSF8_D1(XK, 4, 4)) \
+                 : (m1.g == 2 ? BSF8_D1(XK, 2, 5) : m1.g == 3 ? BSF8_D1(XK, 3, 5) : BSF8_D1(XK, 4, 5)))
+  auto k1 = x_bf16 ? BSF8_DSEL(XK_BF16Q) : BSF8_DSEL(XK_F32Q);
+#undef BSF8_DSEL
+#undef BSF8_DR
+#undef BSF8_D1
+  hipLaunchKernelGGL(k1, dim3(m1.tiles), dim3(THREADS), 0, stream, a);
+  return device_status(hipGetLastError(), "w8a8 dynamic streaming launch");
 }
 
 }  // namespace bsf8

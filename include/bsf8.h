@@ -90,8 +90,10 @@ typedef enum bsf8_dtype {
 typedef enum bsf8_arm {
   BSF8_ARM_W8A16 = 0,  /* F32 activations, F32 accumulation */
   BSF8_ARM_W8A8 = 1,   /* per-token 1x128 E4M3 activations, F32 epilogue */
-  BSF8_ARM_DENSE = 2   /* the handle's upcast dense BF16 copy times BF16 activations (bsf8_linear_dense);
+  BSF8_ARM_DENSE = 2,  /* the handle's upcast dense BF16 copy times BF16 activations (bsf8_linear_dense);
                           for bsf8_workspace_size and bsf8_describe */
+  BSF8_ARM_W8A8_DYNAMIC = 3  /* W8A8 on F32 or BF16 activations quantized in the same call
+                                (bsf8_linear_w8a8_dynamic) */
 } bsf8_arm;
 
 /* Header-level description of one tensor.  data may be NULL for a header-only
@@ -319,6 +321,33 @@ bsf8_status bsf8_linear_w8a16(const bsf8_weight* w, const void* x, int32_t x_dty
 bsf8_status bsf8_linear_w8a8(const bsf8_weight* w, const uint8_t* xq, int64_t ldq, const float* xs,
                              int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, int32_t y_dtype, int64_t ldy,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsf8_linear_w8a8_dynamic -- the W8A8 arm on unquantized activations: x is
+ * quantized per token in 1x128 groups exactly as bsf8_quant_act does (amax /
+ * 448, E4M3 round-to-nearest-even, saturating) and the product is then that
+ * of bsf8_linear_w8a8; the result is bit-identical to those two calls.
+ * ("Module w8a8_prefill", section "WHY (#917 / #928)": the per-token group
+ *  quantization that feeds the FP8 product, and the product itself.)
+ * One token, with the weight and x 16-byte aligned and the one-token streaming
+ * kernels applicable (K up to 65536), is quantized inside those kernels: each
+ * wave quantizes its K range into LDS before its weights land, the codes and
+ * scales never go to memory and no workspace is used.  Otherwise (more tokens,
+ * where every block would quantize all of x again) the codes (row pitch K
+ * rounded up to 16 bytes) and the K-major scales go to the start of the
+ * workspace and the W8A8 kernels read them from there.
+ *
+ * x : [M, K] F32 or BF16, leading dimension ldx (elements); read only.
+ * y : [M, N] BF16 or F32, leading dimension ldy (elements).
+ * workspace: device buffer of bsf8_workspace_size(w, BSF8_ARM_W8A8_DYNAMIC, M)
+ *     bytes, 256-byte aligned; that size covers the two-step path, and the
+ *     buffer may be NULL when the call quantizes inside the one-token kernels.
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, WORKSPACE (a workspace is needed
+ * and missing or too small), DEVICE.
+ */
+bsf8_status bsf8_linear_w8a8_dynamic(const bsf8_weight* w, const void* x, int32_t x_dtype, int64_t M, int64_t ldx,
+                                     void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * bsf8_linear_w8a8_noalloc -- bsf8_linear_w8a8 without a workspace argument and

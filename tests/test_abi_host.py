@@ -126,6 +126,50 @@ def test_workspace_sizes():
         L.bsf8_weight_destroy(h)
 
 
+def test_dynamic_w8a8_workspace_describe_and_refusals():
+    """bsf8_linear_w8a8_dynamic: its workspace is the two-step form's (codes at a
+    16-byte row pitch, K-major scales, the W8A8 call's own workspace, each from a
+    256-byte boundary); one token describes the quantizing one-token kernel, more
+    the quantizer and then the W8A8 kernels; bad arguments are refused before any
+    launch, a missing workspace wherever the two-step form is needed."""
+    L = B.lib()
+    st, h = _handle([5120], 5120)
+    assert st == 0
+    r256 = lambda n: (n + 255) // 256 * 256
+    try:
+        b, w8 = ctypes.c_size_t(), ctypes.c_size_t()
+        for M in (1, 4, 5, 1024):
+            assert L.bsf8_workspace_size(h, B.ARM_W8A8_DYNAMIC, M, ctypes.byref(b)) == 0
+            assert L.bsf8_workspace_size(h, B.ARM_W8A8, M, ctypes.byref(w8)) == 0
+            assert b.value == r256(M * 5120) + r256(M * 40 * 4) + w8.value, M
+        assert L.bsf8_workspace_size(h, B.ARM_W8A8_DYNAMIC, 0, ctypes.byref(b)) == 0 and b.value == 0
+        d1 = L.bsf8_describe(h, B.ARM_W8A8_DYNAMIC, 1).decode()
+        assert "arm=w8a8-dynamic" in d1 and "kernel=w8a16_m1<quantizing>" in d1, d1
+        d3 = L.bsf8_describe(h, B.ARM_W8A8_DYNAMIC, 3).decode()
+        assert d3.startswith("quant_act into the workspace") and "kernel=w8a16_mf" in d3, d3
+        d5 = L.bsf8_describe(h, B.ARM_W8A8_DYNAMIC, 5).decode()
+        assert d5.startswith("quant_act into the workspace") and "w8a8_gemm" in d5, d5
+        fake = ctypes.c_void_p(1 << 40)
+        ws_fake = ctypes.c_void_p(1 << 41)
+        call = lambda x, dt, M, ldx, ws=None, wsb=0: B.status_name(
+            L.bsf8_linear_w8a8_dynamic(h, x, dt, M, ldx, fake, B.DT_BF16, 5120, ws, wsb, None))
+        assert call(fake, B.DT_F32, 0, 5120) == "OK"
+        assert call(fake, B.DT_F32, -1, 5120) == "INVALID_ARG"
+        assert call(fake, B.DT_F16, 2, 5120) == "INVALID_ARG"
+        assert call(fake, B.DT_F32, 2, 5119) == "INVALID_ARG"
+        assert call(None, B.DT_F32, 2, 5120) == "INVALID_ARG"
+        assert call(ctypes.c_void_p((1 << 40) + 2), B.DT_F32, 1, 5120) == "ALIGNMENT"
+        # two or five tokens, or one with x only element-aligned: the two-step form, refused without a workspace
+        assert call(fake, B.DT_F32, 5, 5120) == "WORKSPACE"
+        assert call(fake, B.DT_F32, 2, 5120) == "WORKSPACE"
+        assert call(ctypes.c_void_p((1 << 40) + 4), B.DT_F32, 1, 5120) == "WORKSPACE"
+        assert L.bsf8_workspace_size(h, B.ARM_W8A8_DYNAMIC, 5, ctypes.byref(b)) == 0
+        assert call(fake, B.DT_F32, 5, 5120, ws_fake, b.value - 1) == "WORKSPACE"
+        assert call(fake, B.DT_F32, 5, 5120, ctypes.c_void_p((1 << 41) + 16), b.value) == "ALIGNMENT"
+    finally:
+        L.bsf8_weight_destroy(h)
+
+
 def test_compute_calls_refuse_bad_arguments_without_launching():
     L = B.lib()
     st, h = _handle([128], 256)

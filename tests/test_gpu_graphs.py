@@ -6,8 +6,9 @@ state it shares (a split-K workspace, the no-allocation scratch) was written
 by other calls in between.  One graph holds a call of every kernel family:
 the W8A16 one-token, ring, two-to-four-token, few-token, general and
 LDS-staged GEMM kernels; W8A8 through the streaming kernels and the GEMM with
-split-K partials; the quantizer, the fused GLU quantizer and the activation
-alone; the upcast and the dense product.  Between replays the outputs are
+split-K partials; W8A8 on unquantized activations (quantized inside the
+one-token kernel, or into the workspace before the W8A8 kernels); the quantizer, the
+fused GLU quantizer and the activation alone; the upcast and the dense product.  Between replays the outputs are
 overwritten and eager calls reuse the same workspace and scratch with other
 inputs; after every replay each output must equal its eager bits.
 """
@@ -49,7 +50,9 @@ def test_graph_of_every_kernel_family_replays_eager_bits():
     calls = [("w8a16_m1", w_a, 1, B.ARM_W8A16), ("w8a16_m3", w_a, 3, B.ARM_W8A16), ("w8a16_m7", w_a, 7, B.ARM_W8A16),
              ("w8a16_m40", w_a, 40, B.ARM_W8A16), ("w8a16_gemm_m512", w_g, 512, B.ARM_W8A16),
              ("w8a16_ring_m1", w_r, 1, B.ARM_W8A16),
-             ("w8a8_m1", w_a, 1, B.ARM_W8A8), ("w8a8_m3", w_a, 3, B.ARM_W8A8), ("w8a8_split_m64", w_a, 64, B.ARM_W8A8)]
+             ("w8a8_m1", w_a, 1, B.ARM_W8A8), ("w8a8_m3", w_a, 3, B.ARM_W8A8), ("w8a8_split_m64", w_a, 64, B.ARM_W8A8),
+             ("w8a8_dyn_m1", w_a, 1, B.ARM_W8A8_DYNAMIC), ("w8a8_dyn_m3", w_a, 3, B.ARM_W8A8_DYNAMIC),
+             ("w8a8_dyn_m64", w_a, 64, B.ARM_W8A8_DYNAMIC)]
     describes = {}
     state = {}
     for name, w, M, arm in calls:
@@ -65,7 +68,8 @@ def test_graph_of_every_kernel_family_replays_eager_bits():
         banner(f"graph case {name}: {describes[name]}")
     joined = " ".join(describes.values())
     for kernel in ("kernel=w8a16_m1 ", "kernel=w8a16_m1_ring", "kernel=w8a16_mf", "kernel=w8a16_small_m",
-                   "kernel=w8a16_gemm ", "w8a16_m1<e4m3>", "kernel=w8a8_gemm_fast"):
+                   "kernel=w8a16_gemm ", "w8a16_m1<e4m3>", "kernel=w8a8_gemm_fast", "w8a16_m1<quantizing>",
+                   "arm=w8a8-dynamic", "quant_act into the workspace"):
         assert kernel in joined, (kernel, describes)
     assert "split_k=1 " not in describes["w8a8_split_m64"], describes["w8a8_split_m64"]
 
@@ -87,6 +91,8 @@ def test_graph_of_every_kernel_family_replays_eager_bits():
         for name, (w, M, arm, x, y, ws, xq, xs) in state.items():
             if arm == B.ARM_W8A16:
                 B.linear_w8a16(w, x, out=y, workspace=ws)
+            elif arm == B.ARM_W8A8_DYNAMIC:
+                B.linear_w8a8_dynamic(w, x, out=y, workspace=ws)
             else:
                 B.quant_act(x, xq, xs)
                 B.linear_w8a8(w, xq, xs, out=y, workspace=ws)
