@@ -894,7 +894,7 @@ def main():
                          "launches": v["launches"], "path": v["describe"]} for k, v in d["by_M"].items()},
             "roofline": {"bound": "hbm", "kernel": "w8a16_m1<quantizing> (M=1, quantization inside)",
                          "achieved": round(d1["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(d1["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(d1["gbs"] / HBM_PEAK_GBS, 4), "traffic": profiled_traffic("w8a8_dyn_qkv_m1"),
                          "algorithmic_bytes": d1["algorithmic_bytes"]}}
         line["ffn_down_decode"] = decode_line(extra["down_decode"], profiled_traffic("w8a16_decode_down_m1"))
         d = extra["down_w8a8_dynamic"]["by_M"]["M1"]
@@ -904,7 +904,7 @@ def main():
             "two_calls_us": round(d["two_calls_us"], 2), "launches": d["launches"], "path": d["describe"],
             "roofline": {"bound": "hbm", "kernel": "w8a16_m1_ring<quantizing> (M=1, quantization inside)",
                          "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": profiled_traffic("w8a8_dyn_down_m1"),
                          "algorithmic_bytes": d["algorithmic_bytes"]}}
         d = extra["down_w8a8_decode"]
         line["ffn_down_w8a8_decode"] = {
