@@ -13,9 +13,9 @@
 //    F32 in registers (w8a16_m1_kernel; w8a16_m1_ring_kernel beyond five chunks
 //    per wave);
 //  * 2 to 8 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
-//  * (E4M3 activations at 2 to 4 tokens, the W8A8 arm's few-token path: the
-//    one-token weight stream with the F32 products summed on the matrix
-//    cores, w8a16_mf_kernel, v_mfma_f32_4x4x1f32);
+//  * (the W8A8 arm's E4M3 activations at one to eight tokens take the same two
+//    kernels: codes decoded exactly, each chunk partial scaled by activation
+//    scale x weight scale);
 //  * many tokens, once 256-row x 64-token tiles fill half the compute units:
 //    the LDS-staged GEMM (w8a16_gemm_kernel);
 //  * the tokens in between, or any unaligned operand: the general MFMA kernel.
@@ -117,7 +117,7 @@ struct Args {
   int32_t x_bf16;
   int32_t y_bf16;
   int32_t rows_per_block;   // few-token VALU kernels: rows of a block (at most 8 G)
-  // E4M3-activation instances (the W8A8 arm at one to four tokens): the
+  // E4M3-activation instances (the W8A8 arm at one to eight tokens): the
   // per-token group scales, element (m, kb) at xs[m * xs_sm + kb * xs_sk]
   const float* xs;
   int64_t xs_sm;
@@ -498,8 +498,9 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //    instruction), written to a wave-private LDS buffer when their chunk comes
 //    up and read back in the MFMA layout;
 //  * activations are loaded compactly (32 lanes per F32 token, 16 per BF16
-//    token), each lane splits only what it loaded, and the BF16 terms go to a
-//    wave-private LDS scratch in fragment order; tokens past M read a zero row;
+//    token, 8 per token of E4M3 codes), each lane splits (or decodes) only what
+//    it loaded, and the BF16 terms go to a wave-private LDS scratch in fragment
+//    order; tokens past M read a zero row;
 //  * SM_RING chunks of both operands are in flight per wave in registers, one
 //    chunk: each chunk is about 8 KiB per wave (weights and activations), and
 //    with more in flight the memory system only queues the requests (W
@@ -516,7 +517,13 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //    token g % M, so M <= 5 takes one 16-column pass and M <= 8 two (a third
 //    and a sixth of the general kernel's MFMAs).  Each column keeps its own F32
 //    accumulator over the chunks, and a token's three columns are added once,
-//    when the waves' partial tiles are reduced.
+//    when the waves' partial tiles are reduced;
+//  * E4M3 codes (the W8A8 arm) decode exactly to one BF16 term, column = token,
+//    and the epilogue scales each chunk partial by activation scale x weight
+//    scale, the activation scale of the lane's column token loaded with the
+//    chunk's slot (W [5120, 5120] at two to eight tokens 8.3-8.8 us, where the
+//    F32-matrix-core kernel took 9.9 us at two to four and the GEMM 16.2 us
+//    from five on; grouped Q/K/V 9.7-10.0 us against 13.0 / 19.3 us).
 // In a chunk, lane group gq owns the 32 contiguous K bytes [32 gq, 32 gq + 32)
 // of both operands, and K-step s of the 16x16x32 MFMA the 8 at 32 gq + 8 s.
 // LDS layouts (16-byte pieces, bank-conflict free for the fragment reads):
@@ -538,12 +545,14 @@ constexpr int SM_RING = 1;                    // chunks in flight per wave (the 
 constexpr int SM_SCALE_REGS = 2;               // chunk scales per wave: up to 128 (K up to 131072 with 8 waves)
 constexpr int SM_WBUF = ROWS * CHUNK;          // a wave's weight bytes per chunk: 4 KiB
 
-template <bool XBF16, bool SBF16, int NXI, int NP, int SM_DEPTH>
+template <int XK, bool SBF16, int NXI, int NP, int SM_DEPTH>
 __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
-  constexpr int NT = XBF16 ? 1 : TERMS;          // a BF16 activation is its own single term
+  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
+  constexpr int NT = XK == XK_F32 ? TERMS : 1;   // a BF16 activation, or a decoded E4M3 code, is its own single term
   static_assert(NP == 1 || NP == 2, "one or two 16-column MFMA passes");
-  constexpr int LPT = XBF16 ? 16 : 32;           // lanes per token in a compact load
-  constexpr int EPL = XBF16 ? 8 : 4;             // activations per lane in a compact load
+  static_assert(!XQ8 || NP == 1, "E4M3 tokens take one pass: column = token");
+  constexpr int LPT = XQ8 ? 8 : XBF16 ? 16 : 32;  // lanes per token in a compact load
+  constexpr int EPL = XQ8 ? 16 : XBF16 ? 8 : 4;   // activations per lane in a compact load
   __shared__ __attribute__((aligned(1024))) uint8_t wbuf[WAVES][SM_WBUF];
   __shared__ __attribute__((aligned(16))) uint8_t scratch[WAVES][NT * SM_TERM_BYTES];
   static_assert(sizeof(float) * WAVES * RT * NP * 64 * 4 <= sizeof(uint8_t) * WAVES * SM_WBUF, "reduction fits the buffers");
@@ -607,13 +616,17 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   uint4 xr[SM_DEPTH][NXI];
   uint4 wr[SM_DEPTH][2 * RT];
   const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
-  const uint32_t x_esz = XBF16 ? 2u : 4u;
+  const uint32_t x_esz = XQ8 ? 1u : XBF16 ? 2u : 4u;
   const uint32_t x_bytes = uint32_t(M) * uint32_t(a.ldx) * x_esz;
   const uint32_t s_esz = SBF16 ? 2u : 4u;
   const uint32_t s_bytes = (a.w.s_rs ? uint32_t((mem.rows + 127) >> 7) * uint32_t(Kb) : 1u) * s_esz;
   const v4i rw = make_rsrc(mem.w, w_bytes);
   const v4i rx = make_rsrc(a.x, x_bytes);
   const v4i rs = make_rsrc(mem.s, s_bytes);
+  // E4M3 activations: the group scale of this lane's column token (l16) for each chunk, loaded with its slot
+  const uint32_t xs_bytes = XQ8 ? uint32_t(((int64_t(M) - 1) * a.xs_sm + int64_t(Kb - 1) * a.xs_sk + 1) * 4) : 0u;
+  const v4i rxs = make_rsrc(a.xs, xs_bytes);
+  uint32_t sar[SM_DEPTH];
 
   // The weight scales of this wave's chunks, one per lane (chunk c_begin +
   // 64 h + lane), loaded first: as the oldest loads, waiting for them never
@@ -647,6 +660,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 
   auto issue = [&](int c, int d) {
     const bool live = c < c_end;
+    if (XQ8) {
+      const bool ok = live && l16 < M;
+      sar[d] = uint32_t(bsf8_raw_buffer_load_b32(
+          rxs, ok ? int((int64_t(l16) * a.xs_sm + int64_t(c) * a.xs_sk) * 4) : int(xs_bytes), 0, 0));
+    }
 #pragma unroll
     for (int i = 0; i < NXI; ++i) {
       const int t = i * (64 / LPT) + xt;
@@ -680,7 +698,15 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
         // slot of this lane's 16-byte K piece in term u's row: piece ^ ((u M + t) & 15)
         auto at = [&](int u) { return sc + u * SM_TERM_BYTES + t * SM_ROW_BYTES +
                                       ((xk >> 3) ^ ((u * M + t) & 15)) * 16 + (xk & 7) * 2; };
-        if (XBF16) {
+        if (XQ8) {
+          // 16 codes, decoded exactly to BF16: pieces xk / 8 and xk / 8 + 1 of the token's row
+          const uint4 q = xr[d][i];
+          const v8bf lo = cvt8(q.x, q.y), hi = cvt8(q.z, q.w);
+          uint8_t* row = sc + t * SM_ROW_BYTES;
+          const int key = t & 15;   // u M + t with u = 0
+          *reinterpret_cast<uint4*>(row + (((xk >> 3) ^ key) * 16)) = __builtin_bit_cast(uint4, lo);
+          *reinterpret_cast<uint4*>(row + ((((xk >> 3) + 1) ^ key) * 16)) = __builtin_bit_cast(uint4, hi);
+        } else if (XBF16) {
           *reinterpret_cast<uint4*>(at(0)) = xr[d][i];
         } else {
           const float v[4] = {__uint_as_float(xr[d][i].x), __uint_as_float(xr[d][i].y), __uint_as_float(xr[d][i].z),
@@ -734,8 +760,16 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           v4f s4;
+          if (XQ8) {
+            // the W8A8 epilogue: block partial x (act scale x weight scale)
+            const float sa = __uint_as_float(sar[d]);
+            const float m0 = sa * sw0, m1 = sa * sw1;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s4[e] = (hi_rows >> (4 * t + e)) & 1u ? sw1 : sw0;
+            for (int e = 0; e < 4; ++e) s4[e] = (hi_rows >> (4 * t + e)) & 1u ? m1 : m0;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s4[e] = (hi_rows >> (4 * t + e)) & 1u ? sw1 : sw0;
+          }
           acc[t][p] += pt[p] * s4;
         }
       }
@@ -1208,250 +1242,6 @@ __global__ __launch_bounds__(THREADS) void w8a16_m1_ring_kernel(Args a) {
 }
 
 
-// ---------------------------------------------------------------------------
-// Two to four tokens of E4M3 activations (the W8A8 arm's few-token path;
-// aligned operands, K <= 5120): the one-token kernel's weight stream with the
-// products on the matrix cores, in F32.  (The template also takes F32 and
-// BF16 activations; the W8A16 arm no longer uses it, since the few-token MFMA
-// kernel with one chunk in flight per wave is faster there: W [5120, 5120] at
-// M = 2 / 4 9.3 / 9.5 -> 8.6 / 9.1 us, Q/K/V at M = 4 12.6 -> 10.4 us.)
-// v_mfma_f32_4x4x1f32 treats a wave as 16 blocks of four lanes: lane 4b + i
-// supplies row i of block b's 4 x 1 A operand and column i of its 1 x 4 B
-// operand, and lane 4b + j receives column j of block b's 4 x 4 product, one
-// register per row.  Lane (s, p, j) = (lane >> 5, (lane >> 2) & 7, lane & 3)
-// therefore loads the 16 weight bytes of row 4s + j of an 8-row group at piece
-// p of a chunk (one load instruction still covers 8 rows x 128 contiguous
-// bytes) and reads from LDS the 16 activations of token j at the same K
-// positions; one MFMA per K position adds w[row 4s + i][k] x[token j][k] into
-// block (s, p)'s product for every i and j.  Each wave copies its activation
-// slice (4 tokens x its chunks, widened to F32) into a wave-private LDS
-// region; those loads go out before the weight stream and are written to LDS
-// once the stream is in flight (loads retire in order, so that wait never
-// covers weights).  After a chunk's 16 positions each product register is one
-// row's and one token's partial over the piece; it is scaled by the chunk's
-// block scale (times the token's group scale for E4M3 activations) into an
-// F32 accumulator.  At the end the 8 pieces of a row and token are added
-// across lanes and the waves in LDS, in wave order.  The product of an E4M3
-// weight and an F32 activation is rounded to F32 once, as an FMA's would be;
-// the matrix core's F32 sum takes the place of the FMA chain, and the vector
-// ALU keeps the decoding and the scaling.  Against the same kernel with 16
-// FMAs per weight byte and token on the vector ALU: 9.8-10.2 -> 9.5-9.7 us at
-// two to four F32 tokens of W [5120, 5120].
-// ---------------------------------------------------------------------------
-// Activation slices in LDS carry 4 floats of padding after every 64: a lane
-// reads the 16 activations of its piece (lanes of one piece position read the
-// same address), and unpadded the eight piece positions, 256 bytes apart
-// modulo the 64 banks, met in pairs.
-__device__ __forceinline__ int xpad(int e) { return e + 4 * (e >> 6); }
-
-typedef float mf_v4f __attribute__((ext_vector_type(4)));
-
-template <int XK, bool SBF16, int G, int CPW>
-__global__ __launch_bounds__(THREADS) void w8a16_mf_kernel(Args a) {
-  constexpr int MT = 4;
-  constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
-  constexpr int XS = MT * CPW * CHUNK + 4 * (MT * CPW * CHUNK / 64);   // padded F32 activations per wave
-  __shared__ __attribute__((aligned(16))) float xl[WAVES * XS];
-  const int tile = blockIdx.x;
-  int mi = 0;
-  while (mi + 1 < a.w.n_members && tile >= a.tm.tile0[mi + 1]) ++mi;
-  const int rtile = tile - a.tm.tile0[mi];
-  const MemberDev mem = a.w.m[mi];
-  const int K = a.w.K, Kb = a.w.Kb;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = lane & 3;          // row of the lane's loads within its half group; its token
-  const int p = (lane >> 2) & 7;   // 16-byte piece of a 128-byte chunk
-  const int s = lane >> 5;         // half of the 8-row group
-  const int row0 = rtile * a.rows_per_block;
-  const int rend = min(mem.rows, row0 + a.rows_per_block);   // rows from rend on: zeros
-  const int c_begin = min(Kb, wave * CPW);
-  const int c_end = min(Kb, c_begin + CPW);
-  const int k_end = min(K, c_end * CHUNK);
-
-  const uint32_t w_bytes = uint32_t(mem.rows) * uint32_t(K);
-  const v4i rw = make_rsrc(mem.w, w_bytes);
-  constexpr uint32_t XE = XQ8 ? 1u : XBF16 ? 2u : 4u;
-  const uint32_t x_bytes = uint32_t(a.M) * uint32_t(a.ldx) * XE;
-  const v4i rx = make_rsrc(a.x, x_bytes);
-
-  // ---- chunk scales first (raw bits, widened at use)
-  const int nb = (mem.rows + 127) >> 7;
-  const int srow = row0 >> 7;
-  const int srow1 = min(srow + 1, nb - 1);
-  uint32_t sc0[CPW], sc1[CPW];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    const int chunk = min(c_begin + c, Kb - 1);
-    const int64_t i0 = int64_t(srow) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
-    const int64_t i1 = int64_t(srow1) * a.w.s_rs + int64_t(chunk) * a.w.s_cs;
-    if (SBF16) {
-      sc0[c] = static_cast<const uint16_t*>(mem.s)[i0];
-      sc1[c] = static_cast<const uint16_t*>(mem.s)[i1];
-    } else {
-      sc0[c] = static_cast<const uint32_t*>(mem.s)[i0];
-      sc1[c] = static_cast<const uint32_t*>(mem.s)[i1];
-    }
-  }
-  // the lane's token's group scale of each chunk (E4M3 activations; tokens past M read token 0's)
-  float sa[CPW];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c)
-    sa[c] = XQ8 ? a.xs[int64_t(j < a.M ? j : 0) * a.xs_sm + int64_t(min(c_begin + c, Kb - 1)) * a.xs_sk] : 1.f;
-  // the scale-grid row of each result register i (row 8 g + 4 s + i of the block)
-  bool second[G][4];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) second[g][i] = ((row0 + 8 * g + 4 * s + i) >> 7) != srow;
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- the wave's activation slice: MT tokens x CPW chunks, as 16-byte pieces
-  constexpr int PPT = CPW * CHUNK * int(XE) / 16;   // pieces per token
-  constexpr int XPL = (MT * PPT + 63) / 64;         // pieces per lane
-  constexpr int EPP = 16 / int(XE);                 // elements per piece
-  uint4 xr[XPL];
-#pragma unroll
-  for (int i = 0; i < XPL; ++i) {
-    const int piece = lane + 64 * i;
-    const int t = piece / PPT, pp = piece - t * PPT;
-    const int k = c_begin * CHUNK + pp * EPP;
-    const bool ok = piece < MT * PPT && t < a.M && k < k_end;
-    const uint32_t off = ok ? (uint32_t(t) * uint32_t(a.ldx) + uint32_t(k)) * XE : x_bytes;
-    xr[i] = as_u4(bsf8_raw_buffer_load_b128(rx, int(off), 0, 0));
-  }
-  // ---- the weight stream
-  uint4 wv[CPW][G];
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    const int chunk = c_begin + c;
-    const int k = chunk * CHUNK + 16 * p;
-    const bool live = chunk < c_end && k < K;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int r = row0 + 8 * g + 4 * s + j;
-      const uint32_t off = live && r < rend ? uint32_t(r) * uint32_t(K) + uint32_t(k) : w_bytes;
-      wv[c][g] = as_u4(bsf8_raw_buffer_load_b128(rw, int(off), 0, kStreamLoadAux));
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // ---- activations into this wave's LDS region, as F32: token t, element e of
-  // the slice at xpad(t * CPW*CHUNK + e) (a piece never crosses a padding point)
-  float* xw = xl + wave * XS;
-#pragma unroll
-  for (int i = 0; i < XPL; ++i) {
-    const int piece = lane + 64 * i;
-    if (piece < MT * PPT) {
-      const int t = piece / PPT, pp = piece - t * PPT;
-      float* dst = xw + xpad(t * (CPW * CHUNK) + pp * EPP);
-      if (XQ8) {
-        const uint32_t x4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, false);
-          const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x4[e], 1.0f, true);
-          reinterpret_cast<float4*>(dst)[e] = make_float4(lo[0], lo[1], hi[0], hi[1]);
-        }
-      } else if (XBF16) {
-        const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-        reinterpret_cast<float4*>(dst)[0] = make_float4(__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xFFFF0000u),
-                                                        __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xFFFF0000u));
-        reinterpret_cast<float4*>(dst)[1] = make_float4(__uint_as_float(w4[2] << 16), __uint_as_float(w4[2] & 0xFFFF0000u),
-                                                        __uint_as_float(w4[3] << 16), __uint_as_float(w4[3] & 0xFFFF0000u));
-      } else {
-        *reinterpret_cast<uint4*>(dst) = xr[i];
-      }
-    }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-
-  float acc[G][4];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[g][i] = 0.f;
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    // the lane's token's 16 activations at its piece
-    const float* xp = xw + xpad(j * (CPW * CHUNK) + c * CHUNK + 16 * p);
-    float xv[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = reinterpret_cast<const float4*>(xp)[q];
-      xv[4 * q] = v.x;
-      xv[4 * q + 1] = v.y;
-      xv[4 * q + 2] = v.z;
-      xv[4 * q + 3] = v.w;
-    }
-    // the lane's 16 weights of each row group, decoded exactly (unscaled)
-    float wf[G][16];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint32_t w4[4] = {wv[c][g].x, wv[c][g].y, wv[c][g].z, wv[c][g].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, false);
-        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w4[e], 1.0f, true);
-        wf[g][4 * e] = lo[0];
-        wf[g][4 * e + 1] = lo[1];
-        wf[g][4 * e + 2] = hi[0];
-        wf[g][4 * e + 3] = hi[1];
-      }
-    }
-    // one MFMA per K position and row group; the groups' chains interleaved
-    mf_v4f pr[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) pr[g] = mf_v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-#pragma unroll
-      for (int g = 0; g < G; ++g) pr[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf[g][e], xv[e], pr[g], 0, 0, 0);
-    // the piece partials, scaled by the chunk's multipliers
-    const float sw0 = __uint_as_float(SBF16 ? sc0[c] << 16 : sc0[c]);
-    const float sw1 = __uint_as_float(SBF16 ? sc1[c] << 16 : sc1[c]);
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sw = second[g][i] ? sw1 : sw0;
-        acc[g][i] = fmaf(pr[g][i], XQ8 ? sw * sa[c] : sw, acc[g][i]);
-      }
-  }
-  // ---- the 8 pieces of a row and token (lanes 4 apart within each half), then the waves in order
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = acc[g][i];
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      acc[g][i] = v;
-    }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  if (p == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xw[j * (G * 8) + 8 * g + 4 * s + i] = acc[g][i];
-  }
-  __syncthreads();
-  for (int i = tid; i < G * 8 * MT; i += THREADS) {
-    const int t = i / (G * 8), rr = i - t * (G * 8);
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += xl[w * XS + i];
-    const int row = row0 + rr;
-    if (t < a.M && row < rend) {
-      const int64_t off = int64_t(t) * a.ldy + mem.col0 + row;
-      if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
-      else static_cast<float*>(a.y)[off] = sum;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Many tokens (aligned operands): an LDS-staged tile of 256 weight rows x 64
@@ -1750,45 +1540,6 @@ M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
   return m;
 }
 
-// The F32-MFMA few-token kernel's shape (two to four tokens, aligned
-// operands, at most five chunks per wave): rows per block balanced like the
-// one-token kernel's (the fewest in [16, 32] that keep the grid within one
-// block per compute unit; a block's last 8-row group may be partly masked),
-// G = ceil(rows / 8) row groups and chunks per wave; g = 0 when it does not
-// apply.
-struct MfShape {
-  int g;
-  int rb;
-  int cpw;
-  TileMap tm;
-  int tiles;
-};
-
-MfShape mf_shape(const WeightDev& w, bool aligned, int64_t M) {
-  MfShape m{};
-  if (!aligned || M < 2 || M > 4 || w.Kb > WAVES * 5) return m;
-  const int cus = w16_device_cus();
-  m.rb = 8 * M1_MAX_G;
-  for (int rb = 16; rb < 8 * M1_MAX_G; ++rb) {
-    int64_t n = 0;
-    for (int i = 0; i < w.n_members; ++i) n += (w.m[i].rows + rb - 1) / rb;
-    if (n <= cus) {
-      m.rb = rb;
-      break;
-    }
-  }
-  m.g = (m.rb + 7) / 8;
-  m.cpw = w.Kb <= WAVES * 4 ? 4 : 5;
-  int t = 0;
-  for (int i = 0; i < w.n_members; ++i) {
-    m.tm.tile0[i] = t;
-    m.tm.n_tiles[i] = (w.m[i].rows + m.rb - 1) / m.rb;
-    t += m.tm.n_tiles[i];
-  }
-  m.tm.tile0[w.n_members] = t;
-  m.tiles = t;
-  return m;
-}
 
 // The few-token MFMA kernel's rows per block: the fewest in [16, 32] that keep
 // the grid within one block per compute unit (W [5120, 5120]: 20 rows, 256
@@ -1841,53 +1592,6 @@ Plan make_plan(const WeightDev& w, int64_t M, bool aligned = false) {
 
 typedef void (*KernelFn)(Args);
 
-template <int XK, bool SB, int C>
-KernelFn mf_kernel_for(int g) {
-  return g == 2 ? w8a16_mf_kernel<XK, SB, 2, C> : g == 3 ? w8a16_mf_kernel<XK, SB, 3, C> : w8a16_mf_kernel<XK, SB, 4, C>;
-}
-
-template <int XK>
-KernelFn mf_kernel_for(bool sb, int g, int cpw) {
-  if (sb) return cpw == 4 ? mf_kernel_for<XK, true, 4>(g) : mf_kernel_for<XK, true, 5>(g);
-  return cpw == 4 ? mf_kernel_for<XK, false, 4>(g) : mf_kernel_for<XK, false, 5>(g);
-}
-
-bsf8_status launch_mf(const WeightDev& w, const MfShape& m, int xk, const void* x, int64_t ldx, const float* xs,
-                      int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
-  Args a{};
-  a.w = w;
-  a.tm = m.tm;
-  a.x = x;
-  a.y = y;
-  a.ldx = ldx;
-  a.ldy = ldy;
-  a.M = int32_t(M);
-  a.col_tiles = 1;
-  a.chunks_per_wave = m.cpw;
-  a.rows_per_block = m.rb;
-  a.x_bf16 = xk == XK_BF16 ? 1 : 0;
-  a.y_bf16 = y_bf16 ? 1 : 0;
-  a.xs = xs;
-  a.xs_sm = xs_sm;
-  a.xs_sk = xs_sk;
-  const bool sb = w.scale_bf16 != 0;
-  if (xk != XK_E4M3) {
-    set_error("UNSUPPORTED: the F32-matrix-core few-token kernel is built for E4M3 activations only");
-    return BSF8_E_UNSUPPORTED;
-  }
-  const KernelFn k = mf_kernel_for<XK_E4M3>(sb, m.g, m.cpw);
-  hipLaunchKernelGGL(k, dim3(m.tiles), dim3(THREADS), 0, stream, a);
-  return device_status(hipGetLastError(), "w8a16_mf launch");
-}
-
-char* describe_mf(char* b, size_t n, const MfShape& m, const char* arm, int64_t M) {
-  snprintf(b, n,
-           "%s | kernel=w8a16_mf rows=%d (8-row groups=%d) waves=%d (in-block split-K, %d chunks/wave, all weight "
-           "loads first, 4-token activation slices in LDS, mfma_f32_4x4x1f32: a lane block is 4 rows x 4 tokens, "
-           "8 rows x 128 bytes per load, no LDS transpose) | M=%lld blocks=%d",
-           arm, m.rb, m.g, WAVES, m.cpw, (long long)M, m.tiles);
-  return b;
-}
 
 int gemm_row_tiles(const WeightDev& w, int32_t* rt0);
 
@@ -2054,14 +1758,14 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     grid = sh.tiles;
     // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load,
     // and 3 M term columns of F32 tokens in one 16-column MFMA pass up to M = 5
-#define BSF8_SMALL(XB, NXI, NP) \
-  (sb ? w8a16_small_m_kernel<XB, true, NXI, NP, SM_RING> : w8a16_small_m_kernel<XB, false, NXI, NP, SM_RING>)
+#define BSF8_SMALL(XK, NXI, NP) \
+  (sb ? w8a16_small_m_kernel<XK, true, NXI, NP, SM_RING> : w8a16_small_m_kernel<XK, false, NXI, NP, SM_RING>)
     if (x_bf16) {
-      kern = M <= 4 ? BSF8_SMALL(true, 1, 1) : BSF8_SMALL(true, 2, 1);
+      kern = M <= 4 ? BSF8_SMALL(XK_BF16, 1, 1) : BSF8_SMALL(XK_BF16, 2, 1);
     } else if (M <= 4) {
-      kern = M <= 2 ? BSF8_SMALL(false, 1, 1) : BSF8_SMALL(false, 2, 1);
+      kern = M <= 2 ? BSF8_SMALL(XK_F32, 1, 1) : BSF8_SMALL(XK_F32, 2, 1);
     } else {
-      kern = BSF8_SMALL(false, 4, 2);
+      kern = BSF8_SMALL(XK_F32, 4, 2);
     }
 #undef BSF8_SMALL
   } else if (aligned && p.rt == 4) {
@@ -2078,27 +1782,33 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   return device_status(hipGetLastError(), "w8a16 launch");
 }
 
-// The W8A8 arm at one to four tokens: the same weight stream with E4M3
-// activations.  A decoded code times a decoded weight is exact in F32, so a
-// chunk partial is the method's block partial summed in another order, and
-// it is scaled by activation scale x weight scale as the F32 epilogue states.
-// At these token counts the 256 x 256 matrix-core tile would read the weight
-// for 1 to 4 useful columns out of 256.
+// The W8A8 arm at one to eight tokens: the same weight streams with E4M3
+// activations (the one-token kernels, and from two tokens the few-token
+// kernel).  A decoded code times a decoded weight is exact in F32 (and the
+// BF16 matrix cores add such products exactly into F32), so a chunk partial is
+// the method's block partial summed in another order, and it is scaled by
+// activation scale x weight scale as the F32 epilogue states.  At these token
+// counts a matrix-core GEMM tile would read the weight for 1 to 8 useful
+// columns out of 128 or 256.
 bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
-  if (!aligned || M * ldq >= (int64_t(1) << 31)) return false;
+  // (the streaming kernels hold a wave's chunk scales in two registers per lane: K up to 131072)
+  if (!aligned || M < 1 || M > SM_MAXM || w.Kb > MAX_KB || M * ldq >= (int64_t(1) << 31)) return false;
   for (int i = 0; i < w.n_members; ++i)
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) return false;
-  return m1_shape(w, true, M).g != 0 || mf_shape(w, true, M).g != 0;
+  return M > 1 || m1_shape(w, true, M).g != 0;
 }
 
 std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
-  const MfShape mf = mf_shape(w, true, M);
-  if (mf.g) {
+  if (M > 1) {
+    const SmallShape sh = small_shape(w);
     char b[512];
-    return describe_mf(b, sizeof(b), mf,
-                       "arm=w8a8 arithmetic=e4m3 x e4m3 decoded exactly to f32, products summed on the matrix cores "
-                       "per 16-K piece, piece partials x (act scale x weight scale)",
-                       M);
+    snprintf(b, sizeof(b),
+             "arm=w8a8 arithmetic=e4m3 codes decoded exactly to bf16 x e4m3 weights decoded exactly to bf16, "
+             "mfma_f32_16x16x32_bf16 (column = token), f32 chunk partials x (act scale x weight scale) | "
+             "kernel=w8a16_small_m<e4m3> rows=%d tokens<=%d waves=%d (in-block split-K, weights 8 lanes per "
+             "128-byte row through a wave-private LDS transpose, %d chunk in flight per wave) | M=%lld blocks=%d",
+             sh.rb, SM_MAXM, WAVES, SM_RING, (long long)M, sh.tiles);
+    return b;
   }
   const M1Shape m1 = m1_shape(w, true, M);
   char b[448];
@@ -2113,8 +1823,28 @@ std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
 
 bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t xs_sm,
                                int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
-  const MfShape mf = mf_shape(w, true, M);
-  if (mf.g) return launch_mf(w, mf, XK_E4M3, xq, ldq, xs, xs_sm, xs_sk, M, y, y_bf16, ldy, stream);
+  if (M > 1 && M <= SM_MAXM) {
+    const SmallShape sh = small_shape(w);
+    Args a{};
+    a.w = w;
+    a.tm = sh.tm;
+    a.x = xq;
+    a.y = y;
+    a.ldx = ldq;
+    a.ldy = ldy;
+    a.M = int32_t(M);
+    a.col_tiles = 1;
+    a.chunks_per_wave = (w.Kb + WAVES - 1) / WAVES;
+    a.rows_per_block = sh.rb;
+    a.y_bf16 = y_bf16 ? 1 : 0;
+    a.xs = xs;
+    a.xs_sm = xs_sm;
+    a.xs_sk = xs_sk;
+    const bool sb = w.scale_bf16 != 0;
+    auto k = sb ? w8a16_small_m_kernel<XK_E4M3, true, 1, 1, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, 1, 1, SM_RING>;
+    hipLaunchKernelGGL(k, dim3(sh.tiles), dim3(THREADS), 0, stream, a);
+    return device_status(hipGetLastError(), "w8a8 few-token launch");
+  }
   const M1Shape m1 = m1_shape(w, true, M);
   if (m1.g == 0) {
     set_error("UNSUPPORTED: the streaming W8A8 kernels take one to eight tokens");
@@ -2156,8 +1886,8 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
 // then run as on quantized activations, so codes, scales and results are those
 // of bsf8_quant_act followed by bsf8_linear_w8a8, bit for bit, and the codes
 // never go to memory.  More tokens do not pay: every block would quantize all
-// of them again (two to four tokens measured 1.5-1.8 us slower than the
-// quantizer followed by the few-token kernel on grouped Q/K/V).
+// of them again (at four tokens 40 values per lane, with their quotients in
+// F64, 3-4 us of ALU work per wave ahead of the first chunk).
 bool w8a8_dyn_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldx_bytes) {
   if (M != 1 || !w8a8_stream_applies(w, aligned, M, ldx_bytes)) return false;
   const M1Shape m1 = m1_shape(w, true, M);

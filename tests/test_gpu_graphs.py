@@ -4,8 +4,8 @@ A serving loop records its calls once and replays them, so each kernel path
 must give the same bits from a replay as from an eager call, also when the
 state it shares (a split-K workspace, the no-allocation scratch) was written
 by other calls in between.  One graph holds a call of every kernel family:
-the W8A16 one-token, ring, two-to-four-token, few-token, general and
-LDS-staged GEMM kernels; W8A8 through the streaming kernels and the GEMM with
+the W8A16 one-token, ring, few-token, general and LDS-staged GEMM kernels;
+W8A8 through the one-token and few-token streaming kernels and the GEMM with
 split-K partials; W8A8 on unquantized activations (quantized inside the
 one-token kernel, or into the workspace before the W8A8 kernels); the quantizer, the
 fused GLU quantizer and the activation alone; the upcast and the dense product.  Between replays the outputs are
@@ -67,7 +67,7 @@ def test_graph_of_every_kernel_family_replays_eager_bits():
         describes[name] = w.describe(arm, M)
         banner(f"graph case {name}: {describes[name]}")
     joined = " ".join(describes.values())
-    for kernel in ("kernel=w8a16_m1 ", "kernel=w8a16_m1_ring", "kernel=w8a16_mf", "kernel=w8a16_small_m",
+    for kernel in ("kernel=w8a16_m1 ", "kernel=w8a16_m1_ring", "kernel=w8a16_small_m<e4m3>", "kernel=w8a16_small_m",
                    "kernel=w8a16_gemm ", "w8a16_m1<e4m3>", "kernel=w8a8_gemm_fast", "w8a16_m1<quantizing>",
                    "arm=w8a8-dynamic", "quant_act into the workspace"):
         assert kernel in joined, (kernel, describes)

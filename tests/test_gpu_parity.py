@@ -892,15 +892,16 @@ def test_w8a16_blocks_of_odd_row_counts(sdt, M):
     assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"odd rows {sdt} M={M}")
 
 
-@pytest.mark.parametrize("K", [384, 4000, 5120])
+@pytest.mark.parametrize("K", [384, 4000, 5120, 17408])
 @pytest.mark.parametrize("sdt", ["bf16", "f32"])
 def test_w8a8_few_tokens_streaming(K, sdt):
-    """The W8A8 arm at one to four tokens runs the streaming kernels with E4M3
-    activations (decoded exactly; one token: chunk partials on the vector ALU, two to
-    four: piece partials on the F32 matrix cores; each scaled by activation scale x
-    weight scale).  Grouped members of 200 and 70 rows (blocks straddling 128-row scale
-    blocks, a ragged last member), K with a partial last chunk (4000) and with every
-    wave's five chunks (5120), BF16 and F32 grids, token-major and K-major activation
+    """The W8A8 arm at one to eight tokens runs the streaming kernels with E4M3
+    activations decoded exactly (one token: F32 chunk partials on the vector ALU; two
+    to eight: the few-token kernel's BF16 matrix cores, one column per token; each
+    chunk partial scaled by activation scale x weight scale).  Grouped members of 200
+    and 70 rows (blocks straddling 128-row scale blocks, a ragged last member), K with
+    a partial last chunk (4000), with every wave's five chunks (5120) and a long K
+    (17408: 17 chunks per wave), BF16 and F32 grids, token-major and K-major activation
     scales: every output against the oracle."""
     t = torch()
     g = np.random.default_rng(227 + K)
@@ -915,13 +916,13 @@ def test_w8a8_few_tokens_streaming(K, sdt):
     dt = t.float32 if sdt == "f32" else t.bfloat16
     w = B.BlockFP8Weight([(t.from_numpy(c).to(device()), t.from_numpy(np.asarray(s, np.float32)).to(device()).to(dt))
                           for c, s in om])
-    x_all = synth.gaussian_activations(227, f"stream8_X{K}", 4, K)
+    x_all = synth.gaussian_activations(227, f"stream8_X{K}", 8, K)
     Kb = -(-K // 128)
-    for M in (1, 2, 3, 4):
+    for M in (1, 2, 3, 4, 5, 8):
         x = x_all[:M]
         xq, xs = O.quant_act(x)
         d = w.describe(B.ARM_W8A8, M)
-        assert "e4m3 x e4m3 decoded exactly" in d, d
+        assert ("w8a16_m1" if M == 1 else "w8a16_small_m<e4m3>") in d and "decoded exactly" in d, d
         ref, bound = O.linear_w8a8(xq, xs, om), O.abs_bound_w8a8(xq, xs, om)
         xqd = t.from_numpy(xq).to(device())
         tm = t.from_numpy(xs).to(device())
