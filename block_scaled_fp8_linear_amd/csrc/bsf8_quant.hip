@@ -4,13 +4,15 @@
 //  groups of 128 channels; "FP8 Native Serving", section "FP8 E4M3: range and
 //  quirks": finite range +-448, no infinity.)
 //
-// One group of 128 channels is handled by 32 lanes (half a wave), 4 channels per
-// lane, so a wave covers 256 contiguous channels of one token and every global
-// access is a coalesced 16-byte (F32) or 8-byte (BF16) load and a 4-byte store.
-// A half-wave takes two or four consecutive groups (four for large tensors)
-// and issues all their loads before processing any, so each lane has several
-// loads in flight.
-// The group amax is a 5-step butterfly inside the half-wave.  The arithmetic is
+// One group of 128 channels is handled by the lanes of one 16-byte load each:
+// 32 lanes of 4 F32 channels (half a wave) or 16 lanes of 8 BF16 channels (a
+// quarter), so every global access is a coalesced 16-byte load and a 4- or
+// 8-byte store.  (With BF16 in 8-byte loads the fused GLU step, which reads
+// the gate and the up half, ran at 33.5 us where this layout takes less;
+// see the launch.)  A slot of lanes takes two or four consecutive groups (four
+// for large tensors) and issues all their loads before processing any, so
+// each lane has several loads in flight.
+// The group amax is a butterfly inside the group's lanes.  The arithmetic is
 // the defined one: s = max(amax, 1e-10) / 448 in F32 (IEEE division, hipcc's
 // default), f = x / s with the IEEE F32 quotient, clamp to +-448, then the
 // hardware RNE conversion v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950), which keeps
@@ -56,6 +58,38 @@ constexpr int64_t kManyGroups = int64_t(1) << 18;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// EPL consecutive values (one 16-byte load: 8 BF16 or 4 F32) at element off;
+// zeros from element `valid` on.
+template <bool BF16, int EPL>
+__device__ __forceinline__ void load_lane(const void* x, int64_t off, int valid, bool vec_ok, float (&v)[EPL]) {
+  static_assert(EPL * (BF16 ? 2 : 4) == 16, "one 16-byte load per lane");
+  if (BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+    if (valid == EPL && vec_ok) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[j] = j < valid ? bf16_to_f32(p[j]) : 0.0f;
+    }
+  } else {
+    const float* p = static_cast<const float*>(x) + off;
+    if (valid == EPL && vec_ok) {
+      const float4 u = *reinterpret_cast<const float4*>(p);
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[j] = j < valid ? p[j] : 0.0f;
+    }
+  }
+}
+
+// four channels of the quantizer's unit of work, kept for the activation alone
 template <bool BF16>
 __device__ __forceinline__ void load4(const void* x, int64_t off, int valid, bool vec_ok, float v[4]) {
   if (BF16) {
@@ -92,22 +126,29 @@ __device__ __forceinline__ float silu_glu(float g, float u) {
 }
 
 // GLU: x is the gate/up output; K = F, the up half starts at column K.
-template <bool BF16, bool GLU, int kGroupsPerHalf>
+template <bool BF16, bool GLU, int kGroupsPerSlot>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __restrict__ x, int32_t M, int32_t K,
                                                                   int64_t ldx, uint8_t* __restrict__ xq, int64_t ldq,
                                                                   float* __restrict__ xs, int64_t xs_sm, int64_t xs_sk,
                                                                   int32_t Kb,
                                                                   int32_t x_vec, int32_t q_vec) {
-  // Each 32-lane half-wave quantizes kGroupsPerHalf consecutive groups
+  // A group of 128 channels is held by LPG aligned lanes, EPL channels each
+  // (one 16-byte load: 32 lanes of 4 F32 or 16 lanes of 8 BF16), so a wave has
+  // SLOTS group slots.  Each slot quantizes kGroupsPerSlot consecutive groups
   // (row-major over tokens and groups), loading all of them before any is
   // processed so that several loads per lane are in flight.
-  const int lane32 = threadIdx.x & 31;
+  constexpr int EPL = BF16 ? 8 : 4;
+  constexpr int LPG = kBlock / EPL;
+  constexpr int SLOTS = 64 / LPG;
+  const int lane = threadIdx.x & 63;
+  const int lg = lane & (LPG - 1);
   const int64_t n_groups = int64_t(M) * Kb;
-  const int64_t g0 = (int64_t(blockIdx.x) * (kQuantThreads / 32) + (threadIdx.x >> 5)) * kGroupsPerHalf;
-  // Token row and group column of the half-wave's first group: one division,
-  // in 32 bits whenever the group count allows (a 64-bit division is about a
-  // hundred instructions, as many as the arithmetic of the group's channels);
-  // the following groups step along the row and wrap to the next ones.
+  const int64_t g0 =
+      ((int64_t(blockIdx.x) * (kQuantThreads / 64) + (threadIdx.x >> 6)) * SLOTS + lane / LPG) * kGroupsPerSlot;
+  // Token row and group column of the slot's first group: one division, in 32
+  // bits whenever the group count allows (a 64-bit division is about a hundred
+  // instructions, as many as the arithmetic of the group's channels); the
+  // following groups step along the row and wrap to the next ones.
   int64_t mrow0;
   int32_t gcol0;
   if (n_groups <= int64_t(INT32_MAX)) {
@@ -118,11 +159,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
     mrow0 = g0 / Kb;
     gcol0 = int32_t(g0 - mrow0 * Kb);
   }
-  float v[kGroupsPerHalf][4];
-  int64_t mrow[kGroupsPerHalf];
-  int32_t gcol[kGroupsPerHalf], kk[kGroupsPerHalf], valid[kGroupsPerHalf];
+  float v[kGroupsPerSlot][EPL];
+  int64_t mrow[kGroupsPerSlot];
+  int32_t gcol[kGroupsPerSlot], kk[kGroupsPerSlot], valid[kGroupsPerSlot];
 #pragma unroll
-  for (int j = 0; j < kGroupsPerHalf; ++j) {
+  for (int j = 0; j < kGroupsPerSlot; ++j) {
     const int64_t gi = g0 + j;
     const bool live = gi < n_groups;
     int32_t gc = gcol0 + j;
@@ -135,39 +176,49 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const void* __
       }
     mrow[j] = live ? mr : 0;
     gcol[j] = live ? gc : 0;
-    kk[j] = gcol[j] * kBlock + lane32 * 4;
-    valid[j] = live ? max(0, min(4, K - kk[j])) : 0;
-    load4<BF16>(x, mrow[j] * ldx + kk[j], valid[j], x_vec != 0, v[j]);
+    kk[j] = gcol[j] * kBlock + lg * EPL;
+    valid[j] = live ? max(0, min(EPL, K - kk[j])) : 0;
+    load_lane<BF16, EPL>(x, mrow[j] * ldx + kk[j], valid[j], x_vec != 0, v[j]);
     if (GLU) {
-      float u[4];
-      load4<BF16>(x, mrow[j] * ldx + K + kk[j], valid[j], x_vec != 0, u);
+      float u[EPL];
+      load_lane<BF16, EPL>(x, mrow[j] * ldx + K + kk[j], valid[j], x_vec != 0, u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[j][e] = silu_glu(v[j][e], u[e]);   // lanes past K: silu(0) * 0 = 0
+      for (int e = 0; e < EPL; ++e) v[j][e] = silu_glu(v[j][e], u[e]);   // lanes past K: silu(0) * 0 = 0
     }
   }
 #pragma unroll
-  for (int j = 0; j < kGroupsPerHalf; ++j) {
+  for (int j = 0; j < kGroupsPerSlot; ++j) {
     if (g0 + j >= n_groups) break;
-    float amax = fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3])));
+    float amax = 0.0f;
 #pragma unroll
-    for (int d = 16; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 32));
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+#pragma unroll
+    for (int d = LPG / 2; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, LPG));
     const float s = fmaxf(amax, kAmaxFloor) / kE4M3Max;
     const double rs = 1.0 / static_cast<double>(s);   // fl64(1 / s), once per group
-    float f[4];
+    uint32_t packed[EPL / 4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float qv = static_cast<float>(static_cast<double>(v[j][e]) * rs);   // = the IEEE F32 quotient v / s
-      f[e] = fminf(fmaxf(qv, -kE4M3Max), kE4M3Max);
+    for (int w = 0; w < EPL / 4; ++w) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float qv = static_cast<float>(static_cast<double>(v[j][4 * w + e]) * rs);   // = the IEEE F32 quotient v / s
+        f[e] = fminf(fmaxf(qv, -kE4M3Max), kE4M3Max);
+      }
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
+      packed[w] = uint32_t(pk);
     }
-    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
     uint8_t* q = xq + mrow[j] * ldq + kk[j];
-    if (valid[j] == 4 && q_vec) {
-      *reinterpret_cast<int*>(q) = packed;
+    if (valid[j] == EPL && q_vec) {
+      if (EPL == 8)
+        *reinterpret_cast<uint2*>(q) = make_uint2(packed[0], packed[EPL / 4 - 1]);
+      else
+        *reinterpret_cast<uint32_t*>(q) = packed[0];
     } else {
-      for (int e = 0; e < valid[j]; ++e) q[e] = uint8_t(uint32_t(packed) >> (8 * e));
+      for (int e = 0; e < valid[j]; ++e) q[e] = uint8_t(packed[e >> 2] >> (8 * (e & 3)));
     }
-    if (lane32 == 0) xs[mrow[j] * xs_sm + gcol[j] * xs_sk] = s;
+    if (lg == 0) xs[mrow[j] * xs_sm + gcol[j] * xs_sk] = s;
   }
 }
 
@@ -208,7 +259,8 @@ bsf8_status launch_quant(const void* x, bool x_bf16, bool glu, int64_t M, int64_
   const int32_t Kb = int32_t((K + kBlock - 1) / kBlock);
   const int64_t n_groups = M * Kb;
   const int gph = n_groups >= kManyGroups ? 4 : 2;
-  const int64_t per_block = int64_t(kQuantThreads / 32) * gph;
+  const int slots_per_wave = x_bf16 ? 4 : 2;   // 16 or 32 lanes per group
+  const int64_t per_block = int64_t(kQuantThreads / 64) * slots_per_wave * gph;
   const int64_t grid64 = (n_groups + per_block - 1) / per_block;
   if (grid64 > INT32_MAX) {
     set_error("UNSUPPORTED: %lld activation groups", (long long)n_groups);
@@ -216,10 +268,12 @@ bsf8_status launch_quant(const void* x, bool x_bf16, bool glu, int64_t M, int64_
   }
   const int grid = int(grid64);
   const size_t esz = x_bf16 ? 2 : 4;
-  // 4-element vector loads: the base, every row and (GLU) the up half's offset aligned
-  const int x_vec = (reinterpret_cast<uintptr_t>(x) % (4 * esz) == 0) && ((ldx * esz) % (4 * esz) == 0) &&
-                    (!glu || K % 4 == 0);
-  const int q_vec = (reinterpret_cast<uintptr_t>(xq) % 4 == 0) && (ldq % 4 == 0);
+  const int64_t epl = x_bf16 ? 8 : 4;   // channels per lane: one 16-byte load
+  // 16-byte loads: the base, every row and (GLU) the up half's offset aligned
+  const int x_vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && ((ldx * int64_t(esz)) % 16 == 0) &&
+                    (!glu || K % epl == 0);
+  // a lane's epl codes in one store
+  const int q_vec = (reinterpret_cast<uintptr_t>(xq) % epl == 0) && (ldq % epl == 0);
   using Kern = void (*)(const void*, int32_t, int32_t, int64_t, uint8_t*, int64_t, float*, int64_t, int64_t, int32_t,
                         int32_t, int32_t);
   const Kern kern = gph == 4 ? (x_bf16 ? (glu ? quant_act_kernel<true, true, 4> : quant_act_kernel<true, false, 4>)
