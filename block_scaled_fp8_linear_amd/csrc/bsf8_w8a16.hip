@@ -1540,6 +1540,15 @@ M1Shape m1_shape(const WeightDev& w, bool aligned, int64_t M) {
   return m;
 }
 
+// Whether one token takes the one-token kernels: not with four 8-row groups
+// per block and every load issued at once (25-32 rows per block, five chunks
+// per wave), where a wave holds 20 weight loads in flight and the requests
+// queue; the few-token kernel, one chunk in flight per wave, is faster there
+// (grouped Q/K/V at one token, 32-row blocks: 10.2 -> 9.9 us with F32
+// activations, 10.15 -> 9.62 us with E4M3 codes; W [5120, 5120] keeps the
+// one-token kernel, 7.7 against 8.5 us, with three groups of 20 rows).
+bool m1_preferred(const M1Shape& m1) { return m1.g != 0 && (m1.ring || m1.g < 4); }
+
 
 // The few-token MFMA kernel's rows per block: the fewest in [16, 32] that keep
 // the grid within one block per compute unit (W [5120, 5120]: 20 rows, 256
@@ -1663,7 +1672,7 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
     return b;
   }
   const M1Shape m1 = m1_shape(w, aligned, M > 0 ? M : 1);
-  if (m1.g) {
+  if (m1_preferred(m1)) {
     char b1[448];
     snprintf(b1, sizeof(b1),
              "arm=w8a16 arithmetic=f32 activations x e4m3 weights (exact f32 decode), f32 fma accumulate | "
@@ -1705,7 +1714,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   if (p.tiles == 0) return BSF8_OK;
   if (gemm_applies(w, aligned, M)) return launch_gemm(w, x, x_bf16, M, ldx, y, y_bf16, ldy, stream);
   const M1Shape m1 = m1_shape(w, aligned, M);
-  if (m1.g) {
+  if (m1_preferred(m1)) {
     Args a{};
     a.w = w;
     a.tm = m1.tm;
@@ -1799,7 +1808,7 @@ bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ld
 }
 
 std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
-  if (M > 1) {
+  if (M > 1 || !m1_preferred(m1_shape(w, true, M))) {
     const SmallShape sh = small_shape(w);
     char b[512];
     snprintf(b, sizeof(b),
@@ -1823,7 +1832,7 @@ std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
 
 bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ldq, const float* xs, int64_t xs_sm,
                                int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, hipStream_t stream) {
-  if (M > 1 && M <= SM_MAXM) {
+  if (M > 1 || !m1_preferred(m1_shape(w, true, M))) {
     const SmallShape sh = small_shape(w);
     Args a{};
     a.w = w;

@@ -527,8 +527,8 @@ def _bf16_bits(y):
 RNE_W8A16 = [
     # (name, member rows, K, M): each W8A16 kernel
     ("one_token", (300, 130), 1024, 1),
-    ("two_to_four_tokens", (300, 130), 1024, 3),
-    ("few_token_mfma", (300, 130), 1024, 6),
+    ("few_token_mfma_one_pass", (300, 130), 1024, 3),
+    ("few_token_mfma_two_passes", (300, 130), 1024, 6),
     ("general_mfma", (300, 130), 1024, 40),
     ("lds_staged_gemm", (4100, 700), 1024, 448),
     ("lds_staged_gemm_element_stores", (4101, 700), 1024, 400),
@@ -602,6 +602,7 @@ RNE_W8A8 = [
     # (name, member rows, K, M, code pitch pad, output pitch pad)
     ("streaming_one_token", (300, 130), 1024, 1, 0, 0),
     ("streaming_three_tokens", (300, 130), 1024, 3, 0, 0),
+    ("streaming_eight_tokens", (300, 130), 1024, 8, 0, 0),
     ("fast_whole_tiles", (300, 130), 1024, 300, 0, 0),
     ("fast_split_k", (512,), 8192, 64, 0, 0),
     ("register_staged", (300, 130), 1024, 300, 8, 0),
