@@ -13,8 +13,8 @@
 //    F32 in registers (w8a16_m1_kernel; w8a16_m1_ring_kernel beyond five chunks
 //    per wave);
 //  * 2 to 8 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
-//  * (the W8A8 arm's E4M3 activations at one to eight tokens take the same two
-//    kernels: codes decoded exactly, each chunk partial scaled by activation
+//  * (the W8A8 arm's E4M3 activations at one to sixteen tokens take the same
+//    two kernels: codes decoded exactly, each chunk partial scaled by activation
 //    scale x weight scale);
 //  * many tokens, once 256-row x 64-token tiles fill half the compute units:
 //    the LDS-staged GEMM (w8a16_gemm_kernel);
@@ -117,7 +117,7 @@ struct Args {
   int32_t x_bf16;
   int32_t y_bf16;
   int32_t rows_per_block;   // few-token VALU kernels: rows of a block (at most 8 G)
-  // E4M3-activation instances (the W8A8 arm at one to eight tokens): the
+  // E4M3-activation instances (the W8A8 arm at one to sixteen tokens): the
   // per-token group scales, element (m, kb) at xs[m * xs_sm + kb * xs_sk]
   const float* xs;
   int64_t xs_sm;
@@ -531,16 +531,17 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //  the permutation of r & 7 that puts even rows on {0, 1, 4, 5} and odd rows on
 //  {2, 3, 6, 7}, so a fragment read's 16 lanes over two lane groups hit all 64
 //  banks once (with s(r) = (r >> 1) & 7 they collide in pairs);
-//  activation scratch: term u, token t at u * SM_TERM_BYTES + t * 256, piece p at
+//  activation scratch (one row per token plus a zero row, 256 bytes each, per
+//  term): term u, token t at u * (rows * 256) + t * 256, piece p at
 //  p ^ ((u M + t) & 15) (the column index of that term and token in its pass).
 // Per-chunk scaling and the wave-order reduction are those of the general
 // kernel.
 // ---------------------------------------------------------------------------
 constexpr int SM_MAXM = 8;
+// E4M3 codes take one column per token, so one 16-column pass holds 16
+constexpr int SM_MAXM_Q8 = 16;
 __device__ __forceinline__ int sm_swz(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
-constexpr int SM_ZERO_ROW = SM_MAXM;           // scratch row that stays zero
 constexpr int SM_ROW_BYTES = CHUNK * 2;        // one token's chunk as BF16
-constexpr int SM_TERM_BYTES = (SM_MAXM + 1) * SM_ROW_BYTES;
 constexpr int SM_RING = 1;                    // chunks in flight per wave (the kernel takes any depth)
 constexpr int SM_SCALE_REGS = 2;               // chunk scales per wave: up to 128 (K up to 131072 with 8 waves)
 constexpr int SM_WBUF = ROWS * CHUNK;          // a wave's weight bytes per chunk: 4 KiB
@@ -553,8 +554,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   static_assert(!XQ8 || NP == 1, "E4M3 tokens take one pass: column = token");
   constexpr int LPT = XQ8 ? 8 : XBF16 ? 16 : 32;  // lanes per token in a compact load
   constexpr int EPL = XQ8 ? 16 : XBF16 ? 8 : 4;   // activations per lane in a compact load
+  constexpr int MAXM = XQ8 ? SM_MAXM_Q8 : SM_MAXM;  // tokens per launch
+  constexpr int ZERO_ROW = MAXM;                     // scratch row that stays zero
+  constexpr int TERM_BYTES = (MAXM + 1) * SM_ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t wbuf[WAVES][SM_WBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t scratch[WAVES][NT * SM_TERM_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t scratch[WAVES][NT * TERM_BYTES];
   static_assert(sizeof(float) * WAVES * RT * NP * 64 * 4 <= sizeof(uint8_t) * WAVES * SM_WBUF, "reduction fits the buffers");
 
   const int tile = blockIdx.x;
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   const int64_t soff1 = int64_t(min(srow + 1, ((mem.rows + 127) >> 7) - 1)) * a.w.s_rs;
 
   uint8_t* sc = scratch[wave];
-  for (int i = lane; i < NT * SM_TERM_BYTES / 16; i += 64) reinterpret_cast<uint4*>(sc)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = lane; i < NT * TERM_BYTES / 16; i += 64) reinterpret_cast<uint4*>(sc)[i] = make_uint4(0, 0, 0, 0);
 
   const int xt = lane / LPT;                     // token within a compact load
   const int xk = (lane % LPT) * EPL;             // first K element of the lane in the chunk
@@ -599,7 +603,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
     const int u = g / M;
     const int tk = g - u * M;
     const bool ok = u < NT;
-    boff[p] = ok ? u * SM_TERM_BYTES + tk * SM_ROW_BYTES : SM_ZERO_ROW * SM_ROW_BYTES;
+    boff[p] = ok ? u * TERM_BYTES + tk * SM_ROW_BYTES : ZERO_ROW * SM_ROW_BYTES;
     bkey[p] = ok ? g & 15 : 15;
   }
   // weight loads: lane L takes piece L & 7 of row (L >> 3) + 8 q of the wave's 32
@@ -696,7 +700,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
       for (int i = 0; i < NXI; ++i) {
         const int t = i * (64 / LPT) + xt;
         // slot of this lane's 16-byte K piece in term u's row: piece ^ ((u M + t) & 15)
-        auto at = [&](int u) { return sc + u * SM_TERM_BYTES + t * SM_ROW_BYTES +
+        auto at = [&](int u) { return sc + u * TERM_BYTES + t * SM_ROW_BYTES +
                                       ((xk >> 3) ^ ((u * M + t) & 15)) * 16 + (xk & 7) * 2; };
         if (XQ8) {
           // 16 codes, decoded exactly to BF16: pieces xk / 8 and xk / 8 + 1 of the token's row
@@ -1791,17 +1795,17 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   return device_status(hipGetLastError(), "w8a16 launch");
 }
 
-// The W8A8 arm at one to eight tokens: the same weight streams with E4M3
+// The W8A8 arm at one to sixteen tokens: the same weight streams with E4M3
 // activations (the one-token kernels, and from two tokens the few-token
 // kernel).  A decoded code times a decoded weight is exact in F32 (and the
 // BF16 matrix cores add such products exactly into F32), so a chunk partial is
 // the method's block partial summed in another order, and it is scaled by
 // activation scale x weight scale as the F32 epilogue states.  At these token
-// counts a matrix-core GEMM tile would read the weight for 1 to 8 useful
+// counts a matrix-core GEMM tile would read the weight for 1 to 16 useful
 // columns out of 128 or 256.
 bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
   // (the streaming kernels hold a wave's chunk scales in two registers per lane: K up to 131072)
-  if (!aligned || M < 1 || M > SM_MAXM || w.Kb > MAX_KB || M * ldq >= (int64_t(1) << 31)) return false;
+  if (!aligned || M < 1 || M > SM_MAXM_Q8 || w.Kb > MAX_KB || M * ldq >= (int64_t(1) << 31)) return false;
   for (int i = 0; i < w.n_members; ++i)
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) return false;
   return M > 1 || m1_shape(w, true, M).g != 0;
@@ -1816,7 +1820,7 @@ std::string describe_w8a8_stream(const WeightDev& w, int64_t M) {
              "mfma_f32_16x16x32_bf16 (column = token), f32 chunk partials x (act scale x weight scale) | "
              "kernel=w8a16_small_m<e4m3> rows=%d tokens<=%d waves=%d (in-block split-K, weights 8 lanes per "
              "128-byte row through a wave-private LDS transpose, %d chunk in flight per wave) | M=%lld blocks=%d",
-             sh.rb, SM_MAXM, WAVES, SM_RING, (long long)M, sh.tiles);
+             sh.rb, SM_MAXM_Q8, WAVES, SM_RING, (long long)M, sh.tiles);
     return b;
   }
   const M1Shape m1 = m1_shape(w, true, M);
@@ -1850,7 +1854,9 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
     a.xs_sm = xs_sm;
     a.xs_sk = xs_sk;
     const bool sb = w.scale_bf16 != 0;
-    auto k = sb ? w8a16_small_m_kernel<XK_E4M3, true, 1, 1, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, 1, 1, SM_RING>;
+    // 8 tokens of codes per compact load: one load per lane up to 8 tokens, two up to 16
+    auto k = M <= 8 ? (sb ? w8a16_small_m_kernel<XK_E4M3, true, 1, 1, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, 1, 1, SM_RING>)
+                    : (sb ? w8a16_small_m_kernel<XK_E4M3, true, 2, 1, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, 2, 1, SM_RING>);
     hipLaunchKernelGGL(k, dim3(sh.tiles), dim3(THREADS), 0, stream, a);
     return device_status(hipGetLastError(), "w8a8 few-token launch");
   }
