@@ -13,7 +13,7 @@
 //    F32 in registers (w8a16_m1_kernel; w8a16_m1_ring_kernel beyond five chunks
 //    per wave);
 //  * 2 to 8 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
-//  * (the W8A8 arm's E4M3 activations at one to sixteen tokens take the same
+//  * (the W8A8 arm's E4M3 activations at one to 32 tokens take the same
 //    two kernels: codes decoded exactly, each chunk partial scaled by activation
 //    scale x weight scale);
 //  * many tokens, once 256-row x 64-token tiles fill half the compute units:
@@ -117,7 +117,7 @@ struct Args {
   int32_t x_bf16;
   int32_t y_bf16;
   int32_t rows_per_block;   // few-token VALU kernels: rows of a block (at most 8 G)
-  // E4M3-activation instances (the W8A8 arm at one to sixteen tokens): the
+  // E4M3-activation instances (the W8A8 arm at one to 32 tokens): the
   // per-token group scales, element (m, kb) at xs[m * xs_sm + kb * xs_sk]
   const float* xs;
   int64_t xs_sm;
@@ -538,8 +538,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 // kernel.
 // ---------------------------------------------------------------------------
 constexpr int SM_MAXM = 8;
-// E4M3 codes take one column per token, so one 16-column pass holds 16
-constexpr int SM_MAXM_Q8 = 16;
+// E4M3 codes take one column per token, so two 16-column passes hold 32
+constexpr int SM_MAXM_Q8 = 32;
 __device__ __forceinline__ int sm_swz(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
 constexpr int SM_ROW_BYTES = CHUNK * 2;        // one token's chunk as BF16
 constexpr int SM_RING = 1;                    // chunks in flight per wave (the kernel takes any depth)
@@ -551,10 +551,9 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
   constexpr int NT = XK == XK_F32 ? TERMS : 1;   // a BF16 activation, or a decoded E4M3 code, is its own single term
   static_assert(NP == 1 || NP == 2, "one or two 16-column MFMA passes");
-  static_assert(!XQ8 || NP == 1, "E4M3 tokens take one pass: column = token");
   constexpr int LPT = XQ8 ? 8 : XBF16 ? 16 : 32;  // lanes per token in a compact load
   constexpr int EPL = XQ8 ? 16 : XBF16 ? 8 : 4;   // activations per lane in a compact load
-  constexpr int MAXM = XQ8 ? SM_MAXM_Q8 : SM_MAXM;  // tokens per launch
+  constexpr int MAXM = XQ8 ? 16 * NP : SM_MAXM;     // tokens per launch (E4M3: column = token)
   constexpr int ZERO_ROW = MAXM;                     // scratch row that stays zero
   constexpr int TERM_BYTES = (MAXM + 1) * SM_ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t wbuf[WAVES][SM_WBUF];
@@ -627,10 +626,11 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   const v4i rw = make_rsrc(mem.w, w_bytes);
   const v4i rx = make_rsrc(a.x, x_bytes);
   const v4i rs = make_rsrc(mem.s, s_bytes);
-  // E4M3 activations: the group scale of this lane's column token (l16) for each chunk, loaded with its slot
+  // E4M3 activations: the group scale of this lane's column token in each
+  // pass (token 16 p + l16) for each chunk, loaded with its slot
   const uint32_t xs_bytes = XQ8 ? uint32_t(((int64_t(M) - 1) * a.xs_sm + int64_t(Kb - 1) * a.xs_sk + 1) * 4) : 0u;
   const v4i rxs = make_rsrc(a.xs, xs_bytes);
-  uint32_t sar[SM_DEPTH];
+  uint32_t sar[SM_DEPTH][NP];
 
   // The weight scales of this wave's chunks, one per lane (chunk c_begin +
   // 64 h + lane), loaded first: as the oldest loads, waiting for them never
@@ -665,9 +665,13 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   auto issue = [&](int c, int d) {
     const bool live = c < c_end;
     if (XQ8) {
-      const bool ok = live && l16 < M;
-      sar[d] = uint32_t(bsf8_raw_buffer_load_b32(
-          rxs, ok ? int((int64_t(l16) * a.xs_sm + int64_t(c) * a.xs_sk) * 4) : int(xs_bytes), 0, 0));
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int tk = 16 * p + l16;
+        const bool ok = live && tk < M;
+        sar[d][p] = uint32_t(bsf8_raw_buffer_load_b32(
+            rxs, ok ? int((int64_t(tk) * a.xs_sm + int64_t(c) * a.xs_sk) * 4) : int(xs_bytes), 0, 0));
+      }
     }
 #pragma unroll
     for (int i = 0; i < NXI; ++i) {
@@ -766,7 +770,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
           v4f s4;
           if (XQ8) {
             // the W8A8 epilogue: block partial x (act scale x weight scale)
-            const float sa = __uint_as_float(sar[d]);
+            const float sa = __uint_as_float(sar[d][p]);
             const float m0 = sa * sw0, m1 = sa * sw1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) s4[e] = (hi_rows >> (4 * t + e)) & 1u ? m1 : m0;
@@ -796,8 +800,10 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
     for (int p = 0; p < NP; ++p) *reinterpret_cast<v4f*>(&red[wave][t * NP + p][lane][0]) = acc[t][p];
   __syncthreads();
   const int rr = tid & 31;             // row of the block
-  const int tok = tid >> 5;            // token (16 slots, M <= 8 used)
   const int t = rr >> 4, i = rr & 15;  // row tile, row within the MFMA tile
+#pragma unroll
+  for (int tb = 0; tb < MAXM; tb += 16) {   // 16 token slots at a time
+  const int tok = tb + (tid >> 5);
   if (tok < M) {
     float part[NT];
 #pragma unroll
@@ -819,6 +825,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
       if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(sum);
       else static_cast<float*>(a.y)[off] = sum;
     }
+  }
   }
 }
 
@@ -1795,13 +1802,13 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   return device_status(hipGetLastError(), "w8a16 launch");
 }
 
-// The W8A8 arm at one to sixteen tokens: the same weight streams with E4M3
+// The W8A8 arm at one to 32 tokens: the same weight streams with E4M3
 // activations (the one-token kernels, and from two tokens the few-token
 // kernel).  A decoded code times a decoded weight is exact in F32 (and the
 // BF16 matrix cores add such products exactly into F32), so a chunk partial is
 // the method's block partial summed in another order, and it is scaled by
 // activation scale x weight scale as the F32 epilogue states.  At these token
-// counts a matrix-core GEMM tile would read the weight for 1 to 16 useful
+// counts a matrix-core GEMM tile would read the weight for 1 to 32 useful
 // columns out of 128 or 256.
 bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldq) {
   // (the streaming kernels hold a wave's chunk scales in two registers per lane: K up to 131072)
@@ -1854,9 +1861,12 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
     a.xs_sm = xs_sm;
     a.xs_sk = xs_sk;
     const bool sb = w.scale_bf16 != 0;
-    // 8 tokens of codes per compact load: one load per lane up to 8 tokens, two up to 16
-    auto k = M <= 8 ? (sb ? w8a16_small_m_kernel<XK_E4M3, true, 1, 1, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, 1, 1, SM_RING>)
-                    : (sb ? w8a16_small_m_kernel<XK_E4M3, true, 2, 1, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, 2, 1, SM_RING>);
+    // 8 tokens of codes per compact load (one load per lane up to 8 tokens, two
+    // up to 16, four up to 32) and 16 tokens per MFMA pass
+#define BSF8_SQ8(NXI, NP) \
+  (sb ? w8a16_small_m_kernel<XK_E4M3, true, NXI, NP, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, NXI, NP, SM_RING>)
+    auto k = M <= 8 ? BSF8_SQ8(1, 1) : M <= 16 ? BSF8_SQ8(2, 1) : BSF8_SQ8(4, 2);
+#undef BSF8_SQ8
     hipLaunchKernelGGL(k, dim3(sh.tiles), dim3(THREADS), 0, stream, a);
     return device_status(hipGetLastError(), "w8a8 few-token launch");
   }
