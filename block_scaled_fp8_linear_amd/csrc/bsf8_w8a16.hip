@@ -12,7 +12,7 @@
 //  * 1 token: F32 FMAs on the vector ALUs against weights decoded exactly to
 //    F32 in registers (w8a16_m1_kernel; w8a16_m1_ring_kernel beyond five chunks
 //    per wave);
-//  * 2 to 8 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
+//  * 2 to 16 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
 //  * (the W8A8 arm's E4M3 activations at one to 32 tokens take the same
 //    two kernels: codes decoded exactly, each chunk partial scaled by activation
 //    scale x weight scale);
@@ -489,7 +489,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 
 
 // ---------------------------------------------------------------------------
-// Few tokens (M <= 8, 16-byte aligned operands): the decode-size kernel.  The
+// Few tokens (M <= 16, 16-byte aligned operands; E4M3 codes up to 32): the
+// decode-size kernel.  The
 // general kernel's loads put each lane on one weight row (16 rows x 64 bytes
 // per instruction) and its activation loads fill 16 token lanes even when
 // most are past M; at decode sizes those load patterns, not the arithmetic,
@@ -514,10 +515,12 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //  * the chunk scales of the wave's range are loaded once, first;
 //  * the three BF16 terms of F32 activations are not three MFMA passes: they
 //    fill the MFMA's otherwise idle token columns.  Column g holds term g / M of
-//    token g % M, so M <= 5 takes one 16-column pass and M <= 8 two (a third
-//    and a sixth of the general kernel's MFMAs).  Each column keeps its own F32
-//    accumulator over the chunks, and a token's three columns are added once,
-//    when the waves' partial tiles are reduced;
+//    token g % M, so M <= 5 takes one 16-column pass, M <= 8 two and M <= 16
+//    three (a third and a sixth of the general kernel's MFMAs at five and
+//    eight tokens).  Each column keeps its own F32 accumulator over the chunks,
+//    and a token's three columns are added once, when the waves' partial tiles
+//    are reduced (with three passes, in the activation scratch: the weight
+//    buffers hold two);
 //  * E4M3 codes (the W8A8 arm) decode exactly to one BF16 term, column = token,
 //    and the epilogue scales each chunk partial by activation scale x weight
 //    scale, the activation scale of the lane's column token loaded with the
@@ -537,7 +540,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 // Per-chunk scaling and the wave-order reduction are those of the general
 // kernel.
 // ---------------------------------------------------------------------------
-constexpr int SM_MAXM = 8;
+constexpr int SM_MAXM = 16;   // F32 (three columns per token, three passes) and BF16 activations
 // E4M3 codes take one column per token, so two 16-column passes hold 32
 constexpr int SM_MAXM_Q8 = 32;
 __device__ __forceinline__ int sm_swz(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
@@ -550,15 +553,21 @@ template <int XK, bool SBF16, int NXI, int NP, int SM_DEPTH>
 __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
   constexpr bool XBF16 = XK == XK_BF16, XQ8 = XK == XK_E4M3;
   constexpr int NT = XK == XK_F32 ? TERMS : 1;   // a BF16 activation, or a decoded E4M3 code, is its own single term
-  static_assert(NP == 1 || NP == 2, "one or two 16-column MFMA passes");
+  static_assert(NP >= 1 && NP <= 3, "one to three 16-column MFMA passes");
   constexpr int LPT = XQ8 ? 8 : XBF16 ? 16 : 32;  // lanes per token in a compact load
   constexpr int EPL = XQ8 ? 16 : XBF16 ? 8 : 4;   // activations per lane in a compact load
-  constexpr int MAXM = XQ8 ? 16 * NP : SM_MAXM;     // tokens per launch (E4M3: column = token)
+  // tokens per launch: one column per token for E4M3 codes and BF16, three for
+  // F32 (eight tokens in two passes, sixteen in three)
+  constexpr int MAXM = NT == 1 ? 16 * NP : NP == 3 ? 16 : 8;
   constexpr int ZERO_ROW = MAXM;                     // scratch row that stays zero
   constexpr int TERM_BYTES = (MAXM + 1) * SM_ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t wbuf[WAVES][SM_WBUF];
   __shared__ __attribute__((aligned(16))) uint8_t scratch[WAVES][NT * TERM_BYTES];
-  static_assert(sizeof(float) * WAVES * RT * NP * 64 * 4 <= sizeof(uint8_t) * WAVES * SM_WBUF, "reduction fits the buffers");
+  // the waves' partial tiles are reduced in the weight buffers, or in the
+  // activation scratch when they do not fit there (three passes)
+  constexpr bool RED_IN_WBUF = sizeof(float) * WAVES * RT * NP * 64 * 4 <= sizeof(uint8_t) * WAVES * SM_WBUF;
+  static_assert(RED_IN_WBUF || sizeof(float) * WAVES * RT * NP * 64 * 4 <= sizeof(uint8_t) * WAVES * NT * TERM_BYTES,
+                "reduction fits the buffers");
 
   const int tile = blockIdx.x;
   int mi = 0;
@@ -793,7 +802,8 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 
   // ---- add the 8 waves' partial tiles in wave order, then a token's term
   // columns (smallest first), and store
-  float(*red)[RT * NP][64][4] = reinterpret_cast<float(*)[RT * NP][64][4]>(&wbuf[0][0]);
+  float(*red)[RT * NP][64][4] =
+      reinterpret_cast<float(*)[RT * NP][64][4]>(RED_IN_WBUF ? &wbuf[0][0] : &scratch[0][0]);
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -1777,15 +1787,18 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     a.rows_per_block = sh.rb;
     grid = sh.tiles;
     // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load,
-    // and 3 M term columns of F32 tokens in one 16-column MFMA pass up to M = 5
+    // and 3 M term columns of F32 tokens in 16-column MFMA passes (one up to
+    // M = 5, two up to 8 in use from M = 5, three up to 16); a BF16 token is one column
 #define BSF8_SMALL(XK, NXI, NP) \
   (sb ? w8a16_small_m_kernel<XK, true, NXI, NP, SM_RING> : w8a16_small_m_kernel<XK, false, NXI, NP, SM_RING>)
     if (x_bf16) {
-      kern = M <= 4 ? BSF8_SMALL(XK_BF16, 1, 1) : BSF8_SMALL(XK_BF16, 2, 1);
+      kern = M <= 4 ? BSF8_SMALL(XK_BF16, 1, 1) : M <= 8 ? BSF8_SMALL(XK_BF16, 2, 1) : BSF8_SMALL(XK_BF16, 4, 1);
     } else if (M <= 4) {
       kern = M <= 2 ? BSF8_SMALL(XK_F32, 1, 1) : BSF8_SMALL(XK_F32, 2, 1);
-    } else {
+    } else if (M <= 8) {
       kern = BSF8_SMALL(XK_F32, 4, 2);
+    } else {
+      kern = BSF8_SMALL(XK_F32, 8, 3);
     }
 #undef BSF8_SMALL
   } else if (aligned && p.rt == 4) {
