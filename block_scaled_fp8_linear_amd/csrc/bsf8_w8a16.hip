@@ -1885,7 +1885,7 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
   }
   const M1Shape m1 = m1_shape(w, true, M);
   if (m1.g == 0) {
-    set_error("UNSUPPORTED: the streaming W8A8 kernels take one to eight tokens");
+    set_error("UNSUPPORTED: no one-token streaming shape for this weight");
     return BSF8_E_UNSUPPORTED;
   }
   Args a{};
