@@ -363,6 +363,43 @@ def test_output_padding_untouched_and_m_zero():
     assert y.shape == (0, N)
 
 
+def test_every_call_takes_zero_tokens_and_writes_nothing():
+    """M = 0 on every entry point: each call succeeds, returns [0, ...] results, and
+    writes nothing (outputs are zero-row views at the start of canary buffers)."""
+    t = torch()
+    d = device()
+    members, _x = tax_case("member_local_100_28_130")
+    w, _keep = weight_on_device(members)
+    N, K = w.n_total, w.K
+    Kb = -(-K // 128)
+    banner("zero tokens on every call")
+    for xdt in (t.float32, t.bfloat16):
+        x0 = t.zeros((0, K), dtype=xdt, device=d)
+        for odt in (t.float32, t.bfloat16):
+            buf = t.full((2, N), 7.0, dtype=odt, device=d)
+            assert B.linear_w8a16(w, x0, out_dtype=odt, out=buf[:0]).shape == (0, N)
+            assert B.linear_w8a8_dynamic(w, x0, out_dtype=odt, out=buf[:0]).shape == (0, N)
+            qbuf = t.full((2, K), 0x5A, dtype=t.uint8, device=d)
+            sbuf = t.full((2, Kb), 7.0, dtype=t.float32, device=d)
+            xq, xs = B.quant_act(x0, xq=qbuf[:0], xs=sbuf[:0])
+            assert xq.shape == (0, K) and xs.shape == (0, Kb)
+            assert B.linear_w8a8(w, xq, xs, out_dtype=odt, out=buf[:0]).shape == (0, N)
+            assert B.linear_w8a8_noalloc(w, xq, xs, buf[:0]).shape == (0, N)
+            gy = t.zeros((0, 2 * 200), dtype=xdt, device=d)
+            gq, gs = B.quant_glu(gy, xq=qbuf[:0, :200], xs=sbuf[:0, :2])
+            assert gq.shape == (0, 200) and gs.shape == (0, 2)
+            hbuf = t.full((2, 200), 7.0, dtype=t.float32, device=d)
+            assert B.glu_act(gy, out=hbuf[:0]).shape == (0, 200)
+            t.cuda.synchronize()
+            assert bool((buf == 7.0).all()) and bool((qbuf == 0x5A).all()) and bool((sbuf == 7.0).all())
+            assert bool((hbuf == 7.0).all())
+    wd = B.upcast(w)
+    dbuf = t.full((2, N), 7.0, dtype=t.float32, device=d)
+    assert B.linear_dense(wd, t.zeros((0, K), dtype=t.bfloat16, device=d), out=dbuf[:0]).shape == (0, N)
+    t.cuda.synchronize()
+    assert bool((dbuf == 7.0).all())
+
+
 def test_w8a16_repeated_calls_are_bitwise_identical():
     """The per-wave K partials are added in a fixed order, so repeated calls agree bit for bit."""
     t = torch()
