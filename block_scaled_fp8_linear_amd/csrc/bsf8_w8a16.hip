@@ -510,6 +510,12 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 //    loads retire in issue order, so each slot's loads are issued together and
 //    slots in chunk order (scheduling barriers keep them grouped), and chunks
 //    past the wave's range get past-the-end offsets (zeros, no traffic).
+//    A slot is refilled as soon as its registers are written to LDS, before
+//    the chunk's fragment reads, MFMAs and epilogue, which then overlap the
+//    next chunk's load (refilled after them, W [5120, 5120] took 8.7 / 11.0 us
+//    at two / eight F32 tokens and 8.4 / 8.6 us at two / eight E4M3 tokens,
+//    now 7.7 / 10.3 and 7.7 / 7.9; the FFN down projection 21.5 / 27.7 and
+//    21.2 / 21.4 us, now 18.2 / 25.6 and 18.6 / 18.9).
 //    (Copies straight into LDS would save the registers, but the compiler then
 //    waits for every copy in flight before any other LDS access of the wave.)
 //  * the chunk scales of the wave's range are loaded once, first;
@@ -745,6 +751,20 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
               make_uint2((l[0] >> 16) | (l[1] & 0xFFFF0000u), (l[2] >> 16) | (l[3] & 0xFFFF0000u));
         }
       }
+      // weights: to LDS in rows (read back in the MFMA layout below)
+#pragma unroll
+      for (int q = 0; q < 2 * RT; ++q) {
+        const int rr = 8 * q + crow;
+        *reinterpret_cast<uint4*>(wb + rr * CHUNK + ((cpiece ^ sm_swz(rr)) * 16)) = wr[d][q];
+      }
+      uint32_t sa_now[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) sa_now[p] = XQ8 ? sar[d][p] : 0u;
+      // the slot's registers are free: refill it now, so this chunk's
+      // fragment reads, MFMAs and epilogue overlap the next chunk's load
+      __builtin_amdgcn_sched_barrier(0);
+      issue(c + SM_DEPTH, d);
+      __builtin_amdgcn_sched_barrier(0);
       // B fragments: K-step st holds K = 32 gq + 8 st + j
       v8bf b[NP][STEPS];
 #pragma unroll
@@ -753,12 +773,6 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
 #pragma unroll
         for (int p = 0; p < NP; ++p)
           b[p][st] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(sc + boff[p] + ((kc ^ bkey[p]) * 16)));
-      }
-      // weights: to LDS in rows, back in the MFMA layout
-#pragma unroll
-      for (int q = 0; q < 2 * RT; ++q) {
-        const int rr = 8 * q + crow;
-        *reinterpret_cast<uint4*>(wb + rr * CHUNK + ((cpiece ^ sm_swz(rr)) * 16)) = wr[d][q];
       }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
@@ -779,7 +793,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
           v4f s4;
           if (XQ8) {
             // the W8A8 epilogue: block partial x (act scale x weight scale)
-            const float sa = __uint_as_float(sar[d][p]);
+            const float sa = __uint_as_float(sa_now[p]);
             const float m0 = sa * sw0, m1 = sa * sw1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) s4[e] = (hi_rows >> (4 * t + e)) & 1u ? m1 : m0;
@@ -790,9 +804,6 @@ __global__ __launch_bounds__(THREADS) void w8a16_small_m_kernel(Args a) {
           acc[t][p] += pt[p] * s4;
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      issue(c + SM_DEPTH, d);   // refill this slot
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // the ring's last refills (chunks past the range) are still in flight, and
@@ -1788,13 +1799,14 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     grid = sh.tiles;
     // compact activation loads: 2 F32 (4 BF16) tokens per 16-byte-per-lane load,
     // and 3 M term columns of F32 tokens in 16-column MFMA passes (one up to
-    // M = 5, two up to 8 in use from M = 5, three up to 16); a BF16 token is one column
+    // M = 5, two up to 8, three up to 16: W [5120, 5120] at five tokens 10.9 ->
+    // 9.9 us with one pass instead of two); a BF16 token is one column
 #define BSF8_SMALL(XK, NXI, NP) \
   (sb ? w8a16_small_m_kernel<XK, true, NXI, NP, SM_RING> : w8a16_small_m_kernel<XK, false, NXI, NP, SM_RING>)
     if (x_bf16) {
       kern = M <= 4 ? BSF8_SMALL(XK_BF16, 1, 1) : M <= 8 ? BSF8_SMALL(XK_BF16, 2, 1) : BSF8_SMALL(XK_BF16, 4, 1);
-    } else if (M <= 4) {
-      kern = M <= 2 ? BSF8_SMALL(XK_F32, 1, 1) : BSF8_SMALL(XK_F32, 2, 1);
+    } else if (M <= 5) {
+      kern = M <= 2 ? BSF8_SMALL(XK_F32, 1, 1) : M <= 4 ? BSF8_SMALL(XK_F32, 2, 1) : BSF8_SMALL(XK_F32, 3, 1);
     } else if (M <= 8) {
       kern = BSF8_SMALL(XK_F32, 4, 2);
     } else {
