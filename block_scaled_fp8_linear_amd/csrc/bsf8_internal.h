@@ -67,7 +67,7 @@ bsf8_status launch_w8a8(const WeightDev& w, bool aligned, const uint8_t* xq, int
                         int64_t xs_sm, int64_t xs_sk, int64_t M, void* y, bool y_bf16, int64_t ldy, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 std::string describe_w8a8(const WeightDev& w, bool aligned, int64_t M);
-// The W8A8 arm at one to 32 tokens runs the W8A16 file's streaming kernels
+// The W8A8 arm at one to 48 tokens runs the W8A16 file's streaming kernels
 // with E4M3 activations (no workspace).
 bool w8a8_stream_applies(const WeightDev& w, bool aligned, int64_t M, int64_t ldq);
 std::string describe_w8a8_stream(const WeightDev& w, int64_t M);

@@ -13,7 +13,7 @@
 //    F32 in registers (w8a16_m1_kernel; w8a16_m1_ring_kernel beyond five chunks
 //    per wave);
 //  * 2 to 16 tokens: the few-token MFMA kernel (w8a16_small_m_kernel);
-//  * (the W8A8 arm's E4M3 activations at one to 32 tokens take the same
+//  * (the W8A8 arm's E4M3 activations at one to 48 tokens take the same
 //    two kernels: codes decoded exactly, each chunk partial scaled by activation
 //    scale x weight scale);
 //  * many tokens, once 256-row x 64-token tiles fill half the compute units:
@@ -117,7 +117,7 @@ struct Args {
   int32_t x_bf16;
   int32_t y_bf16;
   int32_t rows_per_block;   // few-token VALU kernels: rows of a block (at most 8 G)
-  // E4M3-activation instances (the W8A8 arm at one to 32 tokens): the
+  // E4M3-activation instances (the W8A8 arm at one to 48 tokens): the
   // per-token group scales, element (m, kb) at xs[m * xs_sm + kb * xs_sk]
   const float* xs;
   int64_t xs_sm;
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 
 
 // ---------------------------------------------------------------------------
-// Few tokens (M <= 16, 16-byte aligned operands; E4M3 codes up to 32): the
+// Few tokens (M <= 16, 16-byte aligned operands; E4M3 codes up to 48): the
 // decode-size kernel.  The
 // general kernel's loads put each lane on one weight row (16 rows x 64 bytes
 // per instruction) and its activation loads fill 16 token lanes even when
@@ -547,8 +547,10 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 // kernel.
 // ---------------------------------------------------------------------------
 constexpr int SM_MAXM = 16;   // F32 (three columns per token, three passes) and BF16 activations
-// E4M3 codes take one column per token, so two 16-column passes hold 32
-constexpr int SM_MAXM_Q8 = 32;
+// E4M3 codes take one column per token, so three 16-column passes hold 48
+// (W [5120, 5120] at 33-48 tokens 17.2-17.4 -> 13.0-13.7 us against the
+// GEMM, grouped Q/K/V 20.9-21.5 -> 14.7-16.1 us)
+constexpr int SM_MAXM_Q8 = 48;
 __device__ __forceinline__ int sm_swz(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
 constexpr int SM_ROW_BYTES = CHUNK * 2;        // one token's chunk as BF16
 constexpr int SM_RING = 1;                    // chunks in flight per wave (the kernel takes any depth)
@@ -1827,7 +1829,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   return device_status(hipGetLastError(), "w8a16 launch");
 }
 
-// The W8A8 arm at one to 32 tokens: the same weight streams with E4M3
+// The W8A8 arm at one to 48 tokens: the same weight streams with E4M3
 // activations (the one-token kernels, and from two tokens the few-token
 // kernel).  A decoded code times a decoded weight is exact in F32 (and the
 // BF16 matrix cores add such products exactly into F32), so a chunk partial is
@@ -1887,10 +1889,10 @@ bsf8_status launch_w8a8_stream(const WeightDev& w, const uint8_t* xq, int64_t ld
     a.xs_sk = xs_sk;
     const bool sb = w.scale_bf16 != 0;
     // 8 tokens of codes per compact load (one load per lane up to 8 tokens, two
-    // up to 16, four up to 32) and 16 tokens per MFMA pass
+    // up to 16, four up to 32, six up to 48) and 16 tokens per MFMA pass
 #define BSF8_SQ8(NXI, NP) \
   (sb ? w8a16_small_m_kernel<XK_E4M3, true, NXI, NP, SM_RING> : w8a16_small_m_kernel<XK_E4M3, false, NXI, NP, SM_RING>)
-    auto k = M <= 8 ? BSF8_SQ8(1, 1) : M <= 16 ? BSF8_SQ8(2, 1) : BSF8_SQ8(4, 2);
+    auto k = M <= 8 ? BSF8_SQ8(1, 1) : M <= 16 ? BSF8_SQ8(2, 1) : M <= 32 ? BSF8_SQ8(4, 2) : BSF8_SQ8(6, 3);
 #undef BSF8_SQ8
     hipLaunchKernelGGL(k, dim3(sh.tiles), dim3(THREADS), 0, stream, a);
     return device_status(hipGetLastError(), "w8a8 few-token launch");

@@ -113,14 +113,14 @@ def test_workspace_sizes():
             assert b.value == (sk * M * rows * tile * 4 if sk > 1 else 0), (M, d)
         # 20 row tiles x 4 token tiles < 256 units: every tile is split
         assert "split_k=3 split_row_tiles=20" in L.bsf8_describe(h, 1, 1024).decode()
-        # one to 32 tokens stream the weight with E4M3 activations and use no
+        # one to 48 tokens stream the weight with E4M3 activations and use no
         # workspace; the size reported stays an upper bound over the paths
         assert "w8a16_m1<e4m3>" in L.bsf8_describe(h, 1, 1).decode()
-        for M in (2, 4, 8, 16, 17, 32):
+        for M in (2, 4, 8, 16, 17, 32, 33, 48):
             d = L.bsf8_describe(h, 1, M).decode()
             assert "kernel=w8a16_small_m<e4m3>" in d and "e4m3 codes decoded exactly to bf16" in d, d
             assert L.bsf8_workspace_size(h, 1, M, ctypes.byref(b)) == 0
-        assert "w8a8_gemm" in L.bsf8_describe(h, 1, 33).decode()
+        assert "w8a8_gemm" in L.bsf8_describe(h, 1, 49).decode()
         assert L.bsf8_workspace_size(h, 7, 8, ctypes.byref(b)) == 1
     finally:
         L.bsf8_weight_destroy(h)
@@ -147,8 +147,8 @@ def test_dynamic_w8a8_workspace_describe_and_refusals():
         assert "arm=w8a8-dynamic" in d1 and "kernel=w8a16_m1<quantizing>" in d1, d1
         d3 = L.bsf8_describe(h, B.ARM_W8A8_DYNAMIC, 3).decode()
         assert d3.startswith("quant_act into the workspace") and "kernel=w8a16_small_m<e4m3>" in d3, d3
-        d33 = L.bsf8_describe(h, B.ARM_W8A8_DYNAMIC, 33).decode()
-        assert d33.startswith("quant_act into the workspace") and "w8a8_gemm" in d33, d33
+        d49 = L.bsf8_describe(h, B.ARM_W8A8_DYNAMIC, 49).decode()
+        assert d49.startswith("quant_act into the workspace") and "w8a8_gemm" in d49, d49
         fake = ctypes.c_void_p(1 << 40)
         ws_fake = ctypes.c_void_p(1 << 41)
         call = lambda x, dt, M, ldx, ws=None, wsb=0: B.status_name(

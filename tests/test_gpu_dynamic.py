@@ -55,6 +55,7 @@ CASES = [
     ("long_k17408_ring", 2, "f32", "two-step"),
     ("long_k40960_ring", 1, "f32", "fused"),
     ("decode_5120", 1, "f32", "fused"), ("decode_5120", 4, "f32", "two-step"), ("decode_5120", 8, "bf16", "two-step"),
+    ("decode_5120", 40, "f32", "two-step"),
 ]
 
 

@@ -35,7 +35,7 @@ def _weight(K):
 
 
 def _x(K, M):
-    return synth.gaussian_activations(SEED, f"maxk_X{K}", 40, K)[:M]
+    return synth.gaussian_activations(SEED, f"maxk_X{K}", 56, K)[:M]
 
 
 @pytest.mark.parametrize("M,xdt,kernel", [(1, "f32", "w8a16_m1_ring"), (3, "f32", "w8a16_small_m"),
@@ -60,7 +60,7 @@ def test_w8a16_at_the_largest_k(M, xdt, kernel):
         assert_within(y, ref, bound, odt == t.bfloat16, f"w8a16 K={K_MAX} M={M} {xdt}")
 
 
-@pytest.mark.parametrize("M,kernel", [(1, "w8a16_m1_ring<e4m3>"), (32, "w8a16_small_m<e4m3>"), (40, "w8a8_gemm_fast")])
+@pytest.mark.parametrize("M,kernel", [(1, "w8a16_m1_ring<e4m3>"), (48, "w8a16_small_m<e4m3>"), (56, "w8a8_gemm_fast")])
 def test_w8a8_at_the_largest_k(M, kernel):
     t = torch()
     members, w = _weight(K_MAX)
