@@ -547,6 +547,18 @@ __global__ __launch_bounds__(THREADS) void w8a16_kernel(Args a) {
 // kernel.
 // ---------------------------------------------------------------------------
 constexpr int SM_MAXM = 16;   // F32 (three columns per token, three passes) and BF16 activations
+// 17 to 32 aligned F32 or BF16 tokens: two launches, the first 16 tokens on the
+// few-token kernel and the rest on whichever kernel their count takes, each
+// streaming the whole weight.  Against the general kernel in one launch:
+// grouped Q/K/V at 17 / 24 / 32 tokens 35.0 / 35.3 / 36.4 -> 25.7 / 28.4 /
+// 32.8 us, W [5120, 5120] 22.3 / 28.4 / 33.3 -> 22.1 / 24.7 / 28.8 us, the FFN
+// down projection 57.4 / 75.5 / 97.7 -> 54.5 / 62.5 / 73.9 us.  (One launch
+// with both token groups on the grid's second dimension reached 28.5 / 29.7 /
+// 31.0, 26.1 / 26.6 / 27.4 and 66.0 / 67.6 / 71.1 us: the second group finds
+// little of the weight still cached, and a 1-token group costs a full one.)
+// At 48 tokens the general kernel is as fast (W [5120, 5120] 34.0 against
+// 42.8 us in three launches).
+constexpr int SM_SPLIT_MAXM = 32;
 // E4M3 codes take one column per token, so three 16-column passes hold 48
 // (W [5120, 5120] at 33-48 tokens 17.2-17.4 -> 13.0-13.7 us against the
 // GEMM, grouped Q/K/V 20.9-21.5 -> 14.7-16.1 us)
@@ -1695,6 +1707,10 @@ bsf8_status launch_gemm(const WeightDev& w, const void* x, bool x_bf16, int64_t 
 size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
 
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
+  if (!gemm_applies(w, aligned, M) && aligned && M > SM_MAXM && M <= SM_SPLIT_MAXM)
+    return "two launches, tokens [0, " + std::to_string(SM_MAXM) + ") then [" + std::to_string(SM_MAXM) + ", " +
+           std::to_string(M) + "): " + describe_w8a16(w, aligned, SM_MAXM) + " ;; " +
+           describe_w8a16(w, aligned, M - SM_MAXM);
   if (gemm_applies(w, aligned, M)) {
     char b[448];
     const int rt = gemm_row_tiles(w, nullptr);
@@ -1747,6 +1763,14 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
   const Plan p = make_plan(w, M, aligned);
   if (p.tiles == 0) return BSF8_OK;
   if (gemm_applies(w, aligned, M)) return launch_gemm(w, x, x_bf16, M, ldx, y, y_bf16, ldy, stream);
+  if (aligned && M > SM_MAXM && M <= SM_SPLIT_MAXM) {
+    // rows SM_MAXM on of x start 16-byte aligned too (ldx * element size is a multiple of 16)
+    const bsf8_status st = launch_w8a16(w, true, x, x_bf16, SM_MAXM, ldx, y, y_bf16, ldy, nullptr, 0, stream);
+    if (st != BSF8_OK) return st;
+    return launch_w8a16(w, true, static_cast<const uint8_t*>(x) + SM_MAXM * ldx * (x_bf16 ? 2 : 4), x_bf16,
+                        M - SM_MAXM, ldx, static_cast<uint8_t*>(y) + SM_MAXM * ldy * (y_bf16 ? 2 : 4), y_bf16, ldy,
+                        nullptr, 0, stream);
+  }
   const M1Shape m1 = m1_shape(w, aligned, M);
   if (m1_preferred(m1)) {
     Args a{};

@@ -290,7 +290,8 @@ bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, si
  * Kernels (aligned operands): one token runs F32 FMAs on the vector ALUs
  * against weights decoded exactly to F32 (any K); more tokens run the BF16
  * matrix cores on an exact three-term split of each F32 activation (a
- * weight-streaming kernel up to sixteen tokens, an LDS-staged GEMM for hundreds).
+ * weight-streaming kernel up to sixteen tokens, and for 17 to 32 two of its
+ * launches, 16 tokens then the rest; an LDS-staged GEMM for hundreds).
  *
  * x : [M, K] F32 or BF16, leading dimension ldx (elements), 16-byte aligned
  *     rows when K allows.

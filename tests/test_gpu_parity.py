@@ -272,16 +272,17 @@ def test_w8a16_bf16_activations_and_f32_scales():
 @pytest.mark.parametrize("K", [384, 3072, 4000, 4224])
 def test_w8a16_few_tokens_sweep(K):
     """M = 1..8 and 9, 12, 16 with F32 and BF16 activations (F32 in one, two and
-    three 16-column passes), on K that give the few-token kernel 1, 3, 4 and 5
-    chunks per wave (4000: a partial last chunk; 4224: 33 chunks, so the last wave
-    has none), 200 rows (a ragged last row tile)."""
+    three 16-column passes), and 17, 20, 31, 32 (two launches: 16 tokens, then
+    the rest on the kernel their count takes), on K that give the
+    few-token kernel 1, 3, 4 and 5 chunks per wave (4000: a partial last chunk;
+    4224: 33 chunks, so the last wave has none), 200 rows (a ragged last row tile)."""
     t = torch()
     cfg = 131
     m = synth.random_code_weight(cfg, f"sweep_W{K}", 200, K, scale_log2=(-9, -3))
     w, _keep = weight_on_device([m])
     om = oracle_members([m])
-    x_all = synth.gaussian_activations(cfg, f"sweep_X{K}", 16, K)
-    for M in list(range(1, 9)) + [9, 12, 16]:
+    x_all = synth.gaussian_activations(cfg, f"sweep_X{K}", 32, K)
+    for M in list(range(1, 9)) + [9, 12, 16, 17, 20, 31, 32]:
         x = x_all[:M]
         banner(f"w8a16 sweep K={K} M={M} f32 {w.describe(B.ARM_W8A16, M)}")
         y = B.linear_w8a16(w, t.from_numpy(x).to(device()))
@@ -568,6 +569,7 @@ RNE_W8A16 = [
     ("few_token_mfma_one_pass", (300, 130), 1024, 3),
     ("few_token_mfma_two_passes", (300, 130), 1024, 6),
     ("few_token_mfma_three_passes", (300, 130), 1024, 13),
+    ("few_token_two_launches", (300, 130), 1024, 27),
     ("general_mfma", (300, 130), 1024, 40),
     ("lds_staged_gemm", (4100, 700), 1024, 448),
     ("lds_staged_gemm_element_stores", (4101, 700), 1024, 400),
