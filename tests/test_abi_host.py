@@ -87,6 +87,14 @@ def test_handle_geometry_and_member_local_rows():
         assert L.bsf8_weight_scale_row(h, 8144, ctypes.byref(mi), ctypes.byref(lr), ctypes.byref(sr)) == 1
         d = L.bsf8_describe(h, 0, 1).decode()
         assert "w8a16" in d and "K=5120" in d and "members=3" in d
+        # W8A16 plans by token count: the few-token kernel to 16, two of its
+        # launches (16, then the rest) to 32, the general kernel beyond
+        assert "kernel=w8a16_small_m " in L.bsf8_describe(h, 0, 16).decode()
+        d = L.bsf8_describe(h, 0, 24).decode()
+        assert d.startswith("two launches, tokens [0, 16) then [16, 24): ") and d.count("kernel=w8a16_small_m ") == 2, d
+        # (one token on this grouped weight also takes the few-token kernel: 32-row blocks)
+        assert L.bsf8_describe(h, 0, 17).decode().startswith("two launches, tokens [0, 16) then [16, 17): ")
+        assert "kernel=w8a16 rows=" in L.bsf8_describe(h, 0, 33).decode()
         d = L.bsf8_describe(h, 1, 512).decode()
         assert "w8a8" in d and "e4m3" in d
     finally:
