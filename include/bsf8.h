@@ -312,6 +312,11 @@ bsf8_status bsf8_linear_w8a16(const bsf8_weight* w, const void* x, int32_t x_dty
  * ("Module w8a8_prefill", section "WHY (#917 / #928)"; "FP8 Native Serving",
  *  section "Native FP8 vs dequant-to-BF16": FP8 operands through the matrix
  *  unit, BF16 only when results are written back.)
+ * Kernels (aligned operands): up to 48 tokens the weight streams through the
+ * W8A16 arm's one-token and few-token kernels with the codes decoded exactly
+ * (the same exact products, each slice partial scaled as above); from 49
+ * tokens the FP8 matrix-core GEMM (256x256 or 128x128 tiles, split-K when the
+ * tile grid leaves compute units idle, the partials added in split order).
  *
  * xq, xs: exactly what bsf8_quant_act writes (ldq bytes; xs in either
  *         activation scale layout, strides xs_sm, xs_sk).
