@@ -1,5 +1,5 @@
 // Plain read of a device buffer, for measurement only: the achievable HBM read
-// rate on the same bytes as a GEMV, against which the GEMV's rate is judged.
+// rate on the same bytes as a GEMV, the rate the GEMV's own is compared with.
 // Each lane reads four 16-byte words per pass, grid-strided so that every wave
 // instruction covers 1 KiB of consecutive bytes.  Each block stores the XOR of
 // what it read into its own sink word (a plain store: one shared word updated

@@ -474,7 +474,7 @@ bsf8_status bsf8_inspect_safetensors(const char* path, const bsf8_decl* decl, bs
 /*
  * bsf8_read_stream -- measurement aid, not part of the projection: reads
  * `bytes` bytes at `p` as a plain coalesced stream.  Timed on a GEMV's weight
- * bytes it gives the achievable read rate the GEMV is judged against.
+ * bytes it gives the achievable read rate to compare the GEMV's rate with.
  * p: device pointer, 16-byte aligned; bytes: a multiple of 16, >= 0.
  * sink: device array of BSF8_READ_STREAM_SINK_WORDS 4-byte words the caller
  * owns.  The launch uses min(ceil(bytes / 16 KiB), BSF8_READ_STREAM_SINK_WORDS)

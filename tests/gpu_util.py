@@ -102,8 +102,9 @@ def sample_tokens(M: int, k: int = 48, seed: int = 1) -> np.ndarray:
 # ------------------------------------------------------------ result records
 # Each comparison with the oracle appends one record (test, what was compared,
 # sha256 of the fixture's arrays and of the oracle's output, worst err/bound,
-# the library's sha256) to gpurun_out/parity_records.jsonl, so the fixture
-# hashes are kept next to the GPU results they produced.
+# the library's sha256) to parity_records.jsonl in the repository's output
+# folder for GPU runs, so the fixture hashes are kept next to the GPU results
+# they produced.
 
 _FIXTURE: dict = {}
 RECORDS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
