@@ -1331,6 +1331,14 @@ struct GemmArgs {
   int32_t M;
   int32_t y_bf16;
   int32_t y_vec;                  // 16-byte (F32) / 8-byte (BF16) output stores allowed
+  // split-K: blocks [s * tiles, (s + 1) * tiles) take K chunks [s * kb_per_split,
+  // + kb_per_split) and, with more than one split, write their F32 partial of y
+  // to ws + s * M * ldws (same row and column indexing as y); a second kernel
+  // adds the splits in order
+  int32_t splits;
+  int32_t kb_per_split;
+  float* ws;
+  int64_t ldws;
 };
 
 template <bool XBF16, bool SBF16>
@@ -1344,11 +1352,14 @@ __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
   constexpr int B_PER = GW_TOKS * CHUNK * XE / 16 / GW_THREADS;   // 4 (F32: 16 consecutive values) / 2
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
 
-  const int R = blockIdx.x / a.m_tiles, T = blockIdx.x - R * a.m_tiles;
+  const int tiles = a.rt0[a.w.n_members] * a.m_tiles;
+  const int sp = blockIdx.x / tiles, bt = blockIdx.x - sp * tiles;
+  const int R = bt / a.m_tiles, T = bt - R * a.m_tiles;
   int mi = 0;
   while (mi + 1 < a.w.n_members && R >= a.rt0[mi + 1]) ++mi;
   const MemberDev mem = a.w.m[mi];
   const int K = a.w.K, Kb = a.w.Kb;
+  const int kb_begin = sp * a.kb_per_split, kb_end = min(Kb, kb_begin + a.kb_per_split);
   const int r0 = (R - a.rt0[mi]) * GW_ROWS;   // member-local first row
   const int t0 = T * GW_TOKS;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1438,11 +1449,12 @@ __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // chunk k goes through stage k & 1: loaded into registers two chunks before its
-  // use and stored into its stage one chunk before
-  load(0);
+  // chunk kb goes through stage (kb - kb_begin) & 1: loaded into registers two
+  // chunks before its use and stored into its stage one chunk before; past the
+  // split's range a load reads chunk Kb (zeros, no traffic)
+  load(kb_begin);
   store(lds);
-  load(1);
+  load(kb_begin + 1 < kb_end ? kb_begin + 1 : Kb);
   const int tw = wc * 16 + l16;   // the lane's token within the tile (B fragments)
   // the fragments of K step st: 8 weight fragments decoded to BF16 and the token
   // fragment's BF16 terms (one per plane)
@@ -1482,11 +1494,12 @@ __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][r] = fmaf(pr[i][r], sw, acc[i][r]);
   };
-  for (int kb = 0; kb < Kb; ++kb) {
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const int j = kb - kb_begin;
     __syncthreads();   // chunk kb's stage is complete; chunk kb - 1's reads are done
-    if (kb + 1 < Kb) store(lds + ((kb + 1) & 1) * STAGE);
-    load(kb + 2);   // past the last chunk: zeros, no traffic
-    compute(lds + (kb & 1) * STAGE, kb);
+    if (kb + 1 < kb_end) store(lds + ((j + 1) & 1) * STAGE);
+    load(kb + 2 < kb_end ? kb + 2 : Kb);
+    compute(lds + (j & 1) * STAGE, kb);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -1498,6 +1511,11 @@ __global__ __launch_bounds__(GW_THREADS) void w8a16_gemm_kernel(GemmArgs a) {
     const int n = r0 + wr * 128 + 16 * i + 4 * g;   // member-local row of register 0
     const int nvalid = mem.rows - n;
     if (nvalid <= 0) continue;
+    if (a.splits > 1) {   // this split's F32 partial
+      float* wp = a.ws + int64_t(sp) * a.M * a.ldws + int64_t(t) * a.ldws + mem.col0 + n;
+      for (int r = 0; r < 4 && r < nvalid; ++r) wp[r] = acc[i][r];
+      continue;
+    }
     const int64_t off = int64_t(t) * a.ldy + mem.col0 + n;
     if (a.y_bf16) {
       uint16_t* yp = static_cast<uint16_t*>(a.y) + off;
@@ -1650,17 +1668,74 @@ typedef void (*KernelFn)(Args);
 
 int gemm_row_tiles(const WeightDev& w, int32_t* rt0);
 
+// The split-K sum of the W8A16 GEMM: y[m, c] = the splits' F32 partials added
+// in split order, for the N output columns of every token, then rounded to y's
+// type.  One thread per output.
+struct W16ReduceArgs {
+  const float* ws;
+  int64_t ldws;
+  int64_t split_stride;   // M * ldws
+  void* y;
+  int64_t ldy;
+  int32_t M;
+  int32_t N;
+  int32_t splits;
+  int32_t y_bf16;
+};
+
+__global__ __launch_bounds__(256) void w8a16_splitk_reduce_kernel(W16ReduceArgs a) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(a.M) * a.N) return;
+  const int m = int(idx / a.N), c = int(idx - int64_t(m) * a.N);
+  const float* p = a.ws + int64_t(m) * a.ldws + c;
+  float v = p[0];
+  for (int s = 1; s < a.splits; ++s) v += p[int64_t(s) * a.split_stride];
+  const int64_t off = int64_t(m) * a.ldy + c;
+  if (a.y_bf16) static_cast<uint16_t*>(a.y)[off] = f32_to_bf16_rne(v);
+  else static_cast<float*>(a.y)[off] = v;
+}
+
 // The LDS-staged GEMM kernel runs for aligned operands when its grid fills at
 // least half the compute units: a block takes about the same time whatever
 // the grid (grouped Q/K/V: 121-130 us from 64 to 512 tokens), so with fewer
 // blocks the general kernel, which splits K inside many small blocks, is
 // faster (44 / 84 us at 64 / 128 tokens against 121 us; at 256 tokens 164
 // against 122 us, at 512 325 against 129 us).
-bool gemm_applies(const WeightDev& w, bool aligned, int64_t M) {
-  if (!aligned || M < GW_TOKS) return false;
+//
+// Split-K: when the tile grid leaves more than half the compute units idle,
+// K is cut into up to 8 ranges of at least 4 chunks so the grid covers the
+// device, the splits write F32 partials to the workspace and a second kernel
+// adds them in order; the GEMM then also takes 33 to 63 tokens (one partly
+// filled token tile).
+struct W16Split {
+  int splits;
+  int kb_per_split;
+};
+
+W16Split w16_split(const WeightDev& w, int64_t M) {
   const int64_t blocks = int64_t(gemm_row_tiles(w, nullptr)) * ((M + GW_TOKS - 1) / GW_TOKS);
-  return 2 * blocks >= w16_device_cus();
+  const int cus = w16_device_cus();
+  int s = 1;
+  if (2 * blocks < cus) s = int(std::min<int64_t>({(cus + blocks - 1) / blocks, 8, w.Kb / 4}));
+  s = std::max(s, 1);
+  const int kps = (w.Kb + s - 1) / s;
+  return W16Split{(w.Kb + kps - 1) / kps, kps};
 }
+
+bool gemm_applies(const WeightDev& w, bool aligned, int64_t M) {
+  if (!aligned || M <= SM_SPLIT_MAXM) return false;
+  const int64_t blocks = int64_t(gemm_row_tiles(w, nullptr)) * ((M + GW_TOKS - 1) / GW_TOKS);
+  return 2 * blocks >= w16_device_cus() || (M >= 33 && w16_split(w, M).splits > 1);
+}
+
+int64_t w16_n_total(const WeightDev& w) {
+  int64_t n = 0;
+  for (int i = 0; i < w.n_members; ++i) n = std::max<int64_t>(n, int64_t(w.m[i].col0) + w.m[i].rows);
+  return n;
+}
+
+// the split partials' row pitch: N rounded up to 4 floats
+int64_t w16_ldws(const WeightDev& w) { return (w16_n_total(w) + 3) / 4 * 4; }
 
 int gemm_row_tiles(const WeightDev& w, int32_t* rt0) {
   int t = 0;
@@ -1673,7 +1748,7 @@ int gemm_row_tiles(const WeightDev& w, int32_t* rt0) {
 }
 
 bsf8_status launch_gemm(const WeightDev& w, const void* x, bool x_bf16, int64_t M, int64_t ldx, void* y, bool y_bf16,
-                        int64_t ldy, hipStream_t stream) {
+                        int64_t ldy, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   GemmArgs a{};
   a.w = w;
   const int rt = gemm_row_tiles(w, a.rt0);
@@ -1689,22 +1764,53 @@ bsf8_status launch_gemm(const WeightDev& w, const void* x, bool x_bf16, int64_t 
   bool vec = reinterpret_cast<uintptr_t>(y) % (4 * ye) == 0 && ldy % 4 == 0;
   for (int i = 0; i < w.n_members; ++i) vec = vec && w.m[i].col0 % 4 == 0;
   a.y_vec = vec ? 1 : 0;
-  const int64_t blocks = int64_t(rt) * a.m_tiles;
+  const W16Split sp = w16_split(w, M);
+  a.splits = sp.splits;
+  a.kb_per_split = sp.kb_per_split;
+  a.ldws = w16_ldws(w);
+  a.ws = static_cast<float*>(workspace);
+  const int64_t blocks = int64_t(rt) * a.m_tiles * sp.splits;
   if (blocks == 0) return BSF8_OK;
   if (blocks >= (int64_t(1) << 31)) {
     set_error("UNSUPPORTED: %lld blocks", (long long)blocks);
     return BSF8_E_UNSUPPORTED;
   }
+  if (sp.splits > 1 && (workspace == nullptr ||
+                        workspace_bytes < size_t(sp.splits) * size_t(M) * size_t(a.ldws) * sizeof(float))) {
+    set_error("WORKSPACE: %d split-K partials of [%lld, %lld] F32 need a workspace", sp.splits, (long long)M,
+              (long long)a.ldws);
+    return BSF8_E_WORKSPACE;
+  }
   const bool sb = w.scale_bf16 != 0;
   auto k = x_bf16 ? (sb ? w8a16_gemm_kernel<true, true> : w8a16_gemm_kernel<true, false>)
                   : (sb ? w8a16_gemm_kernel<false, true> : w8a16_gemm_kernel<false, false>);
   hipLaunchKernelGGL(k, dim3(unsigned(blocks)), dim3(GW_THREADS), 0, stream, a);
-  return device_status(hipGetLastError(), "w8a16_gemm launch");
+  bsf8_status st = device_status(hipGetLastError(), "w8a16_gemm launch");
+  if (st != BSF8_OK || sp.splits == 1) return st;
+  W16ReduceArgs r{};
+  r.ws = a.ws;
+  r.ldws = a.ldws;
+  r.split_stride = M * a.ldws;
+  r.y = y;
+  r.ldy = ldy;
+  r.M = int32_t(M);
+  r.N = int32_t(w16_n_total(w));
+  r.splits = sp.splits;
+  r.y_bf16 = y_bf16 ? 1 : 0;
+  const int64_t n = M * int64_t(r.N);
+  hipLaunchKernelGGL(w8a16_splitk_reduce_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, r);
+  return device_status(hipGetLastError(), "w8a16 split-K reduce launch");
 }
 
 }  // namespace
 
-size_t w8a16_workspace_bytes(const WeightDev&, int64_t) { return 0; }
+// the split-K partials of the GEMM (an upper bound over the paths: operands that
+// are not 16-byte aligned take kernels without a workspace)
+size_t w8a16_workspace_bytes(const WeightDev& w, int64_t M) {
+  if (!gemm_applies(w, true, M)) return 0;
+  const W16Split sp = w16_split(w, M);
+  return sp.splits > 1 ? size_t(sp.splits) * size_t(M) * size_t(w16_ldws(w)) * sizeof(float) : 0;
+}
 
 std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
   if (!gemm_applies(w, aligned, M) && aligned && M > SM_MAXM && M <= SM_SPLIT_MAXM)
@@ -1716,9 +1822,11 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
     const int rt = gemm_row_tiles(w, nullptr);
     snprintf(b, sizeof(b),
              "arm=w8a16 arithmetic=f32 activations (exact 3-term bf16 split) x e4m3 weights, f32 accumulate, "
-             "mfma_f32_16x16x32_bf16 | kernel=w8a16_gemm tile=%dx%d waves=8 lds=2 stages (register-staged copies) | "
-             "M=%lld blocks=%lld",
-             GW_ROWS, GW_TOKS, (long long)M, (long long)rt * ((M + GW_TOKS - 1) / GW_TOKS));
+             "mfma_f32_16x16x32_bf16 | kernel=w8a16_gemm tile=%dx%d waves=8 lds=2 stages (register-staged copies) "
+             "split_k=%d (%d chunks per split%s) | M=%lld blocks=%lld",
+             GW_ROWS, GW_TOKS, w16_split(w, M).splits, w16_split(w, M).kb_per_split,
+             w16_split(w, M).splits > 1 ? ", F32 partials added in split order by a second kernel" : "", (long long)M,
+             (long long)rt * ((M + GW_TOKS - 1) / GW_TOKS) * w16_split(w, M).splits);
     return b;
   }
   const M1Shape m1 = m1_shape(w, aligned, M > 0 ? M : 1);
@@ -1751,7 +1859,7 @@ std::string describe_w8a16(const WeightDev& w, bool aligned, int64_t M) {
 }
 
 bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x_bf16, int64_t M, int64_t ldx,
-                         void* y, bool y_bf16, int64_t ldy, void*, size_t, hipStream_t stream) {
+                         void* y, bool y_bf16, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (w.Kb > MAX_KB) {
     set_error("UNSUPPORTED: K above %d", MAX_KB * CHUNK);
     return BSF8_E_UNSUPPORTED;
@@ -1762,7 +1870,7 @@ bsf8_status launch_w8a16(const WeightDev& w, bool aligned, const void* x, bool x
     if (int64_t(w.m[i].rows) * w.K >= (int64_t(1) << 31)) aligned = false;
   const Plan p = make_plan(w, M, aligned);
   if (p.tiles == 0) return BSF8_OK;
-  if (gemm_applies(w, aligned, M)) return launch_gemm(w, x, x_bf16, M, ldx, y, y_bf16, ldy, stream);
+  if (gemm_applies(w, aligned, M)) return launch_gemm(w, x, x_bf16, M, ldx, y, y_bf16, ldy, ws, ws_bytes, stream);
   if (aligned && M > SM_MAXM && M <= SM_SPLIT_MAXM) {
     // rows SM_MAXM on of x start 16-byte aligned too (ldx * element size is a multiple of 16)
     const bsf8_status st = launch_w8a16(w, true, x, x_bf16, SM_MAXM, ldx, y, y_bf16, ldy, nullptr, 0, stream);

@@ -88,13 +88,18 @@ def test_handle_geometry_and_member_local_rows():
         d = L.bsf8_describe(h, 0, 1).decode()
         assert "w8a16" in d and "K=5120" in d and "members=3" in d
         # W8A16 plans by token count: the few-token kernel to 16, two of its
-        # launches (16, then the rest) to 32, the general kernel beyond
+        # launches (16, then the rest) to 32, then the LDS-staged GEMM, split over
+        # K while its tile grid is small (32 row tiles x 1 token tile x 8 splits)
         assert "kernel=w8a16_small_m " in L.bsf8_describe(h, 0, 16).decode()
         d = L.bsf8_describe(h, 0, 24).decode()
         assert d.startswith("two launches, tokens [0, 16) then [16, 24): ") and d.count("kernel=w8a16_small_m ") == 2, d
         # (one token on this grouped weight also takes the few-token kernel: 32-row blocks)
         assert L.bsf8_describe(h, 0, 17).decode().startswith("two launches, tokens [0, 16) then [16, 17): ")
-        assert "kernel=w8a16 rows=" in L.bsf8_describe(h, 0, 33).decode()
+        d = L.bsf8_describe(h, 0, 33).decode()
+        assert "kernel=w8a16_gemm " in d and "split_k=8 (5 chunks per split" in d and "blocks=256" in d, d
+        b33 = ctypes.c_size_t()
+        assert L.bsf8_workspace_size(h, 0, 33, ctypes.byref(b33)) == 0 and b33.value == 8 * 33 * 8144 * 4
+        assert L.bsf8_workspace_size(h, 0, 32, ctypes.byref(b33)) == 0 and b33.value == 0
         d = L.bsf8_describe(h, 1, 512).decode()
         assert "w8a8" in d and "e4m3" in d
     finally:

@@ -45,10 +45,12 @@ def test_graph_of_every_kernel_family_replays_eager_bits():
     w_a = _weight("graph_WA", 2048, 2048)      # decode-sized: one, three and seven tokens; split-K W8A8
     w_g = _weight("graph_WG", 4096, 1024)      # 16 row tiles x 8 token tiles at M = 512: the LDS-staged GEMM
     w_r = _weight("graph_WR", 512, 8192)       # eight chunks per wave at one token: the ring kernel
+    w_s = _weight("graph_WS", 512, 768)        # six chunks: 40 tokens on the general kernel
 
     # (name, weight, M, arm): F32 activations; the W8A8 calls quantize their own x first
     calls = [("w8a16_m1", w_a, 1, B.ARM_W8A16), ("w8a16_m3", w_a, 3, B.ARM_W8A16), ("w8a16_m7", w_a, 7, B.ARM_W8A16),
-             ("w8a16_m40", w_a, 40, B.ARM_W8A16), ("w8a16_gemm_m512", w_g, 512, B.ARM_W8A16),
+             ("w8a16_m40", w_a, 40, B.ARM_W8A16), ("w8a16_general_m40", w_s, 40, B.ARM_W8A16),
+             ("w8a16_gemm_m512", w_g, 512, B.ARM_W8A16),
              ("w8a16_ring_m1", w_r, 1, B.ARM_W8A16),
              ("w8a8_m1", w_a, 1, B.ARM_W8A8), ("w8a8_m3", w_a, 3, B.ARM_W8A8), ("w8a8_split_m64", w_a, 64, B.ARM_W8A8),
              ("w8a8_dyn_m1", w_a, 1, B.ARM_W8A8_DYNAMIC), ("w8a8_dyn_m3", w_a, 3, B.ARM_W8A8_DYNAMIC),
@@ -68,10 +70,13 @@ def test_graph_of_every_kernel_family_replays_eager_bits():
         banner(f"graph case {name}: {describes[name]}")
     joined = " ".join(describes.values())
     for kernel in ("kernel=w8a16_m1 ", "kernel=w8a16_m1_ring", "kernel=w8a16_small_m<e4m3>", "kernel=w8a16_small_m",
-                   "kernel=w8a16_gemm ", "w8a16_m1<e4m3>", "kernel=w8a8_gemm_fast", "w8a16_m1<quantizing>",
+                   "kernel=w8a16_gemm ", "kernel=w8a16 rows=", "w8a16_m1<e4m3>", "kernel=w8a8_gemm_fast", "w8a16_m1<quantizing>",
                    "arm=w8a8-dynamic", "quant_act into the workspace"):
         assert kernel in joined, (kernel, describes)
     assert "split_k=1 " not in describes["w8a8_split_m64"], describes["w8a8_split_m64"]
+    # the W8A16 GEMM split over K, with its reduction kernel, in the graph too
+    assert "kernel=w8a16_gemm " in describes["w8a16_m40"] and "split_k=1 " not in describes["w8a16_m40"], \
+        describes["w8a16_m40"]
 
     # the fused GLU step and the activation alone on a gate/up output [64, 2 x 640] (a ragged last group)
     yglu = _x("graph_Yglu", 64, 2 * 640, t.bfloat16)

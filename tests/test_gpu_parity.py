@@ -570,7 +570,8 @@ RNE_W8A16 = [
     ("few_token_mfma_two_passes", (300, 130), 1024, 6),
     ("few_token_mfma_three_passes", (300, 130), 1024, 13),
     ("few_token_two_launches", (300, 130), 1024, 27),
-    ("general_mfma", (300, 130), 1024, 40),
+    ("general_mfma", (300, 130), 768, 40),          # 6 chunks: too few to split the GEMM
+    ("lds_gemm_split_k", (300, 130), 1024, 40),
     ("lds_staged_gemm", (4100, 700), 1024, 448),
     ("lds_staged_gemm_element_stores", (4101, 700), 1024, 400),
     ("general_bytewise_k1000", (300, 130), 1000, 5),
@@ -625,11 +626,12 @@ def test_w8a16_lds_gemm(sdt):
             dev_members.append((t.from_numpy(codes).to(device()), t.from_numpy(np.asarray(sc, np.float32)).to(device()).to(dt)))
     w = B.BlockFP8Weight(dev_members, block=(0, 0) if sdt == "per_tensor" else (128, 128))
     x_all = synth.gaussian_activations(241, f"gemm16_X_{sdt}", 448, K)
-    for M in (385, 448):
+    for M in (33, 130, 385, 448):
         x = x_all[:M]
         d = w.describe(B.ARM_W8A16, M)
         if t.cuda.get_device_properties(0).multi_processor_count <= 256:
             assert "kernel=w8a16_gemm" in d, d
+            assert ("split_k=2 (5 chunks per split" if M < 200 else "split_k=1 ") in d, d
         banner(f"w8a16 lds gemm {sdt} M={M}: {d}")
         y = to_np(B.linear_w8a16(w, t.from_numpy(x).to(device())))
         assert_within(y, O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om), False, f"lds gemm {sdt} M={M}")
@@ -637,6 +639,36 @@ def test_w8a16_lds_gemm(sdt):
         xe = xb.float().numpy()
         yb = to_np(B.linear_w8a16(w, xb.to(device()), out_dtype=t.bfloat16))
         assert_within(yb, O.linear_w8a16(xe, om), O.abs_bound_w8a16(xe, om), True, f"lds gemm bf16 {sdt} M={M}")
+
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_w8a16_gemm_split_k(xdt):
+    """The LDS-staged W8A16 GEMM split over K while its tile grid is small: members of
+    700 and 300 rows (5 row tiles), K = 5120 (40 chunks: 8 splits of 5), M = 33 (one
+    partly filled token tile), 64 and 200 (4 token tiles, the last partly filled); F32
+    partials added in split order by a second kernel; F32 and BF16 outputs against
+    the oracle."""
+    t = torch()
+    ms = [synth.random_code_weight(243, f"w16split_W{i}", r, 5120, scale_log2=(-9, -3)) for i, r in enumerate((700, 300))]
+    w, _keep = weight_on_device(ms)
+    om = oracle_members(ms)
+    x_all = synth.gaussian_activations(243, "w16split_X", 200, 5120)
+    if xdt == "bf16":
+        x_all = O.f32_to_bf16(x_all).astype(np.float32)
+    for M in (33, 64, 200):
+        x = x_all[:M]
+        d = w.describe(B.ARM_W8A16, M)
+        banner(f"w8a16 gemm split-K {xdt} M={M}: {d}")
+        if t.cuda.get_device_properties(0).multi_processor_count <= 256:
+            assert "kernel=w8a16_gemm" in d and "split_k=8 (5 chunks per split" in d, d
+        assert w.workspace_size(B.ARM_W8A16, M) >= 8 * M * 1000 * 4
+        xd = t.from_numpy(x).to(device())
+        if xdt == "bf16":
+            xd = xd.to(t.bfloat16)
+        ref, bound = O.linear_w8a16(x, om), O.abs_bound_w8a16(x, om)
+        for odt in (t.float32, t.bfloat16):
+            y = to_np(B.linear_w8a16(w, xd, out_dtype=odt))
+            assert_within(y, ref, bound, odt == t.bfloat16, f"w8a16 gemm split-K {xdt} M={M}")
 
 
 RNE_W8A8 = [
