@@ -273,7 +273,9 @@ bsf8_status bsf8_glu_act(const void* y, int32_t y_dtype, int64_t M, int64_t F, i
  * output features, long K): K is then cut into S ranges, each range's F32
  * partial tile goes to the workspace (S x M x N floats, N rounded up per member
  * to a multiple of 4), and a second kernel adds them in range order, so results
- * do not depend on timing.  The size depends on the device's compute-unit count
+ * do not depend on timing.  The W8A16 arm does the same from 33 tokens while
+ * its GEMM's tiles cannot cover half the device (S x M x N floats, N rounded
+ * up to a multiple of 4); up to 32 tokens it needs none.  The size depends on the device's compute-unit count
  * (the current device).  No initialization is needed; every call overwrites
  * what it reads.  Calls that overlap in time must not share a workspace.  The
  * buffer must be 256-byte aligned.
@@ -291,7 +293,8 @@ bsf8_status bsf8_workspace_size(const bsf8_weight* w, int32_t arm, int64_t M, si
  * against weights decoded exactly to F32 (any K); more tokens run the BF16
  * matrix cores on an exact three-term split of each F32 activation (a
  * weight-streaming kernel up to sixteen tokens, and for 17 to 32 two of its
- * launches, 16 tokens then the rest; an LDS-staged GEMM for hundreds).
+ * launches, 16 tokens then the rest; from 33 tokens an LDS-staged GEMM, split
+ * over K into a workspace while its tiles are too few to fill the device).
  *
  * x : [M, K] F32 or BF16, leading dimension ldx (elements), 16-byte aligned
  *     rows when K allows.
