@@ -1702,7 +1702,7 @@ __global__ __launch_bounds__(256) void w8a16_splitk_reduce_kernel(W16ReduceArgs 
 // faster (44 / 84 us at 64 / 128 tokens against 121 us; at 256 tokens 164
 // against 122 us, at 512 325 against 129 us).
 //
-// Split-K: when the tile grid leaves more than half the compute units idle,
+// Split-K: when the tile grid leaves half the compute units or more idle,
 // K is cut into up to 8 ranges of at least 4 chunks, as many as keep the grid
 // within one block per compute unit, the splits write F32 partials to the workspace and a second kernel
 // adds them in order; the GEMM then also takes 33 to 63 tokens (one partly
@@ -1717,7 +1717,7 @@ W16Split w16_split(const WeightDev& w, int64_t M) {
   const int cus = w16_device_cus();
   int s = 1;
   // the most splits that keep the grid within one round of blocks (one per unit)
-  if (2 * blocks < cus) s = int(std::min<int64_t>({cus / blocks, 8, w.Kb / 4}));
+  if (2 * blocks <= cus) s = int(std::min<int64_t>({cus / blocks, 8, w.Kb / 4}));
   s = std::max(s, 1);
   const int kps = (w.Kb + s - 1) / s;
   return W16Split{(w.Kb + kps - 1) / kps, kps};
