@@ -729,7 +729,7 @@ def main():
     if a.no_clock_sample:
         os.environ["BSF8_BENCH_NO_CLOCK_SAMPLE"] = "1"
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus above 1 is not supported (how the path would shard is described with the design)"}))
         sys.exit(2)
     import torch
     import block_scaled_fp8_linear_amd as B
